@@ -1,0 +1,494 @@
+"""CPU oracle for the FP4 quantize / pre-shift / search / quantized-GEMM path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product package imports this module; only
+``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg use it.
+It shares no code with the HIP library.  The brute-force parts (grid enumeration,
+nearest-point search, exact error sums) are plain C in ``fp4_oracle.c``; everything
+else is numpy, with float64 BLAS for the GEMM contractions.
+
+Sources (web pages, cited by title and section):
+
+* [FP4-LLM]  "首个支持4-bit浮点量化的LLM来了，解决LLaMA、BERT等的部署难题" (811yy.cn),
+  summarising the LLM-FP4 paper: the FP value formula (sign, exponent field
+  p in [0, 2^e-1], mantissa bits, bias b); "scale and clip" eqs. (2)-(3); bias from
+  the chosen range, eq. (4), usable as a real-valued scale; "compare and quantize",
+  eq. (5); the scaling factor kept outside the low-bit matrix product ("efficient
+  matrix multiplication"); the search over exponent/mantissa split and range; the
+  pre-shifted exponent bias (per-channel maxima split into a per-tensor real scale
+  times per-channel powers of two that are folded into the weights).
+* [Overview] "量化技术详解" (aidocs.cortexgrid.cn): floating-point types (FP16 range),
+  granularities, static quantization, section NF4 (grid at normal quantiles).
+* [W8A8]     intelliparadigm.com LLM-quantization practice, section 2.2: scale-factored
+  integer matmul (low-bit product first, scales multiplied afterwards); group size 128.
+* [Tutorial] "为什么我们需要4-bit浮点量化" (devpress.csdn.net), section 2.2: two 4-bit
+  values per byte.
+
+Readings where the pages are silent or garbled are listed in the design doc.  Every
+function that has no independent pin in ``tests/test_oracle_pins.py`` says
+"parity unpinned" in its docstring (none at present).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from dataclasses import dataclass
+from fractions import Fraction
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fp4_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libfp4_oracle.so")
+
+GCC_CMD = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+           "-shared", "-std=c11", "-o", _LIB_PATH, _SRC, "-lm"]
+
+
+def build(force: bool = False) -> str:
+    """Compile the C part of the oracle (gcc, no FMA contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or \
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        subprocess.check_call(GCC_CMD)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _c():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        lib.orc_minifloat_value.restype = ctypes.c_double
+        lib.orc_minifloat_value.argtypes = [ctypes.c_int] * 4
+        lib.orc_minifloat_grid.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P]
+        lib.orc_quantize.argtypes = [P, P, ctypes.c_int64, ctypes.c_int, P, ctypes.c_int, P]
+        lib.orc_search_sse.argtypes = [P, ctypes.c_int64, P, ctypes.c_int, ctypes.c_int, P,
+                                       ctypes.c_int, P]
+        lib.orc_exp_min.restype = ctypes.c_int
+        lib.orc_nbucket.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+# ----------------------------------------------------------------------------------
+# Grids ([FP4-LLM] FP value formula; [Overview] NF4)
+# ----------------------------------------------------------------------------------
+E1M2, E2M1, E3M0 = (1, 2), (2, 1), (3, 0)
+FORMATS_4BIT = (E1M2, E2M1, E3M0)
+
+
+def minifloat_grid(e: int, m: int, b: int = 1) -> np.ndarray:
+    """All 2^(e+m) magnitudes of the FP(e, m, b) grid, indexed by the magnitude code
+    c = p<<m | d.  p == 0 is subnormal (2^(1-b)*d/2^m), p >= 1 normal
+    (2^(p-b)*(1+d/2^m)); no code is reserved for inf/NaN."""
+    out = np.zeros(1 << (e + m), dtype=np.float64)
+    _c().orc_minifloat_grid(e, m, b, _ptr(out))
+    return out
+
+
+def nf4_table() -> np.ndarray:
+    """16-point NF4 grid ([Overview], NF4: levels at quantiles of N(0,1)).
+
+    Plainest 16-level reading: G_i = Phi^-1((i + 1/2)/16) normalised so the end points
+    are +-1, each rounded to binary16 (so every grid value and every midpoint of two
+    neighbours is exact in binary32).  Symmetric, no exact zero."""
+    from scipy.special import ndtri
+    q = ndtri((np.arange(16) + 0.5) / 16.0)
+    g = q / ndtri(15.5 / 16.0)
+    return g.astype(np.float16).astype(np.float64)
+
+
+@dataclass(frozen=True)
+class Grid:
+    """kind 'minifloat': sign-magnitude code sign<<3 | (p<<m | d), values = magnitudes.
+    kind 'lut': code = index into 16 sorted signed values."""
+    kind: str
+    e: int = 0
+    m: int = 0
+    values: tuple = ()
+
+    @property
+    def array(self) -> np.ndarray:
+        return np.asarray(self.values, dtype=np.float64)
+
+    @property
+    def qmax(self) -> float:
+        v = self.array
+        return float(v[-1]) if self.kind == "minifloat" else float(max(abs(v[0]), abs(v[-1])))
+
+    def decode(self, codes: np.ndarray) -> np.ndarray:
+        """Grid value of each code (float64), without any scale."""
+        c = codes.astype(np.int64)
+        if self.kind == "minifloat":
+            mag = self.array[c & 7]
+            return np.where((c >> 3) & 1, -mag, mag)
+        return self.array[c & 15]
+
+
+def minifloat(e: int, m: int) -> Grid:
+    return Grid("minifloat", e, m, tuple(minifloat_grid(e, m, 1)))
+
+
+def lut(values) -> Grid:
+    v = np.asarray(values, dtype=np.float64)
+    assert v.shape == (16,) and np.all(np.diff(v) > 0)
+    return Grid("lut", 0, 0, tuple(v))
+
+
+def nf4() -> Grid:
+    return lut(nf4_table())
+
+
+def qmax(e: int, m: int, b: int = 1) -> float:
+    """Largest magnitude of FP(e, m, b): (2 - 2^-m) * 2^(2^e - 1 - b)  ([FP4-LLM] the
+    clipping bound +-Qmax of eq. (2))."""
+    return float(minifloat_grid(e, m, b)[-1])
+
+
+def real_bias(s: float) -> float:
+    """Real-valued exponent bias equivalent to scale s on the canonical bias-1 grid
+    ([FP4-LLM] eq. (4): the bias derived from the range acts as a real scale):
+    values 2^(p-b)(1+d/2^m) = s * 2^(p-1)(1+d/2^m)  <=>  b = 1 - log2(s)."""
+    return 1.0 - math.log2(float(s)) if s > 0 else math.inf
+
+
+# ----------------------------------------------------------------------------------
+# Rounding helpers (binary16 / bfloat16 storage)
+# ----------------------------------------------------------------------------------
+def f32(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float32)
+
+
+def rne_f16(x) -> np.ndarray:
+    """Round binary32 to binary16 (numpy's cast is round-to-nearest-even)."""
+    return f32(x).astype(np.float16)
+
+
+def rne_bf16_bits(x) -> np.ndarray:
+    """Round finite binary32 values to bfloat16, nearest-even; returns uint16 bits."""
+    u = f32(x).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def reciprocal(s) -> np.ndarray:
+    """r = fl32(1/s), and 0 where s == 0 (an all-zero block quantizes to +-0)."""
+    s = f32(s)
+    with np.errstate(divide="ignore"):
+        r = np.where(s == 0, np.float32(0), np.float32(1) / np.where(s == 0, np.float32(1), s))
+    return r.astype(np.float32)
+
+
+# ----------------------------------------------------------------------------------
+# Quantize ("scale and clip" + "compare and quantize") and pack
+# ----------------------------------------------------------------------------------
+def quantize(x, r, grid: Grid) -> np.ndarray:
+    """codes[i] for y = fl32(x[i] * r[i]); brute-force nearest grid point, exact ties
+    to the even code; minifloat codes carry signbit(x) in bit 3 ([FP4-LLM] eqs. (2)-(5)
+    read as: scale by the reciprocal of the full-precision scale, clip to +-Qmax,
+    round to the nearest representable value)."""
+    x = np.ascontiguousarray(f32(x))
+    r = np.ascontiguousarray(np.broadcast_to(f32(r), x.shape))
+    assert np.all(np.isfinite(x)), "non-finite inputs are not valid"
+    out = np.empty(x.shape, dtype=np.uint8)
+    g = np.ascontiguousarray(grid.array)
+    _c().orc_quantize(_ptr(x), _ptr(r), x.size, 0 if grid.kind == "minifloat" else 1,
+                      _ptr(g), g.size, _ptr(out))
+    return out
+
+
+def pack(codes: np.ndarray) -> np.ndarray:
+    """Two codes per byte along the last axis: byte j = code[2j] | code[2j+1] << 4
+    ([Tutorial] section 2.2, two 4-bit values per byte; the low nibble holding the
+    even element is a reading)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    assert c.shape[-1] % 2 == 0
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = p & 15
+    out[..., 1::2] = p >> 4
+    return out
+
+
+# ----------------------------------------------------------------------------------
+# Calibration ([Overview] granularities; [W8A8] section 2.2 calibrate: max |x|)
+# ----------------------------------------------------------------------------------
+def amax_tensor(x) -> np.float32:
+    return np.float32(np.max(np.abs(f32(x)))) if np.size(x) else np.float32(0)
+
+
+def amax_columns(x, first_rows: int) -> np.ndarray:
+    """Per-column max |x| over rows 0 .. first_rows-1 (static calibration tokens)."""
+    return np.max(np.abs(f32(x)[:first_rows]), axis=0).astype(np.float32)
+
+
+def amax_row_groups(x, group: int) -> np.ndarray:
+    x = f32(x)
+    R, C = x.shape
+    return np.max(np.abs(x.reshape(R, C // group, group)), axis=2).astype(np.float32)
+
+
+def scale_from_amax(amax, grid: Grid) -> np.ndarray:
+    """s = fl32(amax / Qmax): the full-precision scale that maps the range onto +-Qmax."""
+    return (f32(amax) / np.float32(grid.qmax)).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------------
+# Granular quantize + pack, dequantize
+# ----------------------------------------------------------------------------------
+def quantize_pack(x, grid: Grid, mode: str, group: int = 0, scale_dtype: str = "f32",
+                  tensor_scale=None, col_shift=None, amax=None):
+    """mode: 'tensor' | 'row' | 'group' (group columns along each row).
+    scale_dtype 'f16' stores binary16 scales; quantization always uses the STORED
+    scale (r = fl32(1/stored)).  tensor_scale: fixed per-tensor scale (static
+    activation quantization).  col_shift k[cols]: the multiplier of column j becomes
+    r * 2^-k[j] (pre-shifted exponent bias).  Returns (packed uint8, scales)."""
+    x = f32(x)
+    R, C = x.shape
+    if mode == "tensor":
+        if tensor_scale is not None:
+            s = np.float32(tensor_scale)
+        else:
+            s = scale_from_amax(amax_tensor(x) if amax is None else amax, grid)
+        s_st = rne_f16(s).astype(np.float32) if scale_dtype == "f16" else np.float32(s)
+        r = np.full((R, C), reciprocal(s_st), dtype=np.float32)
+        scales = np.array([s_st], dtype=np.float32)
+    elif mode == "row":
+        s = scale_from_amax(np.max(np.abs(x), axis=1) if amax is None else amax, grid)
+        s_st = rne_f16(s).astype(np.float32) if scale_dtype == "f16" else s
+        r = np.repeat(reciprocal(s_st)[:, None], C, axis=1)
+        scales = s_st.astype(np.float32)
+    elif mode == "group":
+        s = scale_from_amax(amax_row_groups(x, group) if amax is None else amax, grid)
+        s_st = rne_f16(s).astype(np.float32) if scale_dtype == "f16" else s
+        r = np.repeat(reciprocal(s_st), group, axis=1)
+        scales = s_st.astype(np.float32)
+    else:
+        raise ValueError(mode)
+    if col_shift is not None:
+        k = np.asarray(col_shift, dtype=np.int64)
+        r = np.ldexp(r, -k[None, :]).astype(np.float32)
+    codes = quantize(x, r, grid)
+    if scale_dtype == "f16":
+        scales = scales.astype(np.float16)
+    return pack(codes), scales
+
+
+def dequantize(packed, grid: Grid, mode: str, scales, group: int = 0, col_shift=None):
+    """v = +-fl32(g(code) * s), times 2^k[j] for a shifted column (exact)."""
+    codes = unpack(packed)
+    R, C = codes.shape
+    s = f32(np.asarray(scales).astype(np.float32))
+    if mode == "tensor":
+        sf = np.full((R, C), s.reshape(-1)[0], dtype=np.float32)
+    elif mode == "row":
+        sf = np.repeat(s.reshape(R, 1), C, axis=1)
+    else:
+        sf = np.repeat(s.reshape(R, C // group), group, axis=1)
+    v = (grid.decode(codes).astype(np.float32) * sf).astype(np.float32)
+    if col_shift is not None:
+        v = np.ldexp(v, np.asarray(col_shift, dtype=np.int64)[None, :]).astype(np.float32)
+    return v
+
+
+# ----------------------------------------------------------------------------------
+# Pre-shifted exponent bias ([FP4-LLM], pre-shifted exponent bias paragraphs)
+# ----------------------------------------------------------------------------------
+K_MIN = -64
+
+
+def preshift(chan_amax, act_grid: Grid):
+    """Split per-channel activation maxima c_k into a per-tensor real scale and
+    per-channel powers of two:  a = fl32(c_max / Qmax),  k_k = the smallest integer j
+    with c_max * 2^j >= c_k (so k_k <= 0 and no calibrated value leaves the range),
+    k_k = 0 for c_k = 0, clamped at -64.  Exact, from frexp: c = f * 2^E with
+    f in [0.5, 1):  k = E_k - E_max + (f_max < f_k)."""
+    c = f32(chan_amax)
+    cmax = np.float32(np.max(c)) if c.size else np.float32(0)
+    a = np.float32(cmax / np.float32(act_grid.qmax))
+    fk, ek = np.frexp(c.astype(np.float64))
+    fm, em = np.frexp(np.float64(cmax))
+    k = (ek - em + (fm < fk).astype(np.int64)).astype(np.int64)
+    k = np.where(c == 0, 0, np.maximum(k, K_MIN)).astype(np.int8)
+    return k, a
+
+
+def shift_weights(w, k) -> np.ndarray:
+    """W'[n, j] = W[n, j] * 2^k[j]  (exact power-of-two scaling)."""
+    return np.ldexp(f32(w), np.asarray(k, dtype=np.int64)[None, :]).astype(np.float32)
+
+
+def preshift_weights(w, chan_amax, act_grid: Grid, w_grid: Grid, w_mode: str = "row",
+                     w_group: int = 0):
+    """Fold the per-channel powers of two into W before weight quantization; the
+    weight scale is taken per output row (or per group) of the shifted W'."""
+    k, a = preshift(chan_amax, act_grid)
+    wp = shift_weights(w, k)
+    packed, scales = quantize_pack(wp, w_grid, w_mode, w_group)
+    return k, a, packed, scales
+
+
+def quantize_activations(x, act_grid: Grid, a, k):
+    """Static activation quantization with the pre-shift: multiplier of column j is
+    fl32(1/a) * 2^-k_j; one per-tensor scale a."""
+    return quantize_pack(x, act_grid, "tensor", tensor_scale=a, col_shift=k)
+
+
+# ----------------------------------------------------------------------------------
+# Format and clip-range search ([FP4-LLM] search-based FP quantization)
+# ----------------------------------------------------------------------------------
+def clip_ratios(nclips: int = 100, lo: float = 0.5, hi: float = 1.0) -> np.ndarray:
+    """nclips evenly spaced fractions of max|w| from lo to hi inclusive, computed in
+    binary64 and rounded once to binary32."""
+    j = np.arange(nclips, dtype=np.float64)
+    return (lo + (hi - lo) * j / (nclips - 1)).astype(np.float32)
+
+
+def _buckets_to_float(buckets: np.ndarray, exp_min: int, denom: int) -> float:
+    """Correctly rounded binary64 of (sum_j bucket_j * 2^(exp_min + j)) / denom."""
+    total = 0
+    lo = buckets[0::2]
+    hi = buckets[1::2]
+    for j in np.nonzero((lo != 0) | (hi != 0))[0]:
+        total += (int(lo[j]) | (int(hi[j]) << 64)) << int(j)
+    # total = sum_j bucket_j * 2^j; the exact sum is total * 2^exp_min
+    return float(Fraction(total, denom) * Fraction(2) ** exp_min)
+
+
+def candidate_mse(w, formats, clips) -> np.ndarray:
+    """mse[f, j] = correctly rounded binary64 of (1/n) * sum_i (w_i - deq_i)^2 for
+    format f and clip value clips[j] (see fp4_oracle.c: exact accumulation)."""
+    w = np.ascontiguousarray(f32(w).reshape(-1))
+    grids = np.ascontiguousarray(np.stack([minifloat_grid(e, m) for (e, m) in formats]))
+    clips = np.ascontiguousarray(f32(clips))
+    lib = _c()
+    nb = lib.orc_nbucket()
+    emin = lib.orc_exp_min()
+    out = np.zeros(len(formats) * clips.size * nb * 2, dtype=np.uint64)
+    lib.orc_search_sse(_ptr(w), w.size, _ptr(grids), len(formats), grids.shape[1],
+                       _ptr(clips), clips.size, _ptr(out))
+    out = out.reshape(len(formats), clips.size, nb * 2)
+    mse = np.empty((len(formats), clips.size), dtype=np.float64)
+    for f in range(len(formats)):
+        for j in range(clips.size):
+            mse[f, j] = _buckets_to_float(out[f, j], emin, w.size)
+    return mse
+
+
+@dataclass
+class SearchRecord:
+    e: int
+    m: int
+    clip_index: int
+    clip: np.float32
+    scale: np.float32
+    bias: float
+    mse: float
+    mse_runner_up: float
+
+
+def search_tensor(w, formats=FORMATS_4BIT, nclips: int = 100, lo: float = 0.5,
+                  hi: float = 1.0):
+    """Evaluate every (format, clip) candidate, pick the minimum-MSE one (exact ties:
+    earliest in enumeration order, formats outer, clips inner), and pack the tensor
+    with the winner.  Returns (SearchRecord, packed codes, mse table)."""
+    w = f32(w).reshape(-1)
+    amax = amax_tensor(w)
+    clips = (np.float32(amax) * clip_ratios(nclips, lo, hi)).astype(np.float32)
+    mse = candidate_mse(w, formats, clips)
+    flat = mse.reshape(-1)
+    best = int(np.argmin(flat))  # argmin returns the first minimum
+    runner = float(np.min(np.delete(flat, best))) if flat.size > 1 else math.inf
+    f, j = divmod(best, nclips)
+    e, m = formats[f]
+    g = minifloat(e, m)
+    s = np.float32(clips[j] / np.float32(g.qmax))
+    packed, _ = quantize_pack(w.reshape(1, -1), g, "tensor", tensor_scale=s)
+    rec = SearchRecord(e, m, j, np.float32(clips[j]), s, real_bias(s), float(flat[best]), runner)
+    return rec, packed.reshape(-1), mse
+
+
+# ----------------------------------------------------------------------------------
+# Quantized GEMMs (scales factored out of the low-bit product: [FP4-LLM] "efficient
+# matrix multiplication"; [W8A8] section 2.2 quantized_matmul).  Y = X W^T, W [N, K].
+# ----------------------------------------------------------------------------------
+def _weight_values(packed, grid: Grid) -> np.ndarray:
+    return grid.decode(unpack(packed))
+
+
+def gemm_w4a16(x, w_packed, w_grid: Grid, mode: str, w_scales, group: int = 0):
+    """r[m, n] = sum_g s[n, g] * sum_{k in g} x[m, k] * g(c[n, k])  in binary64.
+    x: binary32 values (bf16 activations widened exactly)."""
+    X = f32(x).astype(np.float64)
+    V = _weight_values(w_packed, w_grid)
+    N, K = V.shape
+    s = np.asarray(w_scales).astype(np.float64)
+    if mode == "tensor":
+        return (X @ V.T) * s.reshape(-1)[0]
+    if mode == "row":
+        return (X @ V.T) * s.reshape(1, N)
+    G = K // group
+    s = s.reshape(N, G)
+    out = np.zeros((X.shape[0], N), dtype=np.float64)
+    for gi in range(G):
+        sl = slice(gi * group, (gi + 1) * group)
+        out += (X[:, sl] @ V[:, sl].T) * s[None, :, gi]
+    return out
+
+
+def gemm_w4a4(a_packed, a_grid: Grid, a_scale, w_packed, w_grid: Grid, mode: str,
+              w_scales, group: int = 0):
+    """Both operands quantized.  Returns (r, acc):
+    r = a * sum_(blocks) s[n, b] * sum_{k in b} A_q[m, k] * W_q[n, k]  (binary64);
+    acc = the unscaled code product sum_k A_q W_q (exact in binary64 for minifloat
+    grids: every product is a multiple of 2^-4 and the sums stay far below 2^53)."""
+    A = _weight_values(a_packed, a_grid)
+    V = _weight_values(w_packed, w_grid)
+    N, K = V.shape
+    a = float(np.float32(a_scale))
+    s = np.asarray(w_scales).astype(np.float64)
+    if mode in ("tensor", "row"):
+        acc = A @ V.T
+        sv = s.reshape(-1)[0] if mode == "tensor" else s.reshape(1, N)
+        return acc * sv * a, acc
+    G = K // group
+    s = s.reshape(N, G)
+    out = np.zeros((A.shape[0], N), dtype=np.float64)
+    for gi in range(G):
+        sl = slice(gi * group, (gi + 1) * group)
+        out += (A[:, sl] @ V[:, sl].T) * s[None, :, gi]
+    return out * a, None
+
+
+def w4a4_epilogue_f32(acc, a_scale, s_row) -> np.ndarray:
+    """Fixed epilogue of the row-scaled minifloat W4A4 product, used where the result
+    is compared bit for bit: y32 = fl32(acc * fl32(a * s_n))."""
+    a = np.float32(a_scale)
+    sn = (a * f32(s_row)).astype(np.float32)
+    return (f32(acc) * sn[None, :]).astype(np.float32)
+
+
+def rel_err(y, r) -> float:
+    """Normwise max relative error max|y - r| / max|r|."""
+    r = np.asarray(r, dtype=np.float64)
+    d = np.max(np.abs(np.asarray(y, dtype=np.float64) - r)) if r.size else 0.0
+    den = np.max(np.abs(r)) if r.size else 1.0
+    return float(d / den) if den > 0 else float(d)

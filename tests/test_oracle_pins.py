@@ -1,0 +1,428 @@
+"""Pins of the CPU oracle against facts fixed outside it (no GPU needed).
+
+Each test checks the oracle against something other than itself: values printed on
+the pages or fixed by published formats (tests/golden/), textbook rounding routines
+(numpy round-half-even, frexp), exact rational arithmetic, brute-force searches with
+a different structure, and invariants of the method.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line)
+    return rows
+
+
+# ---------------------------------------------------------------- grids ---------
+def test_e2m1_grid_matches_published_element_type():
+    want = [float(r.split()[1]) for r in _read_golden("e2m1_grid.txt")]
+    assert O.minifloat_grid(2, 1).tolist() == want
+    assert O.qmax(2, 1) == 6.0
+
+
+def test_generic_formula_reproduces_fp16_range():
+    rows = {r.split()[0]: float(r.split()[2]) for r in _read_golden("fp16_range.txt")}
+    # smallest normal: p = 1, d = 0 with e=5, m=10, b=15
+    assert O._c().orc_minifloat_value(5, 10, 15, 1 << 10) == rows["min_normal"]
+    # IEEE reserves p = 31; its largest finite value is p = 30, d = 1023
+    assert O._c().orc_minifloat_value(5, 10, 15, (30 << 10) | 1023) == rows["max_finite"]
+    # the smallest subnormal is 2^-24
+    assert O._c().orc_minifloat_value(5, 10, 15, 1) == 2.0 ** -24
+
+
+def test_other_4bit_grids_by_hand():
+    assert O.minifloat_grid(1, 2).tolist() == [0, .25, .5, .75, 1, 1.25, 1.5, 1.75]
+    assert O.minifloat_grid(3, 0).tolist() == [0, 1, 2, 4, 8, 16, 32, 64]
+    for e, m in O.FORMATS_4BIT:
+        g = O.minifloat_grid(e, m)
+        assert np.all(np.diff(g) > 0)
+        assert O.qmax(e, m) == (2 - 2.0 ** -m) * 2.0 ** (2 ** e - 2)
+        # E1M2 with bias 1 is a uniform 8-level grid: 0..7 steps of 1/4
+    assert np.array_equal(O.minifloat_grid(1, 2) * 4, np.arange(8))
+
+
+def test_bias_shifts_grid_by_power_of_two():
+    # a real bias b is the canonical bias-1 grid scaled by 2^(1-b)
+    for e, m in O.FORMATS_4BIT:
+        for b in (-2, 0, 1, 3, 7):
+            assert np.array_equal(O.minifloat_grid(e, m, b), O.minifloat_grid(e, m, 1) * 2.0 ** (1 - b))
+    assert O.real_bias(1.0) == 1.0
+    assert O.real_bias(0.25) == 3.0
+
+
+# ----------------------------------------------------- rounding (textbook) ------
+def _textbook_e2m1(y):
+    """Round |y| to 1 fraction bit (normal) / step 1/2 (subnormal), ties to even,
+    saturate at 6 -- IEEE-style rounding written with numpy's round-half-even."""
+    y = np.abs(y.astype(np.float64))
+    f, E = np.frexp(y)  # y = f * 2^E, f in [0.5, 1)
+    normal = np.ldexp(np.round(f * 4) / 4, E)
+    sub = np.round(y * 2) / 2
+    q = np.where(y < 1.0, sub, normal)
+    q = np.minimum(q, 6.0)
+    return np.searchsorted(O.minifloat_grid(2, 1), q)
+
+
+def _textbook_e1m2(y):
+    return np.minimum(np.round(np.abs(y.astype(np.float64)) * 4), 7).astype(np.int64)
+
+
+def _textbook_e3m0(y):
+    """Nearest power of two (or zero), an exact midpoint going to the even code."""
+    y = np.abs(y.astype(np.float64))
+    out = np.zeros(y.shape, dtype=np.int64)
+    # code c >= 1 has value 2^(c-1); midpoints 0.5, 1.5, 3, 6, 12, 24, 48
+    mids = [0.5] + [1.5 * 2.0 ** (c - 1) for c in range(1, 7)]
+    for c, t in enumerate(mids, start=1):
+        out = np.where((y > t) | ((y == t) & (c % 2 == 0)), c, out)
+    return out
+
+
+def _interesting_values(lim, rng):
+    g = np.concatenate([O.minifloat_grid(e, m) for e, m in O.FORMATS_4BIT])
+    mids = np.concatenate([(O.minifloat_grid(e, m)[1:] + O.minifloat_grid(e, m)[:-1]) / 2
+                           for e, m in O.FORMATS_4BIT])
+    pts = np.concatenate([g, mids])
+    near = np.concatenate([np.nextafter(pts.astype(np.float32), np.float32(np.inf)),
+                           np.nextafter(pts.astype(np.float32), np.float32(-np.inf))])
+    rnd = rng.uniform(0, lim, 20000).astype(np.float32)
+    tiny = np.array([0.0, 1e-45, 1e-38, 1e-20], dtype=np.float32)
+    big = np.array([1e10, 3e38, np.finfo(np.float32).max], dtype=np.float32)
+    v = np.concatenate([pts.astype(np.float32), near, rnd, tiny, big]).astype(np.float32)
+    v = v[v >= 0]
+    return np.concatenate([v, -v])
+
+
+@pytest.mark.parametrize("fmt,ref", [((2, 1), _textbook_e2m1), ((1, 2), _textbook_e1m2),
+                                     ((3, 0), _textbook_e3m0)])
+def test_quantize_matches_textbook_rounding(fmt, ref):
+    v = _interesting_values(80.0, np.random.default_rng(7))
+    codes = O.quantize(v, np.float32(1), O.minifloat(*fmt))
+    assert np.array_equal(codes & 7, ref(v))
+    assert np.array_equal(codes >> 3, np.signbit(v).astype(np.uint8))
+
+
+def test_e2m1_tie_table():
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
+    got = O.minifloat_grid(2, 1)[O.quantize(ties, 1, O.minifloat(2, 1)) & 7]
+    assert got.tolist() == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]
+
+
+def test_golden_tiny_example():
+    rows = _read_golden("e2m1_tiny.txt")
+    X, C, P = [], [], []
+    for r in rows:
+        a, b, c = r.split("|")
+        X.append([float(t) for t in a.split()])
+        C.append([int(t) for t in b.split()])
+        P.append([int(t, 16) for t in c.split()])
+    X = np.array(X, dtype=np.float32)
+    X[1, 0] = -0.0
+    packed, scales = O.quantize_pack(X, O.minifloat(2, 1), "tensor")
+    assert scales.tolist() == [1.0]
+    assert np.array_equal(O.unpack(packed), np.array(C))
+    assert np.array_equal(packed, np.array(P, dtype=np.uint8))
+
+
+def test_idempotence_dequant_quant():
+    rng = np.random.default_rng(3)
+    scales = np.concatenate([[1.0, 0.5, 3.0], rng.uniform(1e-6, 1e3, 40)]).astype(np.float32)
+    codes = np.arange(16, dtype=np.uint8)
+    for e, m in O.FORMATS_4BIT:
+        g = O.minifloat(e, m)
+        for s in scales:
+            v = (g.decode(codes).astype(np.float32) * s).astype(np.float32)
+            c2 = O.quantize(v, O.reciprocal(s), g)
+            assert np.array_equal(c2, codes), (e, m, s)
+    g = O.nf4()
+    for s in scales:
+        v = (g.decode(codes).astype(np.float32) * s).astype(np.float32)
+        assert np.array_equal(O.quantize(v, O.reciprocal(s), g), codes)
+
+
+def test_exhaustive_tiny_tensors_bruteforce():
+    """Every sign x 16 codes x random scales: quantize(+-g*s*(1+-eps)) stays on g."""
+    rng = np.random.default_rng(11)
+    for e, m in O.FORMATS_4BIT:
+        g = O.minifloat(e, m)
+        mags = g.array
+        for s in rng.uniform(0.01, 10, 20).astype(np.float32):
+            for sign in (1.0, -1.0):
+                v = (sign * mags * s * (1 + rng.uniform(-1e-3, 1e-3, mags.size))).astype(np.float32)
+                c = O.quantize(v, O.reciprocal(s), g)
+                assert np.array_equal(c & 7, np.arange(8))
+
+
+def test_zero_scale_gives_signed_zero_codes():
+    x = np.array([[0.0, -0.0, 0.0, -0.0]], dtype=np.float32)
+    packed, s = O.quantize_pack(x, O.minifloat(2, 1), "tensor")
+    assert s.tolist() == [0.0]
+    assert O.unpack(packed).tolist() == [[0, 8, 0, 8]]
+
+
+# ---------------------------------------------------------------- pack ----------
+def test_pack_layout_and_shape():
+    assert O.pack(np.array([[1, 2, 15, 0]], dtype=np.uint8)).tolist() == [[0x21, 0x0F]]
+    w, _ = __import__("synth").tiny()
+    packed, s = O.quantize_pack(w, O.minifloat(2, 1), "tensor")
+    assert packed.shape == (256, 128) and packed.dtype == np.uint8
+    c = np.random.default_rng(0).integers(0, 16, (5, 12)).astype(np.uint8)
+    assert np.array_equal(O.unpack(O.pack(c)), c)
+
+
+# ---------------------------------------------------------------- NF4 -----------
+def _inv_normal_bisect(p):
+    lo, hi = -10.0, 10.0
+    for _ in range(200):
+        mid = (lo + hi) / 2
+        if 0.5 * math.erfc(-mid / math.sqrt(2)) < p:
+            lo = mid
+        else:
+            hi = mid
+    return (lo + hi) / 2
+
+
+def test_nf4_table_construction():
+    G = O.nf4_table()
+    assert G.shape == (16,)
+    assert G[0] == -1.0 and G[-1] == 1.0
+    assert np.all(np.diff(G) > 0)
+    assert np.array_equal(G, -G[::-1])
+    assert np.array_equal(G.astype(np.float16).astype(np.float64), G)
+    z = _inv_normal_bisect(15.5 / 16)
+    for i in range(16):
+        q = _inv_normal_bisect((i + 0.5) / 16) / z
+        assert abs(q - G[i]) <= 2.0 ** -11 * max(abs(q), 2.0 ** -14), (i, q, G[i])
+
+
+def test_nf4_quantize_matches_searchsorted():
+    G = O.nf4_table()
+    mids = ((G[1:] + G[:-1]) / 2).astype(np.float32)
+    rng = np.random.default_rng(5)
+    y = np.concatenate([rng.uniform(-1.3, 1.3, 50000), mids, -mids]).astype(np.float32)
+    got = O.quantize(y, 1, O.nf4())
+    idx = np.searchsorted(mids.astype(np.float64), y.astype(np.float64), side="left")
+    at_mid = np.isin(y, mids)
+    # at an exact midpoint between i and i+1 the even index wins
+    idx = np.where(at_mid & (idx % 2 == 1), idx + 1, idx)
+    assert np.array_equal(got, idx)
+
+
+# ---------------------------------------------------------------- bf16 / f16 ----
+def test_bf16_rounding_matches_torch():
+    import torch
+    rng = np.random.default_rng(1)
+    v = rng.standard_normal(100000).astype(np.float32) * 100
+    ties = (np.arange(1, 200, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    v = np.concatenate([v, ties, -ties, [0.0, -0.0, 1e-40, 3e38]]).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.rne_bf16_bits(v), want)
+
+
+# ---------------------------------------------------------------- calibration ---
+def test_calibration_planted_maxima():
+    rng = np.random.default_rng(2)
+    x = rng.uniform(-1, 1, (300, 64)).astype(np.float32)
+    x[17, 5] = -9.5
+    assert O.amax_tensor(x) == np.float32(9.5)
+    cols = O.amax_columns(x, 128)
+    assert cols[5] == np.float32(9.5)
+    x2 = x.copy()
+    x2[200, 6] = 50.0  # outside the calibration rows
+    assert O.amax_columns(x2, 128)[6] == cols[6] < 1
+    rg = O.amax_row_groups(x, 16)
+    assert rg.shape == (300, 4) and rg[17, 0] == np.float32(9.5)
+    for i in range(0, 300, 37):
+        for j in range(4):
+            assert rg[i, j] == max(abs(float(t)) for t in x[i, 16 * j:16 * j + 16])
+
+
+# ---------------------------------------------------------------- pre-shift -----
+def _k_bruteforce(c, cmax):
+    out = []
+    for ck in c:
+        if ck == 0:
+            out.append(0)
+            continue
+        j = 1
+        while math.ldexp(float(cmax), j - 1) >= float(ck):
+            j -= 1
+        out.append(max(j, O.K_MIN))
+    return np.array(out)
+
+
+def test_preshift_k_bruteforce_and_range():
+    x = __import__("synth").activations(3, 9, 256, 512, outlier_frac=0.01)
+    c = O.amax_columns(x, 128)
+    c[3] = 0.0
+    c[4] = np.float32(c.max() / 2 ** 70)
+    k, a = O.preshift(c, O.minifloat(2, 1))
+    assert np.array_equal(k.astype(np.int64), _k_bruteforce(c, c.max()))
+    assert a == np.float32(c.max() / np.float32(6.0))
+    assert np.all(k <= 0) and k[4] == O.K_MIN
+    cmax = float(c.max())
+    for j in range(c.size):
+        if c[j] > 0 and k[j] > O.K_MIN:
+            assert math.ldexp(cmax, int(k[j])) >= c[j] > math.ldexp(cmax, int(k[j]) - 1)
+    # no calibrated value leaves the range after the shift
+    keep = np.ones(c.size, bool)
+    keep[[3, 4]] = False  # their maxima were overwritten above
+    shifted = np.ldexp(np.abs(x[:128]).astype(np.float64), -k.astype(np.int64)[None, :])
+    assert shifted[:, keep].max() <= cmax
+
+
+def test_preshift_invariance_bitwise():
+    x = __import__("synth").activations(3, 8, 64, 96, outlier_frac=0.05)
+    w = __import__("synth").weight(3, 8, 40, 96)
+    k, _ = O.preshift(O.amax_columns(x, 64), O.minifloat(2, 1))
+    xs = np.ldexp(x, -k.astype(np.int64)[None, :]).astype(np.float32)
+    ws = O.shift_weights(w, k)
+    lhs = (x[:, None, :] * w[None, :, :]).sum(axis=-1, dtype=np.float32)
+    rhs = (xs[:, None, :] * ws[None, :, :]).sum(axis=-1, dtype=np.float32)
+    assert np.array_equal(lhs, rhs)
+    assert (k != 0).any()
+
+
+def test_preshift_all_zero_k_reduces_to_per_tensor():
+    rng = np.random.default_rng(4)
+    x = rng.uniform(-1, 1, (64, 32)).astype(np.float32)
+    x[0, :] = np.linspace(0.6, 1.0, 32, dtype=np.float32)  # every channel max in (1/2, 1]
+    c = O.amax_columns(x, 64)
+    k, a = O.preshift(c, O.minifloat(2, 1))
+    assert not k.any()
+    p1, _ = O.quantize_activations(x, O.minifloat(2, 1), a, k)
+    p2, _ = O.quantize_pack(x, O.minifloat(2, 1), "tensor")
+    assert np.array_equal(p1, p2)
+
+
+# ---------------------------------------------------------------- search --------
+def test_clip_grid():
+    r = O.clip_ratios()
+    assert r.size == 100 and r[0] == np.float32(0.5) and r[-1] == np.float32(1.0)
+    assert np.all(np.diff(r) > 0)
+
+
+@pytest.mark.parametrize("fmt", O.FORMATS_4BIT)
+def test_search_planted_format(fmt):
+    """A tensor lying exactly on one format's grid (all magnitudes used, max at the
+    top grid point) is found with MSE 0 at clip ratio 1."""
+    g = O.minifloat(*fmt)
+    rng = np.random.default_rng(hash(fmt) % 1000)
+    s = np.float32(2.0 ** -6)  # a power of two, so amax / Qmax recovers s exactly
+    codes = np.concatenate([np.arange(8), rng.integers(0, 8, 500)])
+    w = (g.array[codes].astype(np.float32) * s).astype(np.float32)
+    w *= np.where(rng.random(w.size) < 0.5, -1, 1).astype(np.float32)
+    rec, packed, mse = O.search_tensor(w)
+    assert (rec.e, rec.m) == fmt and rec.clip_index == 99 and rec.mse == 0.0
+    assert rec.mse_runner_up > 0
+    assert np.array_equal(O.unpack(packed.reshape(1, -1)).reshape(-1) & 7, codes)
+
+
+def test_search_mse_exact_rational():
+    """Each candidate's MSE equals the exact rational mean of squared errors (rounded
+    once), with dequantized values from the textbook rounding routines."""
+    w = __import__("synth").heavy_tail_weight(4, 99, 3, 40)
+    w = w.reshape(-1)
+    amax = O.amax_tensor(w)
+    clips = (amax * O.clip_ratios(7)).astype(np.float32)
+    mse = O.candidate_mse(w, O.FORMATS_4BIT, clips)
+    refs = {(2, 1): _textbook_e2m1, (1, 2): _textbook_e1m2, (3, 0): _textbook_e3m0}
+    for f, fmt in enumerate(O.FORMATS_4BIT):
+        grid = O.minifloat_grid(*fmt)
+        for j, c in enumerate(clips):
+            s = np.float32(c / np.float32(grid[-1]))
+            r = np.float32(1) / s
+            y = (np.abs(w) * r).astype(np.float32)
+            deq = (grid[refs[fmt](y)].astype(np.float32) * s).astype(np.float32)
+            exact = sum((Fraction(float(abs(a))) - Fraction(float(d))) ** 2 for a, d in zip(w, deq))
+            assert mse[f, j] == float(exact / w.size), (fmt, j)
+
+
+def test_search_picks_minimum_earliest():
+    w = __import__("synth").heavy_tail_weight(4, 98, 16, 64)
+    rec, packed, mse = O.search_tensor(w)
+    flat = mse.reshape(-1)
+    best = min(range(flat.size), key=lambda i: (flat[i], i))
+    assert (O.FORMATS_4BIT.index((rec.e, rec.m)), rec.clip_index) == divmod(best, 100)
+    assert rec.mse == flat[best] and rec.mse_runner_up == np.sort(flat)[1]
+    g = O.minifloat(rec.e, rec.m)
+    assert rec.scale == np.float32(rec.clip / np.float32(g.qmax))
+    assert rec.bias == 1 - math.log2(float(rec.scale))
+
+
+# ---------------------------------------------------------------- GEMMs ---------
+def _exact_gemm_grouped(X, V, S, group):
+    M, K = X.shape
+    N = V.shape[0]
+    out = np.zeros((M, N))
+    for i in range(M):
+        for n in range(N):
+            tot = Fraction(0)
+            for g0 in range(0, K, group):
+                part = sum(Fraction(float(X[i, k])) * Fraction(float(V[n, k]))
+                           for k in range(g0, g0 + group))
+                tot += Fraction(float(S[n, g0 // group])) * part
+            out[i, n] = float(tot)
+    return out
+
+
+def test_w4a16_group_gemm_exact_rational():
+    rng = np.random.default_rng(9)
+    w = rng.normal(0, 0.02, (5, 16)).astype(np.float32)
+    x = __import__("synth").to_bf16_values(rng.normal(0, 1, (3, 16)).astype(np.float32))
+    g = O.minifloat(2, 1)
+    packed, s16 = O.quantize_pack(w, g, "group", group=8, scale_dtype="f16")
+    r = O.gemm_w4a16(x, packed, g, "group", s16, group=8)
+    V = g.decode(O.unpack(packed))
+    ref = _exact_gemm_grouped(x, V, s16.astype(np.float64), 8)
+    assert np.max(np.abs(r - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_w4a4_factoring_identity_integer():
+    """W4A4 E2M1 = (integer code product) x scales, exactly: twice every E2M1 value is
+    an integer, so the code GEMM is an int64 matmul divided by 4."""
+    rng = np.random.default_rng(10)
+    g = O.minifloat(2, 1)
+    A = rng.integers(0, 16, (7, 64)).astype(np.uint8)
+    W = rng.integers(0, 16, (9, 64)).astype(np.uint8)
+    s = rng.uniform(0.001, 0.01, 9).astype(np.float32)
+    a = np.float32(0.37)
+    r, acc = O.gemm_w4a4(O.pack(A), g, a, O.pack(W), g, "row", s)
+    Ai = (g.decode(A) * 2).astype(np.int64)
+    Wi = (g.decode(W) * 2).astype(np.int64)
+    assert np.array_equal(acc * 4, (Ai @ Wi.T).astype(np.float64))
+    y = O.w4a4_epilogue_f32(acc, a, s)
+    for i in range(7):
+        for n in range(9):
+            assert y[i, n] == np.float32(np.float32(acc[i, n]) * np.float32(a * s[n]))
+
+
+def test_nf4_gemm_exact_rational():
+    rng = np.random.default_rng(12)
+    g4 = O.nf4()
+    ge = O.minifloat(2, 1)
+    A = rng.integers(0, 16, (2, 16)).astype(np.uint8)
+    W = rng.normal(0, 0.02, (3, 16)).astype(np.float32)
+    pw, sw = O.quantize_pack(W, g4, "group", group=8)
+    a = np.float32(0.11)
+    r, _ = O.gemm_w4a4(O.pack(A), ge, a, pw, g4, "group", sw, group=8)
+    ref = _exact_gemm_grouped(ge.decode(A), g4.decode(O.unpack(pw)), sw.astype(np.float64), 8)
+    assert np.max(np.abs(r - ref * float(a))) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_rel_err_definition():
+    assert O.rel_err(np.array([1.0, 2.0]), np.array([1.0, 2.002])) == pytest.approx(0.002 / 2.002)
