@@ -1,0 +1,339 @@
+// Host layer of libfp4: argument validation (before any launch), grid tables, and
+// dispatch to the HIP kernels.  Every entry point of include/fp4.h is defined here.
+#include <hip/hip_runtime.h>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fp4.h"
+#include "fp4_internal.h"
+
+using namespace fp4;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fp4_status fail(fp4_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+fp4_status ok() {
+    g_err[0] = 0;
+    return FP4_OK;
+}
+
+fp4_status hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(FP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// value of minifloat magnitude code c (canonical bias 1): p == 0 subnormal d/2^m,
+// p >= 1 normal 2^(p-1) (1 + d/2^m)
+double minifloat_value(int m, int c) {
+    int p = c >> m, d = c & ((1 << m) - 1);
+    if (p == 0) return std::ldexp((double)d, -m);
+    return std::ldexp(1.0 + std::ldexp((double)d, -m), p - 1);
+}
+
+bool f16_exact(float v) {
+    _Float16 h = (_Float16)v;
+    return (float)h == v;
+}
+
+fp4_status make_grid(const fp4_grid& g, QGrid* q) {
+    std::memset(q, 0, sizeof(*q));
+    if (g.reserved != 0) return fail(FP4_ERR_INVALID_ARG, "fp4_grid.reserved must be 0");
+    if (g.kind == FP4_GRID_MINIFLOAT) {
+        if (g.e < 1 || g.m < 0 || g.e + g.m != 3)
+            return fail(FP4_ERR_UNSUPPORTED, "minifloat grid needs e >= 1 and e + m == 3 (got e=%d m=%d)", g.e, g.m);
+        q->kind = 0;
+        q->e = g.e;
+        q->m = g.m;
+        q->is_e2m1 = (g.e == 2 && g.m == 1);
+        for (int c = 0; c < 8; c++) q->val[c] = (float)minifloat_value(g.m, c);
+        for (int i = 0; i < 7; i++) q->thr[i] = (float)((minifloat_value(g.m, i) + minifloat_value(g.m, i + 1)) / 2);
+        q->qmax = q->val[7];
+        return FP4_OK;
+    }
+    if (g.kind == FP4_GRID_LUT16) {
+        for (int i = 0; i < 16; i++) {
+            if (!std::isfinite(g.lut[i]) || !f16_exact(g.lut[i]))
+                return fail(FP4_ERR_INVALID_ARG, "lut[%d] must be finite and exact in binary16", i);
+            if (i > 0 && !(g.lut[i] > g.lut[i - 1])) return fail(FP4_ERR_INVALID_ARG, "lut must be strictly increasing");
+        }
+        q->kind = 1;
+        for (int i = 0; i < 16; i++) q->val[i] = g.lut[i];
+        for (int i = 0; i < 15; i++) q->thr[i] = (float)(((double)g.lut[i] + (double)g.lut[i + 1]) / 2);
+        q->qmax = std::fmax(std::fabs(g.lut[0]), std::fabs(g.lut[15]));
+        if (!(q->qmax > 0)) return fail(FP4_ERR_INVALID_ARG, "lut has no nonzero value");
+        return FP4_OK;
+    }
+    return fail(FP4_ERR_INVALID_ARG, "unknown grid kind %d", g.kind);
+}
+
+fp4_status check_gran(const fp4_gran& g, int64_t cols) {
+    if (g.reserved != 0) return fail(FP4_ERR_INVALID_ARG, "fp4_gran.reserved must be 0");
+    if (g.mode < FP4_SCALE_TENSOR || g.mode > FP4_SCALE_GROUP) return fail(FP4_ERR_INVALID_ARG, "bad scale mode %d", g.mode);
+    if (g.scale_dtype != FP4_F32 && g.scale_dtype != FP4_F16)
+        return fail(FP4_ERR_INVALID_ARG, "scale dtype must be FP4_F32 or FP4_F16");
+    if (g.mode == FP4_SCALE_TENSOR && g.scale_dtype != FP4_F32)
+        return fail(FP4_ERR_UNSUPPORTED, "per-tensor scales are f32 only");
+    if (g.mode == FP4_SCALE_GROUP) {
+        if (!is_pow2(g.group) || g.group < 8 || g.group > 512)
+            return fail(FP4_ERR_UNSUPPORTED, "group must be a power of two in [8, 512] (got %d)", g.group);
+        if (cols % g.group != 0) return fail(FP4_ERR_INVALID_ARG, "cols (%lld) must be a multiple of group %d",
+                                             (long long)cols, g.group);
+    }
+    return FP4_OK;
+}
+
+int64_t units_of(const fp4_gran& g, int64_t rows, int64_t cols) {
+    return g.mode == FP4_SCALE_TENSOR ? 1 : (g.mode == FP4_SCALE_ROW ? rows : rows * (cols / g.group));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp4_status_string(fp4_status s) {
+    switch (s) {
+        case FP4_OK: return "FP4_OK";
+        case FP4_ERR_INVALID_ARG: return "FP4_ERR_INVALID_ARG";
+        case FP4_ERR_UNSUPPORTED: return "FP4_ERR_UNSUPPORTED";
+        case FP4_ERR_ALIGNMENT: return "FP4_ERR_ALIGNMENT";
+        case FP4_ERR_WORKSPACE: return "FP4_ERR_WORKSPACE";
+        case FP4_ERR_HIP: return "FP4_ERR_HIP";
+        default: return "FP4_ERR_UNKNOWN";
+    }
+}
+
+const char* fp4_last_error(void) { return g_err; }
+
+fp4_status fp4_calibrate(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld, int32_t reduce,
+                         int32_t group, int64_t first_rows, float* amax_out, void* stream) {
+    if (!x || !amax_out) return fail(FP4_ERR_INVALID_ARG, "null pointer");
+    if (x_dtype != FP4_F32 && x_dtype != FP4_BF16) return fail(FP4_ERR_INVALID_ARG, "x_dtype must be FP4_F32 or FP4_BF16");
+    if (rows < 0 || cols < 0 || ld < cols) return fail(FP4_ERR_INVALID_ARG, "bad sizes rows=%lld cols=%lld ld=%lld",
+                                                       (long long)rows, (long long)cols, (long long)ld);
+    if (reduce < FP4_REDUCE_TENSOR || reduce > FP4_REDUCE_ROW_GROUP) return fail(FP4_ERR_INVALID_ARG, "bad reduce %d", reduce);
+    if (reduce == FP4_REDUCE_ROW_GROUP) {
+        if (!is_pow2(group) || group < 8 || group > 512) return fail(FP4_ERR_UNSUPPORTED, "group must be a power of two in [8, 512]");
+        if (cols % group) return fail(FP4_ERR_INVALID_ARG, "cols must be a multiple of group");
+    }
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(amax_out) & 3u))
+        return fail(FP4_ERR_ALIGNMENT, "x must be 16-byte aligned and amax_out 4-byte aligned");
+    int64_t r = (first_rows > 0 && first_rows < rows) ? first_rows : rows;
+    int esz = x_dtype == FP4_BF16 ? 2 : 4;
+    int vec = ((ld * esz) % 16 == 0) && (cols % 8 == 0);
+    return hip_status(launch_calibrate(x, x_dtype == FP4_BF16, r, cols, ld, reduce, group, amax_out, vec,
+                                       (hipStream_t)stream),
+                      "fp4_calibrate");
+}
+
+fp4_status fp4_quantize_pack(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx, fp4_grid grid,
+                             fp4_gran gran, const float* amax_in, const float* tensor_scale, const int8_t* col_shift,
+                             uint8_t* packed, int64_t ldp, void* scales_out, void* stream) {
+    if (!x || !packed) return fail(FP4_ERR_INVALID_ARG, "null pointer");
+    if (x_dtype != FP4_F32 && x_dtype != FP4_BF16) return fail(FP4_ERR_INVALID_ARG, "x_dtype must be FP4_F32 or FP4_BF16");
+    if (rows < 0 || cols < 0 || (cols & 1) || ldx < cols || ldp < cols / 2)
+        return fail(FP4_ERR_INVALID_ARG, "bad sizes (cols must be even, ldx >= cols, ldp >= cols/2)");
+    QGrid q;
+    fp4_status st = make_grid(grid, &q);
+    if (st) return st;
+    if ((st = check_gran(gran, cols))) return st;
+    if (tensor_scale && gran.mode != FP4_SCALE_TENSOR) return fail(FP4_ERR_INVALID_ARG, "tensor_scale needs TENSOR mode");
+    if (!scales_out && !tensor_scale) return fail(FP4_ERR_INVALID_ARG, "scales_out may be NULL only with tensor_scale");
+    if (tensor_scale && scales_out && (const void*)tensor_scale == scales_out)
+        return fail(FP4_ERR_INVALID_ARG, "tensor_scale and scales_out must not alias");
+    if (!aligned16(x) || !aligned16(packed)) return fail(FP4_ERR_ALIGNMENT, "x and packed must be 16-byte aligned");
+    int esz = x_dtype == FP4_BF16 ? 2 : 4;
+    QuantParams p{};
+    p.x = x;
+    p.ldx = ldx;
+    p.x_bf16 = x_dtype == FP4_BF16;
+    p.mode = gran.mode;
+    p.rows = rows;
+    p.cols = cols;
+    p.packed = packed;
+    p.ldp = ldp;
+    p.group = gran.mode == FP4_SCALE_GROUP ? gran.group : 0;
+    p.scale_f16 = gran.scale_dtype == FP4_F16;
+    p.amax_in = amax_in;
+    p.tensor_scale = tensor_scale;
+    p.scales_out = scales_out;
+    p.col_shift = col_shift;
+    p.shift_sign = -1;
+    p.vec = ((ldx * esz) % 16 == 0) && (cols % 8 == 0) && (ldp % 4 == 0);
+    p.g = q;
+    hipStream_t s = (hipStream_t)stream;
+    if (gran.mode == FP4_SCALE_TENSOR && !tensor_scale) {
+        // per-tensor scale from the amax: reduce into scales_out (as scratch), quantize
+        // reading that amax, then overwrite it with s = amax / Qmax
+        float* sc = reinterpret_cast<float*>(scales_out);
+        if (amax_in) {
+            p.tensor_amax = amax_in;
+        } else {
+            hipError_t e = launch_calibrate(x, p.x_bf16, rows, cols, ldx, FP4_REDUCE_TENSOR, 0, sc, p.vec, s);
+            if (e != hipSuccess) return hip_status(e, "fp4_quantize_pack/amax");
+            p.tensor_amax = sc;
+        }
+        hipError_t e = launch_quantize(p, s);
+        if (e != hipSuccess) return hip_status(e, "fp4_quantize_pack");
+        return hip_status(launch_tensor_scale_finalize(p.tensor_amax, sc, q.qmax, s), "fp4_quantize_pack/scale");
+    }
+    return hip_status(launch_quantize(p, s), "fp4_quantize_pack");
+}
+
+fp4_status fp4_dequantize(const uint8_t* packed, int64_t rows, int64_t cols, int64_t ldp, fp4_grid grid, fp4_gran gran,
+                          const void* scales, const int8_t* col_shift, float* out, int64_t ldo, void* stream) {
+    if (!packed || !scales || !out) return fail(FP4_ERR_INVALID_ARG, "null pointer");
+    if (rows < 0 || cols < 0 || (cols & 1) || ldp < cols / 2 || ldo < cols) return fail(FP4_ERR_INVALID_ARG, "bad sizes");
+    QGrid q;
+    fp4_status st = make_grid(grid, &q);
+    if (st) return st;
+    if ((st = check_gran(gran, cols))) return st;
+    return hip_status(launch_dequantize(packed, rows, cols, ldp, q, gran.mode, gran.group, scales,
+                                        gran.scale_dtype == FP4_F16, col_shift, out, ldo, (hipStream_t)stream),
+                      "fp4_dequantize");
+}
+
+fp4_status fp4_preshift_weights(const float* w, int64_t n, int64_t k, int64_t ldw, const float* chan_amax,
+                                fp4_grid act_grid, fp4_grid w_grid, fp4_gran w_gran, int8_t* shift_out,
+                                float* act_scale_out, uint8_t* w_packed, int64_t ldp, void* w_scales, void* stream) {
+    if (!w || !chan_amax || !shift_out || !act_scale_out || !w_packed || !w_scales)
+        return fail(FP4_ERR_INVALID_ARG, "null pointer");
+    if (n < 0 || k <= 0 || (k & 1) || ldw < k || ldp < k / 2) return fail(FP4_ERR_INVALID_ARG, "bad sizes");
+    QGrid qa, qw;
+    fp4_status st = make_grid(act_grid, &qa);
+    if (st) return st;
+    if ((st = make_grid(w_grid, &qw))) return st;
+    if ((st = check_gran(w_gran, k))) return st;
+    if (w_gran.mode == FP4_SCALE_TENSOR) return fail(FP4_ERR_UNSUPPORTED, "pre-shifted weights need ROW or GROUP scales");
+    if (!aligned16(w) || !aligned16(w_packed)) return fail(FP4_ERR_ALIGNMENT, "w and w_packed must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_preshift_factors(chan_amax, k, qa.qmax, shift_out, act_scale_out, s);
+    if (e != hipSuccess) return hip_status(e, "fp4_preshift_weights/factors");
+    QuantParams p{};
+    p.x = w;
+    p.ldx = ldw;
+    p.x_bf16 = 0;
+    p.mode = w_gran.mode;
+    p.rows = n;
+    p.cols = k;
+    p.packed = w_packed;
+    p.ldp = ldp;
+    p.group = w_gran.mode == FP4_SCALE_GROUP ? w_gran.group : 0;
+    p.scale_f16 = w_gran.scale_dtype == FP4_F16;
+    p.scales_out = w_scales;
+    p.col_shift = shift_out;
+    p.shift_sign = +1;
+    p.vec = ((ldw * 4) % 16 == 0) && (k % 8 == 0) && (ldp % 4 == 0);
+    p.g = qw;
+    return hip_status(launch_quantize(p, s), "fp4_preshift_weights/quantize");
+}
+
+size_t fp4_search_workspace_size(int64_t ntensors, int64_t numel, int32_t nformats, int32_t nclips) {
+    if (ntensors < 0 || numel < 0 || nformats < 1 || nclips < 1) return 0;
+    return search_workspace_bytes(ntensors, numel, nformats, nclips);
+}
+
+fp4_status fp4_search_format(const float* w, int64_t ntensors, int64_t numel, const int32_t* formats_em,
+                             int32_t nformats, int32_t nclips, float clip_lo, float clip_hi,
+                             fp4_search_result* results, uint8_t* packed, void* workspace, size_t ws_bytes,
+                             void* stream) {
+    if (!w || !formats_em || !results || !packed) return fail(FP4_ERR_INVALID_ARG, "null pointer");
+    if (ntensors < 0 || numel <= 0 || numel % 16 != 0)
+        return fail(FP4_ERR_INVALID_ARG, "numel must be a positive multiple of 16");
+    if (nformats < 1 || nformats > 8 || nclips < 2 || (int64_t)nformats * nclips > 512)
+        return fail(FP4_ERR_UNSUPPORTED, "need 1..8 formats, >= 2 clips, at most 512 candidates");
+    if (!(clip_lo > 0.0f) || !(clip_hi >= clip_lo) || !(clip_hi <= 1.0f))
+        return fail(FP4_ERR_INVALID_ARG, "need 0 < clip_lo <= clip_hi <= 1");
+    SearchCandidates c{};
+    c.nformats = nformats;
+    c.nclips = nclips;
+    for (int f = 0; f < nformats; f++) {
+        int e = formats_em[2 * f], m = formats_em[2 * f + 1];
+        if (e < 1 || m < 0 || e + m != 3) return fail(FP4_ERR_UNSUPPORTED, "format %d: need e >= 1 and e + m == 3", f);
+        c.fmt_e[f] = e;
+        c.fmt_m[f] = m;
+        c.fmt_qmax[f] = (float)minifloat_value(m, 7);
+    }
+    if (!aligned16(w) || !aligned16(packed) || !aligned16(results))
+        return fail(FP4_ERR_ALIGNMENT, "w, packed and results must be 16-byte aligned");
+    size_t need = search_workspace_bytes(ntensors, numel, nformats, nclips);
+    if (!workspace || ws_bytes < need)
+        return fail(FP4_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+    if (!aligned16(workspace)) return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+    return hip_status(launch_search(w, ntensors, numel, c, (double)clip_lo, (double)clip_hi, results, packed, workspace,
+                                    (hipStream_t)stream),
+                      "fp4_search_format");
+}
+
+fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
+    if (!d) return fail(FP4_ERR_INVALID_ARG, "null descriptor");
+    if (!d->a || !d->w || !d->w_scales || !d->y) return fail(FP4_ERR_INVALID_ARG, "null pointer");
+    if (d->M < 0 || d->N < 0 || d->K <= 0 || (d->K & 1)) return fail(FP4_ERR_INVALID_ARG, "bad sizes");
+    if (d->ldw < d->K / 2 || d->ldy < d->N) return fail(FP4_ERR_INVALID_ARG, "bad leading dimensions");
+    if (d->y_dtype != FP4_BF16 && d->y_dtype != FP4_F32) return fail(FP4_ERR_INVALID_ARG, "y_dtype must be BF16 or F32");
+    if (d->reserved0 || d->reserved1) return fail(FP4_ERR_INVALID_ARG, "reserved fields must be 0");
+    GemmParams p{};
+    fp4_status st = make_grid(d->w_grid, &p.wg);
+    if (st) return st;
+    if ((st = check_gran(d->w_gran, d->K))) return st;
+    p.M = d->M;
+    p.N = d->N;
+    p.K = d->K;
+    p.a_kind = d->a_kind;
+    p.a = d->a;
+    p.lda = d->lda;
+    p.a_scale = d->a_scale;
+    p.w = d->w;
+    p.ldw = d->ldw;
+    p.w_mode = d->w_gran.mode;
+    p.w_group = d->w_gran.mode == FP4_SCALE_GROUP ? d->w_gran.group : 0;
+    p.w_scale_f16 = d->w_gran.scale_dtype == FP4_F16;
+    p.w_scales = d->w_scales;
+    p.y = d->y;
+    p.ldy = d->ldy;
+    p.y_bf16 = d->y_dtype == FP4_BF16;
+    hipStream_t s = (hipStream_t)stream;
+    if (!aligned16(d->a) || !aligned16(d->w) || (d->ldw % 16) != 0)
+        return fail(FP4_ERR_ALIGNMENT, "a and w must be 16-byte aligned and ldw a multiple of 16");
+
+    if (d->a_kind == FP4_F32 || d->a_kind == FP4_BF16) {
+        if (d->lda < d->K) return fail(FP4_ERR_INVALID_ARG, "lda < K");
+        bool mfma = d->a_kind == FP4_BF16 && p.wg.is_e2m1 && d->K % 128 == 0 && (d->lda * 2) % 16 == 0 &&
+                    (d->w_gran.mode != FP4_SCALE_GROUP || d->w_gran.group % 128 == 0);
+        if (mfma) return hip_status(launch_w4a16_mfma(p, s), "fp4_gemm/w4a16");
+        return hip_status(launch_w4a16_valu(p, s), "fp4_gemm/w4a16_valu");
+    }
+    if (d->a_kind != FP4_PACKED) return fail(FP4_ERR_INVALID_ARG, "a_kind must be F32, BF16 or PACKED");
+    if (!d->a_scale) return fail(FP4_ERR_INVALID_ARG, "packed activations need a_scale");
+    if (d->lda < d->K / 2 || d->lda % 16 != 0) return fail(FP4_ERR_ALIGNMENT, "packed lda must be >= K/2 and a multiple of 16");
+    if ((st = make_grid(d->a_grid, &p.ag))) return st;
+    if (!p.ag.is_e2m1) return fail(FP4_ERR_UNSUPPORTED, "packed activations must be E2M1");
+    if (d->K % 32 != 0) return fail(FP4_ERR_UNSUPPORTED, "K must be a multiple of 32");
+    if (p.wg.is_e2m1) {
+        if (d->w_gran.mode == FP4_SCALE_GROUP || d->w_gran.scale_dtype != FP4_F32)
+            return fail(FP4_ERR_UNSUPPORTED, "E2M1 x E2M1 needs f32 TENSOR or ROW weight scales");
+        return hip_status(launch_w4a4_fp4(p, s), "fp4_gemm/w4a4");
+    }
+    if (p.wg.kind == 1) {
+        if (d->w_gran.mode != FP4_SCALE_GROUP || d->w_gran.group % 64 != 0 || d->K % 64 != 0)
+            return fail(FP4_ERR_UNSUPPORTED, "lookup-grid weights need GROUP scales with group a multiple of 64");
+        return hip_status(launch_w4a4_lut(p, s), "fp4_gemm/w4a4_lut");
+    }
+    return fail(FP4_ERR_UNSUPPORTED, "W4A4 with minifloat weights other than E2M1 is not implemented");
+}
+
+}  // extern "C"

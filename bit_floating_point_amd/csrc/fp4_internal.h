@@ -1,0 +1,94 @@
+// Internal declarations shared by the host layer (fp4_api.cpp) and the HIP kernels.
+// Nothing here is part of the public ABI (include/fp4.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4 {
+
+// A 4-bit grid as the kernels see it.  Codes come from a compare ladder against the
+// midpoints between neighbouring grid values ([FP4-LLM] "compare and quantize",
+// eq. (5)): code = number of midpoints below y, where a value exactly on the
+// midpoint between codes i-1 and i counts for the even one of the two.
+//   kind 0 (minifloat, sign-magnitude): val[0..7] magnitudes, thr[0..6] midpoints,
+//          applied to |y|; the sign bit of y becomes bit 3.
+//   kind 1 (LUT16, signed):             val[0..15], thr[0..14], applied to y.
+struct QGrid {
+    int32_t kind;
+    int32_t e, m;
+    int32_t is_e2m1;   // minifloat E2M1: the gfx950 FP4 converts apply
+    float qmax;        // largest magnitude
+    float val[16];
+    float thr[15];
+};
+
+struct QuantParams {
+    const void* x;
+    int64_t ldx;           // elements
+    int32_t x_bf16;
+    int32_t mode;          // 0 tensor, 1 row, 2 group
+    int64_t rows, cols;
+    uint8_t* packed;
+    int64_t ldp;           // bytes
+    int32_t group;
+    int32_t scale_f16;
+    const float* amax_in;        // per scale unit, or null
+    const float* tensor_scale;   // tensor mode: fixed scale s, or null
+    const float* tensor_amax;    // tensor mode: amax (when tensor_scale is null)
+    void* scales_out;            // per unit (f32/f16), may be null in tensor mode
+    const int8_t* col_shift;     // or null
+    int32_t shift_sign;          // -1: multiplier r * 2^-k ; +1: input x * 2^k
+    int32_t vec;                 // 16-byte vector path allowed
+    QGrid g;
+};
+
+hipError_t launch_fill_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
+hipError_t launch_calibrate(const void* x, int x_bf16, int64_t rows, int64_t cols,
+                            int64_t ld, int reduce, int group, float* out, int vec,
+                            hipStream_t s);
+hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
+hipError_t launch_tensor_scale_finalize(const float* amax, float* scales_out, float qmax, hipStream_t s);
+hipError_t launch_dequantize(const uint8_t* packed, int64_t rows, int64_t cols, int64_t ldp,
+                             const QGrid& g, int mode, int group, const void* scales,
+                             int scale_f16, const int8_t* col_shift, float* out,
+                             int64_t ldo, hipStream_t s);
+hipError_t launch_preshift_factors(const float* chan_amax, int64_t k, float act_qmax,
+                                   int8_t* shift_out, float* act_scale_out, hipStream_t s);
+
+// quantized GEMMs (Y = X W^T)
+struct GemmParams {
+    int64_t M, N, K;
+    int32_t a_kind;       // 0 f32, 1 bf16, 3 packed
+    const void* a;
+    int64_t lda;
+    QGrid ag;
+    const float* a_scale;
+    const uint8_t* w;
+    int64_t ldw;
+    QGrid wg;
+    int32_t w_mode;       // 0 tensor, 1 row, 2 group
+    int32_t w_group;
+    int32_t w_scale_f16;
+    const void* w_scales;
+    void* y;
+    int64_t ldy;
+    int32_t y_bf16;
+};
+hipError_t launch_w4a16_mfma(const GemmParams& p, hipStream_t s);
+hipError_t launch_w4a16_valu(const GemmParams& p, hipStream_t s);
+hipError_t launch_w4a4_fp4(const GemmParams& p, hipStream_t s);
+hipError_t launch_w4a4_lut(const GemmParams& p, hipStream_t s);
+
+// format search
+struct SearchCandidates {
+    int32_t nformats, nclips;
+    int32_t fmt_e[8], fmt_m[8];
+    float fmt_qmax[8];
+};
+size_t search_workspace_bytes(int64_t ntensors, int64_t numel, int32_t nformats,
+                              int32_t nclips);
+hipError_t launch_search(const float* w, int64_t ntensors, int64_t numel,
+                         const SearchCandidates& c, double clip_lo, double clip_hi,
+                         void* results, uint8_t* packed, void* ws, hipStream_t s);
+
+}  // namespace fp4

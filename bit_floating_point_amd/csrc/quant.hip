@@ -1,0 +1,329 @@
+// Calibration, quantize + pack, dequantize and the pre-shift factors for gfx950.
+//
+// Method ([FP4-LLM] = "首个支持4-bit浮点量化的LLM来了" page, 811yy.cn):
+//   scale and clip (eqs. (2)-(3)): s = amax / Qmax, y = x * (1/s) clipped to +-Qmax;
+//   compare and quantize (eq. (5)): nearest grid point, ties to the even code;
+//   pre-shifted exponent bias: per-channel maxima -> per-tensor a times 2^k.
+// Two 4-bit codes per byte ("为什么我们需要4-bit浮点量化" page, section 2.2).
+//
+// Memory path: every thread owns 8 consecutive elements of a row (one 16-byte load
+// for bf16, two for f32) and writes their 4 packed bytes with one 32-bit store, so a
+// wavefront moves 1-2 KiB per load instruction, fully coalesced.  Scale reductions
+// are lane shuffles inside the wavefront (group <= 512) or an LDS reduction over the
+// workgroup (per-row scales).  HBM-bound: no LDS staging, no re-read except the second
+// pass over one row in per-row mode (L2-resident).
+#include "fp4_device.h"
+
+namespace fp4 {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = kThreads * 8;  // elements of a row per workgroup pass
+
+__global__ void fill_zero_u32_kernel(uint32_t* p, int64_t n) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_fill_zero_u32(uint32_t* p, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(fill_zero_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ calibrate ----
+// TENSOR: one workgroup per (row, 2048-column chunk); wave max -> atomicMax on the
+// float bit pattern (|x| >= 0, so unsigned order equals float order; max is exact and
+// order-free, so the result does not depend on the launch geometry).
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads) amax_tensor_kernel(const void* x, int x_bf16, int64_t cols,
+                                                               int64_t ld, int64_t chunks, float* out) {
+    int64_t b = blockIdx.x;
+    int64_t row = b / chunks;
+    int64_t col = (b % chunks) * kChunk + threadIdx.x * 8;
+    const char* rp = reinterpret_cast<const char*>(x) + row * ld * (x_bf16 ? 2 : 4);
+    float v[8];
+    load8<VEC>(rp, x_bf16, col, cols, v);
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+}
+
+// COLUMN: per-column max over the first `rows` rows.  A thread owns 8 columns and a
+// strip of 32 rows; one atomicMax per column per strip.
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads) amax_column_kernel(const void* x, int x_bf16, int64_t rows,
+                                                               int64_t cols, int64_t ld, float* out) {
+    int64_t col = (int64_t)blockIdx.x * kChunk + threadIdx.x * 8;
+    int64_t r0 = (int64_t)blockIdx.y * 32;
+    int64_t r1 = r0 + 32 < rows ? r0 + 32 : rows;
+    if (col >= cols) return;
+    float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int64_t r = r0; r < r1; r++) {
+        const char* rp = reinterpret_cast<const char*>(x) + r * ld * (x_bf16 ? 2 : 4);
+        float v[8];
+        load8<VEC>(rp, x_bf16, col, cols, v);
+#pragma unroll
+        for (int i = 0; i < 8; i++) m[i] = fmaxf(m[i], fabsf(v[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        if (col + i < cols) atomicMax(reinterpret_cast<unsigned int*>(out) + col + i, __float_as_uint(m[i]));
+}
+
+// ROW_GROUP: per (row, group) max; a group spans group/8 aligned lanes.
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads) amax_rowgroup_kernel(const void* x, int x_bf16, int64_t cols,
+                                                                 int64_t ld, int64_t chunks, int group,
+                                                                 float* out) {
+    int64_t b = blockIdx.x;
+    int64_t row = b / chunks;
+    int64_t col = (b % chunks) * kChunk + threadIdx.x * 8;
+    const char* rp = reinterpret_cast<const char*>(x) + row * ld * (x_bf16 ? 2 : 4);
+    float v[8];
+    load8<VEC>(rp, x_bf16, col, cols, v);
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
+    int lanes = group >> 3;
+    m = group_max(m, lanes);
+    if (col < cols && ((threadIdx.x & (lanes - 1)) == 0)) out[row * (cols / group) + col / group] = m;
+}
+
+hipError_t launch_calibrate(const void* x, int x_bf16, int64_t rows, int64_t cols, int64_t ld,
+                            int reduce, int group, float* out, int vec, hipStream_t s) {
+    int64_t chunks = (cols + kChunk - 1) / kChunk;
+    if (reduce == 0) {
+        hipError_t e = launch_fill_zero_u32(reinterpret_cast<uint32_t*>(out), 1, s);
+        if (e != hipSuccess) return e;
+        if (rows == 0 || cols == 0) return hipSuccess;
+        if (vec) hipLaunchKernelGGL(amax_tensor_kernel<true>, dim3((unsigned)(rows * chunks)), dim3(kThreads), 0, s,
+                                    x, x_bf16, cols, ld, chunks, out);
+        else hipLaunchKernelGGL(amax_tensor_kernel<false>, dim3((unsigned)(rows * chunks)), dim3(kThreads), 0, s,
+                                x, x_bf16, cols, ld, chunks, out);
+    } else if (reduce == 1) {
+        hipError_t e = launch_fill_zero_u32(reinterpret_cast<uint32_t*>(out), cols, s);
+        if (e != hipSuccess) return e;
+        if (rows == 0 || cols == 0) return hipSuccess;
+        dim3 grid((unsigned)chunks, (unsigned)((rows + 31) / 32));
+        if (vec) hipLaunchKernelGGL(amax_column_kernel<true>, grid, dim3(kThreads), 0, s, x, x_bf16, rows, cols, ld, out);
+        else hipLaunchKernelGGL(amax_column_kernel<false>, grid, dim3(kThreads), 0, s, x, x_bf16, rows, cols, ld, out);
+    } else {
+        if (rows == 0 || cols == 0) return hipSuccess;
+        if (vec) hipLaunchKernelGGL(amax_rowgroup_kernel<true>, dim3((unsigned)(rows * chunks)), dim3(kThreads), 0, s,
+                                    x, x_bf16, cols, ld, chunks, group, out);
+        else hipLaunchKernelGGL(amax_rowgroup_kernel<false>, dim3((unsigned)(rows * chunks)), dim3(kThreads), 0, s,
+                                x, x_bf16, cols, ld, chunks, group, out);
+    }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ quantize -----
+__device__ __forceinline__ void store_codes(uint8_t* prow, int64_t col, int64_t cols, uint32_t w, bool vec) {
+    if (vec && col + 8 <= cols) {
+        *reinterpret_cast<uint32_t*>(prow + col / 2) = w;
+    } else {
+        for (int j = 0; j < 4; j++)
+            if (col + 2 * j < cols) prow[col / 2 + j] = (uint8_t)(w >> (8 * j));
+    }
+}
+
+// Apply the optional column shift and the multiplier, producing y = fl32(x * r).
+__device__ __forceinline__ void shift_inputs(const QuantParams& p, int64_t col, float v[8]) {
+    if (p.col_shift && p.shift_sign > 0) {
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            if (col + i < p.cols) v[i] = ldexpf(v[i], (int)p.col_shift[col + i]);
+    }
+}
+
+__device__ __forceinline__ void scale_values(const QuantParams& p, int64_t col, float r, float v[8]) {
+    if (p.col_shift && p.shift_sign < 0) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            int k = (col + i < p.cols) ? (int)p.col_shift[col + i] : 0;
+            v[i] = v[i] * ldexpf(r, -k);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] = v[i] * r;
+    }
+}
+
+// TENSOR and GROUP modes: one workgroup per (row, 2048-column chunk).
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads) quantize_chunk_kernel(QuantParams p, int64_t chunks) {
+    int64_t b = blockIdx.x;
+    int64_t row = b / chunks;
+    int64_t col = (b % chunks) * kChunk + threadIdx.x * 8;
+    const char* rp = reinterpret_cast<const char*>(p.x) + row * p.ldx * (p.x_bf16 ? 2 : 4);
+    float v[8];
+    load8<VEC>(rp, p.x_bf16, col, p.cols, v);
+    shift_inputs(p, col, v);
+    float r;
+    if (p.mode == 0) {
+        float s = p.tensor_scale ? p.tensor_scale[0] : p.tensor_amax[0] / p.g.qmax;
+        r = recip_or_zero(s);
+        if (b == 0 && threadIdx.x == 0 && p.tensor_scale && p.scales_out)
+            reinterpret_cast<float*>(p.scales_out)[0] = s;
+    } else {
+        int lanes = p.group >> 3;
+        int64_t unit = row * (p.cols / p.group) + col / p.group;
+        float amax;
+        if (p.amax_in) {
+            amax = (col < p.cols) ? p.amax_in[unit] : 0.0f;
+        } else {
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
+            amax = group_max(m, lanes);
+        }
+        float s = amax / p.g.qmax;
+        if (p.scale_f16) s = round_f16(s);
+        r = recip_or_zero(s);
+        if (col < p.cols && (threadIdx.x & (lanes - 1)) == 0 && p.scales_out) {
+            if (p.scale_f16) reinterpret_cast<__half*>(p.scales_out)[unit] = __float2half_rn(s);
+            else reinterpret_cast<float*>(p.scales_out)[unit] = s;
+        }
+    }
+    scale_values(p, col, r, v);
+    uint32_t w = pack8(v, p.g);
+    store_codes(p.packed + row * p.ldp, col, p.cols, w, VEC);
+}
+
+// ROW mode: one workgroup per row; pass 1 reduces the row max, pass 2 quantizes.
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads) quantize_row_kernel(QuantParams p) {
+    __shared__ float red[kThreads / 64];
+    int64_t row = blockIdx.x;
+    const char* rp = reinterpret_cast<const char*>(p.x) + row * p.ldx * (p.x_bf16 ? 2 : 4);
+    float amax;
+    if (p.amax_in) {
+        amax = p.amax_in[row];
+    } else {
+        float m = 0.0f;
+        for (int64_t c0 = 0; c0 < p.cols; c0 += kChunk) {
+            int64_t col = c0 + threadIdx.x * 8;
+            float v[8];
+            load8<VEC>(rp, p.x_bf16, col, p.cols, v);
+            shift_inputs(p, col, v);
+#pragma unroll
+            for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
+        }
+        m = wave_max(m);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    }
+    float s = amax / p.g.qmax;
+    if (p.scale_f16) s = round_f16(s);
+    float r = recip_or_zero(s);
+    if (threadIdx.x == 0 && p.scales_out) {
+        if (p.scale_f16) reinterpret_cast<__half*>(p.scales_out)[row] = __float2half_rn(s);
+        else reinterpret_cast<float*>(p.scales_out)[row] = s;
+    }
+    for (int64_t c0 = 0; c0 < p.cols; c0 += kChunk) {
+        int64_t col = c0 + threadIdx.x * 8;
+        if (col >= p.cols) continue;
+        float v[8];
+        load8<VEC>(rp, p.x_bf16, col, p.cols, v);
+        shift_inputs(p, col, v);
+        scale_values(p, col, r, v);
+        uint32_t w = pack8(v, p.g);
+        store_codes(p.packed + row * p.ldp, col, p.cols, w, VEC);
+    }
+}
+
+__global__ void tensor_scale_finalize_kernel(const float* amax, float* scales_out, float qmax) {
+    scales_out[0] = amax[0] / qmax;
+}
+
+hipError_t launch_tensor_scale_finalize(const float* amax, float* scales_out, float qmax, hipStream_t s) {
+    hipLaunchKernelGGL(tensor_scale_finalize_kernel, dim3(1), dim3(1), 0, s, amax, scales_out, qmax);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
+    if (p.rows == 0 || p.cols == 0) return hipSuccess;
+    if (p.mode == 1) {
+        if (p.vec) hipLaunchKernelGGL(quantize_row_kernel<true>, dim3((unsigned)p.rows), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL(quantize_row_kernel<false>, dim3((unsigned)p.rows), dim3(kThreads), 0, s, p);
+    } else {
+        int64_t chunks = (p.cols + kChunk - 1) / kChunk;
+        dim3 grid((unsigned)(p.rows * chunks));
+        if (p.vec) hipLaunchKernelGGL(quantize_chunk_kernel<true>, grid, dim3(kThreads), 0, s, p, chunks);
+        else hipLaunchKernelGGL(quantize_chunk_kernel<false>, grid, dim3(kThreads), 0, s, p, chunks);
+    }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ dequantize ---
+__global__ void __launch_bounds__(kThreads) dequantize_kernel(const uint8_t* packed, int64_t cols, int64_t ldp,
+                                                              QGrid g, int mode, int group, const void* scales,
+                                                              int scale_f16, const int8_t* col_shift, float* out,
+                                                              int64_t ldo, int64_t chunks) {
+    int64_t b = blockIdx.x;
+    int64_t row = b / chunks;
+    int64_t col = (b % chunks) * kChunk + threadIdx.x * 8;
+    if (col >= cols) return;
+    const uint8_t* prow = packed + row * ldp;
+    for (int i = 0; i < 8 && col + i < cols; i++) {
+        int64_t c = col + i;
+        uint32_t code = (prow[c >> 1] >> (4 * (c & 1))) & 15u;
+        int64_t unit = mode == 0 ? 0 : (mode == 1 ? row : row * (cols / group) + c / group);
+        float sc = scale_f16 ? __half2float(reinterpret_cast<const __half*>(scales)[unit])
+                             : reinterpret_cast<const float*>(scales)[unit];
+        float v = grid_value(code, g) * sc;
+        if (col_shift) v = ldexpf(v, (int)col_shift[c]);
+        out[row * ldo + c] = v;
+    }
+}
+
+hipError_t launch_dequantize(const uint8_t* packed, int64_t rows, int64_t cols, int64_t ldp, const QGrid& g,
+                             int mode, int group, const void* scales, int scale_f16, const int8_t* col_shift,
+                             float* out, int64_t ldo, hipStream_t s) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    int64_t chunks = (cols + kChunk - 1) / kChunk;
+    hipLaunchKernelGGL(dequantize_kernel, dim3((unsigned)(rows * chunks)), dim3(kThreads), 0, s, packed, cols, ldp,
+                       g, mode, group, scales, scale_f16, col_shift, out, ldo, chunks);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ pre-shift ----
+// One workgroup: c_max = max_k c[k]; a = fl32(c_max / Qmax); k_j = smallest j with
+// c_max * 2^j >= c[j].  With c = f * 2^E, f in [0.5, 1): k = E_c - E_max + (f_max < f_c),
+// exact; 0 for c == 0; clamped at -64.
+__global__ void __launch_bounds__(1024) preshift_factors_kernel(const float* c, int64_t k, float act_qmax,
+                                                                int8_t* shift_out, float* act_scale_out) {
+    __shared__ float red[16];
+    float m = 0.0f;
+    for (int64_t j = threadIdx.x; j < k; j += blockDim.x) m = fmaxf(m, c[j]);
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    float cmax = 0.0f;
+    for (int i = 0; i < (int)(blockDim.x >> 6); i++) cmax = fmaxf(cmax, red[i]);
+    if (threadIdx.x == 0) act_scale_out[0] = cmax / act_qmax;
+    int em;
+    float fm = frexpf(cmax, &em);
+    for (int64_t j = threadIdx.x; j < k; j += blockDim.x) {
+        float cj = c[j];
+        int ej;
+        float fj = frexpf(cj, &ej);
+        int kk = ej - em + (fm < fj ? 1 : 0);
+        if (kk < -64) kk = -64;
+        if (cj == 0.0f) kk = 0;
+        shift_out[j] = (int8_t)kk;
+    }
+}
+
+hipError_t launch_preshift_factors(const float* chan_amax, int64_t k, float act_qmax, int8_t* shift_out,
+                                   float* act_scale_out, hipStream_t s) {
+    hipLaunchKernelGGL(preshift_factors_kernel, dim3(1), dim3(1024), 0, s, chan_amax, k, act_qmax, shift_out,
+                       act_scale_out);
+    return hipGetLastError();
+}
+
+}  // namespace fp4

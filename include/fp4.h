@@ -1,0 +1,248 @@
+/*
+ * fp4.h -- C ABI of libfp4: low-bit floating-point quantization of LLM weights and
+ * activations and the quantized matrix products that consume them, as hand-written
+ * HIP kernels for AMD MI355X (gfx950).
+ *
+ * Method sources (web pages, cited by title and section):
+ *   [FP4-LLM]  "首个支持4-bit浮点量化的LLM来了，解决LLaMA、BERT等的部署难题" (811yy.cn), a
+ *              summary of the LLM-FP4 paper: FP value formula (sign, exponent field p,
+ *              mantissa bits, bias b); "scale and clip", eqs. (2)-(3); bias from the
+ *              range, eq. (4); "compare and quantize", eq. (5); scales kept outside the
+ *              low-bit product ("efficient matrix multiplication"); search over the
+ *              exponent/mantissa split and range; pre-shifted exponent bias.
+ *   [Overview] "量化技术详解" (aidocs.cortexgrid.cn): granularities (per tensor / channel /
+ *              token), static quantization, NF4.
+ *   [W8A8]     intelliparadigm.com LLM-quantization practice, section 2.2: calibrate by
+ *              max |x|; quantized matmul = low-bit product times the product of scales;
+ *              group size 128.
+ *   [Tutorial] "为什么我们需要4-bit浮点量化" (devpress.csdn.net), section 2.2: two 4-bit
+ *              values per byte, on-the-fly 4->8-bit decode for the matmul.
+ *   [HiFloat4] "HiFloat4格式" (cf-1.com), section 3.2: 128-bit loads of 32 packed values.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the comment says "host".  The caller owns
+ *     all memory; the library allocates nothing and keeps no pointer after returning.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) and never synchronises.  Results are valid once the stream reaches them.
+ *   - Matrices are row-major with a leading dimension (ld, in ELEMENTS for f32/bf16/
+ *     f16 and in BYTES for packed 4-bit data).  Linear-layer shapes: W is [N, K]
+ *     (out x in, K contiguous), X is [M, K], Y = X * W^T is [M, N].
+ *   - Packed 4-bit data: byte j of a row holds element 2j in its low nibble and
+ *     element 2j+1 in its high nibble.  Minifloat code = sign<<3 | p<<m | d; lookup-
+ *     grid code = index into the 16 sorted grid values.
+ *   - Alignment: every pointer 16-byte aligned; see each call for stride rules.
+ *   - Inputs must be finite (no inf/NaN); results for non-finite inputs are unspecified.
+ *   - Return value: FP4_OK, or an error detected on the host BEFORE anything is
+ *     launched (INVALID_ARG, UNSUPPORTED, ALIGNMENT, WORKSPACE), or FP4_ERR_HIP when
+ *     a launch failed.  fp4_last_error() gives a message for the calling thread.
+ *   - Calls are thread-safe; calls that share output buffers must be ordered by the
+ *     caller.
+ */
+#ifndef FP4_H_
+#define FP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t fp4_status;
+#define FP4_OK               0
+#define FP4_ERR_INVALID_ARG  1  /* null pointer, bad size, stride or enum value      */
+#define FP4_ERR_UNSUPPORTED  2  /* valid request this library does not implement     */
+#define FP4_ERR_ALIGNMENT    3  /* pointer or stride breaks the alignment rule       */
+#define FP4_ERR_WORKSPACE    4  /* workspace missing or smaller than required        */
+#define FP4_ERR_HIP          5  /* a HIP launch failed (message in fp4_last_error)   */
+
+/* element types */
+#define FP4_F32     0
+#define FP4_BF16    1
+#define FP4_F16     2
+#define FP4_PACKED  3   /* two 4-bit codes per byte */
+
+/* ---- number grids -------------------------------------------------------------
+ * FP4_GRID_MINIFLOAT: FP(e, m) with e + m == 3 and the canonical bias 1 ([FP4-LLM]
+ *   FP value formula): magnitude of code p<<m | d is 2^(1-1) * d / 2^m for p == 0
+ *   (subnormal) and 2^(p-1) * (1 + d / 2^m) for p >= 1; no code is reserved for
+ *   inf/NaN.  E2M1 = {0, .5, 1, 1.5, 2, 3, 4, 6}, E1M2 = {0, .25, ..., 1.75},
+ *   E3M0 = {0, 1, 2, 4, ..., 64}.  A real-valued bias b is the same grid times
+ *   2^(1-b) ([FP4-LLM] eq. (4)), i.e. it lives entirely in the scale.
+ * FP4_GRID_LUT16: 16 sorted signed values in lut[] (e.g. NF4, [Overview] NF4), each
+ *   exactly representable in binary16.                                              */
+#define FP4_GRID_MINIFLOAT 0
+#define FP4_GRID_LUT16     1
+typedef struct {
+    int32_t kind;     /* FP4_GRID_MINIFLOAT or FP4_GRID_LUT16               */
+    int32_t e;        /* minifloat exponent bits (1, 2 or 3)                 */
+    int32_t m;        /* minifloat mantissa bits (e + m == 3)                */
+    int32_t reserved; /* must be 0                                           */
+    float   lut[16];  /* LUT16 values, strictly increasing; ignored otherwise */
+} fp4_grid;
+
+/* ---- scale granularity ([Overview] granularities; [W8A8] group size 128) -------
+ * TENSOR: one scale; ROW: one scale per row (output channel of a weight, token of an
+ * activation); GROUP: one scale per `group` consecutive elements of a row.          */
+#define FP4_SCALE_TENSOR 0
+#define FP4_SCALE_ROW    1
+#define FP4_SCALE_GROUP  2
+typedef struct {
+    int32_t mode;         /* FP4_SCALE_TENSOR | _ROW | _GROUP                    */
+    int32_t group;        /* GROUP: 8, 16, 32, 64, 128, 256 or 512; else 0       */
+    int32_t scale_dtype;  /* FP4_F32, or FP4_F16 (ROW and GROUP only)            */
+    int32_t reserved;     /* must be 0                                           */
+} fp4_gran;
+
+/* ---- calibration reductions ---------------------------------------------------- */
+#define FP4_REDUCE_TENSOR    0   /* amax_out[0]                                      */
+#define FP4_REDUCE_COLUMN    1   /* amax_out[cols]   (per input channel)             */
+#define FP4_REDUCE_ROW_GROUP 2   /* amax_out[rows * cols/group]                      */
+
+/* ---- search record ([FP4-LLM] search over exponent/mantissa split and range) ---- */
+typedef struct {
+    int32_t e, m;           /* winning format                                       */
+    int32_t clip_index;     /* j in [0, nclips): clip = amax * ratio_j               */
+    int32_t format_index;   /* index into the caller's format list                  */
+    float   clip;           /* fl32(amax * ratio_j)                                 */
+    float   scale;          /* s = fl32(clip / Qmax(e, m)), the stored scale         */
+    float   amax;           /* max |w| of the tensor                                */
+    float   reserved;
+    double  bias;           /* real exponent bias equivalent to s: 1 - log2(s)      */
+    double  mse;            /* mean of (w - dequant(quant(w)))^2, correctly rounded */
+    double  mse_runner_up;  /* smallest MSE among the other candidates              */
+} fp4_search_result;
+
+/* ---- quantized GEMM descriptor ------------------------------------------------- */
+typedef struct {
+    int64_t M, N, K;
+    /* activations X [M, K] */
+    int32_t a_kind;           /* FP4_F32, FP4_BF16 (W4A16) or FP4_PACKED (W4A4)      */
+    int32_t reserved0;
+    const void* a;            /* device                                             */
+    int64_t lda;              /* elements (F32/BF16) or bytes (PACKED)              */
+    fp4_grid a_grid;          /* PACKED only: grid of the activation codes          */
+    const float* a_scale;     /* PACKED only: device pointer to the one f32 scale a */
+    /* weights W [N, K], packed */
+    const uint8_t* w;
+    int64_t ldw;              /* bytes                                              */
+    fp4_grid w_grid;
+    fp4_gran w_gran;          /* TENSOR, ROW or GROUP along K                        */
+    const void* w_scales;     /* f32 or f16 per w_gran                              */
+    /* output Y [M, N] */
+    void* y;
+    int64_t ldy;              /* elements                                           */
+    int32_t y_dtype;          /* FP4_BF16 or FP4_F32                                */
+    int32_t reserved1;
+} fp4_gemm_desc;
+
+/* Human-readable name of a status code (static storage). */
+const char* fp4_status_string(fp4_status s);
+
+/* Message describing the last error returned on the calling thread ("" if none). */
+const char* fp4_last_error(void);
+
+/* Calibrate: amax = max |x| ([W8A8] section 2.2 calibrate; [FP4-LLM] pre-shift uses
+ * per-channel maxima from a small calibration set; [Overview] static quantization).
+ *   x          device, x_dtype FP4_F32 or FP4_BF16, [rows, cols] with leading dim ld
+ *   reduce     FP4_REDUCE_TENSOR | _COLUMN | _ROW_GROUP
+ *   group      ROW_GROUP: group size (divides cols, one of 8..512 as in fp4_gran)
+ *   first_rows only rows [0, first_rows) are reduced (the calibration tokens); <= 0
+ *              means all rows
+ *   amax_out   device f32: 1, cols, or rows*(cols/group) values
+ * The result is exact (max is order-free) and identical for any launch geometry. */
+fp4_status fp4_calibrate(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                         int64_t ld, int32_t reduce, int32_t group, int64_t first_rows,
+                         float* amax_out, void* stream);
+
+/* Quantize and pack ([FP4-LLM] eqs. (2)-(5): scale and clip, compare and quantize;
+ * [Tutorial] section 2.2: two codes per byte).
+ *   For every scale unit u (tensor, row or group): s_u = fl32(amax_u / Qmax) (Qmax =
+ *   largest grid magnitude; for ROW/GROUP with FP4_F16 scales s_u is rounded to
+ *   binary16 and the rounded value is used), r_u = fl32(1 / s_u) (0 if s_u == 0).
+ *   Element x: y = fl32(x * r) with r = r_u, or r_u * 2^-k[col] when col_shift is
+ *   given (pre-shifted exponent bias, activation side); code = nearest grid point to
+ *   y after clipping to +-Qmax, exact ties to the even code; minifloat codes carry
+ *   signbit(x).
+ *   x            device, FP4_F32 or FP4_BF16, [rows, cols], leading dim ldx elements
+ *   cols         even; GROUP: multiple of group
+ *   grid, gran   see above (gran.scale_dtype FP4_F16 only for ROW/GROUP)
+ *   amax_in      device f32 per scale unit from fp4_calibrate, or NULL = computed here
+ *   tensor_scale TENSOR only: device pointer to a fixed f32 scale s (static
+ *                activation quantization, e.g. the per-tensor scale a from
+ *                fp4_preshift_weights), or NULL
+ *   col_shift    device int8 k[cols] (values in [-64, 0]), or NULL
+ *   packed       device u8 [rows, cols/2], leading dim ldp bytes
+ *   scales_out   device, f32 or f16 per scale unit (1, rows, or rows*cols/group);
+ *                may be NULL only when tensor_scale is given                         */
+fp4_status fp4_quantize_pack(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                             int64_t ldx, fp4_grid grid, fp4_gran gran,
+                             const float* amax_in, const float* tensor_scale,
+                             const int8_t* col_shift, uint8_t* packed, int64_t ldp,
+                             void* scales_out, void* stream);
+
+/* Dequantize (inverse of the codec, [Tutorial] section 2.2 decode):
+ *   out = +-fl32(g(code) * s_u), times 2^k[col] when col_shift is given (exact).
+ *   packed [rows, cols/2] (ldp bytes), scales per gran, out f32 [rows, cols] (ldo). */
+fp4_status fp4_dequantize(const uint8_t* packed, int64_t rows, int64_t cols, int64_t ldp,
+                          fp4_grid grid, fp4_gran gran, const void* scales,
+                          const int8_t* col_shift, float* out, int64_t ldo, void* stream);
+
+/* Pre-shifted exponent bias ([FP4-LLM], pre-shifted exponent bias): from per-channel
+ * activation maxima c[k] (fp4_calibrate COLUMN over the calibration tokens):
+ *   c_max = max_k c[k];  a = fl32(c_max / Qmax(act_grid))           -> act_scale_out
+ *   shift k_k = smallest integer j with c_max * 2^j >= c[k] (0 if c[k] == 0, clamped
+ *   at -64; always <= 0), computed exactly from the binary exponents  -> shift_out
+ *   W'[n, k] = W[n, k] * 2^k_k (exact), then W' is quantized with w_grid / w_gran
+ *   (scales from the amax of W') -> w_packed, w_scales.
+ * Activations are then quantized with fp4_quantize_pack(gran TENSOR, tensor_scale =
+ * act_scale_out, col_shift = shift_out), and X * W^T = (X 2^-k) * (W 2^k)^T exactly.
+ *   w            device f32 [n, k], leading dim ldw elements
+ *   chan_amax    device f32 [k]
+ *   w_packed     device u8 [n, k/2], leading dim ldp bytes                          */
+fp4_status fp4_preshift_weights(const float* w, int64_t n, int64_t k, int64_t ldw,
+                                const float* chan_amax, fp4_grid act_grid,
+                                fp4_grid w_grid, fp4_gran w_gran, int8_t* shift_out,
+                                float* act_scale_out, uint8_t* w_packed, int64_t ldp,
+                                void* w_scales, void* stream);
+
+/* Workspace bytes that fp4_search_format needs for these sizes. */
+size_t fp4_search_workspace_size(int64_t ntensors, int64_t numel, int32_t nformats,
+                                 int32_t nclips);
+
+/* Format and clip-range search ([FP4-LLM] search-based FP quantization): for each of
+ * ntensors contiguous tensors of numel f32 values, evaluate every format in
+ * formats_em (host, nformats pairs (e, m), minifloat with e + m == 3) times nclips
+ * clip values c_j = fl32(amax * ratio_j), ratio_j = fl32(lo + (hi - lo) * j /
+ * (nclips - 1)) evaluated in binary64; candidate error = mean over the tensor of
+ * (w - dequant(quant(w)))^2 with s = fl32(c_j / Qmax), accumulated so that the
+ * result is the correctly rounded mean (independent of summation order).  The
+ * winner is the smallest MSE; exact ties go to the earliest candidate (formats
+ * outer, clips inner).  Each tensor is then packed with its winner (TENSOR scale s).
+ *   w        device f32 [ntensors, numel] (numel even)
+ *   results  device fp4_search_result [ntensors]
+ *   packed   device u8 [ntensors, numel/2]
+ *   workspace, ws_bytes  device scratch of at least fp4_search_workspace_size()    */
+fp4_status fp4_search_format(const float* w, int64_t ntensors, int64_t numel,
+                             const int32_t* formats_em, int32_t nformats, int32_t nclips,
+                             float clip_lo, float clip_hi, fp4_search_result* results,
+                             uint8_t* packed, void* workspace, size_t ws_bytes,
+                             void* stream);
+
+/* Quantized GEMM Y = X * W^T with scales factored out of the low-bit inner product
+ * ([FP4-LLM] efficient matrix multiplication; [W8A8] section 2.2 quantized_matmul):
+ *   W4A16 (a_kind F32/BF16):  Y[m,n] = sum_u s[n,u] * sum_{k in u} x[m,k] * g(c[n,k])
+ *                              (u = the scale units of w_gran along K), fp32 accumulate.
+ *   W4A4  (a_kind PACKED):    Y[m,n] = a * sum_u s[n,u] * sum_{k in u} A_q[m,k] W_q[n,k]
+ *     - E2M1 x E2M1 with TENSOR/ROW weight scales runs on the FP4 matrix cores; the
+ *       code product is exact in fp32 and the epilogue is y = fl32(acc * fl32(a * s_n)).
+ *     - E2M1 activations x LUT16 weights (NF4) with GROUP scales runs on the f16
+ *       matrix cores with the group partials scaled in fp32.
+ *   y_dtype FP4_BF16 rounds the f32 result to nearest-even.
+ * Strides: K a multiple of 32 for the matrix-core paths; packed rows 16-byte aligned. */
+fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4_H_ */

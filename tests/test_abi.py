@@ -1,0 +1,159 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the header
+declares with the struct layouts the header defines, and rejects bad arguments on the
+host with the documented status codes before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from bit_floating_point_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load()
+    names = _declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.SIGNATURES)
+
+
+def test_struct_layouts_match_header(tmp_path):
+    src = tmp_path / "sz.c"
+    src.write_text('#include "fp4.h"\n#include <stdio.h>\n#include <stddef.h>\n'
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(fp4_grid), sizeof(fp4_gran),'
+                   ' sizeof(fp4_search_result), sizeof(fp4_gemm_desc), offsetof(fp4_gemm_desc, a_scale),'
+                   ' offsetof(fp4_gemm_desc, w_gran), offsetof(fp4_gemm_desc, y_dtype)); return 0;}\n')
+    exe = tmp_path / "sz"
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
+    want = [ctypes.sizeof(L.fp4_grid), ctypes.sizeof(L.fp4_gran), ctypes.sizeof(L.fp4_search_result),
+            ctypes.sizeof(L.fp4_gemm_desc), L.fp4_gemm_desc.a_scale.offset, L.fp4_gemm_desc.w_gran.offset,
+            L.fp4_gemm_desc.y_dtype.offset]
+    assert got == want
+
+
+def test_status_strings():
+    lib = L.load()
+    assert lib.fp4_status_string(0) == b"FP4_OK"
+    assert lib.fp4_status_string(4) == b"FP4_ERR_WORKSPACE"
+
+
+# ---- host-side validation (no launch happens for any of these) ----
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every call below is rejected first
+ODD = ctypes.c_void_p(0x10004)
+
+
+def _grid(kind=0, e=2, m=1):
+    g = L.fp4_grid()
+    g.kind, g.e, g.m = kind, e, m
+    return g
+
+
+def _gran(mode=0, group=0, sd=0):
+    g = L.fp4_gran()
+    g.mode, g.group, g.scale_dtype = mode, group, sd
+    return g
+
+
+def test_quantize_validation():
+    lib = L.load()
+    q = lib.fp4_quantize_pack
+    N = ctypes.c_void_p(0)
+    assert q(N, 0, 4, 8, 8, _grid(), _gran(), N, N, N, FAKE, 4, FAKE, N) == L.FP4_ERR_INVALID_ARG
+    assert b"null" in lib.fp4_last_error()
+    assert q(FAKE, 0, 4, 7, 8, _grid(), _gran(), N, N, N, FAKE, 4, FAKE, N) == L.FP4_ERR_INVALID_ARG  # odd cols
+    assert q(FAKE, 0, 4, 8, 8, _grid(0, 2, 2), _gran(), N, N, N, FAKE, 4, FAKE, N) == L.FP4_ERR_UNSUPPORTED
+    assert q(FAKE, 0, 4, 8, 8, _grid(0, 0, 3), _gran(), N, N, N, FAKE, 4, FAKE, N) == L.FP4_ERR_UNSUPPORTED
+    assert q(FAKE, 0, 4, 8, 8, _grid(7), _gran(), N, N, N, FAKE, 4, FAKE, N) == L.FP4_ERR_INVALID_ARG
+    assert q(FAKE, 0, 4, 96, 96, _grid(), _gran(2, 64), N, N, N, FAKE, 48, FAKE, N) == L.FP4_ERR_INVALID_ARG
+    assert q(FAKE, 0, 4, 96, 96, _grid(), _gran(2, 24), N, N, N, FAKE, 48, FAKE, N) == L.FP4_ERR_UNSUPPORTED
+    assert q(FAKE, 0, 4, 8, 8, _grid(), _gran(0, 0, 2), N, N, N, FAKE, 4, FAKE, N) == L.FP4_ERR_UNSUPPORTED
+    assert q(ODD, 0, 4, 8, 8, _grid(), _gran(), N, N, N, FAKE, 4, FAKE, N) == L.FP4_ERR_ALIGNMENT
+    assert q(FAKE, 0, 4, 8, 8, _grid(), _gran(), N, N, N, FAKE, 4, N, N) == L.FP4_ERR_INVALID_ARG
+    assert q(FAKE, 5, 4, 8, 8, _grid(), _gran(), N, N, N, FAKE, 4, FAKE, N) == L.FP4_ERR_INVALID_ARG
+    lut = _grid(1)
+    for i in range(16):
+        lut.lut[i] = i * 0.1  # not binary16-exact
+    assert q(FAKE, 0, 4, 8, 8, lut, _gran(), N, N, N, FAKE, 4, FAKE, N) == L.FP4_ERR_INVALID_ARG
+
+
+def test_calibrate_validation():
+    lib = L.load()
+    c = lib.fp4_calibrate
+    N = ctypes.c_void_p(0)
+    assert c(N, 0, 4, 8, 8, 0, 0, 0, FAKE, N) == L.FP4_ERR_INVALID_ARG
+    assert c(FAKE, 0, 4, 8, 4, 0, 0, 0, FAKE, N) == L.FP4_ERR_INVALID_ARG  # ld < cols
+    assert c(FAKE, 0, 4, 8, 8, 9, 0, 0, FAKE, N) == L.FP4_ERR_INVALID_ARG
+    assert c(FAKE, 0, 4, 8, 8, 2, 6, 0, FAKE, N) == L.FP4_ERR_UNSUPPORTED
+    assert c(ODD, 0, 4, 8, 8, 0, 0, 0, FAKE, N) == L.FP4_ERR_ALIGNMENT
+
+
+def test_search_validation():
+    lib = L.load()
+    s = lib.fp4_search_format
+    N = ctypes.c_void_p(0)
+    fm = (ctypes.c_int32 * 6)(1, 2, 2, 1, 3, 0)
+    need = lib.fp4_search_workspace_size(2, 1024, 3, 100)
+    assert need > 0
+    assert s(FAKE, 2, 1024, fm, 3, 100, 0.5, 1.0, FAKE, FAKE, FAKE, need - 1, N) == L.FP4_ERR_WORKSPACE
+    assert s(FAKE, 2, 1024, fm, 3, 100, 0.5, 1.0, FAKE, FAKE, N, need, N) == L.FP4_ERR_WORKSPACE
+    assert s(FAKE, 2, 1000, fm, 3, 100, 0.5, 1.0, FAKE, FAKE, FAKE, need, N) == L.FP4_ERR_INVALID_ARG
+    assert s(FAKE, 2, 1024, fm, 3, 1, 0.5, 1.0, FAKE, FAKE, FAKE, need, N) == L.FP4_ERR_UNSUPPORTED
+    assert s(FAKE, 2, 1024, fm, 3, 200, 0.5, 1.0, FAKE, FAKE, FAKE, need, N) == L.FP4_ERR_UNSUPPORTED
+    assert s(FAKE, 2, 1024, fm, 3, 100, 0.0, 1.0, FAKE, FAKE, FAKE, need, N) == L.FP4_ERR_INVALID_ARG
+    bad = (ctypes.c_int32 * 2)(2, 2)
+    assert s(FAKE, 2, 1024, bad, 1, 100, 0.5, 1.0, FAKE, FAKE, FAKE, need, N) == L.FP4_ERR_UNSUPPORTED
+
+
+def test_gemm_validation():
+    lib = L.load()
+    N = ctypes.c_void_p(0)
+    assert lib.fp4_gemm(None, N) == L.FP4_ERR_INVALID_ARG
+    d = L.fp4_gemm_desc()
+    d.M, d.N, d.K = 16, 32, 256
+    d.a_kind = L.FP4_PACKED
+    d.a, d.lda, d.w, d.ldw, d.w_scales, d.y, d.ldy = 0x10000, 128, 0x20000, 128, 0x30000, 0x40000, 32
+    d.a_grid, d.w_grid = _grid(), _grid()
+    d.w_gran = _gran(1)
+    d.y_dtype = L.FP4_BF16
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_INVALID_ARG  # no a_scale
+    d.a_scale = 0x50000
+    d.a_grid = _grid(0, 1, 2)
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # E1M2 activations
+    d.a_grid = _grid()
+    d.w_gran = _gran(2, 64)
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # E2M1 x E2M1 with group scales
+    d.w_gran = _gran(1)
+    d.ldw = 100
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_INVALID_ARG  # ldw < K/2
+    d.ldw = 136
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_ALIGNMENT
+    d.ldw = 128
+    d.y_dtype = 7
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_INVALID_ARG
+
+
+def test_preshift_validation():
+    lib = L.load()
+    N = ctypes.c_void_p(0)
+    f = lib.fp4_preshift_weights
+    assert f(FAKE, 8, 16, 16, FAKE, _grid(), _grid(), _gran(0), FAKE, FAKE, FAKE, 8, FAKE, N) == L.FP4_ERR_UNSUPPORTED
+    assert f(FAKE, 8, 16, 16, N, _grid(), _grid(), _gran(1), FAKE, FAKE, FAKE, 8, FAKE, N) == L.FP4_ERR_INVALID_ARG
+    assert f(ODD, 8, 16, 16, FAKE, _grid(), _grid(), _gran(1), FAKE, FAKE, FAKE, 8, FAKE, N) == L.FP4_ERR_ALIGNMENT
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    with pytest.raises(ImportError):
+        L.load(str(tmp_path / "missing.so"))

@@ -1,0 +1,333 @@
+"""Parity of the HIP library (through its C ABI) against the CPU oracle.
+
+Bar: codes, packed bytes, scales, shifts and search records bit-exact; W4A4 E2M1
+outputs bit-exact (fp32 accumulation of FP4 products is exact); other GEMM outputs
+within normwise max relative error 1e-3 of the binary64 oracle, measured on the
+kernel's fp32 output, with its bf16 output equal to the round-to-nearest-even of
+that fp32 output.  Sizes span several tiles with ragged tails; full workload sizes
+are checked on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+
+pytestmark = pytest.mark.gpu
+
+F = pytest.importorskip("bit_floating_point_amd")
+DEV = "cuda"
+TOL = 1e-3
+
+
+def dev(x, dtype=torch.float32):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV).to(dtype)
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def grids(fmt):
+    if fmt == "nf4":
+        return O.nf4(), F.grid_nf4()
+    return O.minifloat(*fmt), F.grid_minifloat(*fmt)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    F._lib.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- calibrate -------
+@pytest.mark.parametrize("bf16", [True, False])
+def test_calibrate(bf16):
+    say("calibrate", bf16)
+    x = synth.activations(3, 5, 300, 520, outlier_frac=0.01, bf16=bf16)
+    xt = dev(x, torch.bfloat16 if bf16 else torch.float32)
+    assert host(F.fp4_calibrate(xt, "tensor"))[0] == O.amax_tensor(x)
+    assert np.array_equal(host(F.fp4_calibrate(xt, "column", first_rows=128)), O.amax_columns(x, 128))
+    assert np.array_equal(host(F.fp4_calibrate(xt, "row_group", group=8)), O.amax_row_groups(x, 8).reshape(-1))
+    x2 = x[:, :512]
+    xt2 = dev(x2, torch.bfloat16 if bf16 else torch.float32)
+    assert np.array_equal(host(F.fp4_calibrate(xt2, "row_group", group=64)), O.amax_row_groups(x2, 64).reshape(-1))
+
+
+# ---------------------------------------------------------------- quantize --------
+FMTS = [(2, 1), (1, 2), (3, 0), "nf4"]
+MODES = [("tensor", 0, "f32"), ("row", 0, "f32"), ("row", 0, "f16"), ("group", 128, "f16"),
+         ("group", 64, "f32"), ("group", 8, "f32"), ("group", 512, "f32")]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("mode,group,sd", MODES)
+@pytest.mark.parametrize("bf16", [False, True])
+def test_quantize_pack_dequantize(fmt, mode, group, sd, bf16):
+    say("quantize", fmt, mode, group, sd, bf16)
+    cols = 1024 if mode == "group" else 1030  # 1030: ragged 8-element tail, scalar path
+    x = synth.heavy_tail_weight(2, 7, 37, cols)
+    if bf16:
+        x = synth.to_bf16_values(x)
+    x[3, :] = 0.0  # an all-zero row / group
+    og, fg = grids(fmt)
+    packed, scales = O.quantize_pack(x, og, mode, group, sd)
+    g = F.gran(mode, group, sd)
+    gp, gs = F.fp4_quantize_pack(dev(x, torch.bfloat16 if bf16 else torch.float32), fg, g)
+    assert np.array_equal(host(gp), packed)
+    assert np.array_equal(host(gs).view(np.uint16 if sd == "f16" else np.uint32),
+                          scales.reshape(-1).view(np.uint16 if sd == "f16" else np.uint32))
+    deq = O.dequantize(packed, og, mode, scales, group)
+    gd = F.fp4_dequantize(gp, fg, g, gs)
+    assert np.array_equal(host(gd).view(np.uint32), deq.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_bit_pattern_sweep(fmt):
+    """2^22 binary32 bit patterns spread over the whole encoding space (finite values
+    only), quantized at scale 1: every code must match the brute-force oracle."""
+    say("sweep", fmt)
+    u = (np.arange(1 << 22, dtype=np.uint64) * 1021 + 12345) % (1 << 32)
+    x = u.astype(np.uint32).view(np.float32)
+    x = x[np.isfinite(x)]
+    x = x[: (x.size // 16) * 16].reshape(-1, 1024)
+    og, fg = grids(fmt)
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    gp, _ = F.fp4_quantize_pack(dev(x), fg, F.gran("tensor"), tensor_scale=one)
+    want = O.pack(O.quantize(x, np.float32(1), og))
+    assert np.array_equal(host(gp), want)
+
+
+def test_quantize_edge_cases():
+    og, fg = grids((2, 1))
+    z = torch.zeros((0, 64), device=DEV)
+    p, s = F.fp4_quantize_pack(z, fg, F.gran("row"))
+    assert p.shape == (0, 32)
+    x = np.zeros((4, 64), dtype=np.float32)
+    x[1] = -0.0
+    gp, gs = F.fp4_quantize_pack(dev(x), fg, F.gran("tensor"))
+    assert np.array_equal(host(gp), O.quantize_pack(x, og, "tensor")[0]) and host(gs)[0] == 0
+    tiny = np.full((2, 16), 1e-40, dtype=np.float32)
+    tiny[1] *= -1
+    gp, gs = F.fp4_quantize_pack(dev(tiny), fg, F.gran("row"))
+    p, s = O.quantize_pack(tiny, og, "row")
+    assert np.array_equal(host(gp), p) and np.array_equal(host(gs), s)
+
+
+# ---------------------------------------------------------------- W4A16 -----------
+def test_tiny_round_trip():
+    """4-bit FP round trip on a 256x256 N(0, 0.02) matrix with one per-tensor scale,
+    then an 8x256 fp32-activation GEMM."""
+    w, x = synth.tiny()
+    og, fg = grids((2, 1))
+    packed, scales = O.quantize_pack(w, og, "tensor")
+    assert packed.shape == (256, 128)
+    gp, gs = F.fp4_quantize_pack(dev(w), fg, F.gran("tensor"))
+    assert np.array_equal(host(gp), packed) and host(gs)[0] == scales[0]
+    gd = F.fp4_dequantize(gp, fg, F.gran("tensor"), gs)
+    assert np.array_equal(host(gd), O.dequantize(packed, og, "tensor", scales))
+    r = O.gemm_w4a16(x, packed, og, "tensor", scales)
+    y32 = F.fp4_gemm(dev(x), gp, gs, fg, F.gran("tensor"), y_dtype=torch.float32)
+    assert O.rel_err(host(y32), r) <= TOL
+    yb = F.fp4_gemm(dev(x), gp, gs, fg, F.gran("tensor"), y_dtype=torch.bfloat16)
+    assert np.array_equal(host(yb.view(torch.int16)).view(np.uint16), O.rne_bf16_bits(host(y32)))
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_w4a16_decode_full(M):
+    """LLaMA-7B MLP linear 11008x4096, E2M1 with fp16 scales per 128 along K, bf16
+    activations: full-size weight codes bit-exact, every output within tolerance."""
+    say("w4a16", M)
+    w = _decode_weight()
+    og, fg = grids((2, 1))
+    packed, scales = _decode_packed()
+    g = F.gran("group", 128, "f16")
+    gp, gs = F.fp4_quantize_pack(dev(w), fg, g)
+    assert np.array_equal(host(gp), packed)
+    assert np.array_equal(host(gs).view(np.uint16), scales.reshape(-1).view(np.uint16))
+    x = synth.decode_activations(M)
+    r = O.gemm_w4a16(x, packed, og, "group", scales, group=128)
+    xt = dev(x, torch.bfloat16)
+    y32 = F.fp4_gemm(xt, gp, gs, fg, g, y_dtype=torch.float32)
+    err = O.rel_err(host(y32), r)
+    say("  rel err", err)
+    assert err <= TOL
+    yb = F.fp4_gemm(xt, gp, gs, fg, g, y_dtype=torch.bfloat16)
+    assert np.array_equal(host(yb.view(torch.int16)).view(np.uint16), O.rne_bf16_bits(host(y32)))
+
+
+_cache = {}
+
+
+def _decode_weight():
+    if "w" not in _cache:
+        _cache["w"] = synth.decode_weight()
+    return _cache["w"]
+
+
+def _decode_packed():
+    if "p" not in _cache:
+        _cache["p"] = O.quantize_pack(_decode_weight(), O.minifloat(2, 1), "group", 128, "f16")
+    return _cache["p"]
+
+
+@pytest.mark.parametrize("M,N,K,mode,group,fmt,bf16", [
+    (5, 100, 384, "group", 128, (2, 1), True),     # MFMA path, ragged N and M
+    (19, 70, 512, "group", 256, (2, 1), True),     # two chunks per group, M > 16
+    (3, 48, 640, "row", 0, (2, 1), True),          # per-row scales
+    (7, 33, 96, "group", 32, (2, 1), True),        # VALU path (group < 128)
+    (4, 40, 256, "group", 64, "nf4", True),        # lookup grid, VALU path
+    (6, 20, 128, "group", 64, (3, 0), False),      # f32 activations
+])
+def test_w4a16_shapes(M, N, K, mode, group, fmt, bf16):
+    say("w4a16 shape", M, N, K, mode, group, fmt, bf16)
+    w = synth.weight(2, 11, N, K)
+    x = synth.activations(2, 12, M, K, bf16=bf16)
+    og, fg = grids(fmt)
+    sd = "f16" if mode == "group" and group == 128 else "f32"
+    packed, scales = O.quantize_pack(w, og, mode, group, sd)
+    g = F.gran(mode, group, sd)
+    gp, gs = F.fp4_quantize_pack(dev(w), fg, g)
+    assert np.array_equal(host(gp), packed)
+    r = O.gemm_w4a16(x, packed, og, mode, scales, group=group)
+    y32 = F.fp4_gemm(dev(x, torch.bfloat16 if bf16 else torch.float32), gp, gs, fg, g, y_dtype=torch.float32)
+    assert O.rel_err(host(y32), r) <= TOL
+
+
+# ---------------------------------------------------------------- pre-shift + W4A4 --
+def _preshift_chain(x, w, w_fmt="e2m1", group=64):
+    """Oracle and GPU through calibrate -> pre-shift -> quantize -> GEMM; compares
+    every intermediate bit for bit and returns (oracle pieces, gpu pieces)."""
+    e2 = O.minifloat(2, 1)
+    fe2 = F.grid_minifloat(2, 1)
+    chan = O.amax_columns(x, 128)
+    if w_fmt == "e2m1":
+        k, a, wp, ws = O.preshift_weights(w, chan, e2, e2, "row")
+        fw, fgran = fe2, F.gran("row")
+    else:
+        k, a, wp, ws = O.preshift_weights(w, chan, e2, O.nf4(), "group", group)
+        fw, fgran = F.grid_nf4(), F.gran("group", group)
+    ap, _ = O.quantize_activations(x, e2, a, k)
+    xt = dev(x, torch.bfloat16)
+    gchan = F.fp4_calibrate(xt, "column", first_rows=128)
+    assert np.array_equal(host(gchan), chan)
+    gk, ga, gwp, gws = F.fp4_preshift_weights(dev(w), gchan, fe2, fw, fgran)
+    assert np.array_equal(host(gk), k)
+    assert host(ga)[0] == a
+    assert np.array_equal(host(gwp), wp)
+    assert np.array_equal(host(gws), ws.reshape(-1))
+    gap, _ = F.fp4_quantize_pack(xt, fe2, F.gran("tensor"), tensor_scale=ga, col_shift=gk)
+    assert np.array_equal(host(gap), ap)
+    return (k, a, wp, ws, ap), (gk, ga, gwp, gws, gap, fw, fgran)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 384, 512), (200, 300, 544), (64, 96, 4096), (520, 1100, 1024)])
+def test_preshift_w4a4_e2m1(M, N, K):
+    say("w4a4", M, N, K)
+    x = synth.activations(3, M, M, K, outlier_frac=0.01)
+    w = synth.weight(3, N, N, K)
+    (k, a, wp, ws, ap), (gk, ga, gwp, gws, gap, fw, fgran) = _preshift_chain(x, w)
+    e2 = O.minifloat(2, 1)
+    r, acc = O.gemm_w4a4(ap, e2, a, wp, e2, "row", ws)
+    y_pin = O.w4a4_epilogue_f32(acc, a, ws)
+    fe2 = F.grid_minifloat(2, 1)
+    y32 = F.fp4_gemm(gap, gwp, gws, fw, fgran, K=K, a_grid=fe2, a_scale=ga, y_dtype=torch.float32)
+    assert np.array_equal(host(y32).view(np.uint32), y_pin.view(np.uint32))
+    assert O.rel_err(host(y32), r) <= TOL
+    yb = F.fp4_gemm(gap, gwp, gws, fw, fgran, K=K, a_grid=fe2, a_scale=ga, y_dtype=torch.bfloat16)
+    assert np.array_equal(host(yb.view(torch.int16)).view(np.uint16), O.rne_bf16_bits(y_pin))
+
+
+def test_preshift_w4a4_full_2048x4096x4096():
+    """Calibration + pre-shift + W4A4 at the full 2048-token, 4096x4096 size: every
+    code bit-exact; the GEMM output bit-exact on 64 sampled rows."""
+    say("w4a4 full c3")
+    x, w = synth.preshift_inputs()
+    (k, a, wp, ws, ap), (gk, ga, gwp, gws, gap, fw, fgran) = _preshift_chain(x, w)
+    fe2 = F.grid_minifloat(2, 1)
+    y32 = host(F.fp4_gemm(gap, gwp, gws, fw, fgran, K=4096, a_grid=fe2, a_scale=ga, y_dtype=torch.float32))
+    rows = np.random.default_rng(0).choice(2048, 64, replace=False)
+    e2 = O.minifloat(2, 1)
+    r, acc = O.gemm_w4a4(ap[rows], e2, a, wp, e2, "row", ws)
+    assert np.array_equal(y32[rows].view(np.uint32), O.w4a4_epilogue_f32(acc, a, ws).view(np.uint32))
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 384, 512), (130, 200, 640)])
+def test_preshift_nf4(M, N, K):
+    say("nf4", M, N, K)
+    x = synth.activations(5, M, M, K, outlier_frac=0.01)
+    w = synth.weight(5, N, N, K)
+    (k, a, wp, ws, ap), (gk, ga, gwp, gws, gap, fw, fgran) = _preshift_chain(x, w, "nf4", 64)
+    r, _ = O.gemm_w4a4(ap, O.minifloat(2, 1), a, wp, O.nf4(), "group", ws, group=64)
+    fe2 = F.grid_minifloat(2, 1)
+    y32 = F.fp4_gemm(gap, gwp, gws, fw, fgran, K=K, a_grid=fe2, a_scale=ga, y_dtype=torch.float32)
+    err = O.rel_err(host(y32), r)
+    say("  rel err", err)
+    assert err <= TOL
+    yb = F.fp4_gemm(gap, gwp, gws, fw, fgran, K=K, a_grid=fe2, a_scale=ga, y_dtype=torch.bfloat16)
+    assert np.array_equal(host(yb.view(torch.int16)).view(np.uint16), O.rne_bf16_bits(host(y32)))
+
+
+# ---------------------------------------------------------------- search ----------
+def test_search_small():
+    say("search small")
+    T, rows, cols = 5, 32, 1040  # numel 33280: several passes and a ragged tail
+    ws = np.stack([synth.search_tensor(100 + t, rows, cols).reshape(-1) for t in range(T)])
+    res, packed = F.fp4_search_format(dev(ws))
+    recs = F.search_results_host(res)
+    gp = host(packed)
+    for t in range(T):
+        rec, p, mse = O.search_tensor(ws[t])
+        g = recs[t]
+        assert (g.e, g.m, g.clip_index) == (rec.e, rec.m, rec.clip_index), (t, g, rec)
+        assert np.float32(g.clip) == rec.clip and np.float32(g.scale) == rec.scale
+        assert g.mse == rec.mse and g.mse_runner_up == rec.mse_runner_up
+        assert abs(g.bias - rec.bias) <= 1e-14 * abs(rec.bias)
+        assert np.array_equal(gp[t], p)
+
+
+@pytest.mark.parametrize("fmt", [(1, 2), (2, 1), (3, 0)])
+def test_search_planted(fmt):
+    g = O.minifloat(*fmt)
+    rng = np.random.default_rng(3)
+    codes = np.concatenate([np.arange(8), rng.integers(0, 8, 4096 - 8)])
+    w = (g.array[codes] * 2.0 ** -6).astype(np.float32) * np.where(rng.random(4096) < 0.5, -1, 1).astype(np.float32)
+    res, packed = F.fp4_search_format(dev(w.reshape(1, -1)))
+    r = F.search_results_host(res)[0]
+    assert (r.e, r.m, r.clip_index, r.mse) == (fmt[0], fmt[1], 99, 0.0)
+
+
+def test_search_full_size_one_tensor():
+    """Full 4096x4096 heavy-tailed tensors (2 of them on the GPU); the first is checked
+    against the oracle over all 300 candidates."""
+    say("search full")
+    ws = np.stack([synth.search_tensor(t).reshape(-1) for t in range(2)])
+    res, packed = F.fp4_search_format(dev(ws))
+    g = F.search_results_host(res)[0]
+    rec, p, mse = O.search_tensor(ws[0])
+    assert (g.e, g.m, g.clip_index) == (rec.e, rec.m, rec.clip_index)
+    assert g.mse == rec.mse and g.mse_runner_up == rec.mse_runner_up
+    assert np.array_equal(host(packed)[0], p)
+
+
+# ---------------------------------------------------------------- determinism -----
+def test_repeat_runs_identical():
+    x = synth.activations(3, 1, 256, 1024, outlier_frac=0.01)
+    w = synth.weight(3, 1, 512, 1024)
+    fe2 = F.grid_minifloat(2, 1)
+    xt, wt = dev(x, torch.bfloat16), dev(w)
+    outs = []
+    for _ in range(2):
+        c = F.fp4_calibrate(xt, "column", first_rows=128)
+        k, a, wp, ws = F.fp4_preshift_weights(wt, c, fe2, fe2, F.gran("row"))
+        ap, _ = F.fp4_quantize_pack(xt, fe2, F.gran("tensor"), tensor_scale=a, col_shift=k)
+        y = F.fp4_gemm(ap, wp, ws, fe2, F.gran("row"), K=1024, a_grid=fe2, a_scale=a)
+        outs.append([host(t).tobytes() for t in (c, k, a, wp, ws, ap, y.view(torch.int16))])
+    assert outs[0] == outs[1]
