@@ -121,7 +121,7 @@ const char* fp4_last_error(void) { return g_err; }
 
 fp4_status fp4_calibrate(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ld, int32_t reduce,
                          int32_t group, int64_t first_rows, float* amax_out, void* stream) {
-    if (!x || !amax_out) return fail(FP4_ERR_INVALID_ARG, "null pointer");
+    if (!amax_out || (!x && rows != 0 && cols != 0)) return fail(FP4_ERR_INVALID_ARG, "null pointer");
     if (x_dtype != FP4_F32 && x_dtype != FP4_BF16) return fail(FP4_ERR_INVALID_ARG, "x_dtype must be FP4_F32 or FP4_BF16");
     if (rows < 0 || cols < 0 || ld < cols) return fail(FP4_ERR_INVALID_ARG, "bad sizes rows=%lld cols=%lld ld=%lld",
                                                        (long long)rows, (long long)cols, (long long)ld);
@@ -143,7 +143,8 @@ fp4_status fp4_calibrate(const void* x, int32_t x_dtype, int64_t rows, int64_t c
 fp4_status fp4_quantize_pack(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx, fp4_grid grid,
                              fp4_gran gran, const float* amax_in, const float* tensor_scale, const int8_t* col_shift,
                              uint8_t* packed, int64_t ldp, void* scales_out, void* stream) {
-    if (!x || !packed) return fail(FP4_ERR_INVALID_ARG, "null pointer");
+    const bool empty = rows == 0 || cols == 0;
+    if ((!x || !packed) && !empty) return fail(FP4_ERR_INVALID_ARG, "null pointer");
     if (x_dtype != FP4_F32 && x_dtype != FP4_BF16) return fail(FP4_ERR_INVALID_ARG, "x_dtype must be FP4_F32 or FP4_BF16");
     if (rows < 0 || cols < 0 || (cols & 1) || ldx < cols || ldp < cols / 2)
         return fail(FP4_ERR_INVALID_ARG, "bad sizes (cols must be even, ldx >= cols, ldp >= cols/2)");
@@ -156,6 +157,7 @@ fp4_status fp4_quantize_pack(const void* x, int32_t x_dtype, int64_t rows, int64
     if (tensor_scale && scales_out && (const void*)tensor_scale == scales_out)
         return fail(FP4_ERR_INVALID_ARG, "tensor_scale and scales_out must not alias");
     if (!aligned16(x) || !aligned16(packed)) return fail(FP4_ERR_ALIGNMENT, "x and packed must be 16-byte aligned");
+    if (empty && gran.mode != FP4_SCALE_TENSOR) return ok();  // nothing to quantize, no scale unit
     int esz = x_dtype == FP4_BF16 ? 2 : 4;
     QuantParams p{};
     p.x = x;
@@ -196,8 +198,9 @@ fp4_status fp4_quantize_pack(const void* x, int32_t x_dtype, int64_t rows, int64
 
 fp4_status fp4_dequantize(const uint8_t* packed, int64_t rows, int64_t cols, int64_t ldp, fp4_grid grid, fp4_gran gran,
                           const void* scales, const int8_t* col_shift, float* out, int64_t ldo, void* stream) {
-    if (!packed || !scales || !out) return fail(FP4_ERR_INVALID_ARG, "null pointer");
     if (rows < 0 || cols < 0 || (cols & 1) || ldp < cols / 2 || ldo < cols) return fail(FP4_ERR_INVALID_ARG, "bad sizes");
+    if (rows == 0 || cols == 0) return ok();
+    if (!packed || !scales || !out) return fail(FP4_ERR_INVALID_ARG, "null pointer");
     QGrid q;
     fp4_status st = make_grid(grid, &q);
     if (st) return st;
@@ -281,8 +284,9 @@ fp4_status fp4_search_format(const float* w, int64_t ntensors, int64_t numel, co
 
 fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
     if (!d) return fail(FP4_ERR_INVALID_ARG, "null descriptor");
-    if (!d->a || !d->w || !d->w_scales || !d->y) return fail(FP4_ERR_INVALID_ARG, "null pointer");
     if (d->M < 0 || d->N < 0 || d->K <= 0 || (d->K & 1)) return fail(FP4_ERR_INVALID_ARG, "bad sizes");
+    if (d->M == 0 || d->N == 0) return ok();  // empty output: nothing to do
+    if (!d->a || !d->w || !d->w_scales || !d->y) return fail(FP4_ERR_INVALID_ARG, "null pointer");
     if (d->ldw < d->K / 2 || d->ldy < d->N) return fail(FP4_ERR_INVALID_ARG, "bad leading dimensions");
     if (d->y_dtype != FP4_BF16 && d->y_dtype != FP4_F32) return fail(FP4_ERR_INVALID_ARG, "y_dtype must be BF16 or F32");
     if (d->reserved0 || d->reserved1) return fail(FP4_ERR_INVALID_ARG, "reserved fields must be 0");

@@ -97,7 +97,7 @@ def test_quantize_bit_pattern_sweep(fmt):
     u = (np.arange(1 << 22, dtype=np.uint64) * 1021 + 12345) % (1 << 32)
     x = u.astype(np.uint32).view(np.float32)
     x = x[np.isfinite(x)]
-    x = x[: (x.size // 16) * 16].reshape(-1, 1024)
+    x = x[: (x.size // 1024) * 1024].reshape(-1, 1024)
     og, fg = grids(fmt)
     one = torch.ones(1, dtype=torch.float32, device=DEV)
     gp, _ = F.fp4_quantize_pack(dev(x), fg, F.gran("tensor"), tensor_scale=one)
