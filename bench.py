@@ -1,0 +1,450 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP4 quantize + quantized-GEMM hot path on one MI355X.
+
+Headline line: the LLaMA-7B decode workload -- weight 11008x4096 (N(0, 0.02) fp32)
+quantized to E2M1 with fp16 scales per 128 along K (calibration fused), then the W4A16
+decode GEMV at M = 1, 4 and 16 (bf16 activations, bf16 output).  One step = one weight
+quantize + the three GEMVs; value = algorithmic HBM bytes of the step / step time.
+Inputs are resident in HBM before the timed region; weight copies rotate (2 fp32
+copies, 16 packed copies) so no step reads data the 256 MB Infinity Cache still holds
+from the previous step.  The K timed steps run as one captured HIP graph (launch
+overhead excluded; the graph's outputs are checked against an eager run).
+
+Also measured in the same run, each against its own roofline (the "kernels" list):
+the 2048x4096x4096 calibration + pre-shift + W4A4 GEMM, the LLaMA-13B prefill layer
+(QKV / up / gate / down W4A4 GEMMs with pre-shifted E2M1, and the NF4 repeat), and the
+format/clip search over 32 heavy-tailed 4096x4096 tensors.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--main-only]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP4 quantize GB/s + W4A16/W4A4 GEMM TFLOP/s, % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP4_PEAK_TFLOPS = 10100.0      # dense FP4 MFMA
+F16_PEAK_TFLOPS = 2500.0       # dense f16/bf16 MFMA
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12  # lane-instructions/s: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--main-only", action="store_true", help="only the headline decode workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", choices=["decode", "quantize", "all"], default=None,
+                    help="short run for rocprofv3: a few eager launches, no JSON line")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- timing
+def graph_time(torch, fn, iters: int, reps: int = 3) -> float:
+    """Seconds per iteration of fn(i), i < iters, captured into one HIP graph and
+    replayed; events are recorded on the stream the kernels run on."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(iters):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        st = torch.cuda.current_stream()
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3 / iters)
+    return best
+
+
+def roofline_entry(name, bound, achieved, peak, unit, seconds, work, work_unit, traffic=None, **extra):
+    d = {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "us_per_launch": round(seconds * 1e6, 3), "work_per_launch": work,
+         "work_unit": work_unit, "traffic": traffic}
+    d.update(extra)
+    return d
+
+
+# ----------------------------------------------------------------------------- inputs
+def gen_normal(torch, shape, std, seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32) * std
+
+
+def gen_activations(torch, rows, cols, seed, outlier_frac=0.01, gain=50.0):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.randn((rows, cols), generator=g, device="cuda", dtype=torch.float32)
+    n_out = int(round(outlier_frac * cols))
+    if n_out:
+        idx = torch.randperm(cols, generator=g, device="cuda")[:n_out]
+        x[:, idx] *= gain
+    return x.to(torch.bfloat16)
+
+
+def gen_heavy_tail(torch, shape, seed, std=0.02, p_tail=0.05):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    z = torch.randn(shape, generator=g, device="cuda")
+    chi = sum(torch.randn(shape, generator=g, device="cuda") ** 2 for _ in range(4))
+    t4 = torch.randn(shape, generator=g, device="cuda") / torch.sqrt(chi / 4)
+    sel = torch.rand(shape, generator=g, device="cuda") < p_tail
+    return torch.where(sel, t4, z) * std
+
+
+# ----------------------------------------------------------------------------- traffic
+def traffic_for(kernel_file: str, key: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel source
+    is unchanged since they were taken (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(key)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "bit_floating_point_amd", "csrc", kernel_file)
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != h:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- decode
+DEC_N, DEC_K, DEC_G = 11008, 4096, 128
+DEC_MS = (1, 4, 16)
+
+
+def decode_bytes():
+    q = DEC_N * DEC_K * 4 + DEC_N * DEC_K // 2 + DEC_N * (DEC_K // DEC_G) * 2
+    gemv = {m: DEC_N * DEC_K // 2 + DEC_N * (DEC_K // DEC_G) * 2 + m * DEC_K * 2 + m * DEC_N * 2 for m in DEC_MS}
+    return q, gemv
+
+
+def bench_decode(torch, F, steps, warmup):
+    fe2 = F.grid_minifloat(2, 1)
+    g = F.gran("group", DEC_G, "f16")
+    NW, NP = 2, 16
+    W = [gen_normal(torch, (DEC_N, DEC_K), 0.02, 100 + i) for i in range(NW)]
+    P = [torch.empty((DEC_N, DEC_K // 2), dtype=torch.uint8, device="cuda") for _ in range(NP)]
+    S = [torch.empty(DEC_N * (DEC_K // DEC_G), dtype=torch.float16, device="cuda") for _ in range(NP)]
+    for i in range(NP):
+        F.fp4_quantize_pack(W[i % NW], fe2, g, packed=P[i], scales=S[i])
+    X = {m: gen_activations(torch, m, DEC_K, 200 + m, outlier_frac=0.0) for m in DEC_MS}
+    Y = {m: torch.empty((m, DEC_N), dtype=torch.bfloat16, device="cuda") for m in DEC_MS}
+
+    def step(i):
+        F.fp4_quantize_pack(W[i % NW], fe2, g, packed=P[i % NP], scales=S[i % NP])
+        j = (i + NP // 2) % NP
+        for m in DEC_MS:
+            F.fp4_gemm(X[m], P[j], S[j], fe2, g, y=Y[m])
+
+    qb, gb = decode_bytes()
+    step_bytes = qb + sum(gb.values())
+    # `warmup` untimed steps, then exactly `steps` steps replayed as one captured graph
+    # between two synchronisations; events on the stream the kernels run on
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(warmup):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            step(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    graph.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    t_step = e0.elapsed_time(e1) * 1e-3 / steps
+    # graph outputs equal an eager call on the same inputs
+    j = (steps - 1 + NP // 2) % NP
+    for m in DEC_MS:
+        ref = F.fp4_gemm(X[m], P[j], S[j], fe2, g)
+        assert torch.equal(ref, Y[m]), "graph replay differs from eager run"
+    # per-kernel launch durations
+    t_q = graph_time(torch, lambda i: F.fp4_quantize_pack(W[i % NW], fe2, g, packed=P[i % NP], scales=S[i % NP]), 32)
+    t_g = {m: graph_time(torch, lambda i, m=m: F.fp4_gemm(X[m], P[i % NP], S[i % NP], fe2, g, y=Y[m]), 64)
+           for m in DEC_MS}
+    kernels = [roofline_entry("quantize_pack f32->E2M1 g128 (11008x4096)", "hbm", qb / t_q / 1e9, HBM_PEAK_GBS,
+                              "GB/s", t_q, qb, "bytes", traffic_for("quant.hip", "quantize_decode"))]
+    for m in DEC_MS:
+        flops = 2 * m * DEC_N * DEC_K
+        kernels.append(roofline_entry(f"w4a16 gemv M={m} (11008x4096, g128)", "hbm", gb[m] / t_g[m] / 1e9,
+                                      HBM_PEAK_GBS, "GB/s", t_g[m], gb[m], "bytes",
+                                      traffic_for("gemm_w4a16.hip", f"gemv_m{m}"),
+                                      tflops=round(flops / t_g[m] / 1e12, 3)))
+    del W, P, S
+    torch.cuda.empty_cache()
+    return t_step, step_bytes, kernels
+
+
+# ----------------------------------------------------------------------------- extras
+def bench_preshift_w4a4(torch, F):
+    M, N, K = 2048, 4096, 4096
+    fe2 = F.grid_minifloat(2, 1)
+    NX = 16
+    Xs = [gen_activations(torch, M, K, 300 + i) for i in range(NX)]
+    Ws = [gen_normal(torch, (N, K), 0.02, 400 + i) for i in range(4)]
+    chan = F.fp4_calibrate(Xs[0], "column", first_rows=128)
+    k, a, wp, ws = F.fp4_preshift_weights(Ws[0], chan, fe2, fe2, F.gran("row"))
+    ap, _ = F.fp4_quantize_pack(Xs[0], fe2, F.gran("tensor"), tensor_scale=a, col_shift=k)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    out = []
+    t = graph_time(torch, lambda i: F.fp4_calibrate(Xs[i % NX], "column", first_rows=128, out=chan), 32)
+    b = 128 * K * 2 + K * 4
+    out.append(roofline_entry("calibrate column amax (128 of 2048 tokens x 4096, bf16)", "hbm", b / t / 1e9,
+                              HBM_PEAK_GBS, "GB/s", t, b, "bytes"))
+    packs = [torch.empty_like(wp) for _ in range(4)]
+    scs = [torch.empty_like(ws) for _ in range(4)]
+    ks = [torch.empty_like(k) for _ in range(4)]
+    As = [torch.empty_like(a) for _ in range(4)]
+
+    def pre(i):
+        F.fp4_preshift_weights(Ws[i % 4], chan, fe2, fe2, F.gran("row"), shift=ks[i % 4], act_scale=As[i % 4],
+                               packed=packs[i % 4], scales=scs[i % 4])
+    t = graph_time(torch, pre, 16)
+    b = N * K * 4 + N * K // 2 + N * 4 + K * 4 + K + 4
+    out.append(roofline_entry("preshift + weight quantize E2M1 per-row (4096x4096 f32)", "hbm", b / t / 1e9,
+                              HBM_PEAK_GBS, "GB/s", t, b, "bytes"))
+    aps = [torch.empty_like(ap) for _ in range(NX)]
+    t = graph_time(torch, lambda i: F.fp4_quantize_pack(Xs[i % NX], fe2, F.gran("tensor"), tensor_scale=a,
+                                                        col_shift=k, packed=aps[i % NX]), 32)
+    b = M * K * 2 + M * K // 2 + K
+    out.append(roofline_entry("activation quantize E2M1 + pre-shift (2048x4096 bf16)", "hbm", b / t / 1e9,
+                              HBM_PEAK_GBS, "GB/s", t, b, "bytes", traffic_for("quant.hip", "quantize_act")))
+    t = graph_time(torch, lambda i: F.fp4_gemm(ap, wp, ws, fe2, F.gran("row"), K=K, a_grid=fe2, a_scale=a, y=y), 20)
+    fl = 2 * M * N * K
+    out.append(roofline_entry("w4a4 E2M1 GEMM 2048x4096x4096", "mfma", fl / t / 1e12, FP4_PEAK_TFLOPS, "TFLOP/s",
+                              t, fl, "flop", traffic_for("gemm_w4a4.hip", "w4a4_c3")))
+    del Xs, Ws
+    torch.cuda.empty_cache()
+    return out
+
+
+PREFILL = {"qkv": (15360, 5120), "up": (13824, 5120), "gate": (13824, 5120), "down": (5120, 13824)}
+
+
+def bench_prefill(torch, F):
+    T = 4096
+    fe2, fnf4 = F.grid_minifloat(2, 1), F.grid_nf4()
+    X1 = gen_activations(torch, T, 5120, 500)
+    X2 = gen_activations(torch, T, 13824, 501)
+    c1 = F.fp4_calibrate(X1, "column", first_rows=128)
+    c2 = F.fp4_calibrate(X2, "column", first_rows=128)
+    out = []
+    tot_fl, tot_t, tot_t_nf4 = 0, 0.0, 0.0
+    qa = {}
+    for name, (n, k) in PREFILL.items():
+        w = gen_normal(torch, (n, k), 0.02, 600 + len(qa))
+        chan = c2 if name == "down" else c1
+        X = X2 if name == "down" else X1
+        kk, a, wp, ws = F.fp4_preshift_weights(w, chan, fe2, fe2, F.gran("row"))
+        ap, _ = F.fp4_quantize_pack(X, fe2, F.gran("tensor"), tensor_scale=a, col_shift=kk)
+        y = torch.empty((T, n), dtype=torch.bfloat16, device="cuda")
+        t = graph_time(torch, lambda i: F.fp4_gemm(ap, wp, ws, fe2, F.gran("row"), K=k, a_grid=fe2, a_scale=a, y=y), 5)
+        fl = 2 * T * n * k
+        tot_fl += fl
+        tot_t += t
+        out.append(roofline_entry(f"w4a4 E2M1 GEMM {name} {T}x{n}x{k}", "mfma", fl / t / 1e12, FP4_PEAK_TFLOPS,
+                                  "TFLOP/s", t, fl, "flop"))
+        kn, an, wpn, wsn = F.fp4_preshift_weights(w, chan, fe2, fnf4, F.gran("group", 64))
+        apn, _ = F.fp4_quantize_pack(X, fe2, F.gran("tensor"), tensor_scale=an, col_shift=kn)
+        t = graph_time(torch, lambda i: F.fp4_gemm(apn, wpn, wsn, fnf4, F.gran("group", 64), K=k, a_grid=fe2,
+                                                   a_scale=an, y=y), 3)
+        tot_t_nf4 += t
+        out.append(roofline_entry(f"nf4 x E2M1 GEMM (f16 MFMA) {name} {T}x{n}x{k}", "mfma", fl / t / 1e12,
+                                  F16_PEAK_TFLOPS, "TFLOP/s", t, fl, "flop"))
+        if name in ("qkv", "down"):
+            xb = T * k * 2 + T * k // 2 + k
+            t = graph_time(torch, lambda i: F.fp4_quantize_pack(X, fe2, F.gran("tensor"), tensor_scale=a,
+                                                                col_shift=kk, packed=ap), 8)
+            out.append(roofline_entry(f"activation quantize E2M1 + pre-shift ({T}x{k} bf16)", "hbm",
+                                      xb / t / 1e9, HBM_PEAK_GBS, "GB/s", t, xb, "bytes"))
+            wb = n * k * 4 + n * k // 2 + n * 4 + k * 5 + 4
+            t = graph_time(torch, lambda i: F.fp4_preshift_weights(w, chan, fe2, fe2, F.gran("row"), shift=kk,
+                                                                   act_scale=a, packed=wp, scales=ws), 3)
+            out.append(roofline_entry(f"preshift + weight quantize E2M1 per-row ({n}x{k} f32)", "hbm",
+                                      wb / t / 1e9, HBM_PEAK_GBS, "GB/s", t, wb, "bytes"))
+        qa[name] = True
+        del w, wp, wpn, y
+        torch.cuda.empty_cache()
+    out.append(roofline_entry("prefill layer: 4 W4A4 E2M1 GEMMs (QKV, up, gate, down)", "mfma",
+                              tot_fl / tot_t / 1e12, FP4_PEAK_TFLOPS, "TFLOP/s", tot_t, tot_fl, "flop"))
+    out.append(roofline_entry("prefill layer: 4 NF4 GEMMs (QKV, up, gate, down)", "mfma",
+                              tot_fl / tot_t_nf4 / 1e12, F16_PEAK_TFLOPS, "TFLOP/s", tot_t_nf4, tot_fl, "flop"))
+    return out
+
+
+# VALU instructions per (element, candidate) in the search's inner loop, counted from the
+# gfx950 assembly of search_eval_kernel (E2M1 / E1M2 / E3M0 averaged)
+SEARCH_VALU_PER_EVAL = 17.0
+
+
+def bench_search(torch, F):
+    T, numel = 32, 4096 * 4096
+    w = torch.empty((T, numel), dtype=torch.float32, device="cuda")
+    for t in range(T):
+        w[t] = gen_heavy_tail(torch, (numel,), 700 + t)
+    res, packed = F.fp4_search_format(w)
+    torch.cuda.synchronize()
+    reps = 2
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        F.fp4_search_format(w)
+    e1.record()
+    e1.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    evals = T * numel * 3 * 100
+    ops = evals * SEARCH_VALU_PER_EVAL
+    del w, packed
+    torch.cuda.empty_cache()
+    return [roofline_entry("format/clip search 32 x 4096x4096 (3 formats x 100 clips)", "alu", ops / t / 1e12,
+                           VALU_PEAK_TOPS, "TOP/s", t, evals, "element-candidate evaluations",
+                           evals_per_s=evals / t)]
+
+
+# ----------------------------------------------------------------------------- CPU oracle
+def cpu_baseline(target_s=12.0):
+    """The CPU oracle (as it is) on a bounded sample of the decode step: the first R
+    weight rows quantized (E2M1, fp16 group scales) and the three GEMVs on them."""
+    import numpy as np
+    import oracle as O
+    import synth
+    O.build()
+    e2 = O.minifloat(2, 1)
+
+    def run(rows):
+        w = synth.weight(2, 0, rows, DEC_K)
+        xs = {m: synth.activations(2, m, m, DEC_K) for m in DEC_MS}
+        t0 = time.perf_counter()
+        p, s = O.quantize_pack(w, e2, "group", DEC_G, "f16")
+        for m in DEC_MS:
+            O.gemm_w4a16(xs[m], p, e2, "group", s, group=DEC_G)
+        dt = time.perf_counter() - t0
+        b = rows * DEC_K * 4 + rows * DEC_K // 2 + rows * (DEC_K // DEC_G) * 2
+        b += sum(rows * DEC_K // 2 + rows * (DEC_K // DEC_G) * 2 + m * DEC_K * 2 + m * rows * 2 for m in DEC_MS)
+        return dt, b
+
+    dt, _ = run(128)
+    rows = int(min(DEC_N, max(128, 128 * target_s / max(dt, 1e-3))))
+    dt, b = run(rows)
+    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"decode step on the first {rows} of 11008 weight rows (quantize E2M1 g128 + GEMV M=1,4,16), "
+                      f"{dt:.1f} s"}
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is per-GPU and shards "
+              "without collectives, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_floating_point_amd as F
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.init()
+    if args.profile:
+        profile_run(torch, F, args.profile)
+        return
+    log("decode workload ...")
+    t_step, step_bytes, kernels = bench_decode(torch, F, args.steps, args.warmup)
+    if not args.main_only:
+        log("pre-shift + W4A4 2048x4096x4096 ...")
+        kernels += bench_preshift_w4a4(torch, F)
+        log("LLaMA-13B prefill layer ...")
+        kernels += bench_prefill(torch, F)
+        log("format search ...")
+        kernels += bench_search(torch, F)
+    dominant = max(kernels[:4], key=lambda d: d["us_per_launch"])
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+    line = {
+        "metric": METRIC,
+        "value": round(step_bytes / t_step / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4-e2m1 weights x bf16 activations, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "LLaMA-7B MLP linear 11008x4096: E2M1 g128 fp16-scale weight quantize + "
+                               "W4A16 decode GEMV at M=1,4,16 (bf16)",
+                   "N": DEC_N, "K": DEC_K, "group": DEC_G, "M": list(DEC_MS), "step_bytes": step_bytes},
+        "roofline": {k: dominant[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    line["roofline"]["kernel"] = dominant["kernel"]
+    print(json.dumps(line), flush=True)
+
+
+def profile_run(torch, F, what):
+    """A few eager launches of the chosen kernels plus a plain 256 MiB device copy (the
+    reference for scaling HBM byte counters)."""
+    fe2 = F.grid_minifloat(2, 1)
+    src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    if what in ("quantize", "decode", "all"):
+        W = gen_normal(torch, (DEC_N, DEC_K), 0.02, 100)
+        g = F.gran("group", DEC_G, "f16")
+        for _ in range(3):
+            p, s = F.fp4_quantize_pack(W, fe2, g)
+        if what in ("decode", "all"):
+            for m in DEC_MS:
+                x = gen_activations(torch, m, DEC_K, 200 + m, outlier_frac=0.0)
+                for _ in range(3):
+                    F.fp4_gemm(x, p, s, fe2, g)
+    if what == "all":
+        M, N, K = 2048, 4096, 4096
+        X = gen_activations(torch, M, K, 300)
+        Wt = gen_normal(torch, (N, K), 0.02, 400)
+        chan = F.fp4_calibrate(X, "column", first_rows=128)
+        k, a, wp, ws = F.fp4_preshift_weights(Wt, chan, fe2, fe2, F.gran("row"))
+        for _ in range(3):
+            ap, _ = F.fp4_quantize_pack(X, fe2, F.gran("tensor"), tensor_scale=a, col_shift=k)
+        for _ in range(3):
+            F.fp4_gemm(ap, wp, ws, fe2, F.gran("row"), K=K, a_grid=fe2, a_scale=a)
+    torch.cuda.synchronize()
+    log("profile run done")
+
+
+if __name__ == "__main__":
+    main()

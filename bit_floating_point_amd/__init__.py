@@ -136,14 +136,19 @@ def fp4_dequantize(packed: torch.Tensor, grid: L.fp4_grid, g: L.fp4_gran, scales
 
 
 def fp4_preshift_weights(w: torch.Tensor, chan_amax: torch.Tensor, act_grid: L.fp4_grid,
-                         w_grid: L.fp4_grid, w_gran: L.fp4_gran):
+                         w_grid: L.fp4_grid, w_gran: L.fp4_gran, shift=None, act_scale=None, packed=None,
+                         scales=None):
     n, k = w.shape
     dev = w.device
-    shift = torch.empty(k, dtype=torch.int8, device=dev)
-    act_scale = torch.empty(1, dtype=torch.float32, device=dev)
-    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
-    sd = torch.float16 if w_gran.scale_dtype == FP4_F16 else torch.float32
-    scales = torch.empty(_units(w_gran, n, k), dtype=sd, device=dev)
+    if shift is None:
+        shift = torch.empty(k, dtype=torch.int8, device=dev)
+    if act_scale is None:
+        act_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    if packed is None:
+        packed = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        sd = torch.float16 if w_gran.scale_dtype == FP4_F16 else torch.float32
+        scales = torch.empty(_units(w_gran, n, k), dtype=sd, device=dev)
     L.check(L.lib().fp4_preshift_weights(_ptr(w), n, k, _ld(w), _ptr(chan_amax), act_grid, w_grid, w_gran,
                                          _ptr(shift), _ptr(act_scale), _ptr(packed), _ld(packed),
                                          _ptr(scales), _stream(dev)), "fp4_preshift_weights")
