@@ -156,7 +156,8 @@ fp4_status fp4_quantize_pack(const void* x, int32_t x_dtype, int64_t rows, int64
     if (!scales_out && !tensor_scale) return fail(FP4_ERR_INVALID_ARG, "scales_out may be NULL only with tensor_scale");
     if (tensor_scale && scales_out && (const void*)tensor_scale == scales_out)
         return fail(FP4_ERR_INVALID_ARG, "tensor_scale and scales_out must not alias");
-    if (!aligned16(x) || !aligned16(packed)) return fail(FP4_ERR_ALIGNMENT, "x and packed must be 16-byte aligned");
+    if (!aligned16(x) || !aligned16(packed) || !aligned16(col_shift))
+        return fail(FP4_ERR_ALIGNMENT, "x, packed and col_shift must be 16-byte aligned");
     if (empty && gran.mode != FP4_SCALE_TENSOR) return ok();  // nothing to quantize, no scale unit
     int esz = x_dtype == FP4_BF16 ? 2 : 4;
     QuantParams p{};
@@ -222,7 +223,8 @@ fp4_status fp4_preshift_weights(const float* w, int64_t n, int64_t k, int64_t ld
     if ((st = make_grid(w_grid, &qw))) return st;
     if ((st = check_gran(w_gran, k))) return st;
     if (w_gran.mode == FP4_SCALE_TENSOR) return fail(FP4_ERR_UNSUPPORTED, "pre-shifted weights need ROW or GROUP scales");
-    if (!aligned16(w) || !aligned16(w_packed)) return fail(FP4_ERR_ALIGNMENT, "w and w_packed must be 16-byte aligned");
+    if (!aligned16(w) || !aligned16(w_packed) || !aligned16(shift_out))
+        return fail(FP4_ERR_ALIGNMENT, "w, w_packed and shift_out must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_preshift_factors(chan_amax, k, qa.qmax, shift_out, act_scale_out, s);
     if (e != hipSuccess) return hip_status(e, "fp4_preshift_weights/factors");

@@ -23,8 +23,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kW16Waves = 4;
 constexpr int kBatch = 4;  // K chunks in flight per wavefront
 
-struct U4 { uint32_t v[4]; };
-
 __device__ __forceinline__ bf16x8 decode_e2m1_bf16(uint32_t w) {
     // byte b of w holds codes 2b (low nibble) and 2b+1
     uint32_t o[4];
@@ -35,122 +33,140 @@ __device__ __forceinline__ bf16x8 decode_e2m1_bf16(uint32_t w) {
     return __builtin_bit_cast(bf16x8, o);
 }
 
-template <int MODE>  // 0 tensor, 1 row, 2 group
+__device__ __forceinline__ float load_scale(const GemmParams& p, int64_t idx) {
+    return p.w_scale_f16 ? __half2float(reinterpret_cast<const __half*>(p.w_scales)[idx])
+                         : reinterpret_cast<const float*>(p.w_scales)[idx];
+}
+
+// T = 16-column tiles per wavefront (the activation registers are reused across them)
+template <int MODE, int T>  // MODE 0 tensor, 1 row, 2 group
 __global__ void __launch_bounds__(256) w4a16_mfma_kernel(GemmParams p) {
-    __shared__ f32x4 part[kW16Waves - 1][64];
+    __shared__ f32x4 part[kW16Waves - 1][T][64];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * T;
     const int64_t m0 = (int64_t)blockIdx.y * 16;
-    const int64_t n = n0 + (lane & 15);
-    const int q = lane >> 4;
-    const int64_t m = m0 + (lane & 15);
-    const bool n_ok = n < p.N;
+    const int64_t m = m0 + r16;
     const bool m_ok = m < p.M;
 
-    const int64_t nchunks = p.K / 128;
-    const int64_t c_begin = nchunks * wave / kW16Waves;
-    const int64_t c_end = nchunks * (wave + 1) / kW16Waves;
-    const int chunks_per_group = MODE == 2 ? p.w_group / 128 : 1;
+    const int nchunks = (int)(p.K / 128);
+    const int c_begin = nchunks * wave / kW16Waves;
+    const int c_end = nchunks * (wave + 1) / kW16Waves;
+    const int cpg = MODE == 2 ? p.w_group / 128 : 1;
     const int64_t ngroups = MODE == 2 ? p.K / p.w_group : 1;
 
-    const uint8_t* wrow = p.w + (n_ok ? n : 0) * p.ldw + q * 16;
+    int64_t n[T];
+    bool n_ok[T];
+    const uint8_t* wrow[T];
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+        n[t] = n0 + t * 16 + r16;
+        n_ok[t] = n[t] < p.N;
+        wrow[t] = p.w + (n_ok[t] ? n[t] : 0) * p.ldw + q * 16;
+    }
     const uint16_t* xrow = reinterpret_cast<const uint16_t*>(p.a) + (m_ok ? m : 0) * p.lda + q * 32;
 
-    f32x4 total = {0.f, 0.f, 0.f, 0.f};
-    f32x4 gacc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 total[T], gacc[T];
+#pragma unroll
+    for (int t = 0; t < T; t++) total[t] = gacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t c0 = c_begin; c0 < c_end; c0 += kBatch) {
-        uint4 wv[kBatch];
+    for (int c0 = c_begin; c0 < c_end; c0 += kBatch) {
+        // issue every load of the batch before any arithmetic: weights, group scales and
+        // activations are all independent of the MFMA chain
+        uint4 wv[kBatch][T];
         uint4 xv[kBatch][4];
+        float sc[kBatch][T];
 #pragma unroll
         for (int b = 0; b < kBatch; b++) {
-            int64_t c = c0 + b;
-            if (c < c_end && n_ok) wv[b] = *reinterpret_cast<const uint4*>(wrow + c * 64);
-            else wv[b] = make_uint4(0, 0, 0, 0);
+            const int c = c0 + b;
+            const bool valid = c < c_end;
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                if (c < c_end && m_ok) xv[b][j] = *reinterpret_cast<const uint4*>(xrow + c * 128 + j * 8);
-                else xv[b][j] = make_uint4(0, 0, 0, 0);
+            for (int t = 0; t < T; t++) {
+                wv[b][t] = (valid && n_ok[t]) ? *reinterpret_cast<const uint4*>(wrow[t] + (int64_t)c * 64)
+                                              : make_uint4(0, 0, 0, 0);
+                sc[b][t] = (MODE == 2 && valid && n_ok[t]) ? load_scale(p, n[t] * ngroups + c / cpg) : 0.0f;
             }
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                xv[b][j] = (valid && m_ok) ? *reinterpret_cast<const uint4*>(xrow + (int64_t)c * 128 + j * 8)
+                                           : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int b = 0; b < kBatch; b++) {
-            int64_t c = c0 + b;
+            const int c = c0 + b;
             if (c >= c_end) break;
-            uint32_t wd[4] = {wv[b].x, wv[b].y, wv[b].z, wv[b].w};
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                bf16x8 bop = decode_e2m1_bf16(wd[j]);
-                bf16x8 aop = __builtin_bit_cast(bf16x8, xv[b][j]);
-                gacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, gacc, 0, 0, 0);
+            for (int t = 0; t < T; t++) {
+                const uint32_t wd[4] = {wv[b][t].x, wv[b][t].y, wv[b][t].z, wv[b][t].w};
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    gacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[b][j]),
+                                                                      decode_e2m1_bf16(wd[j]), gacc[t], 0, 0, 0);
             }
-            if (MODE == 2) {
-                if ((c + 1) % chunks_per_group == 0) {
-                    int64_t g = c / chunks_per_group;
-                    float s = 0.0f;
-                    if (n_ok) s = p.w_scale_f16 ? __half2float(reinterpret_cast<const __half*>(p.w_scales)[n * ngroups + g])
-                                                : reinterpret_cast<const float*>(p.w_scales)[n * ngroups + g];
+            if (MODE == 2 && (c + 1) % cpg == 0) {
 #pragma unroll
-                    for (int i = 0; i < 4; i++) total[i] = __builtin_fmaf(gacc[i], s, total[i]);
-                    gacc = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < T; t++) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) total[t][i] = __builtin_fmaf(gacc[t][i], sc[b][t], total[t][i]);
+                    gacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
             }
         }
     }
-    if (MODE == 2 && c_end > c_begin && (c_end % chunks_per_group) != 0) {
-        // this wavefront's range ends inside a group: scale its share of that group
-        int64_t g = (c_end - 1) / chunks_per_group;
-        float s = 0.0f;
-        if (n_ok) s = p.w_scale_f16 ? __half2float(reinterpret_cast<const __half*>(p.w_scales)[n * ngroups + g])
-                                    : reinterpret_cast<const float*>(p.w_scales)[n * ngroups + g];
 #pragma unroll
-        for (int i = 0; i < 4; i++) total[i] = __builtin_fmaf(gacc[i], s, total[i]);
-    }
-    if (MODE != 2) {
-        float s = 0.0f;
-        if (n_ok) {
-            int64_t u = MODE == 1 ? n : 0;
-            s = p.w_scale_f16 ? __half2float(reinterpret_cast<const __half*>(p.w_scales)[u])
-                              : reinterpret_cast<const float*>(p.w_scales)[u];
+    for (int t = 0; t < T; t++) {
+        if (MODE == 2 && c_end > c_begin && (c_end % cpg) != 0) {
+            // this wavefront's range ends inside a group: scale its share of that group
+            float s = n_ok[t] ? load_scale(p, n[t] * ngroups + (c_end - 1) / cpg) : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; i++) total[t][i] = __builtin_fmaf(gacc[t][i], s, total[t][i]);
         }
+        if (MODE != 2) {
+            float s = n_ok[t] ? load_scale(p, MODE == 1 ? n[t] : 0) : 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; i++) total[i] = gacc[i] * s;
+            for (int i = 0; i < 4; i++) total[t][i] = gacc[t][i] * s;
+        }
+        if (wave > 0) part[wave - 1][t][lane] = total[t];
     }
-    if (wave > 0) part[wave - 1][lane] = total;
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
-        for (int w = 0; w < kW16Waves - 1; w++) {
-            f32x4 o = part[w][lane];
+        for (int t = 0; t < T; t++) {
 #pragma unroll
-            for (int i = 0; i < 4; i++) total[i] += o[i];
-        }
-        // D layout of a 16x16 MFMA: lane holds rows 4*(lane/16) + i of column lane%16
-        if (n_ok) {
+            for (int w = 0; w < kW16Waves - 1; w++) {
+                f32x4 o = part[w][t][lane];
+#pragma unroll
+                for (int i = 0; i < 4; i++) total[t][i] += o[i];
+            }
+            // D layout of a 16x16 MFMA: lane holds rows 4*(lane/16) + i of column lane%16
+            if (!n_ok[t]) continue;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 int64_t mm = m0 + 4 * q + i;
                 if (mm < p.M) {
-                    float v = total[i];
-                    if (p.y_bf16) {
-                        __bf16 h = (__bf16)v;
-                        reinterpret_cast<__bf16*>(p.y)[mm * p.ldy + n] = h;
-                    } else {
-                        reinterpret_cast<float*>(p.y)[mm * p.ldy + n] = v;
-                    }
+                    if (p.y_bf16) reinterpret_cast<__bf16*>(p.y)[mm * p.ldy + n[t]] = (__bf16)total[t][i];
+                    else reinterpret_cast<float*>(p.y)[mm * p.ldy + n[t]] = total[t][i];
                 }
             }
         }
     }
 }
 
+template <int T>
+static void launch_w16(const GemmParams& p, hipStream_t s) {
+    dim3 grid((unsigned)((p.N + 16 * T - 1) / (16 * T)), (unsigned)((p.M + 15) / 16));
+    if (p.w_mode == 2) hipLaunchKernelGGL((w4a16_mfma_kernel<2, T>), grid, dim3(256), 0, s, p);
+    else if (p.w_mode == 1) hipLaunchKernelGGL((w4a16_mfma_kernel<1, T>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((w4a16_mfma_kernel<0, T>), grid, dim3(256), 0, s, p);
+}
+
 hipError_t launch_w4a16_mfma(const GemmParams& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
-    dim3 grid((unsigned)((p.N + 15) / 16), (unsigned)((p.M + 15) / 16));
-    if (p.w_mode == 2) hipLaunchKernelGGL(w4a16_mfma_kernel<2>, grid, dim3(256), 0, s, p);
-    else if (p.w_mode == 1) hipLaunchKernelGGL(w4a16_mfma_kernel<1>, grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(w4a16_mfma_kernel<0>, grid, dim3(256), 0, s, p);
+    // small M: one 16-column tile per wavefront keeps the most weight bytes in flight;
+    // larger M: reuse each activation fragment for two weight tiles
+    if (p.M > 8) launch_w16<2>(p, s);
+    else launch_w16<1>(p, s);
     return hipGetLastError();
 }
 

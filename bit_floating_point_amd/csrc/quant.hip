@@ -130,75 +130,158 @@ __device__ __forceinline__ void store_codes(uint8_t* prow, int64_t col, int64_t 
     }
 }
 
-// Apply the optional column shift and the multiplier, producing y = fl32(x * r).
-__device__ __forceinline__ void shift_inputs(const QuantParams& p, int64_t col, float v[8]) {
-    if (p.col_shift && p.shift_sign > 0) {
+// Column shifts of the 8 elements at col (0 beyond the row).
+template <bool VEC>
+__device__ __forceinline__ void load_shift8(const QuantParams& p, int64_t col, int k[8]) {
+    if (VEC && col + 8 <= p.cols) {
+        uint2 w = *reinterpret_cast<const uint2*>(p.col_shift + col);
 #pragma unroll
-        for (int i = 0; i < 8; i++)
-            if (col + i < p.cols) v[i] = ldexpf(v[i], (int)p.col_shift[col + i]);
+        for (int i = 0; i < 4; i++) {
+            k[i] = (int)(int8_t)(w.x >> (8 * i));
+            k[4 + i] = (int)(int8_t)(w.y >> (8 * i));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) k[i] = (col + i < p.cols) ? (int)p.col_shift[col + i] : 0;
     }
 }
 
-__device__ __forceinline__ void scale_values(const QuantParams& p, int64_t col, float r, float v[8]) {
-    if (p.col_shift && p.shift_sign < 0) {
+// Input side of the pre-shift (weights): x' = x * 2^k, exact.
+__device__ __forceinline__ void shift_inputs(float v[8], const int k[8]) {
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            int k = (col + i < p.cols) ? (int)p.col_shift[col + i] : 0;
-            v[i] = v[i] * ldexpf(r, -k);
-        }
+    for (int i = 0; i < 8; i++) v[i] = ldexpf(v[i], k[i]);
+}
+
+// y = fl32(x * r), or fl32(x * (r * 2^-k)) with the activation-side pre-shift.
+__device__ __forceinline__ void scale_values(float v[8], float r, const int* k) {
+    if (k) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] = v[i] * ldexpf(r, -k[i]);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; i++) v[i] = v[i] * r;
     }
 }
 
-// TENSOR and GROUP modes: one workgroup per (row, 2048-column chunk).
-template <bool VEC>
-__global__ void __launch_bounds__(kThreads) quantize_chunk_kernel(QuantParams p, int64_t chunks) {
-    int64_t b = blockIdx.x;
-    int64_t row = b / chunks;
-    int64_t col = (b % chunks) * kChunk + threadIdx.x * 8;
-    const char* rp = reinterpret_cast<const char*>(p.x) + row * p.ldx * (p.x_bf16 ? 2 : 4);
-    float v[8];
-    load8<VEC>(rp, p.x_bf16, col, p.cols, v);
-    shift_inputs(p, col, v);
-    float r;
-    if (p.mode == 0) {
-        float s = p.tensor_scale ? p.tensor_scale[0] : p.tensor_amax[0] / p.g.qmax;
-        r = recip_or_zero(s);
-        if (b == 0 && threadIdx.x == 0 && p.tensor_scale && p.scales_out)
-            reinterpret_cast<float*>(p.scales_out)[0] = s;
-    } else {
-        int lanes = p.group >> 3;
-        int64_t unit = row * (p.cols / p.group) + col / p.group;
-        float amax;
-        if (p.amax_in) {
-            amax = (col < p.cols) ? p.amax_in[unit] : 0.0f;
-        } else {
-            float m = 0.0f;
+__device__ __forceinline__ float max_abs8(const float v[8]) {
+    float m = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
-            amax = group_max(m, lanes);
-        }
-        float s = amax / p.g.qmax;
-        if (p.scale_f16) s = round_f16(s);
-        r = recip_or_zero(s);
-        if (col < p.cols && (threadIdx.x & (lanes - 1)) == 0 && p.scales_out) {
-            if (p.scale_f16) reinterpret_cast<__half*>(p.scales_out)[unit] = __float2half_rn(s);
-            else reinterpret_cast<float*>(p.scales_out)[unit] = s;
-        }
-    }
-    scale_values(p, col, r, v);
-    uint32_t w = pack8(v, p.g);
-    store_codes(p.packed + row * p.ldp, col, p.cols, w, VEC);
+    for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
+    return m;
 }
 
-// ROW mode: one workgroup per row; pass 1 reduces the row max, pass 2 quantizes.
+// TENSOR and GROUP modes.  The (row, 2048-column chunk) units are processed U per
+// workgroup: all U loads are issued before any arithmetic (2 x 16 B per lane in flight
+// for bf16, 4 x 16 B for f32 at U = 2).
+template <bool VEC, int U>
+__global__ void __launch_bounds__(kThreads) quantize_chunk_kernel(QuantParams p, int64_t chunks, int64_t nunits) {
+    const bool has_k = p.col_shift != nullptr;
+    float v[U][8];
+    int k[U][8];
+    int64_t row[U], col[U];
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+        int64_t u = (int64_t)blockIdx.x * U + i;
+        if (u >= nunits) u = nunits - 1;  // duplicate of the last unit: same values, same bytes
+        row[i] = u / chunks;
+        col[i] = (u % chunks) * kChunk + threadIdx.x * 8;
+        const char* rp = reinterpret_cast<const char*>(p.x) + row[i] * p.ldx * (p.x_bf16 ? 2 : 4);
+        load8<VEC>(rp, p.x_bf16, col[i], p.cols, v[i]);
+        if (has_k) load_shift8<VEC>(p, col[i], k[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+        if (has_k && p.shift_sign > 0) shift_inputs(v[i], k[i]);
+        float r;
+        if (p.mode == 0) {
+            float s = p.tensor_scale ? p.tensor_scale[0] : p.tensor_amax[0] / p.g.qmax;
+            r = recip_or_zero(s);
+            if (blockIdx.x == 0 && i == 0 && threadIdx.x == 0 && p.tensor_scale && p.scales_out)
+                reinterpret_cast<float*>(p.scales_out)[0] = s;
+        } else {
+            int lanes = p.group >> 3;
+            int64_t unit = row[i] * (p.cols / p.group) + col[i] / p.group;
+            float amax;
+            if (p.amax_in) amax = (col[i] < p.cols) ? p.amax_in[unit] : 0.0f;
+            else amax = group_max(max_abs8(v[i]), lanes);
+            float s = amax / p.g.qmax;
+            if (p.scale_f16) s = round_f16(s);
+            r = recip_or_zero(s);
+            if (col[i] < p.cols && (threadIdx.x & (lanes - 1)) == 0 && p.scales_out) {
+                if (p.scale_f16) reinterpret_cast<__half*>(p.scales_out)[unit] = __float2half_rn(s);
+                else reinterpret_cast<float*>(p.scales_out)[unit] = s;
+            }
+        }
+        scale_values(v[i], r, (has_k && p.shift_sign < 0) ? k[i] : nullptr);
+        uint32_t w = pack8(v[i], p.g);
+        if (col[i] < p.cols) store_codes(p.packed + row[i] * p.ldp, col[i], p.cols, w, VEC);
+    }
+}
+
+// ROW mode, rows of at most R * 2048 elements: one workgroup per row, the row held in
+// registers (one HBM read), max reduced across the workgroup, then quantized.
+template <bool VEC, int R>
+__global__ void __launch_bounds__(kThreads) quantize_row_reg_kernel(QuantParams p) {
+    __shared__ float red[kThreads / 64];
+    const int64_t row = blockIdx.x;
+    const char* rp = reinterpret_cast<const char*>(p.x) + row * p.ldx * (p.x_bf16 ? 2 : 4);
+    const bool has_k = p.col_shift != nullptr;
+    float v[R][8];
+    int k[R][8];
+#pragma unroll
+    for (int c = 0; c < R; c++) {
+        int64_t col = (int64_t)c * kChunk + threadIdx.x * 8;
+        if (col < p.cols) {
+            load8<VEC>(rp, p.x_bf16, col, p.cols, v[c]);
+            if (has_k) load_shift8<VEC>(p, col, k[c]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; i++) { v[c][i] = 0.0f; k[c][i] = 0; }
+        }
+    }
+    float amax;
+    if (p.amax_in) {
+        amax = p.amax_in[row];
+#pragma unroll
+        for (int c = 0; c < R; c++)
+            if (has_k && p.shift_sign > 0) shift_inputs(v[c], k[c]);
+    } else {
+        float m = 0.0f;
+#pragma unroll
+        for (int c = 0; c < R; c++) {
+            if (has_k && p.shift_sign > 0) shift_inputs(v[c], k[c]);
+            m = fmaxf(m, max_abs8(v[c]));
+        }
+        m = wave_max(m);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    }
+    float s = amax / p.g.qmax;
+    if (p.scale_f16) s = round_f16(s);
+    float r = recip_or_zero(s);
+    if (threadIdx.x == 0 && p.scales_out) {
+        if (p.scale_f16) reinterpret_cast<__half*>(p.scales_out)[row] = __float2half_rn(s);
+        else reinterpret_cast<float*>(p.scales_out)[row] = s;
+    }
+#pragma unroll
+    for (int c = 0; c < R; c++) {
+        int64_t col = (int64_t)c * kChunk + threadIdx.x * 8;
+        if (col >= p.cols) continue;
+        scale_values(v[c], r, (has_k && p.shift_sign < 0) ? k[c] : nullptr);
+        uint32_t w = pack8(v[c], p.g);
+        store_codes(p.packed + row * p.ldp, col, p.cols, w, VEC);
+    }
+}
+
+// ROW mode for longer rows: pass 1 reduces the row max, pass 2 re-reads (L2) and
+// quantizes.
 template <bool VEC>
 __global__ void __launch_bounds__(kThreads) quantize_row_kernel(QuantParams p) {
     __shared__ float red[kThreads / 64];
-    int64_t row = blockIdx.x;
+    const int64_t row = blockIdx.x;
     const char* rp = reinterpret_cast<const char*>(p.x) + row * p.ldx * (p.x_bf16 ? 2 : 4);
+    const bool has_k = p.col_shift != nullptr;
     float amax;
     if (p.amax_in) {
         amax = p.amax_in[row];
@@ -207,10 +290,13 @@ __global__ void __launch_bounds__(kThreads) quantize_row_kernel(QuantParams p) {
         for (int64_t c0 = 0; c0 < p.cols; c0 += kChunk) {
             int64_t col = c0 + threadIdx.x * 8;
             float v[8];
+            int k[8];
             load8<VEC>(rp, p.x_bf16, col, p.cols, v);
-            shift_inputs(p, col, v);
-#pragma unroll
-            for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
+            if (has_k && p.shift_sign > 0) {
+                load_shift8<VEC>(p, col, k);
+                shift_inputs(v, k);
+            }
+            m = fmaxf(m, max_abs8(v));
         }
         m = wave_max(m);
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -228,9 +314,11 @@ __global__ void __launch_bounds__(kThreads) quantize_row_kernel(QuantParams p) {
         int64_t col = c0 + threadIdx.x * 8;
         if (col >= p.cols) continue;
         float v[8];
+        int k[8];
         load8<VEC>(rp, p.x_bf16, col, p.cols, v);
-        shift_inputs(p, col, v);
-        scale_values(p, col, r, v);
+        if (has_k) load_shift8<VEC>(p, col, k);
+        if (has_k && p.shift_sign > 0) shift_inputs(v, k);
+        scale_values(v, r, (has_k && p.shift_sign < 0) ? k : nullptr);
         uint32_t w = pack8(v, p.g);
         store_codes(p.packed + row * p.ldp, col, p.cols, w, VEC);
     }
@@ -248,13 +336,24 @@ hipError_t launch_tensor_scale_finalize(const float* amax, float* scales_out, fl
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
     if (p.rows == 0 || p.cols == 0) return hipSuccess;
     if (p.mode == 1) {
-        if (p.vec) hipLaunchKernelGGL(quantize_row_kernel<true>, dim3((unsigned)p.rows), dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL(quantize_row_kernel<false>, dim3((unsigned)p.rows), dim3(kThreads), 0, s, p);
+        dim3 grid((unsigned)p.rows);
+        if (p.cols <= 4 * kChunk) {
+            if (p.vec) hipLaunchKernelGGL((quantize_row_reg_kernel<true, 4>), grid, dim3(kThreads), 0, s, p);
+            else hipLaunchKernelGGL((quantize_row_reg_kernel<false, 4>), grid, dim3(kThreads), 0, s, p);
+        } else if (p.cols <= 8 * kChunk) {
+            if (p.vec) hipLaunchKernelGGL((quantize_row_reg_kernel<true, 8>), grid, dim3(kThreads), 0, s, p);
+            else hipLaunchKernelGGL((quantize_row_reg_kernel<false, 8>), grid, dim3(kThreads), 0, s, p);
+        } else {
+            if (p.vec) hipLaunchKernelGGL(quantize_row_kernel<true>, grid, dim3(kThreads), 0, s, p);
+            else hipLaunchKernelGGL(quantize_row_kernel<false>, grid, dim3(kThreads), 0, s, p);
+        }
     } else {
+        constexpr int U = 2;
         int64_t chunks = (p.cols + kChunk - 1) / kChunk;
-        dim3 grid((unsigned)(p.rows * chunks));
-        if (p.vec) hipLaunchKernelGGL(quantize_chunk_kernel<true>, grid, dim3(kThreads), 0, s, p, chunks);
-        else hipLaunchKernelGGL(quantize_chunk_kernel<false>, grid, dim3(kThreads), 0, s, p, chunks);
+        int64_t nunits = p.rows * chunks;
+        dim3 grid((unsigned)((nunits + U - 1) / U));
+        if (p.vec) hipLaunchKernelGGL((quantize_chunk_kernel<true, U>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
+        else hipLaunchKernelGGL((quantize_chunk_kernel<false, U>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
     }
     return hipGetLastError();
 }

@@ -331,3 +331,39 @@ def test_repeat_runs_identical():
         y = F.fp4_gemm(ap, wp, ws, fe2, F.gran("row"), K=1024, a_grid=fe2, a_scale=a)
         outs.append([host(t).tobytes() for t in (c, k, a, wp, ws, ap, y.view(torch.int16))])
     assert outs[0] == outs[1]
+
+
+@pytest.mark.parametrize("K", [9000, 17000, 13824])
+def test_preshift_long_rows(K):
+    """Per-row weight scales on long rows (register-resident and two-pass kernels)."""
+    say("preshift long rows", K)
+    x = synth.activations(5, K, 160, K, outlier_frac=0.01)
+    w = synth.weight(5, K, 40, K)
+    _preshift_chain(x, w)
+
+
+def test_prefill_full_sampled():
+    """LLaMA-13B prefill layer at full size: QKV, up, gate (K = 5120, shared activations
+    and shift) and down (K = 13824): every code bit-exact, GEMM outputs bit-exact on
+    sampled rows; the NF4 repeat within tolerance on sampled rows."""
+    e2 = O.minifloat(2, 1)
+    fe2 = F.grid_minifloat(2, 1)
+    rows = np.random.default_rng(1).choice(4096, 24, replace=False)
+    for which, names in ((1, ("qkv", "up", "gate")), (2, ("down",))):
+        x = synth.prefill_activations(which)
+        for name in names:
+            say("prefill", name)
+            w = synth.prefill_weight(name)
+            (k, a, wp, ws, ap), (gk, ga, gwp, gws, gap, fw, fgran) = _preshift_chain(x, w)
+            K = w.shape[1]
+            y32 = host(F.fp4_gemm(gap, gwp, gws, fw, fgran, K=K, a_grid=fe2, a_scale=ga, y_dtype=torch.float32))
+            _, acc = O.gemm_w4a4(ap[rows], e2, a, wp, e2, "row", ws)
+            assert np.array_equal(y32[rows].view(np.uint32), O.w4a4_epilogue_f32(acc, a, ws).view(np.uint32))
+            if name in ("qkv", "down"):
+                (k, a, wp, ws, ap), (gk, ga, gwp, gws, gap, fw, fgran) = _preshift_chain(x, w, "nf4", 64)
+                y32 = host(F.fp4_gemm(gap, gwp, gws, fw, fgran, K=K, a_grid=fe2, a_scale=ga, y_dtype=torch.float32))
+                r, _ = O.gemm_w4a4(ap[rows], e2, a, wp, O.nf4(), "group", ws, group=64)
+                err = O.rel_err(y32[rows], r)
+                say("  nf4 rel err", err)
+                assert err <= TOL
+            del w, wp, gwp
