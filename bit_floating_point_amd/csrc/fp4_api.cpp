@@ -153,12 +153,12 @@ fp4_status fp4_quantize_pack(const void* x, int32_t x_dtype, int64_t rows, int64
     if (st) return st;
     if ((st = check_gran(gran, cols))) return st;
     if (tensor_scale && gran.mode != FP4_SCALE_TENSOR) return fail(FP4_ERR_INVALID_ARG, "tensor_scale needs TENSOR mode");
-    if (!scales_out && !tensor_scale) return fail(FP4_ERR_INVALID_ARG, "scales_out may be NULL only with tensor_scale");
     if (tensor_scale && scales_out && (const void*)tensor_scale == scales_out)
         return fail(FP4_ERR_INVALID_ARG, "tensor_scale and scales_out must not alias");
     if (!aligned16(x) || !aligned16(packed) || !aligned16(col_shift))
         return fail(FP4_ERR_ALIGNMENT, "x, packed and col_shift must be 16-byte aligned");
     if (empty && gran.mode != FP4_SCALE_TENSOR) return ok();  // nothing to quantize, no scale unit
+    if (!scales_out && !tensor_scale) return fail(FP4_ERR_INVALID_ARG, "scales_out may be NULL only with tensor_scale");
     int esz = x_dtype == FP4_BF16 ? 2 : 4;
     QuantParams p{};
     p.x = x;

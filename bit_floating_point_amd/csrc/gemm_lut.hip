@@ -84,10 +84,15 @@ __global__ void __launch_bounds__(256) w4a4_lut_kernel(GemmParams p, int grid_m)
     // global -> LDS: 128 rows x 32 bytes per operand = 256 x 16 B, one load per thread
     const int lrow = tid >> 1, lseg = tid & 1;
     uint4 ra, rb;
+    // unconditional loads (out-of-range rows read row 0 and are zeroed by a select): one
+    // basic block per K step, so the LDS stores stay after the MFMAs
     auto gload = [&](int64_t kb) {
         int64_t gm = m0 + lrow, gn = n0 + lrow;
-        ra = gm < p.M ? *reinterpret_cast<const uint4*>(A + gm * p.lda + kb * kRowBytes + lseg * 16) : make_uint4(0, 0, 0, 0);
-        rb = gn < p.N ? *reinterpret_cast<const uint4*>(p.w + gn * p.ldw + kb * kRowBytes + lseg * 16) : make_uint4(0, 0, 0, 0);
+        bool oka = gm < p.M, okb = gn < p.N;
+        uint4 va = *reinterpret_cast<const uint4*>(A + (oka ? gm : 0) * p.lda + kb * kRowBytes + lseg * 16);
+        uint4 vb = *reinterpret_cast<const uint4*>(p.w + (okb ? gn : 0) * p.ldw + kb * kRowBytes + lseg * 16);
+        ra = oka ? va : make_uint4(0, 0, 0, 0);
+        rb = okb ? vb : make_uint4(0, 0, 0, 0);
     };
     auto sstore = [&](int st) {
         // the 16-byte segment holds two 8-byte units q = 2*lseg, 2*lseg+1
@@ -109,7 +114,7 @@ __global__ void __launch_bounds__(256) w4a4_lut_kernel(GemmParams p, int grid_m)
     __syncthreads();
     for (int64_t kb = 0; kb < nk; kb++) {
         const int st = (int)(kb & 1);
-        if (kb + 1 < nk) gload(kb + 1);
+        gload(kb + 1 < nk ? kb + 1 : kb);
         // lane holds codes [q*16, q*16+16) of its row: sub-step u uses the u-th 8
         f16x8 af[4][2];
 #pragma unroll
@@ -145,7 +150,10 @@ __global__ void __launch_bounds__(256) w4a4_lut_kernel(GemmParams p, int grid_m)
                 }
             }
         }
-        if (kb + 1 < nk) sstore(st ^ 1);
+        // keep the LDS stores (which wait for this step's global loads) after the MFMAs,
+        // so the loads for step kb+1 overlap the matrix work of step kb
+        __builtin_amdgcn_sched_barrier(0);
+        sstore(st ^ 1);
         __syncthreads();
     }
 

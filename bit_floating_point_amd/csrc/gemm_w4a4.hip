@@ -44,21 +44,26 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m)
     const int64_t nk = (p.K + 127) / 128;
     const uint8_t* A = reinterpret_cast<const uint8_t*>(p.a);
 
+    // Loads are unconditional (out-of-range rows and K tails read a valid address and
+    // are then zeroed with a select), so the main loop is one basic block and the
+    // scheduler keeps the LDS stores after the MFMAs.
     uint4 ra[LA], rb[LB];
     auto gload = [&](int64_t kb) {
 #pragma unroll
         for (int i = 0; i < LA; i++) {
             int s = tid + 256 * i, row = s >> 2, seg = s & 3;
             int64_t gm = m0 + row, kc = kb * 128 + seg * 32;
-            ra[i] = (gm < p.M && kc < p.K) ? *reinterpret_cast<const uint4*>(A + gm * p.lda + kb * kBKBytes + seg * 16)
-                                            : make_uint4(0, 0, 0, 0);
+            bool ok = gm < p.M && kc < p.K;
+            uint4 v = *reinterpret_cast<const uint4*>(ok ? A + gm * p.lda + kb * kBKBytes + seg * 16 : A);
+            ra[i] = ok ? v : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < LB; i++) {
             int s = tid + 256 * i, row = s >> 2, seg = s & 3;
             int64_t gn = n0 + row, kc = kb * 128 + seg * 32;
-            rb[i] = (gn < p.N && kc < p.K) ? *reinterpret_cast<const uint4*>(p.w + gn * p.ldw + kb * kBKBytes + seg * 16)
-                                            : make_uint4(0, 0, 0, 0);
+            bool ok = gn < p.N && kc < p.K;
+            uint4 v = *reinterpret_cast<const uint4*>(ok ? p.w + gn * p.ldw + kb * kBKBytes + seg * 16 : p.w);
+            rb[i] = ok ? v : make_uint4(0, 0, 0, 0);
         }
     };
     auto sstore = [&](int st) {
@@ -86,7 +91,7 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m)
     const int q = lane >> 4, r16 = lane & 15;
     for (int64_t kb = 0; kb < nk; kb++) {
         const int st = (int)(kb & 1);
-        if (kb + 1 < nk) gload(kb + 1);
+        gload(kb + 1 < nk ? kb + 1 : kb);  // the last step reloads itself into the idle stage
         i32x8 af[TM];
 #pragma unroll
         for (int i = 0; i < TM; i++) {
@@ -101,7 +106,10 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m)
             for (int i = 0; i < TM; i++)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf, acc[i][j], 4, 4, 0, 127, 0, 127);
         }
-        if (kb + 1 < nk) sstore(st ^ 1);
+        // keep the LDS stores (which wait for this step's global loads) after the MFMAs,
+        // so the loads for step kb+1 overlap the matrix work of step kb
+        __builtin_amdgcn_sched_barrier(0);
+        sstore(st ^ 1);
         __syncthreads();
     }
 

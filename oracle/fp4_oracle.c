@@ -42,18 +42,46 @@ void orc_minifloat_grid(int e, int m, int b, double* out) {
     for (int c = 0; c < (1 << (e + m)); c++) out[c] = orc_minifloat_value(e, m, b, c);
 }
 
+/* a - b = *s + *e exactly (TwoSum with -b; binary64, no FMA contraction). */
+static void two_diff(double a, double b, double* s, double* e) {
+    double d = a - b;
+    double bb = d - a;
+    *s = d;
+    *e = (a - (d - bb)) + (-b - bb);
+}
+
+/* Exact sign of |v - a| - |v - b|: each difference is kept as an unevaluated sum
+ * hi + lo (hi the rounded difference), and such pairs compare lexicographically.     */
+static int exact_dist_cmp(double v, double a, double b) {
+    double sa, ea, sb, eb;
+    two_diff(v, a, &sa, &ea);
+    two_diff(v, b, &sb, &eb);
+    if (sa < 0 || (sa == 0 && ea < 0)) { sa = -sa; ea = -ea; }
+    if (sb < 0 || (sb == 0 && eb < 0)) { sb = -sb; eb = -eb; }
+    if (sa != sb) return sa < sb ? -1 : 1;
+    if (ea != eb) return ea < eb ? -1 : 1;
+    return 0;
+}
+
 /* Brute-force nearest grid point ("compare and quantize", [FP4-LLM] eq. (5)):
  * returns the index c in [0, n) minimising |v - grid[c]|, an exact tie going to the
  * even index.  v has already been clipped to the grid's range ("scale and clip",
- * eq. (2)), so v is a binary32 value of at most the grid's magnitude and the grid
- * points are short dyadic or binary16 numbers: two distances that differ at all
- * differ by far more than a binary64 rounding, so the comparison is exact.          */
+ * eq. (2)).  Rounded binary64 distances decide whenever they differ (rounding is
+ * monotone, so their order is the exact order); equal rounded distances are compared
+ * exactly, so a false tie (e.g. a tiny |v| at the zero midpoint of a symmetric
+ * lookup grid) cannot occur.                                                         */
 static int nearest(double v, const double* grid, int n) {
     int best = 0;
     double bd = fabs(v - grid[0]);
     for (int c = 1; c < n; c++) {
         double dc = fabs(v - grid[c]);
-        if (dc < bd || (dc == bd && (c % 2 == 0) && (best % 2 != 0))) { best = c; bd = dc; }
+        int take = 0;
+        if (dc < bd) take = 1;
+        else if (dc == bd) {
+            int r = exact_dist_cmp(v, grid[c], grid[best]);
+            take = r < 0 || (r == 0 && (c % 2 == 0) && (best % 2 != 0));
+        }
+        if (take) { best = c; bd = dc; }
     }
     return best;
 }

@@ -213,13 +213,17 @@ def test_nf4_quantize_matches_searchsorted():
     G = O.nf4_table()
     mids = ((G[1:] + G[:-1]) / 2).astype(np.float32)
     rng = np.random.default_rng(5)
-    y = np.concatenate([rng.uniform(-1.3, 1.3, 50000), mids, -mids]).astype(np.float32)
+    tiny = np.array([1e-45, 5e-44, 1e-40, 1e-30, 1e-10], dtype=np.float32)  # at the zero midpoint
+    y = np.concatenate([rng.uniform(-1.3, 1.3, 50000), mids, -mids, tiny, -tiny, [0.0, -0.0]]).astype(np.float32)
     got = O.quantize(y, 1, O.nf4())
     idx = np.searchsorted(mids.astype(np.float64), y.astype(np.float64), side="left")
-    at_mid = np.isin(y, mids)
+    at_mid = np.isin(y, mids) | (y == 0)
     # at an exact midpoint between i and i+1 the even index wins
     idx = np.where(at_mid & (idx % 2 == 1), idx + 1, idx)
     assert np.array_equal(got, idx)
+    # the level on the value's own side of zero wins for any tiny nonzero value
+    assert O.quantize(-tiny, 1, O.nf4()).tolist() == [7] * tiny.size
+    assert O.quantize(tiny, 1, O.nf4()).tolist() == [8] * tiny.size
 
 
 # ---------------------------------------------------------------- bf16 / f16 ----
