@@ -11,36 +11,68 @@ namespace fp4 {
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
 
-// 8 consecutive elements of a row as floats; elements at col >= cols read as 0.
-template <bool VEC>
-__device__ __forceinline__ void load8(const void* row_ptr, int x_bf16, int64_t col, int64_t cols,
-                                      float v[8]) {
-    if (VEC && col + 8 <= cols) {
-        if (x_bf16) {
-            uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(row_ptr) + col);
-            uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                v[2 * i] = __uint_as_float(w[i] << 16);
-                v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+// 8 consecutive elements of a row, loaded raw (bf16 bits or f32 bits) so that every
+// load of a thread can be issued before the first conversion waits for data.
+struct Raw8 {
+    uint4 a, b;  // bf16: a holds the 8 values; f32: a = elements 0-3, b = elements 4-7
+};
+
+template <bool VEC, bool BF16>
+__device__ __forceinline__ Raw8 load_raw8(const void* row_ptr, int64_t col, int64_t cols) {
+    Raw8 r;
+    r.a = make_uint4(0, 0, 0, 0);
+    r.b = make_uint4(0, 0, 0, 0);
+    if (VEC) {
+        // vector path: cols is a multiple of 8, so a chunk is either whole or absent
+        if (col < cols) {
+            if (BF16) {
+                r.a = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(row_ptr) + col);
+            } else {
+                const uint4* q = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(row_ptr) + col);
+                r.a = q[0];
+                r.b = q[1];
             }
-        } else {
-            const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(row_ptr) + col);
-            float4 a = p[0], b = p[1];
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
         }
     } else {
+        uint32_t w[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            float t = 0.0f;
+            w[i] = 0;
             if (col + i < cols) {
-                if (x_bf16) t = bf16_bits_to_float(reinterpret_cast<const uint16_t*>(row_ptr)[col + i]);
-                else t = reinterpret_cast<const float*>(row_ptr)[col + i];
+                if (BF16) w[i] = reinterpret_cast<const uint16_t*>(row_ptr)[col + i];
+                else w[i] = __float_as_uint(reinterpret_cast<const float*>(row_ptr)[col + i]);
             }
-            v[i] = t;
+        }
+        if (BF16) {
+            r.a = make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16));
+        } else {
+            r.a = make_uint4(w[0], w[1], w[2], w[3]);
+            r.b = make_uint4(w[4], w[5], w[6], w[7]);
         }
     }
+    return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void raw8_to_float(const Raw8& r, float v[8]) {
+    if (BF16) {
+        const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+        v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y);
+        v[2] = __uint_as_float(r.a.z); v[3] = __uint_as_float(r.a.w);
+        v[4] = __uint_as_float(r.b.x); v[5] = __uint_as_float(r.b.y);
+        v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
+    }
+}
+
+template <bool VEC, bool BF16>
+__device__ __forceinline__ void load8(const void* row_ptr, int64_t col, int64_t cols, float v[8]) {
+    raw8_to_float<BF16>(load_raw8<VEC, BF16>(row_ptr, col, cols), v);
 }
 
 // Magnitude code of a minifloat grid by the compare ladder: count the midpoints below

@@ -33,13 +33,23 @@ __device__ __forceinline__ bf16x8 decode_e2m1_bf16(uint32_t w) {
     return __builtin_bit_cast(bf16x8, o);
 }
 
-__device__ __forceinline__ float load_scale(const GemmParams& p, int64_t idx) {
-    return p.w_scale_f16 ? __half2float(reinterpret_cast<const __half*>(p.w_scales)[idx])
-                         : reinterpret_cast<const float*>(p.w_scales)[idx];
+// Scale loads return raw bits; the conversion waits until the value is used, so a
+// batch's loads are all in flight together.
+template <bool SF16>
+__device__ __forceinline__ uint32_t load_scale_raw(const GemmParams& p, int64_t idx) {
+    if (SF16) return reinterpret_cast<const uint16_t*>(p.w_scales)[idx];
+    return reinterpret_cast<const uint32_t*>(p.w_scales)[idx];
+}
+
+template <bool SF16>
+__device__ __forceinline__ float scale_value(uint32_t raw) {
+    if (SF16) return __half2float(__ushort_as_half((unsigned short)raw));
+    return __uint_as_float(raw);
 }
 
 // T = 16-column tiles per wavefront (the activation registers are reused across them)
-template <int MODE, int T>  // MODE 0 tensor, 1 row, 2 group
+// G1: group scales with exactly one 128-wide chunk per group (group size 128)
+template <int MODE, int T, bool SF16, bool G1>  // MODE 0 tensor, 1 row, 2 group
 __global__ void __launch_bounds__(256) w4a16_mfma_kernel(GemmParams p) {
     __shared__ f32x4 part[kW16Waves - 1][T][64];
     const int lane = threadIdx.x & 63;
@@ -53,7 +63,7 @@ __global__ void __launch_bounds__(256) w4a16_mfma_kernel(GemmParams p) {
     const int nchunks = (int)(p.K / 128);
     const int c_begin = nchunks * wave / kW16Waves;
     const int c_end = nchunks * (wave + 1) / kW16Waves;
-    const int cpg = MODE == 2 ? p.w_group / 128 : 1;
+    const int cpg = (MODE == 2 && !G1) ? p.w_group / 128 : 1;
     const int64_t ngroups = MODE == 2 ? p.K / p.w_group : 1;
 
     int64_t n[T];
@@ -76,39 +86,53 @@ __global__ void __launch_bounds__(256) w4a16_mfma_kernel(GemmParams p) {
         // activations are all independent of the MFMA chain
         uint4 wv[kBatch][T];
         uint4 xv[kBatch][4];
-        float sc[kBatch][T];
+        uint32_t sc[kBatch][T];
+        bool valid[kBatch];
+        // Every load is unconditional: rows beyond N or M were pointed at row 0 above and
+        // chunks past the wavefront's range re-read its last chunk (their codes are then
+        // zeroed).  Values of rows beyond N or M only reach outputs that are never
+        // stored.  No load sits inside a branch, which would force a wait on all loads
+        // in flight.
 #pragma unroll
         for (int b = 0; b < kBatch; b++) {
-            const int c = c0 + b;
-            const bool valid = c < c_end;
+            valid[b] = c0 + b < c_end;
+            const int c = valid[b] ? c0 + b : c_end - 1;
 #pragma unroll
             for (int t = 0; t < T; t++) {
-                wv[b][t] = (valid && n_ok[t]) ? *reinterpret_cast<const uint4*>(wrow[t] + (int64_t)c * 64)
-                                              : make_uint4(0, 0, 0, 0);
-                sc[b][t] = (MODE == 2 && valid && n_ok[t]) ? load_scale(p, n[t] * ngroups + c / cpg) : 0.0f;
+                wv[b][t] = *reinterpret_cast<const uint4*>(wrow[t] + (int64_t)c * 64);
+                if (MODE == 2) sc[b][t] = load_scale_raw<SF16>(p, (n_ok[t] ? n[t] : 0) * ngroups + (G1 ? c : c / cpg));
             }
 #pragma unroll
-            for (int j = 0; j < 4; j++)
-                xv[b][j] = (valid && m_ok) ? *reinterpret_cast<const uint4*>(xrow + (int64_t)c * 128 + j * 8)
-                                           : make_uint4(0, 0, 0, 0);
+            for (int j = 0; j < 4; j++) xv[b][j] = *reinterpret_cast<const uint4*>(xrow + (int64_t)c * 128 + j * 8);
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int b = 0; b < kBatch; b++) {
             const int c = c0 + b;
-            if (c >= c_end) break;
 #pragma unroll
             for (int t = 0; t < T; t++) {
-                const uint32_t wd[4] = {wv[b][t].x, wv[b][t].y, wv[b][t].z, wv[b][t].w};
+                const uint4 w = valid[b] ? wv[b][t] : make_uint4(0, 0, 0, 0);
+                const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+                f32x4 acc = G1 ? f32x4{0.f, 0.f, 0.f, 0.f} : gacc[t];
 #pragma unroll
                 for (int j = 0; j < 4; j++)
-                    gacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[b][j]),
-                                                                      decode_e2m1_bf16(wd[j]), gacc[t], 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[b][j]),
+                                                                  decode_e2m1_bf16(wd[j]), acc, 0, 0, 0);
+                if (G1) {
+                    // one group per chunk: scale its partial sum and add it (no branch)
+                    const float sv = scale_value<SF16>(sc[b][t]);
+#pragma unroll
+                    for (int i = 0; i < 4; i++) total[t][i] = __builtin_fmaf(acc[i], sv, total[t][i]);
+                } else {
+                    gacc[t] = acc;
+                }
             }
-            if (MODE == 2 && (c + 1) % cpg == 0) {
+            if (MODE == 2 && !G1 && valid[b] && (c + 1) % cpg == 0) {
 #pragma unroll
                 for (int t = 0; t < T; t++) {
 #pragma unroll
-                    for (int i = 0; i < 4; i++) total[t][i] = __builtin_fmaf(gacc[t][i], sc[b][t], total[t][i]);
+                    for (int i = 0; i < 4; i++)
+                        total[t][i] = __builtin_fmaf(gacc[t][i], scale_value<SF16>(sc[b][t]), total[t][i]);
                     gacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
             }
@@ -116,14 +140,14 @@ __global__ void __launch_bounds__(256) w4a16_mfma_kernel(GemmParams p) {
     }
 #pragma unroll
     for (int t = 0; t < T; t++) {
-        if (MODE == 2 && c_end > c_begin && (c_end % cpg) != 0) {
+        if (MODE == 2 && !G1 && c_end > c_begin && (c_end % cpg) != 0) {
             // this wavefront's range ends inside a group: scale its share of that group
-            float s = n_ok[t] ? load_scale(p, n[t] * ngroups + (c_end - 1) / cpg) : 0.0f;
+            float s = n_ok[t] ? scale_value<SF16>(load_scale_raw<SF16>(p, n[t] * ngroups + (c_end - 1) / cpg)) : 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; i++) total[t][i] = __builtin_fmaf(gacc[t][i], s, total[t][i]);
         }
         if (MODE != 2) {
-            float s = n_ok[t] ? load_scale(p, MODE == 1 ? n[t] : 0) : 0.0f;
+            float s = n_ok[t] ? scale_value<SF16>(load_scale_raw<SF16>(p, MODE == 1 ? n[t] : 0)) : 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; i++) total[t][i] = gacc[t][i] * s;
         }
@@ -153,20 +177,26 @@ __global__ void __launch_bounds__(256) w4a16_mfma_kernel(GemmParams p) {
     }
 }
 
-template <int T>
+template <int T, bool SF16>
 static void launch_w16(const GemmParams& p, hipStream_t s) {
     dim3 grid((unsigned)((p.N + 16 * T - 1) / (16 * T)), (unsigned)((p.M + 15) / 16));
-    if (p.w_mode == 2) hipLaunchKernelGGL((w4a16_mfma_kernel<2, T>), grid, dim3(256), 0, s, p);
-    else if (p.w_mode == 1) hipLaunchKernelGGL((w4a16_mfma_kernel<1, T>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((w4a16_mfma_kernel<0, T>), grid, dim3(256), 0, s, p);
+    if (p.w_mode == 2 && p.w_group == 128) hipLaunchKernelGGL((w4a16_mfma_kernel<2, T, SF16, true>), grid, dim3(256), 0, s, p);
+    else if (p.w_mode == 2) hipLaunchKernelGGL((w4a16_mfma_kernel<2, T, SF16, false>), grid, dim3(256), 0, s, p);
+    else if (p.w_mode == 1) hipLaunchKernelGGL((w4a16_mfma_kernel<1, T, SF16, false>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((w4a16_mfma_kernel<0, T, SF16, false>), grid, dim3(256), 0, s, p);
 }
 
 hipError_t launch_w4a16_mfma(const GemmParams& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     // small M: one 16-column tile per wavefront keeps the most weight bytes in flight;
     // larger M: reuse each activation fragment for two weight tiles
-    if (p.M > 8) launch_w16<2>(p, s);
-    else launch_w16<1>(p, s);
+    if (p.M > 8) {
+        if (p.w_scale_f16) launch_w16<2, true>(p, s);
+        else launch_w16<2, false>(p, s);
+    } else {
+        if (p.w_scale_f16) launch_w16<1, true>(p, s);
+        else launch_w16<1, false>(p, s);
+    }
     return hipGetLastError();
 }
 

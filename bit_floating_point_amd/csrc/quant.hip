@@ -19,6 +19,13 @@ namespace fp4 {
 constexpr int kThreads = 256;
 constexpr int kChunk = kThreads * 8;  // elements of a row per workgroup pass
 
+__device__ __forceinline__ float max_abs8(const float v[8]) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
+    return m;
+}
+
 __global__ void fill_zero_u32_kernel(uint32_t* p, int64_t n) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0u;
@@ -35,36 +42,40 @@ hipError_t launch_fill_zero_u32(uint32_t* p, int64_t n, hipStream_t s) {
 // TENSOR: one workgroup per (row, 2048-column chunk); wave max -> atomicMax on the
 // float bit pattern (|x| >= 0, so unsigned order equals float order; max is exact and
 // order-free, so the result does not depend on the launch geometry).
-template <bool VEC>
-__global__ void __launch_bounds__(kThreads) amax_tensor_kernel(const void* x, int x_bf16, int64_t cols,
-                                                               int64_t ld, int64_t chunks, float* out) {
+template <bool VEC, bool BF16>
+__global__ void __launch_bounds__(kThreads) amax_tensor_kernel(const void* x, int64_t cols, int64_t ld, int64_t chunks,
+                                                               float* out) {
     int64_t b = blockIdx.x;
     int64_t row = b / chunks;
     int64_t col = (b % chunks) * kChunk + threadIdx.x * 8;
-    const char* rp = reinterpret_cast<const char*>(x) + row * ld * (x_bf16 ? 2 : 4);
+    const char* rp = reinterpret_cast<const char*>(x) + row * ld * (BF16 ? 2 : 4);
     float v[8];
-    load8<VEC>(rp, x_bf16, col, cols, v);
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
-    m = wave_max(m);
+    load8<VEC, BF16>(rp, col, cols, v);
+    float m = wave_max(max_abs8(v));
     if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
 }
 
 // COLUMN: per-column max over the first `rows` rows.  A thread owns 8 columns and a
-// strip of 32 rows; one atomicMax per column per strip.
-template <bool VEC>
-__global__ void __launch_bounds__(kThreads) amax_column_kernel(const void* x, int x_bf16, int64_t rows,
-                                                               int64_t cols, int64_t ld, float* out) {
+// strip of 32 rows (all 32 loads issued before the first max); one atomicMax per column
+// per strip.
+template <bool VEC, bool BF16>
+__global__ void __launch_bounds__(kThreads) amax_column_kernel(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                                                               float* out) {
+    constexpr int kStrip = 32;
     int64_t col = (int64_t)blockIdx.x * kChunk + threadIdx.x * 8;
-    int64_t r0 = (int64_t)blockIdx.y * 32;
-    int64_t r1 = r0 + 32 < rows ? r0 + 32 : rows;
+    int64_t r0 = (int64_t)blockIdx.y * kStrip;
     if (col >= cols) return;
+    Raw8 raw[kStrip];
+#pragma unroll
+    for (int r = 0; r < kStrip; r++) {
+        int64_t rr = r0 + r < rows ? r0 + r : rows - 1;  // a repeated row does not change a max
+        raw[r] = load_raw8<VEC, BF16>(reinterpret_cast<const char*>(x) + rr * ld * (BF16 ? 2 : 4), col, cols);
+    }
     float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int64_t r = r0; r < r1; r++) {
-        const char* rp = reinterpret_cast<const char*>(x) + r * ld * (x_bf16 ? 2 : 4);
+#pragma unroll
+    for (int r = 0; r < kStrip; r++) {
         float v[8];
-        load8<VEC>(rp, x_bf16, col, cols, v);
+        raw8_to_float<BF16>(raw[r], v);
 #pragma unroll
         for (int i = 0; i < 8; i++) m[i] = fmaxf(m[i], fabsf(v[i]));
     }
@@ -74,49 +85,47 @@ __global__ void __launch_bounds__(kThreads) amax_column_kernel(const void* x, in
 }
 
 // ROW_GROUP: per (row, group) max; a group spans group/8 aligned lanes.
-template <bool VEC>
-__global__ void __launch_bounds__(kThreads) amax_rowgroup_kernel(const void* x, int x_bf16, int64_t cols,
-                                                                 int64_t ld, int64_t chunks, int group,
-                                                                 float* out) {
+template <bool VEC, bool BF16>
+__global__ void __launch_bounds__(kThreads) amax_rowgroup_kernel(const void* x, int64_t cols, int64_t ld,
+                                                                 int64_t chunks, int group, float* out) {
     int64_t b = blockIdx.x;
     int64_t row = b / chunks;
     int64_t col = (b % chunks) * kChunk + threadIdx.x * 8;
-    const char* rp = reinterpret_cast<const char*>(x) + row * ld * (x_bf16 ? 2 : 4);
+    const char* rp = reinterpret_cast<const char*>(x) + row * ld * (BF16 ? 2 : 4);
     float v[8];
-    load8<VEC>(rp, x_bf16, col, cols, v);
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
+    load8<VEC, BF16>(rp, col, cols, v);
     int lanes = group >> 3;
-    m = group_max(m, lanes);
+    float m = group_max(max_abs8(v), lanes);
     if (col < cols && ((threadIdx.x & (lanes - 1)) == 0)) out[row * (cols / group) + col / group] = m;
 }
 
-hipError_t launch_calibrate(const void* x, int x_bf16, int64_t rows, int64_t cols, int64_t ld,
-                            int reduce, int group, float* out, int vec, hipStream_t s) {
+template <bool VEC, bool BF16>
+static void calibrate_launch(const void* x, int64_t rows, int64_t cols, int64_t ld, int reduce, int group, float* out,
+                             hipStream_t s) {
     int64_t chunks = (cols + kChunk - 1) / kChunk;
     if (reduce == 0) {
-        hipError_t e = launch_fill_zero_u32(reinterpret_cast<uint32_t*>(out), 1, s);
-        if (e != hipSuccess) return e;
-        if (rows == 0 || cols == 0) return hipSuccess;
-        if (vec) hipLaunchKernelGGL(amax_tensor_kernel<true>, dim3((unsigned)(rows * chunks)), dim3(kThreads), 0, s,
-                                    x, x_bf16, cols, ld, chunks, out);
-        else hipLaunchKernelGGL(amax_tensor_kernel<false>, dim3((unsigned)(rows * chunks)), dim3(kThreads), 0, s,
-                                x, x_bf16, cols, ld, chunks, out);
+        hipLaunchKernelGGL((amax_tensor_kernel<VEC, BF16>), dim3((unsigned)(rows * chunks)), dim3(kThreads), 0, s, x,
+                           cols, ld, chunks, out);
     } else if (reduce == 1) {
-        hipError_t e = launch_fill_zero_u32(reinterpret_cast<uint32_t*>(out), cols, s);
-        if (e != hipSuccess) return e;
-        if (rows == 0 || cols == 0) return hipSuccess;
         dim3 grid((unsigned)chunks, (unsigned)((rows + 31) / 32));
-        if (vec) hipLaunchKernelGGL(amax_column_kernel<true>, grid, dim3(kThreads), 0, s, x, x_bf16, rows, cols, ld, out);
-        else hipLaunchKernelGGL(amax_column_kernel<false>, grid, dim3(kThreads), 0, s, x, x_bf16, rows, cols, ld, out);
+        hipLaunchKernelGGL((amax_column_kernel<VEC, BF16>), grid, dim3(kThreads), 0, s, x, rows, cols, ld, out);
     } else {
-        if (rows == 0 || cols == 0) return hipSuccess;
-        if (vec) hipLaunchKernelGGL(amax_rowgroup_kernel<true>, dim3((unsigned)(rows * chunks)), dim3(kThreads), 0, s,
-                                    x, x_bf16, cols, ld, chunks, group, out);
-        else hipLaunchKernelGGL(amax_rowgroup_kernel<false>, dim3((unsigned)(rows * chunks)), dim3(kThreads), 0, s,
-                                x, x_bf16, cols, ld, chunks, group, out);
+        hipLaunchKernelGGL((amax_rowgroup_kernel<VEC, BF16>), dim3((unsigned)(rows * chunks)), dim3(kThreads), 0, s, x,
+                           cols, ld, chunks, group, out);
     }
+}
+
+hipError_t launch_calibrate(const void* x, int x_bf16, int64_t rows, int64_t cols, int64_t ld, int reduce, int group,
+                            float* out, int vec, hipStream_t s) {
+    if (reduce == 0 || reduce == 1) {
+        hipError_t e = launch_fill_zero_u32(reinterpret_cast<uint32_t*>(out), reduce == 0 ? 1 : cols, s);
+        if (e != hipSuccess) return e;
+    }
+    if (rows == 0 || cols == 0) return hipSuccess;
+    if (vec && x_bf16) calibrate_launch<true, true>(x, rows, cols, ld, reduce, group, out, s);
+    else if (vec) calibrate_launch<true, false>(x, rows, cols, ld, reduce, group, out, s);
+    else if (x_bf16) calibrate_launch<false, true>(x, rows, cols, ld, reduce, group, out, s);
+    else calibrate_launch<false, false>(x, rows, cols, ld, reduce, group, out, s);
     return hipGetLastError();
 }
 
@@ -130,128 +139,120 @@ __device__ __forceinline__ void store_codes(uint8_t* prow, int64_t col, int64_t 
     }
 }
 
-// Column shifts of the 8 elements at col (0 beyond the row).
+// Column shifts of the 8 elements at col, raw (8 int8 in two words).
 template <bool VEC>
-__device__ __forceinline__ void load_shift8(const QuantParams& p, int64_t col, int k[8]) {
-    if (VEC && col + 8 <= p.cols) {
-        uint2 w = *reinterpret_cast<const uint2*>(p.col_shift + col);
+__device__ __forceinline__ uint2 load_shift8(const QuantParams& p, int64_t col) {
+    if (VEC) return col < p.cols ? *reinterpret_cast<const uint2*>(p.col_shift + col) : make_uint2(0, 0);
+    uint32_t w[2] = {0, 0};
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            k[i] = (int)(int8_t)(w.x >> (8 * i));
-            k[4 + i] = (int)(int8_t)(w.y >> (8 * i));
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; i++) k[i] = (col + i < p.cols) ? (int)p.col_shift[col + i] : 0;
-    }
+    for (int i = 0; i < 8; i++)
+        if (col + i < p.cols) w[i >> 2] |= (uint32_t)(uint8_t)p.col_shift[col + i] << (8 * (i & 3));
+    return make_uint2(w[0], w[1]);
+}
+
+__device__ __forceinline__ int shift_of(uint2 k, int i) {
+    return (int)(int8_t)((i < 4 ? k.x : k.y) >> (8 * (i & 3)));
 }
 
 // Input side of the pre-shift (weights): x' = x * 2^k, exact.
-__device__ __forceinline__ void shift_inputs(float v[8], const int k[8]) {
+__device__ __forceinline__ void shift_inputs(float v[8], uint2 k) {
 #pragma unroll
-    for (int i = 0; i < 8; i++) v[i] = ldexpf(v[i], k[i]);
+    for (int i = 0; i < 8; i++) v[i] = ldexpf(v[i], shift_of(k, i));
 }
 
 // y = fl32(x * r), or fl32(x * (r * 2^-k)) with the activation-side pre-shift.
-__device__ __forceinline__ void scale_values(float v[8], float r, const int* k) {
-    if (k) {
+__device__ __forceinline__ void scale_values(float v[8], float r, bool shifted, uint2 k) {
+    if (shifted) {
 #pragma unroll
-        for (int i = 0; i < 8; i++) v[i] = v[i] * ldexpf(r, -k[i]);
+        for (int i = 0; i < 8; i++) v[i] = v[i] * ldexpf(r, -shift_of(k, i));
     } else {
 #pragma unroll
         for (int i = 0; i < 8; i++) v[i] = v[i] * r;
     }
 }
 
-__device__ __forceinline__ float max_abs8(const float v[8]) {
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
-    return m;
+__device__ __forceinline__ void store_scale(const QuantParams& p, int64_t unit, float s) {
+    if (p.scale_f16) reinterpret_cast<__half*>(p.scales_out)[unit] = __float2half_rn(s);
+    else reinterpret_cast<float*>(p.scales_out)[unit] = s;
 }
 
 // TENSOR and GROUP modes.  The (row, 2048-column chunk) units are processed U per
-// workgroup: all U loads are issued before any arithmetic (2 x 16 B per lane in flight
-// for bf16, 4 x 16 B for f32 at U = 2).
-template <bool VEC, int U>
+// workgroup: every load of the U units (values and shifts) is issued before any
+// arithmetic, so a lane has U x 16 B (bf16) or U x 32 B (f32) in flight.
+template <bool VEC, bool BF16, int U>
 __global__ void __launch_bounds__(kThreads) quantize_chunk_kernel(QuantParams p, int64_t chunks, int64_t nunits) {
     const bool has_k = p.col_shift != nullptr;
-    float v[U][8];
-    int k[U][8];
+    Raw8 raw[U];
+    uint2 kk[U];
     int64_t row[U], col[U];
 #pragma unroll
     for (int i = 0; i < U; i++) {
         int64_t u = (int64_t)blockIdx.x * U + i;
-        if (u >= nunits) u = nunits - 1;  // duplicate of the last unit: same values, same bytes
+        if (u >= nunits) u = nunits - 1;  // a duplicate of the last unit writes the same bytes
         row[i] = u / chunks;
         col[i] = (u % chunks) * kChunk + threadIdx.x * 8;
-        const char* rp = reinterpret_cast<const char*>(p.x) + row[i] * p.ldx * (p.x_bf16 ? 2 : 4);
-        load8<VEC>(rp, p.x_bf16, col[i], p.cols, v[i]);
-        if (has_k) load_shift8<VEC>(p, col[i], k[i]);
+        raw[i] = load_raw8<VEC, BF16>(reinterpret_cast<const char*>(p.x) + row[i] * p.ldx * (BF16 ? 2 : 4), col[i],
+                                      p.cols);
+        kk[i] = has_k ? load_shift8<VEC>(p, col[i]) : make_uint2(0, 0);
+    }
+    float tensor_r = 0.0f;
+    if (p.mode == 0) {
+        float s = p.tensor_scale ? p.tensor_scale[0] : p.tensor_amax[0] / p.g.qmax;
+        tensor_r = recip_or_zero(s);
+        if (blockIdx.x == 0 && threadIdx.x == 0 && p.tensor_scale && p.scales_out)
+            reinterpret_cast<float*>(p.scales_out)[0] = s;
     }
 #pragma unroll
     for (int i = 0; i < U; i++) {
-        if (has_k && p.shift_sign > 0) shift_inputs(v[i], k[i]);
-        float r;
-        if (p.mode == 0) {
-            float s = p.tensor_scale ? p.tensor_scale[0] : p.tensor_amax[0] / p.g.qmax;
-            r = recip_or_zero(s);
-            if (blockIdx.x == 0 && i == 0 && threadIdx.x == 0 && p.tensor_scale && p.scales_out)
-                reinterpret_cast<float*>(p.scales_out)[0] = s;
-        } else {
+        float v[8];
+        raw8_to_float<BF16>(raw[i], v);
+        if (has_k && p.shift_sign > 0) shift_inputs(v, kk[i]);
+        float r = tensor_r;
+        if (p.mode != 0) {
             int lanes = p.group >> 3;
             int64_t unit = row[i] * (p.cols / p.group) + col[i] / p.group;
             float amax;
             if (p.amax_in) amax = (col[i] < p.cols) ? p.amax_in[unit] : 0.0f;
-            else amax = group_max(max_abs8(v[i]), lanes);
+            else amax = group_max(max_abs8(v), lanes);
             float s = amax / p.g.qmax;
             if (p.scale_f16) s = round_f16(s);
             r = recip_or_zero(s);
-            if (col[i] < p.cols && (threadIdx.x & (lanes - 1)) == 0 && p.scales_out) {
-                if (p.scale_f16) reinterpret_cast<__half*>(p.scales_out)[unit] = __float2half_rn(s);
-                else reinterpret_cast<float*>(p.scales_out)[unit] = s;
-            }
+            if (col[i] < p.cols && (threadIdx.x & (lanes - 1)) == 0 && p.scales_out) store_scale(p, unit, s);
         }
-        scale_values(v[i], r, (has_k && p.shift_sign < 0) ? k[i] : nullptr);
-        uint32_t w = pack8(v[i], p.g);
+        scale_values(v, r, has_k && p.shift_sign < 0, kk[i]);
+        uint32_t w = pack8(v, p.g);
         if (col[i] < p.cols) store_codes(p.packed + row[i] * p.ldp, col[i], p.cols, w, VEC);
     }
 }
 
 // ROW mode, rows of at most R * 2048 elements: one workgroup per row, the row held in
 // registers (one HBM read), max reduced across the workgroup, then quantized.
-template <bool VEC, int R>
+template <bool VEC, bool BF16, int R>
 __global__ void __launch_bounds__(kThreads) quantize_row_reg_kernel(QuantParams p) {
     __shared__ float red[kThreads / 64];
     const int64_t row = blockIdx.x;
-    const char* rp = reinterpret_cast<const char*>(p.x) + row * p.ldx * (p.x_bf16 ? 2 : 4);
+    const char* rp = reinterpret_cast<const char*>(p.x) + row * p.ldx * (BF16 ? 2 : 4);
     const bool has_k = p.col_shift != nullptr;
-    float v[R][8];
-    int k[R][8];
+    Raw8 raw[R];
+    uint2 kk[R];
 #pragma unroll
     for (int c = 0; c < R; c++) {
         int64_t col = (int64_t)c * kChunk + threadIdx.x * 8;
-        if (col < p.cols) {
-            load8<VEC>(rp, p.x_bf16, col, p.cols, v[c]);
-            if (has_k) load_shift8<VEC>(p, col, k[c]);
-        } else {
+        raw[c] = load_raw8<VEC, BF16>(rp, col, p.cols);
+        kk[c] = has_k ? load_shift8<VEC>(p, col) : make_uint2(0, 0);
+    }
+    float v[R][8];
+    float m = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; i++) { v[c][i] = 0.0f; k[c][i] = 0; }
-        }
+    for (int c = 0; c < R; c++) {
+        raw8_to_float<BF16>(raw[c], v[c]);
+        if (has_k && p.shift_sign > 0) shift_inputs(v[c], kk[c]);
+        m = fmaxf(m, max_abs8(v[c]));
     }
     float amax;
     if (p.amax_in) {
         amax = p.amax_in[row];
-#pragma unroll
-        for (int c = 0; c < R; c++)
-            if (has_k && p.shift_sign > 0) shift_inputs(v[c], k[c]);
     } else {
-        float m = 0.0f;
-#pragma unroll
-        for (int c = 0; c < R; c++) {
-            if (has_k && p.shift_sign > 0) shift_inputs(v[c], k[c]);
-            m = fmaxf(m, max_abs8(v[c]));
-        }
         m = wave_max(m);
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
         __syncthreads();
@@ -260,15 +261,12 @@ __global__ void __launch_bounds__(kThreads) quantize_row_reg_kernel(QuantParams 
     float s = amax / p.g.qmax;
     if (p.scale_f16) s = round_f16(s);
     float r = recip_or_zero(s);
-    if (threadIdx.x == 0 && p.scales_out) {
-        if (p.scale_f16) reinterpret_cast<__half*>(p.scales_out)[row] = __float2half_rn(s);
-        else reinterpret_cast<float*>(p.scales_out)[row] = s;
-    }
+    if (threadIdx.x == 0 && p.scales_out) store_scale(p, row, s);
 #pragma unroll
     for (int c = 0; c < R; c++) {
         int64_t col = (int64_t)c * kChunk + threadIdx.x * 8;
         if (col >= p.cols) continue;
-        scale_values(v[c], r, (has_k && p.shift_sign < 0) ? k[c] : nullptr);
+        scale_values(v[c], r, has_k && p.shift_sign < 0, kk[c]);
         uint32_t w = pack8(v[c], p.g);
         store_codes(p.packed + row * p.ldp, col, p.cols, w, VEC);
     }
@@ -276,11 +274,11 @@ __global__ void __launch_bounds__(kThreads) quantize_row_reg_kernel(QuantParams 
 
 // ROW mode for longer rows: pass 1 reduces the row max, pass 2 re-reads (L2) and
 // quantizes.
-template <bool VEC>
+template <bool VEC, bool BF16>
 __global__ void __launch_bounds__(kThreads) quantize_row_kernel(QuantParams p) {
     __shared__ float red[kThreads / 64];
     const int64_t row = blockIdx.x;
-    const char* rp = reinterpret_cast<const char*>(p.x) + row * p.ldx * (p.x_bf16 ? 2 : 4);
+    const char* rp = reinterpret_cast<const char*>(p.x) + row * p.ldx * (BF16 ? 2 : 4);
     const bool has_k = p.col_shift != nullptr;
     float amax;
     if (p.amax_in) {
@@ -290,12 +288,8 @@ __global__ void __launch_bounds__(kThreads) quantize_row_kernel(QuantParams p) {
         for (int64_t c0 = 0; c0 < p.cols; c0 += kChunk) {
             int64_t col = c0 + threadIdx.x * 8;
             float v[8];
-            int k[8];
-            load8<VEC>(rp, p.x_bf16, col, p.cols, v);
-            if (has_k && p.shift_sign > 0) {
-                load_shift8<VEC>(p, col, k);
-                shift_inputs(v, k);
-            }
+            load8<VEC, BF16>(rp, col, p.cols, v);
+            if (has_k && p.shift_sign > 0) shift_inputs(v, load_shift8<VEC>(p, col));
             m = fmaxf(m, max_abs8(v));
         }
         m = wave_max(m);
@@ -306,19 +300,15 @@ __global__ void __launch_bounds__(kThreads) quantize_row_kernel(QuantParams p) {
     float s = amax / p.g.qmax;
     if (p.scale_f16) s = round_f16(s);
     float r = recip_or_zero(s);
-    if (threadIdx.x == 0 && p.scales_out) {
-        if (p.scale_f16) reinterpret_cast<__half*>(p.scales_out)[row] = __float2half_rn(s);
-        else reinterpret_cast<float*>(p.scales_out)[row] = s;
-    }
+    if (threadIdx.x == 0 && p.scales_out) store_scale(p, row, s);
     for (int64_t c0 = 0; c0 < p.cols; c0 += kChunk) {
         int64_t col = c0 + threadIdx.x * 8;
         if (col >= p.cols) continue;
         float v[8];
-        int k[8];
-        load8<VEC>(rp, p.x_bf16, col, p.cols, v);
-        if (has_k) load_shift8<VEC>(p, col, k);
+        load8<VEC, BF16>(rp, col, p.cols, v);
+        uint2 k = has_k ? load_shift8<VEC>(p, col) : make_uint2(0, 0);
         if (has_k && p.shift_sign > 0) shift_inputs(v, k);
-        scale_values(v, r, (has_k && p.shift_sign < 0) ? k : nullptr);
+        scale_values(v, r, has_k && p.shift_sign < 0, k);
         uint32_t w = pack8(v, p.g);
         store_codes(p.packed + row * p.ldp, col, p.cols, w, VEC);
     }
@@ -333,28 +323,28 @@ hipError_t launch_tensor_scale_finalize(const float* amax, float* scales_out, fl
     return hipGetLastError();
 }
 
-hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
-    if (p.rows == 0 || p.cols == 0) return hipSuccess;
+template <bool VEC, bool BF16>
+static void quantize_launch(const QuantParams& p, hipStream_t s) {
     if (p.mode == 1) {
         dim3 grid((unsigned)p.rows);
-        if (p.cols <= 4 * kChunk) {
-            if (p.vec) hipLaunchKernelGGL((quantize_row_reg_kernel<true, 4>), grid, dim3(kThreads), 0, s, p);
-            else hipLaunchKernelGGL((quantize_row_reg_kernel<false, 4>), grid, dim3(kThreads), 0, s, p);
-        } else if (p.cols <= 8 * kChunk) {
-            if (p.vec) hipLaunchKernelGGL((quantize_row_reg_kernel<true, 8>), grid, dim3(kThreads), 0, s, p);
-            else hipLaunchKernelGGL((quantize_row_reg_kernel<false, 8>), grid, dim3(kThreads), 0, s, p);
-        } else {
-            if (p.vec) hipLaunchKernelGGL(quantize_row_kernel<true>, grid, dim3(kThreads), 0, s, p);
-            else hipLaunchKernelGGL(quantize_row_kernel<false>, grid, dim3(kThreads), 0, s, p);
-        }
+        if (p.cols <= 4 * kChunk) hipLaunchKernelGGL((quantize_row_reg_kernel<VEC, BF16, 4>), grid, dim3(kThreads), 0, s, p);
+        else if (p.cols <= 8 * kChunk) hipLaunchKernelGGL((quantize_row_reg_kernel<VEC, BF16, 8>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((quantize_row_kernel<VEC, BF16>), grid, dim3(kThreads), 0, s, p);
     } else {
         constexpr int U = 2;
         int64_t chunks = (p.cols + kChunk - 1) / kChunk;
         int64_t nunits = p.rows * chunks;
         dim3 grid((unsigned)((nunits + U - 1) / U));
-        if (p.vec) hipLaunchKernelGGL((quantize_chunk_kernel<true, U>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
-        else hipLaunchKernelGGL((quantize_chunk_kernel<false, U>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
+        hipLaunchKernelGGL((quantize_chunk_kernel<VEC, BF16, U>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
     }
+}
+
+hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
+    if (p.rows == 0 || p.cols == 0) return hipSuccess;
+    if (p.vec && p.x_bf16) quantize_launch<true, true>(p, s);
+    else if (p.vec) quantize_launch<true, false>(p, s);
+    else if (p.x_bf16) quantize_launch<false, true>(p, s);
+    else quantize_launch<false, false>(p, s);
     return hipGetLastError();
 }
 

@@ -188,7 +188,7 @@ def bf16_bits_to_f32(b) -> np.ndarray:
 def reciprocal(s) -> np.ndarray:
     """r = fl32(1/s), and 0 where s == 0 (an all-zero block quantizes to +-0)."""
     s = f32(s)
-    with np.errstate(divide="ignore"):
+    with np.errstate(divide="ignore", over="ignore"):
         r = np.where(s == 0, np.float32(0), np.float32(1) / np.where(s == 0, np.float32(1), s))
     return r.astype(np.float32)
 
