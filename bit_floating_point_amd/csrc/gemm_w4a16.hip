@@ -186,9 +186,149 @@ static void launch_w16(const GemmParams& p, hipStream_t s) {
     else hipLaunchKernelGGL((w4a16_mfma_kernel<0, T, SF16, false>), grid, dim3(256), 0, s, p);
 }
 
+// ---------------------------------------------------------------------------------
+// Decode GEMV for M <= 8 (the latency-critical case).  The activations (M x K bf16,
+// at most 64 KB) are staged once per workgroup in LDS; each wavefront then issues the
+// loads of all its weight chunks (up to 8 x 16 B per lane) and their group scales at
+// once, so a CU keeps its whole share of the weight stream in flight and pays one
+// HBM round trip instead of one per batch.  A fragments come from LDS (rows >= M read
+// row 0: they only feed output rows that are never stored).
+constexpr int kGemvChunks = 8;  // weight chunks per wavefront per round
+
+template <int MODE, bool SF16, int XPT>  // MODE 0 tensor, 1 row, 2 group of 128
+__global__ void __launch_bounds__(256) w4a16_gemv_kernel(GemmParams p) {
+    extern __shared__ uint4 xs[];  // [M][K/8] 16-byte vectors of bf16
+    __shared__ f32x4 part[kW16Waves - 1][64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int64_t n = (int64_t)blockIdx.x * 16 + r16;
+    const bool n_ok = n < p.N;
+    const int64_t nrow = n_ok ? n : 0;
+    const int kv = (int)(p.K / 8);  // 16-byte vectors per activation row
+    const int xvec = (int)p.M * kv;
+    const int nchunks = (int)(p.K / 128);
+    const int c_begin = nchunks * wave / kW16Waves;
+    const int c_end = nchunks * (wave + 1) / kW16Waves;
+    const int64_t ngroups = MODE == 2 ? p.K / 128 : 1;
+    const uint8_t* wrow = p.w + nrow * p.ldw + q * 16;
+    const uint16_t* X = reinterpret_cast<const uint16_t*>(p.a);
+
+    // 1. activation loads first (L2-resident, shared by every workgroup)
+    uint4 xr[XPT];
+#pragma unroll
+    for (int i = 0; i < XPT; i++) {
+        int idx = tid + 256 * i;
+        idx = idx < xvec ? idx : xvec - 1;  // past the activations: re-read the last vector
+        unsigned r = (unsigned)idx / (unsigned)kv, cc = (unsigned)idx % (unsigned)kv;
+        xr[i] = *reinterpret_cast<const uint4*>(X + (int64_t)r * p.lda + (int64_t)cc * 8);
+    }
+    // 2. the first round of weight chunks and scales (loads and LDS stores are
+    // unconditional -- a chunk past the range re-reads a valid one, a vector past the
+    // activations goes to a spare LDS slot -- so no load is sunk into a branch where it
+    // would be waited for at once)
+    uint4 wv[kGemvChunks];
+    uint32_t sc[kGemvChunks];
+#pragma unroll
+    for (int b = 0; b < kGemvChunks; b++) {
+        int c = c_begin + b < c_end ? c_begin + b : c_end - 1;
+        c = c < 0 ? 0 : c;
+        wv[b] = *reinterpret_cast<const uint4*>(wrow + (int64_t)c * 64);
+        if (MODE == 2) sc[b] = load_scale_raw<SF16>(p, nrow * ngroups + c);
+    }
+    // 3. activations into LDS
+#pragma unroll
+    for (int i = 0; i < XPT; i++) {
+        int idx = tid + 256 * i;
+        xs[idx < xvec ? idx : xvec + tid] = xr[i];
+    }
+    __syncthreads();
+
+    const int xrow = (r16 < p.M ? r16 : 0) * kv;
+    f32x4 total = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = c_begin; c0 < c_end; c0 += kGemvChunks) {
+#pragma unroll
+        for (int b = 0; b < kGemvChunks; b++) {
+            const int c = c0 + b;
+            const bool valid = c < c_end;
+            const uint4 w = valid ? wv[b] : make_uint4(0, 0, 0, 0);
+            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+            const int cc = valid ? c : c_begin;
+            f32x4 acc = MODE == 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : total;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                uint4 a = xs[xrow + cc * 16 + q * 4 + j];
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), decode_e2m1_bf16(wd[j]),
+                                                              acc, 0, 0, 0);
+            }
+            if (MODE == 2) {
+                const float sv = valid ? scale_value<SF16>(sc[b]) : 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; i++) total[i] = __builtin_fmaf(acc[i], sv, total[i]);
+            } else {
+                total = acc;
+            }
+        }
+        if (c0 + kGemvChunks < c_end) {
+#pragma unroll
+            for (int b = 0; b < kGemvChunks; b++) {
+                int c = c0 + kGemvChunks + b < c_end ? c0 + kGemvChunks + b : c_end - 1;
+                wv[b] = *reinterpret_cast<const uint4*>(wrow + (int64_t)c * 64);
+                if (MODE == 2) sc[b] = load_scale_raw<SF16>(p, nrow * ngroups + c);
+            }
+        }
+    }
+    if (MODE != 2) {
+        float s = scale_value<SF16>(load_scale_raw<SF16>(p, MODE == 1 ? nrow : 0));
+#pragma unroll
+        for (int i = 0; i < 4; i++) total[i] = total[i] * s;
+    }
+    if (wave > 0) part[wave - 1][lane] = total;
+    __syncthreads();
+    if (wave == 0 && n_ok) {
+#pragma unroll
+        for (int w = 0; w < kW16Waves - 1; w++) {
+            f32x4 o = part[w][lane];
+#pragma unroll
+            for (int i = 0; i < 4; i++) total[i] += o[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            int64_t mm = 4 * q + i;
+            if (mm < p.M) {
+                if (p.y_bf16) reinterpret_cast<__bf16*>(p.y)[mm * p.ldy + n] = (__bf16)total[i];
+                else reinterpret_cast<float*>(p.y)[mm * p.ldy + n] = total[i];
+            }
+        }
+    }
+}
+
+template <int MODE, bool SF16>
+static void launch_gemv(const GemmParams& p, hipStream_t s) {
+    dim3 grid((unsigned)((p.N + 15) / 16));
+    size_t lds = (size_t)p.M * p.K * 2 + 256 * 16;  // activations + one spare slot per thread
+    int xpt = (int)((p.M * p.K / 8 + 255) / 256);
+    if (xpt <= 2) hipLaunchKernelGGL((w4a16_gemv_kernel<MODE, SF16, 2>), grid, dim3(256), lds, s, p);
+    else if (xpt <= 4) hipLaunchKernelGGL((w4a16_gemv_kernel<MODE, SF16, 4>), grid, dim3(256), lds, s, p);
+    else if (xpt <= 8) hipLaunchKernelGGL((w4a16_gemv_kernel<MODE, SF16, 8>), grid, dim3(256), lds, s, p);
+    else hipLaunchKernelGGL((w4a16_gemv_kernel<MODE, SF16, 16>), grid, dim3(256), lds, s, p);
+}
+
 hipError_t launch_w4a16_mfma(const GemmParams& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
-    // small M: one 16-column tile per wavefront keeps the most weight bytes in flight;
+    const bool gemv = p.M <= 8 && p.M * p.K <= 32768 && (p.w_mode != 2 || p.w_group == 128);
+    if (gemv) {
+        const int mode = p.w_mode;
+        if (p.w_scale_f16) {
+            if (mode == 2) launch_gemv<2, true>(p, s);
+            else if (mode == 1) launch_gemv<1, true>(p, s);
+            else launch_gemv<0, true>(p, s);
+        } else {
+            if (mode == 2) launch_gemv<2, false>(p, s);
+            else if (mode == 1) launch_gemv<1, false>(p, s);
+            else launch_gemv<0, false>(p, s);
+        }
+        return hipGetLastError();
+    }
     // larger M: reuse each activation fragment for two weight tiles
     if (p.M > 8) {
         if (p.w_scale_f16) launch_w16<2, true>(p, s);
