@@ -332,6 +332,8 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
     if (p.wg.is_e2m1) {
         if (d->w_gran.mode == FP4_SCALE_GROUP || d->w_gran.scale_dtype != FP4_F32)
             return fail(FP4_ERR_UNSUPPORTED, "E2M1 x E2M1 needs f32 TENSOR or ROW weight scales");
+        // quarter-integer partial sums below 36 K stay exact in fp32 while 36 K < 2^22
+        if (d->K > 116508) return fail(FP4_ERR_UNSUPPORTED, "E2M1 x E2M1 needs K <= 116508 (exact fp32 accumulation)");
         return hip_status(launch_w4a4_fp4(p, s), "fp4_gemm/w4a4");
     }
     if (p.wg.kind == 1) {

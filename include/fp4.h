@@ -235,7 +235,9 @@ fp4_status fp4_search_format(const float* w, int64_t ntensors, int64_t numel,
  *                              (u = the scale units of w_gran along K), fp32 accumulate.
  *   W4A4  (a_kind PACKED):    Y[m,n] = a * sum_u s[n,u] * sum_{k in u} A_q[m,k] W_q[n,k]
  *     - E2M1 x E2M1 with TENSOR/ROW weight scales runs on the FP4 matrix cores; the
- *       code product is exact in fp32 and the epilogue is y = fl32(acc * fl32(a * s_n)).
+ *       code product is exact in fp32 and the epilogue is y = fl32(acc * fl32(a * s_n));
+ *       K <= 116508 (the quarter-integer partial sums stay below 2^22), else
+ *       FP4_ERR_UNSUPPORTED.
  *     - E2M1 activations x LUT16 weights (NF4) with GROUP scales runs on the f16
  *       matrix cores with the group partials scaled in fp32.
  *   y_dtype FP4_BF16 rounds the f32 result to nearest-even.

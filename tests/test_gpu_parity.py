@@ -358,7 +358,20 @@ def test_prefill_full_sampled():
             K = w.shape[1]
             y32 = host(F.fp4_gemm(gap, gwp, gws, fw, fgran, K=K, a_grid=fe2, a_scale=ga, y_dtype=torch.float32))
             _, acc = O.gemm_w4a4(ap[rows], e2, a, wp, e2, "row", ws)
-            assert np.array_equal(y32[rows].view(np.uint32), O.w4a4_epilogue_f32(acc, a, ws).view(np.uint32))
+            pin = O.w4a4_epilogue_f32(acc, a, ws)
+            assert np.array_equal(y32[rows].view(np.uint32), pin.view(np.uint32))
+            # bf16 output (the LDS-staged epilogue): sampled rows against the oracle, the
+            # whole tensor against the rounding of the fp32 output, and a second run
+            # identical bit for bit (a stage overwritten while still being read would
+            # show up as run-to-run differences in a few tiles)
+            yb = host(F.fp4_gemm(gap, gwp, gws, fw, fgran, K=K, a_grid=fe2, a_scale=ga,
+                                 y_dtype=torch.bfloat16).view(torch.int16)).view(np.uint16)
+            assert np.array_equal(yb[rows], O.rne_bf16_bits(pin))
+            assert np.array_equal(yb, O.rne_bf16_bits(y32))
+            yb2 = host(F.fp4_gemm(gap, gwp, gws, fw, fgran, K=K, a_grid=fe2, a_scale=ga,
+                                  y_dtype=torch.bfloat16).view(torch.int16)).view(np.uint16)
+            assert np.array_equal(yb2, yb)
+            del yb, yb2
             if name in ("qkv", "down"):
                 (k, a, wp, ws, ap), (gk, ga, gwp, gws, gap, fw, fgran) = _preshift_chain(x, w, "nf4", 64)
                 y32 = host(F.fp4_gemm(gap, gwp, gws, fw, fgran, K=K, a_grid=fe2, a_scale=ga, y_dtype=torch.float32))
