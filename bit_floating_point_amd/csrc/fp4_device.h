@@ -145,4 +145,39 @@ __device__ __forceinline__ float grid_value(uint32_t c, const QGrid& g) {
     return g.val[c & 15];
 }
 
+// ---- buffer resources and direct-to-LDS loads --------------------------------------
+// Raw buffer resource (stride 0): loads at byte offsets >= `bytes` return zeros, so
+// rows and chunks past the end of an operand need no branch.  Offsets are 32-bit;
+// kOOB is an offset past the end of any buffer this library builds.
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kBufWord3 = 0x00020000;
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4v buf_words(const void* base, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4v{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, kBufWord3};
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_make(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// One direct-to-LDS 16-byte buffer load per lane: lane l writes LDS bytes
+// [lds_base + 16 l, lds_base + 16 l + 16).  Issued from inline assembly so that the
+// compiler's wait-count pass, which cannot tell LDS regions apart, does not add a full
+// wait before every LDS read; callers wait for these loads explicitly.  M0 is declared
+// clobbered: no code of these kernels keeps a value in it (clang warns that it will not
+// preserve a reserved register across the statement, which is fine).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(i32x4v rsrc, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(lds_base), "s"(rsrc)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 }  // namespace fp4

@@ -2,17 +2,20 @@
 // (scales factored out of the low-bit inner product: [FP4-LLM] "efficient matrix
 // multiplication"; [W8A8] section 2.2 quantized_matmul; group size 128).
 //
-// Decode GEMV / small GEMM (M <= 16 per tile) for bf16 activations and E2M1 weights:
-// HBM-bound on the packed weights.  A workgroup owns 16 output columns n and splits
-// K over its 4 wavefronts.  Per 128-wide K chunk a lane streams 16 bytes (32 codes)
-// of one weight row with a single 128-bit load, turns them into bf16 with the gfx950
-// FP4->bf16 convert (exact), and feeds four bf16 16x16x32 MFMAs.  The 4-bit codes of
-// one lane are the B operand of those MFMAs under a fixed permutation of K that the
-// activation operand uses too, so no shuffles are needed.  Each scale group's partial
-// sum is kept apart and multiplied by its scale in fp32 before it joins the total.
-// The 4 wavefront partials are combined through LDS in a fixed order.
+// Two bf16-activation, E2M1-weight kernels run on the bf16 matrix cores; both are
+// HBM-bound on the packed weights.  Per 128-wide K chunk a lane streams 16 bytes (32
+// codes) of one weight row with a single 128-bit load, turns them into bf16 with the
+// gfx950 FP4->bf16 convert (exact), and feeds four bf16 16x16x32 MFMAs.  The 4-bit
+// codes of one lane are the B operand of those MFMAs under a fixed permutation of K
+// that the activation operand uses too, so no shuffles are needed.  Each scale group's
+// partial sum is kept apart and multiplied by its scale in fp32 before it joins the
+// total; the wavefront partials are combined through LDS in a fixed order.
+//  * w4a16_small_kernel (M <= 16, the decode case): activations staged in LDS per
+//    wavefront, all of a batch's weight loads in flight at once.
+//  * w4a16_mfma_kernel (any M, 16-row tiles along M): activation fragments loaded
+//    straight from memory, for shapes the small kernel does not take.
 //
-// A second, plain VALU kernel covers f32 activations and the other grids.
+// A third, plain VALU kernel covers f32 activations and the other grids.
 #include "fp4_device.h"
 
 namespace fp4 {
@@ -22,6 +25,19 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kW16Waves = 4;
 constexpr int kBatch = 4;  // K chunks in flight per wavefront
+
+// Small-M path geometry (host and device): per-wavefront X region in 16-byte vectors,
+// padded to whole 64-lane loads, and the workgroup's dynamic LDS (at most 136 KiB, which
+// leaves room for the static partial-sum array within the CU's 160 KiB).
+constexpr int kSmallWavesPerGroup = 8;
+constexpr size_t kSmallMaxLds = 136 * 1024;
+__host__ __device__ inline int small_region(int64_t M, int64_t nchunks) {
+    const int64_t per_wave = (nchunks + kSmallWavesPerGroup - 1) / kSmallWavesPerGroup;
+    return (int)((M * per_wave * 16 + 63) / 64 * 64);
+}
+inline size_t small_lds_bytes(int64_t M, int64_t K) {
+    return (size_t)kSmallWavesPerGroup * small_region(M, K / 128) * 16;
+}
 
 __device__ __forceinline__ bf16x8 decode_e2m1_bf16(uint32_t w) {
     // byte b of w holds codes 2b (low nibble) and 2b+1
@@ -187,148 +203,223 @@ static void launch_w16(const GemmParams& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------------
-// Decode GEMV for M <= 8 (the latency-critical case).  The activations (M x K bf16,
-// at most 64 KB) are staged once per workgroup in LDS; each wavefront then issues the
-// loads of all its weight chunks (up to 8 x 16 B per lane) and their group scales at
-// once, so a CU keeps its whole share of the weight stream in flight and pays one
-// HBM round trip instead of one per batch.  A fragments come from LDS (rows >= M read
-// row 0: they only feed output rows that are never stored).
-constexpr int kGemvChunks = 8;  // weight chunks per wavefront per round
+// Decode GEMV / small batch, M <= 16 (the latency-critical case).  A workgroup of
+// kSmallWaves wavefronts owns 16*T output columns; wavefront w owns 1/kSmallWaves of K.
+//  * Each wavefront stages only its own K range of X (all M rows) in LDS with
+//    direct-to-LDS loads, so no workgroup barrier precedes the main loop and chunk b is
+//    computed as soon as its weights land.  X bytes cost vector-memory issue slots like
+//    the weights do; the T column tiles of a wavefront share one staged copy.
+//  * Weights and scales come through buffer loads (offsets past the end read zeros), a
+//    batch of kSmallChunks chunks x T tiles at once; with group-128 scales the batch's
+//    scales of a row are one vector load (SV).
+//  * A fragments are read from LDS; rows >= M read row M-1 (they only feed output rows
+//    that are never stored).
+// The per-chunk MFMA sums, their scaling and the cross-wavefront sum are the same
+// operations in the same order as in the kernel above.
+constexpr int kSmallWaves = kSmallWavesPerGroup;
+constexpr int kSmallChunks = 4;  // K chunks per wavefront per batch
 
-template <int MODE, bool SF16, int XPT>  // MODE 0 tensor, 1 row, 2 group of 128
-__global__ void __launch_bounds__(256) w4a16_gemv_kernel(GemmParams p) {
-    extern __shared__ uint4 xs[];  // [M][K/8] 16-byte vectors of bf16
-    __shared__ f32x4 part[kW16Waves - 1][64];
+template <int MODE, bool SF16, bool SV, int T>  // MODE 0 tensor, 1 row, 2 group of 128
+__global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParams p) {
+    constexpr int NW = kSmallWaves, CH = kSmallChunks;
+    extern __shared__ uint4 xs[];  // per wavefront: [M][its K range / 8] bf16 vectors
+    __shared__ f32x4 part[NW - 1][T][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int q = lane >> 4, r16 = lane & 15;
-    const int64_t n = (int64_t)blockIdx.x * 16 + r16;
-    const bool n_ok = n < p.N;
-    const int64_t nrow = n_ok ? n : 0;
-    const int kv = (int)(p.K / 8);  // 16-byte vectors per activation row
-    const int xvec = (int)p.M * kv;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * T;
     const int nchunks = (int)(p.K / 128);
-    const int c_begin = nchunks * wave / kW16Waves;
-    const int c_end = nchunks * (wave + 1) / kW16Waves;
+    const int c_begin = nchunks * wave / NW;
+    const int c_end = nchunks * (wave + 1) / NW;
+    // X vectors of one row in this wavefront's range (at least one chunk, so that a
+    // wavefront with an empty range still forms valid addresses)
+    const int nvw = c_end - c_begin > 0 ? (c_end - c_begin) * 16 : 16;
+    const int xw = (int)p.M * nvw;
+    const int region = small_region(p.M, nchunks);
+    const int wbase = wave * region;
     const int64_t ngroups = MODE == 2 ? p.K / 128 : 1;
-    const uint8_t* wrow = p.w + nrow * p.ldw + q * 16;
-    const uint16_t* X = reinterpret_cast<const uint16_t*>(p.a);
+    constexpr int SB = SF16 ? 2 : 4;       // bytes per scale
+    constexpr int SVB = CH * SB;           // bytes of one batch's scales of a row (8 or 16)
+    const __amdgpu_buffer_rsrc_t rsW = buf_make(p.w, p.N * p.ldw);
+    const __amdgpu_buffer_rsrc_t rsS = buf_make(p.w_scales, p.N * ngroups * SB);
+    uint32_t wrow[T], srow[T];
+    bool n_ok[T];
+#pragma unroll
+    for (int t = 0; t < T; t++) {
+        const int64_t n = n0 + 16 * t + r16;
+        n_ok[t] = n < p.N;
+        wrow[t] = n_ok[t] ? (uint32_t)(n * p.ldw + q * 16) : kOOB;
+        srow[t] = n_ok[t] ? (uint32_t)(n * ngroups * SB) : kOOB;
+    }
 
-    // 1. activation loads first (L2-resident, shared by every workgroup)
-    uint4 xr[XPT];
-#pragma unroll
-    for (int i = 0; i < XPT; i++) {
-        int idx = tid + 256 * i;
-        idx = idx < xvec ? idx : xvec - 1;  // past the activations: re-read the last vector
-        unsigned r = (unsigned)idx / (unsigned)kv, cc = (unsigned)idx % (unsigned)kv;
-        xr[i] = *reinterpret_cast<const uint4*>(X + (int64_t)r * p.lda + (int64_t)cc * 8);
+    // 1. this wavefront's X into its LDS region: load i puts vector 64 i + l of the
+    //    region (row m = v / nvw, vector v % nvw of the range) at lane l; vectors past
+    //    the range read zeros into the region's padding
+    {
+        const i32x4v rs = buf_words(p.a, (((int64_t)p.M - 1) * p.lda + p.K) * 2);
+        for (int i = 0; 64 * i < region; i++) {
+            const int v = lane + 64 * i;
+            const int m = (unsigned)v / (unsigned)nvw, cc = v - m * nvw;
+            const uint32_t off = v < xw ? (uint32_t)((m * p.lda + (c_begin * 16 + cc) * 8) * 2) : kOOB;
+            dma16(rs, off, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&xs[wbase + 64 * i]));
+        }
     }
-    // 2. the first round of weight chunks and scales (loads and LDS stores are
-    // unconditional -- a chunk past the range re-reads a valid one, a vector past the
-    // activations goes to a spare LDS slot -- so no load is sunk into a branch where it
-    // would be waited for at once)
-    uint4 wv[kGemvChunks];
-    uint32_t sc[kGemvChunks];
+    // 2. a batch of weights and scales; chunks past the range are loaded too (they
+    //    belong to the next range or read zeros) and contribute nothing
+    uint4 wv[CH][T];
+    uint4 sv[T];
+    uint32_t sc[CH][T];
+    auto load_batch = [&](int cs) {
+        if (MODE == 2 && SV) {
 #pragma unroll
-    for (int b = 0; b < kGemvChunks; b++) {
-        int c = c_begin + b < c_end ? c_begin + b : c_end - 1;
-        c = c < 0 ? 0 : c;
-        wv[b] = *reinterpret_cast<const uint4*>(wrow + (int64_t)c * 64);
-        if (MODE == 2) sc[b] = load_scale_raw<SF16>(p, nrow * ngroups + c);
-    }
-    // 3. activations into LDS
+            for (int t = 0; t < T; t++) {
+                if (SVB == 8) {
+                    const uint2 u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsS, srow[t] + cs * SB, 0, 0));
+                    sv[t] = make_uint4(u.x, u.y, 0, 0);
+                } else {
+                    sv[t] = buf_load16(rsS, srow[t] + cs * SB);
+                }
+            }
+        }
 #pragma unroll
-    for (int i = 0; i < XPT; i++) {
-        int idx = tid + 256 * i;
-        xs[idx < xvec ? idx : xvec + tid] = xr[i];
-    }
-    __syncthreads();
+        for (int b = 0; b < CH; b++) {
+#pragma unroll
+            for (int t = 0; t < T; t++) {
+                wv[b][t] = buf_load16(rsW, wrow[t] + (uint32_t)(cs + b) * 64);
+                if (MODE == 2 && !SV) {
+                    const uint32_t off = srow[t] + (uint32_t)(cs + b) * SB;
+                    sc[b][t] = SF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsS, off, 0, 0)
+                                    : __builtin_amdgcn_raw_buffer_load_b32(rsS, off, 0, 0);
+                }
+            }
+        }
+    };
+    load_batch(c_begin);
+    // 3. the X loads are the oldest in flight: wait until only the batch's loads remain
+    constexpr int kLater = CH * T + (MODE == 2 ? (SV ? T : CH * T) : 0);
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kLater) : "memory");
 
-    const int xrow = (r16 < p.M ? r16 : 0) * kv;
-    f32x4 total = {0.f, 0.f, 0.f, 0.f};
-    for (int c0 = c_begin; c0 < c_end; c0 += kGemvChunks) {
+    const int xrow = wbase + (r16 < p.M ? r16 : (int)p.M - 1) * nvw - c_begin * 16;
+    f32x4 total[T];
 #pragma unroll
-        for (int b = 0; b < kGemvChunks; b++) {
+    for (int t = 0; t < T; t++) total[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = c_begin; c0 < c_end; c0 += CH) {
+        if (MODE == 2 && SV) {
+#pragma unroll
+            for (int t = 0; t < T; t++) {
+                const uint32_t sw[4] = {sv[t].x, sv[t].y, sv[t].z, sv[t].w};
+#pragma unroll
+                for (int b = 0; b < CH; b++) sc[b][t] = SF16 ? ((sw[b >> 1] >> (16 * (b & 1))) & 0xffffu) : sw[b];
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < CH; b++) {
             const int c = c0 + b;
             const bool valid = c < c_end;
-            const uint4 w = valid ? wv[b] : make_uint4(0, 0, 0, 0);
-            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
             const int cc = valid ? c : c_begin;
-            f32x4 acc = MODE == 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : total;
+            uint4 xa[4];
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                uint4 a = xs[xrow + cc * 16 + q * 4 + j];
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), decode_e2m1_bf16(wd[j]),
-                                                              acc, 0, 0, 0);
-            }
-            if (MODE == 2) {
-                const float sv = valid ? scale_value<SF16>(sc[b]) : 0.0f;
+            for (int j = 0; j < 4; j++) xa[j] = xs[xrow + cc * 16 + q * 4 + j];
 #pragma unroll
-                for (int i = 0; i < 4; i++) total[i] = __builtin_fmaf(acc[i], sv, total[i]);
-            } else {
-                total = acc;
-            }
-        }
-        if (c0 + kGemvChunks < c_end) {
+            for (int t = 0; t < T; t++) {
+                const uint32_t wd[4] = {wv[b][t].x, wv[b][t].y, wv[b][t].z, wv[b][t].w};
+                f32x4 acc = MODE == 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : total[t];
 #pragma unroll
-            for (int b = 0; b < kGemvChunks; b++) {
-                int c = c0 + kGemvChunks + b < c_end ? c0 + kGemvChunks + b : c_end - 1;
-                wv[b] = *reinterpret_cast<const uint4*>(wrow + (int64_t)c * 64);
-                if (MODE == 2) sc[b] = load_scale_raw<SF16>(p, nrow * ngroups + c);
+                for (int j = 0; j < 4; j++)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[j]),
+                                                                  decode_e2m1_bf16(wd[j]), acc, 0, 0, 0);
+                if (MODE == 2) {
+                    const float s = valid ? scale_value<SF16>(sc[b][t]) : 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; i++) total[t][i] = __builtin_fmaf(acc[i], s, total[t][i]);
+                } else {
+                    total[t] = valid ? acc : total[t];
+                }
             }
         }
+        if (c0 + CH < c_end) load_batch(c0 + CH);
     }
-    if (MODE != 2) {
-        float s = scale_value<SF16>(load_scale_raw<SF16>(p, MODE == 1 ? nrow : 0));
 #pragma unroll
-        for (int i = 0; i < 4; i++) total[i] = total[i] * s;
+    for (int t = 0; t < T; t++) {
+        if (MODE != 2) {
+            const float s = scale_value<SF16>(load_scale_raw<SF16>(p, MODE == 1 ? (n_ok[t] ? n0 + 16 * t + r16 : 0) : 0));
+#pragma unroll
+            for (int i = 0; i < 4; i++) total[t][i] = total[t][i] * s;
+        }
+        if (wave > 0) part[wave - 1][t][lane] = total[t];
     }
-    if (wave > 0) part[wave - 1][lane] = total;
     __syncthreads();
-    if (wave == 0 && n_ok) {
+    if (wave == 0) {
 #pragma unroll
-        for (int w = 0; w < kW16Waves - 1; w++) {
-            f32x4 o = part[w][lane];
+        for (int t = 0; t < T; t++) {
 #pragma unroll
-            for (int i = 0; i < 4; i++) total[i] += o[i];
-        }
+            for (int w = 0; w < NW - 1; w++) {
+                const f32x4 o = part[w][t][lane];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            int64_t mm = 4 * q + i;
-            if (mm < p.M) {
-                if (p.y_bf16) reinterpret_cast<__bf16*>(p.y)[mm * p.ldy + n] = (__bf16)total[i];
-                else reinterpret_cast<float*>(p.y)[mm * p.ldy + n] = total[i];
+                for (int i = 0; i < 4; i++) total[t][i] += o[i];
+            }
+            if (!n_ok[t]) continue;
+            const int64_t n = n0 + 16 * t + r16;
+            // D layout of a 16x16 MFMA: lane holds rows 4*(lane/16) + i of column lane%16
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int64_t mm = 4 * q + i;
+                if (mm < p.M) {
+                    if (p.y_bf16) reinterpret_cast<__bf16*>(p.y)[mm * p.ldy + n] = (__bf16)total[t][i];
+                    else reinterpret_cast<float*>(p.y)[mm * p.ldy + n] = total[t][i];
+                }
             }
         }
     }
 }
 
-template <int MODE, bool SF16>
-static void launch_gemv(const GemmParams& p, hipStream_t s) {
-    dim3 grid((unsigned)((p.N + 15) / 16));
-    size_t lds = (size_t)p.M * p.K * 2 + 256 * 16;  // activations + one spare slot per thread
-    int xpt = (int)((p.M * p.K / 8 + 255) / 256);
-    if (xpt <= 2) hipLaunchKernelGGL((w4a16_gemv_kernel<MODE, SF16, 2>), grid, dim3(256), lds, s, p);
-    else if (xpt <= 4) hipLaunchKernelGGL((w4a16_gemv_kernel<MODE, SF16, 4>), grid, dim3(256), lds, s, p);
-    else if (xpt <= 8) hipLaunchKernelGGL((w4a16_gemv_kernel<MODE, SF16, 8>), grid, dim3(256), lds, s, p);
-    else hipLaunchKernelGGL((w4a16_gemv_kernel<MODE, SF16, 16>), grid, dim3(256), lds, s, p);
+template <int MODE, bool SF16, bool SV, int T>
+static hipError_t launch_small_t(const GemmParams& p, hipStream_t s) {
+    const size_t lds = small_lds_bytes(p.M, p.K);
+    auto kern = w4a16_small_kernel<MODE, SF16, SV, T>;
+    // the dynamic-LDS limit is a kernel attribute, set once per device
+    static bool attr_set[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+        e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmallMaxLds);
+        if (e != hipSuccess) return e;
+        if (dev >= 0 && dev < 64) attr_set[dev] = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)((p.N + 16 * T - 1) / (16 * T))), dim3(kSmallWaves * 64), lds, s, p);
+    return hipGetLastError();
+}
+
+template <int MODE, bool SF16, bool SV>
+static hipError_t launch_small_sv(const GemmParams& p, hipStream_t s) {
+    // M <= 4: one 16-column tile per wavefront (more workgroups, X is small);
+    // larger M: three tiles share each staged X
+    return p.M <= 4 ? launch_small_t<MODE, SF16, SV, 1>(p, s) : launch_small_t<MODE, SF16, SV, 3>(p, s);
+}
+
+template <bool SF16>
+static hipError_t launch_small(const GemmParams& p, hipStream_t s) {
+    if (p.w_mode == 2) {
+        const int64_t nchunks = p.K / 128;
+        // one vector load per batch needs 4-byte aligned scale rows and batch starts
+        const bool sv = SF16 ? (nchunks % (2 * kSmallWaves) == 0 && (reinterpret_cast<uintptr_t>(p.w_scales) & 3) == 0)
+                             : (reinterpret_cast<uintptr_t>(p.w_scales) & 3) == 0;
+        return sv ? launch_small_sv<2, SF16, true>(p, s) : launch_small_sv<2, SF16, false>(p, s);
+    }
+    if (p.w_mode == 1) return launch_small_sv<1, SF16, false>(p, s);
+    return launch_small_sv<0, SF16, false>(p, s);
 }
 
 hipError_t launch_w4a16_mfma(const GemmParams& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
-    const bool gemv = p.M <= 8 && p.M * p.K <= 32768 && (p.w_mode != 2 || p.w_group == 128);
-    if (gemv) {
-        const int mode = p.w_mode;
-        if (p.w_scale_f16) {
-            if (mode == 2) launch_gemv<2, true>(p, s);
-            else if (mode == 1) launch_gemv<1, true>(p, s);
-            else launch_gemv<0, true>(p, s);
-        } else {
-            if (mode == 2) launch_gemv<2, false>(p, s);
-            else if (mode == 1) launch_gemv<1, false>(p, s);
-            else launch_gemv<0, false>(p, s);
-        }
-        return hipGetLastError();
-    }
+    const int64_t ngroups = p.w_mode == 2 ? p.K / 128 : 1;
+    const int64_t sbytes = p.w_scale_f16 ? 2 : 4;
+    const bool small = p.M <= 16 && (p.w_mode != 2 || p.w_group == 128) &&
+                       small_lds_bytes(p.M, p.K) <= kSmallMaxLds &&
+                       // 32-bit buffer offsets
+                       p.N * p.ldw < kOOB && p.N * ngroups * sbytes < kOOB &&
+                       ((p.M - 1) * p.lda + p.K) * 2 < (int64_t)kOOB;
+    if (small) return p.w_scale_f16 ? launch_small<true>(p, s) : launch_small<false>(p, s);
     // larger M: reuse each activation fragment for two weight tiles
     if (p.M > 8) {
         if (p.w_scale_f16) launch_w16<2, true>(p, s);

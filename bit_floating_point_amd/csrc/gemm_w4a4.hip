@@ -41,25 +41,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // consecutive codes (16 B) of row l%32 at K offset 32*(l/32); D layout: lane l, value v
 // holds D[8*(v/4) + 4*(l/32) + v%4][l%32].  A bf16 result tile is staged in LDS and
 // written with whole-row 16-byte stores.
-constexpr uint32_t kOOB = 0x80000000u;
-constexpr int kBufWord3 = 0x00020000;
-
-// One direct-to-LDS 16-byte buffer load per lane: LDS destination = M0 + 16 * lane.
-// Issued from inline assembly (it has no register outputs) so that the compiler's
-// wait-count pass, which cannot tell the LDS stages apart, does not add a full wait
-// before every LDS read; the kernel waits for each stage explicitly instead.
-// M0 is declared clobbered: no code of these kernels keeps a value in it (clang warns
-// that it will not preserve a reserved register across the statement, which is fine).
-typedef int i32x4v __attribute__((ext_vector_type(4)));
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(i32x4v rsrc, uint32_t voff, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-                 :
-                 : "v"(voff), "s"(lds_base), "s"(rsrc)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // Wait until at most N direct-to-LDS loads of this thread are in flight and every LDS
 // read of this wavefront has returned, then meet the workgroup barrier.  The LDS reads
@@ -89,9 +70,8 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m)
     const int nk = (int)((p.K + 127) / 128);
 
     // buffer resources (base, stride 0, size in bytes, format word)
-    const uint64_t pa = reinterpret_cast<uint64_t>(p.a), pw = reinterpret_cast<uint64_t>(p.w);
-    const i32x4v rsA = {(int)(uint32_t)pa, (int)(uint32_t)(pa >> 32), (int)(p.M * p.lda), kBufWord3};
-    const i32x4v rsB = {(int)(uint32_t)pw, (int)(uint32_t)(pw >> 32), (int)(p.N * p.ldw), kBufWord3};
+    const i32x4v rsA = buf_words(p.a, p.M * p.lda);
+    const i32x4v rsB = buf_words(p.w, p.N * p.ldw);
     // the global piece behind this lane's LDS slot, for each of its LA + LB loads: slot
     // s = (4 i + wave) * 64 + lane holds row s/4, swizzled segment s%4 (see swz)
     uint32_t offA[LA], offB[LB];

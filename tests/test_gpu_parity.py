@@ -201,6 +201,42 @@ def test_w4a16_shapes(M, N, K, mode, group, fmt, bf16):
     assert O.rel_err(host(y32), r) <= TOL
 
 
+@pytest.mark.parametrize("M,N,K,mode,sd", [
+    (1, 100, 128, "group", "f16"),     # one K chunk: seven of eight wavefronts own no K
+    (9, 61, 2176, "group", "f16"),     # 17 chunks: per-chunk scale loads, three tiles, ragged N
+    (16, 100, 4096, "group", "f32"),   # f32 group scales as vector loads, M = 16
+    (2, 50, 1024, "tensor", "f32"),    # one scale for the tensor
+    (12, 70, 768, "row", "f32"),       # per-row scales, three tiles
+    (8, 40, 8192, "group", "f16"),     # 128 KiB of staged activations
+    (16, 40, 8192, "group", "f16"),    # too large to stage: the two-tile kernel
+    (4, 1000, 4096, "group", "f16"),   # decode shape, many workgroups
+])
+def test_w4a16_small_batch(M, N, K, mode, sd):
+    """Decode / small-batch W4A16 (M <= 16, bf16 activations, E2M1): the staged-
+    activation kernel across its geometry cases, within tolerance of the oracle, bf16
+    output the rounding of the fp32 output."""
+    say("w4a16 small", M, N, K, mode, sd)
+    w = synth.weight(2, 13, N, K)
+    x = synth.activations(2, 14, M, K, bf16=True)
+    og, fg = grids((2, 1))
+    group = 128 if mode == "group" else 0
+    packed, scales = O.quantize_pack(w, og, mode, group, sd)
+    g = F.gran(mode, group, sd)
+    gp, gs = F.fp4_quantize_pack(dev(w), fg, g)
+    assert np.array_equal(host(gp), packed)
+    r = O.gemm_w4a16(x, packed, og, mode, scales, group=group)
+    xt = dev(x, torch.bfloat16)
+    y32 = F.fp4_gemm(xt, gp, gs, fg, g, y_dtype=torch.float32)
+    err = O.rel_err(host(y32), r)
+    say("  rel err", err)
+    assert err <= TOL
+    yb = F.fp4_gemm(xt, gp, gs, fg, g, y_dtype=torch.bfloat16)
+    assert np.array_equal(host(yb.view(torch.int16)).view(np.uint16), O.rne_bf16_bits(host(y32)))
+    # a second call gives the same bits (no state carried between launches)
+    y32b = F.fp4_gemm(xt, gp, gs, fg, g, y_dtype=torch.float32)
+    assert np.array_equal(host(y32b).view(np.uint32), host(y32).view(np.uint32))
+
+
 # ---------------------------------------------------------------- pre-shift + W4A4 --
 def _preshift_chain(x, w, w_fmt="e2m1", group=64):
     """Oracle and GPU through calibrate -> pre-shift -> quantize -> GEMM; compares
