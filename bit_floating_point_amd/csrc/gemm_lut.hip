@@ -2,186 +2,344 @@
 // section NF4, levels at quantiles of the normal distribution) and E2M1 activations
 // with the pre-shifted per-tensor scale a:
 //   Y[m, n] = a * sum_g s[n, g] * sum_{k in g} A_q[m, k] * G[c[n, k]]
-// Scales stay outside the low-bit products ([FP4-LLM] "efficient matrix
-// multiplication"): each K group's partial sum is formed on the matrix cores and only
-// then multiplied by its fp32 block scale.
 //
-// gfx950 has no matrix instruction for an arbitrary 16-value grid, so both operands
-// are decoded to f16 in registers (E2M1 via the FP4->f16 convert; the lookup grid via
-// byte permutes of a 32-byte table held in scalar registers; both exact because the
-// grid values are binary16 numbers) and fed to v_mfma_f32_16x16x32_f16.
-// Tiling: 128x128 output tile per 256-thread workgroup, 64x64 per wavefront (4x4
-// accumulators), K step = one 64-code group; packed codes staged in LDS, double
-// buffered, 8-byte segments XOR-swizzled against bank conflicts.
+// gfx950 has no matrix instruction for an arbitrary 16-value grid, so both operands are
+// expanded to f16 once per workgroup and K step, into LDS, and the products run on
+// v_mfma_f32_32x32x16_f16 with fp32 accumulation:
+//  * activations: E2M1 -> f16 with the FP4 convert (exact);
+//  * weights: G[c] by byte permutes of a table held in registers (exact: the grid values
+//    are binary16), times the group scale taken relative to a power of two of the row:
+//    w = fl16(G[c] * fl16(s[n, g] * 2^-e_n)) with 2^e_n the power of two just above the
+//    row's largest group scale, so no scaled weight overflows and only groups whose scale
+//    is far below the row's largest can reach f16 subnormals.  2^e_n and a are applied
+//    to the fp32 result (exactly).  Folding the scale into the expanded weights keeps
+//    the group scales out of the per-output arithmetic: one multiply per weight per
+//    workgroup instead of one per output element and group.
+// The LDS tiles are stored in MFMA fragment order (each 16-byte operand of lane l of a
+// 32-row tile and K16 block at byte 16 l of a 1 KiB block), so every fragment read is
+// one linear wavefront read.  Two LDS stages: while step k's MFMAs run, each wavefront
+// expands a quarter of step k+1 after every K16 block of MFMAs (interleaved so that the
+// VALU work overlaps the matrix work); packed codes for step k+2 are loaded meanwhile.
+// Tiles: 256x256 (4 wavefronts of 128x128) for large grids, 128x128 otherwise.
+#include <algorithm>
+
 #include "fp4_device.h"
 
 namespace fp4 {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kLutBM = 128, kLutBN = 128, kLutBK = 64;  // BK in codes
-constexpr int kRowBytes = kLutBK / 2;                    // 32
+constexpr int kLutBK = 64;  // K codes per step (one 64-code group)
 
-__device__ __forceinline__ int swz8(int row, int q) { return row * kRowBytes + ((q ^ ((row >> 2) & 3)) << 3); }
-
-__device__ __forceinline__ f16x8 decode_e2m1_f16(uint32_t w) {
-    uint32_t o[4];
-    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
-    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
-    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
-    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
-    return __builtin_bit_cast(f16x8, o);
+// 8 E2M1 codes (element 2j in the low nibble of byte j) -> 8 f16 values, exact
+__device__ __forceinline__ uint4 decode_e2m1_f16x8(uint32_t w) {
+    uint4 o;
+    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
+    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
+    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
+    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
+    return o;
 }
 
 // byte lookup T[idx] for the 4 byte-indices (0..15) of idx; T is 16 bytes in 4 words
 __device__ __forceinline__ uint32_t lut_bytes(uint32_t idx, const uint32_t T[4]) {
-    uint32_t i7 = idx & 0x07070707u;
-    uint32_t lo = __builtin_amdgcn_perm(T[1], T[0], i7);
-    uint32_t hi = __builtin_amdgcn_perm(T[3], T[2], i7);
-    uint32_t msk = ((idx >> 3) & 0x01010101u) * 0xFFu;
-    return (hi & msk) | (lo & ~msk);
+    const uint32_t i7 = idx & 0x07070707u;
+    const uint32_t lo = __builtin_amdgcn_perm(T[1], T[0], i7);  // T[i & 7] for i < 8
+    const uint32_t hi = __builtin_amdgcn_perm(T[3], T[2], i7);  // T[8 + (i & 7)]
+    // byte j from lo (selector j) or hi (selector 4 + j) by bit 3 of index byte j
+    const uint32_t sel = ((idx >> 1) & 0x04040404u) | 0x03020100u;
+    return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// 8 lookup-grid codes (element 2j in the low nibble of byte j) -> 8 f16 values
-__device__ __forceinline__ f16x8 decode_lut_f16(uint32_t w, const uint32_t TL[4], const uint32_t TH[4]) {
-    uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
-    uint32_t eL = lut_bytes(ev, TL), eH = lut_bytes(ev, TH);
-    uint32_t oL = lut_bytes(od, TL), oH = lut_bytes(od, TH);
-    uint32_t e01 = __builtin_amdgcn_perm(eH, eL, 0x05010400u);  // f16(x0) | f16(x2) << 16
-    uint32_t e23 = __builtin_amdgcn_perm(eH, eL, 0x07030602u);  // f16(x4) | f16(x6) << 16
-    uint32_t o01 = __builtin_amdgcn_perm(oH, oL, 0x05010400u);  // f16(x1) | f16(x3) << 16
-    uint32_t o23 = __builtin_amdgcn_perm(oH, oL, 0x07030602u);  // f16(x5) | f16(x7) << 16
-    uint32_t o[4];
-    o[0] = __builtin_amdgcn_perm(o01, e01, 0x05040100u);
-    o[1] = __builtin_amdgcn_perm(o01, e01, 0x07060302u);
-    o[2] = __builtin_amdgcn_perm(o23, e23, 0x05040100u);
-    o[3] = __builtin_amdgcn_perm(o23, e23, 0x07060302u);
-    return __builtin_bit_cast(f16x8, o);
+// 8 lookup-grid codes -> 8 f16 grid values (exact: the grid values are binary16)
+__device__ __forceinline__ uint4 decode_lut_f16x8(uint32_t w, const uint32_t TL[4], const uint32_t TH[4]) {
+    const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
+    const uint32_t eL = lut_bytes(ev, TL), eH = lut_bytes(ev, TH);
+    const uint32_t oL = lut_bytes(od, TL), oH = lut_bytes(od, TH);
+    const uint32_t e01 = __builtin_amdgcn_perm(eH, eL, 0x05010400u);  // f16(x0) | f16(x2) << 16
+    const uint32_t e23 = __builtin_amdgcn_perm(eH, eL, 0x07030602u);  // f16(x4) | f16(x6) << 16
+    const uint32_t o01 = __builtin_amdgcn_perm(oH, oL, 0x05010400u);  // f16(x1) | f16(x3) << 16
+    const uint32_t o23 = __builtin_amdgcn_perm(oH, oL, 0x07030602u);  // f16(x5) | f16(x7) << 16
+    uint4 o;
+    o.x = __builtin_amdgcn_perm(o01, e01, 0x05040100u);
+    o.y = __builtin_amdgcn_perm(o01, e01, 0x07060302u);
+    o.z = __builtin_amdgcn_perm(o23, e23, 0x05040100u);
+    o.w = __builtin_amdgcn_perm(o23, e23, 0x07060302u);
+    return o;
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, f16x2 s) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) * s);
+}
+
+template <int BM, int BN>
 __global__ void __launch_bounds__(256) w4a4_lut_kernel(GemmParams p, int grid_m) {
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2][kLutBM * kRowBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[2][kLutBN * kRowBytes];
+    constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+    constexpr int A_BYTES = BM * kLutBK * 2, B_BYTES = BN * kLutBK * 2;  // f16 per stage
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int PA = BM * 2 / 256, PB = BN * 2 / 256;  // 16-byte packed pieces per thread per step
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+    __shared__ float rowfac[BN];  // 2^e_n for the tile's weight rows
+
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
-    const int64_t m0 = (int64_t)(blockIdx.x % grid_m) * kLutBM;
-    const int64_t n0 = (int64_t)(blockIdx.x / grid_m) * kLutBN;
-    const int64_t nk = p.K / kLutBK;
+    const int64_t m0 = (int64_t)(blockIdx.x % grid_m) * BM;
+    const int64_t n0 = (int64_t)(blockIdx.x / grid_m) * BN;
+    const int nk = (int)(p.K / kLutBK);
     const int steps_per_group = p.w_group / kLutBK;
     const int64_t ngroups = p.K / p.w_group;
-    const uint8_t* A = reinterpret_cast<const uint8_t*>(p.a);
+    const int sb = p.w_scale_f16 ? 2 : 4;
 
     // f16 bit patterns of the 16 grid values, split into low and high byte tables
     uint32_t TL[4] = {0, 0, 0, 0}, TH[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)p.wg.val[i]);
+        const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)p.wg.val[i]);
         TL[i >> 2] |= (h & 0xffu) << (8 * (i & 3));
         TH[i >> 2] |= (h >> 8) << (8 * (i & 3));
     }
 
-    // global -> LDS: 128 rows x 32 bytes per operand = 256 x 16 B, one load per thread
-    const int lrow = tid >> 1, lseg = tid & 1;
-    uint4 ra, rb;
-    // unconditional loads (out-of-range rows read row 0 and are zeroed by a select): one
-    // basic block per K step, so the LDS stores stay after the MFMAs
-    auto gload = [&](int64_t kb) {
-        int64_t gm = m0 + lrow, gn = n0 + lrow;
-        bool oka = gm < p.M, okb = gn < p.N;
-        uint4 va = *reinterpret_cast<const uint4*>(A + (oka ? gm : 0) * p.lda + kb * kRowBytes + lseg * 16);
-        uint4 vb = *reinterpret_cast<const uint4*>(p.w + (okb ? gn : 0) * p.ldw + kb * kRowBytes + lseg * 16);
-        ra = oka ? va : make_uint4(0, 0, 0, 0);
-        rb = okb ? vb : make_uint4(0, 0, 0, 0);
-    };
-    auto sstore = [&](int st) {
-        // the 16-byte segment holds two 8-byte units q = 2*lseg, 2*lseg+1
-        *reinterpret_cast<uint2*>(&sA[st][swz8(lrow, 2 * lseg)]) = make_uint2(ra.x, ra.y);
-        *reinterpret_cast<uint2*>(&sA[st][swz8(lrow, 2 * lseg + 1)]) = make_uint2(ra.z, ra.w);
-        *reinterpret_cast<uint2*>(&sB[st][swz8(lrow, 2 * lseg)]) = make_uint2(rb.x, rb.y);
-        *reinterpret_cast<uint2*>(&sB[st][swz8(lrow, 2 * lseg + 1)]) = make_uint2(rb.z, rb.w);
-    };
+    const __amdgpu_buffer_rsrc_t rsA = buf_make(p.a, p.M * p.lda);
+    const __amdgpu_buffer_rsrc_t rsW = buf_make(p.w, p.N * p.ldw);
+    const __amdgpu_buffer_rsrc_t rsS = buf_make(p.w_scales, p.N * ngroups * sb);
 
-    f32x4 acc[4][4], blk[4][4];
+    // the weight rows' power of two: e_n with max_g s[n, g] * 2^-e_n in [0.5, 1).  Row r's
+    // scales are read in 16-byte pieces, eight loads in flight (pieces past the row read
+    // another row's scales or zeros: they are masked out)
+    for (int r = tid; r < BN; r += 256) {
+        const int64_t n = n0 + r;
+        float mx = 0.0f;
+        if (n < p.N) {
+            // the row's bytes [lo, hi) of the scale array, read from a 16-byte aligned start
+            const int64_t lo = n * ngroups * sb, hi = lo + ngroups * sb;
+            for (int64_t b = lo & ~(int64_t)15; b < hi; b += 8 * 16) {
+                uint4 v[8];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+                for (int u = 0; u < 8; u++) v[u] = buf_load16(rsS, (uint32_t)(b + 16 * u));
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = blk[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int q = lane >> 4, r16 = lane & 15;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int64_t kb = 0; kb < nk; kb++) {
-        const int st = (int)(kb & 1);
-        gload(kb + 1 < nk ? kb + 1 : kb);
-        // lane holds codes [q*16, q*16+16) of its row: sub-step u uses the u-th 8
-        f16x8 af[4][2];
+                for (int u = 0; u < 8; u++) {
+                    const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            uint2 v = *reinterpret_cast<const uint2*>(&sA[st][swz8(wm * 64 + i * 16 + r16, q)]);
-            af[i][0] = decode_e2m1_f16(v.x);
-            af[i][1] = decode_e2m1_f16(v.y);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            uint2 v = *reinterpret_cast<const uint2*>(&sB[st][swz8(wn * 64 + j * 16 + r16, q)]);
-            f16x8 b0 = decode_lut_f16(v.x, TL, TH);
-            f16x8 b1 = decode_lut_f16(v.y, TL, TH);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                blk[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i][0], b0, blk[i][j], 0, 0, 0);
-                blk[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i][1], b1, blk[i][j], 0, 0, 0);
-            }
-        }
-        if ((kb + 1) % steps_per_group == 0) {
-            int64_t g = kb / steps_per_group;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                int64_t n = n0 + wn * 64 + j * 16 + r16;
-                float s = 0.0f;
-                if (n < p.N) s = p.w_scale_f16 ? __half2float(reinterpret_cast<const __half*>(p.w_scales)[n * ngroups + g])
-                                               : reinterpret_cast<const float*>(p.w_scales)[n * ngroups + g];
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-#pragma unroll
-                    for (int t = 0; t < 4; t++) acc[i][j][t] = __builtin_fmaf(blk[i][j][t], s, acc[i][j][t]);
-                    blk[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int q = 0; q < 4; q++) {
+                        const int64_t at = b + 16 * u + 4 * q;  // byte offset of this word
+                        if (p.w_scale_f16) {
+                            const float s0 = __half2float(__ushort_as_half((unsigned short)(w4[q] & 0xffffu)));
+                            const float s1 = __half2float(__ushort_as_half((unsigned short)(w4[q] >> 16)));
+                            if (at >= lo && at < hi) mx = fmaxf(mx, s0);
+                            if (at + 2 >= lo && at + 2 < hi) mx = fmaxf(mx, s1);
+                        } else {
+                            if (at >= lo && at < hi) mx = fmaxf(mx, __uint_as_float(w4[q]));
+                        }
+                    }
                 }
             }
         }
-        // keep the LDS stores (which wait for this step's global loads) after the MFMAs,
-        // so the loads for step kb+1 overlap the matrix work of step kb
-        __builtin_amdgcn_sched_barrier(0);
-        sstore(st ^ 1);
+        int e = 0;
+        if (mx > 0.0f) (void)frexpf(mx, &e);
+        rowfac[r] = ldexpf(1.0f, e);
+    }
+
+    // packed pieces of this thread: piece q covers row q/2, codes 32*(q%2) .. +31 of a step
+    uint32_t offA[PA], offB[PB];
+    int rowA[PA], kA[PA], rowB[PB], kB[PB];
+#pragma unroll
+    for (int i = 0; i < PA; i++) {
+        const int q = tid + 256 * i;
+        rowA[i] = q >> 1;
+        kA[i] = (q & 1) * 32;
+        offA[i] = (m0 + rowA[i] < p.M) ? (uint32_t)((m0 + rowA[i]) * p.lda + (q & 1) * 16) : kOOB;
+    }
+#pragma unroll
+    for (int i = 0; i < PB; i++) {
+        const int q = tid + 256 * i;
+        rowB[i] = q >> 1;
+        kB[i] = (q & 1) * 32;
+        offB[i] = (n0 + rowB[i] < p.N) ? (uint32_t)((n0 + rowB[i]) * p.ldw + (q & 1) * 16) : kOOB;
+    }
+    __syncthreads();
+    // 2^-e_n of this thread's weight rows (folded into the decoded weights)
+    float rinv[PB];
+#pragma unroll
+    for (int i = 0; i < PB; i++) rinv[i] = 1.0f / rowfac[rowB[i]];
+
+    uint4 ra[PA], rb[PB];
+    uint32_t rs[PB];
+    auto gload = [&](int k) {
+#pragma unroll
+        for (int i = 0; i < PA; i++) ra[i] = buf_load16(rsA, offA[i] + (uint32_t)k * 32);
+#pragma unroll
+        for (int i = 0; i < PB; i++) {
+            rb[i] = buf_load16(rsW, offB[i] + (uint32_t)k * 32);
+            const int64_t g = k / steps_per_group;
+            const uint32_t off = n0 + rowB[i] < p.N ? (uint32_t)(((n0 + rowB[i]) * ngroups + g) * sb) : kOOB;
+            rs[i] = p.w_scale_f16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsS, off, 0, 0)
+                                  : __builtin_amdgcn_raw_buffer_load_b32(rsS, off, 0, 0);
+        }
+    };
+    // LDS in MFMA fragment order: per K16 block kk and 32-row tile t a 1 KiB block whose
+    // 16-byte slot l holds row 32 t + l%32, K values 8*(l/32) .. +7 of the block
+    // decode + store chunk c (8 codes) of every packed piece of this thread into stage st
+    auto dstore_chunk = [&](int st, int c) {
+        uint8_t* sa = smem + st * STAGE;
+        uint8_t* sw = sa + A_BYTES;
+#pragma unroll
+        for (int i = 0; i < PA; i++) {
+            const uint32_t w[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
+            const int kc = kA[i] / 8 + c, kk = kc >> 1, hh = kc & 1, r = rowA[i];
+            *reinterpret_cast<uint4*>(sa + ((kk * (BM / 32) + (r >> 5)) * 64 + (r & 31) + 32 * hh) * 16) =
+                decode_e2m1_f16x8(w[c]);
+        }
+#pragma unroll
+        for (int i = 0; i < PB; i++) {
+            const float s = p.w_scale_f16 ? __half2float(__ushort_as_half((unsigned short)rs[i])) : __uint_as_float(rs[i]);
+            const _Float16 sh = (_Float16)(s * rinv[i]);
+            const f16x2 s2 = {sh, sh};
+            const uint32_t w[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
+            const int kc = kB[i] / 8 + c, kk = kc >> 1, hh = kc & 1, r = rowB[i];
+            uint4 v = decode_lut_f16x8(w[c], TL, TH);
+            v.x = mul_f16x2(v.x, s2); v.y = mul_f16x2(v.y, s2);
+            v.z = mul_f16x2(v.z, s2); v.w = mul_f16x2(v.w, s2);
+            *reinterpret_cast<uint4*>(sw + ((kk * (BN / 32) + (r >> 5)) * 64 + (r & 31) + 32 * hh) * 16) = v;
+        }
+    };
+    auto dstore = [&](int st) {
+#pragma unroll
+        for (int c = 0; c < 4; c++) dstore_chunk(st, c);
+    };
+
+    f32x16 acc[TN][TM];
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[j][i][v] = 0.0f;
+
+    // one step: for each K16 block, its MFMAs, then a quarter of the next step's decode
+    // (independent of the MFMAs, so it runs while they execute)
+    auto step = [&](int st) {
+        const uint8_t* sa = smem + st * STAGE;
+        const uint8_t* sw = sa + A_BYTES;
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+            f16x8 af[TM];
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+                af[i] = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(sa + ((kk * (BM / 32) + wm * TM + i) * 64 + lane) * 16));
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+                const f16x8 bf = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(sw + ((kk * (BN / 32) + wn * TN + j) * 64 + lane) * 16));
+#pragma unroll
+                for (int i = 0; i < TM; i++) acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf, af[i], acc[j][i], 0, 0, 0);
+            }
+            dstore_chunk(st ^ 1, kk);
+            // interleave: each MFMA is followed by decode work, which then runs while the
+            // MFMA executes
+#pragma unroll
+            for (int x = 0; x < TM * TN; x++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+            }
+        }
+    };
+
+    gload(0);
+    dstore(0);
+    gload(1);
+    __syncthreads();
+    // step k computes stage k%2 and fills stage (k+1)%2 with step k+1 (loaded during
+    // step k-1); the loads for step k+2 are issued afterwards.  Past the last step the
+    // loads read zeros or unused codes and the decoded stage is never read.
+    for (int k = 0; k < nk; k++) {
+        step(k & 1);
+        gload(k + 2);
         __syncthreads();
     }
 
+    // epilogue: y = fl32(acc * fl32(a * 2^e_n)); value v of lane l holds output row
+    // m = l%32 (+ tile offsets) and column n = 8*(v/4) + 4*(l/32) + v%4
     const float a = p.a_scale[0];
+    const int r32 = lane & 31, hk = lane >> 5;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        int64_t n = n0 + wn * 64 + j * 16 + r16;
-        if (n >= p.N) continue;
+    for (int j = 0; j < TN; j++) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int g = 0; g < 4; g++) {
+            const int nl = wn * WN + j * 32 + 8 * g + 4 * hk;
+            float f[4];
 #pragma unroll
-            for (int t = 0; t < 4; t++) {
-                int64_t m = m0 + wm * 64 + i * 16 + q * 4 + t;
-                if (m < p.M) {
-                    float y = acc[i][j][t] * a;
-                    if (p.y_bf16) reinterpret_cast<__bf16*>(p.y)[m * p.ldy + n] = (__bf16)y;
-                    else reinterpret_cast<float*>(p.y)[m * p.ldy + n] = y;
+            for (int t = 0; t < 4; t++) f[t] = a * rowfac[nl + t];
+            const int64_t nb = n0 + nl;
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+                const int64_t m = m0 + wm * WM + i * 32 + r32;
+                if (m >= p.M) continue;
+                float y[4];
+#pragma unroll
+                for (int t = 0; t < 4; t++) y[t] = acc[j][i][4 * g + t] * f[t];
+                if (p.y_bf16) {
+                    __bf16* yp = reinterpret_cast<__bf16*>(p.y) + m * p.ldy + nb;
+                    if (nb + 4 <= p.N && ((reinterpret_cast<uintptr_t>(yp) & 7) == 0)) {
+                        __bf16 h4[4] = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+                        *reinterpret_cast<uint2*>(yp) = __builtin_bit_cast(uint2, h4);
+                    } else {
+                        for (int t = 0; t < 4; t++)
+                            if (nb + t < p.N) yp[t] = (__bf16)y[t];
+                    }
+                } else {
+                    float* yp = reinterpret_cast<float*>(p.y) + m * p.ldy + nb;
+                    if (nb + 4 <= p.N && ((reinterpret_cast<uintptr_t>(yp) & 15) == 0)) {
+                        *reinterpret_cast<float4*>(yp) = make_float4(y[0], y[1], y[2], y[3]);
+                    } else {
+                        for (int t = 0; t < 4; t++)
+                            if (nb + t < p.N) yp[t] = y[t];
+                    }
                 }
             }
         }
     }
 }
 
+static hipError_t launch_lut_block(const GemmParams& p, hipStream_t s) {
+    const int64_t gm256 = (p.M + 255) / 256, gn256 = (p.N + 255) / 256;
+    // 256x256 tiles when they give at least two per CU (one workgroup per CU at a time),
+    // else 128x128 (two per CU: better filled when there are few tiles)
+    if (gm256 * gn256 >= 512) {
+        hipLaunchKernelGGL((w4a4_lut_kernel<256, 256>), dim3((unsigned)(gm256 * gn256)), dim3(256), 0, s, p, (int)gm256);
+    } else {
+        const int64_t gm = (p.M + 127) / 128, gn = (p.N + 127) / 128;
+        hipLaunchKernelGGL((w4a4_lut_kernel<128, 128>), dim3((unsigned)(gm * gn)), dim3(256), 0, s, p, (int)gm);
+    }
+    return hipGetLastError();
+}
+
+// Buffer offsets are 32-bit and kOOB marks "past the end", so one launch covers at most
+// kLutMaxBufBytes of A, of W and of the scales; larger operands are split into row
+// blocks (multiples of 256 rows), each launched on pointers advanced to its start.
+constexpr int64_t kLutMaxBufBytes = 0x7fff0000;
+
 hipError_t launch_w4a4_lut(const GemmParams& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
-    int64_t gm = (p.M + kLutBM - 1) / kLutBM, gn = (p.N + kLutBN - 1) / kLutBN;
-    hipLaunchKernelGGL(w4a4_lut_kernel, dim3((unsigned)(gm * gn)), dim3(256), 0, s, p, (int)gm);
-    return hipGetLastError();
+    const int64_t srow = (p.K / p.w_group) * (p.w_scale_f16 ? 2 : 4);  // scale bytes per weight row
+    const int64_t mstep = std::max<int64_t>(256, kLutMaxBufBytes / std::max<int64_t>(p.lda, 1) / 256 * 256);
+    const int64_t nstep = std::max<int64_t>(
+        256, std::min(kLutMaxBufBytes / std::max<int64_t>(p.ldw, 1), kLutMaxBufBytes / std::max<int64_t>(srow, 1)) / 256 * 256);
+    const size_t ysz = p.y_bf16 ? 2 : 4;
+    for (int64_t m0 = 0; m0 < p.M; m0 += mstep) {
+        for (int64_t n0 = 0; n0 < p.N; n0 += nstep) {
+            GemmParams q = p;
+            q.M = std::min(mstep, p.M - m0);
+            q.N = std::min(nstep, p.N - n0);
+            q.a = reinterpret_cast<const uint8_t*>(p.a) + m0 * p.lda;
+            q.w = p.w + n0 * p.ldw;
+            q.w_scales = reinterpret_cast<const uint8_t*>(p.w_scales) + n0 * srow;
+            q.y = reinterpret_cast<uint8_t*>(p.y) + (m0 * p.ldy + n0) * ysz;
+            const hipError_t e = launch_lut_block(q, s);
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
 }
 
 }  // namespace fp4

@@ -238,8 +238,13 @@ fp4_status fp4_search_format(const float* w, int64_t ntensors, int64_t numel,
  *       code product is exact in fp32 and the epilogue is y = fl32(acc * fl32(a * s_n));
  *       K <= 116508 (the quarter-integer partial sums stay below 2^22), else
  *       FP4_ERR_UNSUPPORTED.
- *     - E2M1 activations x LUT16 weights (NF4) with GROUP scales runs on the f16
- *       matrix cores with the group partials scaled in fp32.
+ *     - E2M1 activations x LUT16 weights (NF4) with GROUP scales (group a multiple of
+ *       64) runs on the f16 matrix cores: each weight is expanded to
+ *       w = fl16(G[c] * fl16(s[n,g] * 2^-e_n)), 2^e_n the power of two just above the
+ *       largest group scale of row n, the f16 products are summed in fp32 and the
+ *       result is y = fl32(acc * fl32(a * 2^e_n)).  Within about 1e-3 (relative, in
+ *       norm) of the exact value; groups whose scale is below 2^-14 of their row's
+ *       largest lose relative precision to f16 subnormals.
  *   y_dtype FP4_BF16 rounds the f32 result to nearest-even.
  * Strides: K a multiple of 32 for the matrix-core paths; packed rows 16-byte aligned. */
 fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream);

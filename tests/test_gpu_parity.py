@@ -311,6 +311,37 @@ def test_preshift_nf4(M, N, K):
     assert np.array_equal(host(yb.view(torch.int16)).view(np.uint16), O.rne_bf16_bits(host(y32)))
 
 
+@pytest.mark.parametrize("M,N,K,group,sd,spread", [
+    (130, 200, 640, 64, "f16", False),     # fp16 group scales, ragged M and N
+    (96, 136, 1024, 128, "f32", False),    # two K steps per scale group
+    (256, 384, 512, 64, "f32", True),      # rows whose group scales span 2^-12 .. 1
+])
+def test_nf4_gemm_scales(M, N, K, group, sd, spread):
+    """NF4 weights x E2M1 activations with directly quantized operands: fp16 or fp32
+    group scales, groups of 64 or 128, and weight rows whose groups differ by many
+    powers of two (the expansion scales each row relative to its largest group)."""
+    say("nf4 scales", M, N, K, group, sd, spread)
+    x = synth.activations(6, M, M, K)
+    w = synth.weight(6, N, N, K)
+    if spread:
+        # group g of every row scaled by 2^(-12 g / (K/group - 1))
+        ng = K // group
+        f = np.repeat(np.float32(2.0) ** (-12.0 * np.arange(ng, dtype=np.float32) / (ng - 1)), group)
+        w = (w * f[None, :]).astype(np.float32)
+    e2, fe2 = O.minifloat(2, 1), F.grid_minifloat(2, 1)
+    wp, ws = O.quantize_pack(w, O.nf4(), "group", group, sd)
+    ap, asc = O.quantize_pack(x, e2, "tensor")
+    gwp, gws = F.fp4_quantize_pack(dev(w), F.grid_nf4(), F.gran("group", group, sd))
+    gap, gasc = F.fp4_quantize_pack(dev(x, torch.bfloat16), fe2, F.gran("tensor"))
+    assert np.array_equal(host(gwp), wp) and np.array_equal(host(gap), ap)
+    r, _ = O.gemm_w4a4(ap, e2, asc[0], wp, O.nf4(), "group", ws.astype(np.float32), group=group)
+    y32 = F.fp4_gemm(gap, gwp, gws, F.grid_nf4(), F.gran("group", group, sd), K=K, a_grid=fe2, a_scale=gasc,
+                     y_dtype=torch.float32)
+    err = O.rel_err(host(y32), r)
+    say("  rel err", err)
+    assert err <= TOL
+
+
 # ---------------------------------------------------------------- search ----------
 def test_search_small():
     say("search small")
