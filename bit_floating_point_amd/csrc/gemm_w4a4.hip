@@ -8,10 +8,13 @@
 // K <= 116508 (36 K < 2^22) all of them are exact in fp32, in any order of
 // accumulation: the result is bit-reproducible.
 //
-// Tiling for CDNA4: a 256-thread workgroup (2x2 wavefronts) computes a BM x BN tile of
+// Tiling for CDNA4: a 256-thread workgroup (2x2 wavefronts) computes BM x BN tiles of
 // Y (256x256 when the grid of such tiles fills the chip, else 128x128); each wavefront
 // a (BM/2) x (BN/2) sub-tile as a grid of 32x32 accumulators.  K advances 128 codes
 // (64 bytes per row) per step through a four-stage LDS ring fed by direct-to-LDS loads.
+// One workgroup per compute unit loops over tiles; the load ring runs on across tile
+// boundaries, so the next tile's first steps load while the last ones of the current
+// tile are computed and while its epilogue stores its outputs straight from registers.
 #include <algorithm>
 
 #include "fp4_device.h"
@@ -48,63 +51,83 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // those reads came from.  One asm block, so the compiler cannot move the reads past it.
 #define FP4_SYNC(N) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory")
 
+// Read an accumulator from its AGPR (keeps the accumulators in AGPRs across the tile loop)
+__device__ __forceinline__ float agpr_read(float a) {
+    float v;
+    asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+
+// Wait for every outstanding memory operation of this thread (loads and stores), every
+// LDS read, and the workgroup barrier.
+#define FP4_SYNC_ALL() asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory")
+// Wait for this wavefront's LDS operations and meet the workgroup barrier.
+#define FP4_BAR() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory")
+// Wait for this wavefront's LDS operations.
+#define FP4_LDS_WAIT() asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory")
+
 template <int BM, int BN>
-__global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m) {
+__global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m, int ntiles) {
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int TM = WM / 32, TN = WN / 32;
     constexpr int LA = BM * 4 / 256, LB = BN * 4 / 256;  // 16-byte pieces per thread per step
     constexpr int STAGE = (BM + BN) * kBKBytes;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * STAGE];
+    // four operand stages, then two 1 KiB blocks of per-column weight scales (tile parity)
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * STAGE + 2048];
     uint8_t* const st0 = smem;
     uint8_t* const st1 = smem + STAGE;
     uint8_t* const st2 = smem + 2 * STAGE;
     uint8_t* const st3 = smem + 3 * STAGE;
+    uint8_t* const scl = smem + 4 * STAGE;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
     const int wm = wave & 1, wn = wave >> 1;
-    const int bm = blockIdx.x % grid_m;
-    const int bn = blockIdx.x / grid_m;
-    const int64_t m0 = (int64_t)bm * BM, n0 = (int64_t)bn * BN;
+    const int r32 = lane & 31, hk = lane >> 5;
     const int nk = (int)((p.K + 127) / 128);
-
-    // buffer resources (base, stride 0, size in bytes, format word)
-    const i32x4v rsA = buf_words(p.a, p.M * p.lda);
-    const i32x4v rsB = buf_words(p.w, p.N * p.ldw);
-    // the global piece behind this lane's LDS slot, for each of its LA + LB loads: slot
-    // s = (4 i + wave) * 64 + lane holds row s/4, swizzled segment s%4 (see swz)
-    uint32_t offA[LA], offB[LB];
-    int segk[LA > LB ? LA : LB];
-#pragma unroll
-    for (int i = 0; i < LA; i++) {
-        int sidx = (4 * i + wave) * 64 + lane, row = sidx >> 2;
-        int seg = (sidx & 3) ^ ((row >> 1) & 3);
-        segk[i] = seg * 32;
-        offA[i] = (m0 + row < p.M) ? (uint32_t)((m0 + row) * p.lda + seg * 16) : kOOB;
-    }
-#pragma unroll
-    for (int i = 0; i < LB; i++) {
-        int sidx = (4 * i + wave) * 64 + lane, row = sidx >> 2;
-        int seg = (sidx & 3) ^ ((row >> 1) & 3);
-        offB[i] = (n0 + row < p.N) ? (uint32_t)((n0 + row) * p.ldw + seg * 16) : kOOB;
-    }
-
-    // The step count is rounded up to a multiple of 4 (the stage rotation); steps past
-    // the last real one load zeros (out-of-range offsets) and add nothing.
+    // The step count per tile is rounded up to a multiple of 4 (the stage rotation);
+    // steps past the last real one load zeros (out-of-range offsets) and add nothing.
     const int nk4 = (nk + 3) & ~3;
 
-    f32x16 acc[TN][TM];
-#pragma unroll
-    for (int j = 0; j < TN; j++)
-#pragma unroll
-        for (int i = 0; i < TM; i++)
-#pragma unroll
-            for (int v = 0; v < 16; v++) acc[j][i][v] = 0.0f;
-    const int r32 = lane & 31, hk = lane >> 5;
+    const i32x4v rsA = buf_words(p.a, p.M * p.lda);
+    const i32x4v rsB = buf_words(p.w, p.N * p.ldw);
+    const i32x4v rsS = buf_words(p.w_scales, p.w_mode == 1 ? p.N * 4 : 4);
+    const float a_scale = p.a_scale[0];
+    const float s_tensor = reinterpret_cast<const float*>(p.w_scales)[0];
 
-// direct-to-LDS loads of step KB into stage array STG
-#define FP4_DMA(STG, KB)                                                                                   \
+    // Loads run ahead of the MFMAs through the tiles of this workgroup (tile t covers
+    // rows bm*BM.., columns bn*BN.. with bm = t % grid_m, bn = t / grid_m; this
+    // workgroup takes t = blockIdx.x, blockIdx.x + gridDim.x, ...).  State of the load
+    // stream: its tile dt, and per load the global piece behind this lane's LDS slot
+    // (slot s = (4 i + wave) * 64 + lane holds row s/4, swizzled segment s%4; see swz).
+    int segk[LA > LB ? LA : LB];
+#pragma unroll
+    for (int i = 0; i < (LA > LB ? LA : LB); i++) {
+        int sidx = (4 * i + wave) * 64 + lane, row = sidx >> 2;
+        segk[i] = ((sidx & 3) ^ ((row >> 1) & 3)) * 32;
+    }
+    uint32_t offA[LA], offB[LB], offS;
+    int dt = blockIdx.x, dpar = 0;
+    auto load_tile = [&](int t) {
+        const bool ok = t < ntiles;
+        const int64_t m0 = (int64_t)(t % grid_m) * BM, n0 = (int64_t)(t / grid_m) * BN;
+#pragma unroll
+        for (int i = 0; i < LA; i++) {
+            int row = ((4 * i + wave) * 64 + lane) >> 2;
+            offA[i] = (ok && m0 + row < p.M) ? (uint32_t)((m0 + row) * p.lda + segk[i] / 2) : kOOB;
+        }
+#pragma unroll
+        for (int i = 0; i < LB; i++) {
+            int row = ((4 * i + wave) * 64 + lane) >> 2;
+            offB[i] = (ok && n0 + row < p.N) ? (uint32_t)((n0 + row) * p.ldw + segk[i] / 2) : kOOB;
+        }
+        offS = (ok && p.w_mode == 1 && n0 + 4 * lane < p.N) ? (uint32_t)((n0 + 4 * lane) * 4) : kOOB;
+    };
+    load_tile(dt);
+
+// direct-to-LDS loads of step KB of the load stream's tile into stage array STG
+#define FP4_DMAK(STG, KB)                                                                                  \
     do {                                                                                                   \
         const int kb_ = (KB);                                                                              \
         _Pragma("unroll") for (int i = 0; i < LA; i++) {                                                   \
@@ -118,138 +141,225 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m)
                                 (uint32_t)(uintptr_t)&STG[BM * kBKBytes + (4 * i + wave) * 1024]));       \
         }                                                                                                  \
     } while (0)
+// the load stream's tile's 256 column scales into scales block dpar (all wavefronts
+// load the same 1 KiB, so every thread issues the same number of loads)
+#define FP4_DMAS() dma16(rsS, offS, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&scl[dpar * 1024]))
+// the load stream moves on to this workgroup's next tile
+#define FP4_NEXT_TILE()                                                                                    \
+    do {                                                                                                   \
+        dt += gridDim.x;                                                                                   \
+        dpar ^= 1;                                                                                         \
+        load_tile(dt);                                                                                     \
+    } while (0)
 
-// the MFMAs of one step from stage array STG
-#define FP4_COMPUTE(STG)                                                                                   \
+// fragments of one step: [h][i] for A (rows), [h][j] for W (columns), 16 bytes each
+#define FP4_READ(STG, FA, FB)                                                                              \
     do {                                                                                                   \
         _Pragma("unroll") for (int h = 0; h < 2; h++) {                                                    \
-            i32x8 af[TM];                                                                                  \
+            _Pragma("unroll") for (int i = 0; i < TM; i++) FA[h][i] =                                      \
+                *reinterpret_cast<const uint4*>(&STG[swz(wm * WM + i * 32 + r32, 2 * h + hk)]);            \
+            _Pragma("unroll") for (int j = 0; j < TN; j++) FB[h][j] = *reinterpret_cast<const uint4*>(     \
+                &STG[BM * kBKBytes + swz(wn * WN + j * 32 + r32, 2 * h + hk)]);                             \
+        }                                                                                                  \
+    } while (0)
+// the MFMAs of one step from fragment registers, with the LDS reads of the next step
+// (issued just before) spread between them
+#define FP4_MMA(FA, FB)                                                                                    \
+    do {                                                                                                   \
+        _Pragma("unroll") for (int h = 0; h < 2; h++)                                                      \
+        _Pragma("unroll") for (int j = 0; j < TN; j++) {                                                   \
+            const uint4 v = FB[h][j];                                                                      \
+            const i32x8 bf = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};                   \
             _Pragma("unroll") for (int i = 0; i < TM; i++) {                                               \
-                uint4 v = *reinterpret_cast<const uint4*>(&STG[swz(wm * WM + i * 32 + r32, 2 * h + hk)]);  \
-                af[i] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};                        \
+                const uint4 u = FA[h][i];                                                                  \
+                const i32x8 af = i32x8{(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};                \
+                acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[j][i], 4, 4, 0, 127, 0, 127); \
             }                                                                                              \
-            _Pragma("unroll") for (int j = 0; j < TN; j++) {                                               \
-                uint4 v = *reinterpret_cast<const uint4*>(                                                 \
-                    &STG[BM * kBKBytes + swz(wn * WN + j * 32 + r32, 2 * h + hk)]);                         \
-                i32x8 bf = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};                     \
-                _Pragma("unroll") for (int i = 0; i < TM; i++) acc[j][i] =                                 \
-                    __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af[i], acc[j][i], 4, 4, 0, 127, 0, 127); \
-            }                                                                                              \
+        }                                                                                                  \
+        _Pragma("unroll") for (int g = 0; g < 2 * (TM + TN); g++) {                                        \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                             \
+            __builtin_amdgcn_sched_group_barrier(0x008, TM * TN / (TM + TN), 0);                           \
         }                                                                                                  \
     } while (0)
 
-    constexpr int PER_STEP = LA + LB;  // direct-to-LDS loads per step and thread
-    FP4_DMA(st0, 0);
-    FP4_DMA(st1, 1);
-    FP4_DMA(st2, 2);
-    // phase kb: wait until step kb landed (steps kb+1 and kb+2 may still be in flight),
-    // barrier, start step kb+3 into the stage that phase kb-1 read, compute step kb
-    for (int kb = 0; kb < nk4; kb += 4) {
-        FP4_SYNC(2 * PER_STEP);
-        FP4_DMA(st3, kb + 3);
-        FP4_COMPUTE(st0);
-        FP4_SYNC(2 * PER_STEP);
-        FP4_DMA(st0, kb + 4);
-        FP4_COMPUTE(st1);
-        FP4_SYNC(2 * PER_STEP);
-        FP4_DMA(st1, kb + 5);
-        FP4_COMPUTE(st2);
-        FP4_SYNC(2 * PER_STEP);
-        FP4_DMA(st2, kb + 6);
-        FP4_COMPUTE(st3);
-    }
-#undef FP4_DMA
-#undef FP4_COMPUTE
-    // drain the (zero) loads still in flight before the workgroup exits
-    FP4_SYNC(0);
+    f32x16 acc[TN][TM];
+    constexpr int PER_STEP = LA + LB;  // operand loads per step and thread (+1 with scales)
+    // 16-byte output stores per thread of a staged epilogue (32 rows x WN bf16 columns
+    // per wavefront and row block)
+    constexpr int CH = WN / 8;  // 16-byte chunks per staged row
+    constexpr int ST_PER = 32 * CH / 64;
+    constexpr int STORES = TM * ST_PER;
+    static_assert(2 * PER_STEP + STORES <= 63, "wait count out of range");
+    uint4 ra[2][TM], rb[2][TN], sa[2][TM], sb[2][TN];
+    FP4_DMAK(st0, 0);
+    FP4_DMAS();
+    FP4_DMAK(st1, 1);
+    FP4_DMAK(st2, 2);
+    FP4_DMAK(st3, 3);
+    FP4_SYNC_ALL();
+    FP4_READ(st0, ra, rb);
 
-    // epilogue: y = fl32(acc * fl32(a * s_n)); value v of lane l holds output row
-    // m = l%32 (+ tile offsets) and column n = 8*(v/4) + 4*(l/32) + v%4.  All scale
-    // loads are issued first.
-    const float a = p.a_scale[0];
-    float f[TN][4][4];
-#pragma unroll
-    for (int j = 0; j < TN; j++)
-#pragma unroll
-        for (int g = 0; g < 4; g++)
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                int64_t n = n0 + wn * WN + j * 32 + 8 * g + 4 * hk + t;
-                n = n < p.N ? n : p.N - 1;
-                f[j][g][t] = reinterpret_cast<const float*>(p.w_scales)[p.w_mode == 1 ? n : 0];
-            }
-#pragma unroll
-    for (int j = 0; j < TN; j++)
-#pragma unroll
-        for (int g = 0; g < 4; g++)
-#pragma unroll
-            for (int t = 0; t < 4; t++) f[j][g][t] = a * f[j][g][t];
-
-    if (p.y_bf16 && BM * BN * 2 <= 4 * STAGE) {
-        // bf16: stage the tile in LDS (row stride BN*2 bytes, 16-byte chunks XOR-swizzled
-        // by row), then write whole rows with 16-byte stores
-        constexpr int CH = BN / 8;  // 16-byte chunks per tile row
+    // Compute stream: tile ct.  Global step s (counted across this workgroup's tiles;
+    // every tile has a multiple of 4 steps) lives in stage s % 4.  Phase q: step q's
+    // fragments are in registers; wait until step q+1 landed and every wavefront has
+    // read step q (its stage is free), start the load step four ahead into that stage
+    // (in a tile's last group: the next tile's first steps), read step q+1's fragments
+    // while computing step q.  Memory operations of a thread complete in issue order
+    // (loads and stores alike), so "step q+1 landed" is "at most the operations issued
+    // after it outstanding": the next two steps' loads, and in the first three phases
+    // of a tile also the previous tile's output stores.  (A step with the scales has one
+    // load more; that only makes a wait longer.)
+#define FP4_GROUP(W0, W1, W2, D0, D1, D2, D3)                                                              \
+    do {                                                                                                   \
+        FP4_SYNC(W0);                                                                                      \
+        D0;                                                                                                \
+        FP4_READ(st1, sa, sb);                                                                             \
+        FP4_MMA(ra, rb);                                                                                   \
+        FP4_SYNC(W1);                                                                                      \
+        D1;                                                                                                \
+        FP4_READ(st2, ra, rb);                                                                             \
+        FP4_MMA(sa, sb);                                                                                   \
+        FP4_SYNC(W2);                                                                                      \
+        D2;                                                                                                \
+        FP4_READ(st3, sa, sb);                                                                             \
+        FP4_MMA(ra, rb);                                                                                   \
+        FP4_SYNC(2 * PER_STEP);                                                                            \
+        D3;                                                                                                \
+        FP4_READ(st0, ra, rb);                                                                             \
+        FP4_MMA(sa, sb);                                                                                   \
+    } while (0)
+    constexpr int WR = 2 * PER_STEP + STORES, WN2 = 2 * PER_STEP;
+    const int ngroups = nk4 / 4;
+    int ct = blockIdx.x, cpar = 0;
+    for (;;) {
 #pragma unroll
         for (int j = 0; j < TN; j++)
 #pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) acc[j][i][v] = 0.0f;
+        if (ngroups == 1) {
+            FP4_NEXT_TILE();
+            FP4_GROUP(WR, WR, WR, { FP4_DMAK(st0, 0); FP4_DMAS(); }, FP4_DMAK(st1, 1), FP4_DMAK(st2, 2),
+                      FP4_DMAK(st3, 3));
+        } else {
+            FP4_GROUP(WR, WR, WR, FP4_DMAK(st0, 4), FP4_DMAK(st1, 5), FP4_DMAK(st2, 6), FP4_DMAK(st3, 7));
+            for (int g = 1; g < ngroups - 1; g++)
+                FP4_GROUP(WN2, WN2, WN2, FP4_DMAK(st0, 4 * g + 4), FP4_DMAK(st1, 4 * g + 5), FP4_DMAK(st2, 4 * g + 6),
+                          FP4_DMAK(st3, 4 * g + 7));
+            FP4_NEXT_TILE();
+            FP4_GROUP(WN2, WN2, WN2, { FP4_DMAK(st0, 0); FP4_DMAS(); }, FP4_DMAK(st1, 1), FP4_DMAK(st2, 2),
+                      FP4_DMAK(st3, 3));
+        }
+
+        // epilogue of tile ct: y = fl32(acc * fl32(a * s_n)); value v of lane l holds
+        // row 32 i + l%32 and column 32 j + 8 (v/4) + 4 (l/32) + v%4 of this wavefront's
+        // sub-tile.
+        const int64_t m0 = (int64_t)(ct % grid_m) * BM, n0 = (int64_t)(ct / grid_m) * BN;
+        const float* sc = reinterpret_cast<const float*>(scl + cpar * 1024);
+        const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
+        if (p.y_bf16 && full && (p.ldy & 7) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0) {
+            // bf16 whole tile: once every wavefront has read the next tile's first step
+            // into registers, stage 0 is staging space, 32 rows x WN columns per wavefront
+            // at a time
+            // (16-byte chunks XOR-swizzled by row), written out as whole 16-byte pieces.
+            // The stores are not waited for: the first three waits of the next tile
+            // count them.
+            FP4_BAR();
+            uint8_t* const stg = st0 + wave * (32 * WN * 2);
+            __bf16* const yt = reinterpret_cast<__bf16*>(p.y) + (m0 + wm * WM) * p.ldy + n0 + wn * WN;
+#pragma unroll
             for (int i = 0; i < TM; i++) {
-                const int ml = wm * WM + i * 32 + r32;
+#pragma unroll
+                for (int j = 0; j < TN; j++)
+#pragma unroll
+                    for (int g = 0; g < 4; g++) {
+                        float4 s4 = make_float4(s_tensor, s_tensor, s_tensor, s_tensor);
+                        if (p.w_mode == 1) s4 = *reinterpret_cast<const float4*>(&sc[wn * WN + j * 32 + 8 * g + 4 * hk]);
+                        const float f[4] = {a_scale * s4.x, a_scale * s4.y, a_scale * s4.z, a_scale * s4.w};
+                        __bf16 h4[4];
+#pragma unroll
+                        for (int t = 0; t < 4; t++) h4[t] = (__bf16)(agpr_read(acc[j][i][4 * g + t]) * f[t]);
+                        const int c = j * 4 + g;
+                        *reinterpret_cast<uint2*>(stg + r32 * (WN * 2) + ((c ^ (r32 & (CH - 1))) << 4) + hk * 8) =
+                            __builtin_bit_cast(uint2, h4);
+                    }
+                FP4_LDS_WAIT();
+#pragma unroll
+                for (int q = 0; q < ST_PER; q++) {
+                    const int piece = q * 64 + lane, row = piece / CH, c = piece % CH;
+                    const uint4 v = *reinterpret_cast<const uint4*>(stg + row * (WN * 2) + ((c ^ (row & (CH - 1))) << 4));
+                    *reinterpret_cast<uint4*>(yt + (int64_t)(i * 32 + row) * p.ldy + c * 8) = v;
+                }
+                FP4_LDS_WAIT();
+            }
+        } else {
+            // edge tiles, f32 output, unaligned rows: stores straight from registers,
+            // then a full wait (their number does not fit the wait counts above)
+#pragma unroll
+            for (int j = 0; j < TN; j++)
 #pragma unroll
                 for (int g = 0; g < 4; g++) {
-                    const int nl = wn * WN + j * 32 + 8 * g + 4 * hk;  // multiple of 4
-                    __bf16 h4[4];
-#pragma unroll
-                    for (int t = 0; t < 4; t++) h4[t] = (__bf16)(acc[j][i][4 * g + t] * f[j][g][t]);
-                    const int chunk = (nl >> 3) ^ (ml & (CH - 1));
-                    *reinterpret_cast<uint2*>(smem + ml * (BN * 2) + chunk * 16 + (nl & 4) * 2) =
-                        __builtin_bit_cast(uint2, h4);
-                }
-            }
-        __syncthreads();
-        for (int idx = tid; idx < BM * CH; idx += 256) {
-            const int ml = idx / CH, c = idx % CH;
-            const int64_t m = m0 + ml, n = n0 + c * 8;
-            if (m >= p.M || n >= p.N) continue;
-            const uint4 v = *reinterpret_cast<const uint4*>(smem + ml * (BN * 2) + ((c ^ (ml & (CH - 1))) * 16));
-            __bf16* yp = reinterpret_cast<__bf16*>(p.y) + m * p.ldy + n;
-            if (n + 8 <= p.N && ((reinterpret_cast<uintptr_t>(yp) & 15) == 0)) {
-                *reinterpret_cast<uint4*>(yp) = v;
-            } else {
-                const __bf16* hv = reinterpret_cast<const __bf16*>(&v);
-                for (int t = 0; t < 8; t++)
-                    if (n + t < p.N) yp[t] = hv[t];
-            }
-        }
-        return;
-    }
-#pragma unroll
-    for (int j = 0; j < TN; j++) {
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-            const int64_t nb = n0 + wn * WN + j * 32 + 8 * g + 4 * hk;
-#pragma unroll
-            for (int i = 0; i < TM; i++) {
-                const int64_t m = m0 + wm * WM + i * 32 + r32;
-                if (m >= p.M) continue;
-                float y[4];
-#pragma unroll
-                for (int t = 0; t < 4; t++) y[t] = acc[j][i][4 * g + t] * f[j][g][t];
-                if (p.y_bf16) {
-                    __bf16* yp = reinterpret_cast<__bf16*>(p.y) + m * p.ldy + nb;
-                    for (int t = 0; t < 4; t++)
-                        if (nb + t < p.N) yp[t] = (__bf16)y[t];
-                } else {
-                    float* yp = reinterpret_cast<float*>(p.y) + m * p.ldy + nb;
-                    if (nb + 4 <= p.N && ((reinterpret_cast<uintptr_t>(yp) & 15) == 0)) {
-                        *reinterpret_cast<float4*>(yp) = make_float4(y[0], y[1], y[2], y[3]);
-                    } else {
-                        for (int t = 0; t < 4; t++)
-                            if (nb + t < p.N) yp[t] = y[t];
+                    const int nl = wn * WN + j * 32 + 8 * g + 4 * hk;
+                    const int64_t n = n0 + nl;
+                    float4 s4 = make_float4(s_tensor, s_tensor, s_tensor, s_tensor);
+                    if (p.w_mode == 1) {
+                        if (full) {
+                            s4 = *reinterpret_cast<const float4*>(&sc[nl]);
+                        } else {  // scales straight from memory; columns past N are not stored
+                            const float* ws = reinterpret_cast<const float*>(p.w_scales);
+                            s4.x = ws[n < p.N ? n : p.N - 1];
+                            s4.y = ws[n + 1 < p.N ? n + 1 : p.N - 1];
+                            s4.z = ws[n + 2 < p.N ? n + 2 : p.N - 1];
+                            s4.w = ws[n + 3 < p.N ? n + 3 : p.N - 1];
+                        }
                     }
+                    const float f0 = a_scale * s4.x, f1 = a_scale * s4.y, f2 = a_scale * s4.z, f3 = a_scale * s4.w;
+                    const bool vec = full && (p.ldy & 3) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
+#pragma unroll
+                    for (int i = 0; i < TM; i++) {
+                        const int64_t m = m0 + wm * WM + i * 32 + r32;
+                        const float y0 = agpr_read(acc[j][i][4 * g]) * f0, y1 = agpr_read(acc[j][i][4 * g + 1]) * f1;
+                        const float y2 = agpr_read(acc[j][i][4 * g + 2]) * f2, y3 = agpr_read(acc[j][i][4 * g + 3]) * f3;
+                        if (p.y_bf16) {
+                            __bf16* yp = reinterpret_cast<__bf16*>(p.y) + m * p.ldy + n;
+                            __bf16 h4[4] = {(__bf16)y0, (__bf16)y1, (__bf16)y2, (__bf16)y3};
+                            if (vec) {
+                                *reinterpret_cast<uint2*>(yp) = __builtin_bit_cast(uint2, h4);
+                            } else if (m < p.M) {
+                                if (n < p.N) yp[0] = h4[0];
+                                if (n + 1 < p.N) yp[1] = h4[1];
+                                if (n + 2 < p.N) yp[2] = h4[2];
+                                if (n + 3 < p.N) yp[3] = h4[3];
+                            }
+                        } else {
+                            float* yp = reinterpret_cast<float*>(p.y) + m * p.ldy + n;
+                            if (vec) {
+                                *reinterpret_cast<float4*>(yp) = make_float4(y0, y1, y2, y3);
+                            } else if (m < p.M) {
+                                if (n < p.N) yp[0] = y0;
+                                if (n + 1 < p.N) yp[1] = y1;
+                                if (n + 2 < p.N) yp[2] = y2;
+                                if (n + 3 < p.N) yp[3] = y3;
+                            }
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-            }
+            FP4_SYNC_ALL();
         }
+        ct += gridDim.x;
+        if (ct >= ntiles) break;
+        cpar ^= 1;
     }
+#undef FP4_DMAK
+#undef FP4_DMAS
+#undef FP4_NEXT_TILE
+#undef FP4_GROUP
+#undef FP4_READ
+#undef FP4_MMA
+    // drain the (zero) loads still in flight before the workgroup exits
+    FP4_SYNC_ALL();
 }
 
 // Buffer offsets are 32-bit and kOOB marks "past the end", so one launch covers at most
@@ -257,14 +367,31 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m)
 // 256 rows, whole tiles either way), each launched on pointers advanced to its start.
 constexpr int64_t kMaxBufBytes = 0x7fff0000;
 
+// one workgroup per compute unit (each holds the whole LDS ring), looping over tiles
+static int cu_count() {
+    static int counts[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (counts[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        counts[dev] = n;
+    }
+    return counts[dev];
+}
+
 static hipError_t launch_block(const GemmParams& p, hipStream_t s) {
     int64_t gm256 = (p.M + 255) / 256, gn256 = (p.N + 255) / 256;
+    const int64_t cus = cu_count();
     if (gm256 * gn256 >= 384) {
-        hipLaunchKernelGGL((w4a4_fp4_kernel<256, 256>), dim3((unsigned)(gm256 * gn256)), dim3(256), 0, s, p,
-                           (int)gm256);
+        const int64_t nt = gm256 * gn256;
+        hipLaunchKernelGGL((w4a4_fp4_kernel<256, 256>), dim3((unsigned)std::min(nt, cus)), dim3(256), 0, s, p,
+                           (int)gm256, (int)nt);
     } else {
         int64_t gm = (p.M + 127) / 128, gn = (p.N + 127) / 128;
-        hipLaunchKernelGGL((w4a4_fp4_kernel<128, 128>), dim3((unsigned)(gm * gn)), dim3(256), 0, s, p, (int)gm);
+        const int64_t nt = gm * gn;
+        hipLaunchKernelGGL((w4a4_fp4_kernel<128, 128>), dim3((unsigned)std::min(nt, cus)), dim3(256), 0, s, p,
+                           (int)gm, (int)nt);
     }
     return hipGetLastError();
 }

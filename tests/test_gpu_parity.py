@@ -295,6 +295,47 @@ def test_preshift_w4a4_full_2048x4096x4096():
     assert np.array_equal(y32[rows].view(np.uint32), O.w4a4_epilogue_f32(acc, a, ws).view(np.uint32))
 
 
+@pytest.mark.parametrize("M,N,K,mode,ldy_pad", [
+    (2100, 2200, 544, "row", 0),     # 17 x 18 tiles of 128: more tiles than workgroups, ragged
+    (4100, 6000, 288, "row", 0),     # 17 x 24 tiles of 256, ragged M, N and K tail
+    (4100, 6000, 256, "tensor", 0),
+    (1500, 3000, 384, "row", 3),     # output rows not 16-byte aligned: element stores
+])
+def test_w4a4_e2m1_many_tiles(M, N, K, mode, ldy_pad):
+    """W4A4 E2M1 GEMM on random codes where each workgroup computes several tiles in
+    turn (edge tiles included): fp32 and bf16 outputs bit-exact."""
+    say("w4a4 tiles", M, N, K, mode, ldy_pad)
+    rng = np.random.default_rng(M + N + K)
+    e2 = O.minifloat(2, 1)
+    ap = rng.integers(0, 256, (M, max(K // 2, 16)), dtype=np.uint8)[:, :K // 2]
+    wp = rng.integers(0, 256, (N, max(K // 2, 16)), dtype=np.uint8)[:, :K // 2]
+    a = np.float32(rng.uniform(0.5, 2.0))
+    ws = (rng.uniform(0.5, 2.0, N if mode == "row" else 1)).astype(np.float32)
+    _, acc = O.gemm_w4a4(ap, e2, a, wp, e2, mode, ws)
+    y_pin = O.w4a4_epilogue_f32(acc, a, np.broadcast_to(ws, (N,)))
+    # packed operands with 16-byte aligned rows (lda, ldw multiples of 16)
+    lda = max((K // 2 + 15) // 16 * 16, 16)
+    gap = torch.zeros((M, lda), dtype=torch.uint8, device=DEV)
+    gwp = torch.zeros((N, lda), dtype=torch.uint8, device=DEV)
+    gap[:, :K // 2] = torch.from_numpy(ap).to(DEV)
+    gwp[:, :K // 2] = torch.from_numpy(wp).to(DEV)
+    fe2 = F.grid_minifloat(2, 1)
+    ga = dev(np.array([a], np.float32))
+    gws = dev(ws)
+    for dt, bits in ((torch.float32, lambda y: y.view(np.uint32)), (torch.bfloat16, None)):
+        ybuf = torch.full((M, N + ldy_pad), -7.0, dtype=dt, device=DEV)
+        y = ybuf[:, :N]
+        F.fp4_gemm(gap, gwp, gws, fe2, F.gran(mode), K=K, a_grid=fe2, a_scale=ga, y=y)
+        if dt == torch.float32:
+            assert np.array_equal(host(y).view(np.uint32), y_pin.view(np.uint32))
+        else:
+            assert np.array_equal(host(y.view(torch.int16)).view(np.uint16), O.rne_bf16_bits(y_pin))
+        if ldy_pad:
+            assert bool((ybuf[:, N:] == -7.0).all())
+    with pytest.raises(F._lib.FP4Error):  # K = 0 is rejected, not computed
+        F.fp4_gemm(gap, gwp, gws, fe2, F.gran(mode), K=0, a_grid=fe2, a_scale=ga)
+
+
 @pytest.mark.parametrize("M,N,K", [(256, 384, 512), (130, 200, 640)])
 def test_preshift_nf4(M, N, K):
     say("nf4", M, N, K)
