@@ -258,16 +258,22 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
         const int64_t m0 = (int64_t)(ct % grid_m) * BM, n0 = (int64_t)(ct / grid_m) * BN;
         const float* sc = reinterpret_cast<const float*>(scl + cpar * 1024);
         const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
-        if (p.y_bf16 && full && (p.ldy & 7) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0) {
+        if (p.y_bf16 && full && (p.ldy & 7) == 0 && p.ldy < (1 << 26) &&
+            (reinterpret_cast<uintptr_t>(p.y) & 15) == 0) {
             // bf16 whole tile: once every wavefront has read the next tile's first step
             // into registers, stage 0 is staging space, 32 rows x WN columns per wavefront
-            // at a time
-            // (16-byte chunks XOR-swizzled by row), written out as whole 16-byte pieces.
-            // The stores are not waited for: the first three waits of the next tile
-            // count them.
+            // at a time (16-byte chunks XOR-swizzled by row), written out as whole
+            // 16-byte pieces.  The stores are not waited for: the first three waits of
+            // the next tile count them.  Addresses: a per-lane 32-bit part plus a
+            // wavefront-uniform row offset, so nothing 64-bit is kept per store.
             FP4_BAR();
             uint8_t* const stg = st0 + wave * (32 * WN * 2);
-            __bf16* const yt = reinterpret_cast<__bf16*>(p.y) + (m0 + wm * WM) * p.ldy + n0 + wn * WN;
+            uint8_t* const wrow = stg + r32 * (WN * 2) + hk * 8;  // this lane's staged row
+            const int xw = (r32 & (CH - 1)) << 4;
+            constexpr int RPQ = 64 / CH;                          // rows per read-back pass
+            const int rl = lane / CH, cl = lane % CH;
+            const uint32_t goff = (uint32_t)(rl * p.ldy * 2 + cl * 16);
+            char* const ytile = reinterpret_cast<char*>(p.y) + ((m0 + wm * WM) * p.ldy + n0 + wn * WN) * 2;
 #pragma unroll
             for (int i = 0; i < TM; i++) {
 #pragma unroll
@@ -280,16 +286,14 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
                         __bf16 h4[4];
 #pragma unroll
                         for (int t = 0; t < 4; t++) h4[t] = (__bf16)(agpr_read(acc[j][i][4 * g + t]) * f[t]);
-                        const int c = j * 4 + g;
-                        *reinterpret_cast<uint2*>(stg + r32 * (WN * 2) + ((c ^ (r32 & (CH - 1))) << 4) + hk * 8) =
-                            __builtin_bit_cast(uint2, h4);
+                        *reinterpret_cast<uint2*>(wrow + (((j * 4 + g) << 4) ^ xw)) = __builtin_bit_cast(uint2, h4);
                     }
                 FP4_LDS_WAIT();
 #pragma unroll
                 for (int q = 0; q < ST_PER; q++) {
-                    const int piece = q * 64 + lane, row = piece / CH, c = piece % CH;
-                    const uint4 v = *reinterpret_cast<const uint4*>(stg + row * (WN * 2) + ((c ^ (row & (CH - 1))) << 4));
-                    *reinterpret_cast<uint4*>(yt + (int64_t)(i * 32 + row) * p.ldy + c * 8) = v;
+                    const int row = q * RPQ + rl;
+                    const uint4 v = *reinterpret_cast<const uint4*>(stg + row * (WN * 2) + ((cl ^ (row & (CH - 1))) << 4));
+                    *reinterpret_cast<uint4*>(ytile + (int64_t)(i * 32 + q * RPQ) * p.ldy * 2 + goff) = v;
                 }
                 FP4_LDS_WAIT();
             }
