@@ -72,13 +72,16 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
     constexpr int TM = WM / 32, TN = WN / 32;
     constexpr int LA = BM * 4 / 256, LB = BN * 4 / 256;  // 16-byte pieces per thread per step
     constexpr int STAGE = (BM + BN) * kBKBytes;
-    // four operand stages, then two 1 KiB blocks of per-column weight scales (tile parity)
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * STAGE + 2048];
+    // four operand stages, two 1 KiB blocks of per-column weight scales (tile parity),
+    // and each wavefront's output staging area (32 rows x WN/2 bf16 columns)
+    constexpr int STG_BYTES = 32 * WN;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * STAGE + 2048 + 4 * STG_BYTES];
     uint8_t* const st0 = smem;
     uint8_t* const st1 = smem + STAGE;
     uint8_t* const st2 = smem + 2 * STAGE;
     uint8_t* const st3 = smem + 3 * STAGE;
     uint8_t* const scl = smem + 4 * STAGE;
+    uint8_t* const stg = smem + 4 * STAGE + 2048 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * STG_BYTES;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -152,31 +155,29 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
         load_tile(dt);                                                                                     \
     } while (0)
 
-// fragments of one step: [h][i] for A (rows), [h][j] for W (columns), 16 bytes each
-#define FP4_READ(STG, FA, FB)                                                                              \
+// fragments of half H of a step (K codes 64 H .. 64 H + 63 under the stage's segment
+// order): FA[i] for A (rows), FB[j] for W (columns), 16 bytes each
+#define FP4_READH(STG, H, FA, FB)                                                                          \
     do {                                                                                                   \
-        _Pragma("unroll") for (int h = 0; h < 2; h++) {                                                    \
-            _Pragma("unroll") for (int i = 0; i < TM; i++) FA[h][i] =                                      \
-                *reinterpret_cast<const uint4*>(&STG[swz(wm * WM + i * 32 + r32, 2 * h + hk)]);            \
-            _Pragma("unroll") for (int j = 0; j < TN; j++) FB[h][j] = *reinterpret_cast<const uint4*>(     \
-                &STG[BM * kBKBytes + swz(wn * WN + j * 32 + r32, 2 * h + hk)]);                             \
-        }                                                                                                  \
+        _Pragma("unroll") for (int i = 0; i < TM; i++) FA[i] =                                             \
+            *reinterpret_cast<const uint4*>(&STG[swz(wm * WM + i * 32 + r32, 2 * (H) + hk)]);              \
+        _Pragma("unroll") for (int j = 0; j < TN; j++) FB[j] =                                             \
+            *reinterpret_cast<const uint4*>(&STG[BM * kBKBytes + swz(wn * WN + j * 32 + r32, 2 * (H) + hk)]); \
     } while (0)
-// the MFMAs of one step from fragment registers, with the LDS reads of the next step
-// (issued just before) spread between them
-#define FP4_MMA(FA, FB)                                                                                    \
+// the MFMAs of one half step from fragment registers, with the LDS reads of the next
+// half step (issued just before) spread between them
+#define FP4_MMAH(FA, FB)                                                                                   \
     do {                                                                                                   \
-        _Pragma("unroll") for (int h = 0; h < 2; h++)                                                      \
         _Pragma("unroll") for (int j = 0; j < TN; j++) {                                                   \
-            const uint4 v = FB[h][j];                                                                      \
+            const uint4 v = FB[j];                                                                         \
             const i32x8 bf = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};                   \
             _Pragma("unroll") for (int i = 0; i < TM; i++) {                                               \
-                const uint4 u = FA[h][i];                                                                  \
+                const uint4 u = FA[i];                                                                     \
                 const i32x8 af = i32x8{(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};                \
                 acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[j][i], 4, 4, 0, 127, 0, 127); \
             }                                                                                              \
         }                                                                                                  \
-        _Pragma("unroll") for (int g = 0; g < 2 * (TM + TN); g++) {                                        \
+        _Pragma("unroll") for (int g = 0; g < TM + TN; g++) {                                              \
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                             \
             __builtin_amdgcn_sched_group_barrier(0x008, TM * TN / (TM + TN), 0);                           \
         }                                                                                                  \
@@ -190,43 +191,41 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
     constexpr int ST_PER = 32 * CH / 64;
     constexpr int STORES = TM * ST_PER;
     static_assert(2 * PER_STEP + STORES <= 63, "wait count out of range");
-    uint4 ra[2][TM], rb[2][TN], sa[2][TM], sb[2][TN];
+    uint4 xa[TM], xb[TN], ya[TM], yb[TN];
     FP4_DMAK(st0, 0);
     FP4_DMAS();
     FP4_DMAK(st1, 1);
     FP4_DMAK(st2, 2);
     FP4_DMAK(st3, 3);
     FP4_SYNC_ALL();
-    FP4_READ(st0, ra, rb);
+    FP4_READH(st0, 0, xa, xb);
 
     // Compute stream: tile ct.  Global step s (counted across this workgroup's tiles;
-    // every tile has a multiple of 4 steps) lives in stage s % 4.  Phase q: step q's
-    // fragments are in registers; wait until step q+1 landed and every wavefront has
-    // read step q (its stage is free), start the load step four ahead into that stage
-    // (in a tile's last group: the next tile's first steps), read step q+1's fragments
-    // while computing step q.  Memory operations of a thread complete in issue order
+    // every tile has a multiple of 4 steps) lives in stage s % 4.  Phase q: the first
+    // half of step q is in registers; read its second half while computing the first;
+    // wait until step q+1 landed and every wavefront has read step q (its stage is
+    // free), start the load step four ahead into that stage (in a tile's last group: the
+    // next tile's first steps), read the first half of step q+1 while computing the
+    // second half of step q.  Memory operations of a thread complete in issue order
     // (loads and stores alike), so "step q+1 landed" is "at most the operations issued
     // after it outstanding": the next two steps' loads, and in the first three phases
     // of a tile also the previous tile's output stores.  (A step with the scales has one
     // load more; that only makes a wait longer.)
+#define FP4_PHASE(W, SQ, SN, D)                                                                            \
+    do {                                                                                                   \
+        FP4_READH(SQ, 1, ya, yb);                                                                          \
+        FP4_MMAH(xa, xb);                                                                                  \
+        FP4_SYNC(W);                                                                                       \
+        D;                                                                                                 \
+        FP4_READH(SN, 0, xa, xb);                                                                          \
+        FP4_MMAH(ya, yb);                                                                                  \
+    } while (0)
 #define FP4_GROUP(W0, W1, W2, D0, D1, D2, D3)                                                              \
     do {                                                                                                   \
-        FP4_SYNC(W0);                                                                                      \
-        D0;                                                                                                \
-        FP4_READ(st1, sa, sb);                                                                             \
-        FP4_MMA(ra, rb);                                                                                   \
-        FP4_SYNC(W1);                                                                                      \
-        D1;                                                                                                \
-        FP4_READ(st2, ra, rb);                                                                             \
-        FP4_MMA(sa, sb);                                                                                   \
-        FP4_SYNC(W2);                                                                                      \
-        D2;                                                                                                \
-        FP4_READ(st3, sa, sb);                                                                             \
-        FP4_MMA(ra, rb);                                                                                   \
-        FP4_SYNC(2 * PER_STEP);                                                                            \
-        D3;                                                                                                \
-        FP4_READ(st0, ra, rb);                                                                             \
-        FP4_MMA(sa, sb);                                                                                   \
+        FP4_PHASE(W0, st0, st1, D0);                                                                       \
+        FP4_PHASE(W1, st1, st2, D1);                                                                       \
+        FP4_PHASE(W2, st2, st3, D2);                                                                       \
+        FP4_PHASE(2 * PER_STEP, st3, st0, D3);                                                             \
     } while (0)
     constexpr int WR = 2 * PER_STEP + STORES, WN2 = 2 * PER_STEP;
     const int ngroups = nk4 / 4;
@@ -260,42 +259,44 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
         const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
         if (p.y_bf16 && full && (p.ldy & 7) == 0 && p.ldy < (1 << 26) &&
             (reinterpret_cast<uintptr_t>(p.y) & 15) == 0) {
-            // bf16 whole tile: once every wavefront has read the next tile's first step
-            // into registers, stage 0 is staging space, 32 rows x WN columns per wavefront
-            // at a time (16-byte chunks XOR-swizzled by row), written out as whole
-            // 16-byte pieces.  The stores are not waited for: the first three waits of
-            // the next tile count them.  Addresses: a per-lane 32-bit part plus a
-            // wavefront-uniform row offset, so nothing 64-bit is kept per store.
-            FP4_BAR();
-            uint8_t* const stg = st0 + wave * (32 * WN * 2);
-            uint8_t* const wrow = stg + r32 * (WN * 2) + hk * 8;  // this lane's staged row
-            const int xw = (r32 & (CH - 1)) << 4;
-            constexpr int RPQ = 64 / CH;                          // rows per read-back pass
-            const int rl = lane / CH, cl = lane % CH;
+            // bf16 whole tile: staged in this wavefront's own LDS area, 32 rows x WN/2
+            // columns at a time (16-byte chunks XOR-swizzled by row), written out as whole
+            // 16-byte pieces.  The stores are not waited for: the first three waits of the
+            // next tile count them.  Addresses: a per-lane 32-bit part plus a
+            // wavefront-uniform row offset.
+            constexpr int CH2 = WN / 16;    // 16-byte chunks per staged row (WN/2 columns)
+            constexpr int RPQ = 64 / CH2;   // rows per read-back pass
+            const int xw = (r32 & (CH2 - 1)) << 4;
+            const int rl = lane / CH2, cl = lane % CH2;
             const uint32_t goff = (uint32_t)(rl * p.ldy * 2 + cl * 16);
             char* const ytile = reinterpret_cast<char*>(p.y) + ((m0 + wm * WM) * p.ldy + n0 + wn * WN) * 2;
 #pragma unroll
             for (int i = 0; i < TM; i++) {
 #pragma unroll
-                for (int j = 0; j < TN; j++)
+                for (int jh = 0; jh < 2; jh++) {
 #pragma unroll
-                    for (int g = 0; g < 4; g++) {
-                        float4 s4 = make_float4(s_tensor, s_tensor, s_tensor, s_tensor);
-                        if (p.w_mode == 1) s4 = *reinterpret_cast<const float4*>(&sc[wn * WN + j * 32 + 8 * g + 4 * hk]);
-                        const float f[4] = {a_scale * s4.x, a_scale * s4.y, a_scale * s4.z, a_scale * s4.w};
-                        __bf16 h4[4];
+                    for (int jj = 0; jj < TN / 2; jj++)
 #pragma unroll
-                        for (int t = 0; t < 4; t++) h4[t] = (__bf16)(agpr_read(acc[j][i][4 * g + t]) * f[t]);
-                        *reinterpret_cast<uint2*>(wrow + (((j * 4 + g) << 4) ^ xw)) = __builtin_bit_cast(uint2, h4);
+                        for (int g = 0; g < 4; g++) {
+                            const int j = jh * (TN / 2) + jj;
+                            float4 s4 = make_float4(s_tensor, s_tensor, s_tensor, s_tensor);
+                            if (p.w_mode == 1) s4 = *reinterpret_cast<const float4*>(&sc[wn * WN + j * 32 + 8 * g + 4 * hk]);
+                            const float f[4] = {a_scale * s4.x, a_scale * s4.y, a_scale * s4.z, a_scale * s4.w};
+                            __bf16 h4[4];
+#pragma unroll
+                            for (int t = 0; t < 4; t++) h4[t] = (__bf16)(agpr_read(acc[j][i][4 * g + t]) * f[t]);
+                            *reinterpret_cast<uint2*>(stg + r32 * (WN) + (((jj * 4 + g) << 4) ^ xw) + hk * 8) =
+                                __builtin_bit_cast(uint2, h4);
+                        }
+                    FP4_LDS_WAIT();
+#pragma unroll
+                    for (int q = 0; q < 32 * CH2 / 64; q++) {
+                        const int row = q * RPQ + rl;
+                        const uint4 v = *reinterpret_cast<const uint4*>(stg + row * WN + ((cl ^ (row & (CH2 - 1))) << 4));
+                        *reinterpret_cast<uint4*>(ytile + (int64_t)(i * 32 + q * RPQ) * p.ldy * 2 + jh * WN + goff) = v;
                     }
-                FP4_LDS_WAIT();
-#pragma unroll
-                for (int q = 0; q < ST_PER; q++) {
-                    const int row = q * RPQ + rl;
-                    const uint4 v = *reinterpret_cast<const uint4*>(stg + row * (WN * 2) + ((cl ^ (row & (CH - 1))) << 4));
-                    *reinterpret_cast<uint4*>(ytile + (int64_t)(i * 32 + q * RPQ) * p.ldy * 2 + goff) = v;
+                    FP4_LDS_WAIT();
                 }
-                FP4_LDS_WAIT();
             }
         } else {
             // edge tiles, f32 output, unaligned rows: stores straight from registers,
@@ -360,8 +361,9 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
 #undef FP4_DMAS
 #undef FP4_NEXT_TILE
 #undef FP4_GROUP
-#undef FP4_READ
-#undef FP4_MMA
+#undef FP4_READH
+#undef FP4_MMAH
+#undef FP4_PHASE
     // drain the (zero) loads still in flight before the workgroup exits
     FP4_SYNC_ALL();
 }
