@@ -386,19 +386,18 @@ static int cu_count() {
     return counts[dev];
 }
 
+template <int BM, int BN>
+static void launch_cfg(const GemmParams& p, hipStream_t s, int64_t cus) {
+    const int64_t gm = (p.M + BM - 1) / BM, gn = (p.N + BN - 1) / BN, nt = gm * gn;
+    hipLaunchKernelGGL((w4a4_fp4_kernel<BM, BN>), dim3((unsigned)std::min(nt, cus)), dim3(256), 0, s, p, (int)gm,
+                       (int)nt);
+}
+// 256x256 tiles when there are enough of them for every compute unit, else 128x128
 static hipError_t launch_block(const GemmParams& p, hipStream_t s) {
-    int64_t gm256 = (p.M + 255) / 256, gn256 = (p.N + 255) / 256;
     const int64_t cus = cu_count();
-    if (gm256 * gn256 >= 384) {
-        const int64_t nt = gm256 * gn256;
-        hipLaunchKernelGGL((w4a4_fp4_kernel<256, 256>), dim3((unsigned)std::min(nt, cus)), dim3(256), 0, s, p,
-                           (int)gm256, (int)nt);
-    } else {
-        int64_t gm = (p.M + 127) / 128, gn = (p.N + 127) / 128;
-        const int64_t nt = gm * gn;
-        hipLaunchKernelGGL((w4a4_fp4_kernel<128, 128>), dim3((unsigned)std::min(nt, cus)), dim3(256), 0, s, p,
-                           (int)gm, (int)nt);
-    }
+    const int64_t gm256 = (p.M + 255) / 256, gn256 = (p.N + 255) / 256;
+    if (gm256 * gn256 >= cus) launch_cfg<256, 256>(p, s, cus);
+    else launch_cfg<128, 128>(p, s, cus);
     return hipGetLastError();
 }
 
