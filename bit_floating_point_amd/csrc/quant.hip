@@ -225,6 +225,57 @@ __global__ void __launch_bounds__(kThreads) quantize_chunk_kernel(QuantParams p,
     }
 }
 
+// Max over the aligned 16-lane group (one 128-element group of 8 elements per lane)
+// with DPP lane permutes, all in VALU: swap neighbours, swap pairs, mirror within 8,
+// mirror within 16.
+__device__ __forceinline__ float dpp_max16(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+
+// GROUP mode with 128-element groups, the E2M1 grid, no column shifts, rows a multiple
+// of 8 elements: the same arithmetic as quantize_chunk_kernel, specialised (group
+// maximum by DPP instead of lane shuffles through LDS, no per-element grid dispatch).
+// U (row, 2048-column chunk) units per workgroup, all loads issued first.
+template <bool BF16, int U>
+__global__ void __launch_bounds__(kThreads) quantize_e2m1_g128_kernel(QuantParams p, int chunks, int nunits) {
+    Raw8 raw[U];
+    int row[U], col[U];
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+        int u = blockIdx.x * U + i;
+        if (u >= nunits) u = nunits - 1;  // a duplicate of the last unit writes the same bytes
+        row[i] = u / chunks;
+        col[i] = (u - row[i] * chunks) * kChunk + threadIdx.x * 8;
+        raw[i] = load_raw8<true, BF16>(reinterpret_cast<const char*>(p.x) + (int64_t)row[i] * p.ldx * (BF16 ? 2 : 4),
+                                       col[i], p.cols);
+    }
+    const int64_t gpr = p.cols / 128;  // groups per row
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+        float v[8];
+        raw8_to_float<BF16>(raw[i], v);
+        const float amax = dpp_max16(max_abs8(v));
+        float s = amax / p.g.qmax;
+        if (p.scale_f16) s = round_f16(s);
+        const float r = recip_or_zero(s);
+        if (col[i] < p.cols) {
+            if ((threadIdx.x & 15) == 0 && p.scales_out) store_scale(p, (int64_t)row[i] * gpr + col[i] / 128, s);
+#pragma unroll
+            for (int k = 0; k < 8; k++) v[k] = v[k] * r;
+            uint32_t w = 0;
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+            *reinterpret_cast<uint32_t*>(p.packed + (int64_t)row[i] * p.ldp + col[i] / 2) = w;
+        }
+    }
+}
+
 // ROW mode, rows of at most R * 2048 elements: one workgroup per row, the row held in
 // registers (one HBM read), max reduced across the workgroup, then quantized.
 template <bool VEC, bool BF16, int R>
@@ -335,7 +386,12 @@ static void quantize_launch(const QuantParams& p, hipStream_t s) {
         int64_t chunks = (p.cols + kChunk - 1) / kChunk;
         int64_t nunits = p.rows * chunks;
         dim3 grid((unsigned)((nunits + U - 1) / U));
-        hipLaunchKernelGGL((quantize_chunk_kernel<VEC, BF16, U>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
+        if (VEC && p.mode == 2 && p.group == 128 && p.g.is_e2m1 && !p.col_shift && !p.amax_in && nunits < (1LL << 30) &&
+            p.cols < (1LL << 30))
+            hipLaunchKernelGGL((quantize_e2m1_g128_kernel<BF16, U>), grid, dim3(kThreads), 0, s, p, (int)chunks,
+                               (int)nunits);
+        else
+            hipLaunchKernelGGL((quantize_chunk_kernel<VEC, BF16, U>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
     }
 }
 

@@ -64,7 +64,7 @@ def test_calibrate(bf16):
 # ---------------------------------------------------------------- quantize --------
 FMTS = [(2, 1), (1, 2), (3, 0), "nf4"]
 MODES = [("tensor", 0, "f32"), ("row", 0, "f32"), ("row", 0, "f16"), ("group", 128, "f16"),
-         ("group", 64, "f32"), ("group", 8, "f32"), ("group", 512, "f32")]
+         ("group", 128, "f32"), ("group", 64, "f32"), ("group", 8, "f32"), ("group", 512, "f32")]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -72,7 +72,9 @@ MODES = [("tensor", 0, "f32"), ("row", 0, "f32"), ("row", 0, "f16"), ("group", 1
 @pytest.mark.parametrize("bf16", [False, True])
 def test_quantize_pack_dequantize(fmt, mode, group, sd, bf16):
     say("quantize", fmt, mode, group, sd, bf16)
-    cols = 1024 if mode == "group" else 1030  # 1030: ragged 8-element tail, scalar path
+    # group: 3072 = one whole 2048-column chunk and a partial one; 1030: ragged
+    # 8-element tail, scalar path
+    cols = 3072 if mode == "group" else 1030
     x = synth.heavy_tail_weight(2, 7, 37, cols)
     if bf16:
         x = synth.to_bf16_values(x)
