@@ -239,9 +239,10 @@ __device__ __forceinline__ float dpp_max16(float v) {
 // GROUP mode with 128-element groups, the E2M1 grid, no column shifts, rows a multiple
 // of 8 elements: the same arithmetic as quantize_chunk_kernel, specialised (group
 // maximum by DPP instead of lane shuffles through LDS, no per-element grid dispatch).
-// U (row, 2048-column chunk) units per workgroup, all loads issued first.
-template <bool BF16, int U>
-__global__ void __launch_bounds__(kThreads) quantize_e2m1_g128_kernel(QuantParams p, int chunks, int nunits) {
+// U (row, T*8-column chunk) units per workgroup of T threads, all loads issued first;
+// one unit per workgroup measured fastest (the most workgroups in flight).
+template <bool BF16, int U, int T>
+__global__ void __launch_bounds__(T) quantize_e2m1_g128_kernel(QuantParams p, int chunks, int nunits) {
     Raw8 raw[U];
     int row[U], col[U];
 #pragma unroll
@@ -249,7 +250,7 @@ __global__ void __launch_bounds__(kThreads) quantize_e2m1_g128_kernel(QuantParam
         int u = blockIdx.x * U + i;
         if (u >= nunits) u = nunits - 1;  // a duplicate of the last unit writes the same bytes
         row[i] = u / chunks;
-        col[i] = (u - row[i] * chunks) * kChunk + threadIdx.x * 8;
+        col[i] = (u - row[i] * chunks) * (T * 8) + threadIdx.x * 8;
         raw[i] = load_raw8<true, BF16>(reinterpret_cast<const char*>(p.x) + (int64_t)row[i] * p.ldx * (BF16 ? 2 : 4),
                                        col[i], p.cols);
     }
@@ -376,6 +377,7 @@ hipError_t launch_tensor_scale_finalize(const float* amax, float* scales_out, fl
 
 template <bool VEC, bool BF16>
 static void quantize_launch(const QuantParams& p, hipStream_t s) {
+    constexpr int QT = 256;  // threads of the E2M1 group-128 kernel
     if (p.mode == 1) {
         dim3 grid((unsigned)p.rows);
         if (p.cols <= 4 * kChunk) hipLaunchKernelGGL((quantize_row_reg_kernel<VEC, BF16, 4>), grid, dim3(kThreads), 0, s, p);
@@ -386,10 +388,12 @@ static void quantize_launch(const QuantParams& p, hipStream_t s) {
         int64_t chunks = (p.cols + kChunk - 1) / kChunk;
         int64_t nunits = p.rows * chunks;
         dim3 grid((unsigned)((nunits + U - 1) / U));
-        if (VEC && p.mode == 2 && p.group == 128 && p.g.is_e2m1 && !p.col_shift && !p.amax_in && nunits < (1LL << 30) &&
-            p.cols < (1LL << 30))
-            hipLaunchKernelGGL((quantize_e2m1_g128_kernel<BF16, U>), grid, dim3(kThreads), 0, s, p, (int)chunks,
-                               (int)nunits);
+        if (VEC && p.mode == 2 && p.group == 128 && p.g.is_e2m1 && !p.col_shift && !p.amax_in &&
+            p.rows * ((p.cols + QT * 8 - 1) / (QT * 8)) < (1LL << 30) && p.cols < (1LL << 30)) {
+            const int64_t qchunks = (p.cols + QT * 8 - 1) / (QT * 8), qunits = p.rows * qchunks;
+            hipLaunchKernelGGL((quantize_e2m1_g128_kernel<BF16, 1, QT>), dim3((unsigned)qunits), dim3(QT), 0, s, p,
+                               (int)qchunks, (int)qunits);
+        }
         else
             hipLaunchKernelGGL((quantize_chunk_kernel<VEC, BF16, U>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
     }
