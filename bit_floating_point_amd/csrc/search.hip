@@ -92,9 +92,21 @@ __device__ __forceinline__ uint32_t e3m0_code(float y) {
     return (uint32_t)(c > 7 ? 7 : c);
 }
 
-__device__ __forceinline__ float e3m0_value(uint32_t c) { return c == 0 ? 0.0f : __uint_as_float((c + 126u) << 23); }
 
 __device__ __forceinline__ uint32_t e1m2_code(float y) { return (uint32_t)fminf(rintf(y * 4.0f), 7.0f); }
+
+// Nearest E3M0 grid value to y >= 0 without branches (same decisions as e3m0_code):
+// y <= 0.5 gives 0; otherwise adding 0x3fffff plus the exponent's low bit to the bit
+// pattern carries into the exponent exactly when the mantissa rounds up (past the
+// midpoint 1.5 * 2^E, or on it when the code E + 2 is even), the exponent is clamped
+// to the codes 1..7 (values 1..64), and NaN or infinity saturate like the code does.
+__device__ __forceinline__ float e3m0_round(float y) {
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t t = u + 0x3fffffu + ((u >> 23) & 1u);
+    uint32_t x = t >> 23;
+    x = x < 127u ? 127u : (x > 133u ? 133u : x);
+    return u > 0x3f000000u ? __uint_as_float(x << 23) : 0.0f;
+}
 
 struct Cand { float s, r; };
 
@@ -111,11 +123,12 @@ __device__ __forceinline__ DD eval_candidate(const float (&v)[kSPer], float s, f
             g0 = gv[0];
             g1 = gv[1];
         } else if (FMT == 0) {
-            g0 = (float)e1m2_code(y0) * 0.25f;
-            g1 = (float)e1m2_code(y1) * 0.25f;
+            // the E1M2 code min(rint(4y), 7) kept as a float: code * 0.25 exactly
+            g0 = fminf(rintf(y0 * 4.0f), 7.0f) * 0.25f;
+            g1 = fminf(rintf(y1 * 4.0f), 7.0f) * 0.25f;
         } else {
-            g0 = e3m0_value(e3m0_code(y0));
-            g1 = e3m0_value(e3m0_code(y1));
+            g0 = e3m0_round(y0);
+            g1 = e3m0_round(y1);
         }
         float q0 = g0 * s, q1 = g1 * s;
         double d0 = (double)v[i] - (double)q0;
