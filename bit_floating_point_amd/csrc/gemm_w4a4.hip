@@ -392,12 +392,50 @@ static void launch_cfg(const GemmParams& p, hipStream_t s, int64_t cus) {
     hipLaunchKernelGGL((w4a4_fp4_kernel<BM, BN>), dim3((unsigned)std::min(nt, cus)), dim3(256), 0, s, p, (int)gm,
                        (int)nt);
 }
-// 256x256 tiles when there are enough of them for every compute unit, else 128x128
+static GemmParams column_block(const GemmParams& p, int64_t n0, int64_t n1) {
+    GemmParams q = p;
+    q.N = n1 - n0;
+    q.w = p.w + n0 * p.ldw;
+    if (p.w_mode == 1) q.w_scales = reinterpret_cast<const float*>(p.w_scales) + n0;
+    q.y = reinterpret_cast<uint8_t*>(p.y) + n0 * (p.y_bf16 ? 2 : 4);
+    return q;
+}
+
+// Tile shapes and the last round.  Time of one round of tiles (every compute unit
+// busy), relative to 256x256 tiles on the same K, measured on the prefill shapes:
+// 256x128 0.59, 128x128 0.35.  With at least one full round of 256x256 tiles, the
+// whole rounds stay 256x256 and the column block left over for a partial last round
+// takes the shape that finishes it soonest (a partial round of big tiles leaves
+// compute units idle).  Fewer tiles than compute units: 128x128.
 static hipError_t launch_block(const GemmParams& p, hipStream_t s) {
     const int64_t cus = cu_count();
-    const int64_t gm256 = (p.M + 255) / 256, gn256 = (p.N + 255) / 256;
-    if (gm256 * gn256 >= cus) launch_cfg<256, 256>(p, s, cus);
-    else launch_cfg<128, 128>(p, s, cus);
+    const int64_t gm256 = (p.M + 255) / 256, gn256 = (p.N + 255) / 256, t256 = gm256 * gn256;
+    if (t256 < cus) {
+        launch_cfg<128, 128>(p, s, cus);
+        return hipGetLastError();
+    }
+    const int64_t full_cols = (t256 / cus) * cus / gm256;  // 256-column blocks of whole rounds
+    const int64_t n1 = std::min<int64_t>(p.N, full_cols * 256);
+    if (n1 >= p.N || t256 % cus == 0) {
+        launch_cfg<256, 256>(p, s, cus);
+        return hipGetLastError();
+    }
+    const int64_t rest = p.N - n1;
+    auto rounds = [&](int64_t bm, int64_t bn) {
+        const int64_t t = ((p.M + bm - 1) / bm) * ((rest + bn - 1) / bn);
+        return (double)((t + cus - 1) / cus);
+    };
+    // cost of the leftover block in 256x256-round units; 256x256 over the whole output
+    // costs one more round than the full ones
+    const double c256 = rounds(256, 256), c256x128 = 0.59 * rounds(256, 128), c128 = 0.35 * rounds(128, 128);
+    if (c256 <= c256x128 && c256 <= c128) {
+        launch_cfg<256, 256>(p, s, cus);
+        return hipGetLastError();
+    }
+    launch_cfg<256, 256>(column_block(p, 0, n1), s, cus);
+    const GemmParams q = column_block(p, n1, p.N);
+    if (c256x128 <= c128) launch_cfg<256, 128>(q, s, cus);
+    else launch_cfg<128, 128>(q, s, cus);
     return hipGetLastError();
 }
 

@@ -302,6 +302,8 @@ def test_preshift_w4a4_full_2048x4096x4096():
     (4100, 6000, 288, "row", 0),     # 17 x 24 tiles of 256, ragged M, N and K tail
     (4100, 6000, 256, "tensor", 0),
     (1500, 3000, 384, "row", 3),     # output rows not 16-byte aligned: element stores
+    (4096, 5200, 256, "row", 0),     # one round of 256x256 tiles, the rest as 256x128
+    (4096, 5120, 512, "tensor", 0),  # one round of 256x256 tiles, the rest as 128x128
 ])
 def test_w4a4_e2m1_many_tiles(M, N, K, mode, ldy_pad):
     """W4A4 E2M1 GEMM on random codes where each workgroup computes several tiles in
