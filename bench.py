@@ -140,12 +140,14 @@ def traffic_for(kernel_file: str, key: str):
 # Dispatches of `bench.py --profile all`, in launch order: (key, kernel file, kernel-name
 # fragment, index range among the dispatches whose name has that fragment).
 TRAFFIC_KERNELS = [
-    ("quantize_decode", "quant.hip", "quantize_chunk_kernel<true, false, 2>", (0, 3)),
+    ("quantize_decode", "quant.hip", "quantize_e2m1_g128_kernel<false, 1, 256>", (0, 3)),
     ("gemv_m1", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 1>", (0, 3)),
     ("gemv_m4", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 1>", (3, 6)),
     ("gemv_m16", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 3>", (0, 3)),
     ("quantize_act", "quant.hip", "quantize_chunk_kernel<true, true, 2>", (0, 3)),
-    ("w4a4_c3", "gemm_w4a4.hip", "w4a4_fp4_kernel", (0, 3)),
+    ("w4a4_c3", "gemm_w4a4.hip", "w4a4_fp4_kernel<128, 128>", (0, 3)),
+    ("w4a4_qkv", "gemm_w4a4.hip", "w4a4_fp4_kernel<256, 256>", (0, 3)),
+    ("nf4_qkv", "gemm_lut.hip", "w4a4_lut_kernel", (0, 3)),
 ]
 COPY_BYTES = 256 * 1024 * 1024  # the reference device copy of profile_run
 
@@ -329,14 +331,16 @@ def bench_prefill(torch, F):
         tot_fl += fl
         tot_t += t
         out.append(roofline_entry(f"w4a4 E2M1 GEMM {name} {T}x{n}x{k}", "mfma", fl / t / 1e12, FP4_PEAK_TFLOPS,
-                                  "TFLOP/s", t, fl, "flop"))
+                                  "TFLOP/s", t, fl, "flop",
+                                  traffic_for("gemm_w4a4.hip", "w4a4_qkv") if name == "qkv" else None))
         kn, an, wpn, wsn = F.fp4_preshift_weights(w, chan, fe2, fnf4, F.gran("group", 64))
         apn, _ = F.fp4_quantize_pack(X, fe2, F.gran("tensor"), tensor_scale=an, col_shift=kn)
         t = graph_time(torch, lambda i: F.fp4_gemm(apn, wpn, wsn, fnf4, F.gran("group", 64), K=k, a_grid=fe2,
                                                    a_scale=an, y=y), 3)
         tot_t_nf4 += t
         out.append(roofline_entry(f"nf4 x E2M1 GEMM (f16 MFMA) {name} {T}x{n}x{k}", "mfma", fl / t / 1e12,
-                                  F16_PEAK_TFLOPS, "TFLOP/s", t, fl, "flop"))
+                                  F16_PEAK_TFLOPS, "TFLOP/s", t, fl, "flop",
+                                  traffic_for("gemm_lut.hip", "nf4_qkv") if name == "qkv" else None))
         if name in ("qkv", "down"):
             xb = T * k * 2 + T * k // 2 + k
             t = graph_time(torch, lambda i: F.fp4_quantize_pack(X, fe2, F.gran("tensor"), tensor_scale=a,
@@ -359,8 +363,9 @@ def bench_prefill(torch, F):
 
 
 # VALU instructions per (element, candidate) in the search's inner loop, counted from the
-# gfx950 assembly of search_eval_kernel (E2M1 / E1M2 / E3M0 averaged)
-SEARCH_VALU_PER_EVAL = 17.0
+# gfx950 assembly of search_eval_kernel: E1M2 14.8, E2M1 12.3, E3M0 17.8 per element, plus
+# 2.4 per element for the per-candidate wavefront reduction; averaged over the formats
+SEARCH_VALU_PER_EVAL = 17.4
 
 
 def bench_search(torch, F):
@@ -504,6 +509,21 @@ def profile_run(torch, F, what):
             ap, _ = F.fp4_quantize_pack(X, fe2, F.gran("tensor"), tensor_scale=a, col_shift=k)
         for _ in range(3):
             F.fp4_gemm(ap, wp, ws, fe2, F.gran("row"), K=K, a_grid=fe2, a_scale=a)
+        # the prefill QKV projection, W4A4 E2M1 and NF4 x E2M1
+        T, (n, k) = 4096, PREFILL["qkv"]
+        X = gen_activations(torch, T, k, 500)
+        chan = F.fp4_calibrate(X, "column", first_rows=128)
+        w = gen_normal(torch, (n, k), 0.02, 600)
+        y = torch.empty((T, n), dtype=torch.bfloat16, device="cuda")
+        kk, a, wp, ws = F.fp4_preshift_weights(w, chan, fe2, fe2, F.gran("row"))
+        ap, _ = F.fp4_quantize_pack(X, fe2, F.gran("tensor"), tensor_scale=a, col_shift=kk)
+        for _ in range(3):
+            F.fp4_gemm(ap, wp, ws, fe2, F.gran("row"), K=k, a_grid=fe2, a_scale=a, y=y)
+        fnf4 = F.grid_nf4()
+        kn, an, wpn, wsn = F.fp4_preshift_weights(w, chan, fe2, fnf4, F.gran("group", 64))
+        apn, _ = F.fp4_quantize_pack(X, fe2, F.gran("tensor"), tensor_scale=an, col_shift=kn)
+        for _ in range(3):
+            F.fp4_gemm(apn, wpn, wsn, fnf4, F.gran("group", 64), K=k, a_grid=fe2, a_scale=an, y=y)
     torch.cuda.synchronize()
     log("profile run done")
 
