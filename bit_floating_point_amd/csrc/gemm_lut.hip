@@ -3,9 +3,8 @@
 // with the pre-shifted per-tensor scale a:
 //   Y[m, n] = a * sum_g s[n, g] * sum_{k in g} A_q[m, k] * G[c[n, k]]
 //
-// gfx950 has no matrix instruction for an arbitrary 16-value grid, so both operands are
-// expanded to f16 once per workgroup and K step, into LDS, and the products run on
-// v_mfma_f32_32x32x16_f16 with fp32 accumulation:
+// gfx950 has no matrix instruction for an arbitrary 16-value grid, so the products run
+// on v_mfma_f32_32x32x16_f16 with fp32 accumulation, both operands as f16:
 //  * activations: E2M1 -> f16 with the FP4 convert (exact);
 //  * weights: G[c] by byte permutes of a table held in registers (exact: the grid values
 //    are binary16), times the group scale taken relative to a power of two of the row:
@@ -15,12 +14,16 @@
 //    to the fp32 result (exactly).  Folding the scale into the expanded weights keeps
 //    the group scales out of the per-output arithmetic: one multiply per weight per
 //    workgroup instead of one per output element and group.
-// The LDS tiles are stored in MFMA fragment order (each 16-byte operand of lane l of a
-// 32-row tile and K16 block at byte 16 l of a 1 KiB block), so every fragment read is
-// one linear wavefront read.  Two LDS stages: while step k's MFMAs run, each wavefront
-// expands a quarter of step k+1 after every K16 block of MFMAs (interleaved so that the
-// VALU work overlaps the matrix work); packed codes for step k+2 are loaded meanwhile.
-// Tiles: 256x256 (4 wavefronts of 128x128) for large grids, 128x128 otherwise.
+// The weights are expanded once per workgroup and K step into LDS in MFMA fragment order
+// (each 16-byte operand of lane l of a 32-row tile and K16 block at byte 16 l of a 1 KiB
+// block), so every fragment read is one linear wavefront read.  The activations are
+// expanded the same way on 256x256 tiles; on 128x128 tiles they stay packed in LDS and
+// every wavefront converts its own fragments (a quarter of the LDS bytes, more VALU per
+// wavefront: better where several workgroups share a CU).  Two LDS stages: while step k's
+// MFMAs run, each wavefront expands a quarter of step k+1 after every K16 block of MFMAs
+// (interleaved so that the VALU work overlaps the matrix work); packed codes for step
+// k+2 are loaded meanwhile.  The MFMAs take the K values of a step in the order block kk,
+// lane half h: codes 32 h + 8 kk .. +7 (the same order on both operands).
 #include <algorithm>
 
 #include "fp4_device.h"
@@ -74,10 +77,10 @@ __device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, f16x2 s) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) * s);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, bool PK>
 __global__ void __launch_bounds__(256) w4a4_lut_kernel(GemmParams p, int grid_m) {
     constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
-    constexpr int A_BYTES = BM * kLutBK * 2, B_BYTES = BN * kLutBK * 2;  // f16 per stage
+    constexpr int A_BYTES = PK ? BM * kLutBK / 2 : BM * kLutBK * 2, B_BYTES = BN * kLutBK * 2;  // per stage
     constexpr int STAGE = A_BYTES + B_BYTES;
     constexpr int PA = BM * 2 / 256, PB = BN * 2 / 256;  // 16-byte packed pieces per thread per step
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
@@ -178,18 +181,33 @@ __global__ void __launch_bounds__(256) w4a4_lut_kernel(GemmParams p, int grid_m)
                                   : __builtin_amdgcn_raw_buffer_load_b32(rsS, off, 0, 0);
         }
     };
-    // LDS in MFMA fragment order: per K16 block kk and 32-row tile t a 1 KiB block whose
-    // 16-byte slot l holds row 32 t + l%32, K values 8*(l/32) .. +7 of the block
-    // decode + store chunk c (8 codes) of every packed piece of this thread into stage st
+    // LDS per stage: the activation codes packed, 32 B per row (row-major, the two 16-byte
+    // halves of a row swapped when bit 3 of the row is set, so a wavefront's 16-byte reads
+    // of 32 rows hit distinct banks); the weights expanded to f16 in MFMA fragment order:
+    // per K16 block kk and 32-row tile t a 1 KiB block whose 16-byte slot l holds row
+    // 32 t + l%32, K values 32 (l/32) + 8 kk .. +7 of the step.  The MFMAs take K in
+    // that order (block kk, lane half h: codes 32 h + 8 kk .. +7) on both operands.
+    // Decode + store chunk c (8 codes) of every weight piece of this thread into stage
+    // st; with chunk 0 the activation pieces are stored as they are.
     auto dstore_chunk = [&](int st, int c) {
         uint8_t* sa = smem + st * STAGE;
         uint8_t* sw = sa + A_BYTES;
+        if (PK) {
+            if (c == 0) {
 #pragma unroll
-        for (int i = 0; i < PA; i++) {
-            const uint32_t w[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
-            const int kc = kA[i] / 8 + c, kk = kc >> 1, hh = kc & 1, r = rowA[i];
-            *reinterpret_cast<uint4*>(sa + ((kk * (BM / 32) + (r >> 5)) * 64 + (r & 31) + 32 * hh) * 16) =
-                decode_e2m1_f16x8(w[c]);
+                for (int i = 0; i < PA; i++) {
+                    const int r = rowA[i], h = kA[i] / 32;
+                    *reinterpret_cast<uint4*>(sa + r * 32 + ((h ^ ((r >> 3) & 1)) << 4)) = ra[i];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PA; i++) {
+                const uint32_t w[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
+                const int h = kA[i] / 32, r = rowA[i];
+                *reinterpret_cast<uint4*>(sa + ((c * (BM / 32) + (r >> 5)) * 64 + (r & 31) + 32 * h) * 16) =
+                    decode_e2m1_f16x8(w[c]);
+            }
         }
 #pragma unroll
         for (int i = 0; i < PB; i++) {
@@ -197,11 +215,11 @@ __global__ void __launch_bounds__(256) w4a4_lut_kernel(GemmParams p, int grid_m)
             const _Float16 sh = (_Float16)(s * rinv[i]);
             const f16x2 s2 = {sh, sh};
             const uint32_t w[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
-            const int kc = kB[i] / 8 + c, kk = kc >> 1, hh = kc & 1, r = rowB[i];
+            const int hh = kB[i] / 32, r = rowB[i];
             uint4 v = decode_lut_f16x8(w[c], TL, TH);
             v.x = mul_f16x2(v.x, s2); v.y = mul_f16x2(v.y, s2);
             v.z = mul_f16x2(v.z, s2); v.w = mul_f16x2(v.w, s2);
-            *reinterpret_cast<uint4*>(sw + ((kk * (BN / 32) + (r >> 5)) * 64 + (r & 31) + 32 * hh) * 16) = v;
+            *reinterpret_cast<uint4*>(sw + ((c * (BN / 32) + (r >> 5)) * 64 + (r & 31) + 32 * hh) * 16) = v;
         }
     };
     auto dstore = [&](int st) {
@@ -222,12 +240,29 @@ __global__ void __launch_bounds__(256) w4a4_lut_kernel(GemmParams p, int grid_m)
     auto step = [&](int st) {
         const uint8_t* sa = smem + st * STAGE;
         const uint8_t* sw = sa + A_BYTES;
+        // this lane's activation codes of the step for its TM row tiles: word kk = the 8
+        // codes of K16 block kk in its half
+        uint4 apk[TM];
+        if (PK) {
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+                const int r = wm * WM + i * 32 + (lane & 31);
+                apk[i] = *reinterpret_cast<const uint4*>(sa + r * 32 + (((lane >> 5) ^ ((r >> 3) & 1)) << 4));
+            }
+        }
 #pragma unroll
         for (int kk = 0; kk < 4; kk++) {
             f16x8 af[TM];
 #pragma unroll
-            for (int i = 0; i < TM; i++)
-                af[i] = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(sa + ((kk * (BM / 32) + wm * TM + i) * 64 + lane) * 16));
+            for (int i = 0; i < TM; i++) {
+                if (PK) {
+                    const uint32_t w4[4] = {apk[i].x, apk[i].y, apk[i].z, apk[i].w};
+                    af[i] = __builtin_bit_cast(f16x8, decode_e2m1_f16x8(w4[kk]));
+                } else {
+                    af[i] = __builtin_bit_cast(
+                        f16x8, *reinterpret_cast<const uint4*>(sa + ((kk * (BM / 32) + wm * TM + i) * 64 + lane) * 16));
+                }
+            }
 #pragma unroll
             for (int j = 0; j < TN; j++) {
                 const f16x8 bf = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(sw + ((kk * (BN / 32) + wn * TN + j) * 64 + lane) * 16));
@@ -301,16 +336,50 @@ __global__ void __launch_bounds__(256) w4a4_lut_kernel(GemmParams p, int grid_m)
     }
 }
 
-static hipError_t launch_lut_block(const GemmParams& p, hipStream_t s) {
-    const int64_t gm256 = (p.M + 255) / 256, gn256 = (p.N + 255) / 256;
-    // 256x256 tiles when they give at least two per CU (one workgroup per CU at a time),
-    // else 128x128 (two per CU: better filled when there are few tiles)
-    if (gm256 * gn256 >= 512) {
-        hipLaunchKernelGGL((w4a4_lut_kernel<256, 256>), dim3((unsigned)(gm256 * gn256)), dim3(256), 0, s, p, (int)gm256);
-    } else {
-        const int64_t gm = (p.M + 127) / 128, gn = (p.N + 127) / 128;
-        hipLaunchKernelGGL((w4a4_lut_kernel<128, 128>), dim3((unsigned)(gm * gn)), dim3(256), 0, s, p, (int)gm);
+static int lut_cu_count() {
+    static int counts[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (counts[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        counts[dev] = n;
     }
+    return counts[dev];
+}
+static void lut256(const GemmParams& p, hipStream_t s) {
+    const int64_t gm = (p.M + 255) / 256, gn = (p.N + 255) / 256;
+    hipLaunchKernelGGL((w4a4_lut_kernel<256, 256, false>), dim3((unsigned)(gm * gn)), dim3(256), 0, s, p, (int)gm);
+}
+static void lut128(const GemmParams& p, hipStream_t s) {
+    const int64_t gm = (p.M + 127) / 128, gn = (p.N + 127) / 128;
+    hipLaunchKernelGGL((w4a4_lut_kernel<128, 128, true>), dim3((unsigned)(gm * gn)), dim3(256), 0, s, p, (int)gm);
+}
+// Whole rounds of 256x256 tiles (one workgroup per CU at a time); the column block left
+// for a partial last round, and grids with fewer 256x256 tiles than CUs, as 128x128
+// tiles with packed activations in LDS (several workgroups per CU).
+static hipError_t launch_lut_block(const GemmParams& p, hipStream_t s) {
+    const int64_t gm256 = (p.M + 255) / 256, gn256 = (p.N + 255) / 256, t256 = gm256 * gn256;
+    const int64_t cus = lut_cu_count();
+    if (t256 < cus) {
+        lut128(p, s);
+        return hipGetLastError();
+    }
+    const int64_t n1 = std::min<int64_t>(p.N, (t256 / cus) * cus / gm256 * 256);
+    if (n1 >= p.N || t256 % cus == 0) {
+        lut256(p, s);
+        return hipGetLastError();
+    }
+    GemmParams q = p;
+    q.N = n1;
+    lut256(q, s);
+    const int64_t srow = (p.K / p.w_group) * (p.w_scale_f16 ? 2 : 4);  // scale bytes per weight row
+    q = p;
+    q.N = p.N - n1;
+    q.w = p.w + n1 * p.ldw;
+    q.w_scales = reinterpret_cast<const uint8_t*>(p.w_scales) + n1 * srow;
+    q.y = reinterpret_cast<uint8_t*>(p.y) + n1 * (p.y_bf16 ? 2 : 4);
+    lut128(q, s);
     return hipGetLastError();
 }
 
