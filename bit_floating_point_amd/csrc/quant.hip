@@ -277,6 +277,34 @@ __global__ void __launch_bounds__(T) quantize_e2m1_g128_kernel(QuantParams p, in
     }
 }
 
+// TENSOR mode with the E2M1 grid (optionally with the activation-side column shifts
+// r * 2^-k), rows a multiple of 8 elements: the arithmetic of quantize_chunk_kernel,
+// specialised, one (row, T*8-column chunk) unit per workgroup.
+template <bool BF16, bool SHIFT, int T>
+__global__ void __launch_bounds__(T) quantize_e2m1_tensor_kernel(QuantParams p, int chunks) {
+    const int u = blockIdx.x;
+    const int row = u / chunks;
+    const int col = (u - row * chunks) * (T * 8) + threadIdx.x * 8;
+    const Raw8 raw =
+        load_raw8<true, BF16>(reinterpret_cast<const char*>(p.x) + (int64_t)row * p.ldx * (BF16 ? 2 : 4), col, p.cols);
+    const uint2 kk = SHIFT ? load_shift8<true>(p, col) : make_uint2(0, 0);
+    const float s = p.tensor_scale ? p.tensor_scale[0] : p.tensor_amax[0] / p.g.qmax;
+    const float r = recip_or_zero(s);
+    if (blockIdx.x == 0 && threadIdx.x == 0 && p.tensor_scale && p.scales_out)
+        reinterpret_cast<float*>(p.scales_out)[0] = s;
+    if (col < p.cols) {
+        float v[8];
+        raw8_to_float<BF16>(raw, v);
+        scale_values(v, r, SHIFT, kk);
+        uint32_t w = 0;
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+        *reinterpret_cast<uint32_t*>(p.packed + (int64_t)row * p.ldp + col / 2) = w;
+    }
+}
+
 // ROW mode, rows of at most R * 2048 elements: one workgroup per row, the row held in
 // registers (one HBM read), max reduced across the workgroup, then quantized.
 template <bool VEC, bool BF16, int R>
@@ -394,7 +422,16 @@ static void quantize_launch(const QuantParams& p, hipStream_t s) {
             hipLaunchKernelGGL((quantize_e2m1_g128_kernel<BF16, 1, QT>), dim3((unsigned)qunits), dim3(QT), 0, s, p,
                                (int)qchunks, (int)qunits);
         }
-        else
+        else if (VEC && p.mode == 0 && p.g.is_e2m1 && !p.amax_in && (!p.col_shift || p.shift_sign < 0) &&
+                 p.rows * ((p.cols + QT * 8 - 1) / (QT * 8)) < (1LL << 30) && p.cols < (1LL << 30)) {
+            const int64_t qchunks = (p.cols + QT * 8 - 1) / (QT * 8), qunits = p.rows * qchunks;
+            if (p.col_shift)
+                hipLaunchKernelGGL((quantize_e2m1_tensor_kernel<BF16, true, QT>), dim3((unsigned)qunits), dim3(QT), 0, s,
+                                   p, (int)qchunks);
+            else
+                hipLaunchKernelGGL((quantize_e2m1_tensor_kernel<BF16, false, QT>), dim3((unsigned)qunits), dim3(QT), 0,
+                                   s, p, (int)qchunks);
+        } else
             hipLaunchKernelGGL((quantize_chunk_kernel<VEC, BF16, U>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
     }
 }
