@@ -26,6 +26,28 @@ __device__ __forceinline__ float max_abs8(const float v[8]) {
     return m;
 }
 
+// Max over the aligned 16-lane group (one 128-element group of 8 elements per lane)
+// with DPP lane permutes, all in VALU: swap neighbours, swap pairs, mirror within 8,
+// mirror within 16.
+__device__ __forceinline__ float dpp_max16(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+
+// Max over the whole wavefront: 16-lane groups by DPP, then the four group maxima read
+// out with readlane (the result is uniform).
+__device__ __forceinline__ float dpp_wave_max(float v) {
+    v = dpp_max16(v);
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
 __global__ void fill_zero_u32_kernel(uint32_t* p, int64_t n) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0u;
@@ -51,7 +73,7 @@ __global__ void __launch_bounds__(kThreads) amax_tensor_kernel(const void* x, in
     const char* rp = reinterpret_cast<const char*>(x) + row * ld * (BF16 ? 2 : 4);
     float v[8];
     load8<VEC, BF16>(rp, col, cols, v);
-    float m = wave_max(max_abs8(v));
+    float m = dpp_wave_max(max_abs8(v));
     if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
 }
 
@@ -225,17 +247,6 @@ __global__ void __launch_bounds__(kThreads) quantize_chunk_kernel(QuantParams p,
     }
 }
 
-// Max over the aligned 16-lane group (one 128-element group of 8 elements per lane)
-// with DPP lane permutes, all in VALU: swap neighbours, swap pairs, mirror within 8,
-// mirror within 16.
-__device__ __forceinline__ float dpp_max16(float v) {
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
-    return v;
-}
-
 // GROUP mode with 128-element groups, the E2M1 grid, no column shifts, rows a multiple
 // of 8 elements: the same arithmetic as quantize_chunk_kernel, specialised (group
 // maximum by DPP instead of lane shuffles through LDS, no per-element grid dispatch).
@@ -333,7 +344,7 @@ __global__ void __launch_bounds__(kThreads) quantize_row_reg_kernel(QuantParams 
     if (p.amax_in) {
         amax = p.amax_in[row];
     } else {
-        m = wave_max(m);
+        m = dpp_wave_max(m);
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
         __syncthreads();
         amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
@@ -372,7 +383,7 @@ __global__ void __launch_bounds__(kThreads) quantize_row_kernel(QuantParams p) {
             if (has_k && p.shift_sign > 0) shift_inputs(v, load_shift8<VEC>(p, col));
             m = fmaxf(m, max_abs8(v));
         }
-        m = wave_max(m);
+        m = dpp_wave_max(m);
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
         __syncthreads();
         amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
@@ -486,7 +497,7 @@ __global__ void __launch_bounds__(1024) preshift_factors_kernel(const float* c, 
     __shared__ float red[16];
     float m = 0.0f;
     for (int64_t j = threadIdx.x; j < k; j += blockDim.x) m = fmaxf(m, c[j]);
-    m = wave_max(m);
+    m = dpp_wave_max(m);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     float cmax = 0.0f;
