@@ -9,12 +9,13 @@
 // accumulation: the result is bit-reproducible.
 //
 // Tiling for CDNA4: a 256-thread workgroup (2x2 wavefronts) computes BM x BN tiles of
-// Y (256x256 when the grid of such tiles fills the chip, else 128x128); each wavefront
-// a (BM/2) x (BN/2) sub-tile as a grid of 32x32 accumulators.  K advances 128 codes
-// (64 bytes per row) per step through a four-stage LDS ring fed by direct-to-LDS loads.
-// One workgroup per compute unit loops over tiles; the load ring runs on across tile
-// boundaries, so the next tile's first steps load while the last ones of the current
-// tile are computed and while its epilogue stores its outputs straight from registers.
+// Y (256x256 for whole rounds of tiles, 256x128 or 128x128 for the column block of a
+// partial last round or for small grids); each wavefront a (BM/2) x (BN/2) sub-tile as
+// a grid of 32x32 accumulators.  K advances 128 codes (64 bytes per row) per step
+// through a four-stage LDS ring fed by direct-to-LDS loads.  One workgroup per compute
+// unit loops over tiles; the load ring runs on across tile boundaries, so the next
+// tile's first steps load while the last ones of the current tile are computed and
+// while its epilogue writes its outputs.
 #include <algorithm>
 
 #include "fp4_device.h"
@@ -36,14 +37,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // XOR-swizzled tile (the 16-byte segments of a row are permuted by row so that the
 // 128-bit LDS reads of a wavefront spread over all banks).  Rows past M or N and K
 // tails get an offset past the buffer's end, which the hardware returns as zeros.
-// Four LDS stages: the loads for step k+3 are issued while step k is computed.
+// Four LDS stages: the loads for step k+4 are issued while step k is computed.
 //
 // 32x32x64 FP4 MFMAs (the 16x16x128 form issues at only the FP8 rate on gfx950), with
 // operands swapped -- D = W_tile * A_tile^T -- so a lane's accumulator holds 4
 // consecutive output columns of one row.  FP4 operand layout: lane l holds 32
 // consecutive codes (16 B) of row l%32 at K offset 32*(l/32); D layout: lane l, value v
-// holds D[8*(v/4) + 4*(l/32) + v%4][l%32].  A bf16 result tile is staged in LDS and
-// written with whole-row 16-byte stores.
+// holds D[8*(v/4) + 4*(l/32) + v%4][l%32].  A bf16 result tile is staged in each
+// wavefront's own LDS area and written with 16-byte stores.
 
 // Wait until at most N direct-to-LDS loads of this thread are in flight and every LDS
 // read of this wavefront has returned, then meet the workgroup barrier.  The LDS reads
@@ -61,8 +62,6 @@ __device__ __forceinline__ float agpr_read(float a) {
 // Wait for every outstanding memory operation of this thread (loads and stores), every
 // LDS read, and the workgroup barrier.
 #define FP4_SYNC_ALL() asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory")
-// Wait for this wavefront's LDS operations and meet the workgroup barrier.
-#define FP4_BAR() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory")
 // Wait for this wavefront's LDS operations.
 #define FP4_LDS_WAIT() asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory")
 
