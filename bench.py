@@ -437,7 +437,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is per-GPU and shards "
-              "without collectives, see DESIGN.md", file=sys.stderr)
+              "without collectives", file=sys.stderr)
         sys.exit(2)
     import torch
     import bit_floating_point_amd as F

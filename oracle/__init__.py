@@ -23,9 +23,10 @@ Sources (web pages, cited by title and section):
 * [Tutorial] "为什么我们需要4-bit浮点量化" (devpress.csdn.net), section 2.2: two 4-bit
   values per byte.
 
-Readings where the pages are silent or garbled are listed in the design doc.  Every
-function that has no independent pin in ``tests/test_oracle_pins.py`` says
-"parity unpinned" in its docstring (none at present).
+Readings where the pages are silent or garbled are stated in the docstrings of the
+functions that take them.  Every function that has no independent pin in
+``tests/test_oracle_pins.py`` says "parity unpinned" in its docstring (none at
+present).
 """
 from __future__ import annotations
 
