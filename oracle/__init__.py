@@ -487,6 +487,59 @@ def w4a4_epilogue_f32(acc, a_scale, s_row) -> np.ndarray:
     return (f32(acc) * sn[None, :]).astype(np.float32)
 
 
+# ----------------------------------------------------------------------------------
+# Activation quantization fused into the producing GEMM (the pages' fused
+# quantize-activation-dequantize idea, [HiFloat4] "Quant-GeLU-Dequant"): the LLaMA MLP
+# producer is SwiGLU, h = SiLU(x W_gate^T) * (x W_up^T), and its consumer the W4A4 down
+# projection, which takes h as E2M1 codes with its own pre-shift.
+# ----------------------------------------------------------------------------------
+LOG2E_F32 = np.float32(1.4426950408889634)
+# 2^f = e^(f ln 2): Taylor coefficients (ln 2)^i / i!, rounded to binary32, i = 0..7
+EXP2_COEF_F32 = [np.float32(math.log(2.0) ** i / math.factorial(i)) for i in range(8)]
+
+
+def exp_f32(x) -> np.ndarray:
+    """e^x as a fixed sequence of binary32 operations, so that any IEEE binary32
+    implementation of the same sequence gives the same bits: t = fl(x * log2 e),
+    n = rint(t) (ties to even), f = t - n (exact, |f| <= 1/2), p = the degree-7 Taylor
+    polynomial of 2^f in Horner form (a multiply and an add per term, no fused
+    multiply-add), result fl(p * 2^n).  Relative error below 1e-5 for |x| <= 88 (the
+    rounding of t dominates); 2^n over- and underflows like e^x."""
+    x = f32(x)
+    t = (x * LOG2E_F32).astype(np.float32)
+    n = np.rint(t).astype(np.float32)
+    fr = (t - n).astype(np.float32)
+    p = np.full_like(fr, EXP2_COEF_F32[7])
+    for c in reversed(EXP2_COEF_F32[:7]):
+        p = ((p * fr).astype(np.float32) + c).astype(np.float32)
+    with np.errstate(over="ignore", under="ignore"):
+        return np.ldexp(p, np.clip(n, -300, 300).astype(np.int64)).astype(np.float32)
+
+
+def silu_f32(x) -> np.ndarray:
+    """SiLU(x) = x * sigmoid(x) = x / (1 + e^-x), in binary32: fl(x / fl(1 + exp_f32(-x)))
+    (the division correctly rounded; e^-x = inf for very negative x gives -0)."""
+    x = f32(x)
+    with np.errstate(over="ignore"):
+        d = (np.float32(1) + exp_f32(-x)).astype(np.float32)
+        return (x / d).astype(np.float32)
+
+
+def w4a4_swiglu_quant(a_packed, a_scale, wg_packed, s_gate, wu_packed, s_up, out_scale, out_shift):
+    """Gate and up W4A4 E2M1 products of the same packed activations, each through the
+    fixed epilogue y = fl32(acc * fl32(a * s_n)) (binary32, before any bf16 rounding),
+    h = fl32(silu_f32(y_gate) * y_up), and h quantized as the next layer's activations:
+    quantize_activations(h, E2M1, out_scale, out_shift).  Returns (codes, h)."""
+    e2 = minifloat(2, 1)
+    _, acc_g = gemm_w4a4(a_packed, e2, a_scale, wg_packed, e2, "row", s_gate)
+    _, acc_u = gemm_w4a4(a_packed, e2, a_scale, wu_packed, e2, "row", s_up)
+    yg = w4a4_epilogue_f32(acc_g, a_scale, s_gate)
+    yu = w4a4_epilogue_f32(acc_u, a_scale, s_up)
+    h = (silu_f32(yg) * yu).astype(np.float32)
+    codes, _ = quantize_activations(h, e2, out_scale, out_shift)
+    return codes, h
+
+
 def rel_err(y, r) -> float:
     """Normwise max relative error max|y - r| / max|r|."""
     r = np.asarray(r, dtype=np.float64)

@@ -430,3 +430,64 @@ def test_nf4_gemm_exact_rational():
 
 def test_rel_err_definition():
     assert O.rel_err(np.array([1.0, 2.0]), np.array([1.0, 2.002])) == pytest.approx(0.002 / 2.002)
+
+
+# ---------------------------------------------------- SwiGLU + fused quantization -----
+def test_exp_f32_against_math_exp():
+    """exp_f32 is e^x to the stated accuracy (the rounding of x * log2 e dominates), exact
+    at 0, and its Horner coefficients are the Taylor coefficients of 2^f."""
+    assert O.exp_f32(np.float32(0.0)) == np.float32(1.0)
+    assert O.EXP2_COEF_F32[0] == np.float32(1.0) and abs(float(O.EXP2_COEF_F32[1]) - math.log(2)) < 1e-7
+    x = np.linspace(-87.0, 88.0, 100001).astype(np.float32)
+    r = np.array([math.exp(float(v)) for v in x[::97]])
+    assert np.max(np.abs(O.exp_f32(x[::97]).astype(np.float64) - r) / r) < 5e-6
+    xs = np.linspace(-10.0, 10.0, 20001).astype(np.float32)
+    rs = np.exp(xs.astype(np.float64))
+    assert np.max(np.abs(O.exp_f32(xs).astype(np.float64) - rs) / rs) < 1e-6
+    # e^x e^-x = 1 and e^1 = e, to binary32 accuracy
+    assert np.max(np.abs(O.exp_f32(xs).astype(np.float64) * O.exp_f32(-xs) - 1.0)) < 2e-6
+    assert abs(float(O.exp_f32(np.float32(1.0))) - math.e) < 4e-7
+
+
+def test_silu_f32_closed_forms():
+    """SiLU(0) = +-0, SiLU(x) - SiLU(-x) = x, SiLU -> x for large x and -> -0 for very
+    negative x, and x / (1 + e^-x) in binary64 to 1e-6 relative."""
+    z = O.silu_f32(np.array([0.0, -0.0], np.float32))
+    assert z[0] == 0 and z[1] == 0 and not np.signbit(z[0]) and np.signbit(z[1])
+    x = np.linspace(-12.0, 12.0, 4801).astype(np.float32)
+    d = O.silu_f32(x).astype(np.float64) - O.silu_f32(-x)
+    assert np.max(np.abs(d - x)) <= 2e-6 * np.max(np.abs(x))
+    big = O.silu_f32(np.array([100.0, 1000.0, -200.0, -1e30], np.float32))
+    assert big[0] == 100.0 and big[1] == 1000.0 and big[2] == 0 and big[3] == 0 and np.signbit(big[3])
+    r = x.astype(np.float64) / (1.0 + np.exp(-x.astype(np.float64)))
+    m = np.abs(r) > 1e-20
+    assert np.max(np.abs(O.silu_f32(x)[m] - r[m]) / np.abs(r[m])) < 1e-6
+
+
+def test_swiglu_quant_composition_by_hand():
+    """A 3x4 output with K = 32 from hand-made codes: gate and up computed directly from
+    the grid values in binary64, h = SiLU(gate) * up, then the next layer's activation
+    codes: matches w4a4_swiglu_quant except where h lies within 1e-5 of a rounding
+    midpoint (none here); swapping gate and up, or applying SiLU to up, changes codes."""
+    rng = np.random.default_rng(7)
+    e2 = O.minifloat(2, 1)
+    M, N, K = 3, 4, 32
+    a_codes = rng.integers(0, 16, (M, K)).astype(np.uint8)
+    g_codes = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    u_codes = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    pk = lambda c: (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    a = np.float32(0.0625)
+    sg = np.array([0.5, 0.25, 1.0, 0.125], np.float32)
+    su = np.array([0.25, 0.5, 0.125, 1.0], np.float32)
+    out_a = np.float32(0.5)
+    k = np.array([0, -1, 0, -2], np.int8)
+    codes, h = O.w4a4_swiglu_quant(pk(a_codes), a, pk(g_codes), sg, pk(u_codes), su, out_a, k)
+    val = lambda c: e2.decode(c).astype(np.float64)
+    yg = (val(a_codes) @ val(g_codes).T) * (float(a) * sg.astype(np.float64))
+    yu = (val(a_codes) @ val(u_codes).T) * (float(a) * su.astype(np.float64))
+    h64 = yg / (1.0 + np.exp(-yg)) * yu
+    assert np.max(np.abs(h - h64)) <= 1e-5 * np.max(np.abs(h64))
+    want, _ = O.quantize_activations(h64.astype(np.float32), e2, out_a, k)
+    assert np.array_equal(codes, want)
+    swapped, _ = O.w4a4_swiglu_quant(pk(a_codes), a, pk(u_codes), su, pk(g_codes), sg, out_a, k)
+    assert not np.array_equal(swapped, codes)
