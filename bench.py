@@ -362,6 +362,49 @@ def bench_prefill(torch, F):
     return out
 
 
+def bench_swiglu(torch, F):
+    """The LLaMA-13B MLP producer: gate and up W4A4 products of the same 4096 tokens with
+    SwiGLU and the down projection's E2M1 quantization (its scale a' and shifts k' from
+    pre-shifting the down weights) in one kernel, against the separate launches it
+    replaces: the gate and up GEMMs to bf16 and the activation quantization of h (the
+    SwiGLU elementwise pass between them is not counted, so the separate figure is a
+    lower bound)."""
+    T, (n, k) = 4096, PREFILL["up"]
+    fe2 = F.grid_minifloat(2, 1)
+    X1 = gen_activations(torch, T, k, 500)
+    X2 = gen_activations(torch, T, n, 501)
+    c1 = F.fp4_calibrate(X1, "column", first_rows=128)
+    c2 = F.fp4_calibrate(X2, "column", first_rows=128)
+    wd = gen_normal(torch, PREFILL["down"], 0.02, 603)
+    kd, ad, _, _ = F.fp4_preshift_weights(wd, c2, fe2, fe2, F.gran("row"))
+    del wd
+    wg = gen_normal(torch, (n, k), 0.02, 601)
+    wu = gen_normal(torch, (n, k), 0.02, 602)
+    kk, a, wgp, wgs = F.fp4_preshift_weights(wg, c1, fe2, fe2, F.gran("row"))
+    _, _, wup, wus = F.fp4_preshift_weights(wu, c1, fe2, fe2, F.gran("row"), shift=kk, act_scale=a)
+    del wg, wu
+    ap, _ = F.fp4_quantize_pack(X1, fe2, F.gran("tensor"), tensor_scale=a, col_shift=kk)
+    h = torch.empty((T, n // 2), dtype=torch.uint8, device="cuda")
+    t_f = graph_time(torch, lambda i: F.fp4_gemm_swiglu_quant(ap, a, wgp, wgs, wup, wus, ad, kd, K=k, h_packed=h), 5)
+    yg = torch.empty((T, n), dtype=torch.bfloat16, device="cuda")
+    yu = torch.empty_like(yg)
+    t_g = graph_time(torch, lambda i: F.fp4_gemm(ap, wgp, wgs, fe2, F.gran("row"), K=k, a_grid=fe2, a_scale=a,
+                                                 y=yg), 5)
+    t_u = graph_time(torch, lambda i: F.fp4_gemm(ap, wup, wus, fe2, F.gran("row"), K=k, a_grid=fe2, a_scale=a,
+                                                 y=yu), 5)
+    t_q = graph_time(torch, lambda i: F.fp4_quantize_pack(X2, fe2, F.gran("tensor"), tensor_scale=ad, col_shift=kd,
+                                                          packed=h), 8)
+    fl = 2 * T * 2 * n * k
+    sep = t_g + t_u + t_q
+    out = [roofline_entry(f"w4a4 gate+up GEMM with SwiGLU + E2M1 quantize epilogue {T}x(2x{n})x{k}", "mfma",
+                          fl / t_f / 1e12, FP4_PEAK_TFLOPS, "TFLOP/s", t_f, fl, "flop",
+                          separate_us=round(sep * 1e6, 2), separate_gemm_us=round((t_g + t_u) * 1e6, 2),
+                          separate_quantize_us=round(t_q * 1e6, 2), speedup_vs_separate=round(sep / t_f, 3))]
+    del X1, X2, ap, wgp, wup, h, yg, yu
+    torch.cuda.empty_cache()
+    return out
+
+
 # VALU instructions per (element, candidate) in the search's inner loop, counted from the
 # gfx950 assembly of search_eval_kernel: E1M2 14.8, E2M1 12.3, E3M0 17.8 per element, plus
 # 2.4 per element for the per-candidate wavefront reduction; averaged over the formats
@@ -453,6 +496,8 @@ def main():
         kernels += bench_preshift_w4a4(torch, F)
         log("LLaMA-13B prefill layer ...")
         kernels += bench_prefill(torch, F)
+        log("fused SwiGLU + quantize ...")
+        kernels += bench_swiglu(torch, F)
         log("format search ...")
         kernels += bench_search(torch, F)
     dominant = max(kernels[:4], key=lambda d: d["us_per_launch"])
@@ -524,6 +569,17 @@ def profile_run(torch, F, what):
         apn, _ = F.fp4_quantize_pack(X, fe2, F.gran("tensor"), tensor_scale=an, col_shift=kn)
         for _ in range(3):
             F.fp4_gemm(apn, wpn, wsn, fnf4, F.gran("group", 64), K=k, a_grid=fe2, a_scale=an, y=y)
+        # the MLP gate/up pair with SwiGLU and the down projection's quantization fused
+        n, k = PREFILL["up"]
+        X = gen_activations(torch, T, k, 500)
+        chan = F.fp4_calibrate(X, "column", first_rows=128)
+        wg = gen_normal(torch, (n, k), 0.02, 601)
+        kk, a, wgp, wgs = F.fp4_preshift_weights(wg, chan, fe2, fe2, F.gran("row"))
+        ap, _ = F.fp4_quantize_pack(X, fe2, F.gran("tensor"), tensor_scale=a, col_shift=kk)
+        h = torch.empty((T, n // 2), dtype=torch.uint8, device="cuda")
+        kd = torch.zeros(n, dtype=torch.int8, device="cuda")
+        for _ in range(3):
+            F.fp4_gemm_swiglu_quant(ap, a, wgp, wgs, wgp, wgs, a, kd, K=k, h_packed=h)
     torch.cuda.synchronize()
     log("profile run done")
 

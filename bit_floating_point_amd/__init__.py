@@ -20,7 +20,7 @@ from ._lib import (FP4Error, FP4_BF16, FP4_F16, FP4_F32, FP4_PACKED, FP4_REDUCE_
 
 __all__ = ["FP4Error", "grid_minifloat", "grid_lut", "grid_nf4", "nf4_values", "gran", "fp4_calibrate", "fp4_quantize_pack",
            "fp4_dequantize", "fp4_preshift_weights", "fp4_search_format", "fp4_gemm",
-           "search_results_host", "E2M1", "E1M2", "E3M0"]
+           "fp4_gemm_swiglu_quant", "search_results_host", "E2M1", "E1M2", "E3M0"]
 
 
 def grid_minifloat(e: int, m: int) -> L.fp4_grid:
@@ -234,3 +234,27 @@ def fp4_gemm(a: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor, w_
     d.y_dtype = FP4_BF16 if y.dtype == torch.bfloat16 else FP4_F32
     L.check(L.lib().fp4_gemm(ctypes.byref(d), _stream(a.device)), "fp4_gemm")
     return y
+
+
+def fp4_gemm_swiglu_quant(a: torch.Tensor, a_scale: torch.Tensor, w_gate: torch.Tensor, s_gate: torch.Tensor,
+                          w_up: torch.Tensor, s_up: torch.Tensor, out_scale: torch.Tensor,
+                          out_shift: torch.Tensor | None = None, K: int | None = None,
+                          h_packed: torch.Tensor | None = None) -> torch.Tensor:
+    """E2M1 codes of h = SiLU(X W_gate^T) * (X W_up^T) quantized for the next layer
+    (scale out_scale, column shifts out_shift).  a: packed E2M1 [M, K/2]; w_gate, w_up:
+    packed E2M1 [N, K/2] with f32 row scales s_gate, s_up.  Returns uint8 [M, N/2]."""
+    M = a.shape[0]
+    N = w_gate.shape[0]
+    K = K if K is not None else 2 * a.shape[1]
+    if h_packed is None:
+        h_packed = torch.empty((M, N // 2), dtype=torch.uint8, device=a.device)
+    d = L.fp4_swiglu_desc()
+    d.M, d.N, d.K = M, N, K
+    d.a, d.lda, d.a_scale = a.data_ptr(), _ld(a), a_scale.data_ptr()
+    d.w_gate, d.w_up, d.ldw = w_gate.data_ptr(), w_up.data_ptr(), _ld(w_gate)
+    d.s_gate, d.s_up = s_gate.data_ptr(), s_up.data_ptr()
+    d.out_scale = out_scale.data_ptr()
+    d.out_shift = out_shift.data_ptr() if out_shift is not None else None
+    d.h_packed, d.ldh = h_packed.data_ptr(), _ld(h_packed)
+    L.check(L.lib().fp4_gemm_swiglu_quant(ctypes.byref(d), _stream(a.device)), "fp4_gemm_swiglu_quant")
+    return h_packed

@@ -47,6 +47,15 @@ class fp4_gemm_desc(ctypes.Structure):
                 ("reserved1", ctypes.c_int32)]
 
 
+
+class fp4_swiglu_desc(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("a", ctypes.c_void_p), ("lda", ctypes.c_int64), ("a_scale", ctypes.c_void_p),
+                ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("ldw", ctypes.c_int64),
+                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p),
+                ("out_scale", ctypes.c_void_p), ("out_shift", ctypes.c_void_p),
+                ("h_packed", ctypes.c_void_p), ("ldh", ctypes.c_int64)]
+
 # exported symbol -> (restype, argtypes)
 P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 SIGNATURES = {
@@ -59,6 +68,7 @@ SIGNATURES = {
     "fp4_search_workspace_size": (ctypes.c_size_t, [I64, I64, I32, I32]),
     "fp4_search_format": (I32, [P, I64, I64, P, I32, I32, F32, F32, P, P, P, ctypes.c_size_t, P]),
     "fp4_gemm": (I32, [ctypes.POINTER(fp4_gemm_desc), P]),
+    "fp4_gemm_swiglu_quant": (I32, [ctypes.POINTER(fp4_swiglu_desc), P]),
 }
 
 

@@ -344,4 +344,37 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
     return fail(FP4_ERR_UNSUPPORTED, "W4A4 with minifloat weights other than E2M1 is not implemented");
 }
 
+fp4_status fp4_gemm_swiglu_quant(const fp4_swiglu_desc* d, void* stream) {
+    if (!d) return fail(FP4_ERR_INVALID_ARG, "null descriptor");
+    if (d->M < 0 || d->N < 0 || d->K <= 0) return fail(FP4_ERR_INVALID_ARG, "bad sizes");
+    if (d->N % 32 != 0) return fail(FP4_ERR_UNSUPPORTED, "N must be a multiple of 32");
+    if (d->K % 32 != 0) return fail(FP4_ERR_UNSUPPORTED, "K must be a multiple of 32");
+    if (d->K > 116508) return fail(FP4_ERR_UNSUPPORTED, "K <= 116508 (exact fp32 accumulation)");
+    if (d->M == 0 || d->N == 0) return ok();
+    if (!d->a || !d->a_scale || !d->w_gate || !d->w_up || !d->s_gate || !d->s_up || !d->out_scale ||
+        !d->h_packed)
+        return fail(FP4_ERR_INVALID_ARG, "null pointer");
+    if (d->lda < d->K / 2 || d->ldw < d->K / 2 || d->ldh < d->N / 2)
+        return fail(FP4_ERR_INVALID_ARG, "bad leading dimensions");
+    if (!aligned16(d->a) || !aligned16(d->w_gate) || !aligned16(d->w_up) || !aligned16(d->h_packed) ||
+        d->lda % 16 != 0 || d->ldw % 16 != 0 || d->ldh % 16 != 0)
+        return fail(FP4_ERR_ALIGNMENT, "a, w_gate, w_up, h_packed 16-byte aligned; lda, ldw, ldh multiples of 16");
+    GemmParams p{};
+    p.M = d->M;
+    p.N = d->N;
+    p.K = d->K;
+    p.a_kind = FP4_PACKED;
+    p.a = d->a;
+    p.lda = d->lda;
+    p.a_scale = d->a_scale;
+    p.w = d->w_gate;
+    p.ldw = d->ldw;
+    p.w_mode = FP4_SCALE_ROW;
+    p.w_scales = d->s_gate;
+    p.y = d->h_packed;
+    p.ldy = d->ldh;
+    GluParams g{d->w_up, d->s_up, d->out_scale, d->out_shift};
+    return hip_status(launch_w4a4_swiglu(p, g, (hipStream_t)stream), "fp4_gemm_swiglu_quant");
+}
+
 }  // extern "C"

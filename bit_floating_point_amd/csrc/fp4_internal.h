@@ -78,6 +78,15 @@ hipError_t launch_w4a16_mfma(const GemmParams& p, hipStream_t s);
 hipError_t launch_w4a16_valu(const GemmParams& p, hipStream_t s);
 hipError_t launch_w4a4_fp4(const GemmParams& p, hipStream_t s);
 hipError_t launch_w4a4_lut(const GemmParams& p, hipStream_t s);
+// W4A4 gate/up products with SwiGLU and the next layer's activation quantization in
+// the epilogue: p.w / p.w_scales are the gate weights and row scales, p.y the E2M1 codes
+struct GluParams {
+    const uint8_t* w_up;
+    const float* s_up;
+    const float* out_scale;   // next layer's per-tensor activation scale
+    const int8_t* out_shift;  // its per-column shifts, or null
+};
+hipError_t launch_w4a4_swiglu(const GemmParams& p, const GluParams& gp, hipStream_t s);
 
 // format search
 struct SearchCandidates {

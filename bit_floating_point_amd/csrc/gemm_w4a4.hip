@@ -62,25 +62,59 @@ __device__ __forceinline__ float agpr_read(float a) {
 // Wait for every outstanding memory operation of this thread (loads and stores), every
 // LDS read, and the workgroup barrier.
 #define FP4_SYNC_ALL() asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory")
+// Wait for this wavefront's LDS operations and meet the workgroup barrier.
+#define FP4_BAR() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory")
 // Wait for this wavefront's LDS operations.
 #define FP4_LDS_WAIT() asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory")
 
-template <int BM, int BN>
-__global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m, int ntiles) {
+// e^x as a fixed sequence of binary32 operations (bit-reproducible on any IEEE
+// binary32 implementation of the same sequence; built without contraction): t =
+// fl(x * log2 e), n = rint(t), f = t - n (exact), 2^f by its degree-7 Taylor polynomial
+// ((ln 2)^i / i!, rounded to binary32) in Horner form, times 2^n.  Relative error below
+// 1e-5 for |x| <= 88.
+__device__ __forceinline__ float exp_f32(float x) {
+    const float t = x * 0x1.715476p+0f;
+    const float n = rintf(t);
+    const float f = t - n;
+    float q = 0x1.ffcbfcp-17f;
+    q = q * f + 0x1.430912p-13f;
+    q = q * f + 0x1.5d87fep-10f;
+    q = q * f + 0x1.3b2ab6p-7f;
+    q = q * f + 0x1.c6b08ep-5f;
+    q = q * f + 0x1.ebfbe0p-3f;
+    q = q * f + 0x1.62e430p-1f;
+    q = q * f + 1.0f;
+    return ldexpf(q, (int)fminf(fmaxf(n, -300.0f), 300.0f));
+}
+// SiLU(x) = x / (1 + e^-x), the division correctly rounded
+__device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + exp_f32(-x)); }
+
+// GLU = false: Y = the W4A4 product through the fixed epilogue (bf16 or f32).
+// GLU = true: a tile's B rows [0, BN/2) are gate rows and [BN/2, BN) the up rows of the
+// same BN/2 output columns; each wavefront computes the gate and the up products of the
+// same rows and BN/4 output columns, and its epilogue writes E2M1 codes of
+// h = fl32(SiLU(y_gate) * y_up) quantized with the next layer's scale and shifts.
+template <int BM, int BN, bool GLU>
+__global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m, int ntiles, GluParams gp) {
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int TM = WM / 32, TN = WN / 32;
     constexpr int LA = BM * 4 / 256, LB = BN * 4 / 256;  // 16-byte pieces per thread per step
     constexpr int STAGE = (BM + BN) * kBKBytes;
-    // four operand stages, two 1 KiB blocks of per-column weight scales (tile parity),
-    // and each wavefront's output staging area (32 rows x WN/2 bf16 columns)
-    constexpr int STG_BYTES = 32 * WN;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * STAGE + 2048 + 4 * STG_BYTES];
+    // four operand stages, per tile parity a 1 KiB block of per-column weight scales (GLU:
+    // gate scales, up scales and the output shifts, 1 KiB each), and each wavefront's
+    // output staging area (32 rows x WN/2 bf16 columns; GLU: its columns' multipliers
+    // and 32 rows of codes)
+    constexpr int SCL_BYTES = GLU ? 3072 : 1024;
+    constexpr int STG_BYTES = GLU ? 2048 : 32 * WN;
+    constexpr int ON = GLU ? BN / 2 : BN;  // output columns per tile
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * STAGE + 2 * SCL_BYTES + 4 * STG_BYTES];
     uint8_t* const st0 = smem;
     uint8_t* const st1 = smem + STAGE;
     uint8_t* const st2 = smem + 2 * STAGE;
     uint8_t* const st3 = smem + 3 * STAGE;
     uint8_t* const scl = smem + 4 * STAGE;
-    uint8_t* const stg = smem + 4 * STAGE + 2048 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * STG_BYTES;
+    uint8_t* const stg_base = smem + 4 * STAGE + 2 * SCL_BYTES;
+    uint8_t* const stg = stg_base + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * STG_BYTES;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -94,9 +128,13 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
 
     const i32x4v rsA = buf_words(p.a, p.M * p.lda);
     const i32x4v rsB = buf_words(p.w, p.N * p.ldw);
+    const i32x4v rsB2 = GLU ? buf_words(gp.w_up, p.N * p.ldw) : rsB;
     const i32x4v rsS = buf_words(p.w_scales, p.w_mode == 1 ? p.N * 4 : 4);
+    const i32x4v rsS2 = GLU ? buf_words(gp.s_up, p.N * 4) : rsS;
+    const i32x4v rsK = (GLU && gp.out_shift) ? buf_words(gp.out_shift, p.N) : buf_words(p.w_scales, 0);
     const float a_scale = p.a_scale[0];
     const float s_tensor = reinterpret_cast<const float*>(p.w_scales)[0];
+    const float r_out = GLU ? recip_or_zero(gp.out_scale[0]) : 0.0f;  // next layer's fl32(1 / a')
 
     // Loads run ahead of the MFMAs through the tiles of this workgroup (tile t covers
     // rows bm*BM.., columns bn*BN.. with bm = t % grid_m, bn = t / grid_m; this
@@ -109,11 +147,11 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
         int sidx = (4 * i + wave) * 64 + lane, row = sidx >> 2;
         segk[i] = ((sidx & 3) ^ ((row >> 1) & 3)) * 32;
     }
-    uint32_t offA[LA], offB[LB], offS;
+    uint32_t offA[LA], offB[LB], offS, offK;
     int dt = blockIdx.x, dpar = 0;
     auto load_tile = [&](int t) {
         const bool ok = t < ntiles;
-        const int64_t m0 = (int64_t)(t % grid_m) * BM, n0 = (int64_t)(t / grid_m) * BN;
+        const int64_t m0 = (int64_t)(t % grid_m) * BM, n0 = (int64_t)(t / grid_m) * ON;
 #pragma unroll
         for (int i = 0; i < LA; i++) {
             int row = ((4 * i + wave) * 64 + lane) >> 2;
@@ -122,9 +160,11 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
 #pragma unroll
         for (int i = 0; i < LB; i++) {
             int row = ((4 * i + wave) * 64 + lane) >> 2;
+            if (GLU && i >= LB / 2) row -= BN / 2;  // up rows (their own buffer)
             offB[i] = (ok && n0 + row < p.N) ? (uint32_t)((n0 + row) * p.ldw + segk[i] / 2) : kOOB;
         }
-        offS = (ok && p.w_mode == 1 && n0 + 4 * lane < p.N) ? (uint32_t)((n0 + 4 * lane) * 4) : kOOB;
+        offS = (ok && p.w_mode == 1 && n0 + 4 * lane < p.N && 4 * lane < ON) ? (uint32_t)((n0 + 4 * lane) * 4) : kOOB;
+        offK = (ok && 16 * lane < ON && n0 + 16 * lane < p.N) ? (uint32_t)(n0 + 16 * lane) : kOOB;
     };
     load_tile(dt);
 
@@ -139,13 +179,21 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
         }                                                                                                  \
         _Pragma("unroll") for (int i = 0; i < LB; i++) {                                                   \
             uint32_t off = (kb_ * 128 + segk[i] < p.K) ? offB[i] + (uint32_t)kb_ * kBKBytes : kOOB;        \
-            dma16(rsB, off, __builtin_amdgcn_readfirstlane(                                                \
+            dma16((GLU && i >= LB / 2) ? rsB2 : rsB, off, __builtin_amdgcn_readfirstlane(                  \
                                 (uint32_t)(uintptr_t)&STG[BM * kBKBytes + (4 * i + wave) * 1024]));       \
         }                                                                                                  \
     } while (0)
 // the load stream's tile's 256 column scales into scales block dpar (all wavefronts
 // load the same 1 KiB, so every thread issues the same number of loads)
-#define FP4_DMAS() dma16(rsS, offS, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&scl[dpar * 1024]))
+#define FP4_DMAS()                                                                                         \
+    do {                                                                                                   \
+        const uint32_t sb_ = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&scl[dpar * SCL_BYTES]); \
+        dma16(rsS, offS, sb_);                                                                             \
+        if (GLU) {                                                                                         \
+            dma16(rsS2, offS, sb_ + 1024);                                                                 \
+            dma16(rsK, offK, sb_ + 2048);                                                                  \
+        }                                                                                                  \
+    } while (0)
 // the load stream moves on to this workgroup's next tile
 #define FP4_NEXT_TILE()                                                                                    \
     do {                                                                                                   \
@@ -155,13 +203,15 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
     } while (0)
 
 // fragments of half H of a step (K codes 64 H .. 64 H + 63 under the stage's segment
-// order): FA[i] for A (rows), FB[j] for W (columns), 16 bytes each
+// order): FA[i] for A (rows), FB[j] for W (columns), 16 bytes each.  B row of fragment
+// j: wn * WN + 32 j; GLU: fragments [0, TN/2) are gate rows wn * WN/2 + 32 j and
+// [TN/2, TN) the up rows of the same columns.
 #define FP4_READH(STG, H, FA, FB)                                                                          \
     do {                                                                                                   \
         _Pragma("unroll") for (int i = 0; i < TM; i++) FA[i] =                                             \
             *reinterpret_cast<const uint4*>(&STG[swz(wm * WM + i * 32 + r32, 2 * (H) + hk)]);              \
         _Pragma("unroll") for (int j = 0; j < TN; j++) FB[j] =                                             \
-            *reinterpret_cast<const uint4*>(&STG[BM * kBKBytes + swz(wn * WN + j * 32 + r32, 2 * (H) + hk)]); \
+            *reinterpret_cast<const uint4*>(&STG[BM * kBKBytes + swz(brow(j) + r32, 2 * (H) + hk)]);       \
     } while (0)
 // the MFMAs of one half step from fragment registers, with the LDS reads of the next
 // half step (issued just before) spread between them
@@ -182,6 +232,9 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
         }                                                                                                  \
     } while (0)
 
+    auto brow = [&](int j) {
+        return GLU ? (j / (TN / 2)) * (BN / 2) + wn * (WN / 2) + (j % (TN / 2)) * 32 : wn * WN + j * 32;
+    };
     f32x16 acc[TN][TM];
     constexpr int PER_STEP = LA + LB;  // operand loads per step and thread (+1 with scales)
     // 16-byte output stores per thread of a staged epilogue (32 rows x WN bf16 columns
@@ -253,104 +306,162 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
         // epilogue of tile ct: y = fl32(acc * fl32(a * s_n)); value v of lane l holds
         // row 32 i + l%32 and column 32 j + 8 (v/4) + 4 (l/32) + v%4 of this wavefront's
         // sub-tile.
-        const int64_t m0 = (int64_t)(ct % grid_m) * BM, n0 = (int64_t)(ct / grid_m) * BN;
-        const float* sc = reinterpret_cast<const float*>(scl + cpar * 1024);
-        const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
-        if (p.y_bf16 && full && (p.ldy & 7) == 0 && p.ldy < (1 << 26) &&
-            (reinterpret_cast<uintptr_t>(p.y) & 15) == 0) {
-            // bf16 whole tile: staged in this wavefront's own LDS area, 32 rows x WN/2
-            // columns at a time (16-byte chunks XOR-swizzled by row), written out as whole
-            // 16-byte pieces.  The stores are not waited for: the first three waits of the
-            // next tile count them.  Addresses: a per-lane 32-bit part plus a
-            // wavefront-uniform row offset.
-            constexpr int CH2 = WN / 16;    // 16-byte chunks per staged row (WN/2 columns)
-            constexpr int RPQ = 64 / CH2;   // rows per read-back pass
-            const int xw = (r32 & (CH2 - 1)) << 4;
-            const int rl = lane / CH2, cl = lane % CH2;
-            const uint32_t goff = (uint32_t)(rl * p.ldy * 2 + cl * 16);
-            char* const ytile = reinterpret_cast<char*>(p.y) + ((m0 + wm * WM) * p.ldy + n0 + wn * WN) * 2;
+        const int64_t m0 = (int64_t)(ct % grid_m) * BM, n0 = (int64_t)(ct / grid_m) * ON;
+        const float* sc = reinterpret_cast<const float*>(scl + cpar * SCL_BYTES);
+        if constexpr (GLU) {
+            // This wavefront's BN/4 output columns c0 + [0, WN/2) of rows wm * WM + [0, WM):
+            // gate accumulators acc[jj], up accumulators acc[jj + TN/2].  First lane l puts
+            // column c0 + l's multipliers fl32(a * s_gate), fl32(a * s_up) and
+            // fl32(r' * 2^-k') in this wavefront's area; then per 32x32 block: h =
+            // fl32(SiLU(y_gate) * y_up), times the multiplier, converted to E2M1 codes
+            // (nearest, ties to even, +-6), 32 rows x 16 bytes staged and stored.  Rows past
+            // M and 32-column blocks past N are not stored.
+            constexpr int WC = WN / 2;  // output columns per wavefront
+            const int c0 = wn * WC;
+            const int8_t* kq = reinterpret_cast<const int8_t*>(scl + cpar * SCL_BYTES + 2048);
+            float* const mul_g = reinterpret_cast<float*>(stg);
+            float* const mul_u = mul_g + WC;
+            float* const mul_k = mul_g + 2 * WC;
+            uint8_t* const cst = stg + 1024;
+            if (lane < WC) {
+                mul_g[lane] = a_scale * sc[c0 + lane];
+                mul_u[lane] = a_scale * sc[256 + c0 + lane];
+                mul_k[lane] = ldexpf(r_out, -(int)kq[c0 + lane]);
+            }
+            FP4_LDS_WAIT();
 #pragma unroll
             for (int i = 0; i < TM; i++) {
 #pragma unroll
-                for (int jh = 0; jh < 2; jh++) {
+                for (int jj = 0; jj < TN / 2; jj++) {
 #pragma unroll
-                    for (int jj = 0; jj < TN / 2; jj++)
+                    for (int g = 0; g < 4; g++) {
+                        const int cl = jj * 32 + 8 * g + 4 * hk;  // column within this wavefront's
+                        const float4 fg = *reinterpret_cast<const float4*>(&mul_g[cl]);
+                        const float4 fu = *reinterpret_cast<const float4*>(&mul_u[cl]);
+                        const float4 fk = *reinterpret_cast<const float4*>(&mul_k[cl]);
+                        const float fg4[4] = {fg.x, fg.y, fg.z, fg.w}, fu4[4] = {fu.x, fu.y, fu.z, fu.w};
+                        const float fk4[4] = {fk.x, fk.y, fk.z, fk.w};
+                        float v[4];
 #pragma unroll
-                        for (int g = 0; g < 4; g++) {
-                            const int j = jh * (TN / 2) + jj;
-                            float4 s4 = make_float4(s_tensor, s_tensor, s_tensor, s_tensor);
-                            if (p.w_mode == 1) s4 = *reinterpret_cast<const float4*>(&sc[wn * WN + j * 32 + 8 * g + 4 * hk]);
-                            const float f[4] = {a_scale * s4.x, a_scale * s4.y, a_scale * s4.z, a_scale * s4.w};
-                            __bf16 h4[4];
-#pragma unroll
-                            for (int t = 0; t < 4; t++) h4[t] = (__bf16)(agpr_read(acc[j][i][4 * g + t]) * f[t]);
-                            *reinterpret_cast<uint2*>(stg + r32 * (WN) + (((jj * 4 + g) << 4) ^ xw) + hk * 8) =
-                                __builtin_bit_cast(uint2, h4);
+                        for (int t = 0; t < 4; t++) {
+                            const float yg = agpr_read(acc[jj][i][4 * g + t]) * fg4[t];
+                            const float yu = agpr_read(acc[jj + TN / 2][i][4 * g + t]) * fu4[t];
+                            v[t] = (silu_f32(yg) * yu) * fk4[t];
                         }
+                        uint32_t w = 0;
+                        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+                        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+                        *reinterpret_cast<uint16_t*>(cst + r32 * 16 + 4 * g + 2 * hk) = (uint16_t)w;
+                    }
                     FP4_LDS_WAIT();
-#pragma unroll
-                    for (int q = 0; q < 32 * CH2 / 64; q++) {
-                        const int row = q * RPQ + rl;
-                        const uint4 v = *reinterpret_cast<const uint4*>(stg + row * WN + ((cl ^ (row & (CH2 - 1))) << 4));
-                        *reinterpret_cast<uint4*>(ytile + (int64_t)(i * 32 + q * RPQ) * p.ldy * 2 + jh * WN + goff) = v;
+                    const int64_t m = m0 + wm * WM + i * 32 + lane;
+                    const int64_t nc = n0 + c0 + jj * 32;
+                    if (lane < 32 && m < p.M && nc < p.N) {
+                        const uint4 c16 = *reinterpret_cast<const uint4*>(cst + lane * 16);
+                        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(p.y) + m * p.ldy + nc / 2) = c16;
                     }
                     FP4_LDS_WAIT();
                 }
             }
-        } else {
-            // edge tiles, f32 output, unaligned rows: stores straight from registers,
-            // then a full wait (their number does not fit the wait counts above)
-#pragma unroll
-            for (int j = 0; j < TN; j++)
-#pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    const int nl = wn * WN + j * 32 + 8 * g + 4 * hk;
-                    const int64_t n = n0 + nl;
-                    float4 s4 = make_float4(s_tensor, s_tensor, s_tensor, s_tensor);
-                    if (p.w_mode == 1) {
-                        if (full) {
-                            s4 = *reinterpret_cast<const float4*>(&sc[nl]);
-                        } else {  // scales straight from memory; columns past N are not stored
-                            const float* ws = reinterpret_cast<const float*>(p.w_scales);
-                            s4.x = ws[n < p.N ? n : p.N - 1];
-                            s4.y = ws[n + 1 < p.N ? n + 1 : p.N - 1];
-                            s4.z = ws[n + 2 < p.N ? n + 2 : p.N - 1];
-                            s4.w = ws[n + 3 < p.N ? n + 3 : p.N - 1];
-                        }
-                    }
-                    const float f0 = a_scale * s4.x, f1 = a_scale * s4.y, f2 = a_scale * s4.z, f3 = a_scale * s4.w;
-                    const bool vec = full && (p.ldy & 3) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
-#pragma unroll
-                    for (int i = 0; i < TM; i++) {
-                        const int64_t m = m0 + wm * WM + i * 32 + r32;
-                        const float y0 = agpr_read(acc[j][i][4 * g]) * f0, y1 = agpr_read(acc[j][i][4 * g + 1]) * f1;
-                        const float y2 = agpr_read(acc[j][i][4 * g + 2]) * f2, y3 = agpr_read(acc[j][i][4 * g + 3]) * f3;
-                        if (p.y_bf16) {
-                            __bf16* yp = reinterpret_cast<__bf16*>(p.y) + m * p.ldy + n;
-                            __bf16 h4[4] = {(__bf16)y0, (__bf16)y1, (__bf16)y2, (__bf16)y3};
-                            if (vec) {
-                                *reinterpret_cast<uint2*>(yp) = __builtin_bit_cast(uint2, h4);
-                            } else if (m < p.M) {
-                                if (n < p.N) yp[0] = h4[0];
-                                if (n + 1 < p.N) yp[1] = h4[1];
-                                if (n + 2 < p.N) yp[2] = h4[2];
-                                if (n + 3 < p.N) yp[3] = h4[3];
-                            }
-                        } else {
-                            float* yp = reinterpret_cast<float*>(p.y) + m * p.ldy + n;
-                            if (vec) {
-                                *reinterpret_cast<float4*>(yp) = make_float4(y0, y1, y2, y3);
-                            } else if (m < p.M) {
-                                if (n < p.N) yp[0] = y0;
-                                if (n + 1 < p.N) yp[1] = y1;
-                                if (n + 2 < p.N) yp[2] = y2;
-                                if (n + 3 < p.N) yp[3] = y3;
-                            }
-                        }
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
             FP4_SYNC_ALL();
+        } else {
+            const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
+            if (p.y_bf16 && full && (p.ldy & 7) == 0 && p.ldy < (1 << 26) &&
+                (reinterpret_cast<uintptr_t>(p.y) & 15) == 0) {
+                // bf16 whole tile: staged in this wavefront's own LDS area, 32 rows x WN/2
+                // columns at a time (16-byte chunks XOR-swizzled by row), written out as whole
+                // 16-byte pieces.  The stores are not waited for: the first three waits of the
+                // next tile count them.  Addresses: a per-lane 32-bit part plus a
+                // wavefront-uniform row offset.
+                constexpr int CH2 = WN / 16;    // 16-byte chunks per staged row (WN/2 columns)
+                constexpr int RPQ = 64 / CH2;   // rows per read-back pass
+                const int xw = (r32 & (CH2 - 1)) << 4;
+                const int rl = lane / CH2, cl = lane % CH2;
+                const uint32_t goff = (uint32_t)(rl * p.ldy * 2 + cl * 16);
+                char* const ytile = reinterpret_cast<char*>(p.y) + ((m0 + wm * WM) * p.ldy + n0 + wn * WN) * 2;
+    #pragma unroll
+                for (int i = 0; i < TM; i++) {
+    #pragma unroll
+                    for (int jh = 0; jh < 2; jh++) {
+    #pragma unroll
+                        for (int jj = 0; jj < TN / 2; jj++)
+    #pragma unroll
+                            for (int g = 0; g < 4; g++) {
+                                const int j = jh * (TN / 2) + jj;
+                                float4 s4 = make_float4(s_tensor, s_tensor, s_tensor, s_tensor);
+                                if (p.w_mode == 1) s4 = *reinterpret_cast<const float4*>(&sc[wn * WN + j * 32 + 8 * g + 4 * hk]);
+                                const float f[4] = {a_scale * s4.x, a_scale * s4.y, a_scale * s4.z, a_scale * s4.w};
+                                __bf16 h4[4];
+    #pragma unroll
+                                for (int t = 0; t < 4; t++) h4[t] = (__bf16)(agpr_read(acc[j][i][4 * g + t]) * f[t]);
+                                *reinterpret_cast<uint2*>(stg + r32 * (WN) + (((jj * 4 + g) << 4) ^ xw) + hk * 8) =
+                                    __builtin_bit_cast(uint2, h4);
+                            }
+                        FP4_LDS_WAIT();
+    #pragma unroll
+                        for (int q = 0; q < 32 * CH2 / 64; q++) {
+                            const int row = q * RPQ + rl;
+                            const uint4 v = *reinterpret_cast<const uint4*>(stg + row * WN + ((cl ^ (row & (CH2 - 1))) << 4));
+                            *reinterpret_cast<uint4*>(ytile + (int64_t)(i * 32 + q * RPQ) * p.ldy * 2 + jh * WN + goff) = v;
+                        }
+                        FP4_LDS_WAIT();
+                    }
+                }
+            } else {
+                // edge tiles, f32 output, unaligned rows: stores straight from registers,
+                // then a full wait (their number does not fit the wait counts above)
+    #pragma unroll
+                for (int j = 0; j < TN; j++)
+    #pragma unroll
+                    for (int g = 0; g < 4; g++) {
+                        const int nl = wn * WN + j * 32 + 8 * g + 4 * hk;
+                        const int64_t n = n0 + nl;
+                        float4 s4 = make_float4(s_tensor, s_tensor, s_tensor, s_tensor);
+                        if (p.w_mode == 1) {
+                            if (full) {
+                                s4 = *reinterpret_cast<const float4*>(&sc[nl]);
+                            } else {  // scales straight from memory; columns past N are not stored
+                                const float* ws = reinterpret_cast<const float*>(p.w_scales);
+                                s4.x = ws[n < p.N ? n : p.N - 1];
+                                s4.y = ws[n + 1 < p.N ? n + 1 : p.N - 1];
+                                s4.z = ws[n + 2 < p.N ? n + 2 : p.N - 1];
+                                s4.w = ws[n + 3 < p.N ? n + 3 : p.N - 1];
+                            }
+                        }
+                        const float f0 = a_scale * s4.x, f1 = a_scale * s4.y, f2 = a_scale * s4.z, f3 = a_scale * s4.w;
+                        const bool vec = full && (p.ldy & 3) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
+    #pragma unroll
+                        for (int i = 0; i < TM; i++) {
+                            const int64_t m = m0 + wm * WM + i * 32 + r32;
+                            const float y0 = agpr_read(acc[j][i][4 * g]) * f0, y1 = agpr_read(acc[j][i][4 * g + 1]) * f1;
+                            const float y2 = agpr_read(acc[j][i][4 * g + 2]) * f2, y3 = agpr_read(acc[j][i][4 * g + 3]) * f3;
+                            if (p.y_bf16) {
+                                __bf16* yp = reinterpret_cast<__bf16*>(p.y) + m * p.ldy + n;
+                                __bf16 h4[4] = {(__bf16)y0, (__bf16)y1, (__bf16)y2, (__bf16)y3};
+                                if (vec) {
+                                    *reinterpret_cast<uint2*>(yp) = __builtin_bit_cast(uint2, h4);
+                                } else if (m < p.M) {
+                                    if (n < p.N) yp[0] = h4[0];
+                                    if (n + 1 < p.N) yp[1] = h4[1];
+                                    if (n + 2 < p.N) yp[2] = h4[2];
+                                    if (n + 3 < p.N) yp[3] = h4[3];
+                                }
+                            } else {
+                                float* yp = reinterpret_cast<float*>(p.y) + m * p.ldy + n;
+                                if (vec) {
+                                    *reinterpret_cast<float4*>(yp) = make_float4(y0, y1, y2, y3);
+                                } else if (m < p.M) {
+                                    if (n < p.N) yp[0] = y0;
+                                    if (n + 1 < p.N) yp[1] = y1;
+                                    if (n + 2 < p.N) yp[2] = y2;
+                                    if (n + 3 < p.N) yp[3] = y3;
+                                }
+                            }
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                FP4_SYNC_ALL();
+            }
         }
         ct += gridDim.x;
         if (ct >= ntiles) break;
@@ -388,8 +499,8 @@ static int cu_count() {
 template <int BM, int BN>
 static void launch_cfg(const GemmParams& p, hipStream_t s, int64_t cus) {
     const int64_t gm = (p.M + BM - 1) / BM, gn = (p.N + BN - 1) / BN, nt = gm * gn;
-    hipLaunchKernelGGL((w4a4_fp4_kernel<BM, BN>), dim3((unsigned)std::min(nt, cus)), dim3(256), 0, s, p, (int)gm,
-                       (int)nt);
+    hipLaunchKernelGGL((w4a4_fp4_kernel<BM, BN, false>), dim3((unsigned)std::min(nt, cus)), dim3(256), 0, s, p,
+                       (int)gm, (int)nt, GluParams{});
 }
 static GemmParams column_block(const GemmParams& p, int64_t n0, int64_t n1) {
     GemmParams q = p;
@@ -453,6 +564,43 @@ hipError_t launch_w4a4_fp4(const GemmParams& p, hipStream_t s) {
             if (p.w_mode == 1) q.w_scales = reinterpret_cast<const float*>(p.w_scales) + n0;
             q.y = reinterpret_cast<uint8_t*>(p.y) + (m0 * p.ldy + n0) * ysz;
             hipError_t e = launch_block(q, s);
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
+// SwiGLU + next-layer quantization: tiles of BM rows x BN/2 output columns (gate and up
+// rows of those columns), 256 x 128 when they give every compute unit a tile, else
+// 128 x 64; operands past the 32-bit buffer range are split into row blocks.
+template <int BM, int BN>
+static void launch_glu_cfg(const GemmParams& p, const GluParams& gp, hipStream_t s, int64_t cus) {
+    const int64_t gm = (p.M + BM - 1) / BM, gn = (p.N + BN / 2 - 1) / (BN / 2), nt = gm * gn;
+    hipLaunchKernelGGL((w4a4_fp4_kernel<BM, BN, true>), dim3((unsigned)std::min(nt, cus)), dim3(256), 0, s, p,
+                       (int)gm, (int)nt, gp);
+}
+
+hipError_t launch_w4a4_swiglu(const GemmParams& p, const GluParams& gp, hipStream_t s) {
+    if (p.M == 0 || p.N == 0) return hipSuccess;
+    const int64_t cus = cu_count();
+    const int64_t mstep = std::max<int64_t>(256, kMaxBufBytes / std::max<int64_t>(p.lda, 1) / 256 * 256);
+    const int64_t nstep = std::max<int64_t>(128, kMaxBufBytes / std::max<int64_t>(p.ldw, 1) / 128 * 128);
+    for (int64_t m0 = 0; m0 < p.M; m0 += mstep) {
+        for (int64_t n0 = 0; n0 < p.N; n0 += nstep) {
+            GemmParams q = p;
+            q.M = std::min(mstep, p.M - m0);
+            q.N = std::min(nstep, p.N - n0);
+            q.a = reinterpret_cast<const uint8_t*>(p.a) + m0 * p.lda;
+            q.w = p.w + n0 * p.ldw;
+            q.w_scales = reinterpret_cast<const float*>(p.w_scales) + n0;
+            q.y = reinterpret_cast<uint8_t*>(p.y) + m0 * p.ldy + n0 / 2;
+            GluParams g = gp;
+            g.w_up = gp.w_up + n0 * p.ldw;
+            g.s_up = gp.s_up + n0;
+            if (gp.out_shift) g.out_shift = gp.out_shift + n0;
+            if (((q.M + 255) / 256) * ((q.N + 127) / 128) >= cus) launch_glu_cfg<256, 256>(q, g, s, cus);
+            else launch_glu_cfg<128, 128>(q, g, s, cus);
+            hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
     }

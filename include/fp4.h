@@ -17,7 +17,9 @@
  *              group size 128.
  *   [Tutorial] "为什么我们需要4-bit浮点量化" (devpress.csdn.net), section 2.2: two 4-bit
  *              values per byte, on-the-fly 4->8-bit decode for the matmul.
- *   [HiFloat4] "HiFloat4格式" (cf-1.com), section 3.2: 128-bit loads of 32 packed values.
+ *   [HiFloat4] "HiFloat4格式" (cf-1.com), section 3.2: 128-bit loads of 32 packed values;
+ *              section 5 (LLaMA-13B case): activation quantization fused with the
+ *              activation function.
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless the comment says "host".  The caller owns
@@ -248,6 +250,42 @@ fp4_status fp4_search_format(const float* w, int64_t ntensors, int64_t numel,
  *   y_dtype FP4_BF16 rounds the f32 result to nearest-even.
  * Strides: K a multiple of 32 for the matrix-core paths; packed rows 16-byte aligned. */
 fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream);
+
+/* ---- fused SwiGLU + next-layer activation quantization ---------------------------- */
+typedef struct {
+    int64_t M, N, K;          /* X [M, K]; W_gate, W_up [N, K]; h [M, N]            */
+    const uint8_t* a;         /* packed E2M1 activations [M, K/2], leading dim lda   */
+    int64_t lda;              /* bytes, multiple of 16                              */
+    const float* a_scale;     /* device: the one f32 activation scale a             */
+    const uint8_t* w_gate;    /* packed E2M1 [N, K/2], leading dim ldw              */
+    const uint8_t* w_up;      /* packed E2M1 [N, K/2], leading dim ldw              */
+    int64_t ldw;              /* bytes, multiple of 16                              */
+    const float* s_gate;      /* f32 [N] row scales of W_gate                       */
+    const float* s_up;        /* f32 [N] row scales of W_up                         */
+    const float* out_scale;   /* device: the consumer's f32 activation scale a'     */
+    const int8_t* out_shift;  /* int8 [N]: the consumer's column shifts k', or NULL */
+    uint8_t* h_packed;        /* E2M1 codes of h [M, N/2], leading dim ldh          */
+    int64_t ldh;              /* bytes, multiple of 16, >= N/2                       */
+} fp4_swiglu_desc;
+
+/* The LLaMA MLP's gate and up products of the same E2M1 activations with the SwiGLU
+ * activation and the down projection's activation quantization in the epilogue, so that
+ * h never exists in high precision in memory ([HiFloat4] section 5: quantization fused
+ * with the activation function; [FP4-LLM] pre-shifted exponent bias on the consumer):
+ *   y_g = fl32(acc_g[m,n] * fl32(a * s_gate[n])),  y_u likewise with W_up, s_up
+ *     (acc = the exact code product, as in fp4_gemm's E2M1 x E2M1 path)
+ *   h   = fl32(SiLU(y_g) * y_u),  SiLU(x) = fl32(x / fl32(1 + exp32(-x))), where
+ *     exp32 is a fixed binary32 operation sequence: t = fl(x * log2 e), n = rint(t),
+ *     f = t - n, 2^f by its degree-7 Taylor polynomial in Horner form (coefficients
+ *     (ln 2)^i / i! rounded to binary32, a separate multiply and add per term), times
+ *     2^n (n clamped to [-300, 300]); relative error below 1e-5 for |x| <= 88
+ *   codes = fp4_quantize_pack(h, E2M1, TENSOR, tensor_scale = out_scale,
+ *     col_shift = out_shift): y = fl32(h * fl32(r' * 2^-k'[n])), r' = fl32(1 / a'),
+ *     nearest E2M1 value after clipping to +-6, ties to even, sign bit of y.
+ * Every step is a fixed binary32 sequence: the codes are bit-reproducible.
+ * Requirements: N a multiple of 32; K a multiple of 32 and <= 116508; a, w_gate, w_up,
+ * h_packed 16-byte aligned.  Empty M or N returns FP4_OK with nothing launched. */
+fp4_status fp4_gemm_swiglu_quant(const fp4_swiglu_desc* d, void* stream);
 
 #ifdef __cplusplus
 }

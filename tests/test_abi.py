@@ -23,7 +23,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = L.load()
     names = _declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES)
@@ -34,13 +34,16 @@ def test_struct_layouts_match_header(tmp_path):
     src.write_text('#include "fp4.h"\n#include <stdio.h>\n#include <stddef.h>\n'
                    'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(fp4_grid), sizeof(fp4_gran),'
                    ' sizeof(fp4_search_result), sizeof(fp4_gemm_desc), offsetof(fp4_gemm_desc, a_scale),'
-                   ' offsetof(fp4_gemm_desc, w_gran), offsetof(fp4_gemm_desc, y_dtype)); return 0;}\n')
+                   ' offsetof(fp4_gemm_desc, w_gran), offsetof(fp4_gemm_desc, y_dtype));'
+                   ' printf("%zu %zu %zu\\n", sizeof(fp4_swiglu_desc), offsetof(fp4_swiglu_desc, out_shift),'
+                   ' offsetof(fp4_swiglu_desc, ldh)); return 0;}\n')
     exe = tmp_path / "sz"
     subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
     got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
     want = [ctypes.sizeof(L.fp4_grid), ctypes.sizeof(L.fp4_gran), ctypes.sizeof(L.fp4_search_result),
             ctypes.sizeof(L.fp4_gemm_desc), L.fp4_gemm_desc.a_scale.offset, L.fp4_gemm_desc.w_gran.offset,
-            L.fp4_gemm_desc.y_dtype.offset]
+            L.fp4_gemm_desc.y_dtype.offset, ctypes.sizeof(L.fp4_swiglu_desc), L.fp4_swiglu_desc.out_shift.offset,
+            L.fp4_swiglu_desc.ldh.offset]
     assert got == want
 
 
@@ -143,6 +146,38 @@ def test_gemm_validation():
     d.ldw = 128
     d.y_dtype = 7
     assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_INVALID_ARG
+
+
+def test_swiglu_validation():
+    lib = L.load()
+    N = ctypes.c_void_p(0)
+    assert lib.fp4_gemm_swiglu_quant(None, N) == L.FP4_ERR_INVALID_ARG
+    d = L.fp4_swiglu_desc()
+    d.M, d.N, d.K = 16, 64, 256
+    d.a, d.lda, d.a_scale = 0x10000, 128, 0x18000
+    d.w_gate, d.w_up, d.ldw = 0x20000, 0x28000, 128
+    d.s_gate, d.s_up, d.out_scale = 0x30000, 0x38000, 0x40000
+    d.h_packed, d.ldh = 0x50000, 32
+    d.N = 48
+    assert lib.fp4_gemm_swiglu_quant(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # N % 32
+    d.N, d.K = 64, 240
+    assert lib.fp4_gemm_swiglu_quant(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # K % 32
+    d.K = 116512
+    assert lib.fp4_gemm_swiglu_quant(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # K too large for exact sums
+    d.K = 256
+    d.s_up = None
+    assert lib.fp4_gemm_swiglu_quant(ctypes.byref(d), N) == L.FP4_ERR_INVALID_ARG
+    d.s_up = 0x38000
+    d.ldh = 16
+    assert lib.fp4_gemm_swiglu_quant(ctypes.byref(d), N) == L.FP4_ERR_INVALID_ARG  # ldh < N/2
+    d.ldh = 40
+    assert lib.fp4_gemm_swiglu_quant(ctypes.byref(d), N) == L.FP4_ERR_ALIGNMENT
+    d.ldh = 32
+    d.w_up = 0x28004
+    assert lib.fp4_gemm_swiglu_quant(ctypes.byref(d), N) == L.FP4_ERR_ALIGNMENT
+    d.w_up = 0x28000
+    d.M = 0
+    assert lib.fp4_gemm_swiglu_quant(ctypes.byref(d), N) == L.FP4_OK  # empty: nothing launched
 
 
 def test_preshift_validation():

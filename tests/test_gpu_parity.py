@@ -340,6 +340,75 @@ def test_w4a4_e2m1_many_tiles(M, N, K, mode, ldy_pad):
         F.fp4_gemm(gap, gwp, gws, fe2, F.gran(mode), K=0, a_grid=fe2, a_scale=ga)
 
 
+def _swiglu_case(rng, M, N, K):
+    """Random E2M1 codes for X, W_gate, W_up (16-byte aligned rows), scales that put
+    y_gate and y_up around +-4, the consumer's scale a' at the 99th percentile of |h| / 6
+    (so some values clip) and shifts k' in [-3, 0] or none."""
+    e2 = O.minifloat(2, 1)
+    ap = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    wg = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    wu = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    a = np.float32(rng.uniform(0.5, 2.0) / np.sqrt(K) / 4)
+    sg = rng.uniform(0.5, 2.0, N).astype(np.float32)
+    su = rng.uniform(0.5, 2.0, N).astype(np.float32)
+    return e2, ap, wg, wu, a, sg, su
+
+
+def _swiglu_dev(ap, wg, wu, a, sg, su, out_scale, out_shift, M, N, K, pad=16):
+    lda = (K // 2 + 15) // 16 * 16
+    gap = torch.zeros((M, lda), dtype=torch.uint8, device=DEV)
+    gwg = torch.zeros((N, lda), dtype=torch.uint8, device=DEV)
+    gwu = torch.zeros((N, lda), dtype=torch.uint8, device=DEV)
+    gap[:, :K // 2] = torch.from_numpy(ap).to(DEV)
+    gwg[:, :K // 2] = torch.from_numpy(wg).to(DEV)
+    gwu[:, :K // 2] = torch.from_numpy(wu).to(DEV)
+    hbuf = torch.full((M, N // 2 + pad), 0xAB, dtype=torch.uint8, device=DEV)
+    gk = dev(out_shift, torch.int8) if out_shift is not None else None
+    F.fp4_gemm_swiglu_quant(gap, dev(np.array([a], np.float32)), gwg, dev(sg), gwu, dev(su),
+                            dev(np.array([out_scale], np.float32)), gk, K=K, h_packed=hbuf[:, :N // 2])
+    return host(hbuf)
+
+
+@pytest.mark.parametrize("M,N,K,shifts", [
+    (300, 320, 544, True),     # 128x128 tiles (64 output columns each), ragged M, K tail
+    (300, 320, 544, False),    # no consumer shifts
+    (2100, 4128, 288, True),   # 256x256 tiles (128 output columns), ragged M; last tile 32 columns
+    (40, 96, 32, True),        # one K step of 32 codes, a single partial tile
+])
+def test_swiglu_quant(M, N, K, shifts):
+    """Gate/up W4A4 with SwiGLU and the consumer's E2M1 quantization in the epilogue:
+    every code bit-exact against the oracle; bytes past N/2 in each row untouched."""
+    say("swiglu", M, N, K, shifts)
+    rng = np.random.default_rng(M * 7 + N + K)
+    e2, ap, wg, wu, a, sg, su = _swiglu_case(rng, M, N, K)
+    k = rng.integers(-3, 1, N).astype(np.int8) if shifts else None
+    _, h = O.w4a4_swiglu_quant(ap, a, wg, sg, wu, su, np.float32(1.0), None)
+    out_scale = np.float32(np.percentile(np.abs(h), 99) / 6.0)
+    codes, _ = O.w4a4_swiglu_quant(ap, a, wg, sg, wu, su, out_scale, k)
+    got = _swiglu_dev(ap, wg, wu, a, sg, su, out_scale, k, M, N, K)
+    assert np.array_equal(got[:, :N // 2], codes)
+    assert bool((got[:, N // 2:] == 0xAB).all())
+    # the codes are not degenerate: several magnitudes and both signs occur
+    u = O.unpack(codes)
+    assert len(np.unique(u & 7)) == 8 and (u >= 8).any()
+
+
+def test_swiglu_quant_full_4096x13824x5120():
+    """The LLaMA-13B MLP gate/up shape (4096 tokens, 5120 -> 2 x 13824): codes of 24
+    sampled rows bit-exact against the oracle."""
+    M, N, K = 4096, 13824, 5120
+    say("swiglu full", M, N, K)
+    rng = np.random.default_rng(13824)
+    e2, ap, wg, wu, a, sg, su = _swiglu_case(rng, M, N, K)
+    k = rng.integers(-3, 1, N).astype(np.int8)
+    rows = np.sort(rng.choice(M, 24, replace=False))
+    _, h = O.w4a4_swiglu_quant(ap[rows], a, wg, sg, wu, su, np.float32(1.0), None)
+    out_scale = np.float32(np.percentile(np.abs(h), 99) / 6.0)
+    codes, _ = O.w4a4_swiglu_quant(ap[rows], a, wg, sg, wu, su, out_scale, k)
+    got = _swiglu_dev(ap, wg, wu, a, sg, su, out_scale, k, M, N, K, pad=0)
+    assert np.array_equal(got[rows], codes)
+
+
 @pytest.mark.parametrize("M,N,K", [(256, 384, 512), (130, 200, 640)])
 def test_preshift_nf4(M, N, K):
     say("nf4", M, N, K)
