@@ -427,6 +427,31 @@ def search_tensor(w, formats=FORMATS_4BIT, nclips: int = 100, lo: float = 0.5,
     return rec, packed.reshape(-1), mse
 
 
+def search_activations(x, unit: str, first_rows: int = 0, formats=FORMATS_4BIT, nclips: int = 100,
+                       lo: float = 0.5, hi: float = 1.0):
+    """The search applied to activations ([FP4-LLM] search-based FP quantization, for
+    activations as for weights; [Overview] static quantization from calibration data,
+    per-token granularity).  x [rows, cols] (bf16 values taken as their binary32 values).
+    unit 'tensor': rows [0, T) (T = first_rows, or every row when first_rows <= 0 or >=
+    rows) are one tensor for search_tensor, and every row is packed with its winner
+    (quantize_pack, TENSOR scale); unit 'row': search_tensor on each row, each row packed
+    with its own winner.  Returns (list of SearchRecord, packed [rows, cols/2])."""
+    x = f32(x)
+    R, C = x.shape
+    if unit == "row":
+        recs, rows = [], []
+        for r in range(R):
+            rec, p, _ = search_tensor(x[r], formats, nclips, lo, hi)
+            recs.append(rec)
+            rows.append(p)
+        return recs, (np.stack(rows) if R else np.zeros((0, C // 2), np.uint8))
+    if unit != "tensor":
+        raise ValueError(unit)
+    T = first_rows if 0 < first_rows < R else R
+    rec, _, _ = search_tensor(x[:T], formats, nclips, lo, hi)
+    packed, _ = quantize_pack(x, minifloat(rec.e, rec.m), "tensor", tensor_scale=rec.scale)
+    return [rec], packed
+
 # ----------------------------------------------------------------------------------
 # Quantized GEMMs (scales factored out of the low-bit product: [FP4-LLM] "efficient
 # matrix multiplication"; [W8A8] section 2.2 quantized_matmul).  Y = X W^T, W [N, K].

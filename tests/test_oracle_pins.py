@@ -491,3 +491,55 @@ def test_swiglu_quant_composition_by_hand():
     assert np.array_equal(codes, want)
     swapped, _ = O.w4a4_swiglu_quant(pk(a_codes), a, pk(u_codes), su, pk(g_codes), sg, out_a, k)
     assert not np.array_equal(swapped, codes)
+
+
+# ---- the search on activations: per-token units and calibration-token units ----------
+def _planted_row(rng, fmt, cols, scale_exp):
+    """A row of exact grid values of one format times 2^scale_exp, every magnitude code
+    present and the largest attained: the clip-1.0 candidate of that format reproduces
+    it with zero error, and no other format's grid holds all its ratios."""
+    g = O.minifloat(*fmt)
+    codes = np.concatenate([np.arange(8), rng.integers(0, 8, cols - 8)])
+    rng.shuffle(codes)
+    sign = np.where(rng.random(cols) < 0.5, -1.0, 1.0)
+    return (g.array[codes] * sign * 2.0 ** scale_exp).astype(np.float32), codes
+
+
+def test_search_activations_per_row_recovers_each_rows_format():
+    rng = np.random.default_rng(21)
+    fmts = [(1, 2), (2, 1), (3, 0), (2, 1), (1, 2)]
+    rows = [_planted_row(rng, f, 64, -3 - i) for i, f in enumerate(fmts)]
+    x = np.stack([r for r, _ in rows])
+    recs, packed = O.search_activations(x, "row", nclips=8)
+    assert packed.shape == (5, 32)
+    for i, (f, rec) in enumerate(zip(fmts, recs)):
+        assert (rec.e, rec.m, rec.clip_index, rec.mse) == (f[0], f[1], 7, 0.0)
+        assert rec.scale == np.float32(2.0 ** (-3 - i))  # largest grid value x 2^e / Qmax
+        mag = O.unpack(packed[i]) & 7
+        assert np.array_equal(mag, rows[i][1])
+
+
+def test_search_activations_calibration_rows_decide_every_row():
+    """Unit 'tensor' with T calibration rows: the winner comes from rows [0, T) only
+    (E3M0 at scale 2^-5), and every row -- the ones past T included -- is packed with it:
+    a row of E1M2 values k 2^-5 (k = 0..7) maps to the E3M0 values 0, 1, 2, 2, 4, 4, 8, 8
+    (3 and 6 are ties, each to the even code), values beyond the clip saturate at code 7."""
+    rng = np.random.default_rng(22)
+    calib = np.stack([_planted_row(rng, (3, 0), 48, -5)[0] for _ in range(3)])
+    later, later_codes = _planted_row(rng, (1, 2), 48, -3)
+    big = np.full(48, 1000.0, np.float32)
+    big[::2] = -1000.0
+    x = np.concatenate([calib, later[None], big[None]])
+    recs, packed = O.search_activations(x, "tensor", first_rows=3, nclips=4)
+    assert len(recs) == 1
+    rec = recs[0]
+    assert (rec.e, rec.m, rec.clip_index, rec.mse) == (3, 0, 3, 0.0)
+    assert rec.scale == np.float32(2.0 ** -5)
+    codes = O.unpack(packed)
+    e3m0 = O.minifloat(3, 0).array
+    assert np.array_equal(e3m0[codes[3] & 7], np.array([0, 1, 2, 2, 4, 4, 8, 8], np.float32)[later_codes])
+    assert np.array_equal(codes[3] >> 3, np.signbit(later).astype(np.uint8))  # -0 keeps its sign
+    assert np.all(codes[4] & 7 == 7) and np.array_equal(codes[4] >> 3, (np.arange(48) % 2 == 0).astype(np.uint8))
+    # taking the E1M2 row into the calibration set makes E3M0 at that scale inexact
+    recs_all, _ = O.search_activations(x[:4], "tensor", nclips=4)
+    assert recs_all[0].mse > 0.0
