@@ -430,9 +430,26 @@ def bench_search(torch, F):
     ops = evals * SEARCH_VALU_PER_EVAL
     del w, packed
     torch.cuda.empty_cache()
-    return [roofline_entry("format/clip search 32 x 4096x4096 (3 formats x 100 clips)", "alu", ops / t / 1e12,
-                           VALU_PEAK_TOPS, "TOP/s", t, evals, "element-candidate evaluations",
-                           evals_per_s=evals / t)]
+    out = [roofline_entry("format/clip search 32 x 4096x4096 (3 formats x 100 clips)", "alu", ops / t / 1e12,
+                          VALU_PEAK_TOPS, "TOP/s", t, evals, "element-candidate evaluations",
+                          evals_per_s=evals / t)]
+    # the same search on activations: per token over the LLaMA-13B prefill input (4096 x
+    # 5120 bf16), and once over its 128 calibration tokens with every token packed
+    X = gen_activations(torch, 4096, 5120, 500)
+    ws = torch.empty(F._lib.lib().fp4_search_workspace_size(4096, 5120, 3, 100), dtype=torch.uint8, device="cuda")
+    packed = torch.empty((4096, 2560), dtype=torch.uint8, device="cuda")
+    for unit, first, name in (("row", 0, "per-token"), ("tensor", 128, "128 calibration tokens")):
+        fn = (lambda i, unit=unit, first=first:
+              F.fp4_search_activations(X, unit, first_rows=first, workspace=ws, packed=packed))
+        t = graph_time(torch, fn, 3)
+        evals = (4096 if unit == "row" else 128) * 5120 * 3 * 100
+        ops = evals * SEARCH_VALU_PER_EVAL
+        out.append(roofline_entry(f"activation format/clip search, {name}, 4096x5120 bf16 (3 formats x 100 clips)",
+                                  "alu", ops / t / 1e12, VALU_PEAK_TOPS, "TOP/s", t, evals,
+                                  "element-candidate evaluations", evals_per_s=evals / t))
+    del X, ws, packed
+    torch.cuda.empty_cache()
+    return out
 
 
 # ----------------------------------------------------------------------------- CPU oracle

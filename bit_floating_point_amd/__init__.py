@@ -20,7 +20,7 @@ from ._lib import (FP4Error, FP4_BF16, FP4_F16, FP4_F32, FP4_PACKED, FP4_REDUCE_
 
 __all__ = ["FP4Error", "grid_minifloat", "grid_lut", "grid_nf4", "nf4_values", "gran", "fp4_calibrate", "fp4_quantize_pack",
            "fp4_dequantize", "fp4_preshift_weights", "fp4_search_format", "fp4_gemm",
-           "fp4_gemm_swiglu_quant", "search_results_host", "E2M1", "E1M2", "E3M0"]
+           "fp4_gemm_swiglu_quant", "fp4_search_activations", "search_results_host", "E2M1", "E1M2", "E3M0"]
 
 
 def grid_minifloat(e: int, m: int) -> L.fp4_grid:
@@ -175,6 +175,32 @@ def fp4_search_format(w: torch.Tensor, formats=(E1M2, E2M1, E3M0), nclips: int =
                                       _stream(dev)), "fp4_search_format")
     return results, packed
 
+
+
+def fp4_search_activations(x: torch.Tensor, unit: str = "row", first_rows: int = 0, formats=(E1M2, E2M1, E3M0),
+                           nclips: int = 100, clip_lo: float = 0.5, clip_hi: float = 1.0,
+                           workspace: torch.Tensor | None = None, packed: torch.Tensor | None = None):
+    """x: [rows, cols] float32 or bfloat16.  unit 'row': a search per row (token);
+    'tensor': one search over rows [0, first_rows) (all rows if first_rows <= 0), every
+    row packed with its winner.  Returns (results buffer, packed [rows, cols/2])."""
+    rows, cols = x.shape
+    dev = x.device
+    per_row = unit == "row"
+    units = rows if per_row else 1
+    t = 1 if per_row else (first_rows if 0 < first_rows < rows else rows)
+    fm = (ctypes.c_int32 * (2 * len(formats)))(*[v for f in formats for v in f])
+    need = L.lib().fp4_search_workspace_size(units, t * cols, len(formats), nclips)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    results = torch.empty(max(units, 1) * SEARCH_RESULT_BYTES, dtype=torch.uint8, device=dev)
+    if packed is None:
+        packed = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    L.check(L.lib().fp4_search_activations(_ptr(x), _dtype_code(x), rows, cols, _ld(x),
+                                           FP4_SCALE_ROW if per_row else FP4_SCALE_TENSOR, first_rows, fm,
+                                           len(formats), nclips, clip_lo, clip_hi, _ptr(results), _ptr(packed),
+                                           _ld(packed), _ptr(workspace), workspace.numel(), _stream(dev)),
+            "fp4_search_activations")
+    return results, packed
 
 @dataclass
 class SearchRecord:

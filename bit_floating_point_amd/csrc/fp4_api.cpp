@@ -252,6 +252,36 @@ size_t fp4_search_workspace_size(int64_t ntensors, int64_t numel, int32_t nforma
     return search_workspace_bytes(ntensors, numel, nformats, nclips);
 }
 
+// candidate list and clip range shared by both search entry points
+static fp4_status search_candidates(const int32_t* formats_em, int32_t nformats, int32_t nclips, float clip_lo,
+                                    float clip_hi, SearchCandidates* c) {
+    if (!formats_em) return fail(FP4_ERR_INVALID_ARG, "null pointer");
+    if (nformats < 1 || nformats > 8 || nclips < 2 || (int64_t)nformats * nclips > 512)
+        return fail(FP4_ERR_UNSUPPORTED, "need 1..8 formats, >= 2 clips, at most 512 candidates");
+    if (!(clip_lo > 0.0f) || !(clip_hi >= clip_lo) || !(clip_hi <= 1.0f))
+        return fail(FP4_ERR_INVALID_ARG, "need 0 < clip_lo <= clip_hi <= 1");
+    *c = SearchCandidates{};
+    c->nformats = nformats;
+    c->nclips = nclips;
+    for (int f = 0; f < nformats; f++) {
+        int e = formats_em[2 * f], m = formats_em[2 * f + 1];
+        if (e < 1 || m < 0 || e + m != 3) return fail(FP4_ERR_UNSUPPORTED, "format %d: need e >= 1 and e + m == 3", f);
+        c->fmt_e[f] = e;
+        c->fmt_m[f] = m;
+        c->fmt_qmax[f] = (float)minifloat_value(m, 7);
+    }
+    return FP4_OK;
+}
+
+static fp4_status search_workspace_check(int64_t units, int64_t numel, const SearchCandidates& c, void* workspace,
+                                         size_t ws_bytes) {
+    size_t need = search_workspace_bytes(units, numel, c.nformats, c.nclips);
+    if (!workspace || ws_bytes < need)
+        return fail(FP4_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+    if (!aligned16(workspace)) return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+    return FP4_OK;
+}
+
 fp4_status fp4_search_format(const float* w, int64_t ntensors, int64_t numel, const int32_t* formats_em,
                              int32_t nformats, int32_t nclips, float clip_lo, float clip_hi,
                              fp4_search_result* results, uint8_t* packed, void* workspace, size_t ws_bytes,
@@ -259,29 +289,41 @@ fp4_status fp4_search_format(const float* w, int64_t ntensors, int64_t numel, co
     if (!w || !formats_em || !results || !packed) return fail(FP4_ERR_INVALID_ARG, "null pointer");
     if (ntensors < 0 || numel <= 0 || numel % 16 != 0)
         return fail(FP4_ERR_INVALID_ARG, "numel must be a positive multiple of 16");
-    if (nformats < 1 || nformats > 8 || nclips < 2 || (int64_t)nformats * nclips > 512)
-        return fail(FP4_ERR_UNSUPPORTED, "need 1..8 formats, >= 2 clips, at most 512 candidates");
-    if (!(clip_lo > 0.0f) || !(clip_hi >= clip_lo) || !(clip_hi <= 1.0f))
-        return fail(FP4_ERR_INVALID_ARG, "need 0 < clip_lo <= clip_hi <= 1");
-    SearchCandidates c{};
-    c.nformats = nformats;
-    c.nclips = nclips;
-    for (int f = 0; f < nformats; f++) {
-        int e = formats_em[2 * f], m = formats_em[2 * f + 1];
-        if (e < 1 || m < 0 || e + m != 3) return fail(FP4_ERR_UNSUPPORTED, "format %d: need e >= 1 and e + m == 3", f);
-        c.fmt_e[f] = e;
-        c.fmt_m[f] = m;
-        c.fmt_qmax[f] = (float)minifloat_value(m, 7);
-    }
+    SearchCandidates c;
+    fp4_status st = search_candidates(formats_em, nformats, nclips, clip_lo, clip_hi, &c);
+    if (st) return st;
     if (!aligned16(w) || !aligned16(packed) || !aligned16(results))
         return fail(FP4_ERR_ALIGNMENT, "w, packed and results must be 16-byte aligned");
-    size_t need = search_workspace_bytes(ntensors, numel, nformats, nclips);
-    if (!workspace || ws_bytes < need)
-        return fail(FP4_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
-    if (!aligned16(workspace)) return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
-    return hip_status(launch_search(w, ntensors, numel, c, (double)clip_lo, (double)clip_hi, results, packed, workspace,
+    if ((st = search_workspace_check(ntensors, numel, c, workspace, ws_bytes))) return st;
+    SearchInput in{w, 0, 1, numel, ntensors, numel, 1};
+    return hip_status(launch_search(in, c, (double)clip_lo, (double)clip_hi, results, packed, numel / 2, workspace,
                                     (hipStream_t)stream),
                       "fp4_search_format");
+}
+
+fp4_status fp4_search_activations(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                  int32_t unit, int64_t first_rows, const int32_t* formats_em, int32_t nformats,
+                                  int32_t nclips, float clip_lo, float clip_hi, fp4_search_result* results,
+                                  uint8_t* packed, int64_t ldp, void* workspace, size_t ws_bytes, void* stream) {
+    if (!x || !formats_em || !results || !packed) return fail(FP4_ERR_INVALID_ARG, "null pointer");
+    if (x_dtype != FP4_F32 && x_dtype != FP4_BF16) return fail(FP4_ERR_INVALID_ARG, "x_dtype must be F32 or BF16");
+    if (rows < 0 || cols <= 0 || cols % 16 != 0) return fail(FP4_ERR_INVALID_ARG, "cols must be a positive multiple of 16");
+    if (ldx < cols || ldx % 4 != 0) return fail(FP4_ERR_ALIGNMENT, "ldx must be >= cols and a multiple of 4");
+    if (ldp < cols / 2 || ldp % 4 != 0) return fail(FP4_ERR_ALIGNMENT, "ldp must be >= cols/2 and a multiple of 4");
+    if (unit != FP4_SCALE_TENSOR && unit != FP4_SCALE_ROW) return fail(FP4_ERR_INVALID_ARG, "unit must be TENSOR or ROW");
+    SearchCandidates c;
+    fp4_status st = search_candidates(formats_em, nformats, nclips, clip_lo, clip_hi, &c);
+    if (st) return st;
+    if (!aligned16(x) || !aligned16(packed) || !aligned16(results))
+        return fail(FP4_ERR_ALIGNMENT, "x, packed and results must be 16-byte aligned");
+    const int64_t t = unit == FP4_SCALE_ROW ? 1 : (first_rows > 0 && first_rows < rows ? first_rows : rows);
+    if (rows == 0) return ok();
+    const int64_t units = unit == FP4_SCALE_ROW ? rows : 1;
+    if ((st = search_workspace_check(units, t * cols, c, workspace, ws_bytes))) return st;
+    SearchInput in{x, x_dtype == FP4_BF16, unit == FP4_SCALE_ROW, ldx, rows, cols, t};
+    return hip_status(launch_search(in, c, (double)clip_lo, (double)clip_hi, results, packed, ldp, workspace,
+                                    (hipStream_t)stream),
+                      "fp4_search_activations");
 }
 
 fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {

@@ -96,8 +96,17 @@ struct SearchCandidates {
 };
 size_t search_workspace_bytes(int64_t ntensors, int64_t numel, int32_t nformats,
                               int32_t nclips);
-hipError_t launch_search(const float* w, int64_t ntensors, int64_t numel,
-                         const SearchCandidates& c, double clip_lo, double clip_hi,
-                         void* results, uint8_t* packed, void* ws, hipStream_t s);
+// search input: a row-major [rows, cols] matrix; units are its rows (per_row_units) or
+// its first unit_rows rows as one unit (then every row is packed with that winner)
+struct SearchInput {
+    const void* x;
+    int32_t bf16;
+    int32_t per_row_units;
+    int64_t ld;  // elements
+    int64_t rows, cols;
+    int64_t unit_rows;
+};
+hipError_t launch_search(const SearchInput& in, const SearchCandidates& c, double clip_lo, double clip_hi,
+                         void* results, uint8_t* packed, int64_t ldp, void* ws, hipStream_t s);
 
 }  // namespace fp4

@@ -231,6 +231,31 @@ fp4_status fp4_search_format(const float* w, int64_t ntensors, int64_t numel,
                              uint8_t* packed, void* workspace, size_t ws_bytes,
                              void* stream);
 
+/* The same search on activations ([FP4-LLM] search-based FP quantization applied to
+ * activations as to weights; [Overview] static quantization from calibration data and
+ * per-token granularity):
+ *   x          device, x_dtype FP4_F32 or FP4_BF16 (bf16 values are searched exactly as
+ *              their binary32 values), [rows, cols], leading dim ldx elements (>= cols,
+ *              a multiple of 4); cols a multiple of 16
+ *   unit       FP4_SCALE_TENSOR: rows [0, T) form one search unit, T = first_rows (all
+ *              rows if first_rows <= 0 or >= rows): the calibration tokens choose one
+ *              format and clip for the activation tensor, and EVERY row (those past T
+ *              included) is packed with it -- static activation quantization;
+ *              FP4_SCALE_ROW: every row (token) is its own unit, searched and packed with
+ *              its own winner -- per-token formats and scales.
+ *   formats_em, nformats, nclips, clip_lo, clip_hi: as fp4_search_format; each unit's
+ *              candidates, error, winner and record are defined as there, with the unit's
+ *              values in place of a tensor's.
+ *   results    device fp4_search_result [1] (TENSOR) or [rows] (ROW)
+ *   packed     device u8 [rows, cols/2], leading dim ldp bytes (>= cols/2, a multiple of 4)
+ *   workspace  at least fp4_search_workspace_size(1, T * cols, ...) (TENSOR) or
+ *              fp4_search_workspace_size(rows, cols, ...) (ROW) bytes                 */
+fp4_status fp4_search_activations(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                  int32_t unit, int64_t first_rows, const int32_t* formats_em,
+                                  int32_t nformats, int32_t nclips, float clip_lo, float clip_hi,
+                                  fp4_search_result* results, uint8_t* packed, int64_t ldp,
+                                  void* workspace, size_t ws_bytes, void* stream);
+
 /* Quantized GEMM Y = X * W^T with scales factored out of the low-bit inner product
  * ([FP4-LLM] efficient matrix multiplication; [W8A8] section 2.2 quantized_matmul):
  *   W4A16 (a_kind F32/BF16):  Y[m,n] = sum_u s[n,u] * sum_{k in u} x[m,k] * g(c[n,k])

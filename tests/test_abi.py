@@ -23,7 +23,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = L.load()
     names = _declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES)
@@ -118,6 +118,36 @@ def test_search_validation():
     assert s(FAKE, 2, 1024, fm, 3, 100, 0.0, 1.0, FAKE, FAKE, FAKE, need, N) == L.FP4_ERR_INVALID_ARG
     bad = (ctypes.c_int32 * 2)(2, 2)
     assert s(FAKE, 2, 1024, bad, 1, 100, 0.5, 1.0, FAKE, FAKE, FAKE, need, N) == L.FP4_ERR_UNSUPPORTED
+
+
+def test_search_activations_validation():
+    lib = L.load()
+    f = lib.fp4_search_activations
+    N = ctypes.c_void_p(0)
+    fm = (ctypes.c_int32 * 6)(1, 2, 2, 1, 3, 0)
+    need = lib.fp4_search_workspace_size(64, 1024, 3, 100)
+    ok = dict(x=FAKE, dt=L.FP4_BF16, rows=64, cols=1024, ldx=1024, unit=L.FP4_SCALE_ROW, first=0, fm=fm, nf=3,
+              nc=100, lo=0.5, hi=1.0, res=FAKE, packed=FAKE, ldp=512, ws=FAKE, wsb=need)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["dt"], a["rows"], a["cols"], a["ldx"], a["unit"], a["first"], a["fm"], a["nf"], a["nc"],
+                 a["lo"], a["hi"], a["res"], a["packed"], a["ldp"], a["ws"], a["wsb"], N)
+
+    assert call(x=N) == L.FP4_ERR_INVALID_ARG
+    assert call(dt=L.FP4_F16) == L.FP4_ERR_INVALID_ARG
+    assert call(cols=1000, ldx=1000, ldp=512) == L.FP4_ERR_INVALID_ARG     # cols % 16
+    assert call(ldx=1026) == L.FP4_ERR_ALIGNMENT
+    assert call(ldp=514) == L.FP4_ERR_ALIGNMENT
+    assert call(ldp=256) == L.FP4_ERR_ALIGNMENT                            # ldp < cols/2
+    assert call(unit=L.FP4_SCALE_GROUP) == L.FP4_ERR_INVALID_ARG
+    assert call(nc=1) == L.FP4_ERR_UNSUPPORTED
+    assert call(x=ODD) == L.FP4_ERR_ALIGNMENT
+    assert call(wsb=need - 1) == L.FP4_ERR_WORKSPACE
+    # TENSOR over the first 16 rows needs the workspace of one unit of 16 x 1024 values
+    need_t = lib.fp4_search_workspace_size(1, 16 * 1024, 3, 100)
+    assert call(unit=L.FP4_SCALE_TENSOR, first=16, wsb=need_t - 1) == L.FP4_ERR_WORKSPACE
+    assert call(rows=0) == L.FP4_OK  # empty: nothing launched
 
 
 def test_gemm_validation():

@@ -498,6 +498,67 @@ def test_search_full_size_one_tensor():
     assert np.array_equal(host(packed)[0], p)
 
 
+def _check_records(gres, orecs):
+    for g, rec in zip(F.search_results_host(gres), orecs):
+        assert (g.e, g.m, g.clip_index) == (rec.e, rec.m, rec.clip_index), (g, rec)
+        assert np.float32(g.clip) == rec.clip and np.float32(g.scale) == rec.scale
+        assert g.mse == rec.mse and g.mse_runner_up == rec.mse_runner_up
+        assert abs(g.bias - rec.bias) <= 1e-14 * abs(rec.bias)
+
+
+@pytest.mark.parametrize("rows,cols,bf16,pad", [
+    (37, 1040, True, 8),     # 1040 per row: 8 values per lane, a ragged last pass
+    (20, 5120, True, 0),     # 24 values per lane
+    (9, 4096, False, 4),     # f32 rows, 16 values per lane
+    (3, 40000, False, 0),    # several passes per row
+])
+def test_search_activations_per_token(rows, cols, bf16, pad):
+    """Per-token search on activations with outlier channels: every record and every
+    packed row bit-exact; packed bytes past cols/2 untouched."""
+    say("search act row", rows, cols, bf16, pad)
+    x = synth.activations(7, rows, rows, cols, outlier_frac=0.01, bf16=bf16)
+    xbuf = torch.zeros((rows, cols + pad), dtype=torch.bfloat16 if bf16 else torch.float32, device=DEV)
+    xbuf[:, :cols] = dev(x, xbuf.dtype)
+    pbuf = torch.full((rows, cols // 2 + 16), 0xAB, dtype=torch.uint8, device=DEV)
+    res, _ = F.fp4_search_activations(xbuf[:, :cols], "row", packed=pbuf[:, :cols // 2])
+    recs, packed = O.search_activations(x, "row")
+    _check_records(res, recs)
+    gp = host(pbuf)
+    assert np.array_equal(gp[:, :cols // 2], packed)
+    assert bool((gp[:, cols // 2:] == 0xAB).all())
+
+
+@pytest.mark.parametrize("rows,first,cols,bf16", [(300, 128, 2048, True), (50, 0, 1040, False), (7, 64, 4096, True)])
+def test_search_activations_calibration(rows, first, cols, bf16):
+    """One search over the calibration tokens (the first rows), every row packed with the
+    winner: the record and all packed rows bit-exact."""
+    say("search act tensor", rows, first, cols, bf16)
+    x = synth.activations(8, rows, rows, cols, outlier_frac=0.01, bf16=bf16)
+    xt = dev(x, torch.bfloat16 if bf16 else torch.float32)
+    res, gp = F.fp4_search_activations(xt, "tensor", first_rows=first)
+    recs, packed = O.search_activations(x, "tensor", first_rows=first)
+    _check_records(res, recs)
+    assert np.array_equal(host(gp), packed)
+
+
+def test_search_activations_full_4096x5120_sampled():
+    """Per-token search at the LLaMA-13B prefill activation shape (4096 tokens x 5120
+    bf16): 12 sampled rows' records and codes bit-exact."""
+    rows, cols = 4096, 5120
+    say("search act full", rows, cols)
+    x = synth.activations(9, rows, rows, cols, outlier_frac=0.01, bf16=True)
+    res, gp = F.fp4_search_activations(dev(x, torch.bfloat16), "row")
+    pick = np.sort(np.random.default_rng(5).choice(rows, 12, replace=False))
+    recs, packed = O.search_activations(x[pick], "row")
+    allrec = F.search_results_host(res)
+    for k, r in enumerate(pick):
+        g, rec = allrec[r], recs[k]
+        assert (g.e, g.m, g.clip_index, g.mse, g.mse_runner_up) == (rec.e, rec.m, rec.clip_index, rec.mse,
+                                                                     rec.mse_runner_up)
+        assert np.float32(g.scale) == rec.scale
+    assert np.array_equal(host(gp)[pick], packed)
+
+
 # ---------------------------------------------------------------- determinism -----
 def test_repeat_runs_identical():
     x = synth.activations(3, 1, 256, 1024, outlier_frac=0.01)
