@@ -145,9 +145,10 @@ TRAFFIC_KERNELS = [
     ("gemv_m4", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 1>", (3, 6)),
     ("gemv_m16", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 3>", (0, 3)),
     ("quantize_act", "quant.hip", "quantize_chunk_kernel<true, true, 2>", (0, 3)),
-    ("w4a4_c3", "gemm_w4a4.hip", "w4a4_fp4_kernel<128, 128>", (0, 3)),
-    ("w4a4_qkv", "gemm_w4a4.hip", "w4a4_fp4_kernel<256, 256>", (0, 3)),
-    ("nf4_qkv", "gemm_lut.hip", "w4a4_lut_kernel", (0, 3)),
+    ("w4a4_c3", "gemm_w4a4.hip", "w4a4_fp4_kernel<128, 128, false>", (0, 3)),
+    ("w4a4_qkv", "gemm_w4a4.hip", "w4a4_fp4_kernel<256, 256, false>", (0, 3)),
+    ("nf4_qkv", "gemm_lut.hip", "w4a4_lut_kernel<256, 256, false>", (0, 3)),
+    ("swiglu", "gemm_w4a4.hip", "w4a4_fp4_kernel<256, 256, true>", (0, 3)),
 ]
 COPY_BYTES = 256 * 1024 * 1024  # the reference device copy of profile_run
 
@@ -397,7 +398,7 @@ def bench_swiglu(torch, F):
     fl = 2 * T * 2 * n * k
     sep = t_g + t_u + t_q
     out = [roofline_entry(f"w4a4 gate+up GEMM with SwiGLU + E2M1 quantize epilogue {T}x(2x{n})x{k}", "mfma",
-                          fl / t_f / 1e12, FP4_PEAK_TFLOPS, "TFLOP/s", t_f, fl, "flop",
+                          fl / t_f / 1e12, FP4_PEAK_TFLOPS, "TFLOP/s", t_f, fl, "flop", traffic_for("gemm_w4a4.hip", "swiglu"),
                           separate_us=round(sep * 1e6, 2), separate_gemm_us=round((t_g + t_u) * 1e6, 2),
                           separate_quantize_us=round(t_q * 1e6, 2), speedup_vs_separate=round(sep / t_f, 3))]
     del X1, X2, ap, wgp, wup, h, yg, yu
