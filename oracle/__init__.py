@@ -311,6 +311,94 @@ def dequantize(packed, grid: Grid, mode: str, scales, group: int = 0, col_shift=
 
 
 # ----------------------------------------------------------------------------------
+# Two-mode grid ([HiFloat4] section 2.1: each value group uses either the small-value
+# layout sign|2 exponent|1 mantissa (E2M1) or the large-value layout sign|1 exponent|
+# 2 mantissa (E1M2), marked by one control bit whose cost is shared by the group)
+# ----------------------------------------------------------------------------------
+TWO_MODES = (E2M1, E1M2)  # mode 0, mode 1
+
+
+def two_mode_error(x, codes, s, grid: Grid) -> float:
+    """Squared quantization error of one group under one mode, as an exact comparison
+    key: the sum over the group of (|x| - fl32(g(code) * s))^2, each difference and
+    square exact in binary64 (|x| and the dequantized value are binary32 values within
+    a factor of 4 of each other or the latter is 0), summed without rounding
+    (math.fsum returns the correctly rounded exact sum)."""
+    q = (grid.array[codes & 7].astype(np.float32) * np.float32(s)).astype(np.float32)
+    d = np.abs(f32(x)).astype(np.float64) - q.astype(np.float64)
+    return math.fsum((d * d).tolist())
+
+
+def quantize_two_mode(x, group: int, scale_dtype: str = "f32"):
+    """Per group of `group` consecutive elements of each row: for each mode m (E2M1,
+    E1M2) the scale s_m = fl32(amax / Qmax_m) (stored rounding: binary16 for f16
+    scales), r_m = fl32(1/s_m), codes = quantize(x, r_m, grid m), and the squared error
+    against fl32(g * s_m).  The mode with the smaller exact error wins (equal errors:
+    E2M1); its codes are stored and its scale with the sign bit set for E1M2 (the control
+    bit, in the otherwise unused sign of the non-negative scale).  Returns (packed,
+    scales [R, C/group], modes [R, C/group])."""
+    x = f32(x)
+    R, C = x.shape
+    G = C // group
+    amax = amax_row_groups(x, group)
+    codes_m, scales_m = [], []
+    for (e, m) in TWO_MODES:
+        g = minifloat(e, m)
+        sc = scale_from_amax(amax, g)
+        st = rne_f16(sc).astype(np.float32) if scale_dtype == "f16" else sc
+        codes_m.append(quantize(x, np.repeat(reciprocal(st), group, axis=1), g))
+        scales_m.append(st)
+    codes = np.empty((R, C), dtype=np.uint8)
+    scales = np.empty((R, G), dtype=np.float32)
+    modes = np.zeros((R, G), dtype=np.uint8)
+    grids = [minifloat(*f) for f in TWO_MODES]
+    for r in range(R):
+        for gi in range(G):
+            sl = slice(gi * group, (gi + 1) * group)
+            e0 = two_mode_error(x[r, sl], codes_m[0][r, sl], scales_m[0][r, gi], grids[0])
+            e1 = two_mode_error(x[r, sl], codes_m[1][r, sl], scales_m[1][r, gi], grids[1])
+            mode = 1 if e1 < e0 else 0
+            modes[r, gi] = mode
+            codes[r, sl] = codes_m[mode][r, sl]
+            scales[r, gi] = -scales_m[1][r, gi] if mode else scales_m[0][r, gi]
+    if scale_dtype == "f16":
+        scales = scales.astype(np.float16)
+    return pack(codes), scales, modes
+
+
+def two_mode_values(packed, scales, group: int) -> np.ndarray:
+    """Dequantized values of a two-mode tensor: v = +-fl32(g_mode(code) * |s|), the mode
+    from the sign bit of the group's stored scale."""
+    codes = unpack(packed)
+    R, C = codes.shape
+    s = np.asarray(scales).astype(np.float32).reshape(R, C // group)
+    mode = np.signbit(s)
+    mag = np.abs(s)
+    e2, e1 = minifloat(*TWO_MODES[0]), minifloat(*TWO_MODES[1])
+    g = np.where(np.repeat(mode, group, axis=1), e1.array[codes & 7], e2.array[codes & 7]).astype(np.float32)
+    v = (g * np.repeat(mag, group, axis=1)).astype(np.float32)
+    return np.where((codes >> 3) & 1, -v, v).astype(np.float32)
+
+
+def gemm_w4a16_two_mode(x, w_packed, w_scales, group: int):
+    """r[m, n] = sum_g |s[n, g]| * sum_{k in g} x[m, k] * g_mode(n,g)(c[n, k]) in binary64
+    (the W4A16 product with the grid chosen per group by the scale's sign bit)."""
+    X = f32(x).astype(np.float64)
+    codes = unpack(w_packed)
+    N, K = codes.shape
+    s = np.asarray(w_scales).astype(np.float32).reshape(N, K // group)
+    mode = np.repeat(np.signbit(s), group, axis=1)
+    e2, e1 = minifloat(*TWO_MODES[0]), minifloat(*TWO_MODES[1])
+    V = np.where(mode, e1.array[codes & 7], e2.array[codes & 7])
+    V = np.where((codes >> 3) & 1, -V, V)
+    mag = np.abs(s).astype(np.float64)
+    out = np.zeros((X.shape[0], N), dtype=np.float64)
+    for gi in range(K // group):
+        sl = slice(gi * group, (gi + 1) * group)
+        out += (X[:, sl] @ V[:, sl].T) * mag[None, :, gi]
+    return out
+
+# ----------------------------------------------------------------------------------
 # Pre-shifted exponent bias ([FP4-LLM], pre-shifted exponent bias paragraphs)
 # ----------------------------------------------------------------------------------
 K_MIN = -64

@@ -543,3 +543,54 @@ def test_search_activations_calibration_rows_decide_every_row():
     # taking the E1M2 row into the calibration set makes E3M0 at that scale inexact
     recs_all, _ = O.search_activations(x[:4], "tensor", nclips=4)
     assert recs_all[0].mse > 0.0
+
+
+# ---- two-mode grid: E2M1 or E1M2 per group, the mode in the scale's sign bit ----------
+def test_two_mode_planted_groups():
+    """A group of exact E1M2 multiples (every magnitude present) has zero error only in
+    E1M2; a group of exact E2M1 multiples only in E2M1; an all-zero group ties and keeps
+    E2M1 with scale +0.  Codes, scales and dequantized values follow exactly."""
+    rng = np.random.default_rng(31)
+    e1m2 = _planted_row(rng, (1, 2), 32, -4)
+    e2m1 = _planted_row(rng, (2, 1), 32, 2)
+    x = np.stack([np.concatenate([e1m2[0], e2m1[0], np.zeros(32, np.float32)])])
+    packed, scales, modes = O.quantize_two_mode(x, 32)
+    assert modes.tolist() == [[1, 0, 0]]
+    assert scales[0, 0] == np.float32(-(1.75 * 2.0 ** -4) / np.float32(1.75))
+    assert scales[0, 0] == np.float32(-(2.0 ** -4)) and scales[0, 1] == np.float32(4.0)
+    assert scales[0, 2] == 0.0 and not np.signbit(scales[0, 2])
+    codes = O.unpack(packed)[0]
+    assert np.array_equal(codes[:32] & 7, e1m2[1]) and np.array_equal(codes[32:64] & 7, e2m1[1])
+    assert np.array_equal(O.two_mode_values(packed, scales, 32), x)
+
+
+def test_two_mode_choice_by_hand():
+    """Group [1.0, 0.3]: E2M1 (s = 1/6) stores 0.3 as 2/6 (error about 1.1e-3), E1M2
+    (s = 1/1.75) as 0.5/1.75 (error about 2.0e-4): E1M2 wins.  Group [1.0, 0.38]: E2M1
+    gives 2/6 (error 2.2e-3), E1M2 0.75/1.75 (error 2.5e-3): E2M1 wins."""
+    x = np.array([[1.0, 0.3, 1.0, 0.38]], np.float32)
+    packed, scales, modes = O.quantize_two_mode(x, 2)
+    assert modes.tolist() == [[1, 0]]
+    v = O.two_mode_values(packed, scales, 2)[0]
+    assert abs(v[1] - 0.5 / 1.75) < 1e-7 and abs(v[3] - 2.0 / 6.0) < 1e-7
+    e2 = O.two_mode_error(x[0, :2], np.array([7, 4]), np.float32(1) / np.float32(6), O.minifloat(2, 1))
+    e1 = O.two_mode_error(x[0, :2], np.array([7, 2]), np.float32(1) / np.float32(1.75), O.minifloat(1, 2))
+    assert abs(e2 - (0.3 - 1 / 3) ** 2) < 1e-8 and abs(e1 - (0.3 - 0.5 / 1.75) ** 2) < 1e-8 and e1 < e2
+
+
+def test_two_mode_f16_scales_and_gemm_special_cases():
+    """f16 scales store the rounded scale with the mode in its sign; when every group takes
+    one mode the two-mode product equals the plain W4A16 product on that grid."""
+    rng = np.random.default_rng(32)
+    w = np.stack([_planted_row(rng, (2, 1), 64, -3)[0] for _ in range(3)])
+    packed, scales, modes = O.quantize_two_mode(w, 32, "f16")
+    assert scales.dtype == np.float16 and not modes.any()
+    x = rng.normal(size=(4, 64)).astype(np.float32)
+    r2 = O.gemm_w4a16_two_mode(x, packed, scales, 32)
+    r = O.gemm_w4a16(x, packed, O.minifloat(2, 1), "group", np.abs(scales.astype(np.float32)), 32)
+    assert np.array_equal(r2, r)
+    w1 = np.stack([_planted_row(rng, (1, 2), 64, -6)[0] for _ in range(3)])
+    p1, s1, m1 = O.quantize_two_mode(w1, 32, "f16")
+    assert m1.all() and np.all(np.signbit(s1))
+    r1 = O.gemm_w4a16_two_mode(x, p1, s1, 32)
+    assert np.array_equal(r1, O.gemm_w4a16(x, p1, O.minifloat(1, 2), "group", np.abs(s1.astype(np.float32)), 32))
