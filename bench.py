@@ -406,6 +406,34 @@ def bench_swiglu(torch, F):
     return out
 
 
+def bench_two_mode(torch, F):
+    """The decode workload with two-mode weights (E2M1 or E1M2 per 128-group, the mode in
+    the fp16 scale's sign): the weight quantize (both candidates and the exact error
+    comparison per group) and the W4A16 GEMV at M = 1, 4, 16.  Same bytes as the E2M1
+    decode step."""
+    tm = F.grid_two_mode()
+    g = F.gran("group", DEC_G, "f16")
+    NP = 16
+    W = gen_normal(torch, (DEC_N, DEC_K), 0.02, 100)
+    P = [torch.empty((DEC_N, DEC_K // 2), dtype=torch.uint8, device="cuda") for _ in range(NP)]
+    S = [torch.empty(DEC_N * (DEC_K // DEC_G), dtype=torch.float16, device="cuda") for _ in range(NP)]
+    for i in range(NP):
+        F.fp4_quantize_pack(W, tm, g, packed=P[i], scales=S[i])
+    qb, gb = decode_bytes()
+    t_q = graph_time(torch, lambda i: F.fp4_quantize_pack(W, tm, g, packed=P[i % NP], scales=S[i % NP]), 32)
+    out = [roofline_entry("quantize_pack f32->two-mode E2M1/E1M2 g128 (11008x4096)", "hbm", qb / t_q / 1e9,
+                          HBM_PEAK_GBS, "GB/s", t_q, qb, "bytes")]
+    for m in DEC_MS:
+        X = gen_activations(torch, m, DEC_K, 200 + m, outlier_frac=0.0)
+        Y = torch.empty((m, DEC_N), dtype=torch.bfloat16, device="cuda")
+        t = graph_time(torch, lambda i: F.fp4_gemm(X, P[i % NP], S[i % NP], tm, g, y=Y), 64)
+        out.append(roofline_entry(f"w4a16 gemv two-mode M={m} (11008x4096, g128)", "hbm", gb[m] / t / 1e9,
+                                  HBM_PEAK_GBS, "GB/s", t, gb[m], "bytes"))
+    del W, P, S
+    torch.cuda.empty_cache()
+    return out
+
+
 # VALU instructions per (element, candidate) in the search's inner loop, counted from the
 # gfx950 assembly of search_eval_kernel: E1M2 14.8, E2M1 12.3, E3M0 17.8 per element, plus
 # 2.4 per element for the per-candidate wavefront reduction; averaged over the formats
@@ -514,6 +542,8 @@ def main():
         kernels += bench_preshift_w4a4(torch, F)
         log("LLaMA-13B prefill layer ...")
         kernels += bench_prefill(torch, F)
+        log("two-mode grid ...")
+        kernels += bench_two_mode(torch, F)
         log("fused SwiGLU + quantize ...")
         kernels += bench_swiglu(torch, F)
         log("format search ...")

@@ -18,7 +18,7 @@ from ._lib import (FP4Error, FP4_BF16, FP4_F16, FP4_F32, FP4_PACKED, FP4_REDUCE_
                    FP4_REDUCE_ROW_GROUP, FP4_REDUCE_TENSOR, FP4_SCALE_GROUP, FP4_SCALE_ROW,
                    FP4_SCALE_TENSOR)
 
-__all__ = ["FP4Error", "grid_minifloat", "grid_lut", "grid_nf4", "nf4_values", "gran", "fp4_calibrate", "fp4_quantize_pack",
+__all__ = ["FP4Error", "grid_minifloat", "grid_lut", "grid_nf4", "grid_two_mode", "nf4_values", "gran", "fp4_calibrate", "fp4_quantize_pack",
            "fp4_dequantize", "fp4_preshift_weights", "fp4_search_format", "fp4_gemm",
            "fp4_gemm_swiglu_quant", "fp4_search_activations", "search_results_host", "E2M1", "E1M2", "E3M0"]
 
@@ -56,6 +56,13 @@ def nf4_values() -> list:
 
 def grid_nf4() -> L.fp4_grid:
     return grid_lut(nf4_values())
+
+
+def grid_two_mode() -> L.fp4_grid:
+    """E2M1 or E1M2 per scale group, the mode in the sign bit of the group's scale."""
+    g = L.fp4_grid()
+    g.kind, g.e, g.m, g.reserved = L.FP4_GRID_TWO_MODE, 0, 0, 0
+    return g
 
 
 def gran(mode: str = "tensor", group: int = 0, scale_dtype: str = "f32") -> L.fp4_gran:

@@ -14,7 +14,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "fp4.h")
 
 FP4_OK, FP4_ERR_INVALID_ARG, FP4_ERR_UNSUPPORTED, FP4_ERR_ALIGNMENT, FP4_ERR_WORKSPACE, FP4_ERR_HIP = range(6)
 FP4_F32, FP4_BF16, FP4_F16, FP4_PACKED = 0, 1, 2, 3
-FP4_GRID_MINIFLOAT, FP4_GRID_LUT16 = 0, 1
+FP4_GRID_MINIFLOAT, FP4_GRID_LUT16, FP4_GRID_TWO_MODE = 0, 1, 2
 FP4_SCALE_TENSOR, FP4_SCALE_ROW, FP4_SCALE_GROUP = 0, 1, 2
 FP4_REDUCE_TENSOR, FP4_REDUCE_COLUMN, FP4_REDUCE_ROW_GROUP = 0, 1, 2
 

@@ -78,6 +78,20 @@ fp4_status make_grid(const fp4_grid& g, QGrid* q) {
         if (!(q->qmax > 0)) return fail(FP4_ERR_INVALID_ARG, "lut has no nonzero value");
         return FP4_OK;
     }
+    if (g.kind == FP4_GRID_TWO_MODE) {
+        // E2M1 (mode 0) magnitudes and midpoints in [0, 8) / [0, 7), E1M2 (mode 1) in [8, 16) / [7, 14)
+        q->kind = 2;
+        for (int c = 0; c < 8; c++) {
+            q->val[c] = (float)minifloat_value(1, c);
+            q->val[8 + c] = (float)minifloat_value(2, c);
+        }
+        for (int i = 0; i < 7; i++) {
+            q->thr[i] = (float)((minifloat_value(1, i) + minifloat_value(1, i + 1)) / 2);
+            q->thr[7 + i] = (float)((minifloat_value(2, i) + minifloat_value(2, i + 1)) / 2);
+        }
+        q->qmax = q->val[7];
+        return FP4_OK;
+    }
     return fail(FP4_ERR_INVALID_ARG, "unknown grid kind %d", g.kind);
 }
 
@@ -152,6 +166,8 @@ fp4_status fp4_quantize_pack(const void* x, int32_t x_dtype, int64_t rows, int64
     fp4_status st = make_grid(grid, &q);
     if (st) return st;
     if ((st = check_gran(gran, cols))) return st;
+    if (q.kind == 2 && (gran.mode != FP4_SCALE_GROUP || col_shift))
+        return fail(FP4_ERR_UNSUPPORTED, "the two-mode grid needs GROUP scales and no column shifts");
     if (tensor_scale && gran.mode != FP4_SCALE_TENSOR) return fail(FP4_ERR_INVALID_ARG, "tensor_scale needs TENSOR mode");
     if (tensor_scale && scales_out && (const void*)tensor_scale == scales_out)
         return fail(FP4_ERR_INVALID_ARG, "tensor_scale and scales_out must not alias");
@@ -206,6 +222,7 @@ fp4_status fp4_dequantize(const uint8_t* packed, int64_t rows, int64_t cols, int
     fp4_status st = make_grid(grid, &q);
     if (st) return st;
     if ((st = check_gran(gran, cols))) return st;
+    if (q.kind == 2 && gran.mode != FP4_SCALE_GROUP) return fail(FP4_ERR_UNSUPPORTED, "the two-mode grid needs GROUP scales");
     return hip_status(launch_dequantize(packed, rows, cols, ldp, q, gran.mode, gran.group, scales,
                                         gran.scale_dtype == FP4_F16, col_shift, out, ldo, (hipStream_t)stream),
                       "fp4_dequantize");
@@ -223,6 +240,7 @@ fp4_status fp4_preshift_weights(const float* w, int64_t n, int64_t k, int64_t ld
     if ((st = make_grid(w_grid, &qw))) return st;
     if ((st = check_gran(w_gran, k))) return st;
     if (w_gran.mode == FP4_SCALE_TENSOR) return fail(FP4_ERR_UNSUPPORTED, "pre-shifted weights need ROW or GROUP scales");
+    if (qa.kind == 2 || qw.kind == 2) return fail(FP4_ERR_UNSUPPORTED, "pre-shift with the two-mode grid is not implemented");
     if (!aligned16(w) || !aligned16(w_packed) || !aligned16(shift_out))
         return fail(FP4_ERR_ALIGNMENT, "w, w_packed and shift_out must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
@@ -358,10 +376,16 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
     if (!aligned16(d->a) || !aligned16(d->w) || (d->ldw % 16) != 0)
         return fail(FP4_ERR_ALIGNMENT, "a and w must be 16-byte aligned and ldw a multiple of 16");
 
+    if (p.wg.kind == 2 && (d->w_gran.mode != FP4_SCALE_GROUP || d->a_kind == FP4_PACKED))
+        return fail(FP4_ERR_UNSUPPORTED, "two-mode weights need GROUP scales and f32/bf16 activations");
     if (d->a_kind == FP4_F32 || d->a_kind == FP4_BF16) {
         if (d->lda < d->K) return fail(FP4_ERR_INVALID_ARG, "lda < K");
         bool mfma = d->a_kind == FP4_BF16 && p.wg.is_e2m1 && d->K % 128 == 0 && (d->lda * 2) % 16 == 0 &&
                     (d->w_gran.mode != FP4_SCALE_GROUP || d->w_gran.group % 128 == 0);
+        // two-mode weights: the small-batch matrix-core kernel (group 128), else the VALU kernel
+        if (p.wg.kind == 2 && d->a_kind == FP4_BF16 && d->K % 128 == 0 && (d->lda * 2) % 16 == 0 &&
+            d->w_gran.group == 128 && d->M <= 16)
+            return hip_status(launch_w4a16_two_mode(p, s), "fp4_gemm/w4a16_two_mode");
         if (mfma) return hip_status(launch_w4a16_mfma(p, s), "fp4_gemm/w4a16");
         return hip_status(launch_w4a16_valu(p, s), "fp4_gemm/w4a16_valu");
     }

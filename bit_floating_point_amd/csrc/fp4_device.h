@@ -136,6 +136,29 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Double-double sums (binary64 pairs, TwoSum error terms): about 100 bits, enough to
+// decide comparisons of sums of exact binary64 terms except near-exact ties.  dd_add is
+// commutative bit for bit (the TwoSum error term is exact whatever the operand order),
+// so a butterfly leaves the same sum in every lane.
+struct DD { double hi, lo; };
+
+__device__ __forceinline__ DD dd_add_d(DD a, double b) {
+    double s = a.hi + b;
+    double bb = s - a.hi;
+    double e = (a.hi - (s - bb)) + (b - bb);
+    return DD{s, a.lo + e};
+}
+
+__device__ __forceinline__ DD dd_add(DD a, DD b) {
+    double s = a.hi + b.hi;
+    double bb = s - a.hi;
+    double e = (a.hi - (s - bb)) + (b.hi - bb);
+    double lo = e + (a.lo + b.lo);
+    double h = s + lo;
+    double l = lo - (h - s);
+    return DD{h, l};
+}
+
 // Decoded value of a 4-bit code (sign applied, no scale).
 __device__ __forceinline__ float grid_value(uint32_t c, const QGrid& g) {
     if (g.kind == 0) {

@@ -13,6 +13,8 @@ namespace fp4 {
 //   kind 0 (minifloat, sign-magnitude): val[0..7] magnitudes, thr[0..6] midpoints,
 //          applied to |y|; the sign bit of y becomes bit 3.
 //   kind 1 (LUT16, signed):             val[0..15], thr[0..14], applied to y.
+//   kind 2 (two-mode, per group):       E2M1 val[0..7] / thr[0..6] (mode 0) and E1M2
+//          val[8..15] / thr[7..13] (mode 1); the mode is the sign bit of the group scale.
 struct QGrid {
     int32_t kind;
     int32_t e, m;
@@ -76,6 +78,7 @@ struct GemmParams {
 };
 hipError_t launch_w4a16_mfma(const GemmParams& p, hipStream_t s);
 hipError_t launch_w4a16_valu(const GemmParams& p, hipStream_t s);
+hipError_t launch_w4a16_two_mode(const GemmParams& p, hipStream_t s);  // M <= 16, bf16, group 128
 hipError_t launch_w4a4_fp4(const GemmParams& p, hipStream_t s);
 hipError_t launch_w4a4_lut(const GemmParams& p, hipStream_t s);
 // W4A4 gate/up products with SwiGLU and the next layer's activation quantization in

@@ -49,6 +49,22 @@ __device__ __forceinline__ bf16x8 decode_e2m1_bf16(uint32_t w) {
     return __builtin_bit_cast(bf16x8, o);
 }
 
+// 8 E1M2 codes -> 8 bf16 values, exact: the nibble (sign, magnitude d) becomes the E4M3
+// byte sign<<7 | d -- the subnormal d * 2^-9 -- and the convert's scale 2^7 makes it d/4.
+__device__ __forceinline__ bf16x8 decode_e1m2_bf16(uint32_t w) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 0,2,4,6 / 1,3,5,7
+    const uint32_t blo = (lo & 0x07070707u) | ((lo & 0x08080808u) << 4);
+    const uint32_t bhi = (hi & 0x07070707u) | ((hi & 0x08080808u) << 4);
+    const uint32_t d0 = __builtin_amdgcn_perm(bhi, blo, 0x05010400u);  // codes 0..3 in byte order
+    const uint32_t d1 = __builtin_amdgcn_perm(bhi, blo, 0x07030602u);  // codes 4..7
+    uint32_t o[4];
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 128.0f, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 128.0f, true));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 128.0f, false));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 128.0f, true));
+    return __builtin_bit_cast(bf16x8, o);
+}
+
 // Scale loads return raw bits; the conversion waits until the value is used, so a
 // batch's loads are all in flight together.
 template <bool SF16>
@@ -219,7 +235,9 @@ static void launch_w16(const GemmParams& p, hipStream_t s) {
 constexpr int kSmallWaves = kSmallWavesPerGroup;
 constexpr int kSmallChunks = 4;  // K chunks per wavefront per batch
 
-template <int MODE, bool SF16, bool SV, int T>  // MODE 0 tensor, 1 row, 2 group of 128
+// TWO: two-mode weights (group 128): a group is E1M2 when the sign bit of its scale is
+// set, E2M1 otherwise, and is scaled by the scale's magnitude.
+template <int MODE, bool SF16, bool SV, int T, bool TWO = false>  // MODE 0 tensor, 1 row, 2 group of 128
 __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParams p) {
     constexpr int NW = kSmallWaves, CH = kSmallChunks;
     extern __shared__ uint4 xs[];  // per wavefront: [M][its K range / 8] bf16 vectors
@@ -323,12 +341,19 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
             for (int t = 0; t < T; t++) {
                 const uint32_t wd[4] = {wv[b][t].x, wv[b][t].y, wv[b][t].z, wv[b][t].w};
                 f32x4 acc = MODE == 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : total[t];
+                constexpr uint32_t kSign = SF16 ? 0x8000u : 0x80000000u;
+                const bool e1m2 = TWO && (sc[b][t] & kSign) != 0;
 #pragma unroll
-                for (int j = 0; j < 4; j++)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[j]),
-                                                                  decode_e2m1_bf16(wd[j]), acc, 0, 0, 0);
+                for (int j = 0; j < 4; j++) {
+                    bf16x8 wf = decode_e2m1_bf16(wd[j]);
+                    if (TWO) {
+                        const bf16x8 w1 = decode_e1m2_bf16(wd[j]);
+                        wf = e1m2 ? w1 : wf;
+                    }
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[j]), wf, acc, 0, 0, 0);
+                }
                 if (MODE == 2) {
-                    const float s = valid ? scale_value<SF16>(sc[b][t]) : 0.0f;
+                    const float s = valid ? scale_value<SF16>(TWO ? (sc[b][t] & ~kSign) : sc[b][t]) : 0.0f;
 #pragma unroll
                     for (int i = 0; i < 4; i++) total[t][i] = __builtin_fmaf(acc[i], s, total[t][i]);
                 } else {
@@ -372,10 +397,10 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
     }
 }
 
-template <int MODE, bool SF16, bool SV, int T>
+template <int MODE, bool SF16, bool SV, int T, bool TWO = false>
 static hipError_t launch_small_t(const GemmParams& p, hipStream_t s) {
     const size_t lds = small_lds_bytes(p.M, p.K);
-    auto kern = w4a16_small_kernel<MODE, SF16, SV, T>;
+    auto kern = w4a16_small_kernel<MODE, SF16, SV, T, TWO>;
     // the dynamic-LDS limit is a kernel attribute, set once per device
     static bool attr_set[64];
     int dev = 0;
@@ -390,36 +415,43 @@ static hipError_t launch_small_t(const GemmParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int MODE, bool SF16, bool SV>
+template <int MODE, bool SF16, bool SV, bool TWO = false>
 static hipError_t launch_small_sv(const GemmParams& p, hipStream_t s) {
     // M <= 4: one 16-column tile per wavefront (more workgroups, X is small);
     // larger M: three tiles share each staged X
-    return p.M <= 4 ? launch_small_t<MODE, SF16, SV, 1>(p, s) : launch_small_t<MODE, SF16, SV, 3>(p, s);
+    return p.M <= 4 ? launch_small_t<MODE, SF16, SV, 1, TWO>(p, s) : launch_small_t<MODE, SF16, SV, 3, TWO>(p, s);
 }
 
-template <bool SF16>
+template <bool SF16, bool TWO = false>
 static hipError_t launch_small(const GemmParams& p, hipStream_t s) {
     if (p.w_mode == 2) {
         const int64_t nchunks = p.K / 128;
         // one vector load per batch needs 4-byte aligned scale rows and batch starts
         const bool sv = SF16 ? (nchunks % (2 * kSmallWaves) == 0 && (reinterpret_cast<uintptr_t>(p.w_scales) & 3) == 0)
                              : (reinterpret_cast<uintptr_t>(p.w_scales) & 3) == 0;
-        return sv ? launch_small_sv<2, SF16, true>(p, s) : launch_small_sv<2, SF16, false>(p, s);
+        return sv ? launch_small_sv<2, SF16, true, TWO>(p, s) : launch_small_sv<2, SF16, false, TWO>(p, s);
     }
     if (p.w_mode == 1) return launch_small_sv<1, SF16, false>(p, s);
     return launch_small_sv<0, SF16, false>(p, s);
 }
 
-hipError_t launch_w4a16_mfma(const GemmParams& p, hipStream_t s) {
-    if (p.M == 0 || p.N == 0) return hipSuccess;
+static bool small_fits(const GemmParams& p) {
     const int64_t ngroups = p.w_mode == 2 ? p.K / 128 : 1;
     const int64_t sbytes = p.w_scale_f16 ? 2 : 4;
-    const bool small = p.M <= 16 && (p.w_mode != 2 || p.w_group == 128) &&
-                       small_lds_bytes(p.M, p.K) <= kSmallMaxLds &&
-                       // 32-bit buffer offsets
-                       p.N * p.ldw < kOOB && p.N * ngroups * sbytes < kOOB &&
-                       ((p.M - 1) * p.lda + p.K) * 2 < (int64_t)kOOB;
-    if (small) return p.w_scale_f16 ? launch_small<true>(p, s) : launch_small<false>(p, s);
+    return p.M <= 16 && (p.w_mode != 2 || p.w_group == 128) && small_lds_bytes(p.M, p.K) <= kSmallMaxLds &&
+           // 32-bit buffer offsets
+           p.N * p.ldw < kOOB && p.N * ngroups * sbytes < kOOB && ((p.M - 1) * p.lda + p.K) * 2 < (int64_t)kOOB;
+}
+
+hipError_t launch_w4a16_two_mode(const GemmParams& p, hipStream_t s) {
+    if (p.M == 0 || p.N == 0) return hipSuccess;
+    if (!small_fits(p)) return launch_w4a16_valu(p, s);
+    return p.w_scale_f16 ? launch_small<true, true>(p, s) : launch_small<false, true>(p, s);
+}
+
+hipError_t launch_w4a16_mfma(const GemmParams& p, hipStream_t s) {
+    if (p.M == 0 || p.N == 0) return hipSuccess;
+    if (small_fits(p)) return p.w_scale_f16 ? launch_small<true>(p, s) : launch_small<false>(p, s);
     // larger M: reuse each activation fragment for two weight tiles
     if (p.M > 8) {
         if (p.w_scale_f16) launch_w16<2, true>(p, s);
@@ -444,16 +476,26 @@ __global__ void __launch_bounds__(256) w4a16_valu_kernel(GemmParams p) {
     int64_t unit = p.w_mode == 2 ? p.w_group : p.K;
     float total = 0.0f;
     for (int64_t k0 = 0; k0 < p.K; k0 += unit) {
+        int64_t u = p.w_mode == 0 ? 0 : (p.w_mode == 1 ? n : n * (p.K / p.w_group) + k0 / p.w_group);
+        float s = p.w_scale_f16 ? __half2float(reinterpret_cast<const __half*>(p.w_scales)[u])
+                                : reinterpret_cast<const float*>(p.w_scales)[u];
+        // two-mode grid: the scale's sign bit picks E1M2 (val[8..15]) over E2M1 (val[0..7])
+        const int vbase = (p.wg.kind == 2 && signbit(s)) ? 8 : 0;
+        if (p.wg.kind == 2) s = fabsf(s);
         float part = 0.0f;
         for (int64_t k = k0; k < k0 + unit; k++) {
             uint32_t c = (wr[k >> 1] >> (4 * (k & 1))) & 15u;
             float xv = p.a_kind == 1 ? bf16_bits_to_float(reinterpret_cast<const uint16_t*>(p.a)[m * p.lda + k])
                                      : reinterpret_cast<const float*>(p.a)[m * p.lda + k];
-            part = __builtin_fmaf(xv, grid_value(c, p.wg), part);
+            float g;
+            if (p.wg.kind == 2) {
+                g = p.wg.val[vbase + (c & 7)];
+                if (c & 8) g = -g;
+            } else {
+                g = grid_value(c, p.wg);
+            }
+            part = __builtin_fmaf(xv, g, part);
         }
-        int64_t u = p.w_mode == 0 ? 0 : (p.w_mode == 1 ? n : n * (p.K / p.w_group) + k0 / p.w_group);
-        float s = p.w_scale_f16 ? __half2float(reinterpret_cast<const __half*>(p.w_scales)[u])
-                                : reinterpret_cast<const float*>(p.w_scales)[u];
         total = __builtin_fmaf(part, s, total);
     }
     if (p.y_bf16) reinterpret_cast<__bf16*>(p.y)[m * p.ldy + n] = (__bf16)total;

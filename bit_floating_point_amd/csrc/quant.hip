@@ -247,6 +247,83 @@ __global__ void __launch_bounds__(kThreads) quantize_chunk_kernel(QuantParams p,
     }
 }
 
+// GROUP mode with the two-mode grid ([HiFloat4] section 2.1: per group the E2M1 or the
+// E1M2 layout, one control bit).  Per group both candidates are formed -- s_m =
+// fl32(amax / Qmax_m) (binary16-rounded for f16 scales), codes of y = fl32(x * fl32(1/s_m))
+// (E2M1 by the FP4 convert, E1M2 as min(rint(4|y|), 7)) -- and the squared errors
+// sum (|x| - fl32(g * s_m))^2 compared: every difference and square is exact in
+// binary64, the difference E2M1 - E1M2 is summed in double-double over each lane's 8
+// values and then over the group's lanes (a butterfly that leaves the same sum in every
+// lane).  E1M2 wins when that sum is positive; its scale is stored negated (the mode bit
+// is the scale's sign bit).
+template <bool VEC, bool BF16, int U>
+__global__ void __launch_bounds__(kThreads) quantize_two_mode_kernel(QuantParams p, int64_t chunks, int64_t nunits) {
+    Raw8 raw[U];
+    int64_t row[U], col[U];
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+        int64_t u = (int64_t)blockIdx.x * U + i;
+        if (u >= nunits) u = nunits - 1;  // a duplicate of the last unit writes the same bytes
+        row[i] = u / chunks;
+        col[i] = (u % chunks) * kChunk + threadIdx.x * 8;
+        raw[i] = load_raw8<VEC, BF16>(reinterpret_cast<const char*>(p.x) + row[i] * p.ldx * (BF16 ? 2 : 4), col[i],
+                                      p.cols);
+    }
+    const int lanes = p.group >> 3;
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+        float v[8];
+        raw8_to_float<BF16>(raw[i], v);
+        const int64_t unit = row[i] * (p.cols / p.group) + col[i] / p.group;
+        float amax;
+        if (p.amax_in) amax = (col[i] < p.cols) ? p.amax_in[unit] : 0.0f;
+        else amax = group_max(max_abs8(v), lanes);
+        float s0 = amax / p.g.val[7], s1 = amax / p.g.val[15];
+        if (p.scale_f16) {
+            s0 = round_f16(s0);
+            s1 = round_f16(s1);
+        }
+        const float r0 = recip_or_zero(s0), r1 = recip_or_zero(s1);
+        float y0[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) y0[k] = v[k] * r0;
+        uint32_t w0 = 0;  // E2M1 codes by the FP4 convert (nearest, ties to even, +-6)
+        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y0[0], y0[1], 1.0f, 0);
+        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y0[2], y0[3], 1.0f, 1);
+        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y0[4], y0[5], 1.0f, 2);
+        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y0[6], y0[7], 1.0f, 3);
+        // their magnitudes back from the codes
+        float g0[8];
+        {
+            const auto a0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w0, 1.0f, 0);
+            const auto a1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w0, 1.0f, 1);
+            const auto a2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w0, 1.0f, 2);
+            const auto a3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w0, 1.0f, 3);
+            g0[0] = a0[0]; g0[1] = a0[1]; g0[2] = a1[0]; g0[3] = a1[1];
+            g0[4] = a2[0]; g0[5] = a2[1]; g0[6] = a3[0]; g0[7] = a3[1];
+        }
+        uint32_t w1 = 0;
+        DD acc{0.0, 0.0};
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const float y1 = v[k] * r1;
+            const float d1c = fminf(rintf(fabsf(y1) * 4.0f), 7.0f);
+            w1 |= ((__float_as_uint(y1) >> 31) << 3 | (uint32_t)d1c) << (4 * k);
+            const float q0 = fabsf(g0[k]) * s0, q1 = (d1c * 0.25f) * s1;
+            const double a = (double)fabsf(v[k]);
+            const double e0 = (a - (double)q0) * (a - (double)q0), e1 = (a - (double)q1) * (a - (double)q1);
+            acc = dd_add_d(acc, e0);
+            acc = dd_add_d(acc, -e1);
+        }
+        for (int o = 1; o < lanes; o <<= 1) acc = dd_add(acc, DD{__shfl_xor(acc.hi, o, 64), __shfl_xor(acc.lo, o, 64)});
+        const bool e1m2 = acc.hi > 0.0 || (acc.hi == 0.0 && acc.lo > 0.0);
+        if (col[i] < p.cols) {
+            store_codes(p.packed + row[i] * p.ldp, col[i], p.cols, e1m2 ? w1 : w0, VEC);
+            if ((threadIdx.x & (lanes - 1)) == 0) store_scale(p, unit, e1m2 ? -s1 : s0);
+        }
+    }
+}
+
 // GROUP mode with 128-element groups, the E2M1 grid, no column shifts, rows a multiple
 // of 8 elements: the same arithmetic as quantize_chunk_kernel, specialised (group
 // maximum by DPP instead of lane shuffles through LDS, no per-element grid dispatch).
@@ -427,7 +504,9 @@ static void quantize_launch(const QuantParams& p, hipStream_t s) {
         int64_t chunks = (p.cols + kChunk - 1) / kChunk;
         int64_t nunits = p.rows * chunks;
         dim3 grid((unsigned)((nunits + U - 1) / U));
-        if (VEC && p.mode == 2 && p.group == 128 && p.g.is_e2m1 && !p.col_shift && !p.amax_in &&
+        if (p.g.kind == 2)
+            hipLaunchKernelGGL((quantize_two_mode_kernel<VEC, BF16, U>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
+        else if (VEC && p.mode == 2 && p.group == 128 && p.g.is_e2m1 && !p.col_shift && !p.amax_in &&
             p.rows * ((p.cols + QT * 8 - 1) / (QT * 8)) < (1LL << 30) && p.cols < (1LL << 30)) {
             const int64_t qchunks = (p.cols + QT * 8 - 1) / (QT * 8), qunits = p.rows * qchunks;
             hipLaunchKernelGGL((quantize_e2m1_g128_kernel<BF16, 1, QT>), dim3((unsigned)qunits), dim3(QT), 0, s, p,
@@ -472,7 +551,13 @@ __global__ void __launch_bounds__(kThreads) dequantize_kernel(const uint8_t* pac
         int64_t unit = mode == 0 ? 0 : (mode == 1 ? row : row * (cols / group) + c / group);
         float sc = scale_f16 ? __half2float(reinterpret_cast<const __half*>(scales)[unit])
                              : reinterpret_cast<const float*>(scales)[unit];
-        float v = grid_value(code, g) * sc;
+        float v;
+        if (g.kind == 2) {  // two-mode: the scale's sign bit picks E1M2 (val[8..15]) over E2M1
+            const float m = g.val[(signbit(sc) ? 8 : 0) + (code & 7)] * fabsf(sc);
+            v = (code & 8) ? -m : m;
+        } else {
+            v = grid_value(code, g) * sc;
+        }
         if (col_shift) v = ldexpf(v, (int)col_shift[c]);
         out[row * ldo + c] = v;
     }

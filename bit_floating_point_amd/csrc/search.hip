@@ -37,25 +37,6 @@ constexpr int kSPerMax = 32;                   // values per lane, at most
 constexpr int kSChunk = kSThreads * kSPerMax;  // 8192 values per pass, at most
 constexpr int kMaxCand = 512;   // formats x clips per call (LDS holds one double-double per wavefront each)
 
-struct DD { double hi, lo; };
-
-__device__ __forceinline__ DD dd_add_d(DD a, double b) {
-    double s = a.hi + b;
-    double bb = s - a.hi;
-    double e = (a.hi - (s - bb)) + (b - bb);
-    return DD{s, a.lo + e};
-}
-
-__device__ __forceinline__ DD dd_add(DD a, DD b) {
-    double s = a.hi + b.hi;
-    double bb = s - a.hi;
-    double e = (a.hi - (s - bb)) + (b.hi - bb);
-    double lo = e + (a.lo + b.lo);
-    double h = s + lo;
-    double l = lo - (h - s);
-    return DD{h, l};
-}
-
 // Workgroups per unit: up to 4 passes of 8192 values each (at most 64 workgroups); when
 // the units give fewer than 768 workgroups (3 per CU), more of them, down to 2048 values
 // (8 per lane) each.

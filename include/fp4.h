@@ -72,11 +72,23 @@ typedef int32_t fp4_status;
  *   E3M0 = {0, 1, 2, 4, ..., 64}.  A real-valued bias b is the same grid times
  *   2^(1-b) ([FP4-LLM] eq. (4)), i.e. it lives entirely in the scale.
  * FP4_GRID_LUT16: 16 sorted signed values in lut[] (e.g. NF4, [Overview] NF4), each
- *   exactly representable in binary16.                                              */
+ *   exactly representable in binary16.
+ * FP4_GRID_TWO_MODE: per scale group either E2M1 (mode 0) or E1M2 (mode 1)
+ *   ([HiFloat4] section 2.1: a small-value and a large-value bit layout, marked by one
+ *   control bit shared by a batch of values).  Only with GROUP granularity.  The
+ *   quantizer computes both candidates for each group -- s_m = fl32(amax / Qmax_m)
+ *   (Qmax 6 and 1.75; rounded to binary16 for f16 scales), the codes of
+ *   y = fl32(x * fl32(1/s_m)) -- and keeps the one whose squared error
+ *   sum (|x| - fl32(g(code) * s_m))^2 is smaller (equal: E2M1).  The mode is the sign
+ *   bit of the stored group scale (scales are otherwise non-negative): a negative
+ *   stored scale -s means E1M2 with scale s.  The comparison uses a double-double sum
+ *   of exact binary64 terms: it equals the exact comparison unless the two errors agree
+ *   to about 2^-100 relative without being equal.  e, m and lut[] are ignored.        */
 #define FP4_GRID_MINIFLOAT 0
 #define FP4_GRID_LUT16     1
+#define FP4_GRID_TWO_MODE  2
 typedef struct {
-    int32_t kind;     /* FP4_GRID_MINIFLOAT or FP4_GRID_LUT16               */
+    int32_t kind;     /* FP4_GRID_MINIFLOAT, FP4_GRID_LUT16 or FP4_GRID_TWO_MODE */
     int32_t e;        /* minifloat exponent bits (1, 2 or 3)                 */
     int32_t m;        /* minifloat mantissa bits (e + m == 3)                */
     int32_t reserved; /* must be 0                                           */
@@ -273,6 +285,8 @@ fp4_status fp4_search_activations(const void* x, int32_t x_dtype, int64_t rows, 
  *       norm) of the exact value; groups whose scale is below 2^-14 of their row's
  *       largest lose relative precision to f16 subnormals.
  *   y_dtype FP4_BF16 rounds the f32 result to nearest-even.
+ *   Two-mode weights (FP4_GRID_TWO_MODE, GROUP scales) take the W4A16 path only: each
+ *   group's codes are read on its own grid (the sign of its scale) and scaled by |s|.
  * Strides: K a multiple of 32 for the matrix-core paths; packed rows 16-byte aligned. */
 fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream);
 

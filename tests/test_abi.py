@@ -210,6 +210,30 @@ def test_swiglu_validation():
     assert lib.fp4_gemm_swiglu_quant(ctypes.byref(d), N) == L.FP4_OK  # empty: nothing launched
 
 
+def test_two_mode_validation():
+    lib = L.load()
+    N = ctypes.c_void_p(0)
+    tm = _grid(2)
+    q = lib.fp4_quantize_pack
+    assert q(FAKE, 0, 4, 256, 256, tm, _gran(1), N, N, N, FAKE, 128, FAKE, N) == L.FP4_ERR_UNSUPPORTED  # ROW
+    assert q(FAKE, 0, 4, 256, 256, tm, _gran(2, 32), N, N, FAKE, FAKE, 128, FAKE, N) == L.FP4_ERR_UNSUPPORTED  # shifts
+    assert lib.fp4_dequantize(FAKE, 4, 256, 128, tm, _gran(0), FAKE, N, FAKE, 256, N) == L.FP4_ERR_UNSUPPORTED
+    f = lib.fp4_preshift_weights
+    assert f(FAKE, 8, 256, 256, FAKE, _grid(), tm, _gran(2, 32), FAKE, FAKE, FAKE, 128, FAKE, N) == L.FP4_ERR_UNSUPPORTED
+    d = L.fp4_gemm_desc()
+    d.M, d.N, d.K = 16, 32, 256
+    d.a_kind = L.FP4_PACKED
+    d.a, d.lda, d.w, d.ldw, d.w_scales, d.y, d.ldy = 0x10000, 128, 0x20000, 128, 0x30000, 0x40000, 32
+    d.a_scale = 0x50000
+    d.a_grid, d.w_grid = _grid(), tm
+    d.w_gran = _gran(2, 128)
+    d.y_dtype = L.FP4_BF16
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # W4A4 with two-mode weights
+    d.a_kind, d.lda = L.FP4_BF16, 256
+    d.w_gran = _gran(1)
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # two-mode needs GROUP scales
+
+
 def test_preshift_validation():
     lib = L.load()
     N = ctypes.c_void_p(0)

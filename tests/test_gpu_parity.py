@@ -559,6 +559,72 @@ def test_search_activations_full_4096x5120_sampled():
     assert np.array_equal(host(gp)[pick], packed)
 
 
+# ---------------------------------------------------------------- two-mode grid ---
+def _f16_or_f32_bits(a):
+    a = np.asarray(a)
+    return a.view(np.uint16) if a.dtype == np.float16 else a.astype(np.float32).view(np.uint32)
+
+
+@pytest.mark.parametrize("rows,cols,group,sd,bf16", [
+    (37, 1040, 8, "f32", False),     # one lane per group, a ragged chunk
+    (64, 4096, 32, "f16", True),
+    (30, 6144, 128, "f16", False),   # the W4A16 group size
+    (9, 2048, 512, "f32", True),     # a whole wavefront per group
+])
+def test_two_mode_quantize_dequantize(rows, cols, group, sd, bf16):
+    """Two-mode quantize: every code, scale and mode (the scale's sign) bit-exact; the
+    dequantized values bit-exact; both modes occur."""
+    say("two-mode", rows, cols, group, sd, bf16)
+    x = synth.weight(11, rows, rows, cols) if not bf16 else synth.activations(11, rows, rows, cols, outlier_frac=0.01,
+                                                                             bf16=True)
+    xt = dev(x, torch.bfloat16 if bf16 else torch.float32)
+    g = F.gran("group", group, sd)
+    packed, scales = F.fp4_quantize_pack(xt, F.grid_two_mode(), g)
+    op, osc, modes = O.quantize_two_mode(x, group, sd)
+    assert np.array_equal(host(packed), op)
+    gs = host(scales).reshape(osc.shape)
+    assert np.array_equal(_f16_or_f32_bits(gs), _f16_or_f32_bits(osc))
+    assert 0 < modes.mean() < 1
+    deq = host(F.fp4_dequantize(packed, F.grid_two_mode(), g, scales))
+    assert np.array_equal(deq.view(np.uint32), O.two_mode_values(op, osc, group).view(np.uint32))
+
+
+_TWO_MODE_W = {}
+
+
+def _two_mode_weight(N, K, sd):
+    """The oracle's two-mode quantization of a synthetic weight, shared by the cases."""
+    if (N, K, sd) not in _TWO_MODE_W:
+        _TWO_MODE_W[(N, K, sd)] = O.quantize_two_mode(synth.weight(12, N, N, K), 128, sd)
+    return _TWO_MODE_W[(N, K, sd)]
+
+
+@pytest.mark.parametrize("M,N,K,sd,adt", [
+    (1, 11008, 4096, "f16", "bf16"),   # decode GEMV shape: the small matrix-core kernel
+    (4, 11008, 4096, "f16", "bf16"),
+    (16, 11008, 4096, "f32", "bf16"),
+    (40, 1000, 1024, "f16", "bf16"),   # larger M: the VALU kernel
+    (3, 520, 512, "f32", "f32"),       # f32 activations: the VALU kernel
+])
+def test_two_mode_w4a16_gemm(M, N, K, sd, adt):
+    """W4A16 with two-mode weights: within the GEMM tolerance of the binary64 oracle,
+    bf16 output the nearest-even rounding of the fp32 output."""
+    say("two-mode gemm", M, N, K, sd, adt)
+    op, osc, modes = _two_mode_weight(N, K, sd)
+    gp = torch.from_numpy(op).to(DEV)
+    gs = torch.from_numpy(np.ascontiguousarray(osc)).to(DEV)
+    x = synth.activations(12, M, M, K, outlier_frac=0.01, bf16=adt == "bf16")
+    xt = dev(x, torch.bfloat16 if adt == "bf16" else torch.float32)
+    g = F.gran("group", 128, sd)
+    y32 = host(F.fp4_gemm(xt, gp, gs, F.grid_two_mode(), g, y_dtype=torch.float32))
+    r = O.gemm_w4a16_two_mode(x, op, osc, 128)
+    err = O.rel_err(y32, r)
+    say("  rel err", err, "modes", modes.mean())
+    assert err <= TOL
+    yb = F.fp4_gemm(xt, gp, gs, F.grid_two_mode(), g, y_dtype=torch.bfloat16)
+    assert np.array_equal(host(yb.view(torch.int16)).view(np.uint16), O.rne_bf16_bits(y32))
+
+
 # ---------------------------------------------------------------- determinism -----
 def test_repeat_runs_identical():
     x = synth.activations(3, 1, 256, 1024, outlier_frac=0.01)
