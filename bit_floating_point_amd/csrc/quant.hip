@@ -251,10 +251,12 @@ __global__ void __launch_bounds__(kThreads) quantize_chunk_kernel(QuantParams p,
 // E1M2 layout, one control bit).  Per group both candidates are formed -- s_m =
 // fl32(amax / Qmax_m) (binary16-rounded for f16 scales), codes of y = fl32(x * fl32(1/s_m))
 // (E2M1 by the FP4 convert, E1M2 as min(rint(4|y|), 7)) -- and the squared errors
-// sum (|x| - fl32(g * s_m))^2 compared: every difference and square is exact in
-// binary64, the difference E2M1 - E1M2 is summed in double-double over each lane's 8
-// values and then over the group's lanes (a butterfly that leaves the same sum in every
-// lane).  E1M2 wins when that sum is positive; its scale is stored negated (the mode bit
+// sum (|x| - fl32(g * s_m))^2 compared: every difference is exact in binary32 and its
+// square exact in binary64, the per-element difference of the two squares is rounded
+// once to binary64, summed in binary64 over each lane's 8 values and in double-double
+// over the group's lanes (a butterfly that leaves the same sum in every lane).  The sign
+// of the sum is the exact comparison's unless the two errors agree to about 2^-49 of
+// their size.  E1M2 wins when the sum is positive; its scale is stored negated (the mode bit
 // is the scale's sign bit).
 template <bool VEC, bool BF16, int U>
 __global__ void __launch_bounds__(kThreads) quantize_two_mode_kernel(QuantParams p, int64_t chunks, int64_t nunits) {
@@ -303,18 +305,20 @@ __global__ void __launch_bounds__(kThreads) quantize_two_mode_kernel(QuantParams
             g0[4] = a2[0]; g0[5] = a2[1]; g0[6] = a3[0]; g0[7] = a3[1];
         }
         uint32_t w1 = 0;
-        DD acc{0.0, 0.0};
+        double diff = 0.0;
 #pragma unroll
         for (int k = 0; k < 8; k++) {
             const float y1 = v[k] * r1;
             const float d1c = fminf(rintf(fabsf(y1) * 4.0f), 7.0f);
             w1 |= ((__float_as_uint(y1) >> 31) << 3 | (uint32_t)d1c) << (4 * k);
-            const float q0 = fabsf(g0[k]) * s0, q1 = (d1c * 0.25f) * s1;
-            const double a = (double)fabsf(v[k]);
-            const double e0 = (a - (double)q0) * (a - (double)q0), e1 = (a - (double)q1) * (a - (double)q1);
-            acc = dd_add_d(acc, e0);
-            acc = dd_add_d(acc, -e1);
+            // |x| and q = fl32(g * s) are within a factor of 2 of each other (q is the
+            // nearest grid value, |x| <= Qmax s) or q = 0, so |x| - q is exact in binary32
+            // (Sterbenz) and its square exact in binary64; their difference is rounded once
+            const float a = fabsf(v[k]);
+            const float d0 = a - fabsf(g0[k]) * s0, d1 = a - (d1c * 0.25f) * s1;
+            diff += (double)d0 * (double)d0 - (double)d1 * (double)d1;
         }
+        DD acc{diff, 0.0};
         for (int o = 1; o < lanes; o <<= 1) acc = dd_add(acc, DD{__shfl_xor(acc.hi, o, 64), __shfl_xor(acc.lo, o, 64)});
         const bool e1m2 = acc.hi > 0.0 || (acc.hi == 0.0 && acc.lo > 0.0);
         if (col[i] < p.cols) {

@@ -81,9 +81,10 @@ typedef int32_t fp4_status;
  *   y = fl32(x * fl32(1/s_m)) -- and keeps the one whose squared error
  *   sum (|x| - fl32(g(code) * s_m))^2 is smaller (equal: E2M1).  The mode is the sign
  *   bit of the stored group scale (scales are otherwise non-negative): a negative
- *   stored scale -s means E1M2 with scale s.  The comparison uses a double-double sum
- *   of exact binary64 terms: it equals the exact comparison unless the two errors agree
- *   to about 2^-100 relative without being equal.  e, m and lut[] are ignored.        */
+ *   stored scale -s means E1M2 with scale s.  The comparison sums the per-element
+ *   differences of the exact squares in binary64 and double-double: it equals the exact
+ *   comparison unless the two errors agree to about 2^-49 of their size without being
+ *   equal.  e, m and lut[] are ignored.                                               */
 #define FP4_GRID_MINIFLOAT 0
 #define FP4_GRID_LUT16     1
 #define FP4_GRID_TWO_MODE  2
