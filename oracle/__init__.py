@@ -111,12 +111,18 @@ def nf4_table() -> np.ndarray:
 
 @dataclass(frozen=True)
 class Grid:
-    """kind 'minifloat': sign-magnitude code sign<<3 | (p<<m | d), values = magnitudes.
+    """kind 'minifloat': sign-magnitude code sign<<(e+m) | (p<<m | d), values = the
+    magnitudes by magnitude code (4-bit: e + m == 3; 8-bit FP8: e + m == 7).
     kind 'lut': code = index into 16 sorted signed values."""
     kind: str
     e: int = 0
     m: int = 0
     values: tuple = ()
+
+    @property
+    def bits(self) -> int:
+        """Bits per code: 4, or 8 for the FP8 grids (one code per byte)."""
+        return 8 if self.kind == "minifloat" and self.e + self.m == 7 else 4
 
     @property
     def array(self) -> np.ndarray:
@@ -131,13 +137,28 @@ class Grid:
         """Grid value of each code (float64), without any scale."""
         c = codes.astype(np.int64)
         if self.kind == "minifloat":
-            mag = self.array[c & 7]
-            return np.where((c >> 3) & 1, -mag, mag)
+            nb = self.e + self.m
+            mag = self.array[c & ((1 << nb) - 1)]
+            return np.where((c >> nb) & 1, -mag, mag)
         return self.array[c & 15]
 
 
 def minifloat(e: int, m: int) -> Grid:
     return Grid("minifloat", e, m, tuple(minifloat_grid(e, m, 1)))
+
+
+def fp8(e: int, m: int) -> Grid:
+    """The OCP 8-bit formats (FP8 for key layers, [FP4-LLM] mixed precision): E4M3 with
+    bias 7 whose all-ones code S.1111.111 is NaN (127 magnitudes, largest 448), and E5M2
+    with bias 15 whose top exponent holds inf/NaN (124 magnitudes, largest 57344).  The
+    magnitude of code p<<m | d follows the same FP value formula as the 4-bit grids."""
+    if (e, m) == (4, 3):
+        g = minifloat_grid(4, 3, 7)[:127]
+    elif (e, m) == (5, 2):
+        g = minifloat_grid(5, 2, 15)[:124]
+    else:
+        raise ValueError((e, m))
+    return Grid("minifloat", e, m, tuple(g))
 
 
 def lut(values) -> Grid:
@@ -207,9 +228,18 @@ def quantize(x, r, grid: Grid) -> np.ndarray:
     assert np.all(np.isfinite(x)), "non-finite inputs are not valid"
     out = np.empty(x.shape, dtype=np.uint8)
     g = np.ascontiguousarray(grid.array)
-    _c().orc_quantize(_ptr(x), _ptr(r), x.size, 0 if grid.kind == "minifloat" else 1,
-                      _ptr(g), g.size, _ptr(out))
+    kind = (2 if grid.bits == 8 else 0) if grid.kind == "minifloat" else 1
+    _c().orc_quantize(_ptr(x), _ptr(r), x.size, kind, _ptr(g), g.size, _ptr(out))
     return out
+
+
+def pack_codes(codes: np.ndarray, grid: Grid) -> np.ndarray:
+    """Storage of codes: two 4-bit codes per byte, or one 8-bit code per byte."""
+    return np.asarray(codes, dtype=np.uint8).copy() if grid.bits == 8 else pack(codes)
+
+
+def unpack_codes(packed: np.ndarray, grid: Grid) -> np.ndarray:
+    return np.asarray(packed, dtype=np.uint8).copy() if grid.bits == 8 else unpack(packed)
 
 
 def pack(codes: np.ndarray) -> np.ndarray:
@@ -290,12 +320,12 @@ def quantize_pack(x, grid: Grid, mode: str, group: int = 0, scale_dtype: str = "
     codes = quantize(x, r, grid)
     if scale_dtype == "f16":
         scales = scales.astype(np.float16)
-    return pack(codes), scales
+    return pack_codes(codes, grid), scales
 
 
 def dequantize(packed, grid: Grid, mode: str, scales, group: int = 0, col_shift=None):
     """v = +-fl32(g(code) * s), times 2^k[j] for a shifted column (exact)."""
-    codes = unpack(packed)
+    codes = unpack_codes(packed, grid)
     R, C = codes.shape
     s = f32(np.asarray(scales).astype(np.float32))
     if mode == "tensor":
@@ -545,7 +575,7 @@ def search_activations(x, unit: str, first_rows: int = 0, formats=FORMATS_4BIT, 
 # matrix multiplication"; [W8A8] section 2.2 quantized_matmul).  Y = X W^T, W [N, K].
 # ----------------------------------------------------------------------------------
 def _weight_values(packed, grid: Grid) -> np.ndarray:
-    return grid.decode(unpack(packed))
+    return grid.decode(unpack_codes(packed, grid))
 
 
 def gemm_w4a16(x, w_packed, w_grid: Grid, mode: str, w_scales, group: int = 0):

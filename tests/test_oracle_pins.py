@@ -594,3 +594,46 @@ def test_two_mode_f16_scales_and_gemm_special_cases():
     assert m1.all() and np.all(np.signbit(s1))
     r1 = O.gemm_w4a16_two_mode(x, p1, s1, 32)
     assert np.array_equal(r1, O.gemm_w4a16(x, p1, O.minifloat(1, 2), "group", np.abs(s1.astype(np.float32)), 32))
+
+
+# ---- FP8 grids (OCP E4M3 / E5M2) ---------------------------------------------------
+def test_fp8_grids_match_the_ocp_definition():
+    """Facts of the OCP 8-bit formats: E4M3 has 127 magnitudes from the subnormal 2^-9 to
+    448 (min normal 2^-6); E5M2 124 from 2^-16 to 57344 (min normal 2^-14)."""
+    g4, g5 = O.fp8(4, 3), O.fp8(5, 2)
+    a4, a5 = g4.array, g5.array
+    assert len(a4) == 127 and a4[0] == 0 and a4[1] == 2.0 ** -9 and a4[8] == 2.0 ** -6 and a4[-1] == 448.0
+    assert len(a5) == 124 and a5[1] == 2.0 ** -16 and a5[4] == 2.0 ** -14 and a5[-1] == 57344.0
+    assert np.all(np.diff(a4) > 0) and np.all(np.diff(a5) > 0)
+    assert g4.bits == 8 and O.minifloat(2, 1).bits == 4
+
+
+@pytest.mark.parametrize("fmt,vals,codes", [
+    ((4, 3), [1.0, 0.1, 1.0625, 1.1875, 500.0, -0.0, -3.0, 2.0 ** -10, 3 * 2.0 ** -10],
+     [0x38, 0x1D, 0x38, 0x3A, 0x7E, 0x80, 0xC4, 0x00, 0x02]),
+    ((5, 2), [1.0, 1.125, 60000.0, -2.0 ** -17, 3 * 2.0 ** -17, 0.75],
+     [0x3C, 0x3C, 0x7B, 0x80, 0x02, 0x3A]),
+])
+def test_fp8_codes_by_hand(fmt, vals, codes):
+    """Nearest value with exact ties to the even code (1.0625 and 1.1875 in E4M3, 1.125
+    in E5M2, the subnormal midpoints), saturation at the largest finite value, sign of -0."""
+    g = O.fp8(*fmt)
+    got = O.quantize(np.array(vals, np.float32), np.ones(len(vals), np.float32), g)
+    assert [int(c) for c in got] == codes
+
+
+def test_fp8_round_trip_and_product():
+    """Grid values times a power-of-two scale quantize to themselves (dequantize is exact),
+    and the W8A16 product of such a weight is the dense product."""
+    rng = np.random.default_rng(41)
+    for fmt in ((4, 3), (5, 2)):
+        g = O.fp8(*fmt)
+        idx = rng.integers(0, len(g.values), (6, 64))
+        idx[:, ::32] = len(g.values) - 1  # every group's largest magnitude is the grid's
+        w = (g.array[idx] * np.where(rng.random((6, 64)) < 0.5, -1, 1) * 2.0 ** -10).astype(np.float32)
+        packed, sc = O.quantize_pack(w, g, "group", group=32)
+        assert packed.shape == (6, 64) and np.array_equal(sc, np.full((6, 2), 2.0 ** -10, np.float32))
+        assert np.array_equal(O.dequantize(packed, g, "group", sc, group=32), w)
+        x = rng.normal(size=(3, 64)).astype(np.float32)
+        r = O.gemm_w4a16(x, packed, g, "group", sc, group=32)
+        assert np.allclose(r, x.astype(np.float64) @ w.astype(np.float64).T, rtol=0, atol=1e-12)
