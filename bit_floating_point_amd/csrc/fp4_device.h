@@ -136,6 +136,38 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// OCP FP8 code of y (nearest value, ties to the even code, saturating at the largest
+// finite value, sign of y in bit 7): E4M3 (E = 4: bias 7, largest code 0x7E = 448) or
+// E5M2 (E = 5: bias 15, largest 0x7B = 57344).  Below the smallest normal the code is
+// rint(|y| / 2^(1 - bias - m)) (2^m is the smallest normal's code); above it the binary32
+// significand is rounded to m bits (nearest-even, carries into the exponent) and its
+// exponent re-biased.
+template <int E>
+__device__ __forceinline__ uint32_t fp8_code(float y) {
+    constexpr int M = 7 - E, BIAS = E == 4 ? 7 : 15;
+    constexpr uint32_t MAXC = E == 4 ? 0x7Eu : 0x7Bu;
+    constexpr float QMAX = E == 4 ? 448.0f : 57344.0f;
+    const float a = fminf(fabsf(y), QMAX);
+    uint32_t c;
+    if (a < __builtin_ldexpf(1.0f, 1 - BIAS)) {
+        c = (uint32_t)rintf(a * __builtin_ldexpf(1.0f, BIAS - 1 + M));
+    } else {
+        uint32_t u = __float_as_uint(a);
+        u += (1u << (22 - M)) - 1u + ((u >> (23 - M)) & 1u);
+        c = (u >> (23 - M)) - ((uint32_t)(127 - BIAS) << M);
+    }
+    return ((__float_as_uint(y) >> 31) << 7) | (c < MAXC ? c : MAXC);
+}
+
+// Value of an OCP FP8 code (sign applied), exact.
+template <int E>
+__device__ __forceinline__ float fp8_value(uint32_t c) {
+    constexpr int M = 7 - E, BIAS = E == 4 ? 7 : 15;
+    const int ex = (int)((c >> M) & ((1u << E) - 1u)), mant = (int)(c & ((1u << M) - 1u));
+    const float v = ex == 0 ? ldexpf((float)mant, 1 - BIAS - M) : ldexpf((float)((1 << M) + mant), ex - BIAS - M);
+    return (c & 0x80u) ? -v : v;
+}
+
 // Double-double sums (binary64 pairs, TwoSum error terms): about 100 bits, enough to
 // decide comparisons of sums of exact binary64 terms except near-exact ties.  dd_add is
 // commutative bit for bit (the TwoSum error term is exact whatever the operand order),

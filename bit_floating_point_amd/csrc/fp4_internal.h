@@ -15,6 +15,8 @@ namespace fp4 {
 //   kind 1 (LUT16, signed):             val[0..15], thr[0..14], applied to y.
 //   kind 2 (two-mode, per group):       E2M1 val[0..7] / thr[0..6] (mode 0) and E1M2
 //          val[8..15] / thr[7..13] (mode 1); the mode is the sign bit of the group scale.
+//   bits 8 (kind 0, e + m == 7): the OCP FP8 formats E4M3 / E5M2, one code per byte
+//          (sign in bit 7), rounded arithmetically; val/thr unused.
 struct QGrid {
     int32_t kind;
     int32_t e, m;
@@ -22,6 +24,7 @@ struct QGrid {
     float qmax;        // largest magnitude
     float val[16];
     float thr[15];
+    int32_t bits;      // 4, or 8 for FP8
 };
 
 struct QuantParams {
@@ -79,6 +82,7 @@ struct GemmParams {
 hipError_t launch_w4a16_mfma(const GemmParams& p, hipStream_t s);
 hipError_t launch_w4a16_valu(const GemmParams& p, hipStream_t s);
 hipError_t launch_w4a16_two_mode(const GemmParams& p, hipStream_t s);  // M <= 16, bf16, group 128
+hipError_t launch_w8a16_small(const GemmParams& p, hipStream_t s);     // FP8 weights, M <= 16, bf16
 hipError_t launch_w4a4_fp4(const GemmParams& p, hipStream_t s);
 hipError_t launch_w4a4_lut(const GemmParams& p, hipStream_t s);
 // W4A4 gate/up products with SwiGLU and the next layer's activation quantization in

@@ -237,7 +237,9 @@ constexpr int kSmallChunks = 4;  // K chunks per wavefront per batch
 
 // TWO: two-mode weights (group 128): a group is E1M2 when the sign bit of its scale is
 // set, E2M1 otherwise, and is scaled by the scale's magnitude.
-template <int MODE, bool SF16, bool SV, int T, bool TWO = false>  // MODE 0 tensor, 1 row, 2 group of 128
+// W8 = 4 / 5: OCP FP8 E4M3 / E5M2 weights, one byte per code: a lane's 32 codes of a
+// chunk are two 16-byte loads, converted to bf16 with the gfx950 FP8 converts (exact).
+template <int MODE, bool SF16, bool SV, int T, bool TWO = false, int W8 = 0>  // MODE 0 tensor, 1 row, 2 group of 128
 __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParams p) {
     constexpr int NW = kSmallWaves, CH = kSmallChunks;
     extern __shared__ uint4 xs[];  // per wavefront: [M][its K range / 8] bf16 vectors
@@ -265,7 +267,7 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
     for (int t = 0; t < T; t++) {
         const int64_t n = n0 + 16 * t + r16;
         n_ok[t] = n < p.N;
-        wrow[t] = n_ok[t] ? (uint32_t)(n * p.ldw + q * 16) : kOOB;
+        wrow[t] = n_ok[t] ? (uint32_t)(n * p.ldw + q * (W8 ? 32 : 16)) : kOOB;
         srow[t] = n_ok[t] ? (uint32_t)(n * ngroups * SB) : kOOB;
     }
 
@@ -283,7 +285,7 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
     }
     // 2. a batch of weights and scales; chunks past the range are loaded too (they
     //    belong to the next range or read zeros) and contribute nothing
-    uint4 wv[CH][T];
+    uint4 wv[CH][T], wv2[CH][T];  // wv2: the second 16 bytes of FP8 codes
     uint4 sv[T];
     uint32_t sc[CH][T];
     auto load_batch = [&](int cs) {
@@ -302,7 +304,8 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
         for (int b = 0; b < CH; b++) {
 #pragma unroll
             for (int t = 0; t < T; t++) {
-                wv[b][t] = buf_load16(rsW, wrow[t] + (uint32_t)(cs + b) * 64);
+                wv[b][t] = buf_load16(rsW, wrow[t] + (uint32_t)(cs + b) * (W8 ? 128 : 64));
+                if (W8) wv2[b][t] = buf_load16(rsW, wrow[t] + (uint32_t)(cs + b) * 128 + 16);
                 if (MODE == 2 && !SV) {
                     const uint32_t off = srow[t] + (uint32_t)(cs + b) * SB;
                     sc[b][t] = SF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsS, off, 0, 0)
@@ -313,7 +316,7 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
     };
     load_batch(c_begin);
     // 3. the X loads are the oldest in flight: wait until only the batch's loads remain
-    constexpr int kLater = CH * T + (MODE == 2 ? (SV ? T : CH * T) : 0);
+    constexpr int kLater = CH * T * (W8 ? 2 : 1) + (MODE == 2 ? (SV ? T : CH * T) : 0);
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kLater) : "memory");
 
     const int xrow = wbase + (r16 < p.M ? r16 : (int)p.M - 1) * nvw - c_begin * 16;
@@ -345,7 +348,27 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
                 const bool e1m2 = TWO && (sc[b][t] & kSign) != 0;
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
-                    bf16x8 wf = decode_e2m1_bf16(wd[j]);
+                    bf16x8 wf;
+                    if (W8) {
+                        // K values 8 j .. 8 j + 7 of the lane's 32: bytes 8 j .. of the two loads
+                        const uint4 h = j < 2 ? wv[b][t] : wv2[b][t];
+                        const uint32_t d0 = (j & 1) ? h.z : h.x, d1 = (j & 1) ? h.w : h.y;
+                        uint32_t o[4];
+                        if (W8 == 4) {
+                            o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false));
+                            o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true));
+                            o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false));
+                            o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true));
+                        } else {
+                            o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d0, 1.0f, false));
+                            o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d0, 1.0f, true));
+                            o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d1, 1.0f, false));
+                            o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d1, 1.0f, true));
+                        }
+                        wf = __builtin_bit_cast(bf16x8, o);
+                    } else {
+                        wf = decode_e2m1_bf16(wd[j]);
+                    }
                     if (TWO) {
                         const bf16x8 w1 = decode_e1m2_bf16(wd[j]);
                         wf = e1m2 ? w1 : wf;
@@ -397,10 +420,10 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
     }
 }
 
-template <int MODE, bool SF16, bool SV, int T, bool TWO = false>
+template <int MODE, bool SF16, bool SV, int T, bool TWO = false, int W8 = 0>
 static hipError_t launch_small_t(const GemmParams& p, hipStream_t s) {
     const size_t lds = small_lds_bytes(p.M, p.K);
-    auto kern = w4a16_small_kernel<MODE, SF16, SV, T, TWO>;
+    auto kern = w4a16_small_kernel<MODE, SF16, SV, T, TWO, W8>;
     // the dynamic-LDS limit is a kernel attribute, set once per device
     static bool attr_set[64];
     int dev = 0;
@@ -415,24 +438,24 @@ static hipError_t launch_small_t(const GemmParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int MODE, bool SF16, bool SV, bool TWO = false>
+template <int MODE, bool SF16, bool SV, bool TWO = false, int W8 = 0>
 static hipError_t launch_small_sv(const GemmParams& p, hipStream_t s) {
     // M <= 4: one 16-column tile per wavefront (more workgroups, X is small);
     // larger M: three tiles share each staged X
-    return p.M <= 4 ? launch_small_t<MODE, SF16, SV, 1, TWO>(p, s) : launch_small_t<MODE, SF16, SV, 3, TWO>(p, s);
+    return p.M <= 4 ? launch_small_t<MODE, SF16, SV, 1, TWO, W8>(p, s) : launch_small_t<MODE, SF16, SV, 3, TWO, W8>(p, s);
 }
 
-template <bool SF16, bool TWO = false>
+template <bool SF16, bool TWO = false, int W8 = 0>
 static hipError_t launch_small(const GemmParams& p, hipStream_t s) {
     if (p.w_mode == 2) {
         const int64_t nchunks = p.K / 128;
         // one vector load per batch needs 4-byte aligned scale rows and batch starts
         const bool sv = SF16 ? (nchunks % (2 * kSmallWaves) == 0 && (reinterpret_cast<uintptr_t>(p.w_scales) & 3) == 0)
                              : (reinterpret_cast<uintptr_t>(p.w_scales) & 3) == 0;
-        return sv ? launch_small_sv<2, SF16, true, TWO>(p, s) : launch_small_sv<2, SF16, false, TWO>(p, s);
+        return sv ? launch_small_sv<2, SF16, true, TWO, W8>(p, s) : launch_small_sv<2, SF16, false, TWO, W8>(p, s);
     }
-    if (p.w_mode == 1) return launch_small_sv<1, SF16, false>(p, s);
-    return launch_small_sv<0, SF16, false>(p, s);
+    if (p.w_mode == 1) return launch_small_sv<1, SF16, false, false, W8>(p, s);
+    return launch_small_sv<0, SF16, false, false, W8>(p, s);
 }
 
 static bool small_fits(const GemmParams& p) {
@@ -441,6 +464,13 @@ static bool small_fits(const GemmParams& p) {
     return p.M <= 16 && (p.w_mode != 2 || p.w_group == 128) && small_lds_bytes(p.M, p.K) <= kSmallMaxLds &&
            // 32-bit buffer offsets
            p.N * p.ldw < kOOB && p.N * ngroups * sbytes < kOOB && ((p.M - 1) * p.lda + p.K) * 2 < (int64_t)kOOB;
+}
+
+hipError_t launch_w8a16_small(const GemmParams& p, hipStream_t s) {
+    if (p.M == 0 || p.N == 0) return hipSuccess;
+    if (!small_fits(p)) return launch_w4a16_valu(p, s);
+    if (p.wg.e == 4) return p.w_scale_f16 ? launch_small<true, false, 4>(p, s) : launch_small<false, false, 4>(p, s);
+    return p.w_scale_f16 ? launch_small<true, false, 5>(p, s) : launch_small<false, false, 5>(p, s);
 }
 
 hipError_t launch_w4a16_two_mode(const GemmParams& p, hipStream_t s) {
@@ -484,11 +514,13 @@ __global__ void __launch_bounds__(256) w4a16_valu_kernel(GemmParams p) {
         if (p.wg.kind == 2) s = fabsf(s);
         float part = 0.0f;
         for (int64_t k = k0; k < k0 + unit; k++) {
-            uint32_t c = (wr[k >> 1] >> (4 * (k & 1))) & 15u;
+            uint32_t c = p.wg.bits == 8 ? wr[k] : (wr[k >> 1] >> (4 * (k & 1))) & 15u;
             float xv = p.a_kind == 1 ? bf16_bits_to_float(reinterpret_cast<const uint16_t*>(p.a)[m * p.lda + k])
                                      : reinterpret_cast<const float*>(p.a)[m * p.lda + k];
             float g;
-            if (p.wg.kind == 2) {
+            if (p.wg.bits == 8) {
+                g = p.wg.e == 4 ? fp8_value<4>(c) : fp8_value<5>(c);
+            } else if (p.wg.kind == 2) {
                 g = p.wg.val[vbase + (c & 7)];
                 if (c & 8) g = -g;
             } else {

@@ -247,6 +247,59 @@ __global__ void __launch_bounds__(kThreads) quantize_chunk_kernel(QuantParams p,
     }
 }
 
+// TENSOR and GROUP modes with an OCP FP8 grid (one code per byte): the same units and
+// scales as quantize_chunk_kernel, codes by fp8_code, 8 bytes stored per lane.
+template <bool VEC, bool BF16, int U, int E>
+__global__ void __launch_bounds__(kThreads) quantize_fp8_kernel(QuantParams p, int64_t chunks, int64_t nunits) {
+    Raw8 raw[U];
+    int64_t row[U], col[U];
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+        int64_t u = (int64_t)blockIdx.x * U + i;
+        if (u >= nunits) u = nunits - 1;  // a duplicate of the last unit writes the same bytes
+        row[i] = u / chunks;
+        col[i] = (u % chunks) * kChunk + threadIdx.x * 8;
+        raw[i] = load_raw8<VEC, BF16>(reinterpret_cast<const char*>(p.x) + row[i] * p.ldx * (BF16 ? 2 : 4), col[i],
+                                      p.cols);
+    }
+    float tensor_r = 0.0f;
+    if (p.mode == 0) {
+        float s = p.tensor_scale ? p.tensor_scale[0] : p.tensor_amax[0] / p.g.qmax;
+        tensor_r = recip_or_zero(s);
+        if (blockIdx.x == 0 && threadIdx.x == 0 && p.tensor_scale && p.scales_out)
+            reinterpret_cast<float*>(p.scales_out)[0] = s;
+    }
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+        float v[8];
+        raw8_to_float<BF16>(raw[i], v);
+        float r = tensor_r;
+        if (p.mode != 0) {
+            const int lanes = p.group >> 3;
+            const int64_t unit = row[i] * (p.cols / p.group) + col[i] / p.group;
+            float amax;
+            if (p.amax_in) amax = (col[i] < p.cols) ? p.amax_in[unit] : 0.0f;
+            else amax = group_max(max_abs8(v), lanes);
+            float s = amax / p.g.qmax;
+            if (p.scale_f16) s = round_f16(s);
+            r = recip_or_zero(s);
+            if (col[i] < p.cols && (threadIdx.x & (lanes - 1)) == 0 && p.scales_out) store_scale(p, unit, s);
+        }
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            lo |= fp8_code<E>(v[k] * r) << (8 * k);
+            hi |= fp8_code<E>(v[k + 4] * r) << (8 * k);
+        }
+        if (col[i] < p.cols) {
+            uint8_t* dst = p.packed + row[i] * p.ldp + col[i];
+            if (VEC) *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+            else
+                for (int k = 0; k < 8 && col[i] + k < p.cols; k++) dst[k] = (uint8_t)((k < 4 ? lo : hi) >> (8 * (k & 3)));
+        }
+    }
+}
+
 // GROUP mode with the two-mode grid ([HiFloat4] section 2.1: per group the E2M1 or the
 // E1M2 layout, one control bit).  Per group both candidates are formed -- s_m =
 // fl32(amax / Qmax_m) (binary16-rounded for f16 scales), codes of y = fl32(x * fl32(1/s_m))
@@ -508,7 +561,11 @@ static void quantize_launch(const QuantParams& p, hipStream_t s) {
         int64_t chunks = (p.cols + kChunk - 1) / kChunk;
         int64_t nunits = p.rows * chunks;
         dim3 grid((unsigned)((nunits + U - 1) / U));
-        if (p.g.kind == 2)
+        if (p.g.bits == 8 && p.g.e == 4)
+            hipLaunchKernelGGL((quantize_fp8_kernel<VEC, BF16, U, 4>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
+        else if (p.g.bits == 8)
+            hipLaunchKernelGGL((quantize_fp8_kernel<VEC, BF16, U, 5>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
+        else if (p.g.kind == 2)
             hipLaunchKernelGGL((quantize_two_mode_kernel<VEC, BF16, U>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
         else if (VEC && p.mode == 2 && p.group == 128 && p.g.is_e2m1 && !p.col_shift && !p.amax_in &&
             p.rows * ((p.cols + QT * 8 - 1) / (QT * 8)) < (1LL << 30) && p.cols < (1LL << 30)) {
@@ -551,12 +608,14 @@ __global__ void __launch_bounds__(kThreads) dequantize_kernel(const uint8_t* pac
     const uint8_t* prow = packed + row * ldp;
     for (int i = 0; i < 8 && col + i < cols; i++) {
         int64_t c = col + i;
-        uint32_t code = (prow[c >> 1] >> (4 * (c & 1))) & 15u;
+        uint32_t code = g.bits == 8 ? prow[c] : (prow[c >> 1] >> (4 * (c & 1))) & 15u;
         int64_t unit = mode == 0 ? 0 : (mode == 1 ? row : row * (cols / group) + c / group);
         float sc = scale_f16 ? __half2float(reinterpret_cast<const __half*>(scales)[unit])
                              : reinterpret_cast<const float*>(scales)[unit];
         float v;
-        if (g.kind == 2) {  // two-mode: the scale's sign bit picks E1M2 (val[8..15]) over E2M1
+        if (g.bits == 8) {
+            v = (g.e == 4 ? fp8_value<4>(code) : fp8_value<5>(code)) * sc;
+        } else if (g.kind == 2) {  // two-mode: the scale's sign bit picks E1M2 (val[8..15]) over E2M1
             const float m = g.val[(signbit(sc) ? 8 : 0) + (code & 7)] * fabsf(sc);
             v = (code & 8) ? -m : m;
         } else {

@@ -234,6 +234,27 @@ def test_two_mode_validation():
     assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # two-mode needs GROUP scales
 
 
+def test_fp8_validation():
+    lib = L.load()
+    N = ctypes.c_void_p(0)
+    g8 = _grid(0, 4, 3)
+    q = lib.fp4_quantize_pack
+    assert q(FAKE, 0, 4, 256, 256, g8, _gran(1), N, N, N, FAKE, 256, FAKE, N) == L.FP4_ERR_UNSUPPORTED  # ROW
+    assert q(FAKE, 0, 4, 256, 256, g8, _gran(2, 32), N, N, N, FAKE, 128, FAKE, N) == L.FP4_ERR_INVALID_ARG  # ldp
+    assert q(FAKE, 0, 4, 256, 256, _grid(0, 3, 4), _gran(2, 32), N, N, N, FAKE, 256, FAKE, N) == L.FP4_ERR_UNSUPPORTED
+    d = L.fp4_gemm_desc()
+    d.M, d.N, d.K = 16, 32, 256
+    d.a_kind = L.FP4_PACKED
+    d.a, d.lda, d.w, d.ldw, d.w_scales, d.y, d.ldy = 0x10000, 128, 0x20000, 256, 0x30000, 0x40000, 32
+    d.a_scale = 0x50000
+    d.a_grid, d.w_grid = _grid(), g8
+    d.w_gran = _gran(1)
+    d.y_dtype = L.FP4_BF16
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # FP8 weights with packed activations
+    d.a_kind, d.lda, d.ldw = L.FP4_BF16, 256, 128
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_INVALID_ARG  # ldw < K
+
+
 def test_preshift_validation():
     lib = L.load()
     N = ctypes.c_void_p(0)
