@@ -434,6 +434,34 @@ def bench_two_mode(torch, F):
     return out
 
 
+def bench_fp8(torch, F):
+    """The decode workload with OCP FP8 E4M3 weights (one byte per code, fp16 scales per
+    128): the weight quantize and the W8A16 GEMV at M = 1, 4, 16."""
+    f8 = F.grid_minifloat(4, 3)
+    g = F.gran("group", DEC_G, "f16")
+    NP = 8
+    W = gen_normal(torch, (DEC_N, DEC_K), 0.02, 100)
+    P = [torch.empty((DEC_N, DEC_K), dtype=torch.uint8, device="cuda") for _ in range(NP)]
+    S = [torch.empty(DEC_N * (DEC_K // DEC_G), dtype=torch.float16, device="cuda") for _ in range(NP)]
+    for i in range(NP):
+        F.fp4_quantize_pack(W, f8, g, packed=P[i], scales=S[i])
+    sb = DEC_N * (DEC_K // DEC_G) * 2
+    qb = DEC_N * DEC_K * 4 + DEC_N * DEC_K + sb
+    t_q = graph_time(torch, lambda i: F.fp4_quantize_pack(W, f8, g, packed=P[i % NP], scales=S[i % NP]), 32)
+    out = [roofline_entry("quantize_pack f32->FP8 E4M3 g128 (11008x4096)", "hbm", qb / t_q / 1e9, HBM_PEAK_GBS,
+                          "GB/s", t_q, qb, "bytes")]
+    for m in DEC_MS:
+        X = gen_activations(torch, m, DEC_K, 200 + m, outlier_frac=0.0)
+        Y = torch.empty((m, DEC_N), dtype=torch.bfloat16, device="cuda")
+        b = DEC_N * DEC_K + sb + m * DEC_K * 2 + m * DEC_N * 2
+        t = graph_time(torch, lambda i: F.fp4_gemm(X, P[i % NP], S[i % NP], f8, g, y=Y), 64)
+        out.append(roofline_entry(f"w8a16 gemv FP8 E4M3 M={m} (11008x4096, g128)", "hbm", b / t / 1e9, HBM_PEAK_GBS,
+                                  "GB/s", t, b, "bytes"))
+    del W, P, S
+    torch.cuda.empty_cache()
+    return out
+
+
 # VALU instructions per (element, candidate) in the search's inner loop, counted from the
 # gfx950 assembly of search_eval_kernel: E1M2 14.8, E2M1 12.3, E3M0 17.8 per element, plus
 # 2.4 per element for the per-candidate wavefront reduction; averaged over the formats
@@ -542,6 +570,8 @@ def main():
         kernels += bench_preshift_w4a4(torch, F)
         log("LLaMA-13B prefill layer ...")
         kernels += bench_prefill(torch, F)
+        log("FP8 grid ...")
+        kernels += bench_fp8(torch, F)
         log("two-mode grid ...")
         kernels += bench_two_mode(torch, F)
         log("fused SwiGLU + quantize ...")
