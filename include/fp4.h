@@ -71,6 +71,12 @@ typedef int32_t fp4_status;
  *   inf/NaN.  E2M1 = {0, .5, 1, 1.5, 2, 3, 4, 6}, E1M2 = {0, .25, ..., 1.75},
  *   E3M0 = {0, 1, 2, 4, ..., 64}.  A real-valued bias b is the same grid times
  *   2^(1-b) ([FP4-LLM] eq. (4)), i.e. it lives entirely in the scale.
+ *   With e + m == 7 the grid is an OCP FP8 format ([FP4-LLM] FP8 for key layers):
+ *   (4, 3) E4M3 (bias 7, S.1111.111 is NaN, largest 448) or (5, 2) E5M2 (bias 15,
+ *   exponent 31 is inf/NaN, largest 57344); one code per byte (sign in bit 7), so
+ *   code arrays hold `cols` bytes per row.  FP8 takes TENSOR or GROUP scales in
+ *   quantize/dequantize and the W4A16 product (W8A16); codes are the nearest finite
+ *   value with ties to the even code, saturating at the largest.
  * FP4_GRID_LUT16: 16 sorted signed values in lut[] (e.g. NF4, [Overview] NF4), each
  *   exactly representable in binary16.
  * FP4_GRID_TWO_MODE: per scale group either E2M1 (mode 0) or E1M2 (mode 1)
@@ -286,6 +292,8 @@ fp4_status fp4_search_activations(const void* x, int32_t x_dtype, int64_t rows, 
  *       norm) of the exact value; groups whose scale is below 2^-14 of their row's
  *       largest lose relative precision to f16 subnormals.
  *   y_dtype FP4_BF16 rounds the f32 result to nearest-even.
+ *   FP8 weights (E4M3 / E5M2) take the W4A16 path only (W8A16), one byte per code
+ *   (ldw >= K).
  *   Two-mode weights (FP4_GRID_TWO_MODE, GROUP scales) take the W4A16 path only: each
  *   group's codes are read on its own grid (the sign of its scale) and scaled by |s|.
  * Strides: K a multiple of 32 for the matrix-core paths; packed rows 16-byte aligned. */
