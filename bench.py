@@ -141,9 +141,9 @@ def traffic_for(kernel_file: str, key: str):
 # fragment, index range among the dispatches whose name has that fragment).
 TRAFFIC_KERNELS = [
     ("quantize_decode", "quant.hip", "quantize_e2m1_g128_kernel<false, 1, 256>", (0, 3)),
-    ("gemv_m1", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 1>", (0, 3)),
-    ("gemv_m4", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 1>", (3, 6)),
-    ("gemv_m16", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 3>", (0, 3)),
+    ("gemv_m1", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 1, false, 0>", (0, 3)),
+    ("gemv_m4", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 1, false, 0>", (3, 6)),
+    ("gemv_m16", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 3, false, 0>", (0, 3)),
     ("quantize_act", "quant.hip", "quantize_e2m1_tensor_kernel<true, true, 256>", (0, 3)),
     ("w4a4_c3", "gemm_w4a4.hip", "w4a4_fp4_kernel<128, 128, false>", (0, 3)),
     ("w4a4_qkv", "gemm_w4a4.hip", "w4a4_fp4_kernel<256, 256, false>", (0, 3)),
