@@ -121,8 +121,10 @@ class Grid:
 
     @property
     def bits(self) -> int:
-        """Bits per code: 4, or 8 for the FP8 grids (one code per byte)."""
-        return 8 if self.kind == "minifloat" and self.e + self.m == 7 else 4
+        """Bits per code: 4, 6 for the FP6 grids, 8 for the FP8 grids."""
+        if self.kind == "minifloat" and self.e + self.m in (5, 7):
+            return self.e + self.m + 1
+        return 4
 
     @property
     def array(self) -> np.ndarray:
@@ -145,6 +147,19 @@ class Grid:
 
 def minifloat(e: int, m: int) -> Grid:
     return Grid("minifloat", e, m, tuple(minifloat_grid(e, m, 1)))
+
+
+def fp6(e: int, m: int) -> Grid:
+    """The OCP 6-bit formats (FP6 of the progressive 8/6/4-bit precision, [FP4-LLM]):
+    E2M3 with bias 1 (largest 7.5) and E3M2 with bias 3 (largest 28), no code reserved;
+    32 magnitudes each by the same FP value formula."""
+    if (e, m) == (2, 3):
+        g = minifloat_grid(2, 3, 1)
+    elif (e, m) == (3, 2):
+        g = minifloat_grid(3, 2, 3)
+    else:
+        raise ValueError((e, m))
+    return Grid("minifloat", e, m, tuple(g))
 
 
 def fp8(e: int, m: int) -> Grid:
@@ -228,18 +243,37 @@ def quantize(x, r, grid: Grid) -> np.ndarray:
     assert np.all(np.isfinite(x)), "non-finite inputs are not valid"
     out = np.empty(x.shape, dtype=np.uint8)
     g = np.ascontiguousarray(grid.array)
-    kind = (2 if grid.bits == 8 else 0) if grid.kind == "minifloat" else 1
+    kind = {4: 0, 6: 3, 8: 2}[grid.bits] if grid.kind == "minifloat" else 1
     _c().orc_quantize(_ptr(x), _ptr(r), x.size, kind, _ptr(g), g.size, _ptr(out))
     return out
 
 
 def pack_codes(codes: np.ndarray, grid: Grid) -> np.ndarray:
-    """Storage of codes: two 4-bit codes per byte, or one 8-bit code per byte."""
-    return np.asarray(codes, dtype=np.uint8).copy() if grid.bits == 8 else pack(codes)
+    """Storage of codes: two 4-bit codes per byte; one 8-bit code per byte; 6-bit codes
+    as a little-endian bit stream, code i in bits [6 i, 6 i + 6) of its row (four codes
+    in three bytes; the matrix cores' FP6 operand layout)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    if grid.bits == 8:
+        return c.copy()
+    if grid.bits == 6:
+        assert c.shape[-1] % 4 == 0
+        q = c.reshape(c.shape[:-1] + (-1, 4)).astype(np.uint32)
+        v = q[..., 0] | (q[..., 1] << 6) | (q[..., 2] << 12) | (q[..., 3] << 18)
+        b = np.stack([v & 255, (v >> 8) & 255, v >> 16], axis=-1).astype(np.uint8)
+        return b.reshape(c.shape[:-1] + (-1,))
+    return pack(c)
 
 
 def unpack_codes(packed: np.ndarray, grid: Grid) -> np.ndarray:
-    return np.asarray(packed, dtype=np.uint8).copy() if grid.bits == 8 else unpack(packed)
+    p = np.asarray(packed, dtype=np.uint8)
+    if grid.bits == 8:
+        return p.copy()
+    if grid.bits == 6:
+        b = p.reshape(p.shape[:-1] + (-1, 3)).astype(np.uint32)
+        v = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16)
+        q = np.stack([(v >> (6 * i)) & 63 for i in range(4)], axis=-1).astype(np.uint8)
+        return q.reshape(p.shape[:-1] + (-1,))
+    return unpack(p)
 
 
 def pack(codes: np.ndarray) -> np.ndarray:

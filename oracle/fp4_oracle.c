@@ -92,18 +92,19 @@ static int nearest(double v, const double* grid, int n) {
  *      Qmax)) over the ng magnitudes, Qmax = grid[ng-1];
  *  grid_kind 1 (16-entry signed lookup grid, e.g. NF4): code = nearest(clip(y,
  *      grid[0], grid[ng-1])) over the ng sorted signed values;
- *  grid_kind 2 (8-bit minifloat, sign-magnitude): as kind 0 with the sign in bit 7.
+ *  grid_kind 2 (8-bit minifloat, sign-magnitude): as kind 0 with the sign in bit 7;
+ *  grid_kind 3 (6-bit minifloat, sign-magnitude): as kind 0 with the sign in bit 5.
  * Non-finite x is not a valid input.                                                */
 void orc_quantize(const float* x, const float* r, int64_t n, int grid_kind,
                   const double* grid, int ng, uint8_t* codes) {
     #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; i++) {
         float y = x[i] * r[i];
-        if (grid_kind == 0 || grid_kind == 2) {
+        if (grid_kind == 0 || grid_kind == 2 || grid_kind == 3) {
             int s = signbit(x[i]) ? 1 : 0;
             double v = fmin(fabs((double)y), grid[ng - 1]);
             int c = nearest(v, grid, ng);
-            codes[i] = (uint8_t)((s << (grid_kind == 0 ? 3 : 7)) | c);
+            codes[i] = (uint8_t)((s << (grid_kind == 0 ? 3 : grid_kind == 2 ? 7 : 5)) | c);
         } else {
             double v = fmax(fmin((double)y, grid[ng - 1]), grid[0]);
             codes[i] = (uint8_t)nearest(v, grid, ng);

@@ -622,18 +622,40 @@ def test_fp8_codes_by_hand(fmt, vals, codes):
     assert [int(c) for c in got] == codes
 
 
-def test_fp8_round_trip_and_product():
+def test_fp8_fp6_round_trip_and_product():
     """Grid values times a power-of-two scale quantize to themselves (dequantize is exact),
-    and the W8A16 product of such a weight is the dense product."""
+    and the W8A16 / W6A16 product of such a weight is the dense product."""
     rng = np.random.default_rng(41)
-    for fmt in ((4, 3), (5, 2)):
-        g = O.fp8(*fmt)
+    for g in (O.fp8(4, 3), O.fp8(5, 2), O.fp6(2, 3), O.fp6(3, 2)):
         idx = rng.integers(0, len(g.values), (6, 64))
         idx[:, ::32] = len(g.values) - 1  # every group's largest magnitude is the grid's
         w = (g.array[idx] * np.where(rng.random((6, 64)) < 0.5, -1, 1) * 2.0 ** -10).astype(np.float32)
         packed, sc = O.quantize_pack(w, g, "group", group=32)
-        assert packed.shape == (6, 64) and np.array_equal(sc, np.full((6, 2), 2.0 ** -10, np.float32))
+        assert packed.shape == (6, 64 * g.bits // 8) and np.array_equal(sc, np.full((6, 2), 2.0 ** -10, np.float32))
         assert np.array_equal(O.dequantize(packed, g, "group", sc, group=32), w)
         x = rng.normal(size=(3, 64)).astype(np.float32)
         r = O.gemm_w4a16(x, packed, g, "group", sc, group=32)
         assert np.allclose(r, x.astype(np.float64) @ w.astype(np.float64).T, rtol=0, atol=1e-12)
+
+
+# ---- FP6 grids (OCP E2M3 / E3M2), packed four codes in three bytes -------------------
+def test_fp6_grids_and_packing():
+    """E2M3: 32 magnitudes in steps of 1/8 below 1, largest 7.5; E3M2: smallest subnormal
+    1/16, largest 28.  Codes by hand (ties to even, saturation, sign in bit 5) and the
+    bit-stream packing of four codes into three bytes."""
+    g23, g32 = O.fp6(2, 3), O.fp6(3, 2)
+    assert len(g23.values) == 32 and g23.array[1] == 0.125 and g23.array[8] == 1.0 and g23.array[-1] == 7.5
+    assert len(g32.values) == 32 and g32.array[1] == 0.0625 and g32.array[4] == 0.25 and g32.array[-1] == 28.0
+    assert g23.bits == 6 and g32.bits == 6
+    vals = np.array([1.0, 1.0625, 1.1875, 9.0, -0.0, -0.1875, 0.0625, 3.3], np.float32)
+    c = O.quantize(vals, np.ones(8, np.float32), g23)
+    # 1.0625 ties 1.0/1.125 -> 1.0 (even code 8); 1.1875 ties 1.125/1.25 -> 1.25 (code 10);
+    # -0.1875 ties 0.125/0.25 -> 0.25 (code 2); 0.0625 ties 0/0.125 -> 0; 3.3 -> 3.25
+    assert [int(v) for v in c] == [8, 8, 10, 31, 32, 32 | 2, 0, 21]
+    codes = np.array([[1, 2, 3, 4, 63, 0, 32, 5]], np.uint8)
+    packed = O.pack_codes(codes, g23)
+    v = 1 | 2 << 6 | 3 << 12 | 4 << 18
+    assert packed[0, :3].tolist() == [v & 255, (v >> 8) & 255, v >> 16]
+    v = 63 | 0 << 6 | 32 << 12 | 5 << 18
+    assert packed[0, 3:].tolist() == [v & 255, (v >> 8) & 255, v >> 16]
+    assert np.array_equal(O.unpack_codes(packed, g23), codes)
