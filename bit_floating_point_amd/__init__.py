@@ -116,16 +116,19 @@ def fp4_calibrate(x: torch.Tensor, reduce: str = "tensor", group: int = 0, first
     return out
 
 
-def _is_fp8(grid: L.fp4_grid) -> bool:
-    """The OCP FP8 grids take one byte per code (the 4-bit grids two codes per byte)."""
-    return grid.kind == L.FP4_GRID_MINIFLOAT and grid.e + grid.m == 7
+def code_bits(grid: L.fp4_grid) -> int:
+    """Bits per stored code: 8 for the FP8 grids, 6 for the FP6 grids (a bit stream),
+    4 otherwise (two codes per byte)."""
+    if grid.kind == L.FP4_GRID_MINIFLOAT and grid.e + grid.m in (5, 7):
+        return grid.e + grid.m + 1
+    return 4
 
 
 def fp4_quantize_pack(x: torch.Tensor, grid: L.fp4_grid, g: L.fp4_gran, amax_in=None, tensor_scale=None,
                       col_shift=None, packed=None, scales=None):
     rows, cols = x.shape
     if packed is None:
-        packed = torch.empty((rows, cols if _is_fp8(grid) else cols // 2), dtype=torch.uint8, device=x.device)
+        packed = torch.empty((rows, cols * code_bits(grid) // 8), dtype=torch.uint8, device=x.device)
     if scales is None and tensor_scale is None:
         sd = torch.float16 if g.scale_dtype == FP4_F16 else torch.float32
         scales = torch.empty(_units(g, rows, cols), dtype=sd, device=x.device)
@@ -138,7 +141,7 @@ def fp4_quantize_pack(x: torch.Tensor, grid: L.fp4_grid, g: L.fp4_gran, amax_in=
 def fp4_dequantize(packed: torch.Tensor, grid: L.fp4_grid, g: L.fp4_gran, scales: torch.Tensor,
                    col_shift=None, out=None) -> torch.Tensor:
     rows, width = packed.shape
-    cols = width if _is_fp8(grid) else 2 * width
+    cols = width * 8 // code_bits(grid)
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.float32, device=packed.device)
     L.check(L.lib().fp4_dequantize(_ptr(packed), rows, cols, _ld(packed), grid, g, _ptr(scales),

@@ -61,6 +61,14 @@ fp4_status make_grid(const fp4_grid& g, QGrid* q) {
         q->qmax = g.e == 4 ? 448.0f : 57344.0f;
         return FP4_OK;
     }
+    if (g.kind == FP4_GRID_MINIFLOAT && ((g.e == 2 && g.m == 3) || (g.e == 3 && g.m == 2))) {
+        q->kind = 0;  // OCP FP6: E2M3 (bias 1, max 7.5) or E3M2 (bias 3, max 28)
+        q->e = g.e;
+        q->m = g.m;
+        q->bits = 6;
+        q->qmax = g.e == 2 ? 7.5f : 28.0f;
+        return FP4_OK;
+    }
     if (g.kind == FP4_GRID_MINIFLOAT) {
         if (g.e < 1 || g.m < 0 || g.e + g.m != 3)
             return fail(FP4_ERR_UNSUPPORTED, "minifloat grid needs e >= 1 and e + m == 3, or FP8 E4M3 / E5M2 (got e=%d m=%d)",
@@ -178,10 +186,11 @@ fp4_status fp4_quantize_pack(const void* x, int32_t x_dtype, int64_t rows, int64
     fp4_status st = make_grid(grid, &q);
     if (st) return st;
     if ((st = check_gran(gran, cols))) return st;
-    if (q.bits == 8) {
-        if (ldp < cols) return fail(FP4_ERR_INVALID_ARG, "FP8 codes take one byte each: ldp >= cols");
-        if (gran.mode == FP4_SCALE_ROW || col_shift || cols % 8 != 0)
-            return fail(FP4_ERR_UNSUPPORTED, "FP8 quantization takes TENSOR or GROUP scales, no column shifts, cols % 8 == 0");
+    if (q.bits != 4) {
+        if (ldp < cols * q.bits / 8) return fail(FP4_ERR_INVALID_ARG, "ldp below the code bytes of a row (cols * bits / 8)");
+        if (gran.mode == FP4_SCALE_ROW || col_shift || cols % 8 != 0 || (q.bits == 6 && ldp % 2 != 0))
+            return fail(FP4_ERR_UNSUPPORTED,
+                        "FP8/FP6 quantization takes TENSOR or GROUP scales, no column shifts, cols % 8 == 0 (FP6: ldp even)");
     }
     if (q.kind == 2 && (gran.mode != FP4_SCALE_GROUP || col_shift))
         return fail(FP4_ERR_UNSUPPORTED, "the two-mode grid needs GROUP scales and no column shifts");
@@ -209,7 +218,7 @@ fp4_status fp4_quantize_pack(const void* x, int32_t x_dtype, int64_t rows, int64
     p.scales_out = scales_out;
     p.col_shift = col_shift;
     p.shift_sign = -1;
-    p.vec = ((ldx * esz) % 16 == 0) && (cols % 8 == 0) && (ldp % (q.bits == 8 ? 8 : 4) == 0);
+    p.vec = ((ldx * esz) % 16 == 0) && (cols % 8 == 0) && (ldp % (q.bits == 8 ? 8 : 4) == 0);  // FP6 stores 16-bit words
     p.g = q;
     hipStream_t s = (hipStream_t)stream;
     if (gran.mode == FP4_SCALE_TENSOR && !tensor_scale) {
@@ -238,7 +247,8 @@ fp4_status fp4_dequantize(const uint8_t* packed, int64_t rows, int64_t cols, int
     QGrid q;
     fp4_status st = make_grid(grid, &q);
     if (st) return st;
-    if (q.bits == 8 && ldp < cols) return fail(FP4_ERR_INVALID_ARG, "FP8 codes take one byte each: ldp >= cols");
+    if (q.bits != 4 && ldp < cols * q.bits / 8) return fail(FP4_ERR_INVALID_ARG, "ldp below the code bytes of a row");
+    if (q.bits == 6 && cols % 4 != 0) return fail(FP4_ERR_INVALID_ARG, "FP6 rows hold whole groups of four codes");
     if ((st = check_gran(gran, cols))) return st;
     if (q.kind == 2 && gran.mode != FP4_SCALE_GROUP) return fail(FP4_ERR_UNSUPPORTED, "the two-mode grid needs GROUP scales");
     return hip_status(launch_dequantize(packed, rows, cols, ldp, q, gran.mode, gran.group, scales,
@@ -258,8 +268,8 @@ fp4_status fp4_preshift_weights(const float* w, int64_t n, int64_t k, int64_t ld
     if ((st = make_grid(w_grid, &qw))) return st;
     if ((st = check_gran(w_gran, k))) return st;
     if (w_gran.mode == FP4_SCALE_TENSOR) return fail(FP4_ERR_UNSUPPORTED, "pre-shifted weights need ROW or GROUP scales");
-    if (qa.kind == 2 || qw.kind == 2 || qa.bits == 8 || qw.bits == 8)
-        return fail(FP4_ERR_UNSUPPORTED, "pre-shift with the two-mode or FP8 grids is not implemented");
+    if (qa.kind == 2 || qw.kind == 2 || qa.bits != 4 || qw.bits != 4)
+        return fail(FP4_ERR_UNSUPPORTED, "pre-shift with the two-mode, FP8 or FP6 grids is not implemented");
     if (!aligned16(w) || !aligned16(w_packed) || !aligned16(shift_out))
         return fail(FP4_ERR_ALIGNMENT, "w, w_packed and shift_out must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
@@ -397,16 +407,17 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
 
     if (p.wg.kind == 2 && (d->w_gran.mode != FP4_SCALE_GROUP || d->a_kind == FP4_PACKED))
         return fail(FP4_ERR_UNSUPPORTED, "two-mode weights need GROUP scales and f32/bf16 activations");
-    if (p.wg.bits == 8) {
-        if (d->a_kind == FP4_PACKED) return fail(FP4_ERR_UNSUPPORTED, "FP8 weights take f32/bf16 activations (W8A16)");
-        if (d->ldw < d->K) return fail(FP4_ERR_INVALID_ARG, "FP8 codes take one byte each: ldw >= K");
+    if (p.wg.bits != 4) {
+        if (d->a_kind == FP4_PACKED) return fail(FP4_ERR_UNSUPPORTED, "FP8/FP6 weights take f32/bf16 activations");
+        if (d->ldw < d->K * p.wg.bits / 8) return fail(FP4_ERR_INVALID_ARG, "ldw below the code bytes of a row");
+        if (p.wg.bits == 6 && d->K % 4 != 0) return fail(FP4_ERR_INVALID_ARG, "FP6 rows hold whole groups of four codes");
     }
     if (d->a_kind == FP4_F32 || d->a_kind == FP4_BF16) {
         if (d->lda < d->K) return fail(FP4_ERR_INVALID_ARG, "lda < K");
         bool mfma = d->a_kind == FP4_BF16 && p.wg.is_e2m1 && d->K % 128 == 0 && (d->lda * 2) % 16 == 0 &&
                     (d->w_gran.mode != FP4_SCALE_GROUP || d->w_gran.group % 128 == 0);
-        // FP8 weights: the small-batch matrix-core kernel, else the VALU kernel
-        if (p.wg.bits == 8) {
+        // FP8 / FP6 weights: the small-batch matrix-core kernel, else the VALU kernel
+        if (p.wg.bits != 4) {
             if (d->a_kind == FP4_BF16 && d->K % 128 == 0 && (d->lda * 2) % 16 == 0 && d->M <= 16 &&
                 (d->w_gran.mode != FP4_SCALE_GROUP || d->w_gran.group == 128))
                 return hip_status(launch_w8a16_small(p, s), "fp4_gemm/w8a16");

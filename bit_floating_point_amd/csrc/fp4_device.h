@@ -136,18 +136,27 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// OCP FP8 code of y (nearest value, ties to the even code, saturating at the largest
-// finite value, sign of y in bit 7): E4M3 (E = 4: bias 7, largest code 0x7E = 448) or
-// E5M2 (E = 5: bias 15, largest 0x7B = 57344).  Below the smallest normal the code is
+// OCP 8- and 6-bit minifloats: E4M3 (bias 7, largest code 0x7E = 448, the all-ones code
+// is NaN), E5M2 (bias 15, largest 0x7B = 57344, exponent 31 is inf/NaN), E2M3 (bias 1,
+// largest 7.5) and E3M2 (bias 3, largest 28), the last two with no reserved code; the
+// sign sits above the e + m magnitude bits.
+template <int E, int M>
+struct Wide {
+    static constexpr int BIAS = E == 4 ? 7 : E == 5 ? 15 : E == 2 ? 1 : 3;
+    static constexpr uint32_t MAXC = E == 4 ? 0x7Eu : E == 5 ? 0x7Bu : 31u;
+    static constexpr float QMAX = E == 4 ? 448.0f : E == 5 ? 57344.0f : E == 2 ? 7.5f : 28.0f;
+};
+
+// Code of y: nearest value, ties to the even code, saturating at the largest finite
+// value, sign of y on top.  Below the smallest normal the magnitude code is
 // rint(|y| / 2^(1 - bias - m)) (2^m is the smallest normal's code); above it the binary32
 // significand is rounded to m bits (nearest-even, carries into the exponent) and its
 // exponent re-biased.
-template <int E>
-__device__ __forceinline__ uint32_t fp8_code(float y) {
-    constexpr int M = 7 - E, BIAS = E == 4 ? 7 : 15;
-    constexpr uint32_t MAXC = E == 4 ? 0x7Eu : 0x7Bu;
-    constexpr float QMAX = E == 4 ? 448.0f : 57344.0f;
-    const float a = fminf(fabsf(y), QMAX);
+template <int E, int M>
+__device__ __forceinline__ uint32_t wide_code(float y) {
+    constexpr int BIAS = Wide<E, M>::BIAS;
+    constexpr uint32_t MAXC = Wide<E, M>::MAXC;
+    const float a = fminf(fabsf(y), Wide<E, M>::QMAX);
     uint32_t c;
     if (a < __builtin_ldexpf(1.0f, 1 - BIAS)) {
         c = (uint32_t)rintf(a * __builtin_ldexpf(1.0f, BIAS - 1 + M));
@@ -156,16 +165,36 @@ __device__ __forceinline__ uint32_t fp8_code(float y) {
         u += (1u << (22 - M)) - 1u + ((u >> (23 - M)) & 1u);
         c = (u >> (23 - M)) - ((uint32_t)(127 - BIAS) << M);
     }
-    return ((__float_as_uint(y) >> 31) << 7) | (c < MAXC ? c : MAXC);
+    return ((__float_as_uint(y) >> 31) << (E + M)) | (c < MAXC ? c : MAXC);
 }
 
-// Value of an OCP FP8 code (sign applied), exact.
-template <int E>
-__device__ __forceinline__ float fp8_value(uint32_t c) {
-    constexpr int M = 7 - E, BIAS = E == 4 ? 7 : 15;
+// Value of a code (sign applied), exact.
+template <int E, int M>
+__device__ __forceinline__ float wide_value(uint32_t c) {
+    constexpr int BIAS = Wide<E, M>::BIAS;
     const int ex = (int)((c >> M) & ((1u << E) - 1u)), mant = (int)(c & ((1u << M) - 1u));
     const float v = ex == 0 ? ldexpf((float)mant, 1 - BIAS - M) : ldexpf((float)((1 << M) + mant), ex - BIAS - M);
-    return (c & 0x80u) ? -v : v;
+    return ((c >> (E + M)) & 1u) ? -v : v;
+}
+
+// Value of a code of an 8- or 6-bit grid (e, m)
+__device__ __forceinline__ float wide_value_rt(uint32_t c, int e) {
+    switch (e) {
+        case 4: return wide_value<4, 3>(c);
+        case 5: return wide_value<5, 2>(c);
+        case 2: return wide_value<2, 3>(c);
+        default: return wide_value<3, 2>(c);
+    }
+}
+
+// Code k of a row of 6-bit codes (bit stream, code k in bits [6 k, 6 k + 6)); codes
+// 4 j + 1 and 4 j + 2 straddle two bytes of their 3-byte group, the others do not.
+__device__ __forceinline__ uint32_t code6_at(const uint8_t* row, int64_t k) {
+    const int64_t bit = 6 * k, b = bit >> 3;
+    const int sh = (int)(bit & 7);
+    uint32_t v = row[b];
+    if (sh > 2) v |= (uint32_t)row[b + 1] << 8;
+    return (v >> sh) & 63u;
 }
 
 // Double-double sums (binary64 pairs, TwoSum error terms): about 100 bits, enough to

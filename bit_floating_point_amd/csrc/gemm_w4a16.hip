@@ -21,6 +21,7 @@
 namespace fp4 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x32 __attribute__((ext_vector_type(32)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kW16Waves = 4;
@@ -239,6 +240,9 @@ constexpr int kSmallChunks = 4;  // K chunks per wavefront per batch
 // set, E2M1 otherwise, and is scaled by the scale's magnitude.
 // W8 = 4 / 5: OCP FP8 E4M3 / E5M2 weights, one byte per code: a lane's 32 codes of a
 // chunk are two 16-byte loads, converted to bf16 with the gfx950 FP8 converts (exact).
+// W8 = 2 / 3: OCP FP6 E2M3 / E3M2 weights, a bit stream of 6-bit codes: a lane's 32
+// codes are 24 bytes (three 8-byte loads), converted at once by the 32-value FP6
+// converts (exact).
 template <int MODE, bool SF16, bool SV, int T, bool TWO = false, int W8 = 0>  // MODE 0 tensor, 1 row, 2 group of 128
 __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParams p) {
     constexpr int NW = kSmallWaves, CH = kSmallChunks;
@@ -267,7 +271,8 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
     for (int t = 0; t < T; t++) {
         const int64_t n = n0 + 16 * t + r16;
         n_ok[t] = n < p.N;
-        wrow[t] = n_ok[t] ? (uint32_t)(n * p.ldw + q * (W8 ? 32 : 16)) : kOOB;
+        constexpr int LB = W8 >= 4 ? 32 : W8 ? 24 : 16;  // bytes of a lane's 32 codes
+        wrow[t] = n_ok[t] ? (uint32_t)(n * p.ldw + q * LB) : kOOB;
         srow[t] = n_ok[t] ? (uint32_t)(n * ngroups * SB) : kOOB;
     }
 
@@ -286,6 +291,7 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
     // 2. a batch of weights and scales; chunks past the range are loaded too (they
     //    belong to the next range or read zeros) and contribute nothing
     uint4 wv[CH][T], wv2[CH][T];  // wv2: the second 16 bytes of FP8 codes
+    uint2 w6[CH][T][3];           // FP6: 24 bytes
     uint4 sv[T];
     uint32_t sc[CH][T];
     auto load_batch = [&](int cs) {
@@ -304,8 +310,15 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
         for (int b = 0; b < CH; b++) {
 #pragma unroll
             for (int t = 0; t < T; t++) {
-                wv[b][t] = buf_load16(rsW, wrow[t] + (uint32_t)(cs + b) * (W8 ? 128 : 64));
-                if (W8) wv2[b][t] = buf_load16(rsW, wrow[t] + (uint32_t)(cs + b) * 128 + 16);
+                if (W8 == 2 || W8 == 3) {
+#pragma unroll
+                    for (int h = 0; h < 3; h++)
+                        w6[b][t][h] = __builtin_bit_cast(
+                            uint2, __builtin_amdgcn_raw_buffer_load_b64(rsW, wrow[t] + (uint32_t)(cs + b) * 96 + 8 * h, 0, 0));
+                } else {
+                    wv[b][t] = buf_load16(rsW, wrow[t] + (uint32_t)(cs + b) * (W8 ? 128 : 64));
+                    if (W8) wv2[b][t] = buf_load16(rsW, wrow[t] + (uint32_t)(cs + b) * 128 + 16);
+                }
                 if (MODE == 2 && !SV) {
                     const uint32_t off = srow[t] + (uint32_t)(cs + b) * SB;
                     sc[b][t] = SF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsS, off, 0, 0)
@@ -316,7 +329,7 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
     };
     load_batch(c_begin);
     // 3. the X loads are the oldest in flight: wait until only the batch's loads remain
-    constexpr int kLater = CH * T * (W8 ? 2 : 1) + (MODE == 2 ? (SV ? T : CH * T) : 0);
+    constexpr int kLater = CH * T * (W8 >= 4 ? 2 : W8 ? 3 : 1) + (MODE == 2 ? (SV ? T : CH * T) : 0);
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kLater) : "memory");
 
     const int xrow = wbase + (r16 < p.M ? r16 : (int)p.M - 1) * nvw - c_begin * 16;
@@ -346,10 +359,21 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
                 f32x4 acc = MODE == 2 ? f32x4{0.f, 0.f, 0.f, 0.f} : total[t];
                 constexpr uint32_t kSign = SF16 ? 0x8000u : 0x80000000u;
                 const bool e1m2 = TWO && (sc[b][t] & kSign) != 0;
+                bf16x32 w32;
+                if (W8 == 2 || W8 == 3) {
+                    typedef unsigned v6u __attribute__((ext_vector_type(6)));
+                    const v6u src = v6u{w6[b][t][0].x, w6[b][t][0].y, w6[b][t][1].x, w6[b][t][1].y, w6[b][t][2].x,
+                                        w6[b][t][2].y};
+                    if (W8 == 2) w32 = __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(src, 1.0f);
+                    else w32 = __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(src, 1.0f);
+                }
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
                     bf16x8 wf;
-                    if (W8) {
+                    if (W8 == 2 || W8 == 3) {
+                        wf = bf16x8{w32[8 * j], w32[8 * j + 1], w32[8 * j + 2], w32[8 * j + 3], w32[8 * j + 4],
+                                    w32[8 * j + 5], w32[8 * j + 6], w32[8 * j + 7]};
+                    } else if (W8) {
                         // K values 8 j .. 8 j + 7 of the lane's 32: bytes 8 j .. of the two loads
                         const uint4 h = j < 2 ? wv[b][t] : wv2[b][t];
                         const uint32_t d0 = (j & 1) ? h.z : h.x, d1 = (j & 1) ? h.w : h.y;
@@ -468,7 +492,11 @@ static bool small_fits(const GemmParams& p) {
 
 hipError_t launch_w8a16_small(const GemmParams& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
-    if (!small_fits(p)) return launch_w4a16_valu(p, s);
+    if (!small_fits(p) || (p.wg.bits == 6 && p.ldw % 8 != 0)) return launch_w4a16_valu(p, s);
+    if (p.wg.bits == 6) {
+        if (p.wg.e == 2) return p.w_scale_f16 ? launch_small<true, false, 2>(p, s) : launch_small<false, false, 2>(p, s);
+        return p.w_scale_f16 ? launch_small<true, false, 3>(p, s) : launch_small<false, false, 3>(p, s);
+    }
     if (p.wg.e == 4) return p.w_scale_f16 ? launch_small<true, false, 4>(p, s) : launch_small<false, false, 4>(p, s);
     return p.w_scale_f16 ? launch_small<true, false, 5>(p, s) : launch_small<false, false, 5>(p, s);
 }
@@ -514,12 +542,12 @@ __global__ void __launch_bounds__(256) w4a16_valu_kernel(GemmParams p) {
         if (p.wg.kind == 2) s = fabsf(s);
         float part = 0.0f;
         for (int64_t k = k0; k < k0 + unit; k++) {
-            uint32_t c = p.wg.bits == 8 ? wr[k] : (wr[k >> 1] >> (4 * (k & 1))) & 15u;
+            uint32_t c = p.wg.bits == 8 ? wr[k] : p.wg.bits == 6 ? code6_at(wr, k) : (wr[k >> 1] >> (4 * (k & 1))) & 15u;
             float xv = p.a_kind == 1 ? bf16_bits_to_float(reinterpret_cast<const uint16_t*>(p.a)[m * p.lda + k])
                                      : reinterpret_cast<const float*>(p.a)[m * p.lda + k];
             float g;
-            if (p.wg.bits == 8) {
-                g = p.wg.e == 4 ? fp8_value<4>(c) : fp8_value<5>(c);
+            if (p.wg.bits != 4) {
+                g = wide_value_rt(c, p.wg.e);
             } else if (p.wg.kind == 2) {
                 g = p.wg.val[vbase + (c & 7)];
                 if (c & 8) g = -g;

@@ -247,10 +247,11 @@ __global__ void __launch_bounds__(kThreads) quantize_chunk_kernel(QuantParams p,
     }
 }
 
-// TENSOR and GROUP modes with an OCP FP8 grid (one code per byte): the same units and
-// scales as quantize_chunk_kernel, codes by fp8_code, 8 bytes stored per lane.
-template <bool VEC, bool BF16, int U, int E>
-__global__ void __launch_bounds__(kThreads) quantize_fp8_kernel(QuantParams p, int64_t chunks, int64_t nunits) {
+// TENSOR and GROUP modes with an OCP 8-bit (one code per byte) or 6-bit (a bit stream,
+// four codes in three bytes) grid: the same units and scales as quantize_chunk_kernel,
+// codes by wide_code; a lane stores its 8 codes as 8 bytes or as three 16-bit words.
+template <bool VEC, bool BF16, int U, int E, int M>
+__global__ void __launch_bounds__(kThreads) quantize_wide_kernel(QuantParams p, int64_t chunks, int64_t nunits) {
     Raw8 raw[U];
     int64_t row[U], col[U];
 #pragma unroll
@@ -285,17 +286,29 @@ __global__ void __launch_bounds__(kThreads) quantize_fp8_kernel(QuantParams p, i
             r = recip_or_zero(s);
             if (col[i] < p.cols && (threadIdx.x & (lanes - 1)) == 0 && p.scales_out) store_scale(p, unit, s);
         }
-        uint32_t lo = 0, hi = 0;
+        if (E + M == 7) {
+            uint32_t lo = 0, hi = 0;
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            lo |= fp8_code<E>(v[k] * r) << (8 * k);
-            hi |= fp8_code<E>(v[k + 4] * r) << (8 * k);
-        }
-        if (col[i] < p.cols) {
-            uint8_t* dst = p.packed + row[i] * p.ldp + col[i];
-            if (VEC) *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-            else
-                for (int k = 0; k < 8 && col[i] + k < p.cols; k++) dst[k] = (uint8_t)((k < 4 ? lo : hi) >> (8 * (k & 3)));
+            for (int k = 0; k < 4; k++) {
+                lo |= wide_code<E, M>(v[k] * r) << (8 * k);
+                hi |= wide_code<E, M>(v[k + 4] * r) << (8 * k);
+            }
+            if (col[i] < p.cols) {
+                uint8_t* dst = p.packed + row[i] * p.ldp + col[i];
+                if (VEC) *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+                else
+                    for (int k = 0; k < 8 && col[i] + k < p.cols; k++) dst[k] = (uint8_t)((k < 4 ? lo : hi) >> (8 * (k & 3)));
+            }
+        } else {
+            uint64_t bits = 0;
+#pragma unroll
+            for (int k = 0; k < 8; k++) bits |= (uint64_t)wide_code<E, M>(v[k] * r) << (6 * k);
+            if (col[i] < p.cols) {  // cols is a multiple of 8: a lane's 6 bytes are whole
+                uint16_t* dst = reinterpret_cast<uint16_t*>(p.packed + row[i] * p.ldp + col[i] / 8 * 6);
+                dst[0] = (uint16_t)bits;
+                dst[1] = (uint16_t)(bits >> 16);
+                dst[2] = (uint16_t)(bits >> 32);
+            }
         }
     }
 }
@@ -561,10 +574,14 @@ static void quantize_launch(const QuantParams& p, hipStream_t s) {
         int64_t chunks = (p.cols + kChunk - 1) / kChunk;
         int64_t nunits = p.rows * chunks;
         dim3 grid((unsigned)((nunits + U - 1) / U));
-        if (p.g.bits == 8 && p.g.e == 4)
-            hipLaunchKernelGGL((quantize_fp8_kernel<VEC, BF16, U, 4>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
-        else if (p.g.bits == 8)
-            hipLaunchKernelGGL((quantize_fp8_kernel<VEC, BF16, U, 5>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
+        if (p.g.bits != 4 && p.g.e == 4)
+            hipLaunchKernelGGL((quantize_wide_kernel<VEC, BF16, U, 4, 3>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
+        else if (p.g.bits != 4 && p.g.e == 5)
+            hipLaunchKernelGGL((quantize_wide_kernel<VEC, BF16, U, 5, 2>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
+        else if (p.g.bits != 4 && p.g.e == 2)
+            hipLaunchKernelGGL((quantize_wide_kernel<VEC, BF16, U, 2, 3>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
+        else if (p.g.bits != 4)
+            hipLaunchKernelGGL((quantize_wide_kernel<VEC, BF16, U, 3, 2>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
         else if (p.g.kind == 2)
             hipLaunchKernelGGL((quantize_two_mode_kernel<VEC, BF16, U>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
         else if (VEC && p.mode == 2 && p.group == 128 && p.g.is_e2m1 && !p.col_shift && !p.amax_in &&
@@ -608,13 +625,13 @@ __global__ void __launch_bounds__(kThreads) dequantize_kernel(const uint8_t* pac
     const uint8_t* prow = packed + row * ldp;
     for (int i = 0; i < 8 && col + i < cols; i++) {
         int64_t c = col + i;
-        uint32_t code = g.bits == 8 ? prow[c] : (prow[c >> 1] >> (4 * (c & 1))) & 15u;
+        uint32_t code = g.bits == 8 ? prow[c] : g.bits == 6 ? code6_at(prow, c) : (prow[c >> 1] >> (4 * (c & 1))) & 15u;
         int64_t unit = mode == 0 ? 0 : (mode == 1 ? row : row * (cols / group) + c / group);
         float sc = scale_f16 ? __half2float(reinterpret_cast<const __half*>(scales)[unit])
                              : reinterpret_cast<const float*>(scales)[unit];
         float v;
-        if (g.bits == 8) {
-            v = (g.e == 4 ? fp8_value<4>(code) : fp8_value<5>(code)) * sc;
+        if (g.bits != 4) {
+            v = wide_value_rt(code, g.e) * sc;
         } else if (g.kind == 2) {  // two-mode: the scale's sign bit picks E1M2 (val[8..15]) over E2M1
             const float m = g.val[(signbit(sc) ? 8 : 0) + (code & 7)] * fabsf(sc);
             v = (code & 8) ? -m : m;

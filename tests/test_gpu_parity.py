@@ -625,8 +625,12 @@ def test_two_mode_w4a16_gemm(M, N, K, sd, adt):
     assert np.array_equal(host(yb.view(torch.int16)).view(np.uint16), O.rne_bf16_bits(y32))
 
 
-# ---------------------------------------------------------------- FP8 grids ------
-@pytest.mark.parametrize("fmt", [(4, 3), (5, 2)])
+# ---------------------------------------------------------------- FP8 / FP6 grids -
+def _wide(fmt):
+    return O.fp8(*fmt) if sum(fmt) == 7 else O.fp6(*fmt)
+
+
+@pytest.mark.parametrize("fmt", [(4, 3), (5, 2), (2, 3), (3, 2)])
 @pytest.mark.parametrize("rows,cols,mode,group,sd,bf16", [
     (37, 1040, "group", 8, "f32", False),
     (64, 4096, "group", 128, "f16", True),
@@ -634,23 +638,23 @@ def test_two_mode_w4a16_gemm(M, N, K, sd, adt):
     (9, 2048, "group", 512, "f32", True),
 ])
 def test_fp8_quantize_dequantize(fmt, rows, cols, mode, group, sd, bf16):
-    """OCP FP8 quantize (one code per byte): every code and scale bit-exact; dequantized
-    values bit-exact."""
-    say("fp8", fmt, rows, cols, mode, group, sd, bf16)
+    """OCP FP8 (one code per byte) and FP6 (four codes in three bytes) quantize: every
+    code byte and scale bit-exact; dequantized values bit-exact."""
+    say("fp8/fp6", fmt, rows, cols, mode, group, sd, bf16)
     x = synth.weight(13, rows, rows, cols) if not bf16 else synth.activations(13, rows, rows, cols,
                                                                              outlier_frac=0.01, bf16=True)
     xt = dev(x, torch.bfloat16 if bf16 else torch.float32)
-    og, fg = O.fp8(*fmt), F.grid_minifloat(*fmt)
+    og, fg = _wide(fmt), F.grid_minifloat(*fmt)
     g = F.gran(mode, group, sd)
     packed, scales = F.fp4_quantize_pack(xt, fg, g)
     op, osc = O.quantize_pack(x, og, mode, group=group, scale_dtype=sd)
-    assert packed.shape == (rows, cols) and np.array_equal(host(packed), op)
+    assert packed.shape == (rows, cols * og.bits // 8) and np.array_equal(host(packed), op)
     assert np.array_equal(_f16_or_f32_bits(host(scales).reshape(np.asarray(osc).shape)), _f16_or_f32_bits(osc))
     deq = host(F.fp4_dequantize(packed, fg, g, scales))
     assert np.array_equal(deq.view(np.uint32), O.dequantize(op, og, mode, osc, group=group).view(np.uint32))
 
 
-@pytest.mark.parametrize("fmt", [(4, 3), (5, 2)])
+@pytest.mark.parametrize("fmt", [(4, 3), (5, 2), (2, 3), (3, 2)])
 @pytest.mark.parametrize("M,N,K,mode,adt", [
     (1, 11008, 4096, "group", "bf16"),   # decode GEMV shape: the small matrix-core kernel
     (16, 11008, 4096, "group", "bf16"),
@@ -658,10 +662,10 @@ def test_fp8_quantize_dequantize(fmt, rows, cols, mode, group, sd, bf16):
     (3, 520, 512, "group", "f32"),       # f32 activations: the VALU kernel
 ])
 def test_fp8_w8a16_gemm(fmt, M, N, K, mode, adt):
-    """W8A16 with FP8 weights: within the GEMM tolerance of the binary64 oracle, bf16
-    output the nearest-even rounding of the fp32 output."""
-    say("w8a16", fmt, M, N, K, mode, adt)
-    og, fg = O.fp8(*fmt), F.grid_minifloat(*fmt)
+    """W8A16 / W6A16 with FP8 / FP6 weights: within the GEMM tolerance of the binary64
+    oracle, bf16 output the nearest-even rounding of the fp32 output."""
+    say("w8a16/w6a16", fmt, M, N, K, mode, adt)
+    og, fg = _wide(fmt), F.grid_minifloat(*fmt)
     w = synth.weight(14, N, N, K)
     gr = 128 if mode == "group" else 0
     op, osc = O.quantize_pack(w, og, mode, group=gr, scale_dtype="f16" if mode == "group" else "f32")
