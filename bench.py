@@ -435,29 +435,34 @@ def bench_two_mode(torch, F):
 
 
 def bench_fp8(torch, F):
-    """The decode workload with OCP FP8 E4M3 weights (one byte per code, fp16 scales per
-    128): the weight quantize and the W8A16 GEMV at M = 1, 4, 16."""
-    f8 = F.grid_minifloat(4, 3)
+    """The decode workload with OCP FP8 E4M3 weights (one byte per code) and FP6 E2M3
+    weights (four codes in three bytes), fp16 scales per 128: the weight quantize and the
+    W8A16 / W6A16 GEMV at M = 1, 4, 16."""
     g = F.gran("group", DEC_G, "f16")
     NP = 8
     W = gen_normal(torch, (DEC_N, DEC_K), 0.02, 100)
-    P = [torch.empty((DEC_N, DEC_K), dtype=torch.uint8, device="cuda") for _ in range(NP)]
-    S = [torch.empty(DEC_N * (DEC_K // DEC_G), dtype=torch.float16, device="cuda") for _ in range(NP)]
-    for i in range(NP):
-        F.fp4_quantize_pack(W, f8, g, packed=P[i], scales=S[i])
     sb = DEC_N * (DEC_K // DEC_G) * 2
-    qb = DEC_N * DEC_K * 4 + DEC_N * DEC_K + sb
-    t_q = graph_time(torch, lambda i: F.fp4_quantize_pack(W, f8, g, packed=P[i % NP], scales=S[i % NP]), 32)
-    out = [roofline_entry("quantize_pack f32->FP8 E4M3 g128 (11008x4096)", "hbm", qb / t_q / 1e9, HBM_PEAK_GBS,
-                          "GB/s", t_q, qb, "bytes")]
-    for m in DEC_MS:
-        X = gen_activations(torch, m, DEC_K, 200 + m, outlier_frac=0.0)
-        Y = torch.empty((m, DEC_N), dtype=torch.bfloat16, device="cuda")
-        b = DEC_N * DEC_K + sb + m * DEC_K * 2 + m * DEC_N * 2
-        t = graph_time(torch, lambda i: F.fp4_gemm(X, P[i % NP], S[i % NP], f8, g, y=Y), 64)
-        out.append(roofline_entry(f"w8a16 gemv FP8 E4M3 M={m} (11008x4096, g128)", "hbm", b / t / 1e9, HBM_PEAK_GBS,
-                                  "GB/s", t, b, "bytes"))
-    del W, P, S
+    out = []
+    for (e, m), name, tag in (((4, 3), "FP8 E4M3", "w8a16"), ((2, 3), "FP6 E2M3", "w6a16")):
+        fg = F.grid_minifloat(e, m)
+        cb = DEC_N * DEC_K * (e + m + 1) // 8  # code bytes
+        P = [torch.empty((DEC_N, DEC_K * (e + m + 1) // 8), dtype=torch.uint8, device="cuda") for _ in range(NP)]
+        S = [torch.empty(DEC_N * (DEC_K // DEC_G), dtype=torch.float16, device="cuda") for _ in range(NP)]
+        for i in range(NP):
+            F.fp4_quantize_pack(W, fg, g, packed=P[i], scales=S[i])
+        qb = DEC_N * DEC_K * 4 + cb + sb
+        t_q = graph_time(torch, lambda i: F.fp4_quantize_pack(W, fg, g, packed=P[i % NP], scales=S[i % NP]), 32)
+        out.append(roofline_entry(f"quantize_pack f32->{name} g128 (11008x4096)", "hbm", qb / t_q / 1e9,
+                                  HBM_PEAK_GBS, "GB/s", t_q, qb, "bytes"))
+        for mm in DEC_MS:
+            X = gen_activations(torch, mm, DEC_K, 200 + mm, outlier_frac=0.0)
+            Y = torch.empty((mm, DEC_N), dtype=torch.bfloat16, device="cuda")
+            b = cb + sb + mm * DEC_K * 2 + mm * DEC_N * 2
+            t = graph_time(torch, lambda i: F.fp4_gemm(X, P[i % NP], S[i % NP], fg, g, y=Y), 64)
+            out.append(roofline_entry(f"{tag} gemv {name} M={mm} (11008x4096, g128)", "hbm", b / t / 1e9,
+                                      HBM_PEAK_GBS, "GB/s", t, b, "bytes"))
+        del P, S
+    del W
     torch.cuda.empty_cache()
     return out
 
@@ -570,7 +575,7 @@ def main():
         kernels += bench_preshift_w4a4(torch, F)
         log("LLaMA-13B prefill layer ...")
         kernels += bench_prefill(torch, F)
-        log("FP8 grid ...")
+        log("FP8 / FP6 grids ...")
         kernels += bench_fp8(torch, F)
         log("two-mode grid ...")
         kernels += bench_two_mode(torch, F)
