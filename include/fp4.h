@@ -74,9 +74,13 @@ typedef int32_t fp4_status;
  *   With e + m == 7 the grid is an OCP FP8 format ([FP4-LLM] FP8 for key layers):
  *   (4, 3) E4M3 (bias 7, S.1111.111 is NaN, largest 448) or (5, 2) E5M2 (bias 15,
  *   exponent 31 is inf/NaN, largest 57344); one code per byte (sign in bit 7), so
- *   code arrays hold `cols` bytes per row.  FP8 takes TENSOR or GROUP scales in
- *   quantize/dequantize and the W4A16 product (W8A16); codes are the nearest finite
- *   value with ties to the even code, saturating at the largest.
+ *   code arrays hold `cols` bytes per row.  With e + m == 5 it is an OCP FP6 format
+ *   ([FP4-LLM] progressive 8/6/4 bits): (2, 3) E2M3 (bias 1, largest 7.5) or (3, 2)
+ *   E3M2 (bias 3, largest 28), no reserved code; codes form a little-endian bit
+ *   stream, code i in bits [6i, 6i+6) of its row (3 cols / 4 bytes; cols a multiple
+ *   of 4).  FP8/FP6 take TENSOR or GROUP scales in quantize/dequantize (cols a
+ *   multiple of 8) and the W4A16 product (W8A16 / W6A16); codes are the nearest
+ *   finite value with ties to the even code, saturating at the largest.
  * FP4_GRID_LUT16: 16 sorted signed values in lut[] (e.g. NF4, [Overview] NF4), each
  *   exactly representable in binary16.
  * FP4_GRID_TWO_MODE: per scale group either E2M1 (mode 0) or E1M2 (mode 1)
@@ -292,8 +296,8 @@ fp4_status fp4_search_activations(const void* x, int32_t x_dtype, int64_t rows, 
  *       norm) of the exact value; groups whose scale is below 2^-14 of their row's
  *       largest lose relative precision to f16 subnormals.
  *   y_dtype FP4_BF16 rounds the f32 result to nearest-even.
- *   FP8 weights (E4M3 / E5M2) take the W4A16 path only (W8A16), one byte per code
- *   (ldw >= K).
+ *   FP8 / FP6 weights take the W4A16 path only (W8A16 / W6A16): ldw >= K (FP8) or
+ *   3K/4 (FP6) bytes.
  *   Two-mode weights (FP4_GRID_TWO_MODE, GROUP scales) take the W4A16 path only: each
  *   group's codes are read on its own grid (the sign of its scale) and scaled by |s|.
  * Strides: K a multiple of 32 for the matrix-core paths; packed rows 16-byte aligned. */
