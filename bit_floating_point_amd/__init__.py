@@ -251,7 +251,7 @@ def fp4_gemm(a: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor, w_
     N = w_packed.shape[0]
     if a.dtype == torch.uint8:
         kind = FP4_PACKED
-        K = K if K is not None else 2 * a.shape[1]
+        K = K if K is not None else a.shape[1] * 8 // code_bits(a_grid if a_grid is not None else w_grid)
     else:
         kind = _dtype_code(a)
         K = K if K is not None else a.shape[1]

@@ -407,8 +407,21 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
 
     if (p.wg.kind == 2 && (d->w_gran.mode != FP4_SCALE_GROUP || d->a_kind == FP4_PACKED))
         return fail(FP4_ERR_UNSUPPORTED, "two-mode weights need GROUP scales and f32/bf16 activations");
+    if (p.wg.bits == 8 && p.wg.e == 4 && d->a_kind == FP4_PACKED) {
+        // W8A8: FP8 E4M3 activations and weights on the FP8 matrix cores
+        QGrid qa;
+        if ((st = make_grid(d->a_grid, &qa))) return st;
+        if (!(qa.bits == 8 && qa.e == 4)) return fail(FP4_ERR_UNSUPPORTED, "FP8 weights with packed activations need E4M3 x E4M3");
+        if (!d->a_scale) return fail(FP4_ERR_INVALID_ARG, "packed activations need a_scale");
+        if (d->lda < d->K || d->ldw < d->K || d->lda % 16 != 0)
+            return fail(FP4_ERR_ALIGNMENT, "FP8 rows: lda, ldw >= K and multiples of 16");
+        if (d->K % 32 != 0) return fail(FP4_ERR_UNSUPPORTED, "K must be a multiple of 32");
+        if (d->w_gran.mode == FP4_SCALE_GROUP || d->w_gran.scale_dtype != FP4_F32)
+            return fail(FP4_ERR_UNSUPPORTED, "W8A8 needs f32 TENSOR or ROW weight scales");
+        return hip_status(launch_w8a8_fp8(p, s), "fp4_gemm/w8a8");
+    }
     if (p.wg.bits != 4) {
-        if (d->a_kind == FP4_PACKED) return fail(FP4_ERR_UNSUPPORTED, "FP8/FP6 weights take f32/bf16 activations");
+        if (d->a_kind == FP4_PACKED) return fail(FP4_ERR_UNSUPPORTED, "FP8 E5M2 / FP6 weights take f32/bf16 activations");
         if (d->ldw < d->K * p.wg.bits / 8) return fail(FP4_ERR_INVALID_ARG, "ldw below the code bytes of a row");
         if (p.wg.bits == 6 && d->K % 4 != 0) return fail(FP4_ERR_INVALID_ARG, "FP6 rows hold whole groups of four codes");
     }

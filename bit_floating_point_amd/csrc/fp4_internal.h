@@ -84,6 +84,7 @@ hipError_t launch_w4a16_valu(const GemmParams& p, hipStream_t s);
 hipError_t launch_w4a16_two_mode(const GemmParams& p, hipStream_t s);  // M <= 16, bf16, group 128
 hipError_t launch_w8a16_small(const GemmParams& p, hipStream_t s);     // FP8 weights, M <= 16, bf16
 hipError_t launch_w4a4_fp4(const GemmParams& p, hipStream_t s);
+hipError_t launch_w8a8_fp8(const GemmParams& p, hipStream_t s);  // FP8 E4M3 x E4M3
 hipError_t launch_w4a4_lut(const GemmParams& p, hipStream_t s);
 // W4A4 gate/up products with SwiGLU and the next layer's activation quantization in
 // the epilogue: p.w / p.w_scales are the gate weights and row scales, p.y the E2M1 codes

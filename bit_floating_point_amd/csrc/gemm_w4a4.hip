@@ -94,8 +94,12 @@ __device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + exp_f32(
 // same BN/2 output columns; each wavefront computes the gate and the up products of the
 // same rows and BN/4 output columns, and its epilogue writes E2M1 codes of
 // h = fl32(SiLU(y_gate) * y_up) quantized with the next layer's scale and shifts.
-template <int BM, int BN, bool GLU>
+// F8 = 1: OCP FP8 E4M3 operands (one code per byte; no SwiGLU): a step is 64 codes (the
+// same 64 bytes per row), one 32x32x64 FP8 MFMA K-block whose lane fragment is the two
+// 16-byte segments 2 hk, 2 hk + 1 (read as the two "halves" of the FP4 pipeline).
+template <int BM, int BN, bool GLU, int F8 = 0>
 __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m, int ntiles, GluParams gp) {
+    constexpr int CPB = F8 ? 1 : 2;  // codes per byte
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int TM = WM / 32, TN = WN / 32;
     constexpr int LA = BM * 4 / 256, LB = BN * 4 / 256;  // 16-byte pieces per thread per step
@@ -121,7 +125,7 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
     const int wm = wave & 1, wn = wave >> 1;
     const int r32 = lane & 31, hk = lane >> 5;
-    const int nk = (int)((p.K + 127) / 128);
+    const int nk = (int)((p.K + 64 * CPB - 1) / (64 * CPB));
     // The step count per tile is rounded up to a multiple of 4 (the stage rotation);
     // steps past the last real one load zeros (out-of-range offsets) and add nothing.
     const int nk4 = (nk + 3) & ~3;
@@ -145,7 +149,7 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
 #pragma unroll
     for (int i = 0; i < (LA > LB ? LA : LB); i++) {
         int sidx = (4 * i + wave) * 64 + lane, row = sidx >> 2;
-        segk[i] = ((sidx & 3) ^ ((row >> 1) & 3)) * 32;
+        segk[i] = ((sidx & 3) ^ ((row >> 1) & 3)) * 16 * CPB;  // codes
     }
     uint32_t offA[LA], offB[LB], offS, offK;
     int dt = blockIdx.x, dpar = 0;
@@ -155,13 +159,13 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
 #pragma unroll
         for (int i = 0; i < LA; i++) {
             int row = ((4 * i + wave) * 64 + lane) >> 2;
-            offA[i] = (ok && m0 + row < p.M) ? (uint32_t)((m0 + row) * p.lda + segk[i] / 2) : kOOB;
+            offA[i] = (ok && m0 + row < p.M) ? (uint32_t)((m0 + row) * p.lda + segk[i] / CPB) : kOOB;
         }
 #pragma unroll
         for (int i = 0; i < LB; i++) {
             int row = ((4 * i + wave) * 64 + lane) >> 2;
             if (GLU && i >= LB / 2) row -= BN / 2;  // up rows (their own buffer)
-            offB[i] = (ok && n0 + row < p.N) ? (uint32_t)((n0 + row) * p.ldw + segk[i] / 2) : kOOB;
+            offB[i] = (ok && n0 + row < p.N) ? (uint32_t)((n0 + row) * p.ldw + segk[i] / CPB) : kOOB;
         }
         offS = (ok && p.w_mode == 1 && n0 + 4 * lane < p.N && 4 * lane < ON) ? (uint32_t)((n0 + 4 * lane) * 4) : kOOB;
         offK = (ok && 16 * lane < ON && n0 + 16 * lane < p.N) ? (uint32_t)(n0 + 16 * lane) : kOOB;
@@ -173,12 +177,12 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
     do {                                                                                                   \
         const int kb_ = (KB);                                                                              \
         _Pragma("unroll") for (int i = 0; i < LA; i++) {                                                   \
-            uint32_t off = (kb_ * 128 + segk[i] < p.K) ? offA[i] + (uint32_t)kb_ * kBKBytes : kOOB;        \
+            uint32_t off = (kb_ * 64 * CPB + segk[i] < p.K) ? offA[i] + (uint32_t)kb_ * kBKBytes : kOOB;   \
             dma16(rsA, off, __builtin_amdgcn_readfirstlane(                                                \
                                 (uint32_t)(uintptr_t)&STG[(4 * i + wave) * 1024]));                       \
         }                                                                                                  \
         _Pragma("unroll") for (int i = 0; i < LB; i++) {                                                   \
-            uint32_t off = (kb_ * 128 + segk[i] < p.K) ? offB[i] + (uint32_t)kb_ * kBKBytes : kOOB;        \
+            uint32_t off = (kb_ * 64 * CPB + segk[i] < p.K) ? offB[i] + (uint32_t)kb_ * kBKBytes : kOOB;   \
             dma16((GLU && i >= LB / 2) ? rsB2 : rsB, off, __builtin_amdgcn_readfirstlane(                  \
                                 (uint32_t)(uintptr_t)&STG[BM * kBKBytes + (4 * i + wave) * 1024]));       \
         }                                                                                                  \
@@ -208,10 +212,11 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
 // [TN/2, TN) the up rows of the same columns.
 #define FP4_READH(STG, H, FA, FB)                                                                          \
     do {                                                                                                   \
+        const int sg_ = F8 ? 2 * hk + (H) : 2 * (H) + hk;                                                  \
         _Pragma("unroll") for (int i = 0; i < TM; i++) FA[i] =                                             \
-            *reinterpret_cast<const uint4*>(&STG[swz(wm * WM + i * 32 + r32, 2 * (H) + hk)]);              \
+            *reinterpret_cast<const uint4*>(&STG[swz(wm * WM + i * 32 + r32, sg_)]);                       \
         _Pragma("unroll") for (int j = 0; j < TN; j++) FB[j] =                                             \
-            *reinterpret_cast<const uint4*>(&STG[BM * kBKBytes + swz(brow(j) + r32, 2 * (H) + hk)]);       \
+            *reinterpret_cast<const uint4*>(&STG[BM * kBKBytes + swz(brow(j) + r32, sg_)]);                \
     } while (0)
 // the MFMAs of one half step from fragment registers, with the LDS reads of the next
 // half step (issued just before) spread between them
@@ -235,6 +240,19 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
     auto brow = [&](int j) {
         return GLU ? (j / (TN / 2)) * (BN / 2) + wn * (WN / 2) + (j % (TN / 2)) * 32 : wn * WN + j * 32;
     };
+// FP8: the MFMAs of one step from both halves' fragments (lo 16 bytes, hi 16 bytes)
+#define FP4_MMA8(XA, YA, XB, YB)                                                                           \
+    do {                                                                                                   \
+        _Pragma("unroll") for (int j = 0; j < TN; j++) {                                                   \
+            const i32x8 bf = i32x8{(int)XB[j].x, (int)XB[j].y, (int)XB[j].z, (int)XB[j].w,                 \
+                                   (int)YB[j].x, (int)YB[j].y, (int)YB[j].z, (int)YB[j].w};                \
+            _Pragma("unroll") for (int i = 0; i < TM; i++) {                                               \
+                const i32x8 af = i32x8{(int)XA[i].x, (int)XA[i].y, (int)XA[i].z, (int)XA[i].w,             \
+                                       (int)YA[i].x, (int)YA[i].y, (int)YA[i].z, (int)YA[i].w};            \
+                acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[j][i], 0, 0, 0, 127, 0, 127); \
+            }                                                                                              \
+        }                                                                                                  \
+    } while (0)
     f32x16 acc[TN][TM];
     constexpr int PER_STEP = LA + LB;  // operand loads per step and thread (+1 with scales)
     // 16-byte output stores per thread of a staged epilogue (32 rows x WN bf16 columns
@@ -266,11 +284,15 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
 #define FP4_PHASE(W, SQ, SN, D)                                                                            \
     do {                                                                                                   \
         FP4_READH(SQ, 1, ya, yb);                                                                          \
-        FP4_MMAH(xa, xb);                                                                                  \
+        if constexpr (F8) {                                                                                \
+            FP4_MMA8(xa, ya, xb, yb);                                                                      \
+        } else {                                                                                           \
+            FP4_MMAH(xa, xb);                                                                              \
+        }                                                                                                  \
         FP4_SYNC(W);                                                                                       \
         D;                                                                                                 \
         FP4_READH(SN, 0, xa, xb);                                                                          \
-        FP4_MMAH(ya, yb);                                                                                  \
+        if constexpr (!F8) FP4_MMAH(ya, yb);                                                               \
     } while (0)
 #define FP4_GROUP(W0, W1, W2, D0, D1, D2, D3)                                                              \
     do {                                                                                                   \
@@ -473,6 +495,7 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
 #undef FP4_GROUP
 #undef FP4_READH
 #undef FP4_MMAH
+#undef FP4_MMA8
 #undef FP4_PHASE
     // drain the (zero) loads still in flight before the workgroup exits
     FP4_SYNC_ALL();
@@ -496,10 +519,10 @@ static int cu_count() {
     return counts[dev];
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int F8 = 0>
 static void launch_cfg(const GemmParams& p, hipStream_t s, int64_t cus) {
     const int64_t gm = (p.M + BM - 1) / BM, gn = (p.N + BN - 1) / BN, nt = gm * gn;
-    hipLaunchKernelGGL((w4a4_fp4_kernel<BM, BN, false>), dim3((unsigned)std::min(nt, cus)), dim3(256), 0, s, p,
+    hipLaunchKernelGGL((w4a4_fp4_kernel<BM, BN, false, F8>), dim3((unsigned)std::min(nt, cus)), dim3(256), 0, s, p,
                        (int)gm, (int)nt, GluParams{});
 }
 static GemmParams column_block(const GemmParams& p, int64_t n0, int64_t n1) {
@@ -517,17 +540,18 @@ static GemmParams column_block(const GemmParams& p, int64_t n0, int64_t n1) {
 // whole rounds stay 256x256 and the column block left over for a partial last round
 // takes the shape that finishes it soonest (a partial round of big tiles leaves
 // compute units idle).  Fewer tiles than compute units: 128x128.
+template <int F8 = 0>
 static hipError_t launch_block(const GemmParams& p, hipStream_t s) {
     const int64_t cus = cu_count();
     const int64_t gm256 = (p.M + 255) / 256, gn256 = (p.N + 255) / 256, t256 = gm256 * gn256;
     if (t256 < cus) {
-        launch_cfg<128, 128>(p, s, cus);
+        launch_cfg<128, 128, F8>(p, s, cus);
         return hipGetLastError();
     }
     const int64_t full_cols = (t256 / cus) * cus / gm256;  // 256-column blocks of whole rounds
     const int64_t n1 = std::min<int64_t>(p.N, full_cols * 256);
     if (n1 >= p.N || t256 % cus == 0) {
-        launch_cfg<256, 256>(p, s, cus);
+        launch_cfg<256, 256, F8>(p, s, cus);
         return hipGetLastError();
     }
     const int64_t rest = p.N - n1;
@@ -539,17 +563,18 @@ static hipError_t launch_block(const GemmParams& p, hipStream_t s) {
     // costs one more round than the full ones
     const double c256 = rounds(256, 256), c256x128 = 0.59 * rounds(256, 128), c128 = 0.35 * rounds(128, 128);
     if (c256 <= c256x128 && c256 <= c128) {
-        launch_cfg<256, 256>(p, s, cus);
+        launch_cfg<256, 256, F8>(p, s, cus);
         return hipGetLastError();
     }
-    launch_cfg<256, 256>(column_block(p, 0, n1), s, cus);
+    launch_cfg<256, 256, F8>(column_block(p, 0, n1), s, cus);
     const GemmParams q = column_block(p, n1, p.N);
-    if (c256x128 <= c128) launch_cfg<256, 128>(q, s, cus);
-    else launch_cfg<128, 128>(q, s, cus);
+    if (c256x128 <= c128) launch_cfg<256, 128, F8>(q, s, cus);
+    else launch_cfg<128, 128, F8>(q, s, cus);
     return hipGetLastError();
 }
 
-hipError_t launch_w4a4_fp4(const GemmParams& p, hipStream_t s) {
+template <int F8>
+static hipError_t launch_split(const GemmParams& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     const int64_t mstep = std::max<int64_t>(256, kMaxBufBytes / std::max<int64_t>(p.lda, 1) / 256 * 256);
     const int64_t nstep = std::max<int64_t>(256, kMaxBufBytes / std::max<int64_t>(p.ldw, 1) / 256 * 256);
@@ -563,12 +588,17 @@ hipError_t launch_w4a4_fp4(const GemmParams& p, hipStream_t s) {
             q.w = p.w + n0 * p.ldw;
             if (p.w_mode == 1) q.w_scales = reinterpret_cast<const float*>(p.w_scales) + n0;
             q.y = reinterpret_cast<uint8_t*>(p.y) + (m0 * p.ldy + n0) * ysz;
-            hipError_t e = launch_block(q, s);
+            hipError_t e = launch_block<F8>(q, s);
             if (e != hipSuccess) return e;
         }
     }
     return hipSuccess;
 }
+
+hipError_t launch_w4a4_fp4(const GemmParams& p, hipStream_t s) { return launch_split<0>(p, s); }
+
+// FP8 E4M3 x E4M3 (W8A8): the same kernel, one code per byte
+hipError_t launch_w8a8_fp8(const GemmParams& p, hipStream_t s) { return launch_split<1>(p, s); }
 
 // SwiGLU + next-layer quantization: tiles of BM rows x BN/2 output columns (gate and up
 // rows of those columns), 256 x 128 when they give every compute unit a tile, else

@@ -636,8 +636,9 @@ def gemm_w4a4(a_packed, a_grid: Grid, a_scale, w_packed, w_grid: Grid, mode: str
               w_scales, group: int = 0):
     """Both operands quantized.  Returns (r, acc):
     r = a * sum_(blocks) s[n, b] * sum_{k in b} A_q[m, k] * W_q[n, k]  (binary64);
-    acc = the unscaled code product sum_k A_q W_q (exact in binary64 for minifloat
-    grids: every product is a multiple of 2^-4 and the sums stay far below 2^53)."""
+    acc = the unscaled code product sum_k A_q W_q (exact in binary64 for the 4-bit
+    minifloat grids: every product is a multiple of 2^-4 and the sums stay far below
+    2^53; for FP8 a binary64 sum)."""
     A = _weight_values(a_packed, a_grid)
     V = _weight_values(w_packed, w_grid)
     N, K = V.shape

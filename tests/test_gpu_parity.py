@@ -683,6 +683,33 @@ def test_fp8_w8a16_gemm(fmt, M, N, K, mode, adt):
     assert np.array_equal(host(yb.view(torch.int16)).view(np.uint16), O.rne_bf16_bits(y32))
 
 
+@pytest.mark.parametrize("M,N,K,mode", [
+    (300, 520, 544, "row"),      # ragged tiles, a K tail of half a step
+    (2100, 2200, 1024, "row"),   # several tiles per workgroup
+    (4096, 5120, 4096, "tensor"),
+])
+def test_fp8_w8a8_gemm(M, N, K, mode):
+    """W8A8: FP8 E4M3 activations (per-tensor scale) x FP8 E4M3 weights on the FP8 matrix
+    cores, within the GEMM tolerance of the binary64 oracle; bf16 output the nearest-even
+    rounding of the fp32 output."""
+    say("w8a8", M, N, K, mode)
+    g8 = O.fp8(4, 3)
+    x = synth.activations(15, M, M, K, outlier_frac=0.01)
+    w = synth.weight(15, N, N, K)
+    ap, asc = O.quantize_pack(x, g8, "tensor")
+    wp, wsc = O.quantize_pack(w, g8, mode)
+    r, _ = O.gemm_w4a4(ap, g8, asc[0], wp, g8, mode, wsc)
+    fg = F.grid_minifloat(4, 3)
+    gap, gwp = torch.from_numpy(ap).to(DEV), torch.from_numpy(wp).to(DEV)
+    ga, gws = dev(np.asarray(asc, np.float32)), dev(np.asarray(wsc, np.float32))
+    y32 = host(F.fp4_gemm(gap, gwp, gws, fg, F.gran(mode), K=K, a_grid=fg, a_scale=ga, y_dtype=torch.float32))
+    err = O.rel_err(y32, r)
+    say("  rel err", err)
+    assert err <= TOL
+    yb = F.fp4_gemm(gap, gwp, gws, fg, F.gran(mode), K=K, a_grid=fg, a_scale=ga, y_dtype=torch.bfloat16)
+    assert np.array_equal(host(yb.view(torch.int16)).view(np.uint16), O.rne_bf16_bits(y32))
+
+
 # ---------------------------------------------------------------- determinism -----
 def test_repeat_runs_identical():
     x = synth.activations(3, 1, 256, 1024, outlier_frac=0.01)
