@@ -33,6 +33,7 @@ METRIC = "FP4 quantize GB/s + W4A16/W4A4 GEMM TFLOP/s, % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP4_PEAK_TFLOPS = 10100.0      # dense FP4 MFMA
 F16_PEAK_TFLOPS = 2500.0       # dense f16/bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # dense FP8 MFMA
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12  # lane-instructions/s: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
 
 
@@ -467,6 +468,27 @@ def bench_fp8(torch, F):
     return out
 
 
+def bench_w8a8(torch, F):
+    """FP8 E4M3 x E4M3 (W8A8, key layers in FP8): activations per-tensor, weights per-row,
+    on the 2048x4096x4096 shape and the LLaMA-13B QKV projection 4096x15360x5120."""
+    f8 = F.grid_minifloat(4, 3)
+    out = []
+    for (M, N, K, name) in ((2048, 4096, 4096, "2048x4096x4096"), (4096, 15360, 5120, "qkv 4096x15360x5120")):
+        X = gen_activations(torch, M, K, 500)
+        W = gen_normal(torch, (N, K), 0.02, 600)
+        ap, asc = F.fp4_quantize_pack(X, f8, F.gran("tensor"))
+        wp, wsc = F.fp4_quantize_pack(W, f8, F.gran("tensor"))
+        ws = wsc.expand(N).contiguous()  # per-row scales (all equal here)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        t = graph_time(torch, lambda i: F.fp4_gemm(ap, wp, ws, f8, F.gran("row"), K=K, a_grid=f8, a_scale=asc, y=y), 5)
+        fl = 2 * M * N * K
+        out.append(roofline_entry(f"w8a8 FP8 E4M3 GEMM {name}", "mfma", fl / t / 1e12, FP8_PEAK_TFLOPS, "TFLOP/s", t,
+                                  fl, "flop"))
+        del X, W, ap, wp, y
+        torch.cuda.empty_cache()
+    return out
+
+
 # VALU instructions per (element, candidate) in the search's inner loop, counted from the
 # gfx950 assembly of search_eval_kernel: E1M2 14.8, E2M1 12.3, E3M0 17.8 per element, plus
 # 2.4 per element for the per-candidate wavefront reduction; averaged over the formats
@@ -577,6 +599,7 @@ def main():
         kernels += bench_prefill(torch, F)
         log("FP8 / FP6 grids ...")
         kernels += bench_fp8(torch, F)
+        kernels += bench_w8a8(torch, F)
         log("two-mode grid ...")
         kernels += bench_two_mode(torch, F)
         log("fused SwiGLU + quantize ...")
