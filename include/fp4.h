@@ -296,8 +296,11 @@ fp4_status fp4_search_activations(const void* x, int32_t x_dtype, int64_t rows, 
  *       norm) of the exact value; groups whose scale is below 2^-14 of their row's
  *       largest lose relative precision to f16 subnormals.
  *   y_dtype FP4_BF16 rounds the f32 result to nearest-even.
- *   FP8 / FP6 weights take the W4A16 path only (W8A16 / W6A16): ldw >= K (FP8) or
- *   3K/4 (FP6) bytes.
+ *   FP8 / FP6 weights take the W4A16 path (W8A16 / W6A16): ldw >= K (FP8) or 3K/4
+ *   (FP6) bytes.  W8A8: PACKED activations with a_grid FP8 E4M3 and E4M3 weights with
+ *   f32 TENSOR/ROW scales run on the FP8 matrix cores, y = fl32(acc * fl32(a * s_n)),
+ *   acc summed in fp32 (not exact for FP8: within the GEMM tolerance); lda, ldw >= K,
+ *   K a multiple of 32.
  *   Two-mode weights (FP4_GRID_TWO_MODE, GROUP scales) take the W4A16 path only: each
  *   group's codes are read on its own grid (the sign of its scale) and scaled by |s|.
  * Strides: K a multiple of 32 for the matrix-core paths; packed rows 16-byte aligned. */
