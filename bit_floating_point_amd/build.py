@@ -25,12 +25,31 @@ CFLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-ffp-contract
           "-Wno-unused-command-line-argument"]
 
 
+# The persistent GEMM kernels count their outstanding loads in their waits; a register
+# spill would add scratch memory operations to those counts, so they must not spill.
+NO_SPILL = ("gemm_w4a4.hip", "gemm_lut.hip")
+
+
+def _check_no_spill(src: str, remarks: str) -> None:
+    name = None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].split()[0]
+        elif "ScratchSize [bytes/lane]:" in line:
+            size = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
+            if size != 0:
+                raise RuntimeError(f"{src}: kernel {name} spills ({size} bytes/lane of scratch)")
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if src in NO_SPILL else []
+    cmd = [HIPCC] + CFLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    if extra:
+        _check_no_spill(src, r.stderr)
     return obj
 
 

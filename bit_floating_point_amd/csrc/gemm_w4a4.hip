@@ -240,15 +240,36 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
     auto brow = [&](int j) {
         return GLU ? (j / (TN / 2)) * (BN / 2) + wn * (WN / 2) + (j % (TN / 2)) * 32 : wn * WN + j * 32;
     };
-// FP8: the MFMAs of one step from both halves' fragments (lo 16 bytes, hi 16 bytes)
-#define FP4_MMA8(XA, YA, XB, YB)                                                                           \
+// FP8: the MFMAs of the step held in registers (lo 16 bytes in x, hi 16 bytes in y),
+// refilling each fragment with step SN's as soon as its last MFMA has issued: the B
+// fragments of column block j after that block's MFMAs, the A fragments at the end.
+#define FP4_MMA8(SN)                                                                                       \
     do {                                                                                                   \
         _Pragma("unroll") for (int j = 0; j < TN; j++) {                                                   \
-            const i32x8 bf = i32x8{(int)XB[j].x, (int)XB[j].y, (int)XB[j].z, (int)XB[j].w,                 \
-                                   (int)YB[j].x, (int)YB[j].y, (int)YB[j].z, (int)YB[j].w};                \
+            const i32x8 bf = i32x8{(int)xb[j].x, (int)xb[j].y, (int)xb[j].z, (int)xb[j].w,                 \
+                                   (int)yb[j].x, (int)yb[j].y, (int)yb[j].z, (int)yb[j].w};                \
             _Pragma("unroll") for (int i = 0; i < TM; i++) {                                               \
-                const i32x8 af = i32x8{(int)XA[i].x, (int)XA[i].y, (int)XA[i].z, (int)XA[i].w,             \
-                                       (int)YA[i].x, (int)YA[i].y, (int)YA[i].z, (int)YA[i].w};            \
+                const i32x8 af = i32x8{(int)xa[i].x, (int)xa[i].y, (int)xa[i].z, (int)xa[i].w,             \
+                                       (int)ya[i].x, (int)ya[i].y, (int)ya[i].z, (int)ya[i].w};            \
+                acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[j][i], 0, 0, 0, 127, 0, 127); \
+            }                                                                                              \
+            xb[j] = *reinterpret_cast<const uint4*>(&SN[BM * kBKBytes + swz(brow(j) + r32, 2 * hk)]);      \
+            yb[j] = *reinterpret_cast<const uint4*>(&SN[BM * kBKBytes + swz(brow(j) + r32, 2 * hk + 1)]);  \
+        }                                                                                                  \
+        _Pragma("unroll") for (int i = 0; i < TM; i++) {                                                   \
+            xa[i] = *reinterpret_cast<const uint4*>(&SN[swz(wm * WM + i * 32 + r32, 2 * hk)]);             \
+            ya[i] = *reinterpret_cast<const uint4*>(&SN[swz(wm * WM + i * 32 + r32, 2 * hk + 1)]);         \
+        }                                                                                                  \
+    } while (0)
+// FP8: the MFMAs of the step in registers, without reads
+#define FP4_MMA8_REGS()                                                                                    \
+    do {                                                                                                   \
+        _Pragma("unroll") for (int j = 0; j < TN; j++) {                                                   \
+            const i32x8 bf = i32x8{(int)xb[j].x, (int)xb[j].y, (int)xb[j].z, (int)xb[j].w,                 \
+                                   (int)yb[j].x, (int)yb[j].y, (int)yb[j].z, (int)yb[j].w};                \
+            _Pragma("unroll") for (int i = 0; i < TM; i++) {                                               \
+                const i32x8 af = i32x8{(int)xa[i].x, (int)xa[i].y, (int)xa[i].z, (int)xa[i].w,             \
+                                       (int)ya[i].x, (int)ya[i].y, (int)ya[i].z, (int)ya[i].w};            \
                 acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[j][i], 0, 0, 0, 127, 0, 127); \
             }                                                                                              \
         }                                                                                                  \
@@ -269,6 +290,7 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
     FP4_DMAK(st3, 3);
     FP4_SYNC_ALL();
     FP4_READH(st0, 0, xa, xb);
+    if (F8 && BM * BN < 256 * 256) FP4_READH(st0, 1, ya, yb);
 
     // Compute stream: tile ct.  Global step s (counted across this workgroup's tiles;
     // every tile has a multiple of 4 steps) lives in stage s % 4.  Phase q: the first
@@ -281,18 +303,31 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
     // after it outstanding": the next two steps' loads, and in the first three phases
     // of a tile also the previous tile's output stores.  (A step with the scales has one
     // load more; that only makes a wait longer.)
+// (FP8: all of step q is in registers at the start of its phase; wait and meet the
+// barrier first -- step q+1 landed, every wavefront holds step q -- start the load into
+// q's stage, then run q's MFMAs while reading step q+1 into the registers they free.)
+// 256x256 FP8 tiles have no registers to spare for that (spills would break the load
+// counting of the waits): there the second halves are read just before the MFMAs.
 #define FP4_PHASE(W, SQ, SN, D)                                                                            \
     do {                                                                                                   \
-        FP4_READH(SQ, 1, ya, yb);                                                                          \
-        if constexpr (F8) {                                                                                \
-            FP4_MMA8(xa, ya, xb, yb);                                                                      \
+        if constexpr (F8 && BM * BN < 256 * 256) {                                                         \
+            FP4_SYNC(W);                                                                                   \
+            D;                                                                                             \
+            FP4_MMA8(SN);                                                                                  \
+        } else if constexpr (F8) {                                                                         \
+            FP4_READH(SQ, 1, ya, yb);                                                                      \
+            FP4_MMA8_REGS();                                                                               \
+            FP4_SYNC(W);                                                                                   \
+            D;                                                                                             \
+            FP4_READH(SN, 0, xa, xb);                                                                      \
         } else {                                                                                           \
+            FP4_READH(SQ, 1, ya, yb);                                                                      \
             FP4_MMAH(xa, xb);                                                                              \
+            FP4_SYNC(W);                                                                                   \
+            D;                                                                                             \
+            FP4_READH(SN, 0, xa, xb);                                                                      \
+            FP4_MMAH(ya, yb);                                                                              \
         }                                                                                                  \
-        FP4_SYNC(W);                                                                                       \
-        D;                                                                                                 \
-        FP4_READH(SN, 0, xa, xb);                                                                          \
-        if constexpr (!F8) FP4_MMAH(ya, yb);                                                               \
     } while (0)
 #define FP4_GROUP(W0, W1, W2, D0, D1, D2, D3)                                                              \
     do {                                                                                                   \
@@ -496,6 +531,7 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
 #undef FP4_READH
 #undef FP4_MMAH
 #undef FP4_MMA8
+#undef FP4_MMA8_REGS
 #undef FP4_PHASE
     // drain the (zero) loads still in flight before the workgroup exits
     FP4_SYNC_ALL();
