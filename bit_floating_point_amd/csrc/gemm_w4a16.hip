@@ -32,12 +32,14 @@ constexpr int kBatch = 4;  // K chunks in flight per wavefront
 // leaves room for the static partial-sum array within the CU's 160 KiB).
 constexpr int kSmallWavesPerGroup = 8;
 constexpr size_t kSmallMaxLds = 136 * 1024;
-__host__ __device__ inline int small_region(int64_t M, int64_t nchunks) {
+// The region also holds the wavefront's T partial-sum vectors per lane after its loop.
+__host__ __device__ inline int small_region(int64_t M, int64_t nchunks, int T) {
     const int64_t per_wave = (nchunks + kSmallWavesPerGroup - 1) / kSmallWavesPerGroup;
-    return (int)((M * per_wave * 16 + 63) / 64 * 64);
+    const int64_t r = (M * per_wave * 16 + 63) / 64 * 64;
+    return (int)(r > 64 * T ? r : 64 * T);
 }
-inline size_t small_lds_bytes(int64_t M, int64_t K) {
-    return (size_t)kSmallWavesPerGroup * small_region(M, K / 128) * 16;
+inline size_t small_lds_bytes(int64_t M, int64_t K, int T) {
+    return (size_t)kSmallWavesPerGroup * small_region(M, K / 128, T) * 16;
 }
 
 __device__ __forceinline__ bf16x8 decode_e2m1_bf16(uint32_t w) {
@@ -241,13 +243,13 @@ constexpr int kSmallChunks = 4;  // K chunks per wavefront per batch
 // W8 = 4 / 5: OCP FP8 E4M3 / E5M2 weights, one byte per code: a lane's 32 codes of a
 // chunk are two 16-byte loads, converted to bf16 with the gfx950 FP8 converts (exact).
 // W8 = 2 / 3: OCP FP6 E2M3 / E3M2 weights, a bit stream of 6-bit codes: a lane's 32
-// codes are 24 bytes (three 8-byte loads), converted at once by the 32-value FP6
+// codes are 24 bytes (a 16-byte and an 8-byte load, which the compiler cannot merge or
+// split, so the wait counts below stay exact), converted at once by the 32-value FP6
 // converts (exact).
 template <int MODE, bool SF16, bool SV, int T, bool TWO = false, int W8 = 0>  // MODE 0 tensor, 1 row, 2 group of 128
 __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParams p) {
     constexpr int NW = kSmallWaves, CH = kSmallChunks;
     extern __shared__ uint4 xs[];  // per wavefront: [M][its K range / 8] bf16 vectors
-    __shared__ f32x4 part[NW - 1][T][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int q = lane >> 4, r16 = lane & 15;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * T;
@@ -258,7 +260,7 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
     // wavefront with an empty range still forms valid addresses)
     const int nvw = c_end - c_begin > 0 ? (c_end - c_begin) * 16 : 16;
     const int xw = (int)p.M * nvw;
-    const int region = small_region(p.M, nchunks);
+    const int region = small_region(p.M, nchunks, T);
     const int wbase = wave * region;
     const int64_t ngroups = MODE == 2 ? p.K / 128 : 1;
     constexpr int SB = SF16 ? 2 : 4;       // bytes per scale
@@ -291,7 +293,8 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
     // 2. a batch of weights and scales; chunks past the range are loaded too (they
     //    belong to the next range or read zeros) and contribute nothing
     uint4 wv[CH][T], wv2[CH][T];  // wv2: the second 16 bytes of FP8 codes
-    uint2 w6[CH][T][3];           // FP6: 24 bytes
+    uint4 w6a[CH][T];             // FP6: bytes 0..15 of 24
+    uint2 w6b[CH][T];             // FP6: bytes 16..23
     uint4 sv[T];
     uint32_t sc[CH][T];
     auto load_batch = [&](int cs) {
@@ -311,10 +314,9 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
 #pragma unroll
             for (int t = 0; t < T; t++) {
                 if (W8 == 2 || W8 == 3) {
-#pragma unroll
-                    for (int h = 0; h < 3; h++)
-                        w6[b][t][h] = __builtin_bit_cast(
-                            uint2, __builtin_amdgcn_raw_buffer_load_b64(rsW, wrow[t] + (uint32_t)(cs + b) * 96 + 8 * h, 0, 0));
+                    w6a[b][t] = buf_load16(rsW, wrow[t] + (uint32_t)(cs + b) * 96);
+                    w6b[b][t] = __builtin_bit_cast(
+                        uint2, __builtin_amdgcn_raw_buffer_load_b64(rsW, wrow[t] + (uint32_t)(cs + b) * 96 + 16, 0, 0));
                 } else {
                     wv[b][t] = buf_load16(rsW, wrow[t] + (uint32_t)(cs + b) * (W8 ? 128 : 64));
                     if (W8) wv2[b][t] = buf_load16(rsW, wrow[t] + (uint32_t)(cs + b) * 128 + 16);
@@ -329,7 +331,7 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
     };
     load_batch(c_begin);
     // 3. the X loads are the oldest in flight: wait until only the batch's loads remain
-    constexpr int kLater = CH * T * (W8 >= 4 ? 2 : W8 ? 3 : 1) + (MODE == 2 ? (SV ? T : CH * T) : 0);
+    constexpr int kLater = CH * T * (W8 ? 2 : 1) + (MODE == 2 ? (SV ? T : CH * T) : 0);
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kLater) : "memory");
 
     const int xrow = wbase + (r16 < p.M ? r16 : (int)p.M - 1) * nvw - c_begin * 16;
@@ -362,8 +364,7 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
                 bf16x32 w32;
                 if (W8 == 2 || W8 == 3) {
                     typedef unsigned v6u __attribute__((ext_vector_type(6)));
-                    const v6u src = v6u{w6[b][t][0].x, w6[b][t][0].y, w6[b][t][1].x, w6[b][t][1].y, w6[b][t][2].x,
-                                        w6[b][t][2].y};
+                    const v6u src = v6u{w6a[b][t].x, w6a[b][t].y, w6a[b][t].z, w6a[b][t].w, w6b[b][t].x, w6b[b][t].y};
                     if (W8 == 2) w32 = __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(src, 1.0f);
                     else w32 = __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(src, 1.0f);
                 }
@@ -417,7 +418,8 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
 #pragma unroll
             for (int i = 0; i < 4; i++) total[t][i] = total[t][i] * s;
         }
-        if (wave > 0) part[wave - 1][t][lane] = total[t];
+        // partial sums into this wavefront's own region (its X is no longer read)
+        if (wave > 0) xs[wbase + t * 64 + lane] = __builtin_bit_cast(uint4, total[t]);
     }
     __syncthreads();
     if (wave == 0) {
@@ -425,7 +427,7 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
         for (int t = 0; t < T; t++) {
 #pragma unroll
             for (int w = 0; w < NW - 1; w++) {
-                const f32x4 o = part[w][t][lane];
+                const f32x4 o = __builtin_bit_cast(f32x4, xs[(w + 1) * region + t * 64 + lane]);
 #pragma unroll
                 for (int i = 0; i < 4; i++) total[t][i] += o[i];
             }
@@ -446,7 +448,7 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
 
 template <int MODE, bool SF16, bool SV, int T, bool TWO = false, int W8 = 0>
 static hipError_t launch_small_t(const GemmParams& p, hipStream_t s) {
-    const size_t lds = small_lds_bytes(p.M, p.K);
+    const size_t lds = small_lds_bytes(p.M, p.K, T);
     auto kern = w4a16_small_kernel<MODE, SF16, SV, T, TWO, W8>;
     // the dynamic-LDS limit is a kernel attribute, set once per device
     static bool attr_set[64];
@@ -485,7 +487,7 @@ static hipError_t launch_small(const GemmParams& p, hipStream_t s) {
 static bool small_fits(const GemmParams& p) {
     const int64_t ngroups = p.w_mode == 2 ? p.K / 128 : 1;
     const int64_t sbytes = p.w_scale_f16 ? 2 : 4;
-    return p.M <= 16 && (p.w_mode != 2 || p.w_group == 128) && small_lds_bytes(p.M, p.K) <= kSmallMaxLds &&
+    return p.M <= 16 && (p.w_mode != 2 || p.w_group == 128) && small_lds_bytes(p.M, p.K, 4) <= kSmallMaxLds &&
            // 32-bit buffer offsets
            p.N * p.ldw < kOOB && p.N * ngroups * sbytes < kOOB && ((p.M - 1) * p.lda + p.K) * 2 < (int64_t)kOOB;
 }
