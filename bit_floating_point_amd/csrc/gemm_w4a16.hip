@@ -331,7 +331,10 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
     };
     load_batch(c_begin);
     // 3. the X loads are the oldest in flight: wait until only the batch's loads remain
-    constexpr int kLater = CH * T * (W8 ? 2 : 1) + (MODE == 2 ? (SV ? T : CH * T) : 0);
+    // Counted as the fewest instructions the compiler can make of the batch: the 16-byte
+    // weight loads (FP6: 16 + 8 bytes) cannot be merged, but a tile's CH adjacent scale
+    // loads can become one; counting too few only waits for some batch loads as well.
+    constexpr int kLater = CH * T * (W8 ? 2 : 1) + (MODE == 2 ? T : 0);
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kLater) : "memory");
 
     const int xrow = wbase + (r16 < p.M ? r16 : (int)p.M - 1) * nvw - c_begin * 16;
