@@ -146,10 +146,10 @@ TRAFFIC_KERNELS = [
     ("gemv_m4", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 1, false, 0>", (3, 6)),
     ("gemv_m16", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 3, false, 0>", (0, 3)),
     ("quantize_act", "quant.hip", "quantize_e2m1_tensor_kernel<true, true, 256>", (0, 3)),
-    ("w4a4_c3", "gemm_w4a4.hip", "w4a4_fp4_kernel<128, 128, false>", (0, 3)),
-    ("w4a4_qkv", "gemm_w4a4.hip", "w4a4_fp4_kernel<256, 256, false>", (0, 3)),
+    ("w4a4_c3", "gemm_w4a4.hip", "w4a4_fp4_kernel<128, 128, false, 0>", (0, 3)),
+    ("w4a4_qkv", "gemm_w4a4.hip", "w4a4_fp4_kernel<256, 256, false, 0>", (0, 3)),
     ("nf4_qkv", "gemm_lut.hip", "w4a4_lut_kernel<256, 256, false>", (0, 3)),
-    ("swiglu", "gemm_w4a4.hip", "w4a4_fp4_kernel<256, 256, true>", (0, 3)),
+    ("swiglu", "gemm_w4a4.hip", "w4a4_fp4_kernel<256, 256, true, 0>", (0, 3)),
 ]
 COPY_BYTES = 256 * 1024 * 1024  # the reference device copy of profile_run
 
