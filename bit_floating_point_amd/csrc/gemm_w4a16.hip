@@ -11,11 +11,13 @@
 // partial sum is kept apart and multiplied by its scale in fp32 before it joins the
 // total; the wavefront partials are combined through LDS in a fixed order.
 //  * w4a16_small_kernel (M <= 16, the decode case): activations staged in LDS per
-//    wavefront, all of a batch's weight loads in flight at once.
+//    wavefront, all of a batch's weight loads in flight at once.  Its variants also
+//    take two-mode weights (E2M1 or E1M2 per group, by the scale's sign bit) and the
+//    OCP FP8 / FP6 weights (W8A16 / W6A16), each decoded exactly to bf16.
 //  * w4a16_mfma_kernel (any M, 16-row tiles along M): activation fragments loaded
 //    straight from memory, for shapes the small kernel does not take.
 //
-// A third, plain VALU kernel covers f32 activations and the other grids.
+// A third, plain VALU kernel covers f32 activations and the other grids and shapes.
 #include "fp4_device.h"
 
 namespace fp4 {

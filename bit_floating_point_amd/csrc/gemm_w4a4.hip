@@ -16,6 +16,10 @@
 // unit loops over tiles; the load ring runs on across tile boundaries, so the next
 // tile's first steps load while the last ones of the current tile are computed and
 // while its epilogue writes its outputs.
+//
+// The same kernel also runs the LLaMA MLP's gate/up pair with SwiGLU and the next
+// layer's E2M1 quantization in the epilogue (GLU), and the FP8 E4M3 x E4M3 product
+// (F8: one code per byte, 64-code steps; fp32 sums not exact, so held to a tolerance).
 #include <algorithm>
 
 #include "fp4_device.h"

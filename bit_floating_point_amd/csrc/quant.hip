@@ -4,7 +4,10 @@
 //   scale and clip (eqs. (2)-(3)): s = amax / Qmax, y = x * (1/s) clipped to +-Qmax;
 //   compare and quantize (eq. (5)): nearest grid point, ties to the even code;
 //   pre-shifted exponent bias: per-channel maxima -> per-tensor a times 2^k.
-// Two 4-bit codes per byte ("为什么我们需要4-bit浮点量化" page, section 2.2).
+// Two 4-bit codes per byte ("为什么我们需要4-bit浮点量化" page, section 2.2).  Also the
+// two-mode grid ("HiFloat4格式" page, section 2.1: E2M1 or E1M2 per group, one control
+// bit) and the OCP FP8 / FP6 grids (the FP8 key layers and 8/6/4-bit precision of the
+// [FP4-LLM] page), one code per byte or four codes in three bytes.
 //
 // Memory path: every thread owns 8 consecutive elements of a row (one 16-byte load
 // for bf16, two for f32) and writes their 4 packed bytes with one 32-bit store, so a
