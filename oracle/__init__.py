@@ -642,7 +642,9 @@ def gemm_w4a4(a_packed, a_grid: Grid, a_scale, w_packed, w_grid: Grid, mode: str
     A = _weight_values(a_packed, a_grid)
     V = _weight_values(w_packed, w_grid)
     N, K = V.shape
-    a = float(np.float32(a_scale))
+    # one activation scale, or one per row (token) of A ([Overview] per-token granularity)
+    a_arr = np.asarray(a_scale, dtype=np.float32).astype(np.float64)
+    a = a_arr.reshape(-1, 1) if a_arr.size > 1 else float(a_arr.reshape(-1)[0])
     s = np.asarray(w_scales).astype(np.float64)
     if mode in ("tensor", "row"):
         acc = A @ V.T
@@ -659,9 +661,13 @@ def gemm_w4a4(a_packed, a_grid: Grid, a_scale, w_packed, w_grid: Grid, mode: str
 
 def w4a4_epilogue_f32(acc, a_scale, s_row) -> np.ndarray:
     """Fixed epilogue of the row-scaled minifloat W4A4 product, used where the result
-    is compared bit for bit: y32 = fl32(acc * fl32(a * s_n))."""
-    a = np.float32(a_scale)
-    sn = (a * f32(s_row)).astype(np.float32)
+    is compared bit for bit: y32 = fl32(acc * fl32(a * s_n)); with one activation scale
+    per token, y32[m, n] = fl32(acc * fl32(a_m * s_n))."""
+    a = f32(a_scale)
+    if a.size > 1:
+        mult = (a.reshape(-1, 1) * f32(s_row).reshape(1, -1)).astype(np.float32)
+        return (f32(acc) * mult).astype(np.float32)
+    sn = (np.float32(a.reshape(-1)[0]) * f32(s_row)).astype(np.float32)
     return (f32(acc) * sn[None, :]).astype(np.float32)
 
 

@@ -659,3 +659,27 @@ def test_fp6_grids_and_packing():
     v = 63 | 0 << 6 | 32 << 12 | 5 << 18
     assert packed[0, 3:].tolist() == [v & 255, (v >> 8) & 255, v >> 16]
     assert np.array_equal(O.unpack_codes(packed, g23), codes)
+
+
+# ---- per-token activation scales in the W4A4 product ---------------------------------
+def test_w4a4_per_token_scales():
+    """With one scale per token the product is the per-tensor one row by row: equal
+    scales reproduce the per-tensor result bit for bit, and power-of-two scales scale
+    each output row exactly."""
+    rng = np.random.default_rng(51)
+    e2 = O.minifloat(2, 1)
+    ap = rng.integers(0, 256, (6, 64), dtype=np.uint8)
+    wp = rng.integers(0, 256, (5, 64), dtype=np.uint8)
+    ws = rng.uniform(0.5, 2.0, 5).astype(np.float32)
+    r1, acc = O.gemm_w4a4(ap, e2, np.float32(0.75), wp, e2, "row", ws)
+    rr, _ = O.gemm_w4a4(ap, e2, np.full(6, 0.75, np.float32), wp, e2, "row", ws)
+    assert np.array_equal(r1, rr)
+    y1 = O.w4a4_epilogue_f32(acc, np.float32(0.75), ws)
+    assert np.array_equal(O.w4a4_epilogue_f32(acc, np.full(6, 0.75, np.float32), ws), y1)
+    p2 = (2.0 ** np.arange(-3, 3)).astype(np.float32)
+    rp, _ = O.gemm_w4a4(ap, e2, p2, wp, e2, "row", ws)
+    r_unit, _ = O.gemm_w4a4(ap, e2, np.float32(1.0), wp, e2, "row", ws)
+    assert np.array_equal(rp, r_unit * p2[:, None].astype(np.float64))
+    yp = O.w4a4_epilogue_f32(acc, p2, ws)
+    yu = O.w4a4_epilogue_f32(acc, np.float32(1.0), ws)
+    assert np.array_equal(yp, (yu * p2[:, None]).astype(np.float32))
