@@ -265,6 +265,7 @@ def fp4_gemm(a: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor, w_
     if a_grid is not None:
         d.a_grid = a_grid
     d.a_scale = a_scale.data_ptr() if a_scale is not None else None
+    d.a_scale_mode = FP4_SCALE_ROW if (a_scale is not None and a_scale.numel() > 1) else FP4_SCALE_TENSOR
     d.w = w_packed.data_ptr()
     d.ldw = _ld(w_packed)
     d.w_grid = w_grid

@@ -38,7 +38,7 @@ class fp4_search_result(ctypes.Structure):
 
 class fp4_gemm_desc(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
-                ("a_kind", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("a_kind", ctypes.c_int32), ("a_scale_mode", ctypes.c_int32),
                 ("a", ctypes.c_void_p), ("lda", ctypes.c_int64), ("a_grid", fp4_grid),
                 ("a_scale", ctypes.c_void_p),
                 ("w", ctypes.c_void_p), ("ldw", ctypes.c_int64), ("w_grid", fp4_grid),

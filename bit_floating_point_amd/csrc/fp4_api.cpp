@@ -380,7 +380,9 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
     if (!d->a || !d->w || !d->w_scales || !d->y) return fail(FP4_ERR_INVALID_ARG, "null pointer");
     if (d->ldw < d->K / 2 || d->ldy < d->N) return fail(FP4_ERR_INVALID_ARG, "bad leading dimensions");
     if (d->y_dtype != FP4_BF16 && d->y_dtype != FP4_F32) return fail(FP4_ERR_INVALID_ARG, "y_dtype must be BF16 or F32");
-    if (d->reserved0 || d->reserved1) return fail(FP4_ERR_INVALID_ARG, "reserved fields must be 0");
+    if (d->reserved1) return fail(FP4_ERR_INVALID_ARG, "reserved fields must be 0");
+    if (d->a_scale_mode != FP4_SCALE_TENSOR && d->a_scale_mode != FP4_SCALE_ROW)
+        return fail(FP4_ERR_INVALID_ARG, "a_scale_mode must be TENSOR or ROW");
     GemmParams p{};
     fp4_status st = make_grid(d->w_grid, &p.wg);
     if (st) return st;
@@ -392,6 +394,7 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
     p.a = d->a;
     p.lda = d->lda;
     p.a_scale = d->a_scale;
+    p.a_row = d->a_scale_mode == FP4_SCALE_ROW;
     p.w = d->w;
     p.ldw = d->ldw;
     p.w_mode = d->w_gran.mode;
@@ -407,6 +410,8 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
 
     if (p.wg.kind == 2 && (d->w_gran.mode != FP4_SCALE_GROUP || d->a_kind == FP4_PACKED))
         return fail(FP4_ERR_UNSUPPORTED, "two-mode weights need GROUP scales and f32/bf16 activations");
+    if (p.a_row && (d->a_kind != FP4_PACKED || !p.wg.is_e2m1))
+        return fail(FP4_ERR_UNSUPPORTED, "per-token activation scales are taken by the E2M1 x E2M1 product only");
     if (p.wg.bits == 8 && p.wg.e == 4 && d->a_kind == FP4_PACKED) {
         // W8A8: FP8 E4M3 activations and weights on the FP8 matrix cores
         QGrid qa;

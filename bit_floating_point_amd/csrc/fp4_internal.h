@@ -68,6 +68,7 @@ struct GemmParams {
     int64_t lda;
     QGrid ag;
     const float* a_scale;
+    int32_t a_row;        // packed activations: one scale per row (token) of A
     const uint8_t* w;
     int64_t ldw;
     QGrid wg;

@@ -442,6 +442,8 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
                 char* const ytile = reinterpret_cast<char*>(p.y) + ((m0 + wm * WM) * p.ldy + n0 + wn * WN) * 2;
     #pragma unroll
                 for (int i = 0; i < TM; i++) {
+                    // this lane's row's activation scale (one per token, or the tensor's)
+                    const float am = p.a_row ? p.a_scale[m0 + wm * WM + i * 32 + r32] : a_scale;
     #pragma unroll
                     for (int jh = 0; jh < 2; jh++) {
     #pragma unroll
@@ -451,7 +453,7 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
                                 const int j = jh * (TN / 2) + jj;
                                 float4 s4 = make_float4(s_tensor, s_tensor, s_tensor, s_tensor);
                                 if (p.w_mode == 1) s4 = *reinterpret_cast<const float4*>(&sc[wn * WN + j * 32 + 8 * g + 4 * hk]);
-                                const float f[4] = {a_scale * s4.x, a_scale * s4.y, a_scale * s4.z, a_scale * s4.w};
+                                const float f[4] = {am * s4.x, am * s4.y, am * s4.z, am * s4.w};
                                 __bf16 h4[4];
     #pragma unroll
                                 for (int t = 0; t < 4; t++) h4[t] = (__bf16)(agpr_read(acc[j][i][4 * g + t]) * f[t]);
@@ -489,11 +491,12 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
                                 s4.w = ws[n + 3 < p.N ? n + 3 : p.N - 1];
                             }
                         }
-                        const float f0 = a_scale * s4.x, f1 = a_scale * s4.y, f2 = a_scale * s4.z, f3 = a_scale * s4.w;
                         const bool vec = full && (p.ldy & 3) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
     #pragma unroll
                         for (int i = 0; i < TM; i++) {
                             const int64_t m = m0 + wm * WM + i * 32 + r32;
+                            const float am = p.a_row ? p.a_scale[m < p.M ? m : p.M - 1] : a_scale;
+                            const float f0 = am * s4.x, f1 = am * s4.y, f2 = am * s4.z, f3 = am * s4.w;
                             const float y0 = agpr_read(acc[j][i][4 * g]) * f0, y1 = agpr_read(acc[j][i][4 * g + 1]) * f1;
                             const float y2 = agpr_read(acc[j][i][4 * g + 2]) * f2, y3 = agpr_read(acc[j][i][4 * g + 3]) * f3;
                             if (p.y_bf16) {

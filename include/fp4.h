@@ -143,11 +143,13 @@ typedef struct {
     int64_t M, N, K;
     /* activations X [M, K] */
     int32_t a_kind;           /* FP4_F32, FP4_BF16 (W4A16) or FP4_PACKED (W4A4)      */
-    int32_t reserved0;
+    int32_t a_scale_mode;     /* PACKED: FP4_SCALE_TENSOR (one a) or FP4_SCALE_ROW    */
     const void* a;            /* device                                             */
     int64_t lda;              /* elements (F32/BF16) or bytes (PACKED)              */
     fp4_grid a_grid;          /* PACKED only: grid of the activation codes          */
-    const float* a_scale;     /* PACKED only: device pointer to the one f32 scale a */
+    const float* a_scale;     /* PACKED only: device f32, the one scale a, or with
+                                 a_scale_mode ROW one scale a_m per row (token) of X
+                                 ([Overview] per-token granularity; E2M1 x E2M1 only) */
     /* weights W [N, K], packed */
     const uint8_t* w;
     int64_t ldw;              /* bytes                                              */
@@ -285,7 +287,8 @@ fp4_status fp4_search_activations(const void* x, int32_t x_dtype, int64_t rows, 
  *                              (u = the scale units of w_gran along K), fp32 accumulate.
  *   W4A4  (a_kind PACKED):    Y[m,n] = a * sum_u s[n,u] * sum_{k in u} A_q[m,k] W_q[n,k]
  *     - E2M1 x E2M1 with TENSOR/ROW weight scales runs on the FP4 matrix cores; the
- *       code product is exact in fp32 and the epilogue is y = fl32(acc * fl32(a * s_n));
+ *       code product is exact in fp32 and the epilogue is y = fl32(acc * fl32(a * s_n))
+ *       (per-token activation scales: y = fl32(acc * fl32(a_m * s_n)));
  *       K <= 116508 (the quarter-integer partial sums stay below 2^22), else
  *       FP4_ERR_UNSUPPORTED.
  *     - E2M1 activations x LUT16 weights (NF4) with GROUP scales (group a multiple of

@@ -176,6 +176,14 @@ def test_gemm_validation():
     d.ldw = 128
     d.y_dtype = 7
     assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_INVALID_ARG
+    d.y_dtype = L.FP4_BF16
+    d.a_scale_mode = 5
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_INVALID_ARG
+    d.a_scale_mode = L.FP4_SCALE_ROW  # per-token activation scales: E2M1 x E2M1 only
+    d.w_grid, d.w_gran = _grid(1), _gran(2, 64)
+    for i in range(16):
+        d.w_grid.lut[i] = (i - 7.5) / 8
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED
 
 
 def test_swiglu_validation():

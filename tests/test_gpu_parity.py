@@ -409,6 +409,29 @@ def test_swiglu_quant_full_4096x13824x5120():
     assert np.array_equal(got[rows], codes)
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 520, 544), (2100, 2200, 1024), (4096, 5120, 512)])
+def test_w4a4_per_token_scales(M, N, K):
+    """Dynamic per-token activation quantization (E2M1, one scale per token) into the
+    W4A4 product with per-token scales: fp32 and bf16 outputs bit-exact."""
+    say("w4a4 per-token", M, N, K)
+    e2 = O.minifloat(2, 1)
+    x = synth.activations(16, M, M, K, outlier_frac=0.01, bf16=True)
+    w = synth.weight(16, N, N, K)
+    ap, asc = O.quantize_pack(x, e2, "row")
+    wp, ws = O.quantize_pack(w, e2, "row")
+    _, acc = O.gemm_w4a4(ap, e2, asc, wp, e2, "row", ws)
+    y_pin = O.w4a4_epilogue_f32(acc, asc, ws)
+    fe2 = F.grid_minifloat(2, 1)
+    # the activation codes and scales come from the library's own per-token quantizer
+    gap, gas = F.fp4_quantize_pack(dev(x, torch.bfloat16), fe2, F.gran("row"))
+    assert np.array_equal(host(gap), ap) and np.array_equal(host(gas), asc)
+    gwp, gws = torch.from_numpy(wp).to(DEV), dev(ws)
+    y32 = F.fp4_gemm(gap, gwp, gws, fe2, F.gran("row"), K=K, a_grid=fe2, a_scale=gas, y_dtype=torch.float32)
+    assert np.array_equal(host(y32).view(np.uint32), y_pin.view(np.uint32))
+    yb = F.fp4_gemm(gap, gwp, gws, fe2, F.gran("row"), K=K, a_grid=fe2, a_scale=gas, y_dtype=torch.bfloat16)
+    assert np.array_equal(host(yb.view(torch.int16)).view(np.uint16), O.rne_bf16_bits(y_pin))
+
+
 @pytest.mark.parametrize("M,N,K", [(256, 384, 512), (130, 200, 640)])
 def test_preshift_nf4(M, N, K):
     say("nf4", M, N, K)
