@@ -357,6 +357,24 @@ def bench_prefill(torch, F):
         qa[name] = True
         del w, wp, wpn, y
         torch.cuda.empty_cache()
+    # dynamic per-token activation quantization (E2M1, one scale per token) into the QKV
+    # product with per-token scales
+    n, k = PREFILL["qkv"]
+    w = gen_normal(torch, (n, k), 0.02, 600)
+    wp, ws = F.fp4_quantize_pack(w, fe2, F.gran("row"))
+    del w
+    apt, ast = F.fp4_quantize_pack(X1, fe2, F.gran("row"))
+    xb = T * k * 2 + T * k // 2 + T * 4
+    t = graph_time(torch, lambda i: F.fp4_quantize_pack(X1, fe2, F.gran("row"), packed=apt, scales=ast), 8)
+    out.append(roofline_entry(f"activation quantize E2M1 per-token ({T}x{k} bf16)", "hbm", xb / t / 1e9,
+                              HBM_PEAK_GBS, "GB/s", t, xb, "bytes"))
+    y = torch.empty((T, n), dtype=torch.bfloat16, device="cuda")
+    t = graph_time(torch, lambda i: F.fp4_gemm(apt, wp, ws, fe2, F.gran("row"), K=k, a_grid=fe2, a_scale=ast, y=y), 5)
+    fl = 2 * T * n * k
+    out.append(roofline_entry(f"w4a4 E2M1 GEMM qkv {T}x{n}x{k}, per-token activation scales", "mfma",
+                              fl / t / 1e12, FP4_PEAK_TFLOPS, "TFLOP/s", t, fl, "flop"))
+    del wp, y
+    torch.cuda.empty_cache()
     out.append(roofline_entry("prefill layer: 4 W4A4 E2M1 GEMMs (QKV, up, gate, down)", "mfma",
                               tot_fl / tot_t / 1e12, FP4_PEAK_TFLOPS, "TFLOP/s", tot_t, tot_fl, "flop"))
     out.append(roofline_entry("prefill layer: 4 NF4 GEMMs (QKV, up, gate, down)", "mfma",
