@@ -734,6 +734,49 @@ def test_fp8_w8a8_gemm(M, N, K, mode):
 
 
 # ---------------------------------------------------------------- determinism -----
+def test_graph_replays_match_eager():
+    """The library's calls captured in one HIP graph (calibrate, pre-shift, quantize,
+    W4A4, W4A16, the activation search with its zero-filled workspace) and replayed
+    several times with eager work in between: every replay equals the eager results."""
+    fe2 = F.grid_minifloat(2, 1)
+    x = dev(synth.activations(17, 1, 300, 1024, outlier_frac=0.01), torch.bfloat16)
+    w = dev(synth.weight(17, 1, 512, 1024))
+    ws = torch.empty(F._lib.lib().fp4_search_workspace_size(300, 1024, 3, 100), dtype=torch.uint8, device=DEV)
+    gpk = torch.empty((300, 512), dtype=torch.uint8, device=DEV)
+
+    def run():
+        c = F.fp4_calibrate(x, "column", first_rows=128)
+        k, a, wp, wsc = F.fp4_preshift_weights(w, c, fe2, fe2, F.gran("row"))
+        ap, _ = F.fp4_quantize_pack(x, fe2, F.gran("tensor"), tensor_scale=a, col_shift=k)
+        y = F.fp4_gemm(ap, wp, wsc, fe2, F.gran("row"), K=1024, a_grid=fe2, a_scale=a, y_dtype=torch.float32)
+        p16, s16 = F.fp4_quantize_pack(w, fe2, F.gran("group", 128, "f16"))
+        y16 = F.fp4_gemm(x[:4], p16, s16, fe2, F.gran("group", 128, "f16"), y_dtype=torch.float32)
+        res, _ = F.fp4_search_activations(x, "row", workspace=ws, packed=gpk)
+        return [y, y16, res, gpk]
+
+    eager = [t.clone() for t in run()]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = run()
+    for rep in range(4):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs, eager):
+            assert torch.equal(got, want), rep
+        run()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_repeat_runs_identical():
     x = synth.activations(3, 1, 256, 1024, outlier_frac=0.01)
     w = synth.weight(3, 1, 512, 1024)
