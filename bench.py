@@ -504,6 +504,29 @@ def bench_w8a8(torch, F):
                                   fl, "flop"))
         del X, W, ap, wp, y
         torch.cuda.empty_cache()
+    # W6A6 (FP6 E2M3 x E2M3, whose matrix-core rate is the FP4 one) and W8A8 with E5M2
+    # operands, on the tiled FP8/FP6 kernel; FP6 rows padded to 16-byte multiples
+    for (wf, peak, shapes) in (((2, 3), FP4_PEAK_TFLOPS, ((2048, 4096, 4096, "2048x4096x4096"),
+                                                           (4096, 15360, 5120, "qkv 4096x15360x5120"))),
+                               ((5, 2), FP8_PEAK_TFLOPS, ((2048, 4096, 4096, "2048x4096x4096"),))):
+        g = F.grid_minifloat(*wf)
+        label = "w6a6 FP6 E2M3" if wf == (2, 3) else "w8a8 FP8 E5M2"
+        for (M, N, K, name) in shapes:
+            X = gen_activations(torch, M, K, 500)
+            W = gen_normal(torch, (N, K), 0.02, 600)
+            row = K * (8 if sum(wf) == 7 else 6) // 8
+            ap = torch.empty((M, row), dtype=torch.uint8, device="cuda")
+            wp = torch.empty((N, row), dtype=torch.uint8, device="cuda")
+            _, asc = F.fp4_quantize_pack(X, g, F.gran("tensor"), packed=ap)
+            _, wsc = F.fp4_quantize_pack(W, g, F.gran("tensor"), packed=wp)
+            ws = wsc.expand(N).contiguous()
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            t = graph_time(torch, lambda i: F.fp4_gemm(ap, wp, ws, g, F.gran("row"), K=K, a_grid=g, a_scale=asc, y=y),
+                           5)
+            fl = 2 * M * N * K
+            out.append(roofline_entry(f"{label} GEMM {name}", "mfma", fl / t / 1e12, peak, "TFLOP/s", t, fl, "flop"))
+            del X, W, ap, wp, y
+            torch.cuda.empty_cache()
     return out
 
 

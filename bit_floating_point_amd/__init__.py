@@ -245,8 +245,8 @@ def fp4_gemm(a: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor, w_
              w_gran: L.fp4_gran, K: int | None = None, a_grid: L.fp4_grid | None = None,
              a_scale: torch.Tensor | None = None, y_dtype: torch.dtype = torch.bfloat16,
              y: torch.Tensor | None = None) -> torch.Tensor:
-    """Y = X W^T.  a: [M, K] f32/bf16 (W4A16) or packed uint8 [M, K/2] (W4A4, with
-    a_grid and a_scale)."""
+    """Y = X W^T.  a: [M, K] f32/bf16 (W4A16), or packed codes uint8 [M, K * bits / 8]
+    (W4A4, W8A8, W6A6, with a_grid and a_scale)."""
     M = a.shape[0]
     N = w_packed.shape[0]
     if a.dtype == torch.uint8:

@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libfp4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["quant.hip", "gemm_w4a16.hip", "gemm_w4a4.hip", "gemm_lut.hip", "search.hip", "fp4_api.cpp"]
+SOURCES = ["quant.hip", "gemm_w4a16.hip", "gemm_w4a4.hip", "gemm_lut.hip", "gemm_f8f6.hip", "search.hip", "fp4_api.cpp"]
 
 # -ffp-contract=off: no silent a*b+c fusion, so every rounding is the one written
 # (fused multiply-adds are explicit); packed-fp32 instructions are disabled.

@@ -1,6 +1,7 @@
 // Host layer of libfp4: argument validation (before any launch), grid tables, and
 // dispatch to the HIP kernels.  Every entry point of include/fp4.h is defined here.
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -412,21 +413,27 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
         return fail(FP4_ERR_UNSUPPORTED, "two-mode weights need GROUP scales and f32/bf16 activations");
     if (p.a_row && (d->a_kind != FP4_PACKED || !p.wg.is_e2m1))
         return fail(FP4_ERR_UNSUPPORTED, "per-token activation scales are taken by the E2M1 x E2M1 product only");
-    if (p.wg.bits == 8 && p.wg.e == 4 && d->a_kind == FP4_PACKED) {
-        // W8A8: FP8 E4M3 activations and weights on the FP8 matrix cores
+    if (p.wg.bits != 4 && d->a_kind == FP4_PACKED) {
+        // both operands FP8 / FP6 on the f8f6f4 matrix cores: E4M3 x E4M3 on the
+        // persistent kernel, every other pair (W6A6 among them) on the tiled one
         QGrid qa;
         if ((st = make_grid(d->a_grid, &qa))) return st;
-        if (!(qa.bits == 8 && qa.e == 4)) return fail(FP4_ERR_UNSUPPORTED, "FP8 weights with packed activations need E4M3 x E4M3");
+        if (qa.bits != 8 && qa.bits != 6)
+            return fail(FP4_ERR_UNSUPPORTED, "FP8 / FP6 weights with packed activations need FP8 / FP6 activations");
         if (!d->a_scale) return fail(FP4_ERR_INVALID_ARG, "packed activations need a_scale");
-        if (d->lda < d->K || d->ldw < d->K || d->lda % 16 != 0)
-            return fail(FP4_ERR_ALIGNMENT, "FP8 rows: lda, ldw >= K and multiples of 16");
         if (d->K % 32 != 0) return fail(FP4_ERR_UNSUPPORTED, "K must be a multiple of 32");
+        if (d->lda < d->K * qa.bits / 8 || d->ldw < d->K * p.wg.bits / 8 || d->lda % 16 != 0)
+            return fail(FP4_ERR_ALIGNMENT, "FP8 / FP6 rows: lda, ldw >= the code bytes of a row, lda a multiple of 16");
         if (d->w_gran.mode == FP4_SCALE_GROUP || d->w_gran.scale_dtype != FP4_F32)
-            return fail(FP4_ERR_UNSUPPORTED, "W8A8 needs f32 TENSOR or ROW weight scales");
-        return hip_status(launch_w8a8_fp8(p, s), "fp4_gemm/w8a8");
+            return fail(FP4_ERR_UNSUPPORTED, "FP8 / FP6 products need f32 TENSOR or ROW weight scales");
+        p.ag = qa;
+        if (p.wg.bits == 8 && p.wg.e == 4 && qa.bits == 8 && qa.e == 4)
+            return hip_status(launch_w8a8_fp8(p, s), "fp4_gemm/w8a8");
+        if (256 * std::max(d->lda, d->ldw) >= 0x7fff0000)
+            return fail(FP4_ERR_UNSUPPORTED, "FP8 / FP6 rows longer than 8 MiB are not supported");
+        return hip_status(launch_f8f6_gemm(p, s), "fp4_gemm/f8f6");
     }
     if (p.wg.bits != 4) {
-        if (d->a_kind == FP4_PACKED) return fail(FP4_ERR_UNSUPPORTED, "FP8 E5M2 / FP6 weights take f32/bf16 activations");
         if (d->ldw < d->K * p.wg.bits / 8) return fail(FP4_ERR_INVALID_ARG, "ldw below the code bytes of a row");
         if (p.wg.bits == 6 && d->K % 4 != 0) return fail(FP4_ERR_INVALID_ARG, "FP6 rows hold whole groups of four codes");
     }

@@ -86,6 +86,9 @@ hipError_t launch_w4a16_two_mode(const GemmParams& p, hipStream_t s);  // M <= 1
 hipError_t launch_w8a16_small(const GemmParams& p, hipStream_t s);     // FP8 weights, M <= 16, bf16
 hipError_t launch_w4a4_fp4(const GemmParams& p, hipStream_t s);
 hipError_t launch_w8a8_fp8(const GemmParams& p, hipStream_t s);  // FP8 E4M3 x E4M3
+// every other pair of FP8 (E4M3, E5M2) / FP6 (E2M3, E3M2) operands, W6A6 among them
+int f8f6_format_code(const QGrid& g);  // MFMA operand format, or -1
+hipError_t launch_f8f6_gemm(const GemmParams& p, hipStream_t s);
 hipError_t launch_w4a4_lut(const GemmParams& p, hipStream_t s);
 // W4A4 gate/up products with SwiGLU and the next layer's activation quantization in
 // the epilogue: p.w / p.w_scales are the gate weights and row scales, p.y the E2M1 codes

@@ -299,11 +299,14 @@ fp4_status fp4_search_activations(const void* x, int32_t x_dtype, int64_t rows, 
  *       norm) of the exact value; groups whose scale is below 2^-14 of their row's
  *       largest lose relative precision to f16 subnormals.
  *   y_dtype FP4_BF16 rounds the f32 result to nearest-even.
- *   FP8 / FP6 weights take the W4A16 path (W8A16 / W6A16): ldw >= K (FP8) or 3K/4
- *   (FP6) bytes.  W8A8: PACKED activations with a_grid FP8 E4M3 and E4M3 weights with
- *   f32 TENSOR/ROW scales run on the FP8 matrix cores, y = fl32(acc * fl32(a * s_n)),
- *   acc summed in fp32 (not exact for FP8: within the GEMM tolerance); lda, ldw >= K,
- *   K a multiple of 32.
+ *   FP8 / FP6 weights with F32/BF16 activations take the W4A16 path (W8A16 / W6A16):
+ *   ldw >= K (FP8) or 3K/4 (FP6) bytes.  With PACKED activations both operands are FP8
+ *   (E4M3, E5M2) or FP6 (E2M3, E3M2), in any pairing (W8A8, W6A6, mixed), on the
+ *   f8f6f4 matrix cores with f32 TENSOR/ROW weight scales and one activation scale:
+ *   y = fl32(acc * fl32(a * s_n)), acc summed in fp32 (not exact: within the GEMM
+ *   tolerance); lda, ldw >= the code bytes of a row (K or 3K/4), lda a multiple of 16,
+ *   K a multiple of 32, rows shorter than 8 MiB.  Packed E2M1 activations with FP8 /
+ *   FP6 weights: FP4_ERR_UNSUPPORTED.
  *   Two-mode weights (FP4_GRID_TWO_MODE, GROUP scales) take the W4A16 path only: each
  *   group's codes are read on its own grid (the sign of its scale) and scaled by |s|.
  * Strides: K a multiple of 32 for the matrix-core paths; packed rows 16-byte aligned. */

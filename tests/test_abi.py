@@ -258,7 +258,21 @@ def test_fp8_validation():
     d.a_grid, d.w_grid = _grid(), g8
     d.w_gran = _gran(1)
     d.y_dtype = L.FP4_BF16
-    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # FP8 weights with packed activations
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # FP8 weights with packed E2M1 activations
+    # W6A6 (FP6 E2M3 x FP6 E2M3): rows of 256 codes are 192 bytes
+    g6 = _grid(0, 2, 3)
+    d.a_grid, d.w_grid, d.lda, d.ldw = g6, g6, 192, 192
+    d.K = 240
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # K not a multiple of 32
+    d.K, d.lda = 256, 176
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_ALIGNMENT  # lda below a row's code bytes
+    d.lda, d.w_gran = 192, _gran(2, 32)
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # GROUP weight scales
+    d.w_gran, d.a_scale = _gran(1), 0
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_INVALID_ARG  # no activation scale
+    d.a_scale, d.a_grid = 0x50000, _grid(0, 3, 4)
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # E3M4 is no grid
+    d.a_grid, d.w_grid, d.lda, d.ldw = g6, g8, 192, 256
     d.a_kind, d.lda, d.ldw = L.FP4_BF16, 256, 128
     assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_INVALID_ARG  # ldw < K
 

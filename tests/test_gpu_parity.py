@@ -733,6 +733,46 @@ def test_fp8_w8a8_gemm(M, N, K, mode):
     assert np.array_equal(host(yb.view(torch.int16)).view(np.uint16), O.rne_bf16_bits(y32))
 
 
+def _padded_rows(packed, align=16):
+    """uint8 rows copied into a device buffer whose row stride is a multiple of `align`
+    bytes (the packed products need 16-byte aligned rows), returned as the [:, :bytes] view."""
+    R, B = packed.shape
+    ld = (B + align - 1) // align * align
+    buf = torch.zeros((R, ld), dtype=torch.uint8, device=DEV)
+    buf[:, :B] = torch.from_numpy(np.ascontiguousarray(packed)).to(DEV)
+    return buf[:, :B]
+
+
+@pytest.mark.parametrize("M,N,K,wf,af,mode", [
+    (300, 520, 544, (2, 3), (2, 3), "row"),     # W6A6 E2M3: ragged tiles, a half-filled last FP6 piece
+    (2100, 2200, 1024, (3, 2), (3, 2), "row"),  # W6A6 E3M2, several tile rows and columns
+    (4096, 5120, 4096, (2, 3), (2, 3), "tensor"),
+    (256, 384, 512, (5, 2), (5, 2), "row"),     # W8A8 with E5M2
+    (300, 520, 544, (4, 3), (2, 3), "row"),     # mixed: FP8 E4M3 weights, FP6 E2M3 activations
+    (130, 270, 96, (2, 3), (5, 2), "tensor"),   # mixed: FP6 weights, FP8 E5M2 activations; K below one step
+])
+def test_f8f6_gemm(M, N, K, wf, af, mode):
+    """Both operands FP8 / FP6 (every pair other than E4M3 x E4M3, which the W8A8 test
+    covers) on the f8f6f4 matrix cores: within the GEMM tolerance of the binary64
+    oracle; bf16 output the nearest-even rounding of the fp32 output."""
+    say("f8f6", M, N, K, wf, af, mode)
+    og_w, og_a = _wide(wf), _wide(af)
+    x = synth.activations(16, M, M, K, outlier_frac=0.01)
+    w = synth.weight(16, N, N, K)
+    ap, asc = O.quantize_pack(x, og_a, "tensor")
+    wp, wsc = O.quantize_pack(w, og_w, mode)
+    r, _ = O.gemm_w4a4(ap, og_a, asc[0], wp, og_w, mode, wsc)
+    fw, fa = F.grid_minifloat(*wf), F.grid_minifloat(*af)
+    gap, gwp = _padded_rows(ap), _padded_rows(wp)
+    ga, gws = dev(np.asarray(asc, np.float32)), dev(np.asarray(wsc, np.float32))
+    y32 = host(F.fp4_gemm(gap, gwp, gws, fw, F.gran(mode), K=K, a_grid=fa, a_scale=ga, y_dtype=torch.float32))
+    err = O.rel_err(y32, r)
+    say("  rel err", err)
+    assert err <= TOL
+    yb = F.fp4_gemm(gap, gwp, gws, fw, F.gran(mode), K=K, a_grid=fa, a_scale=ga, y_dtype=torch.bfloat16)
+    assert np.array_equal(host(yb.view(torch.int16)).view(np.uint16), O.rne_bf16_bits(y32))
+
+
 # ---------------------------------------------------------------- determinism -----
 def test_graph_replays_match_eager():
     """The library's calls captured in one HIP graph (calibrate, pre-shift, quantize,
