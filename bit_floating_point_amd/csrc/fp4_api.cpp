@@ -189,9 +189,8 @@ fp4_status fp4_quantize_pack(const void* x, int32_t x_dtype, int64_t rows, int64
     if ((st = check_gran(gran, cols))) return st;
     if (q.bits != 4) {
         if (ldp < cols * q.bits / 8) return fail(FP4_ERR_INVALID_ARG, "ldp below the code bytes of a row (cols * bits / 8)");
-        if (gran.mode == FP4_SCALE_ROW || col_shift || cols % 8 != 0 || (q.bits == 6 && ldp % 2 != 0))
-            return fail(FP4_ERR_UNSUPPORTED,
-                        "FP8/FP6 quantization takes TENSOR or GROUP scales, no column shifts, cols % 8 == 0 (FP6: ldp even)");
+        if (col_shift || cols % 8 != 0 || (q.bits == 6 && ldp % 2 != 0))
+            return fail(FP4_ERR_UNSUPPORTED, "FP8/FP6 quantization takes no column shifts, cols % 8 == 0 (FP6: ldp even)");
     }
     if (q.kind == 2 && (gran.mode != FP4_SCALE_GROUP || col_shift))
         return fail(FP4_ERR_UNSUPPORTED, "the two-mode grid needs GROUP scales and no column shifts");

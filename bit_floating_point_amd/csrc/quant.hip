@@ -250,6 +250,37 @@ __global__ void __launch_bounds__(kThreads) quantize_chunk_kernel(QuantParams p,
     }
 }
 
+// the 8 codes of y = fl32(v * r) at columns col .. col + 7 of a row on an FP8 grid (8
+// bytes) or an FP6 grid (6 bytes as three 16-bit words; cols is a multiple of 8, so a
+// lane's 6 bytes are whole)
+template <bool VEC, int E, int M>
+__device__ __forceinline__ void store_wide8(const QuantParams& p, int64_t row, int64_t col, const float v[8], float r) {
+    if (E + M == 7) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            lo |= wide_code<E, M>(v[k] * r) << (8 * k);
+            hi |= wide_code<E, M>(v[k + 4] * r) << (8 * k);
+        }
+        if (col < p.cols) {
+            uint8_t* dst = p.packed + row * p.ldp + col;
+            if (VEC) *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+            else
+                for (int k = 0; k < 8 && col + k < p.cols; k++) dst[k] = (uint8_t)((k < 4 ? lo : hi) >> (8 * (k & 3)));
+        }
+    } else {
+        uint64_t bits = 0;
+#pragma unroll
+        for (int k = 0; k < 8; k++) bits |= (uint64_t)wide_code<E, M>(v[k] * r) << (6 * k);
+        if (col < p.cols) {
+            uint16_t* dst = reinterpret_cast<uint16_t*>(p.packed + row * p.ldp + col / 8 * 6);
+            dst[0] = (uint16_t)bits;
+            dst[1] = (uint16_t)(bits >> 16);
+            dst[2] = (uint16_t)(bits >> 32);
+        }
+    }
+}
+
 // TENSOR and GROUP modes with an OCP 8-bit (one code per byte) or 6-bit (a bit stream,
 // four codes in three bytes) grid: the same units and scales as quantize_chunk_kernel,
 // codes by wide_code; a lane stores its 8 codes as 8 bytes or as three 16-bit words.
@@ -289,30 +320,7 @@ __global__ void __launch_bounds__(kThreads) quantize_wide_kernel(QuantParams p, 
             r = recip_or_zero(s);
             if (col[i] < p.cols && (threadIdx.x & (lanes - 1)) == 0 && p.scales_out) store_scale(p, unit, s);
         }
-        if (E + M == 7) {
-            uint32_t lo = 0, hi = 0;
-#pragma unroll
-            for (int k = 0; k < 4; k++) {
-                lo |= wide_code<E, M>(v[k] * r) << (8 * k);
-                hi |= wide_code<E, M>(v[k + 4] * r) << (8 * k);
-            }
-            if (col[i] < p.cols) {
-                uint8_t* dst = p.packed + row[i] * p.ldp + col[i];
-                if (VEC) *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-                else
-                    for (int k = 0; k < 8 && col[i] + k < p.cols; k++) dst[k] = (uint8_t)((k < 4 ? lo : hi) >> (8 * (k & 3)));
-            }
-        } else {
-            uint64_t bits = 0;
-#pragma unroll
-            for (int k = 0; k < 8; k++) bits |= (uint64_t)wide_code<E, M>(v[k] * r) << (6 * k);
-            if (col[i] < p.cols) {  // cols is a multiple of 8: a lane's 6 bytes are whole
-                uint16_t* dst = reinterpret_cast<uint16_t*>(p.packed + row[i] * p.ldp + col[i] / 8 * 6);
-                dst[0] = (uint16_t)bits;
-                dst[1] = (uint16_t)(bits >> 16);
-                dst[2] = (uint16_t)(bits >> 32);
-            }
-        }
+        store_wide8<VEC, E, M>(p, row[i], col[i], v, r);
     }
 }
 
@@ -555,6 +563,42 @@ __global__ void __launch_bounds__(kThreads) quantize_row_kernel(QuantParams p) {
     }
 }
 
+// ROW mode on an FP8 / FP6 grid: one workgroup per row, the row's amax (or amax_in[row])
+// in a first pass, s = amax / Qmax (binary16-rounded for f16 scales), then the codes of
+// y = fl32(x * fl32(1/s)) in a second pass, as the 4-bit row kernel does.
+template <bool VEC, bool BF16, int E, int M>
+__global__ void __launch_bounds__(kThreads) quantize_wide_row_kernel(QuantParams p) {
+    __shared__ float red[kThreads / 64];
+    const int64_t row = blockIdx.x;
+    const char* rp = reinterpret_cast<const char*>(p.x) + row * p.ldx * (BF16 ? 2 : 4);
+    float amax;
+    if (p.amax_in) {
+        amax = p.amax_in[row];
+    } else {
+        float m = 0.0f;
+        for (int64_t c0 = 0; c0 < p.cols; c0 += kChunk) {
+            float v[8];
+            load8<VEC, BF16>(rp, c0 + threadIdx.x * 8, p.cols, v);
+            m = fmaxf(m, max_abs8(v));
+        }
+        m = dpp_wave_max(m);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    }
+    float s = amax / p.g.qmax;
+    if (p.scale_f16) s = round_f16(s);
+    const float r = recip_or_zero(s);
+    if (threadIdx.x == 0 && p.scales_out) store_scale(p, row, s);
+    for (int64_t c0 = 0; c0 < p.cols; c0 += kChunk) {
+        const int64_t col = c0 + threadIdx.x * 8;
+        if (col >= p.cols) continue;
+        float v[8];
+        load8<VEC, BF16>(rp, col, p.cols, v);
+        store_wide8<VEC, E, M>(p, row, col, v, r);
+    }
+}
+
 __global__ void tensor_scale_finalize_kernel(const float* amax, float* scales_out, float qmax) {
     scales_out[0] = amax[0] / qmax;
 }
@@ -567,7 +611,13 @@ hipError_t launch_tensor_scale_finalize(const float* amax, float* scales_out, fl
 template <bool VEC, bool BF16>
 static void quantize_launch(const QuantParams& p, hipStream_t s) {
     constexpr int QT = 256;  // threads of the E2M1 group-128 kernel
-    if (p.mode == 1) {
+    if (p.mode == 1 && p.g.bits != 4) {
+        dim3 grid((unsigned)p.rows);
+        if (p.g.e == 4) hipLaunchKernelGGL((quantize_wide_row_kernel<VEC, BF16, 4, 3>), grid, dim3(kThreads), 0, s, p);
+        else if (p.g.e == 5) hipLaunchKernelGGL((quantize_wide_row_kernel<VEC, BF16, 5, 2>), grid, dim3(kThreads), 0, s, p);
+        else if (p.g.e == 2) hipLaunchKernelGGL((quantize_wide_row_kernel<VEC, BF16, 2, 3>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((quantize_wide_row_kernel<VEC, BF16, 3, 2>), grid, dim3(kThreads), 0, s, p);
+    } else if (p.mode == 1) {
         dim3 grid((unsigned)p.rows);
         if (p.cols <= 4 * kChunk) hipLaunchKernelGGL((quantize_row_reg_kernel<VEC, BF16, 4>), grid, dim3(kThreads), 0, s, p);
         else if (p.cols <= 8 * kChunk) hipLaunchKernelGGL((quantize_row_reg_kernel<VEC, BF16, 8>), grid, dim3(kThreads), 0, s, p);

@@ -78,8 +78,8 @@ typedef int32_t fp4_status;
  *   ([FP4-LLM] progressive 8/6/4 bits): (2, 3) E2M3 (bias 1, largest 7.5) or (3, 2)
  *   E3M2 (bias 3, largest 28), no reserved code; codes form a little-endian bit
  *   stream, code i in bits [6i, 6i+6) of its row (3 cols / 4 bytes; cols a multiple
- *   of 4).  FP8/FP6 take TENSOR or GROUP scales in quantize/dequantize (cols a
- *   multiple of 8) and the W4A16 product (W8A16 / W6A16); codes are the nearest
+ *   of 4).  FP8/FP6 take TENSOR, ROW or GROUP scales in quantize/dequantize (cols a
+ *   multiple of 8, no column shifts) and the W4A16 product (W8A16 / W6A16); codes are the nearest
  *   finite value with ties to the even code, saturating at the largest.
  * FP4_GRID_LUT16: 16 sorted signed values in lut[] (e.g. NF4, [Overview] NF4), each
  *   exactly representable in binary16.

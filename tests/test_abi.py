@@ -247,7 +247,8 @@ def test_fp8_validation():
     N = ctypes.c_void_p(0)
     g8 = _grid(0, 4, 3)
     q = lib.fp4_quantize_pack
-    assert q(FAKE, 0, 4, 256, 256, g8, _gran(1), N, N, N, FAKE, 256, FAKE, N) == L.FP4_ERR_UNSUPPORTED  # ROW
+    assert q(FAKE, 0, 4, 256, 256, g8, _gran(1), N, N, FAKE, FAKE, 256, FAKE, N) == L.FP4_ERR_UNSUPPORTED  # column shifts
+    assert q(FAKE, 0, 4, 252, 256, g8, _gran(1), N, N, N, FAKE, 256, FAKE, N) == L.FP4_ERR_UNSUPPORTED  # cols % 8
     assert q(FAKE, 0, 4, 256, 256, g8, _gran(2, 32), N, N, N, FAKE, 128, FAKE, N) == L.FP4_ERR_INVALID_ARG  # ldp
     assert q(FAKE, 0, 4, 256, 256, _grid(0, 3, 4), _gran(2, 32), N, N, N, FAKE, 256, FAKE, N) == L.FP4_ERR_UNSUPPORTED
     d = L.fp4_gemm_desc()

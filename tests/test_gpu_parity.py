@@ -659,6 +659,8 @@ def _wide(fmt):
     (64, 4096, "group", 128, "f16", True),
     (30, 2056, "tensor", 0, "f32", False),   # a ragged last chunk, amax computed here
     (9, 2048, "group", 512, "f32", True),
+    (40, 2056, "row", 0, "f32", False),      # one scale per row, a ragged last chunk
+    (33, 4096, "row", 0, "f16", True),
 ])
 def test_fp8_quantize_dequantize(fmt, rows, cols, mode, group, sd, bf16):
     """OCP FP8 (one code per byte) and FP6 (four codes in three bytes) quantize: every
