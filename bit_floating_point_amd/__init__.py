@@ -160,7 +160,7 @@ def fp4_preshift_weights(w: torch.Tensor, chan_amax: torch.Tensor, act_grid: L.f
     if act_scale is None:
         act_scale = torch.empty(1, dtype=torch.float32, device=dev)
     if packed is None:
-        packed = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+        packed = torch.empty((n, k * code_bits(w_grid) // 8), dtype=torch.uint8, device=dev)
     if scales is None:
         sd = torch.float16 if w_gran.scale_dtype == FP4_F16 else torch.float32
         scales = torch.empty(_units(w_gran, n, k), dtype=sd, device=dev)

@@ -189,8 +189,8 @@ fp4_status fp4_quantize_pack(const void* x, int32_t x_dtype, int64_t rows, int64
     if ((st = check_gran(gran, cols))) return st;
     if (q.bits != 4) {
         if (ldp < cols * q.bits / 8) return fail(FP4_ERR_INVALID_ARG, "ldp below the code bytes of a row (cols * bits / 8)");
-        if (col_shift || cols % 8 != 0 || (q.bits == 6 && ldp % 2 != 0))
-            return fail(FP4_ERR_UNSUPPORTED, "FP8/FP6 quantization takes no column shifts, cols % 8 == 0 (FP6: ldp even)");
+        if (cols % 8 != 0 || (q.bits == 6 && ldp % 2 != 0))
+            return fail(FP4_ERR_UNSUPPORTED, "FP8/FP6 quantization needs cols % 8 == 0 (FP6: ldp even)");
     }
     if (q.kind == 2 && (gran.mode != FP4_SCALE_GROUP || col_shift))
         return fail(FP4_ERR_UNSUPPORTED, "the two-mode grid needs GROUP scales and no column shifts");
@@ -268,8 +268,12 @@ fp4_status fp4_preshift_weights(const float* w, int64_t n, int64_t k, int64_t ld
     if ((st = make_grid(w_grid, &qw))) return st;
     if ((st = check_gran(w_gran, k))) return st;
     if (w_gran.mode == FP4_SCALE_TENSOR) return fail(FP4_ERR_UNSUPPORTED, "pre-shifted weights need ROW or GROUP scales");
-    if (qa.kind == 2 || qw.kind == 2 || qa.bits != 4 || qw.bits != 4)
-        return fail(FP4_ERR_UNSUPPORTED, "pre-shift with the two-mode, FP8 or FP6 grids is not implemented");
+    if (qa.kind == 2 || qw.kind == 2) return fail(FP4_ERR_UNSUPPORTED, "pre-shift with the two-mode grid is not implemented");
+    if (qw.bits != 4) {
+        if (ldp < k * qw.bits / 8) return fail(FP4_ERR_INVALID_ARG, "ldp below the code bytes of a row (k * bits / 8)");
+        if (k % 8 != 0 || (qw.bits == 6 && ldp % 2 != 0))
+            return fail(FP4_ERR_UNSUPPORTED, "FP8/FP6 weights need k % 8 == 0 (FP6: ldp even)");
+    }
     if (!aligned16(w) || !aligned16(w_packed) || !aligned16(shift_out))
         return fail(FP4_ERR_ALIGNMENT, "w, w_packed and shift_out must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
@@ -289,7 +293,7 @@ fp4_status fp4_preshift_weights(const float* w, int64_t n, int64_t k, int64_t ld
     p.scales_out = w_scales;
     p.col_shift = shift_out;
     p.shift_sign = +1;
-    p.vec = ((ldw * 4) % 16 == 0) && (k % 8 == 0) && (ldp % 4 == 0);
+    p.vec = ((ldw * 4) % 16 == 0) && (k % 8 == 0) && (ldp % (qw.bits == 8 ? 8 : 4) == 0);
     p.g = qw;
     return hip_status(launch_quantize(p, s), "fp4_preshift_weights/quantize");
 }

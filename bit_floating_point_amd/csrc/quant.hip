@@ -250,17 +250,17 @@ __global__ void __launch_bounds__(kThreads) quantize_chunk_kernel(QuantParams p,
     }
 }
 
-// the 8 codes of y = fl32(v * r) at columns col .. col + 7 of a row on an FP8 grid (8
-// bytes) or an FP6 grid (6 bytes as three 16-bit words; cols is a multiple of 8, so a
+// the 8 codes of the scaled values y at columns col .. col + 7 of a row on an FP8 grid
+// (8 bytes) or an FP6 grid (6 bytes as three 16-bit words; cols is a multiple of 8, so a
 // lane's 6 bytes are whole)
 template <bool VEC, int E, int M>
-__device__ __forceinline__ void store_wide8(const QuantParams& p, int64_t row, int64_t col, const float v[8], float r) {
+__device__ __forceinline__ void store_wide8(const QuantParams& p, int64_t row, int64_t col, const float y[8]) {
     if (E + M == 7) {
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int k = 0; k < 4; k++) {
-            lo |= wide_code<E, M>(v[k] * r) << (8 * k);
-            hi |= wide_code<E, M>(v[k + 4] * r) << (8 * k);
+            lo |= wide_code<E, M>(y[k]) << (8 * k);
+            hi |= wide_code<E, M>(y[k + 4]) << (8 * k);
         }
         if (col < p.cols) {
             uint8_t* dst = p.packed + row * p.ldp + col;
@@ -271,7 +271,7 @@ __device__ __forceinline__ void store_wide8(const QuantParams& p, int64_t row, i
     } else {
         uint64_t bits = 0;
 #pragma unroll
-        for (int k = 0; k < 8; k++) bits |= (uint64_t)wide_code<E, M>(v[k] * r) << (6 * k);
+        for (int k = 0; k < 8; k++) bits |= (uint64_t)wide_code<E, M>(y[k]) << (6 * k);
         if (col < p.cols) {
             uint16_t* dst = reinterpret_cast<uint16_t*>(p.packed + row * p.ldp + col / 8 * 6);
             dst[0] = (uint16_t)bits;
@@ -288,6 +288,8 @@ template <bool VEC, bool BF16, int U, int E, int M>
 __global__ void __launch_bounds__(kThreads) quantize_wide_kernel(QuantParams p, int64_t chunks, int64_t nunits) {
     Raw8 raw[U];
     int64_t row[U], col[U];
+    uint2 kk[U];
+    const bool has_k = p.col_shift != nullptr;
 #pragma unroll
     for (int i = 0; i < U; i++) {
         int64_t u = (int64_t)blockIdx.x * U + i;
@@ -296,6 +298,7 @@ __global__ void __launch_bounds__(kThreads) quantize_wide_kernel(QuantParams p, 
         col[i] = (u % chunks) * kChunk + threadIdx.x * 8;
         raw[i] = load_raw8<VEC, BF16>(reinterpret_cast<const char*>(p.x) + row[i] * p.ldx * (BF16 ? 2 : 4), col[i],
                                       p.cols);
+        kk[i] = has_k ? load_shift8<VEC>(p, col[i]) : make_uint2(0, 0);
     }
     float tensor_r = 0.0f;
     if (p.mode == 0) {
@@ -308,6 +311,7 @@ __global__ void __launch_bounds__(kThreads) quantize_wide_kernel(QuantParams p, 
     for (int i = 0; i < U; i++) {
         float v[8];
         raw8_to_float<BF16>(raw[i], v);
+        if (has_k && p.shift_sign > 0) shift_inputs(v, kk[i]);  // pre-shifted weights W' = W 2^k
         float r = tensor_r;
         if (p.mode != 0) {
             const int lanes = p.group >> 3;
@@ -320,7 +324,8 @@ __global__ void __launch_bounds__(kThreads) quantize_wide_kernel(QuantParams p, 
             r = recip_or_zero(s);
             if (col[i] < p.cols && (threadIdx.x & (lanes - 1)) == 0 && p.scales_out) store_scale(p, unit, s);
         }
-        store_wide8<VEC, E, M>(p, row[i], col[i], v, r);
+        scale_values(v, r, has_k && p.shift_sign < 0, kk[i]);  // activations: r 2^-k per column
+        store_wide8<VEC, E, M>(p, row[i], col[i], v);
     }
 }
 
@@ -571,6 +576,7 @@ __global__ void __launch_bounds__(kThreads) quantize_wide_row_kernel(QuantParams
     __shared__ float red[kThreads / 64];
     const int64_t row = blockIdx.x;
     const char* rp = reinterpret_cast<const char*>(p.x) + row * p.ldx * (BF16 ? 2 : 4);
+    const bool has_k = p.col_shift != nullptr;
     float amax;
     if (p.amax_in) {
         amax = p.amax_in[row];
@@ -579,6 +585,7 @@ __global__ void __launch_bounds__(kThreads) quantize_wide_row_kernel(QuantParams
         for (int64_t c0 = 0; c0 < p.cols; c0 += kChunk) {
             float v[8];
             load8<VEC, BF16>(rp, c0 + threadIdx.x * 8, p.cols, v);
+            if (has_k && p.shift_sign > 0) shift_inputs(v, load_shift8<VEC>(p, c0 + threadIdx.x * 8));
             m = fmaxf(m, max_abs8(v));
         }
         m = dpp_wave_max(m);
@@ -595,7 +602,10 @@ __global__ void __launch_bounds__(kThreads) quantize_wide_row_kernel(QuantParams
         if (col >= p.cols) continue;
         float v[8];
         load8<VEC, BF16>(rp, col, p.cols, v);
-        store_wide8<VEC, E, M>(p, row, col, v, r);
+        const uint2 k = has_k ? load_shift8<VEC>(p, col) : make_uint2(0, 0);
+        if (has_k && p.shift_sign > 0) shift_inputs(v, k);
+        scale_values(v, r, has_k && p.shift_sign < 0, k);
+        store_wide8<VEC, E, M>(p, row, col, v);
     }
 }
 

@@ -79,7 +79,7 @@ typedef int32_t fp4_status;
  *   E3M2 (bias 3, largest 28), no reserved code; codes form a little-endian bit
  *   stream, code i in bits [6i, 6i+6) of its row (3 cols / 4 bytes; cols a multiple
  *   of 4).  FP8/FP6 take TENSOR, ROW or GROUP scales in quantize/dequantize (cols a
- *   multiple of 8, no column shifts) and the W4A16 product (W8A16 / W6A16); codes are the nearest
+ *   multiple of 8; column shifts allowed) and the W4A16 product (W8A16 / W6A16); codes are the nearest
  *   finite value with ties to the even code, saturating at the largest.
  * FP4_GRID_LUT16: 16 sorted signed values in lut[] (e.g. NF4, [Overview] NF4), each
  *   exactly representable in binary16.
@@ -224,9 +224,11 @@ fp4_status fp4_dequantize(const uint8_t* packed, int64_t rows, int64_t cols, int
  *   (scales from the amax of W') -> w_packed, w_scales.
  * Activations are then quantized with fp4_quantize_pack(gran TENSOR, tensor_scale =
  * act_scale_out, col_shift = shift_out), and X * W^T = (X 2^-k) * (W 2^k)^T exactly.
+ * act_grid and w_grid are any minifloat / LUT16 grids or the FP8 / FP6 grids (not the
+ * two-mode grid); FP8 / FP6 weights need k a multiple of 8 (FP6: ldp even).
  *   w            device f32 [n, k], leading dim ldw elements
  *   chan_amax    device f32 [k]
- *   w_packed     device u8 [n, k/2], leading dim ldp bytes                          */
+ *   w_packed     device u8 [n, k * bits / 8], leading dim ldp bytes                 */
 fp4_status fp4_preshift_weights(const float* w, int64_t n, int64_t k, int64_t ldw,
                                 const float* chan_amax, fp4_grid act_grid,
                                 fp4_grid w_grid, fp4_gran w_gran, int8_t* shift_out,

@@ -247,7 +247,12 @@ def test_fp8_validation():
     N = ctypes.c_void_p(0)
     g8 = _grid(0, 4, 3)
     q = lib.fp4_quantize_pack
-    assert q(FAKE, 0, 4, 256, 256, g8, _gran(1), N, N, FAKE, FAKE, 256, FAKE, N) == L.FP4_ERR_UNSUPPORTED  # column shifts
+    g6 = _grid(0, 2, 3)
+    assert q(FAKE, 0, 4, 256, 256, g6, _gran(1), N, N, N, FAKE, 193, FAKE, N) == L.FP4_ERR_UNSUPPORTED  # FP6: odd ldp
+    assert q(FAKE, 0, 4, 256, 256, g6, _gran(1), N, N, N, FAKE, 190, FAKE, N) == L.FP4_ERR_INVALID_ARG  # ldp < 192
+    f = lib.fp4_preshift_weights  # FP8 weights: ldp below a row's 256 code bytes, then k % 8
+    assert f(FAKE, 8, 256, 256, FAKE, g8, g8, _gran(1), FAKE, FAKE, FAKE, 128, FAKE, N) == L.FP4_ERR_INVALID_ARG
+    assert f(FAKE, 8, 252, 256, FAKE, g8, g8, _gran(1), FAKE, FAKE, FAKE, 256, FAKE, N) == L.FP4_ERR_UNSUPPORTED
     assert q(FAKE, 0, 4, 252, 256, g8, _gran(1), N, N, N, FAKE, 256, FAKE, N) == L.FP4_ERR_UNSUPPORTED  # cols % 8
     assert q(FAKE, 0, 4, 256, 256, g8, _gran(2, 32), N, N, N, FAKE, 128, FAKE, N) == L.FP4_ERR_INVALID_ARG  # ldp
     assert q(FAKE, 0, 4, 256, 256, _grid(0, 3, 4), _gran(2, 32), N, N, N, FAKE, 256, FAKE, N) == L.FP4_ERR_UNSUPPORTED

@@ -735,6 +735,36 @@ def test_fp8_w8a8_gemm(M, N, K, mode):
     assert np.array_equal(host(yb.view(torch.int16)).view(np.uint16), O.rne_bf16_bits(y32))
 
 
+@pytest.mark.parametrize("M,N,K", [(256, 384, 512), (520, 1100, 1024)])
+@pytest.mark.parametrize("af,wf", [((4, 3), (4, 3)), ((2, 3), (2, 3)), ((4, 3), (2, 3))])
+def test_preshift_fp8_fp6(M, N, K, af, wf):
+    """The pre-shifted exponent bias with FP8 / FP6 grids: channel maxima, shifts, the
+    activation scale, the shifted weights' codes and row scales and the shifted
+    activations' codes bit-exact; the W8A8 / W6A6 / mixed product from them within the
+    GEMM tolerance of the binary64 oracle."""
+    say("preshift fp8/fp6", M, N, K, af, wf)
+    x = synth.activations(18, M, M, K, outlier_frac=0.01, bf16=True)
+    w = synth.weight(18, N, N, K)
+    og_a, og_w = _wide(af), _wide(wf)
+    chan = O.amax_columns(x, 128)
+    k, a, wp, ws = O.preshift_weights(w, chan, og_a, og_w, "row")
+    ap, _ = O.quantize_activations(x, og_a, a, k)
+    fa, fw = F.grid_minifloat(*af), F.grid_minifloat(*wf)
+    xt = dev(x, torch.bfloat16)
+    gchan = F.fp4_calibrate(xt, "column", first_rows=128)
+    assert np.array_equal(host(gchan), chan)
+    gk, ga, gwp, gws = F.fp4_preshift_weights(dev(w), gchan, fa, fw, F.gran("row"))
+    assert np.array_equal(host(gk), k) and host(ga)[0] == a
+    assert np.array_equal(host(gwp), wp) and np.array_equal(host(gws), np.asarray(ws).reshape(-1))
+    gap, _ = F.fp4_quantize_pack(xt, fa, F.gran("tensor"), tensor_scale=ga, col_shift=gk)
+    assert np.array_equal(host(gap), ap)
+    r, _ = O.gemm_w4a4(ap, og_a, a, wp, og_w, "row", ws)
+    y32 = host(F.fp4_gemm(gap, gwp, gws, fw, F.gran("row"), K=K, a_grid=fa, a_scale=ga, y_dtype=torch.float32))
+    err = O.rel_err(y32, r)
+    say("  rel err", err)
+    assert err <= TOL
+
+
 def _padded_rows(packed, align=16):
     """uint8 rows copied into a device buffer whose row stride is a multiple of `align`
     bytes (the packed products need 16-byte aligned rows), returned as the [:, :bytes] view."""
