@@ -414,8 +414,8 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
 
     if (p.wg.kind == 2 && (d->w_gran.mode != FP4_SCALE_GROUP || d->a_kind == FP4_PACKED))
         return fail(FP4_ERR_UNSUPPORTED, "two-mode weights need GROUP scales and f32/bf16 activations");
-    if (p.a_row && (d->a_kind != FP4_PACKED || !p.wg.is_e2m1))
-        return fail(FP4_ERR_UNSUPPORTED, "per-token activation scales are taken by the E2M1 x E2M1 product only");
+    if (p.a_row && (d->a_kind != FP4_PACKED || !(p.wg.is_e2m1 || p.wg.bits != 4)))
+        return fail(FP4_ERR_UNSUPPORTED, "per-token activation scales are taken by the E2M1 x E2M1 and FP8 / FP6 products only");
     if (p.wg.bits != 4 && d->a_kind == FP4_PACKED) {
         // both operands FP8 / FP6 on the f8f6f4 matrix cores: E4M3 x E4M3 on the
         // persistent kernel, every other pair (W6A6 among them) on the tiled one

@@ -2,8 +2,9 @@
 // matrix cores:  Y[m, n] = fl32(acc[m, n] * fl32(a * s_n)),  acc = sum_k A_q[m, k] W_q[n, k]
 // in fp32 by the MFMA.  Scales are factored out of the low-bit product as the
 // FP4-LLM paper's efficient matrix multiplication section describes (one activation
-// scale a per tensor, one weight scale per tensor or per output row); the progressive
-// 8/6/4-bit formats come from the low-bit FP overview's FP8/FP6 sections.
+// scale a per tensor or one per row of A, one weight scale per tensor or per output
+// row); the progressive 8/6/4-bit formats come from the low-bit FP overview's FP8/FP6
+// sections.
 //
 // Formats (the MFMA's operand format codes): 0 FP8 E4M3, 1 FP8 E5M2, 2 FP6 E2M3,
 // 3 FP6 E3M2.  FP8 rows hold one code per byte; FP6 rows are a bit stream, code k in
@@ -205,19 +206,18 @@ __global__ void __launch_bounds__(256) f8f6_gemm_kernel(GemmParams p, int grid_m
 #pragma unroll
         for (int g = 0; g < 4; g++) {
             const int64_t n = n0 + wn * 128 + 32 * j + 8 * g + 4 * hk;
-            float f[4];
+            float sn[4];
 #pragma unroll
-            for (int c = 0; c < 4; c++) {
-                const float sn = p.w_mode == 1 ? ws[n + c < p.N ? n + c : p.N - 1] : ws[0];
-                f[c] = a_scale * sn;
-            }
+            for (int c = 0; c < 4; c++) sn[c] = p.w_mode == 1 ? ws[n + c < p.N ? n + c : p.N - 1] : ws[0];
 #pragma unroll
             for (int i = 0; i < 2; i++) {
                 const int64_t m = m0 + wm * 64 + 32 * i + r32;
                 if (m >= p.M) continue;
+                // one activation scale, or one per row (token) of A: y = fl32(acc * fl32(a_m * s_n))
+                const float am = p.a_row ? p.a_scale[m] : a_scale;
                 float y[4];
 #pragma unroll
-                for (int c = 0; c < 4; c++) y[c] = acc[j][i][4 * g + c] * f[c];
+                for (int c = 0; c < 4; c++) y[c] = acc[j][i][4 * g + c] * (am * sn[c]);
                 const bool vec = vec_ok && n + 3 < p.N;
                 if (p.y_bf16) {
                     __bf16* yp = reinterpret_cast<__bf16*>(p.y) + m * p.ldy + n;

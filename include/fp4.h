@@ -149,7 +149,8 @@ typedef struct {
     fp4_grid a_grid;          /* PACKED only: grid of the activation codes          */
     const float* a_scale;     /* PACKED only: device f32, the one scale a, or with
                                  a_scale_mode ROW one scale a_m per row (token) of X
-                                 ([Overview] per-token granularity; E2M1 x E2M1 only) */
+                                 ([Overview] per-token granularity; the E2M1 x E2M1
+                                 and FP8 / FP6 products)                            */
     /* weights W [N, K], packed */
     const uint8_t* w;
     int64_t ldw;              /* bytes                                              */
@@ -304,7 +305,8 @@ fp4_status fp4_search_activations(const void* x, int32_t x_dtype, int64_t rows, 
  *   FP8 / FP6 weights with F32/BF16 activations take the W4A16 path (W8A16 / W6A16):
  *   ldw >= K (FP8) or 3K/4 (FP6) bytes.  With PACKED activations both operands are FP8
  *   (E4M3, E5M2) or FP6 (E2M3, E3M2), in any pairing (W8A8, W6A6, mixed), on the
- *   f8f6f4 matrix cores with f32 TENSOR/ROW weight scales and one activation scale:
+ *   f8f6f4 matrix cores with f32 TENSOR/ROW weight scales and one activation scale
+ *   (or one per row of A with a_scale_mode ROW, y = fl32(acc * fl32(a_m * s_n))):
  *   y = fl32(acc * fl32(a * s_n)), acc summed in fp32 (not exact: within the GEMM
  *   tolerance); lda, ldw >= the code bytes of a row (K or 3K/4), lda a multiple of 16,
  *   K a multiple of 32, rows shorter than 8 MiB.  Packed E2M1 activations with FP8 /

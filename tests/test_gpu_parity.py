@@ -765,6 +765,30 @@ def test_preshift_fp8_fp6(M, N, K, af, wf):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("af,wf", [((4, 3), (4, 3)), ((2, 3), (2, 3)), ((5, 2), (2, 3))])
+def test_f8f6_per_token_scales(af, wf):
+    """FP8 / FP6 activations quantized per token (one scale per row, on the GPU) and
+    their product with row-scaled FP8 / FP6 weights (y = fl32(acc * fl32(a_m * s_n))):
+    codes and scales bit-exact, the product within the GEMM tolerance."""
+    M, N, K = 300, 520, 512
+    say("f8f6 per-token", af, wf)
+    x = synth.activations(19, M, M, K, outlier_frac=0.01, bf16=True)
+    w = synth.weight(19, N, N, K)
+    og_a, og_w = _wide(af), _wide(wf)
+    ap, asc = O.quantize_pack(x, og_a, "row")
+    wp, wsc = O.quantize_pack(w, og_w, "row")
+    fa, fw = F.grid_minifloat(*af), F.grid_minifloat(*wf)
+    gap, gas = F.fp4_quantize_pack(dev(x, torch.bfloat16), fa, F.gran("row"))
+    gwp, gws = F.fp4_quantize_pack(dev(w), fw, F.gran("row"))
+    assert np.array_equal(host(gap), ap) and np.array_equal(host(gas), np.asarray(asc, np.float32))
+    assert np.array_equal(host(gwp), wp) and np.array_equal(host(gws), np.asarray(wsc, np.float32))
+    r, _ = O.gemm_w4a4(ap, og_a, asc, wp, og_w, "row", wsc)
+    y32 = host(F.fp4_gemm(gap, gwp, gws, fw, F.gran("row"), K=K, a_grid=fa, a_scale=gas, y_dtype=torch.float32))
+    err = O.rel_err(y32, r)
+    say("  rel err", err)
+    assert err <= TOL
+
+
 def _padded_rows(packed, align=16):
     """uint8 rows copied into a device buffer whose row stride is a multiple of `align`
     bytes (the packed products need 16-byte aligned rows), returned as the [:, :bytes] view."""
