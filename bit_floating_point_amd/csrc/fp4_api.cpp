@@ -421,8 +421,8 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
         // persistent kernel, every other pair (W6A6 among them) on the tiled one
         QGrid qa;
         if ((st = make_grid(d->a_grid, &qa))) return st;
-        if (qa.bits != 8 && qa.bits != 6)
-            return fail(FP4_ERR_UNSUPPORTED, "FP8 / FP6 weights with packed activations need FP8 / FP6 activations");
+        if (qa.kind != 0 || (qa.bits == 4 && !qa.is_e2m1))
+            return fail(FP4_ERR_UNSUPPORTED, "FP8 / FP6 weights with packed activations need FP8 / FP6 / E2M1 activations");
         if (!d->a_scale) return fail(FP4_ERR_INVALID_ARG, "packed activations need a_scale");
         if (d->K % 32 != 0) return fail(FP4_ERR_UNSUPPORTED, "K must be a multiple of 32");
         if (d->lda < d->K * qa.bits / 8 || d->ldw < d->K * p.wg.bits / 8 || d->lda % 16 != 0)
@@ -460,8 +460,19 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
     }
     if (d->a_kind != FP4_PACKED) return fail(FP4_ERR_INVALID_ARG, "a_kind must be F32, BF16 or PACKED");
     if (!d->a_scale) return fail(FP4_ERR_INVALID_ARG, "packed activations need a_scale");
-    if (d->lda < d->K / 2 || d->lda % 16 != 0) return fail(FP4_ERR_ALIGNMENT, "packed lda must be >= K/2 and a multiple of 16");
     if ((st = make_grid(d->a_grid, &p.ag))) return st;
+    if (p.ag.kind == 0 && p.ag.bits != 4 && p.wg.is_e2m1) {
+        // FP8 / FP6 activations with E2M1 weights: the tiled f8f6f4 kernel
+        if (d->K % 32 != 0) return fail(FP4_ERR_UNSUPPORTED, "K must be a multiple of 32");
+        if (d->lda < d->K * p.ag.bits / 8 || d->lda % 16 != 0)
+            return fail(FP4_ERR_ALIGNMENT, "FP8 / FP6 rows: lda >= the code bytes of a row, a multiple of 16");
+        if (d->w_gran.mode == FP4_SCALE_GROUP || d->w_gran.scale_dtype != FP4_F32)
+            return fail(FP4_ERR_UNSUPPORTED, "FP8 / FP6 products need f32 TENSOR or ROW weight scales");
+        if (256 * std::max(d->lda, d->ldw) >= 0x7fff0000)
+            return fail(FP4_ERR_UNSUPPORTED, "FP8 / FP6 rows longer than 8 MiB are not supported");
+        return hip_status(launch_f8f6_gemm(p, s), "fp4_gemm/f8f6");
+    }
+    if (d->lda < d->K / 2 || d->lda % 16 != 0) return fail(FP4_ERR_ALIGNMENT, "packed lda must be >= K/2 and a multiple of 16");
     if (!p.ag.is_e2m1) return fail(FP4_ERR_UNSUPPORTED, "packed activations must be E2M1");
     if (d->K % 32 != 0) return fail(FP4_ERR_UNSUPPORTED, "K must be a multiple of 32");
     if (p.wg.is_e2m1) {

@@ -7,9 +7,10 @@
 // sections.
 //
 // Formats (the MFMA's operand format codes): 0 FP8 E4M3, 1 FP8 E5M2, 2 FP6 E2M3,
-// 3 FP6 E3M2.  FP8 rows hold one code per byte; FP6 rows are a bit stream, code k in
-// bits [6 k, 6 k + 6) of the row, so 16 consecutive codes starting at a multiple of 16
-// are 12 contiguous bytes, half of the six registers of an FP6 MFMA operand.
+// 3 FP6 E3M2, 4 FP4 E2M1.  FP8 rows hold one code per byte, FP4 rows two (low nibble
+// first); FP6 rows are a bit stream, code k in bits [6 k, 6 k + 6) of the row, so 16
+// consecutive codes starting at a multiple of 16 are 12 contiguous bytes, half of the
+// six registers of an FP6 MFMA operand.
 //
 // Tiling: a workgroup (four wavefronts) computes a 128 x 256 tile of Y (128 rows of A,
 // 256 rows of W); each wavefront a 64 x 128 block as 2 x 4 MFMAs of 32 x 32 x 64.  A
@@ -19,8 +20,9 @@
 // step.  The waits are the compiler's own.  Units past K are zeros, so the padding of a
 // row adds nothing.
 //
-// The E4M3 x E4M3 pair has its own persistent kernel (gemm_w4a4.hip); this kernel
-// takes every other pair, W6A6 among them.
+// The E4M3 x E4M3 and E2M1 x E2M1 pairs have their own persistent kernel
+// (gemm_w4a4.hip); this kernel takes every other pair with an FP8 or FP6 operand, W6A6
+// among them.
 #include "fp4_device.h"
 #include "fp4_internal.h"
 
@@ -39,22 +41,22 @@ constexpr int kStepCodes = 128;
 // loop is not bound by load latency)
 constexpr int kSets = 2;
 
-// A step of a row is 8 units: FP8 16-byte pieces (32 codes), or FP6 12-byte runs (16
-// codes).  Each unit is staged in its own 16-byte LDS slot (row stride 8 slots + 16
+// A step of a row is 8 units: FP8 16-byte pieces (32 codes), FP6 12-byte runs or FP4
+// 8-byte runs (16 codes).  Each unit is staged in its own 16-byte LDS slot (row stride 8 slots + 16
 // bytes of padding, so the 16-byte fragment reads of 16 consecutive rows hit distinct
 // banks).  With K a multiple of 32 a row ends on a unit boundary, so a unit is either
 // wholly inside the row or wholly past it.
 template <int F>
 struct Fmt {
-    static constexpr int bits = F < 2 ? 8 : 6;
-    static constexpr int step_bytes = kStepCodes * bits / 8;  // 128 or 96
-    static constexpr int unit_bytes = step_bytes / 8;         // 16 or 12
+    static constexpr int bits = F < 2 ? 8 : (F < 4 ? 6 : 4);
+    static constexpr int step_bytes = kStepCodes * bits / 8;  // 128, 96 or 64
+    static constexpr int unit_bytes = step_bytes / 8;         // 16, 12 or 8
     static constexpr int stride = 8 * 16 + 16;                // LDS row stride (bytes)
     // LDS slot of unit j.  The matrix cores pair the two operands' values in a fixed K
     // order that differs by format (measured on gfx950 with one-hot operands): an FP8
     // operand's 32 values are codes 32 hk + i of the 64-code K-block, i = 0..31; an FP6
     // (and FP4) operand's are two runs of 16, codes 16 hk + i and 32 + 16 hk + i.  FP8
-    // pieces stay in order; FP6 runs are placed so that lane half hk of K-block h finds
+    // pieces stay in order; FP6 / FP4 runs are placed so that lane half hk of K-block h finds
     // its two runs (4 h + hk, 4 h + 2 + hk) in slots 4 h + 2 hk and 4 h + 2 hk + 1.
     static __device__ __forceinline__ int slot(int j) {
         return bits == 8 ? j : 4 * (j >> 2) + 2 * (j & 1) + ((j >> 1) & 1);
@@ -62,16 +64,18 @@ struct Fmt {
 };
 
 // Operand of K-block h for lane half hk: slots 4 h + 2 hk and 4 h + 2 hk + 1 of the row
-// (an FP6 slot holds 12 code bytes and 4 unused ones).  The same slots line up FP8 with
-// FP8, FP6 with FP6 and mixed pairs.
+// (an FP6 slot holds 12 code bytes and 4 unused ones, an FP4 slot 8 and 8).  The same
+// slots line up every pair of formats.
 template <int F>
 __device__ __forceinline__ i32x8 frag(const uint8_t* row, int h, int hk) {
     const uint4 u = *reinterpret_cast<const uint4*>(row + 64 * h + 32 * hk);
     const uint4 v = *reinterpret_cast<const uint4*>(row + 64 * h + 32 * hk + 16);
     if constexpr (Fmt<F>::bits == 8)
         return i32x8{(int)u.x, (int)u.y, (int)u.z, (int)u.w, (int)v.x, (int)v.y, (int)v.z, (int)v.w};
-    else
+    else if constexpr (Fmt<F>::bits == 6)
         return i32x8{(int)u.x, (int)u.y, (int)u.z, (int)v.x, (int)v.y, (int)v.z, 0, 0};
+    else
+        return i32x8{(int)u.x, (int)u.y, (int)v.x, (int)v.y, 0, 0, 0, 0};
 }
 
 // one unit of a row, `valid` code bytes of the row remaining from it on; a unit past K
@@ -83,9 +87,12 @@ __device__ __forceinline__ uint4 unit_load(__amdgpu_buffer_rsrc_t r, int64_t row
     const uint32_t off = valid > 0 ? (uint32_t)row_off : kOOB;
     if constexpr (Fmt<F>::bits == 8) {
         return buf_load16(r, off);
-    } else {
+    } else if constexpr (Fmt<F>::bits == 6) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
         return make_uint4(v[0], v[1], v[2], 0u);
+    } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        return make_uint4(v[0], v[1], 0u, 0u);
     }
 }
 
@@ -259,15 +266,18 @@ hipError_t launch_w(const GemmParams& p, int fa, hipStream_t s) {
         case 0: return launch_pair<FW, 0>(p, s);
         case 1: return launch_pair<FW, 1>(p, s);
         case 2: return launch_pair<FW, 2>(p, s);
-        default: return launch_pair<FW, 3>(p, s);
+        case 3: return launch_pair<FW, 3>(p, s);
+        default: return launch_pair<FW, 4>(p, s);
     }
 }
 
 }  // namespace
 
-// MFMA operand format code of an FP8 / FP6 grid: 0 E4M3, 1 E5M2, 2 E2M3, 3 E3M2
+// MFMA operand format code of an FP8 / FP6 / FP4 grid: 0 E4M3, 1 E5M2, 2 E2M3, 3 E3M2,
+// 4 E2M1
 int f8f6_format_code(const QGrid& g) {
     if (g.kind != 0) return -1;
+    if (g.bits == 4) return g.is_e2m1 ? 4 : -1;
     if (g.bits == 8) return g.e == 4 && g.m == 3 ? 0 : (g.e == 5 && g.m == 2 ? 1 : -1);
     if (g.bits == 6) return g.e == 2 && g.m == 3 ? 2 : (g.e == 3 && g.m == 2 ? 3 : -1);
     return -1;
@@ -284,7 +294,8 @@ hipError_t launch_f8f6_gemm(const GemmParams& p, hipStream_t s) {
         case 0: return launch_w<0>(p, fa, s);
         case 1: return launch_w<1>(p, fa, s);
         case 2: return launch_w<2>(p, fa, s);
-        default: return launch_w<3>(p, fa, s);
+        case 3: return launch_w<3>(p, fa, s);
+        default: return launch_w<4>(p, fa, s);
     }
 }
 

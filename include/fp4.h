@@ -309,8 +309,8 @@ fp4_status fp4_search_activations(const void* x, int32_t x_dtype, int64_t rows, 
  *   (or one per row of A with a_scale_mode ROW, y = fl32(acc * fl32(a_m * s_n))):
  *   y = fl32(acc * fl32(a * s_n)), acc summed in fp32 (not exact: within the GEMM
  *   tolerance); lda, ldw >= the code bytes of a row (K or 3K/4), lda a multiple of 16,
- *   K a multiple of 32, rows shorter than 8 MiB.  Packed E2M1 activations with FP8 /
- *   FP6 weights: FP4_ERR_UNSUPPORTED.
+ *   K a multiple of 32, rows shorter than 8 MiB.  The same holds when one operand is
+ *   E2M1 and the other FP8 / FP6 (rows of K/2 bytes).
  *   Two-mode weights (FP4_GRID_TWO_MODE, GROUP scales) take the W4A16 path only: each
  *   group's codes are read on its own grid (the sign of its scale) and scaled by |s|.
  * Strides: K a multiple of 32 for the matrix-core paths; packed rows 16-byte aligned. */

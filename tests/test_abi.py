@@ -261,10 +261,10 @@ def test_fp8_validation():
     d.a_kind = L.FP4_PACKED
     d.a, d.lda, d.w, d.ldw, d.w_scales, d.y, d.ldy = 0x10000, 128, 0x20000, 256, 0x30000, 0x40000, 32
     d.a_scale = 0x50000
-    d.a_grid, d.w_grid = _grid(), g8
+    d.a_grid, d.w_grid = _grid(0, 1, 2), g8
     d.w_gran = _gran(1)
     d.y_dtype = L.FP4_BF16
-    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # FP8 weights with packed E2M1 activations
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # FP8 weights with packed E1M2 activations
     # W6A6 (FP6 E2M3 x FP6 E2M3): rows of 256 codes are 192 bytes
     g6 = _grid(0, 2, 3)
     d.a_grid, d.w_grid, d.lda, d.ldw = g6, g6, 192, 192

@@ -650,7 +650,7 @@ def test_two_mode_w4a16_gemm(M, N, K, sd, adt):
 
 # ---------------------------------------------------------------- FP8 / FP6 grids -
 def _wide(fmt):
-    return O.fp8(*fmt) if sum(fmt) == 7 else O.fp6(*fmt)
+    return O.fp8(*fmt) if sum(fmt) == 7 else (O.fp6(*fmt) if sum(fmt) == 5 else O.minifloat(*fmt))
 
 
 @pytest.mark.parametrize("fmt", [(4, 3), (5, 2), (2, 3), (3, 2)])
@@ -806,10 +806,13 @@ def _padded_rows(packed, align=16):
     (256, 384, 512, (5, 2), (5, 2), "row"),     # W8A8 with E5M2
     (300, 520, 544, (4, 3), (2, 3), "row"),     # mixed: FP8 E4M3 weights, FP6 E2M3 activations
     (130, 270, 96, (2, 3), (5, 2), "tensor"),   # mixed: FP6 weights, FP8 E5M2 activations; K below one step
+    (300, 520, 544, (4, 3), (2, 1), "row"),     # FP8 weights, FP4 E2M1 activations
+    (300, 520, 544, (2, 1), (2, 3), "row"),     # FP4 E2M1 weights, FP6 activations
+    (130, 270, 1024, (3, 2), (2, 1), "tensor"),
 ])
 def test_f8f6_gemm(M, N, K, wf, af, mode):
-    """Both operands FP8 / FP6 (every pair other than E4M3 x E4M3, which the W8A8 test
-    covers) on the f8f6f4 matrix cores: within the GEMM tolerance of the binary64
+    """Both operands FP8 / FP6, or one of them FP4 E2M1 (every pair other than E4M3 x
+    E4M3, which the W8A8 test covers) on the f8f6f4 matrix cores: within the GEMM tolerance of the binary64
     oracle; bf16 output the nearest-even rounding of the fp32 output."""
     say("f8f6", M, N, K, wf, af, mode)
     og_w, og_a = _wide(wf), _wide(af)
