@@ -18,7 +18,7 @@ from ._lib import (FP4Error, FP4_BF16, FP4_F16, FP4_F32, FP4_PACKED, FP4_REDUCE_
                    FP4_REDUCE_ROW_GROUP, FP4_REDUCE_TENSOR, FP4_SCALE_GROUP, FP4_SCALE_ROW,
                    FP4_SCALE_TENSOR)
 
-__all__ = ["FP4Error", "grid_minifloat", "grid_lut", "grid_nf4", "grid_two_mode", "nf4_values", "gran", "fp4_calibrate", "fp4_quantize_pack",
+__all__ = ["FP4Error", "grid_minifloat", "grid_lut", "grid_nf4", "grid_two_mode", "nf4_values", "set_split_limit", "gran", "fp4_calibrate", "fp4_quantize_pack",
            "fp4_dequantize", "fp4_preshift_weights", "fp4_search_format", "fp4_gemm",
            "fp4_gemm_swiglu_quant", "fp4_search_activations", "search_results_host", "E2M1", "E1M2", "E3M0"]
 
@@ -43,19 +43,22 @@ def grid_lut(values) -> L.fp4_grid:
 E2M1, E1M2, E3M0 = (2, 1), (1, 2), (3, 0)
 
 
-def nf4_values() -> list:
-    """The 16 NF4 levels ("量化技术详解" page, section NF4: levels at quantiles of the
-    normal distribution): Phi^-1((i + 1/2)/16) scaled so the end points are +-1, each
-    rounded to binary16 (so every level and every midpoint is exact in binary32)."""
-    from statistics import NormalDist
-    nd = NormalDist()
-    z = nd.inv_cdf(15.5 / 16)
-    return [float(torch.tensor(nd.inv_cdf((i + 0.5) / 16) / z, dtype=torch.float64).to(torch.float16))
-            for i in range(16)]
-
-
 def grid_nf4() -> L.fp4_grid:
-    return grid_lut(nf4_values())
+    """The library's NF4 lookup grid (fp4_nf4_grid: 16 levels at normal quantiles)."""
+    g = L.fp4_grid()
+    L.check(L.lib().fp4_nf4_grid(ctypes.byref(g)), "fp4_nf4_grid")
+    return g
+
+
+def nf4_values() -> list:
+    """The 16 NF4 levels of grid_nf4() as Python floats."""
+    return [float(v) for v in grid_nf4().lut]
+
+
+def set_split_limit(nbytes: int = 0) -> None:
+    """fp4_set_split_limit: operand bytes per launch of the W4A4 / W8A8 products (<= 0:
+    the default 32-bit buffer range)."""
+    L.check(L.lib().fp4_set_split_limit(int(nbytes)), "fp4_set_split_limit")
 
 
 def grid_two_mode() -> L.fp4_grid:
@@ -244,11 +247,21 @@ def search_results_host(results: torch.Tensor) -> list:
 def fp4_gemm(a: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor, w_grid: L.fp4_grid,
              w_gran: L.fp4_gran, K: int | None = None, a_grid: L.fp4_grid | None = None,
              a_scale: torch.Tensor | None = None, y_dtype: torch.dtype = torch.bfloat16,
-             y: torch.Tensor | None = None) -> torch.Tensor:
+             y: torch.Tensor | None = None, a_scale_mode: str | None = None) -> torch.Tensor:
     """Y = X W^T.  a: [M, K] f32/bf16 (W4A16), or packed codes uint8 [M, K * bits / 8]
-    (W4A4, W8A8, W6A6, with a_grid and a_scale)."""
+    (W4A4, W8A8, W6A6, with a_grid and a_scale).  a_scale: float32 on a's device, one
+    value ('tensor') or one per row of a ('row'); a_scale_mode defaults to 'row' when
+    a_scale holds M > 1 values."""
     M = a.shape[0]
     N = w_packed.shape[0]
+    if a_scale is not None:
+        if a_scale.dtype != torch.float32 or a_scale.device != a.device or not a_scale.is_contiguous():
+            raise ValueError("a_scale must be a contiguous float32 tensor on the activations' device")
+        if a_scale_mode is None:
+            a_scale_mode = "row" if a_scale.numel() > 1 else "tensor"
+        want = M if a_scale_mode == "row" else 1
+        if a_scale_mode not in ("tensor", "row") or a_scale.numel() != want:
+            raise ValueError(f"a_scale_mode {a_scale_mode!r} needs {want} scale(s), got {a_scale.numel()}")
     if a.dtype == torch.uint8:
         kind = FP4_PACKED
         K = K if K is not None else a.shape[1] * 8 // code_bits(a_grid if a_grid is not None else w_grid)
@@ -265,7 +278,7 @@ def fp4_gemm(a: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor, w_
     if a_grid is not None:
         d.a_grid = a_grid
     d.a_scale = a_scale.data_ptr() if a_scale is not None else None
-    d.a_scale_mode = FP4_SCALE_ROW if (a_scale is not None and a_scale.numel() > 1) else FP4_SCALE_TENSOR
+    d.a_scale_mode = FP4_SCALE_ROW if a_scale_mode == "row" else FP4_SCALE_TENSOR
     d.w = w_packed.data_ptr()
     d.ldw = _ld(w_packed)
     d.w_grid = w_grid

@@ -71,6 +71,8 @@ SIGNATURES = {
                                      ctypes.c_size_t, P]),
     "fp4_gemm": (I32, [ctypes.POINTER(fp4_gemm_desc), P]),
     "fp4_gemm_swiglu_quant": (I32, [ctypes.POINTER(fp4_swiglu_desc), P]),
+    "fp4_set_split_limit": (I32, [I64]),
+    "fp4_nf4_grid": (I32, [ctypes.POINTER(fp4_grid)]),
 }
 
 

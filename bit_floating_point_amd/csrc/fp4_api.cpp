@@ -490,6 +490,42 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
     return fail(FP4_ERR_UNSUPPORTED, "W4A4 with minifloat weights other than E2M1 is not implemented");
 }
 
+// Standard normal quantile: the x with Phi(x) = 0.5 erfc(-x / sqrt 2) = p, by bisection
+// in binary64 until the bracket cannot shrink (monotone, so the last midpoint is within
+// one binary64 step of the root for 0 < p < 1).
+static double normal_quantile(double p) {
+    double lo = -40.0, hi = 40.0;
+    for (int i = 0; i < 200; i++) {
+        const double mid = 0.5 * (lo + hi);
+        if (mid == lo || mid == hi) break;
+        if (0.5 * std::erfc(-mid / std::sqrt(2.0)) < p) lo = mid;
+        else hi = mid;
+    }
+    return 0.5 * (lo + hi);
+}
+
+// Round a binary64 value in the binary16 normal range to the nearest binary16 value,
+// ties to even (11 significant bits; the current rounding mode is round-to-nearest-even).
+static double round_to_f16(double v) {
+    int e = 0;
+    const double f = std::frexp(v, &e);  // v = f 2^e, 0.5 <= |f| < 1
+    return std::ldexp(std::nearbyint(std::ldexp(f, 11)), e - 11);
+}
+
+fp4_status fp4_nf4_grid(fp4_grid* out) {
+    if (!out) return fail(FP4_ERR_INVALID_ARG, "null grid");
+    std::memset(out, 0, sizeof(*out));
+    out->kind = FP4_GRID_LUT16;
+    const double z = normal_quantile(15.5 / 16.0);
+    for (int i = 0; i < 16; i++) out->lut[i] = (float)round_to_f16(normal_quantile((i + 0.5) / 16.0) / z);
+    return ok();
+}
+
+fp4_status fp4_set_split_limit(int64_t bytes) {
+    set_split_limit(bytes);
+    return ok();
+}
+
 fp4_status fp4_gemm_swiglu_quant(const fp4_swiglu_desc* d, void* stream) {
     if (!d) return fail(FP4_ERR_INVALID_ARG, "null descriptor");
     if (d->M < 0 || d->N < 0 || d->K <= 0) return fail(FP4_ERR_INVALID_ARG, "bad sizes");

@@ -21,6 +21,7 @@
 // layer's E2M1 quantization in the epilogue (GLU), and the FP8 E4M3 x E4M3 product
 // (F8: one code per byte, 64-code steps; fp32 sums not exact, so held to a tolerance).
 #include <algorithm>
+#include <atomic>
 
 #include "fp4_device.h"
 
@@ -616,11 +617,18 @@ static hipError_t launch_block(const GemmParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Byte limit of one launch's A and W ranges (the 32-bit buffer range by default); a
+// smaller limit only splits a product into more row blocks, with the same result.
+static std::atomic<int64_t> g_split_limit{kMaxBufBytes};
+
+void set_split_limit(int64_t bytes) { g_split_limit.store(bytes > 0 && bytes < kMaxBufBytes ? bytes : kMaxBufBytes); }
+
 template <int F8>
 static hipError_t launch_split(const GemmParams& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
-    const int64_t mstep = std::max<int64_t>(256, kMaxBufBytes / std::max<int64_t>(p.lda, 1) / 256 * 256);
-    const int64_t nstep = std::max<int64_t>(256, kMaxBufBytes / std::max<int64_t>(p.ldw, 1) / 256 * 256);
+    const int64_t lim = g_split_limit.load();
+    const int64_t mstep = std::max<int64_t>(256, lim / std::max<int64_t>(p.lda, 1) / 256 * 256);
+    const int64_t nstep = std::max<int64_t>(256, lim / std::max<int64_t>(p.ldw, 1) / 256 * 256);
     const size_t ysz = p.y_bf16 ? 2 : 4;
     for (int64_t m0 = 0; m0 < p.M; m0 += mstep) {
         for (int64_t n0 = 0; n0 < p.N; n0 += nstep) {
@@ -628,6 +636,7 @@ static hipError_t launch_split(const GemmParams& p, hipStream_t s) {
             q.M = std::min(mstep, p.M - m0);
             q.N = std::min(nstep, p.N - n0);
             q.a = reinterpret_cast<const uint8_t*>(p.a) + m0 * p.lda;
+            if (p.a_row) q.a_scale = p.a_scale + m0;  // per-token scales of this row block
             q.w = p.w + n0 * p.ldw;
             if (p.w_mode == 1) q.w_scales = reinterpret_cast<const float*>(p.w_scales) + n0;
             q.y = reinterpret_cast<uint8_t*>(p.y) + (m0 * p.ldy + n0) * ysz;
@@ -656,8 +665,9 @@ static void launch_glu_cfg(const GemmParams& p, const GluParams& gp, hipStream_t
 hipError_t launch_w4a4_swiglu(const GemmParams& p, const GluParams& gp, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     const int64_t cus = cu_count();
-    const int64_t mstep = std::max<int64_t>(256, kMaxBufBytes / std::max<int64_t>(p.lda, 1) / 256 * 256);
-    const int64_t nstep = std::max<int64_t>(128, kMaxBufBytes / std::max<int64_t>(p.ldw, 1) / 128 * 128);
+    const int64_t lim = g_split_limit.load();
+    const int64_t mstep = std::max<int64_t>(256, lim / std::max<int64_t>(p.lda, 1) / 256 * 256);
+    const int64_t nstep = std::max<int64_t>(128, lim / std::max<int64_t>(p.ldw, 1) / 128 * 128);
     for (int64_t m0 = 0; m0 < p.M; m0 += mstep) {
         for (int64_t n0 = 0; n0 < p.N; n0 += nstep) {
             GemmParams q = p;

@@ -352,6 +352,25 @@ typedef struct {
  * h_packed 16-byte aligned.  Empty M or N returns FP4_OK with nothing launched. */
 fp4_status fp4_gemm_swiglu_quant(const fp4_swiglu_desc* d, void* stream);
 
+/* NF4 lookup grid ([Overview], NF4: 16 levels placed at quantiles of the normal
+ * distribution).  Fills *out (host) with kind FP4_GRID_LUT16 and
+ *   lut[i] = RNE_binary16( Phi^-1((i + 1/2) / 16) / Phi^-1(15.5 / 16) ),  i = 0..15:
+ * symmetric, end points -1 and +1, no exact zero; every level is a binary16 value, so
+ * levels and the midpoints between neighbours are exact in binary32.  Phi^-1 is found
+ * by bisection on Phi(x) = erfc(-x / sqrt 2) / 2 in binary64.  Host only, no launch.
+ * Returns FP4_ERR_INVALID_ARG for a null pointer. */
+fp4_status fp4_nf4_grid(fp4_grid* out);
+
+/* Launch splitting of the W4A4 / W8A8 matrix-core products (host setting, process-wide).
+ * Those kernels address each operand through a 32-bit buffer range, so a product whose A
+ * or W spans more than `bytes` is launched as several row blocks of A and W (the per-row
+ * scales, per-token scales and Y offset with them); the result is the same bit for bit.
+ * The default, and the value set by bytes <= 0 or >= 0x7fff0000, is 0x7fff0000.  A
+ * smaller limit lets a test exercise the block split on small shapes.  Takes effect for
+ * launches made after it returns; not synchronised with calls running on other threads.
+ * Always returns FP4_OK. */
+fp4_status fp4_set_split_limit(int64_t bytes);
+
 #ifdef __cplusplus
 }
 #endif

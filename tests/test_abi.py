@@ -23,7 +23,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = L.load()
     names = _declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES)
@@ -45,6 +45,29 @@ def test_struct_layouts_match_header(tmp_path):
             L.fp4_gemm_desc.y_dtype.offset, ctypes.sizeof(L.fp4_swiglu_desc), L.fp4_swiglu_desc.out_shift.offset,
             L.fp4_swiglu_desc.ldh.offset]
     assert got == want
+
+
+def test_nf4_grid_matches_oracle_table():
+    """The library's host NF4 table (bisection on erfc, manual binary16 rounding) equals
+    the oracle's (scipy's ndtri, numpy's binary16 cast): two independent computations of
+    the same closed form."""
+    import numpy as np
+    import oracle as O
+    lib = L.load()
+    g = L.fp4_grid()
+    assert lib.fp4_nf4_grid(ctypes.byref(g)) == L.FP4_OK
+    assert g.kind == L.FP4_GRID_LUT16 and g.e == 0 and g.m == 0 and g.reserved == 0
+    got = np.array(list(g.lut), dtype=np.float64)
+    assert np.array_equal(got, O.nf4_table())
+    assert got[0] == -1.0 and got[-1] == 1.0 and np.array_equal(got, -got[::-1])
+    assert lib.fp4_nf4_grid(None) == L.FP4_ERR_INVALID_ARG
+
+
+def test_split_limit_hook_accepts_any_value():
+    lib = L.load()
+    for v in (0, -5, 4096, 1 << 40):
+        assert lib.fp4_set_split_limit(v) == L.FP4_OK
+    assert lib.fp4_set_split_limit(0) == L.FP4_OK
 
 
 def test_status_strings():

@@ -683,3 +683,125 @@ def test_w4a4_per_token_scales():
     yp = O.w4a4_epilogue_f32(acc, p2, ws)
     yu = O.w4a4_epilogue_f32(acc, np.float32(1.0), ws)
     assert np.array_equal(yp, (yu * p2[:, None]).astype(np.float32))
+
+
+# ------------------------------------- ROW / GROUP quantize, binary16, dequantize --------
+def _hexf32(tok):
+    return np.uint32(int(tok, 16)).view(np.float32)
+
+
+def _group_golden():
+    X, C, P, S = [], [], [], []
+    for r in _read_golden("quantize_group_f16.txt"):
+        a, b, c, d = r.split("|")
+        X.append([np.float32(t) if t != "-0.0" else np.float32(-0.0) for t in a.split()])
+        C.append([int(t) for t in b.split()])
+        P.append([int(t, 16) for t in c.split()])
+        S.append([int(t, 16) for t in d.split()])
+    return (np.array(X, np.float32), np.array(C, np.uint8), np.array(P, np.uint8), np.array(S, np.uint16))
+
+
+def _row_golden():
+    X, C, P, S = [], [], [], []
+    for r in _read_golden("quantize_row_f32.txt"):
+        a, b, c, d = r.split("|")
+        X.append([np.float32(t) for t in a.split()])
+        C.append([int(t) for t in b.split()])
+        P.append([int(t, 16) for t in c.split()])
+        S.append(int(d.strip(), 16))
+    return (np.array(X, np.float32), np.array(C, np.uint8), np.array(P, np.uint8), np.array(S, np.uint32))
+
+
+def _matches_group_golden(quantize_pack):
+    x, codes, packed, sbits = _group_golden()
+    p, s = quantize_pack(x, O.minifloat(2, 1), "group", 8, "f16")
+    return (np.array_equal(p, packed) and np.array_equal(O.unpack(p), codes)
+            and np.array_equal(np.asarray(s).view(np.uint16).reshape(sbits.shape), sbits))
+
+
+def test_group_f16_quantize_golden():
+    """GROUP quantization with stored binary16 scales against a hand-worked 2x16 case."""
+    assert _matches_group_golden(O.quantize_pack)
+
+
+def test_row_quantize_golden():
+    x, codes, packed, sbits = _row_golden()
+    p, s = O.quantize_pack(x, O.minifloat(2, 1), "row")
+    assert np.array_equal(O.unpack(p), codes)
+    assert np.array_equal(p, packed)
+    assert np.array_equal(np.asarray(s, np.float32).view(np.uint32), sbits)
+
+
+def test_rne_f16_golden():
+    rows = [r.split("|") for r in _read_golden("rne_f16.txt")]
+    src = np.array([int(a, 16) for a, _, _ in rows], dtype=np.uint32).view(np.float32)
+    want = np.array([int(b, 16) for _, b, _ in rows], dtype=np.uint16)
+    with np.errstate(over="ignore"):
+        got = O.rne_f16(src).view(np.uint16)
+    assert np.array_equal(got, want), [(hex(a), hex(b)) for a, b in zip(got, want) if a != b]
+
+
+def _dequant_golden():
+    out = []
+    for r in _read_golden("dequantize_e2m1.txt"):
+        mode, sc, cs, vs = [t.strip() for t in r.split("|")]
+        codes = np.array([int(t) for t in cs.split()], np.uint8).reshape(1, -1)
+        vals = np.array([int(t, 16) for t in vs.split()], np.uint32)
+        out.append((mode, sc.split(), codes, vals))
+    return out
+
+
+def test_dequantize_golden():
+    for mode, sc, codes, vals in _dequant_golden():
+        packed = O.pack(codes)
+        if mode == "tensor":
+            v = O.dequantize(packed, O.minifloat(2, 1), "tensor", np.array([_hexf32(sc[0])], np.float32))
+        else:
+            s16 = np.array([int(t, 16) for t in sc], np.uint16).view(np.float16).reshape(1, -1)
+            v = O.dequantize(packed, O.minifloat(2, 1), "group", s16, group=8)
+        assert np.array_equal(np.asarray(v, np.float32).reshape(-1).view(np.uint32), vals), mode
+
+
+class _NumpyTiledScales:
+    """numpy, except that repeat along axis 1 tiles instead (scales laid out
+    [s0, s1, s0, s1, ...] instead of [s0 x group, s1 x group]): a planted mistake."""
+
+    def __getattr__(self, k):
+        return getattr(np, k)
+
+    @staticmethod
+    def repeat(a, n, axis=None):
+        if axis == 1:
+            return np.tile(np.asarray(a), (1, n))
+        return np.repeat(a, n, axis=axis)
+
+
+def test_planted_oracle_mistakes_fail_the_pins(monkeypatch):
+    """Each plausible mistake in the ROW/GROUP quantizer and the dequantizer, planted in the
+    oracle on the CPU, fails a golden pin above."""
+    # 1. group scales tiled instead of repeated along the row
+    with monkeypatch.context() as m:
+        m.setattr(O, "np", _NumpyTiledScales())
+        assert not _matches_group_golden(O.quantize_pack)
+    # 2. quantizing with the unrounded fp32 scale instead of the stored binary16 one
+    with monkeypatch.context() as m:
+        m.setattr(O, "rne_f16", lambda v: np.asarray(v, np.float32))
+        x, codes, _, _ = _group_golden()
+        p, _ = O.quantize_pack(x, O.minifloat(2, 1), "group", 8, "f16")
+        assert not np.array_equal(O.unpack(p), codes)
+    # 3. x / s in place of x * fl32(1/s) changes no code of these cases, but dropping the
+    #    sign of zero does: codes of -0.0 and of negatives rounding to 0 must be 8
+    x, codes, _, _ = _row_golden()
+    c = O.quantize(np.abs(x), 1, O.minifloat(2, 1))
+    assert not np.array_equal(c, codes)
+    # 4. dequantize with tiled scales, or with the sign bit ignored
+    (_, _, c_t, v_t), (_, sc_g, c_g, v_g) = _dequant_golden()
+    s16 = np.array([int(t, 16) for t in sc_g], np.uint16).view(np.float16).reshape(1, -1)
+    with monkeypatch.context() as m:
+        m.setattr(O, "np", _NumpyTiledScales())
+        v = O.dequantize(O.pack(c_g), O.minifloat(2, 1), "group", s16, group=8)
+        assert not np.array_equal(np.asarray(v, np.float32).reshape(-1).view(np.uint32), v_g)
+    v = O.dequantize(O.pack(c_t & 7), O.minifloat(2, 1), "tensor", np.array([_hexf32("3e4ccccd")], np.float32))
+    assert not np.array_equal(np.asarray(v, np.float32).reshape(-1).view(np.uint32), v_t)
+    # 5. a double rounding binary64 -> binary32 -> binary16 is caught by the tie rows
+    assert O.rne_f16(np.float32(1 + 2.0 ** -11)).view(np.uint16) == 0x3C00
