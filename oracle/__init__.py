@@ -444,17 +444,21 @@ def two_mode_values(packed, scales, group: int) -> np.ndarray:
     return np.where((codes >> 3) & 1, -v, v).astype(np.float32)
 
 
-def gemm_w4a16_two_mode(x, w_packed, w_scales, group: int):
+def gemm_w4a16_two_mode(x, w_packed, w_scales, group: int, absolute: bool = False):
     """r[m, n] = sum_g |s[n, g]| * sum_{k in g} x[m, k] * g_mode(n,g)(c[n, k]) in binary64
-    (the W4A16 product with the grid chosen per group by the scale's sign bit)."""
+    (the W4A16 product with the grid chosen per group by the scale's sign bit);
+    absolute=True sums magnitudes instead."""
     X = f32(x).astype(np.float64)
+    if absolute:
+        X = np.abs(X)
     codes = unpack(w_packed)
     N, K = codes.shape
     s = np.asarray(w_scales).astype(np.float32).reshape(N, K // group)
     mode = np.repeat(np.signbit(s), group, axis=1)
     e2, e1 = minifloat(*TWO_MODES[0]), minifloat(*TWO_MODES[1])
     V = np.where(mode, e1.array[codes & 7], e2.array[codes & 7])
-    V = np.where((codes >> 3) & 1, -V, V)
+    if not absolute:
+        V = np.where((codes >> 3) & 1, -V, V)
     mag = np.abs(s).astype(np.float64)
     out = np.zeros((X.shape[0], N), dtype=np.float64)
     for gi in range(K // group):
@@ -612,13 +616,16 @@ def _weight_values(packed, grid: Grid) -> np.ndarray:
     return grid.decode(unpack_codes(packed, grid))
 
 
-def gemm_w4a16(x, w_packed, w_grid: Grid, mode: str, w_scales, group: int = 0):
+def gemm_w4a16(x, w_packed, w_grid: Grid, mode: str, w_scales, group: int = 0, absolute: bool = False):
     """r[m, n] = sum_g s[n, g] * sum_{k in g} x[m, k] * g(c[n, k])  in binary64.
-    x: binary32 values (bf16 activations widened exactly)."""
+    x: binary32 values (bf16 activations widened exactly).  absolute=True evaluates the
+    same sum over |x|, |g(c)| and |s| (the magnitude that bounds rounding errors)."""
     X = f32(x).astype(np.float64)
     V = _weight_values(w_packed, w_grid)
     N, K = V.shape
     s = np.asarray(w_scales).astype(np.float64)
+    if absolute:
+        X, V, s = np.abs(X), np.abs(V), np.abs(s)
     if mode == "tensor":
         return (X @ V.T) * s.reshape(-1)[0]
     if mode == "row":
@@ -633,7 +640,7 @@ def gemm_w4a16(x, w_packed, w_grid: Grid, mode: str, w_scales, group: int = 0):
 
 
 def gemm_w4a4(a_packed, a_grid: Grid, a_scale, w_packed, w_grid: Grid, mode: str,
-              w_scales, group: int = 0):
+              w_scales, group: int = 0, absolute: bool = False):
     """Both operands quantized.  Returns (r, acc):
     r = a * sum_(blocks) s[n, b] * sum_{k in b} A_q[m, k] * W_q[n, k]  (binary64);
     acc = the unscaled code product sum_k A_q W_q (exact in binary64 for the 4-bit
@@ -641,11 +648,17 @@ def gemm_w4a4(a_packed, a_grid: Grid, a_scale, w_packed, w_grid: Grid, mode: str
     2^53; for FP8 a binary64 sum)."""
     A = _weight_values(a_packed, a_grid)
     V = _weight_values(w_packed, w_grid)
+    if absolute:  # the same sums over magnitudes (bounds rounding errors)
+        A, V = np.abs(A), np.abs(V)
     N, K = V.shape
     # one activation scale, or one per row (token) of A ([Overview] per-token granularity)
     a_arr = np.asarray(a_scale, dtype=np.float32).astype(np.float64)
+    if absolute:
+        a_arr = np.abs(a_arr)
     a = a_arr.reshape(-1, 1) if a_arr.size > 1 else float(a_arr.reshape(-1)[0])
     s = np.asarray(w_scales).astype(np.float64)
+    if absolute:
+        s = np.abs(s)
     if mode in ("tensor", "row"):
         acc = A @ V.T
         sv = s.reshape(-1)[0] if mode == "tensor" else s.reshape(1, N)
@@ -730,3 +743,44 @@ def rel_err(y, r) -> float:
     d = np.max(np.abs(np.asarray(y, dtype=np.float64) - r)) if r.size else 0.0
     den = np.max(np.abs(r)) if r.size else 1.0
     return float(d / den) if den > 0 else float(d)
+
+
+# ----------------------------------------------------------------------------------
+# Elementwise error bounds (test tolerances).  A float computation whose additions and
+# multiplications are each rounded (relative error <= u = 2^-24 when rounded to nearest)
+# and whose products of terms are exact satisfies, for each output,
+# |y - r| <= d * u * S + O(u^2), with S the same sum over magnitudes
+# (gemm_*(..., absolute=True)) and d the largest number of roundings on the path from one
+# product to the output (Higham, Accuracy and Stability of Numerical Algorithms,
+# sections 3.1 and 4.2: the error bounds of recursive and tree summation).  The callers
+# give each output its bound d * u * S (+ any further term of their arithmetic).
+# ----------------------------------------------------------------------------------
+U32 = 2.0 ** -24
+
+
+def elementwise_excess(y32, r, bound) -> float:
+    """max over outputs of |y32 - r| / bound; <= 1 means every output is within its
+    bound."""
+    y = np.asarray(y32, np.float64)
+    r = np.asarray(r, np.float64)
+    bound = np.broadcast_to(np.asarray(bound, np.float64), r.shape)
+    err = np.abs(y - r)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(err == 0, 0.0, err / bound)
+    return float(np.max(q)) if q.size else 0.0
+
+
+def bf16_ulps_from_rounded(yb_bits, r, bound):
+    """For the outputs whose binary32 error bound is at most 2^-10 |r| (a quarter of a
+    bfloat16 ulp or less), the distance in bfloat16 ulps between the output's bf16 bits
+    and RNE_bf16(r).  Returns (largest distance, number of outputs checked)."""
+    r = np.asarray(r, np.float64)
+    mask = np.broadcast_to(np.asarray(bound, np.float64), r.shape) <= 2.0 ** -10 * np.abs(r)
+    if not mask.any():
+        return 0, 0
+    f, e = np.frexp(r[mask])  # RNE to 8 significant bits straight from binary64
+    want = rne_bf16_bits(np.ldexp(np.rint(np.ldexp(f, 8)), e - 8).astype(np.float32)).astype(np.int64)
+    got = np.asarray(yb_bits, np.uint16)[mask].astype(np.int64)
+    # same sign (the bound keeps y32 on r's side of zero): compare magnitudes
+    dist = np.abs((got & 0x7FFF) - (want & 0x7FFF)) + 0x10000 * ((got ^ want) >> 15 & 1)
+    return int(dist.max()), int(mask.sum())

@@ -805,3 +805,57 @@ def test_planted_oracle_mistakes_fail_the_pins(monkeypatch):
     assert not np.array_equal(np.asarray(v, np.float32).reshape(-1).view(np.uint32), v_t)
     # 5. a double rounding binary64 -> binary32 -> binary16 is caught by the tie rows
     assert O.rne_f16(np.float32(1 + 2.0 ** -11)).view(np.uint16) == 0x3C00
+
+
+# ------------------------------------------------ elementwise GEMM error bounds ---------
+def test_absolute_gemm_is_the_sum_of_magnitudes():
+    rng = np.random.default_rng(4)
+    e2 = O.minifloat(2, 1)
+    w = rng.normal(0, 1, (6, 64)).astype(np.float32)
+    x = rng.normal(0, 1, (3, 64)).astype(np.float32)
+    p, s = O.quantize_pack(w, e2, "group", 32)
+    V = e2.decode(O.unpack(p)) * np.repeat(s.astype(np.float64), 32, axis=1)
+    want = np.abs(x.astype(np.float64)) @ np.abs(V).T
+    assert np.allclose(O.gemm_w4a16(x, p, e2, "group", s, 32, absolute=True), want, rtol=1e-15, atol=0)
+    # with non-negative operands the two agree; otherwise |r| <= S
+    r = O.gemm_w4a16(x, p, e2, "group", s, 32)
+    assert np.all(np.abs(r) <= want * (1 + 1e-15))
+    pa = O.pack(O.unpack(p) & 7)
+    assert np.array_equal(O.gemm_w4a16(np.abs(x), pa, e2, "group", s, 32),
+                          O.gemm_w4a16(np.abs(x), pa, e2, "group", s, 32, absolute=True))
+    ap, asc = O.quantize_pack(x, e2, "tensor")
+    ra, _ = O.gemm_w4a4(ap, e2, asc[0], p, e2, "group", s, group=32, absolute=True)
+    A = e2.decode(O.unpack(ap)) * float(asc[0])
+    assert np.allclose(ra, np.abs(A) @ np.abs(V).T, rtol=1e-15, atol=0)
+
+
+def test_elementwise_bound_holds_for_binary32_summation_and_catches_an_error():
+    """Recursive binary32 summation of K exact products stays within d = K of the bound;
+    one output perturbed by 1e-3 of a small value's magnitude sum is flagged."""
+    rng = np.random.default_rng(5)
+    K = 4096
+    x = rng.normal(0, 1, (8, K)).astype(np.float32)
+    w = rng.normal(0, 1, (16, K)).astype(np.float32)
+    xb = O.bf16_bits_to_f32(O.rne_bf16_bits(x))
+    wq = (np.round(w * 2) / 2).astype(np.float32)  # products of bf16 and half-integers: exact
+    r = xb.astype(np.float64) @ wq.astype(np.float64).T
+    S = np.abs(xb).astype(np.float64) @ np.abs(wq).astype(np.float64).T
+    y = np.zeros(r.shape, np.float32)
+    for k in range(K):  # one rounding per addition
+        y = (y + (xb[:, k:k + 1] * wq[None, :, k]).reshape(8, 16)).astype(np.float32)
+    assert O.elementwise_excess(y, r, K * O.U32 * S) <= 1.0
+    y2 = y.copy()
+    y2[3, 5] += np.float32(1e-3 * S[3, 5])
+    assert O.elementwise_excess(y2, r, K * O.U32 * S) > 1.0
+
+
+def test_bf16_ulp_distance():
+    r = np.array([1.0, 1.0 + 2.0 ** -9, 3.0, -2.5], np.float64)  # 1 + 2^-9: tie -> 1.0
+    S = np.abs(r)
+    bits = O.rne_bf16_bits(np.array([1.0, 1.0, 3.0 + 2 ** -6, -2.5], np.float32))
+    # 3 + 2^-6 is one bf16 ulp (2^-6 at 2..4) above 3.0
+    assert O.bf16_ulps_from_rounded(bits, r, 0 * S) == (1, 4)
+    far = O.rne_bf16_bits(np.array([1.0, 1.0, 3.0, -2.5 - 2 ** -5], np.float32))
+    assert O.bf16_ulps_from_rounded(far, r, 0 * S) == (2, 4)
+    # outputs whose binary32 bound exceeds a quarter ulp are not checked
+    assert O.bf16_ulps_from_rounded(far, r, S * 1e-2)[1] == 0
