@@ -19,7 +19,7 @@ from ._lib import (FP4Error, FP4_BF16, FP4_F16, FP4_F32, FP4_PACKED, FP4_REDUCE_
                    FP4_SCALE_TENSOR)
 
 __all__ = ["FP4Error", "grid_minifloat", "grid_lut", "grid_nf4", "grid_two_mode", "nf4_values", "set_split_limit", "gran", "fp4_calibrate", "fp4_quantize_pack",
-           "fp4_dequantize", "fp4_preshift_weights", "fp4_search_format", "fp4_gemm",
+           "fp4_dequantize", "fp4_preshift_weights", "fp4_search_format", "fp4_search_format_static", "fp4_gemm",
            "fp4_gemm_swiglu_quant", "fp4_search_activations", "search_results_host", "E2M1", "E1M2", "E3M0"]
 
 
@@ -193,6 +193,24 @@ def fp4_search_format(w: torch.Tensor, formats=(E1M2, E2M1, E3M0), nclips: int =
                                       _stream(dev)), "fp4_search_format")
     return results, packed
 
+
+
+def fp4_search_format_static(w: torch.Tensor, formats=(E1M2, E2M1, E3M0), nclips: int = 100,
+                             clip_lo: float = 0.5, clip_hi: float = 1.0, results: torch.Tensor | None = None,
+                             packed: torch.Tensor | None = None):
+    """fp4_search_format on the library's static scratch (no workspace is allocated;
+    calls on one GPU must not overlap).  results / packed may be given to make the call
+    allocate nothing at all.  Returns (results buffer, packed [ntensors, numel/2])."""
+    T, numel = w.shape
+    dev = w.device
+    fm = (ctypes.c_int32 * (2 * len(formats)))(*[v for f in formats for v in f])
+    if results is None:
+        results = torch.empty(T * SEARCH_RESULT_BYTES, dtype=torch.uint8, device=dev)
+    if packed is None:
+        packed = torch.empty((T, numel // 2), dtype=torch.uint8, device=dev)
+    L.check(L.lib().fp4_search_format_static(_ptr(w), T, numel, fm, len(formats), nclips, clip_lo, clip_hi,
+                                             _ptr(results), _ptr(packed), _stream(dev)), "fp4_search_format_static")
+    return results, packed
 
 
 def fp4_search_activations(x: torch.Tensor, unit: str = "row", first_rows: int = 0, formats=(E1M2, E2M1, E3M0),

@@ -67,6 +67,7 @@ SIGNATURES = {
     "fp4_preshift_weights": (I32, [P, I64, I64, I64, P, fp4_grid, fp4_grid, fp4_gran, P, P, P, I64, P, P]),
     "fp4_search_workspace_size": (ctypes.c_size_t, [I64, I64, I32, I32]),
     "fp4_search_format": (I32, [P, I64, I64, P, I32, I32, F32, F32, P, P, P, ctypes.c_size_t, P]),
+    "fp4_search_format_static": (I32, [P, I64, I64, P, I32, I32, F32, F32, P, P, P]),
     "fp4_search_activations": (I32, [P, I32, I64, I64, I64, I32, I64, P, I32, I32, F32, F32, P, P, I64, P,
                                      ctypes.c_size_t, P]),
     "fp4_gemm": (I32, [ctypes.POINTER(fp4_gemm_desc), P]),

@@ -352,6 +352,30 @@ fp4_status fp4_search_format(const float* w, int64_t ntensors, int64_t numel, co
                       "fp4_search_format");
 }
 
+fp4_status fp4_search_format_static(const float* w, int64_t ntensors, int64_t numel, const int32_t* formats_em,
+                                    int32_t nformats, int32_t nclips, float clip_lo, float clip_hi,
+                                    fp4_search_result* results, uint8_t* packed, void* stream) {
+    if (!w || !formats_em || !results || !packed) return fail(FP4_ERR_INVALID_ARG, "null pointer");
+    if (ntensors < 0 || numel <= 0 || numel % 16 != 0)
+        return fail(FP4_ERR_INVALID_ARG, "numel must be a positive multiple of 16");
+    SearchCandidates c;
+    fp4_status st = search_candidates(formats_em, nformats, nclips, clip_lo, clip_hi, &c);
+    if (st) return st;
+    if (!aligned16(w) || !aligned16(packed) || !aligned16(results))
+        return fail(FP4_ERR_ALIGNMENT, "w, packed and results must be 16-byte aligned");
+    const size_t need = search_workspace_bytes(ntensors, numel, c.nformats, c.nclips);
+    if (need > kSearchScratchBytes)
+        return fail(FP4_ERR_WORKSPACE, "this search needs %zu bytes of scratch; the static scratch holds %zu "
+                    "(use fp4_search_format with a workspace)", need, kSearchScratchBytes);
+    if (ntensors == 0) return ok();
+    void* ws = nullptr;
+    if ((st = hip_status(search_scratch(&ws), "fp4_search_format_static: scratch address"))) return st;
+    SearchInput in{w, 0, 1, numel, ntensors, numel, 1};
+    return hip_status(launch_search(in, c, (double)clip_lo, (double)clip_hi, results, packed, numel / 2, ws,
+                                    (hipStream_t)stream),
+                      "fp4_search_format_static");
+}
+
 fp4_status fp4_search_activations(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                                   int32_t unit, int64_t first_rows, const int32_t* formats_em, int32_t nformats,
                                   int32_t nclips, float clip_lo, float clip_hi, fp4_search_result* results,

@@ -121,5 +121,11 @@ struct SearchInput {
 };
 hipError_t launch_search(const SearchInput& in, const SearchCandidates& c, double clip_lo, double clip_hi,
                          void* results, uint8_t* packed, int64_t ldp, void* ws, hipStream_t s);
+// The allocation-free search's scratch: a file-scope device array of this many bytes,
+// one copy per GPU; search_scratch() returns the current device's copy (looked up on the
+// first call on each device).
+constexpr size_t kSearchScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t search_scratch(void** ptr);
 
 }  // namespace fp4

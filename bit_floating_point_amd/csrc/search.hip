@@ -28,6 +28,8 @@
 // rounding boundary.  The work is VALU-bound (binary64 add throughput).
 #include <algorithm>
 
+#include <mutex>
+
 #include "fp4_device.h"
 
 namespace fp4 {
@@ -377,6 +379,31 @@ static int search_per(int64_t numel, int64_t nb) {
         }
     }
     return best;
+}
+
+// Scratch of the allocation-free search entry point: one copy per GPU, held until the
+// process ends.  Host code never uses the array's name as an address (on the host it
+// stands for the symbol, not for device memory): it looks up each device's copy with
+// hipGetSymbolAddress, once per device with that device current, and passes the
+// returned pointer to the kernels.
+static __device__ __align__(256) uint8_t scratch[kSearchScratchBytes];
+
+hipError_t search_scratch(void** ptr) {
+    static std::mutex mu;
+    static void* addr[kMaxDevices];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_search(const SearchInput& in, const SearchCandidates& c, double clip_lo, double clip_hi,

@@ -259,6 +259,22 @@ fp4_status fp4_search_format(const float* w, int64_t ntensors, int64_t numel,
                              uint8_t* packed, void* workspace, size_t ws_bytes,
                              void* stream);
 
+/* fp4_search_format without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, results and errors
+ * as fp4_search_format; the cross-workgroup partial sums live instead in a scratch array
+ * of 16 MiB that the library holds on each GPU it runs on until the process ends (one
+ * copy per GPU, located on the first call on that GPU).  Sizes whose
+ * fp4_search_workspace_size() exceeds 16 MiB return FP4_ERR_WORKSPACE before anything
+ * is launched (32 tensors of 4096 x 4096 with 3 formats x 100 clips need about 9.8 MB).
+ * Every call on one GPU shares that GPU's scratch and leaves its contents behind (each
+ * call clears what it needs zeroed): calls that may overlap on one GPU -- on different
+ * streams, or from several threads -- race and must be ordered by the caller. */
+fp4_status fp4_search_format_static(const float* w, int64_t ntensors, int64_t numel,
+                                    const int32_t* formats_em, int32_t nformats, int32_t nclips,
+                                    float clip_lo, float clip_hi, fp4_search_result* results,
+                                    uint8_t* packed, void* stream);
+
 /* The same search on activations ([FP4-LLM] search-based FP quantization applied to
  * activations as to weights; [Overview] static quantization from calibration data and
  * per-token granularity):

@@ -23,7 +23,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = L.load()
     names = _declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES)
@@ -61,6 +61,17 @@ def test_nf4_grid_matches_oracle_table():
     assert np.array_equal(got, O.nf4_table())
     assert got[0] == -1.0 and got[-1] == 1.0 and np.array_equal(got, -got[::-1])
     assert lib.fp4_nf4_grid(None) == L.FP4_ERR_INVALID_ARG
+
+
+def test_search_static_rejects_before_launch():
+    lib = L.load()
+    fm = (ctypes.c_int32 * 6)(1, 2, 2, 1, 3, 0)
+    # 64 tensors of 2^24 values need more than the 16 MiB static scratch
+    st = lib.fp4_search_format_static(FAKE, 64, 1 << 24, fm, 3, 100, 0.5, 1.0, FAKE, FAKE, None)
+    assert st == L.FP4_ERR_WORKSPACE and b"16777216" in lib.fp4_last_error()
+    assert lib.fp4_search_format_static(None, 1, 1024, fm, 3, 100, 0.5, 1.0, FAKE, FAKE, None) == L.FP4_ERR_INVALID_ARG
+    assert lib.fp4_search_format_static(FAKE, 1, 1000, fm, 3, 100, 0.5, 1.0, FAKE, FAKE, None) == L.FP4_ERR_INVALID_ARG
+    assert lib.fp4_search_format_static(ODD, 1, 1024, fm, 3, 100, 0.5, 1.0, FAKE, FAKE, None) == L.FP4_ERR_ALIGNMENT
 
 
 def test_split_limit_hook_accepts_any_value():
