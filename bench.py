@@ -85,6 +85,45 @@ def graph_time(torch, fn, iters: int, reps: int = 3) -> float:
     return best
 
 
+ROTATE_BYTES = 512 * 1024 * 1024  # rotated working set: twice the 256 MB Infinity Cache
+
+
+def rotations(nbytes: int, least: int = 2) -> int:
+    """Distinct input copies to rotate so that the copies together pass ROTATE_BYTES (no
+    launch reads data the Infinity Cache still holds from an earlier one)."""
+    return max(least, -(-ROTATE_BYTES // max(int(nbytes), 1)))
+
+
+def clones(t, n):
+    return [t] + [t.clone() for _ in range(n - 1)]
+
+
+_BENCH_LIB = None
+
+
+def stream_read_ceiling(torch, nbytes: int):
+    """Seconds per launch of a plain streaming read of nbytes (whole-line nontemporal 16-byte
+    loads, libfp4_bench.so) over rotating buffers, in the graph harness of the kernels:
+    the attainable HBM rate for a kernel that moves that many bytes."""
+    import ctypes
+    global _BENCH_LIB
+    if _BENCH_LIB is None:
+        _BENCH_LIB = ctypes.CDLL(os.path.join(ROOT, "bit_floating_point_amd", "libfp4_bench.so"))
+        _BENCH_LIB.fp4bench_stream_read.restype = ctypes.c_int
+        _BENCH_LIB.fp4bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    n = rotations(nbytes)
+    bufs = [torch.full((nbytes,), 1, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def fn(i):
+        st = torch.cuda.current_stream().cuda_stream
+        rc = _BENCH_LIB.fp4bench_stream_read(bufs[i % n].data_ptr(), nbytes, sink.data_ptr(), st)
+        assert rc == 0, rc
+    t = graph_time(torch, fn, 64)
+    del bufs
+    return t
+
+
 def roofline_entry(name, bound, achieved, peak, unit, seconds, work, work_unit, traffic=None, **extra):
     d = {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
          "frac": round(achieved / peak, 4), "us_per_launch": round(seconds * 1e6, 3), "work_per_launch": work,
@@ -256,10 +295,14 @@ def bench_decode(torch, F, steps, warmup):
                               "GB/s", t_q, qb, "bytes", traffic_for("quant.hip", "quantize_decode"))]
     for m in DEC_MS:
         flops = 2 * m * DEC_N * DEC_K
+        t_c = stream_read_ceiling(torch, gb[m])
         kernels.append(roofline_entry(f"w4a16 gemv M={m} (11008x4096, g128)", "hbm", gb[m] / t_g[m] / 1e9,
                                       HBM_PEAK_GBS, "GB/s", t_g[m], gb[m], "bytes",
                                       traffic_for("gemm_w4a16.hip", f"gemv_m{m}"),
-                                      tflops=round(flops / t_g[m] / 1e12, 3)))
+                                      tflops=round(flops / t_g[m] / 1e12, 3),
+                                      read_ceiling_gbs=round(gb[m] / t_c / 1e9, 1),
+                                      read_ceiling_us=round(t_c * 1e6, 3),
+                                      frac_of_read_ceiling=round(t_c / t_g[m], 4)))
     del W, P, S
     torch.cuda.empty_cache()
     return t_step, step_bytes, kernels
@@ -269,9 +312,10 @@ def bench_decode(torch, F, steps, warmup):
 def bench_preshift_w4a4(torch, F):
     M, N, K = 2048, 4096, 4096
     fe2 = F.grid_minifloat(2, 1)
-    NX = 16
-    Xs = [gen_activations(torch, M, K, 300 + i) for i in range(NX)]
-    Ws = [gen_normal(torch, (N, K), 0.02, 400 + i) for i in range(4)]
+    NX = rotations(M * K * 2)
+    Xs = clones(gen_activations(torch, M, K, 300), NX)
+    NWc = rotations(N * K * 4)
+    Ws = clones(gen_normal(torch, (N, K), 0.02, 400), NWc)
     chan = F.fp4_calibrate(Xs[0], "column", first_rows=128)
     k, a, wp, ws = F.fp4_preshift_weights(Ws[0], chan, fe2, fe2, F.gran("row"))
     ap, _ = F.fp4_quantize_pack(Xs[0], fe2, F.gran("tensor"), tensor_scale=a, col_shift=k)
@@ -281,14 +325,15 @@ def bench_preshift_w4a4(torch, F):
     b = 128 * K * 2 + K * 4
     out.append(roofline_entry("calibrate column amax (128 of 2048 tokens x 4096, bf16)", "hbm", b / t / 1e9,
                               HBM_PEAK_GBS, "GB/s", t, b, "bytes"))
-    packs = [torch.empty_like(wp) for _ in range(4)]
-    scs = [torch.empty_like(ws) for _ in range(4)]
-    ks = [torch.empty_like(k) for _ in range(4)]
-    As = [torch.empty_like(a) for _ in range(4)]
+    packs = [torch.empty_like(wp) for _ in range(NWc)]
+    scs = [torch.empty_like(ws) for _ in range(NWc)]
+    ks = [torch.empty_like(k) for _ in range(NWc)]
+    As = [torch.empty_like(a) for _ in range(NWc)]
 
     def pre(i):
-        F.fp4_preshift_weights(Ws[i % 4], chan, fe2, fe2, F.gran("row"), shift=ks[i % 4], act_scale=As[i % 4],
-                               packed=packs[i % 4], scales=scs[i % 4])
+        j = i % NWc
+        F.fp4_preshift_weights(Ws[j], chan, fe2, fe2, F.gran("row"), shift=ks[j], act_scale=As[j], packed=packs[j],
+                               scales=scs[j])
     t = graph_time(torch, pre, 16)
     b = N * K * 4 + N * K // 2 + N * 4 + K * 4 + K + 4
     out.append(roofline_entry("preshift + weight quantize E2M1 per-row (4096x4096 f32)", "hbm", b / t / 1e9,
@@ -345,15 +390,25 @@ def bench_prefill(torch, F):
                                   traffic_for("gemm_lut.hip", "nf4_qkv") if name == "qkv" else None))
         if name in ("qkv", "down"):
             xb = T * k * 2 + T * k // 2 + k
-            t = graph_time(torch, lambda i: F.fp4_quantize_pack(X, fe2, F.gran("tensor"), tensor_scale=a,
-                                                                col_shift=kk, packed=ap), 8)
+            nx = rotations(T * k * 2)
+            Xr = clones(X, nx)
+            apr = [torch.empty_like(ap) for _ in range(nx)]
+            t = graph_time(torch, lambda i: F.fp4_quantize_pack(Xr[i % nx], fe2, F.gran("tensor"), tensor_scale=a,
+                                                                col_shift=kk, packed=apr[i % nx]), 2 * nx)
             out.append(roofline_entry(f"activation quantize E2M1 + pre-shift ({T}x{k} bf16)", "hbm",
-                                      xb / t / 1e9, HBM_PEAK_GBS, "GB/s", t, xb, "bytes"))
+                                      xb / t / 1e9, HBM_PEAK_GBS, "GB/s", t, xb, "bytes", rotated_copies=nx))
+            del Xr, apr
             wb = n * k * 4 + n * k // 2 + n * 4 + k * 5 + 4
-            t = graph_time(torch, lambda i: F.fp4_preshift_weights(w, chan, fe2, fe2, F.gran("row"), shift=kk,
-                                                                   act_scale=a, packed=wp, scales=ws), 3)
+            nw = rotations(n * k * 4)
+            wr = clones(w, nw)
+            wpr = [torch.empty_like(wp) for _ in range(nw)]
+            wsr = [torch.empty_like(ws) for _ in range(nw)]
+            t = graph_time(torch, lambda i: F.fp4_preshift_weights(wr[i % nw], chan, fe2, fe2, F.gran("row"),
+                                                                   shift=kk, act_scale=a, packed=wpr[i % nw],
+                                                                   scales=wsr[i % nw]), 2 * nw)
             out.append(roofline_entry(f"preshift + weight quantize E2M1 per-row ({n}x{k} f32)", "hbm",
-                                      wb / t / 1e9, HBM_PEAK_GBS, "GB/s", t, wb, "bytes"))
+                                      wb / t / 1e9, HBM_PEAK_GBS, "GB/s", t, wb, "bytes", rotated_copies=nw))
+            del wr, wpr, wsr
         qa[name] = True
         del w, wp, wpn, y
         torch.cuda.empty_cache()
@@ -365,9 +420,15 @@ def bench_prefill(torch, F):
     del w
     apt, ast = F.fp4_quantize_pack(X1, fe2, F.gran("row"))
     xb = T * k * 2 + T * k // 2 + T * 4
-    t = graph_time(torch, lambda i: F.fp4_quantize_pack(X1, fe2, F.gran("row"), packed=apt, scales=ast), 8)
+    nx = rotations(T * k * 2)
+    Xr = clones(X1, nx)
+    aptr = [torch.empty_like(apt) for _ in range(nx)]
+    astr = [torch.empty_like(ast) for _ in range(nx)]
+    t = graph_time(torch, lambda i: F.fp4_quantize_pack(Xr[i % nx], fe2, F.gran("row"), packed=aptr[i % nx],
+                                                        scales=astr[i % nx]), 2 * nx)
     out.append(roofline_entry(f"activation quantize E2M1 per-token ({T}x{k} bf16)", "hbm", xb / t / 1e9,
-                              HBM_PEAK_GBS, "GB/s", t, xb, "bytes"))
+                              HBM_PEAK_GBS, "GB/s", t, xb, "bytes", rotated_copies=nx))
+    del Xr, aptr, astr
     y = torch.empty((T, n), dtype=torch.bfloat16, device="cuda")
     t = graph_time(torch, lambda i: F.fp4_gemm(apt, wp, ws, fe2, F.gran("row"), K=k, a_grid=fe2, a_scale=ast, y=y), 5)
     fl = 2 * T * n * k
@@ -412,8 +473,11 @@ def bench_swiglu(torch, F):
                                                  y=yg), 5)
     t_u = graph_time(torch, lambda i: F.fp4_gemm(ap, wup, wus, fe2, F.gran("row"), K=k, a_grid=fe2, a_scale=a,
                                                  y=yu), 5)
-    t_q = graph_time(torch, lambda i: F.fp4_quantize_pack(X2, fe2, F.gran("tensor"), tensor_scale=ad, col_shift=kd,
-                                                          packed=h), 8)
+    nx = rotations(T * n * 2)
+    X2r = clones(X2, nx)
+    t_q = graph_time(torch, lambda i: F.fp4_quantize_pack(X2r[i % nx], fe2, F.gran("tensor"), tensor_scale=ad,
+                                                          col_shift=kd, packed=h), 2 * nx)
+    del X2r
     fl = 2 * T * 2 * n * k
     sep = t_g + t_u + t_q
     out = [roofline_entry(f"w4a4 gate+up GEMM with SwiGLU + E2M1 quantize epilogue {T}x(2x{n})x{k}", "mfma",
@@ -439,7 +503,10 @@ def bench_two_mode(torch, F):
     for i in range(NP):
         F.fp4_quantize_pack(W, tm, g, packed=P[i], scales=S[i])
     qb, gb = decode_bytes()
-    t_q = graph_time(torch, lambda i: F.fp4_quantize_pack(W, tm, g, packed=P[i % NP], scales=S[i % NP]), 32)
+    nw = rotations(DEC_N * DEC_K * 4)
+    Wr = clones(W, nw)
+    t_q = graph_time(torch, lambda i: F.fp4_quantize_pack(Wr[i % nw], tm, g, packed=P[i % NP], scales=S[i % NP]), 32)
+    del Wr
     out = [roofline_entry("quantize_pack f32->two-mode E2M1/E1M2 g128 (11008x4096)", "hbm", qb / t_q / 1e9,
                           HBM_PEAK_GBS, "GB/s", t_q, qb, "bytes")]
     for m in DEC_MS:
@@ -470,7 +537,11 @@ def bench_fp8(torch, F):
         for i in range(NP):
             F.fp4_quantize_pack(W, fg, g, packed=P[i], scales=S[i])
         qb = DEC_N * DEC_K * 4 + cb + sb
-        t_q = graph_time(torch, lambda i: F.fp4_quantize_pack(W, fg, g, packed=P[i % NP], scales=S[i % NP]), 32)
+        nw = rotations(DEC_N * DEC_K * 4)
+        Wr = clones(W, nw)
+        t_q = graph_time(torch, lambda i: F.fp4_quantize_pack(Wr[i % nw], fg, g, packed=P[i % NP], scales=S[i % NP]),
+                         32)
+        del Wr
         out.append(roofline_entry(f"quantize_pack f32->{name} g128 (11008x4096)", "hbm", qb / t_q / 1e9,
                                   HBM_PEAK_GBS, "GB/s", t_q, qb, "bytes"))
         for mm in DEC_MS:
@@ -529,10 +600,28 @@ def bench_w8a8(torch, F):
     return out
 
 
-# VALU instructions per (element, candidate) in the search's inner loop, counted from the
-# gfx950 assembly of search_eval_kernel: E1M2 14.8, E2M1 12.3, E3M0 17.8 per element, plus
-# 2.4 per element for the per-candidate wavefront reduction; averaged over the formats
+# Operations per (element, candidate) fixed by the definition of the search ("首个支持4-bit
+# 浮点量化的LLM来了" page, the format/range search: quantize every weight with every
+# candidate and sum the squared error): the multiply y = w * r, the clip to Qmax, the
+# rounding to the nearest grid point, the dequantizing multiply g * s, the difference
+# from w, its square and its addition to the sum: 7.  Each is one lane operation (binary32
+# or binary64, not fused), whose peak rate is 256 CU x 4 SIMD x 16 lanes x 2.4 GHz.
+SEARCH_DEF_OPS_PER_EVAL = 7
+# VALU instructions the kernel issues per (element, candidate), counted from the gfx950
+# assembly of search_eval_kernel: E1M2 14.8, E2M1 12.3, E3M0 17.8 per element, plus 2.4 per
+# element for the per-candidate wavefront reduction, averaged over the formats (the
+# exact, order-independent MSE costs a double-double TwoSum per term)
 SEARCH_VALU_PER_EVAL = 17.4
+
+
+def search_entry(name, t, evals):
+    """The search against the ALU roofline of the operations its definition needs, with the
+    kernel's VALU issue utilisation beside it."""
+    return roofline_entry(name, "alu", evals * SEARCH_DEF_OPS_PER_EVAL / t / 1e12, VALU_PEAK_TOPS, "TOP/s", t,
+                          evals, "element-candidate evaluations", evals_per_s=evals / t,
+                          ops_per_eval_definition=SEARCH_DEF_OPS_PER_EVAL,
+                          valu_instructions_per_eval=SEARCH_VALU_PER_EVAL,
+                          valu_issue_frac=round(evals * SEARCH_VALU_PER_EVAL / t / 1e12 / VALU_PEAK_TOPS, 4))
 
 
 def bench_search(torch, F):
@@ -551,12 +640,9 @@ def bench_search(torch, F):
     e1.synchronize()
     t = e0.elapsed_time(e1) * 1e-3 / reps
     evals = T * numel * 3 * 100
-    ops = evals * SEARCH_VALU_PER_EVAL
     del w, packed
     torch.cuda.empty_cache()
-    out = [roofline_entry("format/clip search 32 x 4096x4096 (3 formats x 100 clips)", "alu", ops / t / 1e12,
-                          VALU_PEAK_TOPS, "TOP/s", t, evals, "element-candidate evaluations",
-                          evals_per_s=evals / t)]
+    out = [search_entry("format/clip search 32 x 4096x4096 (3 formats x 100 clips)", t, evals)]
     # the same search on activations: per token over the LLaMA-13B prefill input (4096 x
     # 5120 bf16), and once over its 128 calibration tokens with every token packed
     X = gen_activations(torch, 4096, 5120, 500)
@@ -567,10 +653,8 @@ def bench_search(torch, F):
               F.fp4_search_activations(X, unit, first_rows=first, workspace=ws, packed=packed))
         t = graph_time(torch, fn, 3)
         evals = (4096 if unit == "row" else 128) * 5120 * 3 * 100
-        ops = evals * SEARCH_VALU_PER_EVAL
-        out.append(roofline_entry(f"activation format/clip search, {name}, 4096x5120 bf16 (3 formats x 100 clips)",
-                                  "alu", ops / t / 1e12, VALU_PEAK_TOPS, "TOP/s", t, evals,
-                                  "element-candidate evaluations", evals_per_s=evals / t))
+        out.append(search_entry(f"activation format/clip search, {name}, 4096x5120 bf16 (3 formats x 100 clips)",
+                                t, evals))
     del X, ws, packed
     torch.cuda.empty_cache()
     return out
@@ -669,6 +753,15 @@ def main():
         "kernels": kernels,
     }
     line["roofline"]["kernel"] = dominant["kernel"]
+    for k in kernels:  # the metric's W4A4 half, on the LLaMA-13B prefill layer and the 2048-token GEMM
+        if k["kernel"].startswith("prefill layer: 4 W4A4"):
+            line["w4a4_prefill"] = {"workload": "LLaMA-13B prefill layer, 4096 tokens: QKV 15360x5120, up and gate "
+                                                "13824x5120, down 5120x13824, W4A4 E2M1 pre-shifted, bf16 out",
+                                    "value": k["achieved"], "unit": "TFLOP/s", "peak": k["peak"], "frac": k["frac"],
+                                    "us": k["us_per_launch"]}
+        if k["kernel"] == "w4a4 E2M1 GEMM 2048x4096x4096":
+            line["w4a4_2048x4096x4096"] = {"value": k["achieved"], "unit": "TFLOP/s", "peak": k["peak"],
+                                           "frac": k["frac"], "us": k["us_per_launch"]}
     print(json.dumps(line), flush=True)
 
 

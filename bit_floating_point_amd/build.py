@@ -53,10 +53,22 @@ def _compile(src: str) -> str:
     return obj
 
 
+# Measurement helper of bench.py (the streaming-read ceiling), a library of its own: it is
+# not part of libfp4 or of include/fp4.h.
+BENCH_SOURCE = "bench_read.hip"
+BENCH_LIB = os.path.join(HERE, "libfp4_bench.so")
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES) + 1, os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, SOURCES + [BENCH_SOURCE]))
+    bench_obj = objs.pop()
+    r = subprocess.run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", BENCH_LIB + ".tmp", bench_obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed (bench helper):\n" + r.stderr)
+    os.replace(BENCH_LIB + ".tmp", BENCH_LIB)
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -458,36 +458,45 @@ __global__ void __launch_bounds__(T) quantize_e2m1_g128_kernel(QuantParams p, in
 // group maximum: the 16-lane DPP maximum, then one exchange between the two rows of
 // 16).  Loads and code stores bypass the caches' retention (nontemporal): the weights
 // are read and the codes written once.  The arithmetic is that of the kernel above.
-template <int T>
-__global__ void __launch_bounds__(T) quantize_e2m1_g128_f32_kernel(QuantParams p, int chunks) {
+template <int T, int U>
+__global__ void __launch_bounds__(T) quantize_e2m1_g128_f32_kernel(QuantParams p, int chunks, int nunits) {
     typedef float f32x4v __attribute__((ext_vector_type(4)));
-    const int u = blockIdx.x;
-    const int row = u / chunks;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t c0 = (int64_t)(u - row * chunks) * (T * 8) + wave * 512 + 4 * lane;
-    const float* xr = reinterpret_cast<const float*>(p.x) + (int64_t)row * p.ldx;
-    f32x4v v[2];
+    f32x4v v[2 * U];
+    int row[U];
+    int64_t c0[U];
 #pragma unroll
-    for (int h = 0; h < 2; h++) {
-        const int64_t c = c0 + 256 * h;
-        v[h] = c < p.cols ? __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(xr + c)) : f32x4v{0, 0, 0, 0};
+    for (int i = 0; i < U; i++) {
+        int u = blockIdx.x * U + i;
+        if (u >= nunits) u = nunits - 1;  // a duplicate of the last unit writes the same bytes
+        row[i] = u / chunks;
+        c0[i] = (int64_t)(u - row[i] * chunks) * (T * 8) + wave * 512 + 4 * lane;
+        const float* xr = reinterpret_cast<const float*>(p.x) + (int64_t)row[i] * p.ldx;
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int64_t c = c0[i] + 256 * h;
+            v[2 * i + h] = c < p.cols ? __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(xr + c))
+                                      : f32x4v{0, 0, 0, 0};
+        }
     }
     const int64_t gpr = p.cols / 128;  // groups per row
 #pragma unroll
-    for (int h = 0; h < 2; h++) {
-        const int64_t c = c0 + 256 * h;
-        float m = fmaxf(fmaxf(fabsf(v[h][0]), fabsf(v[h][1])), fmaxf(fabsf(v[h][2]), fabsf(v[h][3])));
+    for (int j = 0; j < 2 * U; j++) {
+        const int i = j >> 1, h = j & 1;
+        const int64_t c = c0[i] + 256 * h;
+        float m = fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3])));
         m = dpp_max16(m);
         m = fmaxf(m, __shfl_xor(m, 16, 64));
         float s = m / p.g.qmax;
         if (p.scale_f16) s = round_f16(s);
         const float r = recip_or_zero(s);
         if (c < p.cols) {  // cols is a multiple of 128: the whole group is in range
-            if ((lane & 31) == 0 && p.scales_out) store_scale(p, (int64_t)row * gpr + c / 128, s);
+            if ((lane & 31) == 0 && p.scales_out) store_scale(p, (int64_t)row[i] * gpr + c / 128, s);
             uint32_t w = 0;
-            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[h][0] * r, v[h][1] * r, 1.0f, 0);
-            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[h][2] * r, v[h][3] * r, 1.0f, 1);
-            __builtin_nontemporal_store((uint16_t)w, reinterpret_cast<uint16_t*>(p.packed + (int64_t)row * p.ldp + c / 2));
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[j][0] * r, v[j][1] * r, 1.0f, 0);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[j][2] * r, v[j][3] * r, 1.0f, 1);
+            __builtin_nontemporal_store((uint16_t)w,
+                                        reinterpret_cast<uint16_t*>(p.packed + (int64_t)row[i] * p.ldp + c / 2));
         }
     }
 }
@@ -694,9 +703,14 @@ static void quantize_launch(const QuantParams& p, hipStream_t s) {
             if (BF16)
                 hipLaunchKernelGGL((quantize_e2m1_g128_kernel<BF16, 1, QT>), dim3((unsigned)qunits), dim3(QT), 0, s, p,
                                    (int)qchunks, (int)qunits);
-            else
-                hipLaunchKernelGGL((quantize_e2m1_g128_f32_kernel<QT>), dim3((unsigned)qunits), dim3(QT), 0, s, p,
-                                   (int)qchunks);
+            else {
+                // 512 threads, one (row, 4096-column) unit per workgroup: measured fastest of
+                // 256 / 512 / 1024 threads with one or two units (33.5 us at 11008 x 4096)
+                constexpr int FT = 512, FU = 1;
+                const int64_t fchunks = (p.cols + FT * 8 - 1) / (FT * 8), funits = p.rows * fchunks;
+                hipLaunchKernelGGL((quantize_e2m1_g128_f32_kernel<FT, FU>), dim3((unsigned)((funits + FU - 1) / FU)),
+                                   dim3(FT), 0, s, p, (int)fchunks, (int)funits);
+            }
         }
         else if (VEC && p.mode == 0 && p.g.is_e2m1 && !p.amax_in && (!p.col_shift || p.shift_sign < 0) &&
                  p.rows * ((p.cols + QT * 8 - 1) / (QT * 8)) < (1LL << 30) && p.cols < (1LL << 30)) {

@@ -312,6 +312,10 @@ def test_w4a16_shapes(M, N, K, mode, group, fmt, bf16):
     (8, 40, 8192, "group", "f16"),     # 128 KiB of staged activations
     (16, 40, 8192, "group", "f16"),    # too large to stage: the two-tile kernel
     (4, 1000, 4096, "group", "f16"),   # decode shape, many workgroups
+    (1, 13000, 3072, "group", "f16"),  # three chunks per wavefront, ragged N
+    (3, 700, 1024, "group", "f16"),    # one chunk per wavefront
+    (2, 2000, 4096, "group", "f32"),   # f32 scales
+    (4, 40, 2048, "group", "f16"),     # fewer workgroups than compute units
 ])
 def test_w4a16_small_batch(M, N, K, mode, sd):
     """Decode / small-batch W4A16 (M <= 16, bf16 activations, E2M1): the staged-
