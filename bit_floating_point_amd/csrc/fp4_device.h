@@ -262,6 +262,15 @@ __device__ __forceinline__ void dma16(i32x4v rsrc, uint32_t voff, uint32_t lds_b
                  : "v"(voff), "s"(lds_base), "s"(rsrc)
                  : "memory", "m0");
 }
+// The same load into LDS byte base + off, M0 formed inside the asm: `base` is one
+// long-lived register and `off` a constant the compiler can rematerialise, so a kernel
+// issuing loads into many fixed LDS slots does not hold every slot address live.
+__device__ __forceinline__ void dma16_at(i32x4v rsrc, uint32_t voff, uint32_t base, uint32_t off) {
+    asm volatile("s_add_u32 m0, %1, %2\n\tbuffer_load_dwordx4 %0, %3, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(base), "s"(off), "s"(rsrc)
+                 : "memory", "m0", "scc");
+}
 #pragma clang diagnostic pop
 
 }  // namespace fp4

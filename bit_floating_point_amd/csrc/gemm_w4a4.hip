@@ -13,7 +13,8 @@
 // partial last round or for small grids); each wavefront a (BM/2) x (BN/2) sub-tile as
 // a grid of 32x32 accumulators.  K advances 128 codes (64 bytes per row) per step
 // through a four-stage LDS ring fed by direct-to-LDS loads.  One workgroup per compute
-// unit loops over tiles; the load ring runs on across tile boundaries, so the next
+// unit loops over tiles (each XCD over its own range of them, so that an XCD reads
+// about an eighth of W); the load ring runs on across tile boundaries, so the next
 // tile's first steps load while the last ones of the current tile are computed and
 // while its epilogue writes its outputs.
 //
@@ -102,12 +103,15 @@ __device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + exp_f32(
 // F8 = 1: OCP FP8 E4M3 operands (one code per byte; no SwiGLU): a step is 64 codes (the
 // same 64 bytes per row), one 32x32x64 FP8 MFMA K-block whose lane fragment is the two
 // 16-byte segments 2 hk, 2 hk + 1 (read as the two "halves" of the FP4 pipeline).
-template <int BM, int BN, bool GLU, int F8 = 0>
-__global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m, int ntiles, GluParams gp) {
+// NWV = 4 or 8 wavefronts per workgroup in a 2 x NWV/2 grid (rows x columns of the
+// tile): with 8, two wavefronts share each SIMD, so one's LDS fragment reads overlap the
+// other's MFMAs (each holds a (BM/2) x (BN/4) sub-tile, half the accumulators).
+template <int BM, int BN, bool GLU, int F8 = 0, int NWV = 4>
+__global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int grid_m, int ntiles, GluParams gp) {
     constexpr int CPB = F8 ? 1 : 2;  // codes per byte
-    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int WM = BM / 2, WN = BN / (NWV / 2);
     constexpr int TM = WM / 32, TN = WN / 32;
-    constexpr int LA = BM * 4 / 256, LB = BN * 4 / 256;  // 16-byte pieces per thread per step
+    constexpr int LA = BM * 4 / (64 * NWV), LB = BN * 4 / (64 * NWV);  // 16-byte pieces per thread per step
     constexpr int STAGE = (BM + BN) * kBKBytes;
     // four operand stages, per tile parity a 1 KiB block of per-column weight scales (GLU:
     // gate scales, up scales and the output shifts, 1 KiB each), and each wavefront's
@@ -116,7 +120,8 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
     constexpr int SCL_BYTES = GLU ? 3072 : 1024;
     constexpr int STG_BYTES = GLU ? 2048 : 32 * WN;
     constexpr int ON = GLU ? BN / 2 : BN;  // output columns per tile
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * STAGE + 2 * SCL_BYTES + 4 * STG_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * STAGE + 2 * SCL_BYTES + NWV * STG_BYTES];
+    constexpr int BOFF = BM * kBKBytes;  // a stage: its A block, then its B block
     uint8_t* const st0 = smem;
     uint8_t* const st1 = smem + STAGE;
     uint8_t* const st2 = smem + 2 * STAGE;
@@ -146,29 +151,48 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
     const float r_out = GLU ? recip_or_zero(gp.out_scale[0]) : 0.0f;  // next layer's fl32(1 / a')
 
     // Loads run ahead of the MFMAs through the tiles of this workgroup (tile t covers
-    // rows bm*BM.., columns bn*BN.. with bm = t % grid_m, bn = t / grid_m; this
-    // workgroup takes t = blockIdx.x, blockIdx.x + gridDim.x, ...).  State of the load
-    // stream: its tile dt, and per load the global piece behind this lane's LDS slot
-    // (slot s = (4 i + wave) * 64 + lane holds row s/4, swizzled segment s%4; see swz).
+    // rows bm*BM.., columns bn*BN.. with bm = t % grid_m, bn = t / grid_m; the tiles of a
+    // workgroup in turn: tile_of below).  State of the load stream: its tile dt, and per
+    // load the global piece behind this lane's LDS slot (slot s = (NWV i + wave) * 64 +
+    // lane holds row s/4, swizzled segment s%4; see swz).
     int segk[LA > LB ? LA : LB];
 #pragma unroll
     for (int i = 0; i < (LA > LB ? LA : LB); i++) {
-        int sidx = (4 * i + wave) * 64 + lane, row = sidx >> 2;
+        int sidx = (NWV * i + wave) * 64 + lane, row = sidx >> 2;
         segk[i] = ((sidx & 3) ^ ((row >> 1) & 3)) * 16 * CPB;  // codes
     }
     uint32_t offA[LA], offB[LB], offS, offK;
-    int dt = blockIdx.x, dpar = 0;
+    // Tile order.  Workgroups are dispatched to the 8 XCDs in turn (workgroup b on XCD
+    // b % 8), each XCD with its own L2.  When the grid is a multiple of 8, XCD x takes the
+    // tiles [ntiles x / 8, ntiles (x + 1) / 8) of the column-major tile order (tile t:
+    // row block t % grid_m, column block t / grid_m), shared by its workgroups in turn:
+    // an XCD then reads about an eighth of the column blocks of W, each once, and all of
+    // A.  Otherwise workgroup b takes tiles b, b + grid, ...
+    constexpr int kXcds = 8;
+    const bool xcd_order = gridDim.x % kXcds == 0;
+    const int xcd = blockIdx.x % kXcds, xwg = blockIdx.x / kXcds, xwgs = gridDim.x / kXcds;
+    const int x_first = (int)((int64_t)ntiles * xcd / kXcds);
+    const int x_count = (int)((int64_t)ntiles * (xcd + 1) / kXcds) - x_first;
+    auto tile_of = [&](int k) -> int {  // this workgroup's k-th tile, or ntiles once done
+        if (!xcd_order) {
+            const int64_t t = blockIdx.x + (int64_t)k * gridDim.x;
+            return t < ntiles ? (int)t : ntiles;
+        }
+        const int64_t u = xwg + (int64_t)k * xwgs;
+        return u < x_count ? x_first + (int)u : ntiles;
+    };
+    int dk = 0, dt = tile_of(0), dpar = 0;
     auto load_tile = [&](int t) {
         const bool ok = t < ntiles;
         const int64_t m0 = (int64_t)(t % grid_m) * BM, n0 = (int64_t)(t / grid_m) * ON;
 #pragma unroll
         for (int i = 0; i < LA; i++) {
-            int row = ((4 * i + wave) * 64 + lane) >> 2;
+            int row = ((NWV * i + wave) * 64 + lane) >> 2;
             offA[i] = (ok && m0 + row < p.M) ? (uint32_t)((m0 + row) * p.lda + segk[i] / CPB) : kOOB;
         }
 #pragma unroll
         for (int i = 0; i < LB; i++) {
-            int row = ((4 * i + wave) * 64 + lane) >> 2;
+            int row = ((NWV * i + wave) * 64 + lane) >> 2;
             if (GLU && i >= LB / 2) row -= BN / 2;  // up rows (their own buffer)
             offB[i] = (ok && n0 + row < p.N) ? (uint32_t)((n0 + row) * p.ldw + segk[i] / CPB) : kOOB;
         }
@@ -176,20 +200,21 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
         offK = (ok && 16 * lane < ON && n0 + 16 * lane < p.N) ? (uint32_t)(n0 + 16 * lane) : kOOB;
     };
     load_tile(dt);
+    // this wavefront's LDS slot base: load piece i of a stage goes to stage + (NWV i + wave) KiB
+    const uint32_t wave_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&smem[wave * 1024]);
 
 // direct-to-LDS loads of step KB of the load stream's tile into stage array STG
 #define FP4_DMAK(STG, KB)                                                                                  \
     do {                                                                                                   \
         const int kb_ = (KB);                                                                              \
+        const uint32_t st_ = (uint32_t)((STG) - smem);                                                     \
         _Pragma("unroll") for (int i = 0; i < LA; i++) {                                                   \
             uint32_t off = (kb_ * 64 * CPB + segk[i] < p.K) ? offA[i] + (uint32_t)kb_ * kBKBytes : kOOB;   \
-            dma16(rsA, off, __builtin_amdgcn_readfirstlane(                                                \
-                                (uint32_t)(uintptr_t)&STG[(4 * i + wave) * 1024]));                       \
+            dma16_at(rsA, off, wave_lds, st_ + (uint32_t)(NWV * i * 1024));                                \
         }                                                                                                  \
         _Pragma("unroll") for (int i = 0; i < LB; i++) {                                                   \
             uint32_t off = (kb_ * 64 * CPB + segk[i] < p.K) ? offB[i] + (uint32_t)kb_ * kBKBytes : kOOB;   \
-            dma16((GLU && i >= LB / 2) ? rsB2 : rsB, off, __builtin_amdgcn_readfirstlane(                  \
-                                (uint32_t)(uintptr_t)&STG[BM * kBKBytes + (4 * i + wave) * 1024]));       \
+            dma16_at((GLU && i >= LB / 2) ? rsB2 : rsB, off, wave_lds, st_ + (uint32_t)(BOFF + NWV * i * 1024)); \
         }                                                                                                  \
     } while (0)
 // the load stream's tile's 256 column scales into scales block dpar (all wavefronts
@@ -206,7 +231,7 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
 // the load stream moves on to this workgroup's next tile
 #define FP4_NEXT_TILE()                                                                                    \
     do {                                                                                                   \
-        dt += gridDim.x;                                                                                   \
+        dt = tile_of(++dk);                                                                                \
         dpar ^= 1;                                                                                         \
         load_tile(dt);                                                                                     \
     } while (0)
@@ -221,7 +246,7 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
         _Pragma("unroll") for (int i = 0; i < TM; i++) FA[i] =                                             \
             *reinterpret_cast<const uint4*>(&STG[swz(wm * WM + i * 32 + r32, sg_)]);                       \
         _Pragma("unroll") for (int j = 0; j < TN; j++) FB[j] =                                             \
-            *reinterpret_cast<const uint4*>(&STG[BM * kBKBytes + swz(brow(j) + r32, sg_)]);                \
+            *reinterpret_cast<const uint4*>(&STG[BOFF + swz(brow(j) + r32, sg_)]);                         \
     } while (0)
 // the MFMAs of one half step from fragment registers, with the LDS reads of the next
 // half step (issued just before) spread between them
@@ -238,7 +263,7 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
         }                                                                                                  \
         _Pragma("unroll") for (int g = 0; g < TM + TN; g++) {                                              \
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                             \
-            __builtin_amdgcn_sched_group_barrier(0x008, TM * TN / (TM + TN), 0);                           \
+            __builtin_amdgcn_sched_group_barrier(0x008, (TM * TN + TM + TN - 1) / (TM + TN), 0);           \
         }                                                                                                  \
     } while (0)
 
@@ -258,8 +283,8 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
                                        (int)ya[i].x, (int)ya[i].y, (int)ya[i].z, (int)ya[i].w};            \
                 acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[j][i], 0, 0, 0, 127, 0, 127); \
             }                                                                                              \
-            xb[j] = *reinterpret_cast<const uint4*>(&SN[BM * kBKBytes + swz(brow(j) + r32, 2 * hk)]);      \
-            yb[j] = *reinterpret_cast<const uint4*>(&SN[BM * kBKBytes + swz(brow(j) + r32, 2 * hk + 1)]);  \
+            xb[j] = *reinterpret_cast<const uint4*>(&SN[BOFF + swz(brow(j) + r32, 2 * hk)]);               \
+            yb[j] = *reinterpret_cast<const uint4*>(&SN[BOFF + swz(brow(j) + r32, 2 * hk + 1)]);           \
         }                                                                                                  \
         _Pragma("unroll") for (int i = 0; i < TM; i++) {                                                   \
             xa[i] = *reinterpret_cast<const uint4*>(&SN[swz(wm * WM + i * 32 + r32, 2 * hk)]);             \
@@ -325,6 +350,15 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
             FP4_SYNC(W);                                                                                   \
             D;                                                                                             \
             FP4_READH(SN, 0, xa, xb);                                                                      \
+        } else if constexpr (NWV == 8) {                                                                   \
+            /* two wavefronts per SIMD hide each other's fragment reads: one set of      */              \
+            /* fragment registers, each half read just before its MFMAs                  */              \
+            FP4_MMAH(xa, xb);                                                                              \
+            FP4_READH(SQ, 1, xa, xb);                                                                      \
+            FP4_MMAH(xa, xb);                                                                              \
+            FP4_SYNC(W);                                                                                   \
+            D;                                                                                             \
+            FP4_READH(SN, 0, xa, xb);                                                                      \
         } else {                                                                                           \
             FP4_READH(SQ, 1, ya, yb);                                                                      \
             FP4_MMAH(xa, xb);                                                                              \
@@ -343,7 +377,7 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
     } while (0)
     constexpr int WR = 2 * PER_STEP + STORES, WN2 = 2 * PER_STEP;
     const int ngroups = nk4 / 4;
-    int ct = blockIdx.x, cpar = 0;
+    int ck = 0, ct = tile_of(0), cpar = 0;
     for (;;) {
 #pragma unroll
         for (int j = 0; j < TN; j++)
@@ -528,7 +562,7 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
                 FP4_SYNC_ALL();
             }
         }
-        ct += gridDim.x;
+        ct = tile_of(++ck);
         if (ct >= ntiles) break;
         cpar ^= 1;
     }
@@ -549,6 +583,9 @@ __global__ void __launch_bounds__(256) w4a4_fp4_kernel(GemmParams p, int grid_m,
 // kMaxBufBytes of A and of W; larger operands are split into row blocks (multiples of
 // 256 rows, whole tiles either way), each launched on pointers advanced to its start.
 constexpr int64_t kMaxBufBytes = 0x7fff0000;
+// 256 x 256 E2M1 tiles run 8 wavefronts (measured 6% faster than 4 on the LLaMA-13B
+// prefill layer, bit-identical)
+constexpr int kBigTileWaves = 8;
 
 // one workgroup per compute unit (each holds the whole LDS ring), looping over tiles
 static int cu_count() {
@@ -563,11 +600,13 @@ static int cu_count() {
     return counts[dev];
 }
 
+// 256 x 256 FP4 tiles run 8 wavefronts (2 per SIMD); smaller tiles and FP8 4.
 template <int BM, int BN, int F8 = 0>
 static void launch_cfg(const GemmParams& p, hipStream_t s, int64_t cus) {
     const int64_t gm = (p.M + BM - 1) / BM, gn = (p.N + BN - 1) / BN, nt = gm * gn;
-    hipLaunchKernelGGL((w4a4_fp4_kernel<BM, BN, false, F8>), dim3((unsigned)std::min(nt, cus)), dim3(256), 0, s, p,
-                       (int)gm, (int)nt, GluParams{});
+    constexpr int NWV = (BM == 256 && BN == 256 && F8 == 0) ? kBigTileWaves : 4;
+    hipLaunchKernelGGL((w4a4_fp4_kernel<BM, BN, false, F8, NWV>), dim3((unsigned)std::min(nt, cus)), dim3(64 * NWV), 0,
+                       s, p, (int)gm, (int)nt, GluParams{});
 }
 static GemmParams column_block(const GemmParams& p, int64_t n0, int64_t n1) {
     GemmParams q = p;
@@ -589,6 +628,7 @@ static hipError_t launch_block(const GemmParams& p, hipStream_t s) {
     const int64_t cus = cu_count();
     const int64_t gm256 = (p.M + 255) / 256, gn256 = (p.N + 255) / 256, t256 = gm256 * gn256;
     if (t256 < cus) {
+        // (one round of 256 x 128 tiles measured the same as two of 128 x 128 at 2048 x 4096)
         launch_cfg<128, 128, F8>(p, s, cus);
         return hipGetLastError();
     }
@@ -658,8 +698,9 @@ hipError_t launch_w8a8_fp8(const GemmParams& p, hipStream_t s) { return launch_s
 template <int BM, int BN>
 static void launch_glu_cfg(const GemmParams& p, const GluParams& gp, hipStream_t s, int64_t cus) {
     const int64_t gm = (p.M + BM - 1) / BM, gn = (p.N + BN / 2 - 1) / (BN / 2), nt = gm * gn;
-    hipLaunchKernelGGL((w4a4_fp4_kernel<BM, BN, true>), dim3((unsigned)std::min(nt, cus)), dim3(256), 0, s, p,
-                       (int)gm, (int)nt, gp);
+    constexpr int NWV = (BM == 256 && BN == 256) ? kBigTileWaves : 4;
+    hipLaunchKernelGGL((w4a4_fp4_kernel<BM, BN, true, 0, NWV>), dim3((unsigned)std::min(nt, cus)), dim3(64 * NWV), 0,
+                       s, p, (int)gm, (int)nt, gp);
 }
 
 hipError_t launch_w4a4_swiglu(const GemmParams& p, const GluParams& gp, hipStream_t s) {
