@@ -438,15 +438,15 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
 
     if (p.wg.kind == 2 && (d->w_gran.mode != FP4_SCALE_GROUP || d->a_kind == FP4_PACKED))
         return fail(FP4_ERR_UNSUPPORTED, "two-mode weights need GROUP scales and f32/bf16 activations");
-    if (p.a_row && (d->a_kind != FP4_PACKED || !(p.wg.is_e2m1 || p.wg.bits != 4)))
-        return fail(FP4_ERR_UNSUPPORTED, "per-token activation scales are taken by the E2M1 x E2M1 and FP8 / FP6 products only");
+    if (p.a_row && (d->a_kind != FP4_PACKED || p.wg.kind != 0))
+        return fail(FP4_ERR_UNSUPPORTED, "per-token activation scales are taken by the products of two minifloat grids only");
     if (p.wg.bits != 4 && d->a_kind == FP4_PACKED) {
         // both operands FP8 / FP6 on the f8f6f4 matrix cores: E4M3 x E4M3 on the
         // persistent kernel, every other pair (W6A6 among them) on the tiled one
         QGrid qa;
         if ((st = make_grid(d->a_grid, &qa))) return st;
-        if (qa.kind != 0 || (qa.bits == 4 && !qa.is_e2m1))
-            return fail(FP4_ERR_UNSUPPORTED, "FP8 / FP6 weights with packed activations need FP8 / FP6 / E2M1 activations");
+        if (qa.kind != 0)
+            return fail(FP4_ERR_UNSUPPORTED, "FP8 / FP6 weights with packed activations need minifloat activations");
         if (!d->a_scale) return fail(FP4_ERR_INVALID_ARG, "packed activations need a_scale");
         if (d->K % 32 != 0) return fail(FP4_ERR_UNSUPPORTED, "K must be a multiple of 32");
         if (d->lda < d->K * qa.bits / 8 || d->ldw < d->K * p.wg.bits / 8 || d->lda % 16 != 0)
@@ -466,7 +466,9 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
     }
     if (d->a_kind == FP4_F32 || d->a_kind == FP4_BF16) {
         if (d->lda < d->K) return fail(FP4_ERR_INVALID_ARG, "lda < K");
-        bool mfma = d->a_kind == FP4_BF16 && p.wg.is_e2m1 && d->K % 128 == 0 && (d->lda * 2) % 16 == 0 &&
+        // 4-bit minifloat weights E1M2, E2M1, E3M0: the bf16 matrix-core kernels
+        const bool mini4 = p.wg.kind == 0 && p.wg.bits == 4 && p.wg.e >= 1 && p.wg.e <= 3;
+        bool mfma = d->a_kind == FP4_BF16 && mini4 && d->K % 128 == 0 && (d->lda * 2) % 16 == 0 &&
                     (d->w_gran.mode != FP4_SCALE_GROUP || d->w_gran.group % 128 == 0);
         // FP8 / FP6 weights: the small-batch matrix-core kernel, else the VALU kernel
         if (p.wg.bits != 4) {
@@ -485,11 +487,13 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
     if (d->a_kind != FP4_PACKED) return fail(FP4_ERR_INVALID_ARG, "a_kind must be F32, BF16 or PACKED");
     if (!d->a_scale) return fail(FP4_ERR_INVALID_ARG, "packed activations need a_scale");
     if ((st = make_grid(d->a_grid, &p.ag))) return st;
-    if (p.ag.kind == 0 && p.ag.bits != 4 && p.wg.is_e2m1) {
-        // FP8 / FP6 activations with E2M1 weights: the tiled f8f6f4 kernel
+    const bool w4_mini = p.wg.kind == 0 && p.wg.bits == 4, a4_mini = p.ag.kind == 0 && p.ag.bits == 4;
+    if ((p.ag.kind == 0 && p.ag.bits != 4 && w4_mini) || (w4_mini && a4_mini && !(p.wg.is_e2m1 && p.ag.is_e2m1))) {
+        // FP8 / FP6 activations with 4-bit minifloat weights, and the 4-bit pairs with an
+        // E1M2 or E3M0 operand (rewritten as FP8 E4M3 in LDS): the tiled f8f6f4 kernel
         if (d->K % 32 != 0) return fail(FP4_ERR_UNSUPPORTED, "K must be a multiple of 32");
         if (d->lda < d->K * p.ag.bits / 8 || d->lda % 16 != 0)
-            return fail(FP4_ERR_ALIGNMENT, "FP8 / FP6 rows: lda >= the code bytes of a row, a multiple of 16");
+            return fail(FP4_ERR_ALIGNMENT, "packed rows: lda >= the code bytes of a row, a multiple of 16");
         if (d->w_gran.mode == FP4_SCALE_GROUP || d->w_gran.scale_dtype != FP4_F32)
             return fail(FP4_ERR_UNSUPPORTED, "FP8 / FP6 products need f32 TENSOR or ROW weight scales");
         if (256 * std::max(d->lda, d->ldw) >= 0x7fff0000)
@@ -511,7 +515,7 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
             return fail(FP4_ERR_UNSUPPORTED, "lookup-grid weights need GROUP scales with group a multiple of 64");
         return hip_status(launch_w4a4_lut(p, s), "fp4_gemm/w4a4_lut");
     }
-    return fail(FP4_ERR_UNSUPPORTED, "W4A4 with minifloat weights other than E2M1 is not implemented");
+    return fail(FP4_ERR_UNSUPPORTED, "unsupported pair of weight and activation grids");
 }
 
 // Standard normal quantile: the x with Phi(x) = 0.5 erfc(-x / sqrt 2) = p, by bisection

@@ -7,7 +7,8 @@
 // sections.
 //
 // Formats (the MFMA's operand format codes): 0 FP8 E4M3, 1 FP8 E5M2, 2 FP6 E2M3,
-// 3 FP6 E3M2, 4 FP4 E2M1.  FP8 rows hold one code per byte, FP4 rows two (low nibble
+// 3 FP6 E3M2, 4 FP4 E2M1; and 5 E1M2, 6 E3M0 (the 4-bit grids the format search can
+// choose that have no format code: rewritten as E4M3 on their way into LDS).  FP8 rows hold one code per byte, FP4 rows two (low nibble
 // first); FP6 rows are a bit stream, code k in bits [6 k, 6 k + 6) of the row, so 16
 // consecutive codes starting at a multiple of 16 are 12 contiguous bytes, half of the
 // six registers of an FP6 MFMA operand.
@@ -46,12 +47,19 @@ constexpr int kSets = 2;
 // bytes of padding, so the 16-byte fragment reads of 16 consecutive rows hit distinct
 // banks).  With K a multiple of 32 a row ends on a unit boundary, so a unit is either
 // wholly inside the row or wholly past it.
+// F = 5 (E1M2) and 6 (E3M0): the 4-bit grids that have no matrix-core format of their
+// own.  Their rows are loaded as FP4 rows are (8-byte runs of 16 codes) and every code is
+// rewritten on its way into LDS as the FP8 E4M3 byte of the same value (every E1M2 and
+// E3M0 value is an E4M3 value), staged and multiplied as E4M3 (format code 0).
 template <int F>
 struct Fmt {
-    static constexpr int bits = F < 2 ? 8 : (F < 4 ? 6 : 4);
-    static constexpr int step_bytes = kStepCodes * bits / 8;  // 128, 96 or 64
-    static constexpr int unit_bytes = step_bytes / 8;         // 16, 12 or 8
-    static constexpr int stride = 8 * 16 + 16;                // LDS row stride (bytes)
+    static constexpr bool expand = F >= 5;                     // 4-bit codes staged as E4M3
+    static constexpr int bits = F < 2 ? 8 : (F < 4 ? 6 : (expand ? 8 : 4));  // bits per staged code
+    static constexpr int lbits = expand ? 4 : bits;            // bits per loaded code
+    static constexpr int code = expand ? 0 : F;                // MFMA operand format
+    static constexpr int step_bytes = kStepCodes * lbits / 8;  // 128, 96 or 64 bytes loaded per step
+    static constexpr int unit_bytes = step_bytes / 8;          // 16, 12 or 8
+    static constexpr int stride = 8 * 16 + 16;                 // LDS row stride (bytes)
     // LDS slot of unit j.  The matrix cores pair the two operands' values in a fixed K
     // order that differs by format (measured on gfx950 with one-hot operands): an FP8
     // operand's 32 values are codes 32 hk + i of the 64-code K-block, i = 0..31; an FP6
@@ -85,15 +93,48 @@ __device__ __forceinline__ i32x8 frag(const uint8_t* row, int h, int hk) {
 template <int F>
 __device__ __forceinline__ uint4 unit_load(__amdgpu_buffer_rsrc_t r, int64_t row_off, int64_t valid) {
     const uint32_t off = valid > 0 ? (uint32_t)row_off : kOOB;
-    if constexpr (Fmt<F>::bits == 8) {
+    if constexpr (Fmt<F>::lbits == 8) {
         return buf_load16(r, off);
-    } else if constexpr (Fmt<F>::bits == 6) {
+    } else if constexpr (Fmt<F>::lbits == 6) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
         return make_uint4(v[0], v[1], v[2], 0u);
     } else {
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
         return make_uint4(v[0], v[1], 0u, 0u);
     }
+}
+
+// E4M3 bytes of the eight magnitudes of a 4-bit grid, bytes 0..3 and 4..7 of a lookup
+// table for v_perm: E1M2 {0, .25, .5, .75, 1, 1.25, 1.5, 1.75}, E3M0 {0, 1, 2, 4, ..., 64}.
+template <int F>
+struct E4m3Table {
+    static constexpr uint32_t lo = F == 5 ? 0x34302800u : 0x48403800u;
+    static constexpr uint32_t hi = F == 5 ? 0x3e3c3a38u : 0x68605850u;
+};
+
+// 16 codes (8 bytes, code 2b in the low nibble of byte b) -> their 16 E4M3 bytes in code
+// order: the magnitude picks a table byte, the code's sign bit becomes bit 7.
+template <int F>
+__device__ __forceinline__ uint4 expand16(uint4 u) {
+    const uint32_t in[2] = {u.x, u.y};
+    uint32_t out[4];
+#pragma unroll
+    for (int d = 0; d < 2; d++) {
+        const uint32_t w = in[d];
+        const uint32_t ev = __builtin_amdgcn_perm(E4m3Table<F>::hi, E4m3Table<F>::lo, w & 0x07070707u) |
+                            ((w & 0x08080808u) << 4);  // codes 0, 2, 4, 6 of the dword
+        const uint32_t od = __builtin_amdgcn_perm(E4m3Table<F>::hi, E4m3Table<F>::lo, (w >> 4) & 0x07070707u) |
+                            (w & 0x80808080u);         // codes 1, 3, 5, 7
+        out[2 * d] = __builtin_amdgcn_perm(od, ev, 0x05010400u);
+        out[2 * d + 1] = __builtin_amdgcn_perm(od, ev, 0x07030602u);
+    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+template <int F>
+__device__ __forceinline__ uint4 staged(uint4 u) {
+    if constexpr (Fmt<F>::expand) return expand16<F>(u);
+    else return u;
 }
 
 }  // namespace
@@ -122,7 +163,7 @@ __global__ void __launch_bounds__(256) f8f6_gemm_kernel(GemmParams p, int grid_m
     const __amdgpu_buffer_rsrc_t rA =
         buf_make(reinterpret_cast<const uint8_t*>(p.a) + m0 * p.lda, rows_a * p.lda);
     const __amdgpu_buffer_rsrc_t rW = buf_make(p.w + n0 * p.ldw, rows_w * p.ldw);
-    const int64_t bytes_a = p.K * WA::bits / 8, bytes_w = p.K * WW::bits / 8;  // code bytes per row
+    const int64_t bytes_a = p.K * WA::lbits / 8, bytes_w = p.K * WW::lbits / 8;  // code bytes per row
     const int nsteps = (int)((p.K + kStepCodes - 1) / kStepCodes);
 
     // kSets register sets of units: set t % kSets holds step t; the loads of step
@@ -147,12 +188,12 @@ __global__ void __launch_bounds__(256) f8f6_gemm_kernel(GemmParams p, int grid_m
 #pragma unroll
         for (int i = 0; i < LA; i++) {
             const int q = tid + 256 * i, row = q >> 3, j = q & 7;
-            *reinterpret_cast<uint4*>(buf + row * WA::stride + 16 * WA::slot(j)) = a[i];
+            *reinterpret_cast<uint4*>(buf + row * WA::stride + 16 * WA::slot(j)) = staged<FA>(a[i]);
         }
 #pragma unroll
         for (int i = 0; i < LW; i++) {
             const int q = tid + 256 * i, row = q >> 3, j = q & 7;
-            *reinterpret_cast<uint4*>(buf + SA + row * WW::stride + 16 * WW::slot(j)) = w[i];
+            *reinterpret_cast<uint4*>(buf + SA + row * WW::stride + 16 * WW::slot(j)) = staged<FW>(w[i]);
         }
     };
 
@@ -176,8 +217,8 @@ __global__ void __launch_bounds__(256) f8f6_gemm_kernel(GemmParams p, int grid_m
             for (int j = 0; j < 4; j++)
 #pragma unroll
                 for (int i = 0; i < 2; i++)
-                    acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[j], fa[i], acc[j][i], FW, FA, 0,
-                                                                               127, 0, 127);
+                    acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[j], fa[i], acc[j][i], WW::code,
+                                                                               WA::code, 0, 127, 0, 127);
         }
         // keep the MFMAs ahead of the waits for the next units
         __builtin_amdgcn_sched_barrier(0);
@@ -267,7 +308,9 @@ hipError_t launch_w(const GemmParams& p, int fa, hipStream_t s) {
         case 1: return launch_pair<FW, 1>(p, s);
         case 2: return launch_pair<FW, 2>(p, s);
         case 3: return launch_pair<FW, 3>(p, s);
-        default: return launch_pair<FW, 4>(p, s);
+        case 4: return launch_pair<FW, 4>(p, s);
+        case 5: return launch_pair<FW, 5>(p, s);
+        default: return launch_pair<FW, 6>(p, s);
     }
 }
 
@@ -277,7 +320,7 @@ hipError_t launch_w(const GemmParams& p, int fa, hipStream_t s) {
 // 4 E2M1
 int f8f6_format_code(const QGrid& g) {
     if (g.kind != 0) return -1;
-    if (g.bits == 4) return g.is_e2m1 ? 4 : -1;
+    if (g.bits == 4) return g.is_e2m1 ? 4 : (g.e == 1 ? 5 : (g.e == 3 ? 6 : -1));
     if (g.bits == 8) return g.e == 4 && g.m == 3 ? 0 : (g.e == 5 && g.m == 2 ? 1 : -1);
     if (g.bits == 6) return g.e == 2 && g.m == 3 ? 2 : (g.e == 3 && g.m == 2 ? 3 : -1);
     return -1;
@@ -295,7 +338,9 @@ hipError_t launch_f8f6_gemm(const GemmParams& p, hipStream_t s) {
         case 1: return launch_w<1>(p, fa, s);
         case 2: return launch_w<2>(p, fa, s);
         case 3: return launch_w<3>(p, fa, s);
-        default: return launch_w<4>(p, fa, s);
+        case 4: return launch_w<4>(p, fa, s);
+        case 5: return launch_w<5>(p, fa, s);
+        default: return launch_w<6>(p, fa, s);
     }
 }
 

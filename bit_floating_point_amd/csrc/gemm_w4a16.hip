@@ -2,10 +2,11 @@
 // (scales factored out of the low-bit inner product: [FP4-LLM] "efficient matrix
 // multiplication"; [W8A8] section 2.2 quantized_matmul; group size 128).
 //
-// Two bf16-activation, E2M1-weight kernels run on the bf16 matrix cores; both are
-// HBM-bound on the packed weights.  Per 128-wide K chunk a lane streams 16 bytes (32
-// codes) of one weight row with a single 128-bit load, turns them into bf16 with the
-// gfx950 FP4->bf16 convert (exact), and feeds four bf16 16x16x32 MFMAs.  The 4-bit
+// Two bf16-activation, 4-bit-minifloat-weight kernels run on the bf16 matrix cores;
+// both are HBM-bound on the packed weights.  Per 128-wide K chunk a lane streams 16
+// bytes (32 codes) of one weight row with a single 128-bit load, turns them into bf16
+// (E2M1 with the gfx950 FP4->bf16 convert, E1M2 and E3M0 through the FP8 convert; all
+// exact), and feeds four bf16 16x16x32 MFMAs.  The 4-bit
 // codes of one lane are the B operand of those MFMAs under a fixed permutation of K
 // that the activation operand uses too, so no shuffles are needed.  Each scale group's
 // partial sum is kept apart and multiplied by its scale in fp32 before it joins the
@@ -54,20 +55,33 @@ __device__ __forceinline__ bf16x8 decode_e2m1_bf16(uint32_t w) {
     return __builtin_bit_cast(bf16x8, o);
 }
 
-// 8 E1M2 codes -> 8 bf16 values, exact: the nibble (sign, magnitude d) becomes the E4M3
-// byte sign<<7 | d -- the subnormal d * 2^-9 -- and the convert's scale 2^7 makes it d/4.
-__device__ __forceinline__ bf16x8 decode_e1m2_bf16(uint32_t w) {
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 0,2,4,6 / 1,3,5,7
-    const uint32_t blo = (lo & 0x07070707u) | ((lo & 0x08080808u) << 4);
-    const uint32_t bhi = (hi & 0x07070707u) | ((hi & 0x08080808u) << 4);
-    const uint32_t d0 = __builtin_amdgcn_perm(bhi, blo, 0x05010400u);  // codes 0..3 in byte order
-    const uint32_t d1 = __builtin_amdgcn_perm(bhi, blo, 0x07030602u);  // codes 4..7
-    uint32_t o[4];
-    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 128.0f, false));
-    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 128.0f, true));
-    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 128.0f, false));
-    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 128.0f, true));
-    return __builtin_bit_cast(bf16x8, o);
+// 8 E1M2 or E3M0 codes -> 8 bf16 values, exact, through the FP8 E4M3 convert: the
+// nibble's sign becomes bit 7 of a byte and its magnitude code c goes to
+//  E1M2 (GE = 1): bits 0..2, the E4M3 subnormal c * 2^-9; the convert's scale 2^7 makes
+//       it c / 4, which is the E1M2 value of c (c / 4 below 1, 1 + (c - 4) / 4 above);
+//  E3M0 (GE = 3): bits 3..5, the E4M3 value 2^(c - 7) (zero for c = 0); the scale 2^6
+//       makes it 2^(c - 1).
+// GE = 2 is E2M1, which the FP4 convert takes directly.
+template <int GE>
+__device__ __forceinline__ bf16x8 decode_mini4_bf16(uint32_t w) {
+    if constexpr (GE == 2) {
+        return decode_e2m1_bf16(w);
+    } else {
+        static_assert(GE == 1 || GE == 3, "4-bit minifloat weights: E1M2, E2M1 or E3M0");
+        constexpr int SH = GE == 3 ? 3 : 0;
+        constexpr float kScale = GE == 3 ? 64.0f : 128.0f;
+        const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 0,2,4,6 / 1,3,5,7
+        const uint32_t blo = ((lo & 0x07070707u) << SH) | ((lo & 0x08080808u) << 4);
+        const uint32_t bhi = ((hi & 0x07070707u) << SH) | ((hi & 0x08080808u) << 4);
+        const uint32_t d0 = __builtin_amdgcn_perm(bhi, blo, 0x05010400u);  // codes 0..3 in byte order
+        const uint32_t d1 = __builtin_amdgcn_perm(bhi, blo, 0x07030602u);  // codes 4..7
+        uint32_t o[4];
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, kScale, false));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, kScale, true));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, kScale, false));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, kScale, true));
+        return __builtin_bit_cast(bf16x8, o);
+    }
 }
 
 // Scale loads return raw bits; the conversion waits until the value is used, so a
@@ -86,7 +100,8 @@ __device__ __forceinline__ float scale_value(uint32_t raw) {
 
 // T = 16-column tiles per wavefront (the activation registers are reused across them)
 // G1: group scales with exactly one 128-wide chunk per group (group size 128)
-template <int MODE, int T, bool SF16, bool G1>  // MODE 0 tensor, 1 row, 2 group
+// GE: exponent bits of the 4-bit minifloat weights (1 E1M2, 2 E2M1, 3 E3M0)
+template <int MODE, int T, bool SF16, bool G1, int GE = 2>  // MODE 0 tensor, 1 row, 2 group
 __global__ void __launch_bounds__(256) w4a16_mfma_kernel(GemmParams p) {
     __shared__ f32x4 part[kW16Waves - 1][T][64];
     const int lane = threadIdx.x & 63;
@@ -154,7 +169,7 @@ __global__ void __launch_bounds__(256) w4a16_mfma_kernel(GemmParams p) {
 #pragma unroll
                 for (int j = 0; j < 4; j++)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[b][j]),
-                                                                  decode_e2m1_bf16(wd[j]), acc, 0, 0, 0);
+                                                                  decode_mini4_bf16<GE>(wd[j]), acc, 0, 0, 0);
                 if (G1) {
                     // one group per chunk: scale its partial sum and add it (no branch)
                     const float sv = scale_value<SF16>(sc[b][t]);
@@ -214,13 +229,13 @@ __global__ void __launch_bounds__(256) w4a16_mfma_kernel(GemmParams p) {
     }
 }
 
-template <int T, bool SF16>
+template <int T, bool SF16, int GE>
 static void launch_w16(const GemmParams& p, hipStream_t s) {
     dim3 grid((unsigned)((p.N + 16 * T - 1) / (16 * T)), (unsigned)((p.M + 15) / 16));
-    if (p.w_mode == 2 && p.w_group == 128) hipLaunchKernelGGL((w4a16_mfma_kernel<2, T, SF16, true>), grid, dim3(256), 0, s, p);
-    else if (p.w_mode == 2) hipLaunchKernelGGL((w4a16_mfma_kernel<2, T, SF16, false>), grid, dim3(256), 0, s, p);
-    else if (p.w_mode == 1) hipLaunchKernelGGL((w4a16_mfma_kernel<1, T, SF16, false>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((w4a16_mfma_kernel<0, T, SF16, false>), grid, dim3(256), 0, s, p);
+    if (p.w_mode == 2 && p.w_group == 128) hipLaunchKernelGGL((w4a16_mfma_kernel<2, T, SF16, true, GE>), grid, dim3(256), 0, s, p);
+    else if (p.w_mode == 2) hipLaunchKernelGGL((w4a16_mfma_kernel<2, T, SF16, false, GE>), grid, dim3(256), 0, s, p);
+    else if (p.w_mode == 1) hipLaunchKernelGGL((w4a16_mfma_kernel<1, T, SF16, false, GE>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((w4a16_mfma_kernel<0, T, SF16, false, GE>), grid, dim3(256), 0, s, p);
 }
 
 // ---------------------------------------------------------------------------------
@@ -248,7 +263,8 @@ constexpr int kSmallChunks = 4;  // K chunks per wavefront per batch
 // codes are 24 bytes (a 16-byte and an 8-byte load, which the compiler cannot merge or
 // split, so the wait counts below stay exact), converted at once by the 32-value FP6
 // converts (exact).
-template <int MODE, bool SF16, bool SV, int T, bool TWO = false, int W8 = 0>  // MODE 0 tensor, 1 row, 2 group of 128
+// GE: exponent bits of 4-bit minifloat weights (1 E1M2, 2 E2M1, 3 E3M0) when W8 = 0.
+template <int MODE, bool SF16, bool SV, int T, bool TWO = false, int W8 = 0, int GE = 2>  // MODE 0 tensor, 1 row, 2 group of 128
 __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParams p) {
     constexpr int NW = kSmallWaves, CH = kSmallChunks;
     extern __shared__ uint4 xs[];  // per wavefront: [M][its K range / 8] bf16 vectors
@@ -397,10 +413,10 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
                         }
                         wf = __builtin_bit_cast(bf16x8, o);
                     } else {
-                        wf = decode_e2m1_bf16(wd[j]);
+                        wf = decode_mini4_bf16<GE>(wd[j]);
                     }
                     if (TWO) {
-                        const bf16x8 w1 = decode_e1m2_bf16(wd[j]);
+                        const bf16x8 w1 = decode_mini4_bf16<1>(wd[j]);
                         wf = e1m2 ? w1 : wf;
                     }
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[j]), wf, acc, 0, 0, 0);
@@ -451,10 +467,10 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
     }
 }
 
-template <int MODE, bool SF16, bool SV, int T, bool TWO = false, int W8 = 0>
+template <int MODE, bool SF16, bool SV, int T, bool TWO = false, int W8 = 0, int GE = 2>
 static hipError_t launch_small_t(const GemmParams& p, hipStream_t s) {
     const size_t lds = small_lds_bytes(p.M, p.K, T);
-    auto kern = w4a16_small_kernel<MODE, SF16, SV, T, TWO, W8>;
+    auto kern = w4a16_small_kernel<MODE, SF16, SV, T, TWO, W8, GE>;
     // the dynamic-LDS limit is a kernel attribute, set once per device
     static bool attr_set[64];
     int dev = 0;
@@ -469,24 +485,24 @@ static hipError_t launch_small_t(const GemmParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int MODE, bool SF16, bool SV, bool TWO = false, int W8 = 0>
+template <int MODE, bool SF16, bool SV, bool TWO = false, int W8 = 0, int GE = 2>
 static hipError_t launch_small_sv(const GemmParams& p, hipStream_t s) {
     // M <= 4: one 16-column tile per wavefront (more workgroups, X is small);
     // larger M: three tiles share each staged X
-    return p.M <= 4 ? launch_small_t<MODE, SF16, SV, 1, TWO, W8>(p, s) : launch_small_t<MODE, SF16, SV, 3, TWO, W8>(p, s);
+    return p.M <= 4 ? launch_small_t<MODE, SF16, SV, 1, TWO, W8, GE>(p, s) : launch_small_t<MODE, SF16, SV, 3, TWO, W8, GE>(p, s);
 }
 
-template <bool SF16, bool TWO = false, int W8 = 0>
+template <bool SF16, bool TWO = false, int W8 = 0, int GE = 2>
 static hipError_t launch_small(const GemmParams& p, hipStream_t s) {
     if (p.w_mode == 2) {
         const int64_t nchunks = p.K / 128;
         // one vector load per batch needs 4-byte aligned scale rows and batch starts
         const bool sv = SF16 ? (nchunks % (2 * kSmallWaves) == 0 && (reinterpret_cast<uintptr_t>(p.w_scales) & 3) == 0)
                              : (reinterpret_cast<uintptr_t>(p.w_scales) & 3) == 0;
-        return sv ? launch_small_sv<2, SF16, true, TWO, W8>(p, s) : launch_small_sv<2, SF16, false, TWO, W8>(p, s);
+        return sv ? launch_small_sv<2, SF16, true, TWO, W8, GE>(p, s) : launch_small_sv<2, SF16, false, TWO, W8, GE>(p, s);
     }
-    if (p.w_mode == 1) return launch_small_sv<1, SF16, false, false, W8>(p, s);
-    return launch_small_sv<0, SF16, false, false, W8>(p, s);
+    if (p.w_mode == 1) return launch_small_sv<1, SF16, false, false, W8, GE>(p, s);
+    return launch_small_sv<0, SF16, false, false, W8, GE>(p, s);
 }
 
 static bool small_fits(const GemmParams& p) {
@@ -514,18 +530,25 @@ hipError_t launch_w4a16_two_mode(const GemmParams& p, hipStream_t s) {
     return p.w_scale_f16 ? launch_small<true, true>(p, s) : launch_small<false, true>(p, s);
 }
 
-hipError_t launch_w4a16_mfma(const GemmParams& p, hipStream_t s) {
-    if (p.M == 0 || p.N == 0) return hipSuccess;
-    if (small_fits(p)) return p.w_scale_f16 ? launch_small<true>(p, s) : launch_small<false>(p, s);
+template <int GE>
+static hipError_t launch_w4a16_mfma_ge(const GemmParams& p, hipStream_t s) {
+    if (small_fits(p))
+        return p.w_scale_f16 ? launch_small<true, false, 0, GE>(p, s) : launch_small<false, false, 0, GE>(p, s);
     // larger M: reuse each activation fragment for two weight tiles
     if (p.M > 8) {
-        if (p.w_scale_f16) launch_w16<2, true>(p, s);
-        else launch_w16<2, false>(p, s);
+        if (p.w_scale_f16) launch_w16<2, true, GE>(p, s);
+        else launch_w16<2, false, GE>(p, s);
     } else {
-        if (p.w_scale_f16) launch_w16<1, true>(p, s);
-        else launch_w16<1, false>(p, s);
+        if (p.w_scale_f16) launch_w16<1, true, GE>(p, s);
+        else launch_w16<1, false, GE>(p, s);
     }
     return hipGetLastError();
+}
+hipError_t launch_w4a16_mfma(const GemmParams& p, hipStream_t s) {
+    if (p.M == 0 || p.N == 0) return hipSuccess;
+    if (p.wg.e == 1) return launch_w4a16_mfma_ge<1>(p, s);
+    if (p.wg.e == 3) return launch_w4a16_mfma_ge<3>(p, s);
+    return launch_w4a16_mfma_ge<2>(p, s);
 }
 
 // ---------------------------------------------------------------------------------

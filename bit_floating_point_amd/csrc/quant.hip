@@ -393,12 +393,13 @@ __global__ void __launch_bounds__(kThreads) quantize_two_mode_kernel(QuantParams
             const float y1 = v[k] * r1;
             const float d1c = fminf(rintf(fabsf(y1) * 4.0f), 7.0f);
             w1 |= ((__float_as_uint(y1) >> 31) << 3 | (uint32_t)d1c) << (4 * k);
-            // |x| and q = fl32(g * s) are within a factor of 2 of each other (q is the
-            // nearest grid value, |x| <= Qmax s) or q = 0, so |x| - q is exact in binary32
-            // (Sterbenz) and its square exact in binary64; their difference is rounded once
-            const float a = fabsf(v[k]);
-            const float d0 = a - fabsf(g0[k]) * s0, d1 = a - (d1c * 0.25f) * s1;
-            diff += (double)d0 * (double)d0 - (double)d1 * (double)d1;
+            // q = fl32(g * s) is the dequantized value; |x| - q is formed in binary64, where
+            // it is exact (q = 0, or |x| and q are binary32 values within a factor of 2 of
+            // each other: at most 26 significant bits), and so is its square (at most 52);
+            // the difference of the two squares is rounded once
+            const double a = (double)fabsf(v[k]);
+            const double d0 = a - (double)(fabsf(g0[k]) * s0), d1 = a - (double)((d1c * 0.25f) * s1);
+            diff += d0 * d0 - d1 * d1;
         }
         DD acc{diff, 0.0};
         for (int o = 1; o < lanes; o <<= 1) acc = dd_add(acc, DD{__shfl_xor(acc.hi, o, 64), __shfl_xor(acc.lo, o, 64)});

@@ -149,8 +149,8 @@ typedef struct {
     fp4_grid a_grid;          /* PACKED only: grid of the activation codes          */
     const float* a_scale;     /* PACKED only: device f32, the one scale a, or with
                                  a_scale_mode ROW one scale a_m per row (token) of X
-                                 ([Overview] per-token granularity; the E2M1 x E2M1
-                                 and FP8 / FP6 products)                            */
+                                 ([Overview] per-token granularity; the products
+                                 of two minifloat grids)                            */
     /* weights W [N, K], packed */
     const uint8_t* w;
     int64_t ldw;              /* bytes                                              */
@@ -310,6 +310,13 @@ fp4_status fp4_search_activations(const void* x, int32_t x_dtype, int64_t rows, 
  *       (per-token activation scales: y = fl32(acc * fl32(a_m * s_n)));
  *       K <= 116508 (the quarter-integer partial sums stay below 2^22), else
  *       FP4_ERR_UNSUPPORTED.
+ *     - E1M2 or E3M0 on either side, the other operand a 4-bit minifloat grid, runs on
+ *       the f8f6f4 matrix cores with each E1M2 / E3M0 code rewritten as the E4M3 byte
+ *       of the same value on its way into LDS (every E1M2 and E3M0 value is an E4M3
+ *       value).  Products of two 4-bit grids, or of a 4-bit grid and E2M3, are
+ *       multiples of 2^-5 that the instruction keeps whole, so acc is exact while
+ *       |acc| stays below 2^19; y = fl32(acc * fl32(a * s_n)) (per token: a_m) as
+ *       above, with f32 TENSOR/ROW weight scales and K a multiple of 32.
  *     - E2M1 activations x LUT16 weights (NF4) with GROUP scales (group a multiple of
  *       64) runs on the f16 matrix cores: each weight is expanded to
  *       w = fl16(G[c] * fl16(s[n,g] * 2^-e_n)), 2^e_n the power of two just above the
@@ -318,6 +325,10 @@ fp4_status fp4_search_activations(const void* x, int32_t x_dtype, int64_t rows, 
  *       norm) of the exact value; groups whose scale is below 2^-14 of their row's
  *       largest lose relative precision to f16 subnormals.
  *   y_dtype FP4_BF16 rounds the f32 result to nearest-even.
+ *   4-bit minifloat weights (E2M1, E1M2, E3M0) with BF16 activations run on the bf16
+ *   matrix cores (each code decoded exactly to bf16) when K is a multiple of 128, lda a
+ *   multiple of 8 and GROUP scales have a group that is a multiple of 128; other W4A16
+ *   shapes, and F32 activations, on a VALU kernel.
  *   FP8 / FP6 weights with F32/BF16 activations take the W4A16 path (W8A16 / W6A16):
  *   ldw >= K (FP8) or 3K/4 (FP6) bytes.  With PACKED activations both operands are FP8
  *   (E4M3, E5M2) or FP6 (E2M3, E3M2), in any pairing (W8A8, W6A6, mixed), on the
@@ -325,8 +336,8 @@ fp4_status fp4_search_activations(const void* x, int32_t x_dtype, int64_t rows, 
  *   (or one per row of A with a_scale_mode ROW, y = fl32(acc * fl32(a_m * s_n))):
  *   y = fl32(acc * fl32(a * s_n)), acc summed in fp32 (not exact: within the GEMM
  *   tolerance); lda, ldw >= the code bytes of a row (K or 3K/4), lda a multiple of 16,
- *   K a multiple of 32, rows shorter than 8 MiB.  The same holds when one operand is
- *   E2M1 and the other FP8 / FP6 (rows of K/2 bytes).
+ *   K a multiple of 32, rows shorter than 8 MiB.  The same holds when one operand is a
+ *   4-bit minifloat grid (E2M1, E1M2, E3M0) and the other FP8 / FP6 (rows of K/2 bytes).
  *   Two-mode weights (FP4_GRID_TWO_MODE, GROUP scales) take the W4A16 path only: each
  *   group's codes are read on its own grid (the sign of its scale) and scaled by |s|.
  * Strides: K a multiple of 32 for the matrix-core paths; packed rows 16-byte aligned. */

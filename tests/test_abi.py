@@ -198,7 +198,9 @@ def test_gemm_validation():
     assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_INVALID_ARG  # no a_scale
     d.a_scale = 0x50000
     d.a_grid = _grid(0, 1, 2)
-    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # E1M2 activations
+    d.w_gran = _gran(2, 64)
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # E1M2 activations, group weight scales
+    d.w_gran = _gran(1)
     d.a_grid = _grid()
     d.w_gran = _gran(2, 64)
     assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # E2M1 x E2M1 with group scales
@@ -213,7 +215,7 @@ def test_gemm_validation():
     d.y_dtype = L.FP4_BF16
     d.a_scale_mode = 5
     assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_INVALID_ARG
-    d.a_scale_mode = L.FP4_SCALE_ROW  # per-token activation scales: E2M1 x E2M1 only
+    d.a_scale_mode = L.FP4_SCALE_ROW  # per-token activation scales: minifloat weights only
     d.w_grid, d.w_gran = _grid(1), _gran(2, 64)
     for i in range(16):
         d.w_grid.lut[i] = (i - 7.5) / 8
@@ -298,7 +300,9 @@ def test_fp8_validation():
     d.a_grid, d.w_grid = _grid(0, 1, 2), g8
     d.w_gran = _gran(1)
     d.y_dtype = L.FP4_BF16
-    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # FP8 weights with packed E1M2 activations
+    d.lda = 120
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_ALIGNMENT  # E1M2 activation rows below K/2 bytes
+    d.lda = 128
     # W6A6 (FP6 E2M3 x FP6 E2M3): rows of 256 codes are 192 bytes
     g6 = _grid(0, 2, 3)
     d.a_grid, d.w_grid, d.lda, d.ldw = g6, g6, 192, 192

@@ -73,14 +73,17 @@ def depth_packed(K):
 # A group of 8 then loses less than 7 * 2^(E - 13) <= 7 * 2^-13 * (its magnitude sum).
 # Products that are multiples of 2^(E - 13) lose nothing: every E2M1 x E2M1, E2M3 x
 # E2M3 and E2M3 x E2M1 product (multiples of 2^-6 at most 56.25 in magnitude), so those
-# pairs are exact; FP8 and E3M2 operands span more binades and can lose bits.
+# pairs are exact.  E1M2 values are multiples of 2^-2 below 2, E3M0 values powers of two
+# from 1 to 64: their products with each other, with E2M1 and with E2M3 are multiples of
+# 2^-5 no larger than 480 (2^-5 >= 2^(8 - 13)), exact too.  FP8 and E3M2 operands span
+# more binades and can lose bits.
 WINDOW_LOSS = 7 * 2.0 ** -13
 
 
 def packed_window_term(af, wf, S):
     """The extra bound of the matrix instruction's product window (zero for the pairs
     whose products it keeps exactly)."""
-    exact = {(2, 1), (2, 3)}
+    exact = {(2, 1), (2, 3), (1, 2), (3, 0)}
     return 0.0 if (tuple(af) in exact and tuple(wf) in exact) else WINDOW_LOSS * np.asarray(S, np.float64)
 
 
@@ -366,6 +369,35 @@ def _preshift_chain(x, w, w_fmt="e2m1", group=64):
     gap, _ = F.fp4_quantize_pack(xt, fe2, F.gran("tensor"), tensor_scale=ga, col_shift=gk)
     assert np.array_equal(host(gap), ap)
     return (k, a, wp, ws, ap), (gk, ga, gwp, gws, gap, fw, fgran)
+
+
+@pytest.mark.parametrize("M,N,K,mode,group,sd,fmt", [
+    (1, 100, 128, "group", 128, "f16", (1, 2)),    # staged-activation kernel, one K chunk
+    (9, 61, 2176, "group", 128, "f16", (3, 0)),    # 17 chunks, ragged N
+    (16, 100, 4096, "group", 128, "f32", (1, 2)),  # f32 group scales as vector loads
+    (12, 70, 768, "row", 0, "f32", (3, 0)),        # per-row scales
+    (4, 1000, 4096, "group", 128, "f16", (3, 0)),  # decode shape, many workgroups
+    (19, 70, 512, "group", 256, "f32", (1, 2)),    # M > 16: the 16-row tile kernel, two chunks per group
+    (40, 200, 1024, "tensor", 0, "f32", (3, 0)),   # M > 16, one scale
+])
+def test_w4a16_e1m2_e3m0_matrix_cores(M, N, K, mode, group, sd, fmt):
+    """E1M2 / E3M0 weights with bf16 activations on the bf16 matrix-core kernels (each
+    code decoded exactly to bf16 through the FP8 convert): codes bit-exact, the product
+    within the bound of the binary64 oracle, bf16 output the rounding of the fp32 one."""
+    say("w4a16 e1m2/e3m0", M, N, K, mode, group, sd, fmt)
+    w = synth.weight(3, 15, N, K)
+    x = synth.activations(3, 16, M, K, bf16=True)
+    og, fg = grids(fmt)
+    packed, scales = O.quantize_pack(w, og, mode, group, sd)
+    g = F.gran(mode, group, sd)
+    gp, gs = F.fp4_quantize_pack(dev(w), fg, g)
+    assert np.array_equal(host(gp), packed)
+    r = O.gemm_w4a16(x, packed, og, mode, scales, group=group)
+    S = O.gemm_w4a16(x, packed, og, mode, scales, group=group, absolute=True)
+    xt = dev(x, torch.bfloat16)
+    y32 = F.fp4_gemm(xt, gp, gs, fg, g, y_dtype=torch.float32)
+    yb = F.fp4_gemm(xt, gp, gs, fg, g, y_dtype=torch.bfloat16)
+    _check_gemm(host(y32), r, S, depth_w4a16(K, group or K), yb)
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 384, 512), (200, 300, 544), (64, 96, 4096), (520, 1100, 1024)])
@@ -974,6 +1006,64 @@ def test_f8f6_gemm(M, N, K, wf, af, mode):
     S, _ = O.gemm_w4a4(ap, og_a, asc[0], wp, og_w, mode, wsc, absolute=True)
     y32 = host(F.fp4_gemm(gap, gwp, gws, fw, F.gran(mode), K=K, a_grid=fa, a_scale=ga, y_dtype=torch.float32))
     yb = F.fp4_gemm(gap, gwp, gws, fw, F.gran(mode), K=K, a_grid=fa, a_scale=ga, y_dtype=torch.bfloat16)
+    _check_gemm(y32, r, S, depth_packed(K), yb, packed_window_term(af, wf, S))
+
+
+@pytest.mark.parametrize("M,N,K,wf,af,mode", [
+    (300, 520, 544, (1, 2), (1, 2), "row"),      # E1M2 x E1M2, ragged tiles and K tail
+    (2100, 2200, 1024, (3, 0), (3, 0), "row"),   # E3M0 x E3M0, several tile rows and columns
+    (300, 520, 544, (2, 1), (1, 2), "tensor"),   # E2M1 weights, E1M2 activations
+    (300, 520, 544, (1, 2), (2, 1), "row"),      # E1M2 weights, E2M1 activations
+    (130, 270, 96, (3, 0), (2, 1), "row"),       # K below one step
+    (300, 520, 544, (2, 1), (3, 0), "row"),
+    (300, 520, 544, (3, 0), (1, 2), "tensor"),
+])
+def test_w4a4_e1m2_e3m0_exact(M, N, K, wf, af, mode):
+    """W4A4 with E1M2 or E3M0 on either side (codes expanded to E4M3 on their way into
+    LDS, every value of both grids being an E4M3 value): all their products with a 4-bit
+    grid are multiples of 2^-4 that the matrix instruction keeps whole, and the fp32 sums
+    stay exact, so the fp32 output is fl32(acc * fl32(a * s_n)) bit for bit and the bf16
+    output its nearest-even rounding."""
+    say("w4a4 e1m2/e3m0", M, N, K, wf, af, mode)
+    rng = np.random.default_rng(M + K + 7 * sum(wf) + af[0])
+    og_w, og_a = _wide(wf), _wide(af)
+    ap = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    wp = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    a = np.float32(rng.uniform(0.5, 2.0))
+    ws = rng.uniform(0.5, 2.0, N if mode == "row" else 1).astype(np.float32)
+    _, acc = O.gemm_w4a4(ap, og_a, a, wp, og_w, mode, ws)
+    assert np.array_equal(acc, acc.astype(np.float32).astype(np.float64))  # exact in binary32
+    y_pin = O.w4a4_epilogue_f32(acc, a, np.broadcast_to(ws, (N,)))
+    fw, fa = F.grid_minifloat(*wf), F.grid_minifloat(*af)
+    gap, gwp = _padded_rows(ap), _padded_rows(wp)
+    ga, gws = dev(np.array([a], np.float32)), dev(ws)
+    y32 = host(F.fp4_gemm(gap, gwp, gws, fw, F.gran(mode), K=K, a_grid=fa, a_scale=ga, y_dtype=torch.float32))
+    assert np.array_equal(y32.view(np.uint32), y_pin.view(np.uint32))
+    yb = F.fp4_gemm(gap, gwp, gws, fw, F.gran(mode), K=K, a_grid=fa, a_scale=ga, y_dtype=torch.bfloat16)
+    assert np.array_equal(_bf16_bits(yb), O.rne_bf16_bits(y_pin))
+
+
+@pytest.mark.parametrize("wf,af", [((4, 3), (1, 2)), ((1, 2), (4, 3)), ((3, 0), (2, 3)), ((2, 3), (1, 2)),
+                                   ((3, 0), (5, 2))])
+def test_w4a4_e1m2_e3m0_with_wide_grids(wf, af):
+    """E1M2 / E3M0 paired with an FP8 or FP6 grid, per-token activation scales: within
+    the GEMM tolerance of the binary64 oracle (with the product-window term where a
+    pair can lose product bits)."""
+    M, N, K = 300, 520, 512
+    say("w4a4 e1m2/e3m0 wide", wf, af)
+    x = synth.activations(21, M, M, K, outlier_frac=0.01, bf16=True)
+    w = synth.weight(21, N, N, K)
+    og_a, og_w = _wide(af), _wide(wf)
+    ap, asc = O.quantize_pack(x, og_a, "row")
+    wp, wsc = O.quantize_pack(w, og_w, "row")
+    fa, fw = F.grid_minifloat(*af), F.grid_minifloat(*wf)
+    gap, gas = F.fp4_quantize_pack(dev(x, torch.bfloat16), fa, F.gran("row"))
+    gwp, gws = F.fp4_quantize_pack(dev(w), fw, F.gran("row"))
+    assert np.array_equal(host(gap), ap) and np.array_equal(host(gwp), wp)
+    r, _ = O.gemm_w4a4(ap, og_a, asc, wp, og_w, "row", wsc)
+    S, _ = O.gemm_w4a4(ap, og_a, asc, wp, og_w, "row", wsc, absolute=True)
+    y32 = host(F.fp4_gemm(gap, gwp, gws, fw, F.gran("row"), K=K, a_grid=fa, a_scale=gas, y_dtype=torch.float32))
+    yb = F.fp4_gemm(gap, gwp, gws, fw, F.gran("row"), K=K, a_grid=fa, a_scale=gas, y_dtype=torch.bfloat16)
     _check_gemm(y32, r, S, depth_packed(K), yb, packed_window_term(af, wf, S))
 
 
