@@ -113,11 +113,11 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     constexpr int TM = WM / 32, TN = WN / 32;
     constexpr int LA = BM * 4 / (64 * NWV), LB = BN * 4 / (64 * NWV);  // 16-byte pieces per thread per step
     constexpr int STAGE = (BM + BN) * kBKBytes;
-    // four operand stages, per tile parity a 1 KiB block of per-column weight scales (GLU:
-    // gate scales, up scales and the output shifts, 1 KiB each), and each wavefront's
-    // output staging area (32 rows x WN/2 bf16 columns; GLU: its columns' multipliers
-    // and 32 rows of codes)
-    constexpr int SCL_BYTES = GLU ? 3072 : 1024;
+    // four operand stages, per tile parity a block of per-column weight scales and the
+    // tile's per-row (per-token) activation scales, 1 KiB each (GLU: gate scales, up
+    // scales and the output shifts), and each wavefront's output staging area (32 rows x
+    // WN/2 bf16 columns; GLU: its columns' multipliers and 32 rows of codes)
+    constexpr int SCL_BYTES = GLU ? 3072 : 2048;
     constexpr int STG_BYTES = GLU ? 2048 : 32 * WN;
     constexpr int ON = GLU ? BN / 2 : BN;  // output columns per tile
     __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * STAGE + 2 * SCL_BYTES + NWV * STG_BYTES];
@@ -146,6 +146,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     const i32x4v rsS = buf_words(p.w_scales, p.w_mode == 1 ? p.N * 4 : 4);
     const i32x4v rsS2 = GLU ? buf_words(gp.s_up, p.N * 4) : rsS;
     const i32x4v rsK = (GLU && gp.out_shift) ? buf_words(gp.out_shift, p.N) : buf_words(p.w_scales, 0);
+    const i32x4v rsR = buf_words(p.a_scale, p.a_row ? p.M * 4 : 0);  // per-token scales
     const float a_scale = p.a_scale[0];
     const float s_tensor = reinterpret_cast<const float*>(p.w_scales)[0];
     const float r_out = GLU ? recip_or_zero(gp.out_scale[0]) : 0.0f;  // next layer's fl32(1 / a')
@@ -161,7 +162,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
         int sidx = (NWV * i + wave) * 64 + lane, row = sidx >> 2;
         segk[i] = ((sidx & 3) ^ ((row >> 1) & 3)) * 16 * CPB;  // codes
     }
-    uint32_t offA[LA], offB[LB], offS, offK;
+    uint32_t offA[LA], offB[LB], offS, offK, offR;
     // Tile order.  Workgroups are dispatched to the 8 XCDs in turn (workgroup b on XCD
     // b % 8), each XCD with its own L2.  When the grid is a multiple of 8, XCD x takes the
     // tiles [ntiles x / 8, ntiles (x + 1) / 8) of the column-major tile order (tile t:
@@ -198,6 +199,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
         }
         offS = (ok && p.w_mode == 1 && n0 + 4 * lane < p.N && 4 * lane < ON) ? (uint32_t)((n0 + 4 * lane) * 4) : kOOB;
         offK = (ok && 16 * lane < ON && n0 + 16 * lane < p.N) ? (uint32_t)(n0 + 16 * lane) : kOOB;
+        offR = (ok && p.a_row && 4 * lane < BM && m0 + 4 * lane < p.M) ? (uint32_t)((m0 + 4 * lane) * 4) : kOOB;
     };
     load_tile(dt);
     // this wavefront's LDS slot base: load piece i of a stage goes to stage + (NWV i + wave) KiB
@@ -217,8 +219,11 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
             dma16_at((GLU && i >= LB / 2) ? rsB2 : rsB, off, wave_lds, st_ + (uint32_t)(BOFF + NWV * i * 1024)); \
         }                                                                                                  \
     } while (0)
-// the load stream's tile's 256 column scales into scales block dpar (all wavefronts
-// load the same 1 KiB, so every thread issues the same number of loads)
+// the load stream's tile's 256 column scales into scales block dpar, and its BM
+// per-token activation scales after them (zeros without them); all wavefronts load the
+// same bytes, so every thread issues the same number of loads.  The epilogue reads the
+// per-token scales from LDS: a register load there would need a full vmcnt(0) wait,
+// which would also wait for the next tile's first four steps.
 #define FP4_DMAS()                                                                                         \
     do {                                                                                                   \
         const uint32_t sb_ = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&scl[dpar * SCL_BYTES]); \
@@ -226,6 +231,8 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
         if (GLU) {                                                                                         \
             dma16(rsS2, offS, sb_ + 1024);                                                                 \
             dma16(rsK, offK, sb_ + 2048);                                                                  \
+        } else {                                                                                           \
+            dma16(rsR, offR, sb_ + 1024);                                                                  \
         }                                                                                                  \
     } while (0)
 // the load stream moves on to this workgroup's next tile
@@ -305,7 +312,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
         }                                                                                                  \
     } while (0)
     f32x16 acc[TN][TM];
-    constexpr int PER_STEP = LA + LB;  // operand loads per step and thread (+1 with scales)
+    constexpr int PER_STEP = LA + LB;  // operand loads per step and thread (+2 or +3 with the scales)
     // 16-byte output stores per thread of a staged epilogue (32 rows x WN bf16 columns
     // per wavefront and row block)
     constexpr int CH = WN / 8;  // 16-byte chunks per staged row
@@ -331,8 +338,8 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     // second half of step q.  Memory operations of a thread complete in issue order
     // (loads and stores alike), so "step q+1 landed" is "at most the operations issued
     // after it outstanding": the next two steps' loads, and in the first three phases
-    // of a tile also the previous tile's output stores.  (A step with the scales has one
-    // load more; that only makes a wait longer.)
+    // of a tile also the previous tile's output stores.  (A step with the scales has two
+    // or three loads more; that only makes a wait longer.)
 // (FP8: all of step q is in registers at the start of its phase; wait and meet the
 // barrier first -- step q+1 landed, every wavefront holds step q -- start the load into
 // q's stage, then run q's MFMAs while reading step q+1 into the registers they free.)
@@ -404,6 +411,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
         // sub-tile.
         const int64_t m0 = (int64_t)(ct % grid_m) * BM, n0 = (int64_t)(ct / grid_m) * ON;
         const float* sc = reinterpret_cast<const float*>(scl + cpar * SCL_BYTES);
+        const float* asc = reinterpret_cast<const float*>(scl + cpar * SCL_BYTES + 1024);  // per-token scales
         if constexpr (GLU) {
             // This wavefront's BN/4 output columns c0 + [0, WN/2) of rows wm * WM + [0, WM):
             // gate accumulators acc[jj], up accumulators acc[jj + TN/2].  First lane l puts
@@ -478,7 +486,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     #pragma unroll
                 for (int i = 0; i < TM; i++) {
                     // this lane's row's activation scale (one per token, or the tensor's)
-                    const float am = p.a_row ? p.a_scale[m0 + wm * WM + i * 32 + r32] : a_scale;
+                    const float am = p.a_row ? asc[wm * WM + i * 32 + r32] : a_scale;
     #pragma unroll
                     for (int jh = 0; jh < 2; jh++) {
     #pragma unroll
@@ -530,7 +538,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     #pragma unroll
                         for (int i = 0; i < TM; i++) {
                             const int64_t m = m0 + wm * WM + i * 32 + r32;
-                            const float am = p.a_row ? p.a_scale[m < p.M ? m : p.M - 1] : a_scale;
+                            const float am = p.a_row ? asc[wm * WM + i * 32 + r32] : a_scale;  // 0 past M
                             const float f0 = am * s4.x, f1 = am * s4.y, f2 = am * s4.z, f3 = am * s4.w;
                             const float y0 = agpr_read(acc[j][i][4 * g]) * f0, y1 = agpr_read(acc[j][i][4 * g + 1]) * f1;
                             const float y2 = agpr_read(acc[j][i][4 * g + 2]) * f2, y3 = agpr_read(acc[j][i][4 * g + 3]) * f3;
