@@ -36,8 +36,12 @@ constexpr int kBatch = 4;  // K chunks in flight per wavefront
 constexpr int kSmallWavesPerGroup = 8;
 constexpr size_t kSmallMaxLds = 136 * 1024;
 // The region also holds the wavefront's T partial-sum vectors per lane after its loop.
+// Wavefronts own whole pairs of 128-wide K chunks (the last pair may be a single chunk).
+__host__ __device__ inline int small_chunk_begin(int64_t nchunks, int wave) {
+    return (int)(2 * (((nchunks + 1) / 2) * wave / kSmallWavesPerGroup));
+}
 __host__ __device__ inline int small_region(int64_t M, int64_t nchunks, int T) {
-    const int64_t per_wave = (nchunks + kSmallWavesPerGroup - 1) / kSmallWavesPerGroup;
+    const int64_t per_wave = 2 * (((nchunks + 1) / 2 + kSmallWavesPerGroup - 1) / kSmallWavesPerGroup);
     const int64_t r = (M * per_wave * 16 + 63) / 64 * 64;
     return (int)(r > 64 * T ? r : 64 * T);
 }
@@ -82,6 +86,25 @@ __device__ __forceinline__ bf16x8 decode_mini4_bf16(uint32_t w) {
         o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, kScale, true));
         return __builtin_bit_cast(bf16x8, o);
     }
+}
+
+// The 16-byte pieces of two chunk loads e (rows r16 / 2) and o (rows 8 + r16 / 2),
+// swapped between neighbouring lanes 2i, 2i + 1 so that each lane ends up with both
+// chunks of one row: lane 2i keeps e (row i, chunk 2j) and takes its neighbour's e
+// (row i, chunk 2j + 1); lane 2i + 1 takes its neighbour's o (row 8 + i, chunk 2j) and
+// keeps o (row 8 + i, chunk 2j + 1).  One DPP quad permutation [1, 0, 3, 2] per dword.
+__device__ __forceinline__ void pair_swap(uint4& e, uint4& o, bool odd) {
+    uint32_t ev[4] = {e.x, e.y, e.z, e.w}, ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t send = odd ? ev[i] : ov[i];
+        const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xF, 0xF, false);
+        const uint32_t first = odd ? got : ev[i], second = odd ? ov[i] : got;
+        ev[i] = first;
+        ov[i] = second;
+    }
+    e = make_uint4(ev[0], ev[1], ev[2], ev[3]);
+    o = make_uint4(ov[0], ov[1], ov[2], ov[3]);
 }
 
 // Scale loads return raw bits; the conversion waits until the value is used, so a
@@ -272,8 +295,8 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
     const int q = lane >> 4, r16 = lane & 15;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * T;
     const int nchunks = (int)(p.K / 128);
-    const int c_begin = nchunks * wave / NW;
-    const int c_end = nchunks * (wave + 1) / NW;
+    const int c_begin = small_chunk_begin(nchunks, wave);
+    const int c_end = min(nchunks, small_chunk_begin(nchunks, wave + 1));
     // X vectors of one row in this wavefront's range (at least one chunk, so that a
     // wavefront with an empty range still forms valid addresses)
     const int nvw = c_end - c_begin > 0 ? (c_end - c_begin) * 16 : 16;
@@ -285,14 +308,32 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
     constexpr int SVB = CH * SB;           // bytes of one batch's scales of a row (8 or 16)
     const __amdgpu_buffer_rsrc_t rsW = buf_make(p.w, p.N * p.ldw);
     const __amdgpu_buffer_rsrc_t rsS = buf_make(p.w_scales, p.N * ngroups * SB);
-    uint32_t wrow[T], srow[T];
+    // PAIRS (4-bit weights, one tile per wavefront): each load instruction reads whole
+    // 128-byte lines.  Chunks 2j and 2j + 1 of a row are one 128-byte piece; the load of
+    // chunk 2j reads the pieces of the tile's rows 0..7, that of chunk 2j + 1 those of rows
+    // 8..15, lane (q, r16) the 16 bytes at (r16 % 2) * 64 + 16 q of row r16 / 2 (+ 8).  One
+    // swap between neighbouring lanes (pair_swap) then leaves lane (q, r16) with quarter q
+    // of both chunks of the row rho = r16 / 2 + 8 (r16 % 2), so column r16 of the tile's
+    // MFMAs is weight row rho.  Measured 1.5-3% faster at M = 1 and 4 (11008 x 4096); with
+    // three tiles per wavefront the swaps cost more than the loads gain, so those keep
+    // rho = r16 and 64 bytes of 16 rows per load, as FP8 / FP6 weights do.
+    constexpr bool PAIRS = !W8 && T == 1;
+    const int rho = PAIRS ? (r16 >> 1) + 8 * (r16 & 1) : r16;
+    uint32_t wrow[T], wrow2[T], srow[T];
     bool n_ok[T];
 #pragma unroll
     for (int t = 0; t < T; t++) {
-        const int64_t n = n0 + 16 * t + r16;
+        const int64_t n = n0 + 16 * t + rho;
         n_ok[t] = n < p.N;
         constexpr int LB = W8 >= 4 ? 32 : W8 ? 24 : 16;  // bytes of a lane's 32 codes
-        wrow[t] = n_ok[t] ? (uint32_t)(n * p.ldw + q * LB) : kOOB;
+        if (!PAIRS) {
+            wrow[t] = n_ok[t] ? (uint32_t)(n * p.ldw + q * LB) : kOOB;
+        } else {
+            const int64_t re = n0 + 16 * t + (r16 >> 1), ro = re + 8;
+            const int in = (r16 & 1) * 64 + q * 16;
+            wrow[t] = re < p.N ? (uint32_t)(re * p.ldw + in) : kOOB;
+            wrow2[t] = ro < p.N ? (uint32_t)(ro * p.ldw + in) : kOOB;
+        }
         srow[t] = n_ok[t] ? (uint32_t)(n * ngroups * SB) : kOOB;
     }
 
@@ -336,8 +377,14 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
                     w6b[b][t] = __builtin_bit_cast(
                         uint2, __builtin_amdgcn_raw_buffer_load_b64(rsW, wrow[t] + (uint32_t)(cs + b) * 96 + 16, 0, 0));
                 } else {
-                    wv[b][t] = buf_load16(rsW, wrow[t] + (uint32_t)(cs + b) * (W8 ? 128 : 64));
-                    if (W8) wv2[b][t] = buf_load16(rsW, wrow[t] + (uint32_t)(cs + b) * 128 + 16);
+                    if (W8) {
+                        wv[b][t] = buf_load16(rsW, wrow[t] + (uint32_t)(cs + b) * 128);
+                        wv2[b][t] = buf_load16(rsW, wrow[t] + (uint32_t)(cs + b) * 128 + 16);
+                    } else if (PAIRS) {  // cs is even: chunk cs + b is of parity b
+                        wv[b][t] = buf_load16(rsW, ((b & 1) ? wrow2[t] : wrow[t]) + (uint32_t)(cs / 2 + b / 2) * 128);
+                    } else {
+                        wv[b][t] = buf_load16(rsW, wrow[t] + (uint32_t)(cs + b) * 64);
+                    }
                 }
                 if (MODE == 2 && !SV) {
                     const uint32_t off = srow[t] + (uint32_t)(cs + b) * SB;
@@ -373,6 +420,10 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
             const int c = c0 + b;
             const bool valid = c < c_end;
             const int cc = valid ? c : c_begin;
+            if (PAIRS && (b & 1) == 0) {
+#pragma unroll
+                for (int t = 0; t < T; t++) pair_swap(wv[b][t], wv[b + 1][t], (r16 & 1) != 0);
+            }
             uint4 xa[4];
 #pragma unroll
             for (int j = 0; j < 4; j++) xa[j] = xs[xrow + cc * 16 + q * 4 + j];
@@ -435,7 +486,7 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
 #pragma unroll
     for (int t = 0; t < T; t++) {
         if (MODE != 2) {
-            const float s = scale_value<SF16>(load_scale_raw<SF16>(p, MODE == 1 ? (n_ok[t] ? n0 + 16 * t + r16 : 0) : 0));
+            const float s = scale_value<SF16>(load_scale_raw<SF16>(p, MODE == 1 ? (n_ok[t] ? n0 + 16 * t + rho : 0) : 0));
 #pragma unroll
             for (int i = 0; i < 4; i++) total[t][i] = total[t][i] * s;
         }
@@ -453,7 +504,7 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
                 for (int i = 0; i < 4; i++) total[t][i] += o[i];
             }
             if (!n_ok[t]) continue;
-            const int64_t n = n0 + 16 * t + r16;
+            const int64_t n = n0 + 16 * t + rho;
             // D layout of a 16x16 MFMA: lane holds rows 4*(lane/16) + i of column lane%16
 #pragma unroll
             for (int i = 0; i < 4; i++) {
