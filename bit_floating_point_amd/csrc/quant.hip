@@ -577,6 +577,70 @@ __global__ void __launch_bounds__(kThreads) quantize_row_reg_kernel(QuantParams 
     }
 }
 
+// ROW mode, E2M1, f32 input, rows of at most NB * 1024 elements: one workgroup per row
+// with every load instruction reading 1 KiB contiguous (whole 128-byte lines): load b of
+// lane l of wavefront w takes columns 1024 b + 256 w + 4 l .. + 3.  The loads are buffer
+// loads (offsets past the row read zeros, so no load sits under a lane-dependent
+// branch) that bypass the caches' retention; the row stays in registers (one HBM read).
+// SH = 1: the weights' pre-shift x' = x * 2^k, applied as the row is loaded (before the
+// row maximum); SH = -1: the activation-side y = fl32(x * fl32(r * 2^-k)); SH = 0: no
+// shifts.  Codes are stored as 16-bit pieces.  The arithmetic is that of
+// quantize_row_reg_kernel.
+template <int NB, int SH>
+__global__ void __launch_bounds__(kThreads) quantize_e2m1_row_f32_kernel(QuantParams p) {
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    __shared__ float red[kThreads / 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t row = blockIdx.x;
+    const __amdgpu_buffer_rsrc_t rx = buf_make(reinterpret_cast<const float*>(p.x) + row * p.ldx, p.cols * 4);
+    const __amdgpu_buffer_rsrc_t rk = buf_make(p.col_shift, SH ? p.cols : 0);
+    f32x4v v[NB];
+    uint32_t kk[SH < 0 ? NB : 1];
+    float m = 0.0f;
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        const uint32_t c = 1024 * b + 256 * wave + 4 * lane;
+        v[b] = __builtin_bit_cast(f32x4v, __builtin_amdgcn_raw_buffer_load_b128(rx, 4 * c, 0, 2));
+        if (SH != 0) {
+            const uint32_t k = __builtin_amdgcn_raw_buffer_load_b32(rk, c, 0, 0);
+            if (SH > 0) {
+#pragma unroll
+                for (int i = 0; i < 4; i++) v[b][i] = __builtin_amdgcn_ldexpf(v[b][i], (int)(int8_t)(k >> (8 * i)));
+            } else {
+                kk[b] = k;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) m = fmaxf(m, fabsf(v[b][i]));
+    }
+    float amax;
+    if (p.amax_in) {
+        amax = p.amax_in[row];
+    } else {
+        m = dpp_wave_max(m);
+        if (lane == 0) red[wave] = m;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    }
+    float s = amax / p.g.qmax;
+    if (p.scale_f16) s = round_f16(s);
+    const float r = recip_or_zero(s);
+    if (threadIdx.x == 0 && p.scales_out) store_scale(p, row, s);
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        const int64_t c = 1024 * b + 256 * wave + 4 * lane;
+        float y[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            y[i] = SH < 0 ? v[b][i] * __builtin_amdgcn_ldexpf(r, -(int)(int8_t)(kk[b] >> (8 * i))) : v[b][i] * r;
+        uint32_t w = 0;
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+        if (c < p.cols)  // cols is a multiple of 8: the 4 columns are in range together
+            __builtin_nontemporal_store((uint16_t)w, reinterpret_cast<uint16_t*>(p.packed + row * p.ldp + c / 2));
+    }
+}
+
 // ROW mode for longer rows: pass 1 reduces the row max, pass 2 re-reads (L2) and
 // quantizes.
 template <bool VEC, bool BF16>
@@ -669,6 +733,14 @@ hipError_t launch_tensor_scale_finalize(const float* amax, float* scales_out, fl
     return hipGetLastError();
 }
 
+template <int SH>
+static void row_f32_launch(const QuantParams& p, dim3 grid, hipStream_t s) {
+    if (p.cols <= 4 * 1024) hipLaunchKernelGGL((quantize_e2m1_row_f32_kernel<4, SH>), grid, dim3(kThreads), 0, s, p);
+    else if (p.cols <= 6 * 1024) hipLaunchKernelGGL((quantize_e2m1_row_f32_kernel<6, SH>), grid, dim3(kThreads), 0, s, p);
+    else if (p.cols <= 8 * 1024) hipLaunchKernelGGL((quantize_e2m1_row_f32_kernel<8, SH>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((quantize_e2m1_row_f32_kernel<14, SH>), grid, dim3(kThreads), 0, s, p);
+}
+
 template <bool VEC, bool BF16>
 static void quantize_launch(const QuantParams& p, hipStream_t s) {
     constexpr int QT = 256;  // threads of the E2M1 group-128 kernel
@@ -680,7 +752,11 @@ static void quantize_launch(const QuantParams& p, hipStream_t s) {
         else hipLaunchKernelGGL((quantize_wide_row_kernel<VEC, BF16, 3, 2>), grid, dim3(kThreads), 0, s, p);
     } else if (p.mode == 1) {
         dim3 grid((unsigned)p.rows);
-        if (p.cols <= 4 * kChunk) hipLaunchKernelGGL((quantize_row_reg_kernel<VEC, BF16, 4>), grid, dim3(kThreads), 0, s, p);
+        if (VEC && !BF16 && p.g.is_e2m1 && p.cols <= 14 * 1024) {
+            if (!p.col_shift) row_f32_launch<0>(p, grid, s);
+            else if (p.shift_sign > 0) row_f32_launch<1>(p, grid, s);
+            else row_f32_launch<-1>(p, grid, s);
+        } else if (p.cols <= 4 * kChunk) hipLaunchKernelGGL((quantize_row_reg_kernel<VEC, BF16, 4>), grid, dim3(kThreads), 0, s, p);
         else if (p.cols <= 8 * kChunk) hipLaunchKernelGGL((quantize_row_reg_kernel<VEC, BF16, 8>), grid, dim3(kThreads), 0, s, p);
         else hipLaunchKernelGGL((quantize_row_kernel<VEC, BF16>), grid, dim3(kThreads), 0, s, p);
     } else {
