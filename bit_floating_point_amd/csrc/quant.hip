@@ -577,6 +577,58 @@ __global__ void __launch_bounds__(kThreads) quantize_row_reg_kernel(QuantParams 
     }
 }
 
+// TENSOR mode with the E2M1 grid on bf16 input (the activations; optionally with the
+// column shifts r * 2^-k): U (row, 2048-column) units per workgroup of 256 threads, lane
+// l of wavefront w taking columns 512 w + 8 l .. + 7 of each, so every load instruction
+// reads 1 KiB contiguous.  Buffer loads (zeros past the row, no lane-dependent branch
+// around a load) that bypass the caches' retention, all U issued before any arithmetic;
+// 4-byte code stores, also nontemporal.  The arithmetic is that of
+// quantize_e2m1_tensor_kernel.
+template <bool SHIFT, int U>
+__global__ void __launch_bounds__(kThreads) quantize_e2m1_tensor_bf16_kernel(QuantParams p, int chunks, int nunits) {
+    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t rx = buf_make(p.x, (int64_t)p.rows * p.ldx * 2);
+    const __amdgpu_buffer_rsrc_t rk = buf_make(p.col_shift, SHIFT ? p.cols : 0);
+    u32x4v raw[U];
+    uint2 kk[U];
+    int row[U];
+    int64_t col[U];
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+        int u = blockIdx.x * U + i;
+        if (u >= nunits) u = nunits - 1;  // a duplicate of the last unit writes the same bytes
+        row[i] = u / chunks;
+        col[i] = (int64_t)(u - row[i] * chunks) * 2048 + threadIdx.x * 8;
+        const uint32_t off = col[i] < p.cols ? (uint32_t)(((int64_t)row[i] * p.ldx + col[i]) * 2) : kOOB;
+        raw[i] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 2));
+        if (SHIFT) {
+            const uint32_t ko = col[i] < p.cols ? (uint32_t)col[i] : kOOB;
+            kk[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, ko, 0, 0));
+        }
+    }
+    const float s = p.tensor_scale ? p.tensor_scale[0] : p.tensor_amax[0] / p.g.qmax;
+    const float r = recip_or_zero(s);
+    if (blockIdx.x == 0 && threadIdx.x == 0 && p.tensor_scale && p.scales_out)
+        reinterpret_cast<float*>(p.scales_out)[0] = s;
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            v[2 * j] = __uint_as_float(raw[i][j] << 16);
+            v[2 * j + 1] = __uint_as_float(raw[i][j] & 0xffff0000u);
+        }
+        scale_values(v, r, SHIFT, SHIFT ? kk[i] : make_uint2(0, 0));
+        uint32_t w = 0;
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+        if (col[i] < p.cols)
+            __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(p.packed + (int64_t)row[i] * p.ldp + col[i] / 2));
+    }
+}
+
 // ROW mode, E2M1, f32 input, rows of at most NB * 1024 elements: one workgroup per row
 // with every load instruction reading 1 KiB contiguous (whole 128-byte lines): load b of
 // lane l of wavefront w takes columns 1024 b + 256 w + 4 l .. + 3.  The loads are buffer
@@ -638,6 +690,65 @@ __global__ void __launch_bounds__(kThreads) quantize_e2m1_row_f32_kernel(QuantPa
         w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
         if (c < p.cols)  // cols is a multiple of 8: the 4 columns are in range together
             __builtin_nontemporal_store((uint16_t)w, reinterpret_cast<uint16_t*>(p.packed + row * p.ldp + c / 2));
+    }
+}
+
+// ROW mode, E2M1, bf16 input (per-token activation scales), rows of at most NB * 2048
+// elements: the f32 kernel above with 8 values (16 bytes) per lane and load, lane l of
+// wavefront w taking columns 2048 b + 512 w + 8 l .. + 7 of load b (1 KiB contiguous per
+// load instruction); 4-byte code stores.  SH as above.
+template <int NB, int SH>
+__global__ void __launch_bounds__(kThreads) quantize_e2m1_row_bf16_kernel(QuantParams p) {
+    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+    __shared__ float red[kThreads / 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t row = blockIdx.x;
+    const __amdgpu_buffer_rsrc_t rx = buf_make(reinterpret_cast<const uint16_t*>(p.x) + row * p.ldx, p.cols * 2);
+    const __amdgpu_buffer_rsrc_t rk = buf_make(p.col_shift, SH ? p.cols : 0);
+    float v[NB][8];
+    uint2 kk[SH < 0 ? NB : 1];
+    float m = 0.0f;
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        const uint32_t c = 2048 * b + 512 * wave + 8 * lane;
+        const u32x4v raw = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * c, 0, 2));
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            v[b][2 * j] = __uint_as_float(raw[j] << 16);
+            v[b][2 * j + 1] = __uint_as_float(raw[j] & 0xffff0000u);
+        }
+        if (SH != 0) {
+            const uint2 k = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, c, 0, 0));
+            if (SH > 0) shift_inputs(v[b], k);
+            else kk[b] = k;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[b][i]));
+    }
+    float amax;
+    if (p.amax_in) {
+        amax = p.amax_in[row];
+    } else {
+        m = dpp_wave_max(m);
+        if (lane == 0) red[wave] = m;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    }
+    float s = amax / p.g.qmax;
+    if (p.scale_f16) s = round_f16(s);
+    const float r = recip_or_zero(s);
+    if (threadIdx.x == 0 && p.scales_out) store_scale(p, row, s);
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        const int64_t c = 2048 * b + 512 * wave + 8 * lane;
+        scale_values(v[b], r, SH < 0, SH < 0 ? kk[b] : make_uint2(0, 0));
+        uint32_t w = 0;
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[b][0], v[b][1], 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[b][2], v[b][3], 1.0f, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[b][4], v[b][5], 1.0f, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[b][6], v[b][7], 1.0f, 3);
+        if (c < p.cols)  // cols is a multiple of 8: the 8 columns are in range together
+            __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(p.packed + row * p.ldp + c / 2));
     }
 }
 
@@ -734,6 +845,14 @@ hipError_t launch_tensor_scale_finalize(const float* amax, float* scales_out, fl
 }
 
 template <int SH>
+static void row_bf16_launch(const QuantParams& p, dim3 grid, hipStream_t s) {
+    if (p.cols <= 2 * 2048) hipLaunchKernelGGL((quantize_e2m1_row_bf16_kernel<2, SH>), grid, dim3(kThreads), 0, s, p);
+    else if (p.cols <= 3 * 2048) hipLaunchKernelGGL((quantize_e2m1_row_bf16_kernel<3, SH>), grid, dim3(kThreads), 0, s, p);
+    else if (p.cols <= 4 * 2048) hipLaunchKernelGGL((quantize_e2m1_row_bf16_kernel<4, SH>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((quantize_e2m1_row_bf16_kernel<7, SH>), grid, dim3(kThreads), 0, s, p);
+}
+
+template <int SH>
 static void row_f32_launch(const QuantParams& p, dim3 grid, hipStream_t s) {
     if (p.cols <= 4 * 1024) hipLaunchKernelGGL((quantize_e2m1_row_f32_kernel<4, SH>), grid, dim3(kThreads), 0, s, p);
     else if (p.cols <= 6 * 1024) hipLaunchKernelGGL((quantize_e2m1_row_f32_kernel<6, SH>), grid, dim3(kThreads), 0, s, p);
@@ -756,6 +875,10 @@ static void quantize_launch(const QuantParams& p, hipStream_t s) {
             if (!p.col_shift) row_f32_launch<0>(p, grid, s);
             else if (p.shift_sign > 0) row_f32_launch<1>(p, grid, s);
             else row_f32_launch<-1>(p, grid, s);
+        } else if (VEC && BF16 && p.g.is_e2m1 && p.cols <= 7 * 2048) {
+            if (!p.col_shift) row_bf16_launch<0>(p, grid, s);
+            else if (p.shift_sign > 0) row_bf16_launch<1>(p, grid, s);
+            else row_bf16_launch<-1>(p, grid, s);
         } else if (p.cols <= 4 * kChunk) hipLaunchKernelGGL((quantize_row_reg_kernel<VEC, BF16, 4>), grid, dim3(kThreads), 0, s, p);
         else if (p.cols <= 8 * kChunk) hipLaunchKernelGGL((quantize_row_reg_kernel<VEC, BF16, 8>), grid, dim3(kThreads), 0, s, p);
         else hipLaunchKernelGGL((quantize_row_kernel<VEC, BF16>), grid, dim3(kThreads), 0, s, p);
@@ -792,7 +915,20 @@ static void quantize_launch(const QuantParams& p, hipStream_t s) {
         else if (VEC && p.mode == 0 && p.g.is_e2m1 && !p.amax_in && (!p.col_shift || p.shift_sign < 0) &&
                  p.rows * ((p.cols + QT * 8 - 1) / (QT * 8)) < (1LL << 30) && p.cols < (1LL << 30)) {
             const int64_t qchunks = (p.cols + QT * 8 - 1) / (QT * 8), qunits = p.rows * qchunks;
-            if (p.col_shift)
+#ifndef TBF_U
+#define TBF_U 4
+#endif
+            if (BF16 && p.rows * p.ldx * 2 < 0x7fff0000LL) {
+                constexpr int TU = TBF_U;  // measured: 1 / 2 / 4 units at 0.47 / 0.49 / 0.49 (2048x4096),
+                                           // 0.65 / 0.69 / 0.76 (4096x13824) of HBM
+                const dim3 g((unsigned)((qunits + TU - 1) / TU));
+                if (p.col_shift)
+                    hipLaunchKernelGGL((quantize_e2m1_tensor_bf16_kernel<true, TU>), g, dim3(kThreads), 0, s, p,
+                                       (int)qchunks, (int)qunits);
+                else
+                    hipLaunchKernelGGL((quantize_e2m1_tensor_bf16_kernel<false, TU>), g, dim3(kThreads), 0, s, p,
+                                       (int)qchunks, (int)qunits);
+            } else if (p.col_shift)
                 hipLaunchKernelGGL((quantize_e2m1_tensor_kernel<BF16, true, QT>), dim3((unsigned)qunits), dim3(QT), 0, s,
                                    p, (int)qchunks);
             else
