@@ -329,6 +329,63 @@ __global__ void __launch_bounds__(kThreads) quantize_wide_kernel(QuantParams p, 
     }
 }
 
+// GROUP mode, group 128, f32 input, on an OCP 8-bit or 6-bit grid: the load pattern of
+// quantize_e2m1_g128_f32_kernel (wavefront w of a (row, 4096-column) unit takes columns
+// c0 + 512 w + 256 h + 4 l .. + 3 in its load h, every load instruction 1 KiB contiguous,
+// a 128-element group is 32 lanes of one load), codes by wide_code.  FP8: a lane stores
+// its 4 codes as one 4-byte word.  FP6: a lane's 4 codes are 24 bits; a DPP swap gives
+// each even lane its odd neighbour's 24 bits and the even lane stores the pair's 6 bytes
+// as three 16-bit words.  Loads and code stores are nontemporal.  The arithmetic is that
+// of quantize_wide_kernel.
+template <int E, int M>
+__global__ void __launch_bounds__(512) quantize_wide_g128_f32_kernel(QuantParams p, int chunks) {
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = blockIdx.x / chunks;
+    const int64_t c0 = (int64_t)(blockIdx.x - row * chunks) * 4096 + wave * 512 + 4 * lane;
+    const float* xr = reinterpret_cast<const float*>(p.x) + (int64_t)row * p.ldx;
+    f32x4v v[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const int64_t c = c0 + 256 * h;
+        v[h] = c < p.cols ? __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(xr + c)) : f32x4v{0, 0, 0, 0};
+    }
+    const int64_t gpr = p.cols / 128;  // groups per row
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const int64_t c = c0 + 256 * h;
+        float m = fmaxf(fmaxf(fabsf(v[h][0]), fabsf(v[h][1])), fmaxf(fabsf(v[h][2]), fabsf(v[h][3])));
+        m = dpp_max16(m);
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        float s = m / p.g.qmax;
+        if (p.scale_f16) s = round_f16(s);
+        const float r = recip_or_zero(s);
+        uint32_t code[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) code[i] = wide_code<E, M>(v[h][i] * r);
+        if (E + M == 7) {
+            if (c < p.cols) {  // cols is a multiple of 128: the whole group is in range
+                if ((lane & 31) == 0 && p.scales_out) store_scale(p, (int64_t)row * gpr + c / 128, s);
+                const uint32_t w = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+                __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(p.packed + (int64_t)row * p.ldp + c));
+            }
+        } else {
+            const uint32_t b24 = code[0] | (code[1] << 6) | (code[2] << 12) | (code[3] << 18);
+            const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b24, 0xB1, 0xF, 0xF, false);
+            if (c < p.cols) {
+                if ((lane & 31) == 0 && p.scales_out) store_scale(p, (int64_t)row * gpr + c / 128, s);
+                if ((lane & 1) == 0) {
+                    const uint64_t bits = (uint64_t)b24 | ((uint64_t)nb << 24);
+                    uint16_t* dst = reinterpret_cast<uint16_t*>(p.packed + (int64_t)row * p.ldp + c / 4 * 3);
+                    __builtin_nontemporal_store((uint16_t)bits, dst);
+                    __builtin_nontemporal_store((uint16_t)(bits >> 16), dst + 1);
+                    __builtin_nontemporal_store((uint16_t)(bits >> 32), dst + 2);
+                }
+            }
+        }
+    }
+}
+
 // GROUP mode with the two-mode grid ([HiFloat4] section 2.1: per group the E2M1 or the
 // E1M2 layout, one control bit).  Per group both candidates are formed -- s_m =
 // fl32(amax / Qmax_m) (binary16-rounded for f16 scales), codes of y = fl32(x * fl32(1/s_m))
@@ -887,7 +944,17 @@ static void quantize_launch(const QuantParams& p, hipStream_t s) {
         int64_t chunks = (p.cols + kChunk - 1) / kChunk;
         int64_t nunits = p.rows * chunks;
         dim3 grid((unsigned)((nunits + U - 1) / U));
-        if (p.g.bits != 4 && p.g.e == 4)
+        const bool wide_g128 = VEC && !BF16 && p.g.bits != 4 && p.mode == 2 && p.group == 128 && !p.col_shift &&
+                               !p.amax_in && p.cols % 128 == 0 && p.rows * ((p.cols + 4095) / 4096) < (1LL << 31) &&
+                               p.cols < (1LL << 30);
+        if (wide_g128) {
+            const int wchunks = (int)((p.cols + 4095) / 4096);
+            const dim3 wg((unsigned)(p.rows * wchunks));
+            if (p.g.e == 4) hipLaunchKernelGGL((quantize_wide_g128_f32_kernel<4, 3>), wg, dim3(512), 0, s, p, wchunks);
+            else if (p.g.e == 5) hipLaunchKernelGGL((quantize_wide_g128_f32_kernel<5, 2>), wg, dim3(512), 0, s, p, wchunks);
+            else if (p.g.e == 2) hipLaunchKernelGGL((quantize_wide_g128_f32_kernel<2, 3>), wg, dim3(512), 0, s, p, wchunks);
+            else hipLaunchKernelGGL((quantize_wide_g128_f32_kernel<3, 2>), wg, dim3(512), 0, s, p, wchunks);
+        } else if (p.g.bits != 4 && p.g.e == 4)
             hipLaunchKernelGGL((quantize_wide_kernel<VEC, BF16, U, 4, 3>), grid, dim3(kThreads), 0, s, p, chunks, nunits);
         else if (p.g.bits != 4 && p.g.e == 5)
             hipLaunchKernelGGL((quantize_wide_kernel<VEC, BF16, U, 5, 2>), grid, dim3(kThreads), 0, s, p, chunks, nunits);

@@ -837,6 +837,8 @@ def _wide(fmt):
 
 @pytest.mark.parametrize("fmt", [(4, 3), (5, 2), (2, 3), (3, 2)])
 @pytest.mark.parametrize("rows,cols,mode,group,sd,bf16", [
+    (33, 5120, "group", 128, "f16", False),  # f32 group-128 kernel: a partial second 4096-column unit
+    (7, 256, "group", 128, "f32", False),
     (37, 1040, "group", 8, "f32", False),
     (64, 4096, "group", 128, "f16", True),
     (30, 2056, "tensor", 0, "f32", False),   # a ragged last chunk, amax computed here
