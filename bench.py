@@ -180,15 +180,15 @@ def traffic_for(kernel_file: str, key: str):
 # Dispatches of `bench.py --profile all`, in launch order: (key, kernel file, kernel-name
 # fragment, index range among the dispatches whose name has that fragment).
 TRAFFIC_KERNELS = [
-    ("quantize_decode", "quant.hip", "quantize_e2m1_g128_kernel<false, 1, 256>", (0, 3)),
-    ("gemv_m1", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 1, false, 0>", (0, 3)),
-    ("gemv_m4", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 1, false, 0>", (3, 6)),
-    ("gemv_m16", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 3, false, 0>", (0, 3)),
-    ("quantize_act", "quant.hip", "quantize_e2m1_tensor_kernel<true, true, 256>", (0, 3)),
-    ("w4a4_c3", "gemm_w4a4.hip", "w4a4_fp4_kernel<128, 128, false, 0>", (0, 3)),
-    ("w4a4_qkv", "gemm_w4a4.hip", "w4a4_fp4_kernel<256, 256, false, 0>", (0, 3)),
+    ("quantize_decode", "quant.hip", "quantize_e2m1_g128_f32_kernel<512, 1>", (0, 3)),
+    ("gemv_m1", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 1, false, 0, 2>", (0, 3)),
+    ("gemv_m4", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 1, false, 0, 2>", (3, 6)),
+    ("gemv_m16", "gemm_w4a16.hip", "w4a16_small_kernel<2, true, true, 3, false, 0, 2>", (0, 3)),
+    ("quantize_act", "quant.hip", "quantize_e2m1_tensor_bf16_kernel<true, 4>", (0, 3)),
+    ("w4a4_c3", "gemm_w4a4.hip", "w4a4_fp4_kernel<128, 128, false, 0, 4>", (0, 3)),
+    ("w4a4_qkv", "gemm_w4a4.hip", "w4a4_fp4_kernel<256, 256, false, 0, 8>", (0, 3)),
     ("nf4_qkv", "gemm_lut.hip", "w4a4_lut_kernel<256, 256, false>", (0, 3)),
-    ("swiglu", "gemm_w4a4.hip", "w4a4_fp4_kernel<256, 256, true, 0>", (0, 3)),
+    ("swiglu", "gemm_w4a4.hip", "w4a4_fp4_kernel<256, 256, true, 0, 8>", (0, 3)),
 ]
 COPY_BYTES = 256 * 1024 * 1024  # the reference device copy of profile_run
 

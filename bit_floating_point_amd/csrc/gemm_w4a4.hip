@@ -33,7 +33,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBKBytes = 64;  // 128 codes per K step
 
-__device__ __forceinline__ int swz(int row, int seg) { return row * kBKBytes + ((seg ^ ((row >> 1) & 3)) << 4); }
+// A stage row is 64 bytes (four 16-byte segments); segment seg of row r sits in slot
+// seg ^ ((r >> 2) & 3).  The 128-bit fragment reads are served 16 lanes at a time, the
+// lanes of a group reading 16 consecutive rows at the same segment: rows r, r + 4, r + 8,
+// r + 12 share their position in the 256-byte bank row and the XOR with r / 4 sends them
+// to four different slots, so the 16 reads cover all 64 banks once.  (An XOR with r / 2
+// repeats every 8 rows and left every group 2-way conflicted: half of all LDS cycles
+// were bank-conflict cycles in the counters.)
+__device__ __forceinline__ int swz(int row, int seg) { return row * kBKBytes + ((seg ^ ((row >> 2) & 3)) << 4); }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -160,7 +167,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
 #pragma unroll
     for (int i = 0; i < (LA > LB ? LA : LB); i++) {
         int sidx = (NWV * i + wave) * 64 + lane, row = sidx >> 2;
-        segk[i] = ((sidx & 3) ^ ((row >> 1) & 3)) * 16 * CPB;  // codes
+        segk[i] = ((sidx & 3) ^ ((row >> 2) & 3)) * 16 * CPB;  // codes (the segment stored in slot sidx % 4)
     }
     uint32_t offA[LA], offB[LB], offS, offK, offR;
     // Tile order.  Workgroups are dispatched to the 8 XCDs in turn (workgroup b on XCD
