@@ -143,6 +143,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     const int wm = wave & 1, wn = wave >> 1;
     const int r32 = lane & 31, hk = lane >> 5;
     const int nk = (int)((p.K + 64 * CPB - 1) / (64 * CPB));
+    const int kK = (int)p.K;  // 32-bit bound checks (rows are below 2^31 bytes; K far smaller)
     // The step count per tile is rounded up to a multiple of 4 (the stage rotation);
     // steps past the last real one load zeros (out-of-range offsets) and add nothing.
     const int nk4 = (nk + 3) & ~3;
@@ -154,6 +155,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     const i32x4v rsS2 = GLU ? buf_words(gp.s_up, p.N * 4) : rsS;
     const i32x4v rsK = (GLU && gp.out_shift) ? buf_words(gp.out_shift, p.N) : buf_words(p.w_scales, 0);
     const i32x4v rsR = buf_words(p.a_scale, p.a_row ? p.M * 4 : 0);  // per-token scales
+    // read before any store of this kernel, so they can come through the scalar cache
     const float a_scale = p.a_scale[0];
     const float s_tensor = reinterpret_cast<const float*>(p.w_scales)[0];
     const float r_out = GLU ? recip_or_zero(gp.out_scale[0]) : 0.0f;  // next layer's fl32(1 / a')
@@ -218,11 +220,11 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
         const int kb_ = (KB);                                                                              \
         const uint32_t st_ = (uint32_t)((STG) - smem);                                                     \
         _Pragma("unroll") for (int i = 0; i < LA; i++) {                                                   \
-            uint32_t off = (kb_ * 64 * CPB + segk[i] < p.K) ? offA[i] + (uint32_t)kb_ * kBKBytes : kOOB;   \
+            uint32_t off = (kb_ * 64 * CPB + segk[i] < kK) ? offA[i] + (uint32_t)kb_ * kBKBytes : kOOB;    \
             dma16_at(rsA, off, wave_lds, st_ + (uint32_t)(NWV * i * 1024));                                \
         }                                                                                                  \
         _Pragma("unroll") for (int i = 0; i < LB; i++) {                                                   \
-            uint32_t off = (kb_ * 64 * CPB + segk[i] < p.K) ? offB[i] + (uint32_t)kb_ * kBKBytes : kOOB;   \
+            uint32_t off = (kb_ * 64 * CPB + segk[i] < kK) ? offB[i] + (uint32_t)kb_ * kBKBytes : kOOB;    \
             dma16_at((GLU && i >= LB / 2) ? rsB2 : rsB, off, wave_lds, st_ + (uint32_t)(BOFF + NWV * i * 1024)); \
         }                                                                                                  \
     } while (0)
@@ -413,6 +415,12 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
                       FP4_DMAK(st3, 3));
         }
 
+        // The epilogue's lane-dependent values are derived again here from a copy of the
+        // lane index the compiler cannot see through, so they are not computed before the
+        // main loop and held (in registers it needs) across it.
+        int lane_e = lane;
+        asm volatile("" : "+v"(lane_e));
+        const int r32 = lane_e & 31, hk = lane_e >> 5;
         // epilogue of tile ct: y = fl32(acc * fl32(a * s_n)); value v of lane l holds
         // row 32 i + l%32 and column 32 j + 8 (v/4) + 4 (l/32) + v%4 of this wavefront's
         // sub-tile.

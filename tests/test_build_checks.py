@@ -7,8 +7,9 @@ These tests read the assembly hipcc emits and check that:
     issued after the staging loads (it may merge adjacent loads);
   * every direct-to-LDS buffer load is directly preceded by the M0 write of its own asm
     block, and nothing else reads or writes M0;
-  * every barrier wait of the persistent W4A4 / W8A8 pipeline, s_waitcnt vmcnt(N) + s_barrier,
-    still covers the step it waits for on every path through the kernel (below);
+  * every barrier wait of the persistent W4A4 / W8A8 pipeline (both its schedules),
+    s_waitcnt vmcnt(N) + s_barrier, still covers the step it waits for on every path
+    through the kernel (below);
   * no kernel spills to scratch memory (the hand-counted waits assume that no spill
     load or store is issued in between; spills would also cost bandwidth).
 """
@@ -58,20 +59,17 @@ def instructions(body):
 
 
 # ------------------------------------------------------------------ waits ---------
-# The W4A4 pipeline's phase q waits until step q + 1 has landed in LDS and meets the
-# workgroup barrier (s_waitcnt vmcnt(N) lgkmcnt(0); s_barrier).  Step q + 1 was loaded
-# by the direct-to-LDS loads issued right after the barrier of phase q - 3, three
-# barrier intervals back.  A thread's vector-memory operations complete in issue order,
-# so the wait is sufficient exactly when at least N operations were issued after the
-# last of those loads.  The check runs a forward data-flow pass over the kernel's
-# control-flow graph that keeps, per path, the operations issued
-#   cur        in the current barrier interval,
-#   cur_after  in the current interval after its last direct-to-LDS load,
-#   p1         in the previous interval,
-#   p1_after   in the previous interval after its last direct-to-LDS load,
-#   p2_after   in the interval before that after its last direct-to-LDS load,
-# takes the minimum over all paths and requires N <= p2_after + p1 + cur at every barrier
-# wait.  A full wait (vmcnt(0)) retires everything issued before it (SAFE).
+# Both schedules of the W4A4 kernel wait at a workgroup barrier (s_waitcnt vmcnt(N) ...;
+# s_barrier) for the step whose direct-to-LDS loads were issued two load groups earlier:
+# after those loads the wavefront has issued the loads of the next two steps (and, at a
+# tile's start, the previous tile's output stores).  A load group is the direct-to-LDS
+# loads between two consecutive barriers.  A thread's vector-memory operations complete
+# in issue order, so the wait is sufficient exactly when at least N operations were issued
+# after the last load of the third most recent group.  The check runs a forward data-flow
+# pass over the kernel's control-flow graph that keeps, per path, the operations issued
+# after each of the three most recent load groups, takes the minimum over all paths, and
+# requires N <= that count for the third group at every barrier wait.  A full wait
+# (vmcnt(0)) retires everything issued before it (SAFE).
 # Paths the hardware cannot take are left out:
 #   * exec-mask skips (s_cbranch_execz / execnz) are followed as by a wavefront with
 #     active lanes: the tile loop runs with every lane active;
@@ -119,22 +117,27 @@ def _sat(x):
 
 
 def _step(c, k, st, flags):
-    """State after instruction c[k], and the (N, bound) of a barrier wait there."""
+    """State after instruction c[k], and the (N, bound) of a barrier wait there.
+    st = (a0, a1, a2, fresh): operations issued after the last load of the most recent,
+    second and third most recent load group; fresh: a barrier came after the last load
+    (the next load starts a new group)."""
     t = c[k]
-    cur, cur_after, p1, p1_after, p2_after = st
+    a0, a1, a2, fresh = st
     chk = None
-    if VMEM.match(t):
-        cur, cur_after = _sat(cur + 1), _sat(cur_after + 1)
-        if LDS_LOAD.match(t):
-            cur_after = 0
+    if LDS_LOAD.match(t):
+        a0, a1, a2 = (0, _sat(a0 + 1), _sat(a1 + 1)) if fresh else (0, _sat(a1 + 1), _sat(a2 + 1))
+        fresh = False
+    elif VMEM.match(t):
+        a0, a1, a2 = _sat(a0 + 1), _sat(a1 + 1), _sat(a2 + 1)
     m = re.match(r"^s_waitcnt vmcnt\((\d+)\)", t)
     if m:
         n = int(m.group(1))
         if n == 0:
-            cur = cur_after = p1 = p1_after = p2_after = SAFE
+            a0 = a1 = a2 = SAFE
         elif k + 1 < len(c) and c[k + 1] == "s_barrier":
-            chk = (n, _sat(p2_after + p1 + cur))
-            cur, cur_after, p1, p1_after, p2_after = 0, 0, cur, cur_after, p1_after
+            chk = (n, a2)
+    if t == "s_barrier":
+        fresh = True
     parts = t.split(None, 1)
     mn, ops = parts[0], ([o.strip() for o in parts[1].split(",")] if len(parts) > 1 else [])
     d = dict(flags)
@@ -149,7 +152,7 @@ def _step(c, k, st, flags):
             del d[key]
         if mn == "s_mov_b64" and len(ops) == 2 and ops[1] in ("-1", "0") and ops[0].startswith("s["):
             d[ops[0]] = int(ops[1])
-    return (cur, cur_after, p1, p1_after, p2_after), frozenset(d.items()), chk
+    return (a0, a1, a2, fresh), frozenset(d.items()), chk
 
 
 def _successors(bl, idx, i, flags):
@@ -176,25 +179,26 @@ def _successors(bl, idx, i, flags):
 
 
 def barrier_waits(ins):
-    """{(block, index): (N, fewest operations issued after the awaited loads)}."""
+    """{(block, index): (N, fewest operations issued after the awaited load group)}."""
     bl, idx = _blocks(ins)
     state = [dict() for _ in bl]
-    state[0][frozenset()] = (0, 0, 0, 0, 0)
+    state[0][(frozenset(), True)] = (SAFE, SAFE, SAFE)
     work, res = [0], {}
     while work:
         i = work.pop()
-        for flags, st in list(state[i].items()):
-            c, fl = bl[i][1], flags
+        for (flags, fresh), cnt in list(state[i].items()):
+            c, fl, st = bl[i][1], flags, cnt + (fresh,)
             for k in range(len(c)):
                 st, fl, chk = _step(c, k, st, fl)
                 if chk:
                     old = res.get((i, k))
                     res[(i, k)] = (chk[0], chk[1] if old is None else min(old[1], chk[1]))
+            key, cnt2 = (fl, st[3]), st[:3]
             for j in _successors(bl, idx, i, fl):
-                cur = state[j].get(fl)
-                new = st if cur is None else tuple(min(x, y) for x, y in zip(cur, st))
+                cur = state[j].get(key)
+                new = cnt2 if cur is None else tuple(min(x, y) for x, y in zip(cur, cnt2))
                 if new != cur:
-                    state[j][fl] = new
+                    state[j][key] = new
                     if j not in work:
                         work.append(j)
     return res
