@@ -174,22 +174,52 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     uint32_t offA[LA], offB[LB], offS, offK, offR;
     // Tile order.  Workgroups are dispatched to the 8 XCDs in turn (workgroup b on XCD
     // b % 8), each XCD with its own L2.  When the grid is a multiple of 8, XCD x takes the
-    // tiles [ntiles x / 8, ntiles (x + 1) / 8) of the column-major tile order (tile t:
-    // row block t % grid_m, column block t / grid_m), shared by its workgroups in turn:
-    // an XCD then reads about an eighth of the column blocks of W, each once, and all of
-    // A.  Otherwise workgroup b takes tiles b, b + grid, ...
+    // column blocks [grid_n x / 8, grid_n (x + 1) / 8) and its workgroups share that
+    // block's tiles in turn, ordered in panels of P row blocks: panel by panel, and within
+    // a panel column by column.  The tiles an XCD computes at the same time then form a
+    // compact block (4 row blocks x 8 column blocks for 32 workgroups), whose operand
+    // row and column blocks are fetched from HBM about once per round instead of all row
+    // blocks for every two columns.  Where whole columns per XCD would give some
+    // workgroup more tiles than an even split of the tiles does (few columns), XCD x takes
+    // the tiles [ntiles x / 8, ntiles (x + 1) / 8) of the column-major order instead.
+    // Otherwise (a grid that is not a multiple of 8) workgroup b takes tiles b, b + grid, ...
     constexpr int kXcds = 8;
+#ifndef FP4_PANEL
+#define FP4_PANEL 4
+#endif
     const bool xcd_order = gridDim.x % kXcds == 0;
     const int xcd = blockIdx.x % kXcds, xwg = blockIdx.x / kXcds, xwgs = gridDim.x / kXcds;
+    const int grid_n = ntiles / grid_m;
+    const int c_first = (int)((int64_t)grid_n * xcd / kXcds);
+    const int c_cnt = (int)((int64_t)grid_n * (xcd + 1) / kXcds) - c_first;
+    const int pan = grid_m < FP4_PANEL ? grid_m : FP4_PANEL;
+    const int full_rows = grid_m / pan * pan;  // rows in whole panels
+    // tiles per workgroup at most, whole columns per XCD against an even split
+    const int64_t by_cols = ((grid_n + kXcds - 1) / kXcds * (int64_t)grid_m + xwgs - 1) / xwgs;
+    const int64_t by_tiles = (((int64_t)ntiles + kXcds - 1) / kXcds + xwgs - 1) / xwgs;
+    const bool panels = by_cols <= by_tiles;
     const int x_first = (int)((int64_t)ntiles * xcd / kXcds);
-    const int x_count = (int)((int64_t)ntiles * (xcd + 1) / kXcds) - x_first;
+    const int x_count = panels ? grid_m * c_cnt : (int)((int64_t)ntiles * (xcd + 1) / kXcds) - x_first;
     auto tile_of = [&](int k) -> int {  // this workgroup's k-th tile, or ntiles once done
         if (!xcd_order) {
             const int64_t t = blockIdx.x + (int64_t)k * gridDim.x;
             return t < ntiles ? (int)t : ntiles;
         }
-        const int64_t u = xwg + (int64_t)k * xwgs;
-        return u < x_count ? x_first + (int)u : ntiles;
+        const int64_t u64 = xwg + (int64_t)k * xwgs;
+        if (u64 >= x_count) return ntiles;
+        const int u = (int)u64;
+        if (!panels) return x_first + u;
+        int row, col;
+        if (u < full_rows * c_cnt) {
+            const int pn = u / (pan * c_cnt), v = u - pn * pan * c_cnt;
+            col = v / pan;
+            row = pn * pan + (v - col * pan);
+        } else {  // the last panel, grid_m % pan rows
+            const int h = grid_m - full_rows, v = u - full_rows * c_cnt;
+            col = v / h;
+            row = full_rows + (v - col * h);
+        }
+        return (c_first + col) * grid_m + row;
     };
     int dk = 0, dt = tile_of(0), dpar = 0;
     auto load_tile = [&](int t) {
