@@ -79,6 +79,14 @@ __device__ __forceinline__ float agpr_read(float a) {
 #define FP4_BAR() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory")
 // Wait for this wavefront's LDS operations.
 #define FP4_LDS_WAIT() asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory")
+// Meet the workgroup barrier (separates two load groups; waits for nothing).
+#define FP4_BARRIER_ONLY() asm volatile("s_barrier" : : : "memory")
+// One buffer store at an offset past the end of `none` (a buffer of size zero): the
+// hardware discards it, and counts it among this thread's outstanding memory operations
+// until it completes, in issue order with the others.
+__device__ __forceinline__ void discarded_store(i32x4v none) {
+    asm volatile("buffer_store_dword %0, %1, %2, 0 offen" : : "v"(0), "v"(kOOB), "s"(none) : "memory");
+}
 
 // e^x as a fixed sequence of binary32 operations (bit-reproducible on any IEEE
 // binary32 implementation of the same sequence; built without contraction): t =
@@ -359,12 +367,27 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     constexpr int STORES = TM * ST_PER;
     static_assert(2 * PER_STEP + STORES <= 63, "wait count out of range");
     uint4 xa[TM], xb[TN], ya[TM], yb[TN];
+    // Prologue: the first four steps, one load group each (a barrier between groups, as
+    // between the phases below).  The first three waits of every tile count, after the
+    // awaited step's loads, the next two steps' loads and the previous tile's STORES output
+    // stores; before the first tile the same number of stores is issued here, through a
+    // buffer of size zero (the hardware discards every store out of a buffer's range, and
+    // counts it like any other).  Then wait as every phase does: for the third most recent
+    // group (step 1, and step 0 and the scales before it).
     FP4_DMAK(st0, 0);
     FP4_DMAS();
+    FP4_BARRIER_ONLY();
     FP4_DMAK(st1, 1);
+    FP4_BARRIER_ONLY();
     FP4_DMAK(st2, 2);
+    FP4_BARRIER_ONLY();
     FP4_DMAK(st3, 3);
-    FP4_SYNC_ALL();
+    {
+        const i32x4v none = buf_words(p.a, 0);
+#pragma unroll
+        for (int i = 0; i < STORES; i++) discarded_store(none);
+    }
+    FP4_SYNC(2 * PER_STEP + STORES);
     FP4_READH(st0, 0, xa, xb);
     if (F8 && BM * BN < 256 * 256) FP4_READH(st0, 1, ya, yb);
 
@@ -522,40 +545,57 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
                 // 16-byte pieces.  The stores are not waited for: the first three waits of the
                 // next tile count them.  Addresses: a per-lane 32-bit part plus a
                 // wavefront-uniform row offset.
+                // The scales are read from LDS once per tile (the rows' activation scales) and
+                // once per column half (the columns'), not once per 4-column group: each read
+                // is a round trip every wavefront of the CU waits for at the same time.  No
+                // wait separates the staging writes, the read-back and the next block's writes:
+                // a wavefront's LDS operations are performed in issue order, and the stores
+                // wait for the read-back data they take.
                 constexpr int CH2 = WN / 16;    // 16-byte chunks per staged row (WN/2 columns)
                 constexpr int RPQ = 64 / CH2;   // rows per read-back pass
                 const int xw = (r32 & (CH2 - 1)) << 4;
                 const int rl = lane / CH2, cl = lane % CH2;
                 const uint32_t goff = (uint32_t)(rl * p.ldy * 2 + cl * 16);
                 char* const ytile = reinterpret_cast<char*>(p.y) + ((m0 + wm * WM) * p.ldy + n0 + wn * WN) * 2;
+                const bool col_scales = p.w_mode == 1, row_scales = p.a_row != 0;
+                // this lane's rows' activation scales (one per token, or the tensor's)
+                float am[TM];
     #pragma unroll
                 for (int i = 0; i < TM; i++) {
-                    // this lane's row's activation scale (one per token, or the tensor's)
-                    const float am = p.a_row ? asc[wm * WM + i * 32 + r32] : a_scale;
+                    const float v = asc[wm * WM + i * 32 + r32];
+                    am[i] = row_scales ? v : a_scale;
+                }
     #pragma unroll
-                    for (int jh = 0; jh < 2; jh++) {
+                for (int jh = 0; jh < 2; jh++) {
+                    float4 s4[TN / 2][4];  // this lane's columns' weight scales in this half
+    #pragma unroll
+                    for (int jj = 0; jj < TN / 2; jj++)
+    #pragma unroll
+                        for (int g = 0; g < 4; g++) {
+                            const float4 v = *reinterpret_cast<const float4*>(&sc[wn * WN + (jh * (TN / 2) + jj) * 32 + 8 * g + 4 * hk]);
+                            s4[jj][g] = col_scales ? v : make_float4(s_tensor, s_tensor, s_tensor, s_tensor);
+                        }
+    #pragma unroll
+                    for (int i = 0; i < TM; i++) {
     #pragma unroll
                         for (int jj = 0; jj < TN / 2; jj++)
     #pragma unroll
                             for (int g = 0; g < 4; g++) {
                                 const int j = jh * (TN / 2) + jj;
-                                float4 s4 = make_float4(s_tensor, s_tensor, s_tensor, s_tensor);
-                                if (p.w_mode == 1) s4 = *reinterpret_cast<const float4*>(&sc[wn * WN + j * 32 + 8 * g + 4 * hk]);
-                                const float f[4] = {am * s4.x, am * s4.y, am * s4.z, am * s4.w};
+                                const float4 s = s4[jj][g];
+                                const float f[4] = {am[i] * s.x, am[i] * s.y, am[i] * s.z, am[i] * s.w};
                                 __bf16 h4[4];
     #pragma unroll
                                 for (int t = 0; t < 4; t++) h4[t] = (__bf16)(agpr_read(acc[j][i][4 * g + t]) * f[t]);
                                 *reinterpret_cast<uint2*>(stg + r32 * (WN) + (((jj * 4 + g) << 4) ^ xw) + hk * 8) =
                                     __builtin_bit_cast(uint2, h4);
                             }
-                        FP4_LDS_WAIT();
     #pragma unroll
                         for (int q = 0; q < 32 * CH2 / 64; q++) {
                             const int row = q * RPQ + rl;
                             const uint4 v = *reinterpret_cast<const uint4*>(stg + row * WN + ((cl ^ (row & (CH2 - 1))) << 4));
                             *reinterpret_cast<uint4*>(ytile + (int64_t)(i * 32 + q * RPQ) * p.ldy * 2 + jh * WN + goff) = v;
                         }
-                        FP4_LDS_WAIT();
                     }
                 }
             } else {
