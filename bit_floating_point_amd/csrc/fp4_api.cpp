@@ -451,10 +451,20 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
         if (d->K % 32 != 0) return fail(FP4_ERR_UNSUPPORTED, "K must be a multiple of 32");
         if (d->lda < d->K * qa.bits / 8 || d->ldw < d->K * p.wg.bits / 8 || d->lda % 16 != 0)
             return fail(FP4_ERR_ALIGNMENT, "FP8 / FP6 rows: lda, ldw >= the code bytes of a row, lda a multiple of 16");
-        if (d->w_gran.mode == FP4_SCALE_GROUP || d->w_gran.scale_dtype != FP4_F32)
-            return fail(FP4_ERR_UNSUPPORTED, "FP8 / FP6 products need f32 TENSOR or ROW weight scales");
+        // weight scales: f32 per tensor or per output row, or f32 / f16 per row and group of
+        // G codes along K (G a multiple of 64 dividing K: the tiled kernel, E4M3 x E4M3 too)
+        const bool grp = d->w_gran.mode == FP4_SCALE_GROUP;
+        if (grp) {
+            if (d->w_gran.group % 64 != 0 || d->K % d->w_gran.group != 0)
+                return fail(FP4_ERR_UNSUPPORTED,
+                            "group-scaled FP8 / FP6 weights need a group that is a multiple of 64 and divides K");
+            if (256 * (d->K / d->w_gran.group) * 4 >= 0x7fff0000)
+                return fail(FP4_ERR_UNSUPPORTED, "too many weight groups per row");
+        } else if (d->w_gran.scale_dtype != FP4_F32) {
+            return fail(FP4_ERR_UNSUPPORTED, "FP8 / FP6 products need f32 TENSOR or ROW weight scales, or GROUP scales");
+        }
         p.ag = qa;
-        if (p.wg.bits == 8 && p.wg.e == 4 && qa.bits == 8 && qa.e == 4)
+        if (!grp && p.wg.bits == 8 && p.wg.e == 4 && qa.bits == 8 && qa.e == 4)
             return hip_status(launch_w8a8_fp8(p, s), "fp4_gemm/w8a8");
         if (256 * std::max(d->lda, d->ldw) >= 0x7fff0000)
             return fail(FP4_ERR_UNSUPPORTED, "FP8 / FP6 rows longer than 8 MiB are not supported");

@@ -21,9 +21,17 @@
 // step.  The waits are the compiler's own.  Units past K are zeros, so the padding of a
 // row adds nothing.
 //
+// Group-scaled FP8 / FP6 weights (GRP: one scale per output row and group of G codes of
+// K, G a multiple of 64 dividing K, [W8A8] section 2.2's group size 128 among them):
+//   Y[m, n] = fl32(T[m, n] * a_m),  T = sum over groups g of s[n, g] * P_g[m, n]
+// where P_g is the group's fp32 MFMA sum, folded into T with one fused multiply-add per
+// group (T = fma(P_g, s[n, g], T), group order) after the MFMA K-block that ends the
+// group.  The scales of a step's two K-blocks (256 columns each) ride in LDS with the
+// step's operand units.
+//
 // The E4M3 x E4M3 and E2M1 x E2M1 pairs have their own persistent kernel
 // (gemm_w4a4.hip); this kernel takes every other pair with an FP8 or FP6 operand, W6A6
-// among them.
+// among them, and every group-scaled FP8 / FP6 weight (E4M3 x E4M3 included).
 #include "fp4_device.h"
 #include "fp4_internal.h"
 
@@ -139,13 +147,17 @@ __device__ __forceinline__ uint4 staged(uint4 u) {
 
 }  // namespace
 
-template <int FW, int FA>
+template <int FW, int FA, bool GRP>
 __global__ void __launch_bounds__(256) f8f6_gemm_kernel(GemmParams p, int grid_m, int ntiles) {
     using WA = Fmt<FA>;
     using WW = Fmt<FW>;
     constexpr int LA = kBM * 8 / 256, LW = kBN * 8 / 256;  // units per thread and step
     constexpr int SA = kBM * WA::stride, SW = kBN * WW::stride;               // LDS bytes per buffer
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (SA + SW)];
+    constexpr int SG = GRP ? 2 * kBN * 4 : 0;  // GRP: the 256 columns' f32 scales of the step's two K-blocks
+    constexpr int BUF = SA + SW + SG;
+    // register sets of units (GRP: one, the running sums take the registers of the second)
+    constexpr int NSET = GRP ? 1 : kSets;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
 
     // workgroups go round-robin over the eight XCDs; give each XCD a contiguous run of
     // tiles so the ones sharing operand rows meet in the same L2
@@ -165,11 +177,32 @@ __global__ void __launch_bounds__(256) f8f6_gemm_kernel(GemmParams p, int grid_m
     const __amdgpu_buffer_rsrc_t rW = buf_make(p.w + n0 * p.ldw, rows_w * p.ldw);
     const int64_t bytes_a = p.K * WA::lbits / 8, bytes_w = p.K * WW::lbits / 8;  // code bytes per row
     const int nsteps = (int)((p.K + kStepCodes - 1) / kStepCodes);
+    // GRP: this thread's column tid of the tile; its scale of group g at (tid * ngroups + g)
+    // of a buffer over the tile's rows of scales (out of range past N: zeros)
+    const int ngroups = GRP ? (int)(p.K / p.w_group) : 1;
+    const int esz = p.w_scale_f16 ? 2 : 4;
+    const __amdgpu_buffer_rsrc_t rS =
+        buf_make(reinterpret_cast<const uint8_t*>(p.w_scales) + (GRP ? n0 * ngroups * esz : 0),
+                 GRP ? rows_w * ngroups * esz : 0);
 
-    // kSets register sets of units: set t % kSets holds step t; the loads of step
-    // t + kSets are issued while step t is computed and stored into LDS at the end of
-    // step t + kSets - 1
-    uint4 ra[kSets][LA], rw[kSets][LW];
+    // NSET register sets of units: set t % NSET holds step t; the loads of step
+    // t + NSET are issued while step t is computed and stored into LDS at the end of
+    // step t + NSET - 1
+    uint4 ra[NSET][LA], rw[NSET][LW];
+    float rs[NSET][2];  // GRP: this thread's column's scales for the two K-blocks of a step
+    auto sload = [&](float (&v)[2], int s) {
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int g = (int)(((int64_t)s * kStepCodes + 64 * h) / p.w_group);  // K-blocks past K: g >= ngroups
+            const uint32_t off = g < ngroups ? (uint32_t)((tid * ngroups + g) * esz) : kOOB;
+            if (p.w_scale_f16) {
+                const short b = __builtin_amdgcn_raw_buffer_load_b16(rS, off, 0, 0);
+                v[h] = (float)__builtin_bit_cast(_Float16, b);
+            } else {
+                v[h] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, off, 0, 0));
+            }
+        }
+    };
     auto gload = [&](uint4 (&a)[LA], uint4 (&w)[LW], int s) {
 #pragma unroll
         for (int i = 0; i < LA; i++) {
@@ -183,6 +216,11 @@ __global__ void __launch_bounds__(256) f8f6_gemm_kernel(GemmParams p, int grid_m
             const int64_t kb = (int64_t)s * WW::step_bytes + WW::unit_bytes * j;
             w[i] = unit_load<FW>(rW, row * p.ldw + kb, bytes_w - kb);
         }
+    };
+    auto sstore = [&](uint8_t* buf, const float (&v)[2]) {
+        float* sg = reinterpret_cast<float*>(buf + SA + SW);
+        sg[tid] = v[0];
+        sg[kBN + tid] = v[1];
     };
     auto lstore = [&](uint8_t* buf, const uint4 (&a)[LA], const uint4 (&w)[LW]) {
 #pragma unroll
@@ -198,14 +236,43 @@ __global__ void __launch_bounds__(256) f8f6_gemm_kernel(GemmParams p, int grid_m
     };
 
     f32x16 acc[4][2];
+    f32x16 tot[GRP ? 4 : 1][2];  // GRP: the sum over finished groups
 #pragma unroll
     for (int j = 0; j < 4; j++)
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[j][i][v] = 0.0f;
+    if constexpr (GRP) {
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) tot[j][i][v] = 0.0f;
+    }
+    // GRP: K-block h of step t ends a group: T = fma(P, s[n, g], T) for every value, then
+    // P = 0.  Value v of block (j, i) is column wn*128 + 32 j + 8 (v/4) + 4 hk + v%4 of the
+    // tile.  (K-blocks past K end "groups" whose scale is 0 and whose P is 0: T stays.)
+    auto fold = [&](const uint8_t* cur, int h) {
+        const float* sg = reinterpret_cast<const float*>(cur + SA + SW) + h * kBN;
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const float4 s4 = *reinterpret_cast<const float4*>(&sg[wn * 128 + 32 * j + 8 * g + 4 * hk]);
+                const float sc[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+                for (int i = 0; i < 2; i++)
+#pragma unroll
+                    for (int c = 0; c < 4; c++) {
+                        tot[j][i][4 * g + c] = __builtin_fmaf(acc[j][i][4 * g + c], sc[c], tot[j][i][4 * g + c]);
+                        acc[j][i][4 * g + c] = 0.0f;
+                    }
+            }
+    };
 
-    auto compute = [&](const uint8_t* cur) {
+    auto compute = [&](const uint8_t* cur, int t) {
 #pragma unroll
         for (int h = 0; h < 2; h++) {
             i32x8 fa[2], fw[4];
@@ -219,27 +286,36 @@ __global__ void __launch_bounds__(256) f8f6_gemm_kernel(GemmParams p, int grid_m
                 for (int i = 0; i < 2; i++)
                     acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[j], fa[i], acc[j][i], WW::code,
                                                                                WA::code, 0, 127, 0, 127);
+            if constexpr (GRP) {
+                if (((int64_t)t * kStepCodes + 64 * (h + 1)) % p.w_group == 0) fold(cur, h);
+            }
         }
         // keep the MFMAs ahead of the waits for the next units
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // steps rounded up to a multiple of kSets; the loads of steps past K read zeros and
+    // steps rounded up to a multiple of NSET; the loads of steps past K read zeros and
     // the extra steps add nothing.  Loop body without branches: every load and store is
     // unconditional.  Step t is computed from LDS buffer t % 2.
 #pragma unroll
-    for (int u = 0; u < kSets; u++) gload(ra[u], rw[u], u);
+    for (int u = 0; u < NSET; u++) {
+        gload(ra[u], rw[u], u);
+        if constexpr (GRP) sload(rs[u], u);
+    }
     lstore(smem, ra[0], rw[0]);
+    if constexpr (GRP) sstore(smem, rs[0]);
     __syncthreads();
-    for (int s = 0; s < nsteps; s += kSets) {
+    for (int s = 0; s < nsteps; s += NSET) {
 #pragma unroll
-        for (int u = 0; u < kSets; u++) {
+        for (int u = 0; u < NSET; u++) {
             const int t = s + u;
-            uint8_t* const cur = smem + (t & 1) * (SA + SW);
-            uint8_t* const nxt = smem + ((t + 1) & 1) * (SA + SW);
-            gload(ra[u], rw[u], t + kSets);
-            compute(cur);
-            lstore(nxt, ra[(u + 1) % kSets], rw[(u + 1) % kSets]);
+            uint8_t* const cur = smem + (t & 1) * BUF;
+            uint8_t* const nxt = smem + ((t + 1) & 1) * BUF;
+            gload(ra[u], rw[u], t + NSET);
+            if constexpr (GRP) sload(rs[u], t + NSET);
+            compute(cur, t);
+            lstore(nxt, ra[(u + 1) % NSET], rw[(u + 1) % NSET]);
+            if constexpr (GRP) sstore(nxt, rs[(u + 1) % NSET]);
             __syncthreads();
         }
     }
@@ -256,16 +332,18 @@ __global__ void __launch_bounds__(256) f8f6_gemm_kernel(GemmParams p, int grid_m
             const int64_t n = n0 + wn * 128 + 32 * j + 8 * g + 4 * hk;
             float sn[4];
 #pragma unroll
-            for (int c = 0; c < 4; c++) sn[c] = p.w_mode == 1 ? ws[n + c < p.N ? n + c : p.N - 1] : ws[0];
+            for (int c = 0; c < 4; c++) sn[c] = GRP ? 1.0f : (p.w_mode == 1 ? ws[n + c < p.N ? n + c : p.N - 1] : ws[0]);
 #pragma unroll
             for (int i = 0; i < 2; i++) {
                 const int64_t m = m0 + wm * 64 + 32 * i + r32;
                 if (m >= p.M) continue;
                 // one activation scale, or one per row (token) of A: y = fl32(acc * fl32(a_m * s_n))
                 const float am = p.a_row ? p.a_scale[m] : a_scale;
+                // GRP: y = fl32(T * a_m)
                 float y[4];
 #pragma unroll
-                for (int c = 0; c < 4; c++) y[c] = acc[j][i][4 * g + c] * (am * sn[c]);
+                for (int c = 0; c < 4; c++)
+                    y[c] = GRP ? tot[GRP ? j : 0][i][4 * g + c] * am : acc[j][i][4 * g + c] * (am * sn[c]);
                 const bool vec = vec_ok && n + 3 < p.N;
                 if (p.y_bf16) {
                     __bf16* yp = reinterpret_cast<__bf16*>(p.y) + m * p.ldy + n;
@@ -296,7 +374,15 @@ namespace {
 template <int FW, int FA>
 hipError_t launch_pair(const GemmParams& p, hipStream_t s) {
     const int64_t gm = (p.M + kBM - 1) / kBM, gn = (p.N + kBN - 1) / kBN;
-    hipLaunchKernelGGL((f8f6_gemm_kernel<FW, FA>), dim3((unsigned)(gm * gn)), dim3(256), 0, s, p, (int)gm,
+    if constexpr (FW <= 3) {  // FP8 / FP6 weights: group scales
+        if (p.w_mode == 2) {
+            hipLaunchKernelGGL((f8f6_gemm_kernel<FW, FA, true>), dim3((unsigned)(gm * gn)), dim3(256), 0, s, p,
+                               (int)gm, (int)(gm * gn));
+            return hipGetLastError();
+        }
+    }
+    if (p.w_mode == 2) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((f8f6_gemm_kernel<FW, FA, false>), dim3((unsigned)(gm * gn)), dim3(256), 0, s, p, (int)gm,
                        (int)(gm * gn));
     return hipGetLastError();
 }
@@ -333,6 +419,10 @@ hipError_t launch_f8f6_gemm(const GemmParams& p, hipStream_t s) {
     // per-tile buffer ranges are 32-bit: a tile's rows must span less than 2 GiB
     if ((int64_t)kBN * std::max(p.lda, p.ldw) >= 0x7fff0000) return hipErrorInvalidValue;
     if ((p.M + kBM - 1) / kBM * ((p.N + kBN - 1) / kBN) >= (int64_t)1 << 31) return hipErrorInvalidValue;
+    // group scales: G a multiple of 64 dividing K; a tile's scales within the 32-bit range
+    if (p.w_mode == 2 && (p.w_group < 64 || p.w_group % 64 != 0 || p.K % p.w_group != 0 ||
+                          (int64_t)kBN * (p.K / p.w_group) * 4 >= 0x7fff0000))
+        return hipErrorInvalidValue;
     switch (fw) {
         case 0: return launch_w<0>(p, fa, s);
         case 1: return launch_w<1>(p, fa, s);

@@ -338,6 +338,12 @@ fp4_status fp4_search_activations(const void* x, int32_t x_dtype, int64_t rows, 
  *   tolerance); lda, ldw >= the code bytes of a row (K or 3K/4), lda a multiple of 16,
  *   K a multiple of 32, rows shorter than 8 MiB.  The same holds when one operand is a
  *   4-bit minifloat grid (E2M1, E1M2, E3M0) and the other FP8 / FP6 (rows of K/2 bytes).
+ *   FP8 / FP6 weights with PACKED activations also take GROUP weight scales (f32 or
+ *   f16, group G a multiple of 64 dividing K; [W8A8] section 2.2's group of 128):
+ *   y = fl32(T * a) (per token: a_m), T = sum over the groups g in K order of
+ *   T = fma(P_g, s[n, g], T), P_g the group's fp32 sum; within the GEMM tolerance.  A
+ *   group that is not a multiple of 64 (one matrix instruction spans 64 codes of K)
+ *   returns FP4_ERR_UNSUPPORTED.
  *   Two-mode weights (FP4_GRID_TWO_MODE, GROUP scales) take the W4A16 path only: each
  *   group's codes are read on its own grid (the sign of its scale) and scaled by |s|.
  * Strides: K a multiple of 32 for the matrix-core paths; packed rows 16-byte aligned. */

@@ -311,7 +311,10 @@ def test_fp8_validation():
     d.K, d.lda = 256, 176
     assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_ALIGNMENT  # lda below a row's code bytes
     d.lda, d.w_gran = 192, _gran(2, 32)
-    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # GROUP weight scales
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_UNSUPPORTED  # GROUP of 32: below one instruction's 64 codes
+    d.K, d.lda, d.ldw, d.w_gran = 320, 240, 240, _gran(2, 128)
+    assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_INVALID_ARG  # a group of 128 does not divide K = 320
+    d.K, d.lda, d.ldw = 256, 192, 192
     d.w_gran, d.a_scale = _gran(1), 0
     assert lib.fp4_gemm(ctypes.byref(d), N) == L.FP4_ERR_INVALID_ARG  # no activation scale
     d.a_scale, d.a_grid = 0x50000, _grid(0, 3, 4)

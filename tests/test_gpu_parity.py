@@ -968,6 +968,48 @@ def test_f8f6_per_token_scales(af, wf):
     _check_gemm(y32, r, S, depth_packed(K), None, packed_window_term(af, wf, S))
 
 
+def depth_packed_group(K, G):
+    """Group-scaled FP8 / FP6 weights with packed activations: each group's partial sum
+    as in depth_packed, one fused multiply-add per group folding it into the running sum,
+    and the final scaling by the activation scale."""
+    return 2 * K + K // G + 4
+
+
+@pytest.mark.parametrize("M,N,K,wf,af,G,sdt,per_token", [
+    (300, 520, 640, (4, 3), (4, 3), 128, "f16", False),    # E4M3 x E4M3, [W8A8] group 128
+    (300, 520, 640, (2, 3), (2, 3), 64, "f32", False),     # W6A6, two groups per 128-code step
+    (130, 270, 1024, (5, 2), (4, 3), 256, "f16", False),   # a group spans two steps
+    (257, 300, 512, (3, 2), (2, 1), 512, "f32", False),    # one group per row; E2M1 activations
+    (300, 520, 640, (4, 3), (2, 3), 128, "f16", True),     # per-token activation scales
+    (2100, 2200, 1024, (2, 3), (2, 3), 128, "f16", False), # several tile rows and columns
+])
+def test_f8f6_group_scaled_weights(M, N, K, wf, af, G, sdt, per_token):
+    """FP8 / FP6 weights with one scale per row and group of G codes along K ([W8A8]
+    section 2.2), quantized on the GPU (codes and scales bit-exact against the oracle), and
+    their product with packed activations: within the GEMM tolerance of the binary64
+    oracle's a * sum_g s[n, g] * sum_{k in g} A_q W_q, elementwise; bf16 the nearest-even
+    rounding of the fp32 output."""
+    say("f8f6 group", M, N, K, wf, af, G, sdt, per_token)
+    x = synth.activations(21, M, M, K, outlier_frac=0.01)
+    w = synth.weight(21, N, N, K)
+    og_a, og_w = _wide(af), _wide(wf)
+    amode = "row" if per_token else "tensor"
+    ap, asc = O.quantize_pack(x, og_a, amode)
+    wp, wsc = O.quantize_pack(w, og_w, "group", G, sdt)
+    fa, fw = F.grid_minifloat(*af), F.grid_minifloat(*wf)
+    wg = F.gran("group", G, sdt)
+    gwp, gws = F.fp4_quantize_pack(dev(w), fw, wg)
+    assert np.array_equal(host(gwp), wp)
+    assert np.array_equal(host(gws.float()), np.asarray(wsc, np.float32).reshape(-1))
+    gap = _padded_rows(ap)
+    ga = dev(np.asarray(asc, np.float32).reshape(-1))
+    r, _ = O.gemm_w4a4(ap, og_a, asc, wp, og_w, "group", wsc, group=G)
+    S, _ = O.gemm_w4a4(ap, og_a, asc, wp, og_w, "group", wsc, group=G, absolute=True)
+    y32 = host(F.fp4_gemm(gap, gwp, gws, fw, wg, K=K, a_grid=fa, a_scale=ga, y_dtype=torch.float32))
+    yb = F.fp4_gemm(gap, gwp, gws, fw, wg, K=K, a_grid=fa, a_scale=ga, y_dtype=torch.bfloat16)
+    _check_gemm(y32, r, S, depth_packed_group(K, G), yb, packed_window_term(af, wf, S))
+
+
 def _padded_rows(packed, align=16):
     """uint8 rows copied into a device buffer whose row stride is a multiple of `align`
     bytes (the packed products need 16-byte aligned rows), returned as the [:, :bytes] view."""
