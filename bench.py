@@ -575,6 +575,20 @@ def bench_w8a8(torch, F):
                                   fl, "flop"))
         del X, W, ap, wp, y
         torch.cuda.empty_cache()
+    # group-scaled FP8 weights (one f16 scale per row and 128 codes of K) on the tiled kernel
+    M, N, K = 4096, 15360, 5120
+    X = gen_activations(torch, M, K, 500)
+    W = gen_normal(torch, (N, K), 0.02, 600)
+    g128 = F.gran("group", 128, "f16")
+    ap, asc = F.fp4_quantize_pack(X, f8, F.gran("tensor"))
+    wp, ws = F.fp4_quantize_pack(W, f8, g128)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    t = graph_time(torch, lambda i: F.fp4_gemm(ap, wp, ws, f8, g128, K=K, a_grid=f8, a_scale=asc, y=y), 5)
+    fl = 2 * M * N * K
+    out.append(roofline_entry("w8a8 FP8 E4M3 GEMM qkv 4096x15360x5120, group-128 weight scales", "mfma", fl / t / 1e12,
+                              FP8_PEAK_TFLOPS, "TFLOP/s", t, fl, "flop"))
+    del X, W, ap, wp, y
+    torch.cuda.empty_cache()
     # W6A6 (FP6 E2M3 x E2M3, whose matrix-core rate is the FP4 one) and W8A8 with E5M2
     # operands, on the tiled FP8/FP6 kernel; FP6 rows padded to 16-byte multiples
     for (wf, peak, shapes) in (((2, 3), FP4_PEAK_TFLOPS, ((2048, 4096, 4096, "2048x4096x4096"),
