@@ -72,6 +72,15 @@ __device__ __forceinline__ uint4 decode_lut_f16x8(uint32_t w, const uint32_t TL[
     return o;
 }
 
+// Slot of fragment position s (0..63) in a 1 KiB block of expanded f16 operands: s for
+// s < 32, s ^ 12 above.  A thread expands the two halves of one row into positions j and
+// j + 32 and neighbouring lanes take neighbouring rows, so the lanes of a 128-bit LDS
+// write meet positions j and j + 32 together: unswizzled they lie 512 bytes apart, on the
+// same banks.  With the XOR, the slots of any 8 or 16 neighbouring lanes differ modulo 8
+// or 16 (the groups in which 128-bit accesses are served), for these writes and for the
+// fragment reads (lane l at position l) alike.
+__device__ __forceinline__ int frag_slot(int s) { return s ^ (((s >> 5) & 1) * 12); }
+
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, f16x2 s) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) * s);
@@ -184,8 +193,8 @@ __global__ void __launch_bounds__(256) w4a4_lut_kernel(GemmParams p, int grid_m)
     // LDS per stage: the activation codes packed, 32 B per row (row-major, the two 16-byte
     // halves of a row swapped when bit 3 of the row is set, so a wavefront's 16-byte reads
     // of 32 rows hit distinct banks); the weights expanded to f16 in MFMA fragment order:
-    // per K16 block kk and 32-row tile t a 1 KiB block whose 16-byte slot l holds row
-    // 32 t + l%32, K values 32 (l/32) + 8 kk .. +7 of the step.  The MFMAs take K in
+    // per K16 block kk and 32-row tile t a 1 KiB block whose 16-byte slot frag_slot(l)
+    // holds row 32 t + l%32, K values 32 (l/32) + 8 kk .. +7 of the step.  The MFMAs take K in
     // that order (block kk, lane half h: codes 32 h + 8 kk .. +7) on both operands.
     // Decode + store chunk c (8 codes) of every weight piece of this thread into stage
     // st; with chunk 0 the activation pieces are stored as they are.
@@ -205,7 +214,7 @@ __global__ void __launch_bounds__(256) w4a4_lut_kernel(GemmParams p, int grid_m)
             for (int i = 0; i < PA; i++) {
                 const uint32_t w[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
                 const int h = kA[i] / 32, r = rowA[i];
-                *reinterpret_cast<uint4*>(sa + ((c * (BM / 32) + (r >> 5)) * 64 + (r & 31) + 32 * h) * 16) =
+                *reinterpret_cast<uint4*>(sa + ((c * (BM / 32) + (r >> 5)) * 64 + frag_slot((r & 31) + 32 * h)) * 16) =
                     decode_e2m1_f16x8(w[c]);
             }
         }
@@ -219,7 +228,7 @@ __global__ void __launch_bounds__(256) w4a4_lut_kernel(GemmParams p, int grid_m)
             uint4 v = decode_lut_f16x8(w[c], TL, TH);
             v.x = mul_f16x2(v.x, s2); v.y = mul_f16x2(v.y, s2);
             v.z = mul_f16x2(v.z, s2); v.w = mul_f16x2(v.w, s2);
-            *reinterpret_cast<uint4*>(sw + ((c * (BN / 32) + (r >> 5)) * 64 + (r & 31) + 32 * hh) * 16) = v;
+            *reinterpret_cast<uint4*>(sw + ((c * (BN / 32) + (r >> 5)) * 64 + frag_slot((r & 31) + 32 * hh)) * 16) = v;
         }
     };
     auto dstore = [&](int st) {
@@ -260,12 +269,12 @@ __global__ void __launch_bounds__(256) w4a4_lut_kernel(GemmParams p, int grid_m)
                     af[i] = __builtin_bit_cast(f16x8, decode_e2m1_f16x8(w4[kk]));
                 } else {
                     af[i] = __builtin_bit_cast(
-                        f16x8, *reinterpret_cast<const uint4*>(sa + ((kk * (BM / 32) + wm * TM + i) * 64 + lane) * 16));
+                        f16x8, *reinterpret_cast<const uint4*>(sa + ((kk * (BM / 32) + wm * TM + i) * 64 + frag_slot(lane)) * 16));
                 }
             }
 #pragma unroll
             for (int j = 0; j < TN; j++) {
-                const f16x8 bf = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(sw + ((kk * (BN / 32) + wn * TN + j) * 64 + lane) * 16));
+                const f16x8 bf = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(sw + ((kk * (BN / 32) + wn * TN + j) * 64 + frag_slot(lane)) * 16));
 #pragma unroll
                 for (int i = 0; i < TM; i++) acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf, af[i], acc[j][i], 0, 0, 0);
             }
