@@ -9,8 +9,9 @@
 // accumulation: the result is bit-reproducible.
 //
 // Tiling for CDNA4: a workgroup computes BM x BN tiles of Y (256x256 for whole rounds
-// of tiles, 256x128 or 128x128 for the column block of a partial last round or for
-// small grids) with 2x4 wavefronts (256x256: two per SIMD) or 2x2; each wavefront a
+// of tiles, 256x128 or 128x128 for the column block of a partial last round, 128x256 or
+// 128x128 for small grids) with 2x4 wavefronts (256x256, 128x256: two per SIMD) or 2x2;
+// each wavefront a
 // (BM/2) x (BN/4 or BN/2) sub-tile as a grid of 32x32 accumulators.  K advances 128 codes (64 bytes per row) per step
 // through a four-stage LDS ring fed by direct-to-LDS loads.  One workgroup per compute
 // unit loops over tiles (each XCD over its own range of them, so that an XCD reads
@@ -693,12 +694,14 @@ static int cu_count() {
     return counts[dev];
 }
 
-// 256 x 256 tiles run 8 wavefronts (2 per SIMD), smaller tiles 4.  (FP8 256 x 256 tiles:
-// 4 to 10% faster with 8 than with 4 on the LLaMA-13B QKV shape, bit-identical.)
+// 256 x 256 and 128 x 256 tiles run 8 wavefronts (2 per SIMD), smaller tiles 4.  (FP8
+// 256 x 256 tiles: 4 to 10% faster with 8 than with 4 on the LLaMA-13B QKV shape; E2M1
+// 128 x 256 tiles at 2048 x 4096 x 4096: 5% faster with 8 than two rounds of 128 x 128,
+// 6% slower with 4.  Bit-identical.)
 template <int BM, int BN, int F8 = 0>
 static void launch_cfg(const GemmParams& p, hipStream_t s, int64_t cus) {
     const int64_t gm = (p.M + BM - 1) / BM, gn = (p.N + BN - 1) / BN, nt = gm * gn;
-    constexpr int NWV = (BM == 256 && BN == 256) ? kBigTileWaves : 4;
+    constexpr int NWV = BN == 256 ? kBigTileWaves : 4;
     hipLaunchKernelGGL((w4a4_fp4_kernel<BM, BN, false, F8, NWV>), dim3((unsigned)std::min(nt, cus)), dim3(64 * NWV), 0,
                        s, p, (int)gm, (int)nt, GluParams{});
 }
@@ -716,14 +719,17 @@ static GemmParams column_block(const GemmParams& p, int64_t n0, int64_t n1) {
 // 256x128 0.59, 128x128 0.35.  With at least one full round of 256x256 tiles, the
 // whole rounds stay 256x256 and the column block left over for a partial last round
 // takes the shape that finishes it soonest (a partial round of big tiles leaves
-// compute units idle).  Fewer tiles than compute units: 128x128.
+// compute units idle).  Fewer 256x256 tiles than compute units: 128x256 (E2M1) when they
+// give every compute unit a tile, else 128x128.
 template <int F8 = 0>
 static hipError_t launch_block(const GemmParams& p, hipStream_t s) {
     const int64_t cus = cu_count();
     const int64_t gm256 = (p.M + 255) / 256, gn256 = (p.N + 255) / 256, t256 = gm256 * gn256;
     if (t256 < cus) {
-        // (one round of 256 x 128 tiles measured the same as two of 128 x 128 at 2048 x 4096)
-        launch_cfg<128, 128, F8>(p, s, cus);
+        // (one round of 256 x 128 tiles on 4 wavefronts measured the same as two of 128 x 128
+        // at 2048 x 4096)
+        if (!F8 && ((p.M + 127) / 128) * gn256 >= cus) launch_cfg<128, 256, F8>(p, s, cus);
+        else launch_cfg<128, 128, F8>(p, s, cus);
         return hipGetLastError();
     }
     const int64_t full_cols = (t256 / cus) * cus / gm256;  // 256-column blocks of whole rounds

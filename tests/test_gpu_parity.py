@@ -438,6 +438,8 @@ def test_preshift_w4a4_full_2048x4096x4096():
     (1500, 3000, 384, "row", 3),     # output rows not 16-byte aligned: element stores
     (4096, 5200, 256, "row", 0),     # one round of 256x256 tiles, the rest as 256x128
     (4096, 5120, 512, "tensor", 0),  # one round of 256x256 tiles, the rest as 128x128
+    (2048, 4096, 256, "row", 0),     # one round of 128x256 tiles on 8 wavefronts
+    (2000, 4000, 288, "row", 0),     # 128x256 tiles, ragged M, N and K tail
 ])
 def test_w4a4_e2m1_many_tiles(M, N, K, mode, ldy_pad):
     """W4A4 E2M1 GEMM on random codes where each workgroup computes several tiles in
@@ -543,7 +545,7 @@ def test_swiglu_quant_full_4096x13824x5120():
     assert np.array_equal(got[rows], codes)
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 520, 544), (2100, 2200, 1024), (4096, 5120, 512)])
+@pytest.mark.parametrize("M,N,K", [(300, 520, 544), (2100, 2200, 1024), (4096, 5120, 512), (2048, 4096, 256)])
 def test_w4a4_per_token_scales(M, N, K):
     """Dynamic per-token activation quantization (E2M1, one scale per token) into the
     W4A4 product with per-token scales: fp32 and bf16 outputs bit-exact."""
