@@ -21,7 +21,9 @@
 //
 // The same kernel also runs the LLaMA MLP's gate/up pair with SwiGLU and the next
 // layer's E2M1 quantization in the epilogue (GLU), and the FP8 E4M3 x E4M3 product
-// (F8: one code per byte, 64-code steps; fp32 sums not exact, so held to a tolerance).
+// (F8: one code per byte, 64-code steps; fp32 sums not exact, so held to a tolerance),
+// with tensor or row weight scales or, on 128x256 tiles, one scale per row and group of
+// 128 codes ([W8A8] section 2.2's group size; F8 = 2 / 3 for f32 / f16 scales).
 #include <algorithm>
 #include <atomic>
 
@@ -125,6 +127,13 @@ __device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + exp_f32(
 template <int BM, int BN, bool GLU, int F8 = 0, int NWV = 4>
 __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int grid_m, int ntiles, GluParams gp) {
     constexpr int CPB = F8 ? 1 : 2;  // codes per byte
+    // F8 = 2 / 3: E4M3 weights with one f32 / f16 scale per output row and group of 128
+    // codes along K: each group's MFMA sum P_g (two 64-code K-blocks) is folded into a
+    // running sum T = fma(P_g, s[n, g], T) once the group's last MFMA has issued, and the
+    // epilogue gives y = fl32(T * a_m)
+    constexpr bool GRP = F8 >= 2;
+    constexpr bool GF16 = F8 == 3;
+    static_assert(!GRP || (BM == 128 && BN == 256 && NWV == 8 && !GLU), "group-scaled FP8: 128x256 tiles");
     constexpr int WM = BM / 2, WN = BN / (NWV / 2);
     constexpr int TM = WM / 32, TN = WN / 32;
     constexpr int LA = BM * 4 / (64 * NWV), LB = BN * 4 / (64 * NWV);  // 16-byte pieces per thread per step
@@ -136,7 +145,11 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     constexpr int SCL_BYTES = GLU ? 3072 : 2048;
     constexpr int STG_BYTES = GLU ? 2048 : 32 * WN;
     constexpr int ON = GLU ? BN / 2 : BN;  // output columns per tile
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * STAGE + 2 * SCL_BYTES + NWV * STG_BYTES];
+    // GRP: two blocks of the tile's group scales (256 columns x 16 bytes: the 16 bytes of a
+    // column's scale row from the first group of a four-step group on), and 1 KiB that the
+    // scale loads of the wavefronts without a column share write and no one reads
+    constexpr int GS_BYTES = GRP ? 9 * 1024 : 0;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * STAGE + 2 * SCL_BYTES + NWV * STG_BYTES + GS_BYTES];
     constexpr int BOFF = BM * kBKBytes;  // a stage: its A block, then its B block
     uint8_t* const st0 = smem;
     uint8_t* const st1 = smem + STAGE;
@@ -145,6 +158,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     uint8_t* const scl = smem + 4 * STAGE;
     uint8_t* const stg_base = smem + 4 * STAGE + 2 * SCL_BYTES;
     uint8_t* const stg = stg_base + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * STG_BYTES;
+    uint8_t* const gsb = smem + 4 * STAGE + 2 * SCL_BYTES + NWV * STG_BYTES;  // GRP scale blocks
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -180,7 +194,11 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
         int sidx = (NWV * i + wave) * 64 + lane, row = sidx >> 2;
         segk[i] = ((sidx & 3) ^ ((row >> 2) & 3)) * 16 * CPB;  // codes (the segment stored in slot sidx % 4)
     }
-    uint32_t offA[LA], offB[LB], offS, offK, offR;
+    uint32_t offA[LA], offB[LB], offS, offK, offR, offG = kOOB;
+    // GRP: scale bytes per element and per output row (K / 128 groups)
+    constexpr int gsz = GF16 ? 2 : 4;
+    const int64_t grow = GRP ? p.K / 128 * gsz : 0;
+    const i32x4v rsG = buf_words(p.w_scales, GRP ? p.N * grow : 0);
     // Tile order.  Workgroups are dispatched to the 8 XCDs in turn (workgroup b on XCD
     // b % 8), each XCD with its own L2.  When the grid is a multiple of 8, XCD x takes the
     // column blocks [grid_n x / 8, grid_n (x + 1) / 8) and its workgroups share that
@@ -248,6 +266,10 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
         offS = (ok && p.w_mode == 1 && n0 + 4 * lane < p.N && 4 * lane < ON) ? (uint32_t)((n0 + 4 * lane) * 4) : kOOB;
         offK = (ok && 16 * lane < ON && n0 + 16 * lane < p.N) ? (uint32_t)(n0 + 16 * lane) : kOOB;
         offR = (ok && p.a_row && 4 * lane < BM && m0 + 4 * lane < p.M) ? (uint32_t)((m0 + 4 * lane) * 4) : kOOB;
+        if constexpr (GRP) {  // wavefronts 0..3: column 64 wave + lane of the tile
+            const int64_t n = n0 + 64 * wave + lane;
+            offG = (ok && wave < 4 && n < p.N) ? (uint32_t)(n * grow) : kOOB;
+        }
     };
     load_tile(dt);
     // this wavefront's LDS slot base: load piece i of a stage goes to stage + (NWV i + wave) KiB
@@ -281,6 +303,19 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
             dma16(rsK, offK, sb_ + 2048);                                                                  \
         } else {                                                                                           \
             dma16(rsR, offR, sb_ + 1024);                                                                  \
+        }                                                                                                  \
+    } while (0)
+// GRP: the group scales of the four-step group that starts at step KB (a multiple of 4)
+// of the load stream's tile into scale block BLK: 16 bytes of each column's scale row
+// from group KB / 2 on (f32: groups KB/2 .. +3, f16: .. +7; the fold uses the first
+// two).  Every thread issues one load (wavefronts 4..7 an out-of-range one into the
+// unread KiB), so that all threads issue the same number of memory operations.
+#define FP4_DMAG(KB, BLK)                                                                                  \
+    do {                                                                                                   \
+        if constexpr (GRP) {                                                                               \
+            const uint32_t go_ = offG == kOOB ? kOOB : offG + (uint32_t)((KB) / 2 * gsz);                  \
+            const uint32_t gb_ = (uint32_t)(uintptr_t)gsb + (wave < 4 ? (BLK) * 4096 + wave * 1024 : 8192); \
+            dma16(rsG, go_, __builtin_amdgcn_readfirstlane(gb_));                                          \
         }                                                                                                  \
     } while (0)
 // the load stream moves on to this workgroup's next tile
@@ -360,6 +395,8 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
         }                                                                                                  \
     } while (0)
     f32x16 acc[TN][TM];
+    f32x16 tot[GRP ? TN : 1][GRP ? TM : 1];  // GRP: the sum over the tile's finished groups
+    int gcnt = 0;  // GRP: four-step groups computed so far (their scale block is gcnt % 2)
     constexpr int PER_STEP = LA + LB;  // operand loads per step and thread (+2 or +3 with the scales)
     // 16-byte output stores per thread of a staged epilogue (32 rows x WN bf16 columns
     // per wavefront and row block)
@@ -375,6 +412,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     // buffer of size zero (the hardware discards every store out of a buffer's range, and
     // counts it like any other).  Then wait as every phase does: for the third most recent
     // group (step 1, and step 0 and the scales before it).
+    FP4_DMAG(0, 0);
     FP4_DMAK(st0, 0);
     FP4_DMAS();
     FP4_BARRIER_ONLY();
@@ -389,8 +427,8 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
         for (int i = 0; i < STORES; i++) discarded_store(none);
     }
     FP4_SYNC(2 * PER_STEP + STORES);
-    FP4_READH(st0, 0, xa, xb);
-    if (F8 && BM * BN < 256 * 256) FP4_READH(st0, 1, ya, yb);
+    if (!GRP) FP4_READH(st0, 0, xa, xb);
+    if (F8 && BM * BN < 256 * 256 && !GRP) FP4_READH(st0, 1, ya, yb);
 
     // Compute stream: tile ct.  Global step s (counted across this workgroup's tiles;
     // every tile has a multiple of 4 steps) lives in stage s % 4.  Phase q: the first
@@ -408,9 +446,18 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
 // q's stage, then run q's MFMAs while reading step q+1 into the registers they free.)
 // 256x256 FP8 tiles have no registers to spare for that (spills would break the load
 // counting of the waits): there the second halves are read just before the MFMAs.
-#define FP4_PHASE(W, SQ, SN, D)                                                                            \
+#define FP4_PHASE(W, SQ, SN, D, PH)                                                                        \
     do {                                                                                                   \
-        if constexpr (F8 && BM * BN < 256 * 256) {                                                         \
+        if constexpr (GRP) {                                                                               \
+            /* the step's fragments read just before its MFMAs: nothing is held across */             \
+            /* the barrier (the running sums take the registers)                        */             \
+            FP4_READH(SQ, 0, xa, xb);                                                                      \
+            FP4_READH(SQ, 1, ya, yb);                                                                      \
+            FP4_MMA8_REGS();                                                                               \
+            if constexpr ((PH) & 1) FP4_FOLD((PH) >> 1);                                                   \
+            FP4_SYNC(W);                                                                                   \
+            D;                                                                                             \
+        } else if constexpr (F8 && BM * BN < 256 * 256) {                                                  \
             FP4_SYNC(W);                                                                                   \
             D;                                                                                             \
             FP4_MMA8(SN);                                                                                  \
@@ -440,10 +487,37 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     } while (0)
 #define FP4_GROUP(W0, W1, W2, D0, D1, D2, D3)                                                              \
     do {                                                                                                   \
-        FP4_PHASE(W0, st0, st1, D0);                                                                       \
-        FP4_PHASE(W1, st1, st2, D1);                                                                       \
-        FP4_PHASE(W2, st2, st3, D2);                                                                       \
-        FP4_PHASE(2 * PER_STEP, st3, st0, D3);                                                             \
+        FP4_PHASE(W0, st0, st1, D0, 0);                                                                    \
+        FP4_PHASE(W1, st1, st2, D1, 1);                                                                    \
+        FP4_PHASE(W2, st2, st3, D2, 2);                                                                    \
+        FP4_PHASE(2 * PER_STEP, st3, st0, D3, 3);                                                          \
+        if constexpr (GRP) gcnt++;                                                                         \
+    } while (0)
+// GRP: fold group 2 gcnt + GG of the tile (the MFMA sums of its two steps) into the running
+// sums: value v of block (j, i) is column wn * WN + 32 j + 8 (v/4) + 4 hk + v%4 of the
+// tile; its scale is element GG of that column's 16 bytes in scale block gcnt % 2.  The
+// accumulators start the next group at zero.  (Steps past K read zero operands: their
+// sums are zero and leave T unchanged.)
+#define FP4_FOLD(GG)                                                                                       \
+    do {                                                                                                   \
+        const uint8_t* gs_ = gsb + (gcnt & 1) * 4096 + (GG) * gsz;                                         \
+        _Pragma("unroll") for (int j = 0; j < TN; j++) {                                                   \
+            _Pragma("unroll") for (int g = 0; g < 4; g++) {                                                \
+                float sc_[4];                                                                              \
+                _Pragma("unroll") for (int c = 0; c < 4; c++) {                                            \
+                    const uint8_t* a_ = gs_ + (wn * WN + 32 * j + 8 * g + 4 * hk + c) * 16;                \
+                    if constexpr (GF16) sc_[c] = __half2float(*reinterpret_cast<const __half*>(a_));       \
+                    else sc_[c] = *reinterpret_cast<const float*>(a_);                                     \
+                }                                                                                          \
+                _Pragma("unroll") for (int i = 0; i < TM; i++)                                             \
+                    _Pragma("unroll") for (int c = 0; c < 4; c++) {                                        \
+                        tot[j][i][4 * g + c] = __builtin_fmaf(acc[j][i][4 * g + c], sc_[c], tot[j][i][4 * g + c]); \
+                        acc[j][i][4 * g + c] = 0.0f;                                                       \
+                    }                                                                                      \
+                /* four scales live at a time: the VGPRs are taken by the operand pipeline */             \
+                __builtin_amdgcn_sched_barrier(0);                                                         \
+            }                                                                                              \
+        }                                                                                                  \
     } while (0)
     constexpr int WR = 2 * PER_STEP + STORES, WN2 = 2 * PER_STEP;
     const int ngroups = nk4 / 4;
@@ -455,18 +529,27 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
             for (int i = 0; i < TM; i++)
 #pragma unroll
                 for (int v = 0; v < 16; v++) acc[j][i][v] = 0.0f;
+        if constexpr (GRP) {
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+#pragma unroll
+                for (int i = 0; i < TM; i++)
+#pragma unroll
+                    for (int v = 0; v < 16; v++) tot[j][i][v] = 0.0f;
+        }
         if (ngroups == 1) {
             FP4_NEXT_TILE();
-            FP4_GROUP(WR, WR, WR, { FP4_DMAK(st0, 0); FP4_DMAS(); }, FP4_DMAK(st1, 1), FP4_DMAK(st2, 2),
-                      FP4_DMAK(st3, 3));
+            FP4_GROUP(WR, WR, WR, { FP4_DMAG(0, (gcnt + 1) & 1); FP4_DMAK(st0, 0); FP4_DMAS(); }, FP4_DMAK(st1, 1),
+                      FP4_DMAK(st2, 2), FP4_DMAK(st3, 3));
         } else {
-            FP4_GROUP(WR, WR, WR, FP4_DMAK(st0, 4), FP4_DMAK(st1, 5), FP4_DMAK(st2, 6), FP4_DMAK(st3, 7));
+            FP4_GROUP(WR, WR, WR, { FP4_DMAG(4, (gcnt + 1) & 1); FP4_DMAK(st0, 4); }, FP4_DMAK(st1, 5),
+                      FP4_DMAK(st2, 6), FP4_DMAK(st3, 7));
             for (int g = 1; g < ngroups - 1; g++)
-                FP4_GROUP(WN2, WN2, WN2, FP4_DMAK(st0, 4 * g + 4), FP4_DMAK(st1, 4 * g + 5), FP4_DMAK(st2, 4 * g + 6),
-                          FP4_DMAK(st3, 4 * g + 7));
+                FP4_GROUP(WN2, WN2, WN2, { FP4_DMAG(4 * g + 4, (gcnt + 1) & 1); FP4_DMAK(st0, 4 * g + 4); },
+                          FP4_DMAK(st1, 4 * g + 5), FP4_DMAK(st2, 4 * g + 6), FP4_DMAK(st3, 4 * g + 7));
             FP4_NEXT_TILE();
-            FP4_GROUP(WN2, WN2, WN2, { FP4_DMAK(st0, 0); FP4_DMAS(); }, FP4_DMAK(st1, 1), FP4_DMAK(st2, 2),
-                      FP4_DMAK(st3, 3));
+            FP4_GROUP(WN2, WN2, WN2, { FP4_DMAG(0, (gcnt + 1) & 1); FP4_DMAK(st0, 0); FP4_DMAS(); }, FP4_DMAK(st1, 1),
+                      FP4_DMAK(st2, 2), FP4_DMAK(st3, 3));
         }
 
         // The epilogue's lane-dependent values are derived again here from a copy of the
@@ -587,7 +670,9 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
                                 const float f[4] = {am[i] * s.x, am[i] * s.y, am[i] * s.z, am[i] * s.w};
                                 __bf16 h4[4];
     #pragma unroll
-                                for (int t = 0; t < 4; t++) h4[t] = (__bf16)(agpr_read(acc[j][i][4 * g + t]) * f[t]);
+                                for (int t = 0; t < 4; t++)
+                                    h4[t] = GRP ? (__bf16)(tot[GRP ? j : 0][GRP ? i : 0][4 * g + t] * am[i])
+                                                : (__bf16)(agpr_read(acc[j][i][4 * g + t]) * f[t]);
                                 *reinterpret_cast<uint2*>(stg + r32 * (WN) + (((jj * 4 + g) << 4) ^ xw) + hk * 8) =
                                     __builtin_bit_cast(uint2, h4);
                             }
@@ -626,8 +711,14 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
                             const int64_t m = m0 + wm * WM + i * 32 + r32;
                             const float am = p.a_row ? asc[wm * WM + i * 32 + r32] : a_scale;  // 0 past M
                             const float f0 = am * s4.x, f1 = am * s4.y, f2 = am * s4.z, f3 = am * s4.w;
-                            const float y0 = agpr_read(acc[j][i][4 * g]) * f0, y1 = agpr_read(acc[j][i][4 * g + 1]) * f1;
-                            const float y2 = agpr_read(acc[j][i][4 * g + 2]) * f2, y3 = agpr_read(acc[j][i][4 * g + 3]) * f3;
+                            float y0, y1, y2, y3;
+                            if constexpr (GRP) {  // y = fl32(T * a_m)
+                                y0 = tot[j][i][4 * g] * am, y1 = tot[j][i][4 * g + 1] * am;
+                                y2 = tot[j][i][4 * g + 2] * am, y3 = tot[j][i][4 * g + 3] * am;
+                            } else {
+                                y0 = agpr_read(acc[j][i][4 * g]) * f0, y1 = agpr_read(acc[j][i][4 * g + 1]) * f1;
+                                y2 = agpr_read(acc[j][i][4 * g + 2]) * f2, y3 = agpr_read(acc[j][i][4 * g + 3]) * f3;
+                            }
                             if (p.y_bf16) {
                                 __bf16* yp = reinterpret_cast<__bf16*>(p.y) + m * p.ldy + n;
                                 __bf16 h4[4] = {(__bf16)y0, (__bf16)y1, (__bf16)y2, (__bf16)y3};
@@ -669,6 +760,8 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
 #undef FP4_MMA8
 #undef FP4_MMA8_REGS
 #undef FP4_PHASE
+#undef FP4_FOLD
+#undef FP4_DMAG
     // drain the (zero) loads still in flight before the workgroup exits
     FP4_SYNC_ALL();
 }
@@ -791,6 +884,27 @@ hipError_t launch_w4a4_fp4(const GemmParams& p, hipStream_t s) { return launch_s
 
 // FP8 E4M3 x E4M3 (W8A8): the same kernel, one code per byte
 hipError_t launch_w8a8_fp8(const GemmParams& p, hipStream_t s) { return launch_split<1>(p, s); }
+
+// FP8 E4M3 x E4M3 with f32 or f16 weight scales per row and group of 128 codes: the same
+// kernel on 128x256 tiles (8 wavefronts; the running sums take the registers that 256x256
+// tiles would need for accumulators), one launch.
+bool w8a8_group_fits(const GemmParams& p) {
+    const int64_t grow = p.K / 128 * (p.w_scale_f16 ? 2 : 4);  // scale bytes per output row
+    return p.w_mode == 2 && p.w_group == 128 && p.K % 128 == 0 && grow % 4 == 0 && p.M * p.lda < kMaxBufBytes &&
+           p.N * p.ldw < kMaxBufBytes && p.N * grow < kMaxBufBytes;
+}
+hipError_t launch_w8a8_fp8_group(const GemmParams& p, hipStream_t s) {
+    if (p.M == 0 || p.N == 0) return hipSuccess;
+    const int64_t cus = cu_count();
+    const int64_t gm = (p.M + 127) / 128, gn = (p.N + 255) / 256, nt = gm * gn;
+    if (p.w_scale_f16)
+        hipLaunchKernelGGL((w4a4_fp4_kernel<128, 256, false, 3, kBigTileWaves>), dim3((unsigned)std::min(nt, cus)),
+                           dim3(64 * kBigTileWaves), 0, s, p, (int)gm, (int)nt, GluParams{});
+    else
+        hipLaunchKernelGGL((w4a4_fp4_kernel<128, 256, false, 2, kBigTileWaves>), dim3((unsigned)std::min(nt, cus)),
+                           dim3(64 * kBigTileWaves), 0, s, p, (int)gm, (int)nt, GluParams{});
+    return hipGetLastError();
+}
 
 // SwiGLU + next-layer quantization: tiles of BM rows x BN/2 output columns (gate and up
 // rows of those columns), 256 x 128 when they give every compute unit a tile, else

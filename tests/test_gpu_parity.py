@@ -984,6 +984,10 @@ def depth_packed_group(K, G):
     (257, 300, 512, (3, 2), (2, 1), 512, "f32", False),    # one group per row; E2M1 activations
     (300, 520, 640, (4, 3), (2, 3), 128, "f16", True),     # per-token activation scales
     (2100, 2200, 1024, (2, 3), (2, 3), 128, "f16", False), # several tile rows and columns
+    # E4M3 x E4M3, group 128, whole 4-byte scale rows: the persistent kernel's 128x256 tiles
+    (300, 520, 1024, (4, 3), (4, 3), 128, "f16", False),   # ragged tiles
+    (300, 520, 1152, (4, 3), (4, 3), 128, "f32", False),   # K steps past the last group
+    (4100, 2200, 1280, (4, 3), (4, 3), 128, "f32", True),  # several tiles per workgroup, per-token
 ])
 def test_f8f6_group_scaled_weights(M, N, K, wf, af, G, sdt, per_token):
     """FP8 / FP6 weights with one scale per row and group of G codes along K ([W8A8]
