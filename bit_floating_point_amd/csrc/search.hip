@@ -40,14 +40,16 @@ constexpr int kSChunk = kSThreads * kSPerMax;  // 8192 values per pass, at most
 constexpr int kMaxCand = 512;   // formats x clips per call (LDS holds one double-double per wavefront each)
 
 // Workgroups per unit: up to 4 passes of 8192 values each (at most 64 workgroups); when
-// the units give fewer than 768 workgroups (3 per CU), more of them, down to 2048 values
-// (8 per lane) each.
+// the units give fewer than 768 workgroups (3 per CU), more of them, down to 3072 values
+// (12 per lane, the most for which a wavefront still evaluates four candidates at a
+// time) each.  (Down to 8 per lane, the search over one 128 x 5120 unit ran 5% slower:
+// each candidate's wavefront sum is amortised over fewer values.)
 static int64_t search_blocks(int64_t units, int64_t numel) {
     int64_t b = (numel + 4 * kSChunk - 1) / (4 * kSChunk);
     if (b < 1) b = 1;
     if (b > 64) b = 64;
     const int64_t want = (768 + units - 1) / std::max<int64_t>(units, 1);
-    const int64_t most = (numel + kSThreads * 8 - 1) / (kSThreads * 8);
+    const int64_t most = (numel + kSThreads * 12 - 1) / (kSThreads * 12);
     return std::max(b, std::min(want, most));
 }
 
@@ -280,7 +282,10 @@ __global__ void __launch_bounds__(1024) search_reduce_kernel(SearchCandidates sc
     const double n = (double)numel;
     // few partials: one thread per candidate adds them in order; many: one wavefront per
     // candidate, lane l adding partials l, l + 64, ..., then the wavefront's butterfly
-    // (either way a fixed order for a given nb)
+    // (either way a fixed order for a given nb).  A wavefront takes four candidates at a
+    // time, their loads and butterflies interleaved: one at a time, each candidate waited
+    // for its loads and its six dependent shuffle steps in turn (70 us for one unit of 300
+    // candidates x 320 partials).
     if (nb <= 16) {
         for (int c = threadIdx.x; c < ncand; c += blockDim.x) {
             DD s{0.0, 0.0};
@@ -291,24 +296,51 @@ __global__ void __launch_bounds__(1024) search_reduce_kernel(SearchCandidates sc
         }
     } else {
         const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-        for (int c = threadIdx.x >> 6; c < ncand; c += nw) {
-            DD s{0.0, 0.0};
-            for (int b = lane; b < nb; b += 64) s = dd_add(s, part[((int64_t)t * ncand + c) * nb + b]);
-            s = wave_dd_sum(s);
+        for (int c0 = threadIdx.x >> 6; c0 < ncand; c0 += 4 * nw) {
+            DD d[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) d[q] = DD{0.0, 0.0};
+            for (int b = lane; b < nb; b += 64) {
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int c = c0 + q * nw;  // uniform per wavefront
+                    if (c < ncand) d[q] = dd_add(d[q], part[((int64_t)t * ncand + c) * nb + b]);
+                }
+            }
+            wave_dd_sum4(d);
             if (lane != 0) continue;
-            const double q1 = s.hi / n;
-            const double rem = fma(-q1, n, s.hi);
-            mse[c] = q1 + (rem + s.lo) / n;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int c = c0 + q * nw;
+                if (c >= ncand) continue;
+                const double q1 = d[q].hi / n;
+                const double rem = fma(-q1, n, d[q].hi);
+                mse[c] = q1 + (rem + d[q].lo) / n;
+            }
         }
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int best = 0;
-        for (int c = 1; c < ncand; c++)
-            if (mse[c] < mse[best]) best = c;
-        double runner = __builtin_inf();
-        for (int c = 0; c < ncand; c++)
-            if (c != best && mse[c] < runner) runner = mse[c];
+    // argmin (the smallest MSE, exact ties to the earliest candidate) and the runner-up's
+    // MSE, over the candidates by the first wavefront: each lane scans every 64th, then a
+    // butterfly (a single thread scanning all of them in turn took ~30 us)
+    if (threadIdx.x >= 64) return;
+    const int l = threadIdx.x;
+    double bv = __builtin_inf();
+    int best = ncand;  // none yet
+    for (int c = l; c < ncand; c += 64)
+        if (best == ncand || mse[c] < bv) bv = mse[c], best = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(best, o, 64);
+        if (ov < bv || (ov == bv && oi < best)) bv = ov, best = oi;
+    }
+    double runner = __builtin_inf();
+    for (int c = l; c < ncand; c += 64)
+        if (c != best && mse[c] < runner) runner = mse[c];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) runner = fmin(runner, __shfl_xor(runner, o, 64));
+    if (l == 0) {
         int f = best / sc.nclips, j = best % sc.nclips;
         float amax = amax_t[t];
         double ratio = lo + (hi - lo) * (double)j / (double)(sc.nclips - 1);
