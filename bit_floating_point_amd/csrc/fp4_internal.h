@@ -87,6 +87,7 @@ hipError_t launch_w8a16_small(const GemmParams& p, hipStream_t s);     // FP8 we
 hipError_t launch_w4a4_fp4(const GemmParams& p, hipStream_t s);
 void set_split_limit(int64_t bytes);  // 0: the 32-bit buffer range
 hipError_t launch_w8a8_fp8(const GemmParams& p, hipStream_t s);  // FP8 E4M3 x E4M3
+hipError_t launch_w8a8_e5m2(const GemmParams& p, hipStream_t s); // FP8 E5M2 x E5M2
 bool w8a8_group_fits(const GemmParams& p);                          // E4M3 x E4M3, group-128 scales
 hipError_t launch_w8a8_fp8_group(const GemmParams& p, hipStream_t s);
 // every other pair of FP8 (E4M3, E5M2) / FP6 (E2M3, E3M2) operands, W6A6 among them

@@ -21,7 +21,8 @@
 //
 // The same kernel also runs the LLaMA MLP's gate/up pair with SwiGLU and the next
 // layer's E2M1 quantization in the epilogue (GLU), and the FP8 E4M3 x E4M3 product
-// (F8: one code per byte, 64-code steps; fp32 sums not exact, so held to a tolerance),
+// (F8: one code per byte, 64-code steps; fp32 sums not exact, so held to a tolerance;
+// E5M2 x E5M2 too),
 // with tensor or row weight scales or, on 128x256 tiles, one scale per row and group of
 // 128 codes ([W8A8] section 2.2's group size; F8 = 2 / 3 for f32 / f16 scales).
 #include <algorithm>
@@ -131,8 +132,11 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     // codes along K: each group's MFMA sum P_g (two 64-code K-blocks) is folded into a
     // running sum T = fma(P_g, s[n, g], T) once the group's last MFMA has issued, and the
     // epilogue gives y = fl32(T * a_m)
-    constexpr bool GRP = F8 >= 2;
+    constexpr bool GRP = F8 == 2 || F8 == 3;
     constexpr bool GF16 = F8 == 3;
+    // F8 = 4: OCP FP8 E5M2 x E5M2 (the MFMA's format code 1 on both operands), tensor or
+    // row weight scales; every other FP8 instance is E4M3 (code 0)
+    constexpr int FC = F8 == 4 ? 1 : 0;
     static_assert(!GRP || (BM == 128 && BN == 256 && NWV == 8 && !GLU), "group-scaled FP8: 128x256 tiles");
     constexpr int WM = BM / 2, WN = BN / (NWV / 2);
     constexpr int TM = WM / 32, TN = WN / 32;
@@ -371,7 +375,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
             _Pragma("unroll") for (int i = 0; i < TM; i++) {                                               \
                 const i32x8 af = i32x8{(int)xa[i].x, (int)xa[i].y, (int)xa[i].z, (int)xa[i].w,             \
                                        (int)ya[i].x, (int)ya[i].y, (int)ya[i].z, (int)ya[i].w};            \
-                acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[j][i], 0, 0, 0, 127, 0, 127); \
+                acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[j][i], FC, FC, 0, 127, 0, 127); \
             }                                                                                              \
             xb[j] = *reinterpret_cast<const uint4*>(&SN[BOFF + swz(brow(j) + r32, 2 * hk)]);               \
             yb[j] = *reinterpret_cast<const uint4*>(&SN[BOFF + swz(brow(j) + r32, 2 * hk + 1)]);           \
@@ -390,7 +394,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
             _Pragma("unroll") for (int i = 0; i < TM; i++) {                                               \
                 const i32x8 af = i32x8{(int)xa[i].x, (int)xa[i].y, (int)xa[i].z, (int)xa[i].w,             \
                                        (int)ya[i].x, (int)ya[i].y, (int)ya[i].z, (int)ya[i].w};            \
-                acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[j][i], 0, 0, 0, 127, 0, 127); \
+                acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[j][i], FC, FC, 0, 127, 0, 127); \
             }                                                                                              \
         }                                                                                                  \
     } while (0)
@@ -884,6 +888,9 @@ hipError_t launch_w4a4_fp4(const GemmParams& p, hipStream_t s) { return launch_s
 
 // FP8 E4M3 x E4M3 (W8A8): the same kernel, one code per byte
 hipError_t launch_w8a8_fp8(const GemmParams& p, hipStream_t s) { return launch_split<1>(p, s); }
+
+// FP8 E5M2 x E5M2: the same kernel with the MFMA's E5M2 format code
+hipError_t launch_w8a8_e5m2(const GemmParams& p, hipStream_t s) { return launch_split<4>(p, s); }
 
 // FP8 E4M3 x E4M3 with f32 or f16 weight scales per row and group of 128 codes: the same
 // kernel on 128x256 tiles (8 wavefronts; the running sums take the registers that 256x256
