@@ -22,7 +22,7 @@
 // The same kernel also runs the LLaMA MLP's gate/up pair with SwiGLU and the next
 // layer's E2M1 quantization in the epilogue (GLU), and the FP8 E4M3 x E4M3 product
 // (F8: one code per byte, 64-code steps; fp32 sums not exact, so held to a tolerance;
-// E5M2 x E5M2 too),
+// E5M2 x E5M2 too; and FP6 x FP6 of one format, 96-byte rows of 128-code steps),
 // with tensor or row weight scales or, on 128x256 tiles, one scale per row and group of
 // 128 codes ([W8A8] section 2.2's group size; F8 = 2 / 3 for f32 / f16 scales).
 #include <algorithm>
@@ -137,11 +137,22 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     // F8 = 4: OCP FP8 E5M2 x E5M2 (the MFMA's format code 1 on both operands), tensor or
     // row weight scales; every other FP8 instance is E4M3 (code 0)
     constexpr int FC = F8 == 4 ? 1 : 0;
+    // F8 = 8 / 9: FP6 E2M3 / E3M2 on both operands (128x128 tiles, 4 wavefronts).  A step
+    // is 128 codes, 96 bytes per row (six 16-byte segments); a lane's fragment of a 64-code
+    // K-block is the 24 bytes [48 H + 24 hk, +24) of its row, read as three 8-byte pieces.
+    // Both operands take the same order of K, so the product is the same as in the matrix
+    // cores' own FP6 order.  Segment g of stage row r sits in slot (g + 3 ((r >> 3) & 1)) % 6:
+    // rows r and r + 8 (the same banks at a 96-byte row stride) then differ by 12 banks.
+    constexpr bool F6 = F8 >= 8;
+    constexpr int FC6 = F8 == 9 ? 3 : 2;
+    constexpr int RB = F6 ? 96 : kBKBytes;  // bytes per row and step
+    constexpr int NSEG = RB / 16;
+    static_assert(!F6 || (BM == 128 && BN == 128 && NWV == 4 && !GLU), "FP6: 128x128 tiles");
     static_assert(!GRP || (BM == 128 && BN == 256 && NWV == 8 && !GLU), "group-scaled FP8: 128x256 tiles");
     constexpr int WM = BM / 2, WN = BN / (NWV / 2);
     constexpr int TM = WM / 32, TN = WN / 32;
-    constexpr int LA = BM * 4 / (64 * NWV), LB = BN * 4 / (64 * NWV);  // 16-byte pieces per thread per step
-    constexpr int STAGE = (BM + BN) * kBKBytes;
+    constexpr int LA = BM * NSEG / (64 * NWV), LB = BN * NSEG / (64 * NWV);  // 16-byte pieces per thread per step
+    constexpr int STAGE = (BM + BN) * RB;
     // four operand stages, per tile parity a block of per-column weight scales and the
     // tile's per-row (per-token) activation scales, 1 KiB each (GLU: gate scales, up
     // scales and the output shifts), and each wavefront's output staging area (32 rows x
@@ -154,7 +165,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     // scale loads of the wavefronts without a column share write and no one reads
     constexpr int GS_BYTES = GRP ? 9 * 1024 : 0;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * STAGE + 2 * SCL_BYTES + NWV * STG_BYTES + GS_BYTES];
-    constexpr int BOFF = BM * kBKBytes;  // a stage: its A block, then its B block
+    constexpr int BOFF = BM * RB;  // a stage: its A block, then its B block
     uint8_t* const st0 = smem;
     uint8_t* const st1 = smem + STAGE;
     uint8_t* const st2 = smem + 2 * STAGE;
@@ -169,7 +180,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
     const int wm = wave & 1, wn = wave >> 1;
     const int r32 = lane & 31, hk = lane >> 5;
-    const int nk = (int)((p.K + 64 * CPB - 1) / (64 * CPB));
+    const int nk = F6 ? (int)(p.K / 128) : (int)((p.K + 64 * CPB - 1) / (64 * CPB));
     const int kK = (int)p.K;  // 32-bit bound checks (rows are below 2^31 bytes; K far smaller)
     // The step count per tile is rounded up to a multiple of 4 (the stage rotation);
     // steps past the last real one load zeros (out-of-range offsets) and add nothing.
@@ -195,8 +206,13 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     int segk[LA > LB ? LA : LB];
 #pragma unroll
     for (int i = 0; i < (LA > LB ? LA : LB); i++) {
-        int sidx = (NWV * i + wave) * 64 + lane, row = sidx >> 2;
-        segk[i] = ((sidx & 3) ^ ((row >> 2) & 3)) * 16 * CPB;  // codes (the segment stored in slot sidx % 4)
+        if constexpr (F6) {  // bytes: the segment stored in slot sidx % 6 of row sidx / 6
+            const int sidx = (NWV * i + wave) * 64 + lane, row = sidx / 6;
+            segk[i] = ((sidx - 6 * row + 3 * ((row >> 3) & 1)) % 6) * 16;
+        } else {
+            int sidx = (NWV * i + wave) * 64 + lane, row = sidx >> 2;
+            segk[i] = ((sidx & 3) ^ ((row >> 2) & 3)) * 16 * CPB;  // codes (the segment stored in slot sidx % 4)
+        }
     }
     uint32_t offA[LA], offB[LB], offS, offK, offR, offG = kOOB;
     // GRP: scale bytes per element and per output row (K / 128 groups)
@@ -258,14 +274,14 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
         const int64_t m0 = (int64_t)(t % grid_m) * BM, n0 = (int64_t)(t / grid_m) * ON;
 #pragma unroll
         for (int i = 0; i < LA; i++) {
-            int row = ((NWV * i + wave) * 64 + lane) >> 2;
-            offA[i] = (ok && m0 + row < p.M) ? (uint32_t)((m0 + row) * p.lda + segk[i] / CPB) : kOOB;
+            int row = F6 ? ((NWV * i + wave) * 64 + lane) / 6 : ((NWV * i + wave) * 64 + lane) >> 2;
+            offA[i] = (ok && m0 + row < p.M) ? (uint32_t)((m0 + row) * p.lda + (F6 ? segk[i] : segk[i] / CPB)) : kOOB;
         }
 #pragma unroll
         for (int i = 0; i < LB; i++) {
-            int row = ((NWV * i + wave) * 64 + lane) >> 2;
+            int row = F6 ? ((NWV * i + wave) * 64 + lane) / 6 : ((NWV * i + wave) * 64 + lane) >> 2;
             if (GLU && i >= LB / 2) row -= BN / 2;  // up rows (their own buffer)
-            offB[i] = (ok && n0 + row < p.N) ? (uint32_t)((n0 + row) * p.ldw + segk[i] / CPB) : kOOB;
+            offB[i] = (ok && n0 + row < p.N) ? (uint32_t)((n0 + row) * p.ldw + (F6 ? segk[i] : segk[i] / CPB)) : kOOB;
         }
         offS = (ok && p.w_mode == 1 && n0 + 4 * lane < p.N && 4 * lane < ON) ? (uint32_t)((n0 + 4 * lane) * 4) : kOOB;
         offK = (ok && 16 * lane < ON && n0 + 16 * lane < p.N) ? (uint32_t)(n0 + 16 * lane) : kOOB;
@@ -285,11 +301,11 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
         const int kb_ = (KB);                                                                              \
         const uint32_t st_ = (uint32_t)((STG) - smem);                                                     \
         _Pragma("unroll") for (int i = 0; i < LA; i++) {                                                   \
-            uint32_t off = (kb_ * 64 * CPB + segk[i] < kK) ? offA[i] + (uint32_t)kb_ * kBKBytes : kOOB;    \
+            uint32_t off = (F6 ? kb_ < nk : kb_ * 64 * CPB + segk[i] < kK) ? offA[i] + (uint32_t)kb_ * RB : kOOB; \
             dma16_at(rsA, off, wave_lds, st_ + (uint32_t)(NWV * i * 1024));                                \
         }                                                                                                  \
         _Pragma("unroll") for (int i = 0; i < LB; i++) {                                                   \
-            uint32_t off = (kb_ * 64 * CPB + segk[i] < kK) ? offB[i] + (uint32_t)kb_ * kBKBytes : kOOB;    \
+            uint32_t off = (F6 ? kb_ < nk : kb_ * 64 * CPB + segk[i] < kK) ? offB[i] + (uint32_t)kb_ * RB : kOOB; \
             dma16_at((GLU && i >= LB / 2) ? rsB2 : rsB, off, wave_lds, st_ + (uint32_t)(BOFF + NWV * i * 1024)); \
         }                                                                                                  \
     } while (0)
@@ -385,6 +401,44 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
             ya[i] = *reinterpret_cast<const uint4*>(&SN[swz(wm * WM + i * 32 + r32, 2 * hk + 1)]);         \
         }                                                                                                  \
     } while (0)
+// FP6: LDS byte of the 8-byte piece at byte B (a multiple of 8) of stage row R
+    auto f6_at = [&](int R, int B) { return R * 96 + (((B >> 4) + 3 * ((R >> 3) & 1)) % 6) * 16 + (B & 8); };
+// FP6: both K-blocks of a step, three 8-byte pieces per fragment
+#define FP6_READ(STG)                                                                                      \
+    do {                                                                                                   \
+        _Pragma("unroll") for (int i = 0; i < TM; i++)                                                     \
+            _Pragma("unroll") for (int h = 0; h < 2; h++)                                                  \
+                _Pragma("unroll") for (int m = 0; m < 3; m++) fa6[i][h][m] =                               \
+                    *reinterpret_cast<const uint2*>(&STG[f6_at(wm * WM + i * 32 + r32, 48 * h + 24 * hk + 8 * m)]); \
+        _Pragma("unroll") for (int j = 0; j < TN; j++)                                                     \
+            _Pragma("unroll") for (int h = 0; h < 2; h++)                                                  \
+                _Pragma("unroll") for (int m = 0; m < 3; m++) fb6[j][h][m] =                               \
+                    *reinterpret_cast<const uint2*>(&STG[BOFF + f6_at(brow(j) + r32, 48 * h + 24 * hk + 8 * m)]); \
+    } while (0)
+// FP6: the step's MFMAs from registers, refilling each fragment with step SN's as soon as
+// its last MFMA has issued (the W fragments of column block j after that block's MFMAs,
+// the A fragments at the end)
+#define FP6_MMA(SN)                                                                                        \
+    do {                                                                                                   \
+        _Pragma("unroll") for (int j = 0; j < TN; j++) {                                                   \
+            _Pragma("unroll") for (int h = 0; h < 2; h++) {                                                \
+                const i32x8 bf = i32x8{(int)fb6[j][h][0].x, (int)fb6[j][h][0].y, (int)fb6[j][h][1].x,      \
+                                       (int)fb6[j][h][1].y, (int)fb6[j][h][2].x, (int)fb6[j][h][2].y, 0, 0}; \
+                _Pragma("unroll") for (int i = 0; i < TM; i++) {                                           \
+                    const i32x8 af = i32x8{(int)fa6[i][h][0].x, (int)fa6[i][h][0].y, (int)fa6[i][h][1].x,  \
+                                           (int)fa6[i][h][1].y, (int)fa6[i][h][2].x, (int)fa6[i][h][2].y, 0, 0}; \
+                    acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[j][i], FC6, FC6, 0, 127, 0, 127); \
+                }                                                                                          \
+            }                                                                                              \
+            _Pragma("unroll") for (int h = 0; h < 2; h++)                                                  \
+                _Pragma("unroll") for (int m = 0; m < 3; m++) fb6[j][h][m] =                               \
+                    *reinterpret_cast<const uint2*>(&SN[BOFF + f6_at(brow(j) + r32, 48 * h + 24 * hk + 8 * m)]); \
+        }                                                                                                  \
+        _Pragma("unroll") for (int i = 0; i < TM; i++)                                                     \
+            _Pragma("unroll") for (int h = 0; h < 2; h++)                                                  \
+                _Pragma("unroll") for (int m = 0; m < 3; m++) fa6[i][h][m] =                               \
+                    *reinterpret_cast<const uint2*>(&SN[f6_at(wm * WM + i * 32 + r32, 48 * h + 24 * hk + 8 * m)]); \
+    } while (0)
 // FP8: the MFMAs of the step in registers, without reads
 #define FP4_MMA8_REGS()                                                                                    \
     do {                                                                                                   \
@@ -399,6 +453,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
         }                                                                                                  \
     } while (0)
     f32x16 acc[TN][TM];
+    uint2 fa6[F6 ? TM : 1][2][3], fb6[F6 ? TN : 1][2][3];  // FP6 fragments of a step
     f32x16 tot[GRP ? TN : 1][GRP ? TM : 1];  // GRP: the sum over the tile's finished groups
     int gcnt = 0;  // GRP: four-step groups computed so far (their scale block is gcnt % 2)
     constexpr int PER_STEP = LA + LB;  // operand loads per step and thread (+2 or +3 with the scales)
@@ -431,8 +486,9 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
         for (int i = 0; i < STORES; i++) discarded_store(none);
     }
     FP4_SYNC(2 * PER_STEP + STORES);
-    if (!GRP) FP4_READH(st0, 0, xa, xb);
-    if (F8 && BM * BN < 256 * 256 && !GRP) FP4_READH(st0, 1, ya, yb);
+    if (!GRP && !F6) FP4_READH(st0, 0, xa, xb);
+    if (F8 && BM * BN < 256 * 256 && !GRP && !F6) FP4_READH(st0, 1, ya, yb);
+    if constexpr (F6) FP6_READ(st0);
 
     // Compute stream: tile ct.  Global step s (counted across this workgroup's tiles;
     // every tile has a multiple of 4 steps) lives in stage s % 4.  Phase q: the first
@@ -452,7 +508,11 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
 // counting of the waits): there the second halves are read just before the MFMAs.
 #define FP4_PHASE(W, SQ, SN, D, PH)                                                                        \
     do {                                                                                                   \
-        if constexpr (GRP) {                                                                               \
+        if constexpr (F6) {                                                                                \
+            FP4_SYNC(W);                                                                                   \
+            D;                                                                                             \
+            FP6_MMA(SN);                                                                                   \
+        } else if constexpr (GRP) {                                                                        \
             /* the step's fragments read just before its MFMAs: nothing is held across */             \
             /* the barrier (the running sums take the registers)                        */             \
             FP4_READH(SQ, 0, xa, xb);                                                                      \
@@ -764,6 +824,8 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
 #undef FP4_MMA8
 #undef FP4_MMA8_REGS
 #undef FP4_PHASE
+#undef FP6_READ
+#undef FP6_MMA
 #undef FP4_FOLD
 #undef FP4_DMAG
     // drain the (zero) loads still in flight before the workgroup exits
@@ -891,6 +953,23 @@ hipError_t launch_w8a8_fp8(const GemmParams& p, hipStream_t s) { return launch_s
 
 // FP8 E5M2 x E5M2: the same kernel with the MFMA's E5M2 format code
 hipError_t launch_w8a8_e5m2(const GemmParams& p, hipStream_t s) { return launch_split<4>(p, s); }
+
+// FP6 x FP6 of one format (W6A6), tensor or row weight scales: 128x128 tiles on 4
+// wavefronts (a 96-byte step row; larger tiles leave no room in LDS for four stages), one
+// launch.
+bool w6a6_fits(const GemmParams& p) {
+    return p.w_mode != 2 && p.K % 128 == 0 && p.lda % 4 == 0 && p.ldw % 4 == 0 && p.M * p.lda < kMaxBufBytes &&
+           p.N * p.ldw < kMaxBufBytes;
+}
+hipError_t launch_w6a6_fp6(const GemmParams& p, hipStream_t s) {
+    if (p.M == 0 || p.N == 0) return hipSuccess;
+    const int64_t cus = cu_count();
+    const int64_t gm = (p.M + 127) / 128, gn = (p.N + 127) / 128, nt = gm * gn;
+    const dim3 grid((unsigned)std::min(nt, cus));
+    if (p.wg.e == 3) hipLaunchKernelGGL((w4a4_fp4_kernel<128, 128, false, 9, 4>), grid, dim3(256), 0, s, p, (int)gm, (int)nt, GluParams{});
+    else hipLaunchKernelGGL((w4a4_fp4_kernel<128, 128, false, 8, 4>), grid, dim3(256), 0, s, p, (int)gm, (int)nt, GluParams{});
+    return hipGetLastError();
+}
 
 // FP8 E4M3 x E4M3 with f32 or f16 weight scales per row and group of 128 codes: the same
 // kernel on 128x256 tiles (8 wavefronts; the running sums take the registers that 256x256

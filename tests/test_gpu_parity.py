@@ -1029,6 +1029,7 @@ def _padded_rows(packed, align=16):
 @pytest.mark.parametrize("M,N,K,wf,af,mode", [
     (300, 520, 544, (2, 3), (2, 3), "row"),     # W6A6 E2M3: ragged tiles, a half-filled last FP6 piece
     (2100, 2200, 1024, (3, 2), (3, 2), "row"),  # W6A6 E3M2, several tile rows and columns
+    (300, 520, 640, (2, 3), (2, 3), "row"),     # W6A6 on the persistent kernel: ragged 128x128 tiles
     (4096, 5120, 4096, (2, 3), (2, 3), "tensor"),
     (256, 384, 512, (5, 2), (5, 2), "row"),     # W8A8 with E5M2
     (2100, 2200, 1024, (5, 2), (5, 2), "row"),  # E5M2 x E5M2 on the persistent kernel: 128x128 tiles, ragged
