@@ -988,6 +988,8 @@ def depth_packed_group(K, G):
     (300, 520, 1024, (4, 3), (4, 3), 128, "f16", False),   # ragged tiles
     (300, 520, 1152, (4, 3), (4, 3), 128, "f32", False),   # K steps past the last group
     (4100, 2200, 1280, (4, 3), (4, 3), 128, "f32", True),  # several tiles per workgroup, per-token
+    (130, 300, 128, (4, 3), (4, 3), 128, "f32", False),    # one group per row (a single four-step group)
+    (64, 260, 256, (4, 3), (4, 3), 128, "f16", True),      # two groups, one partial tile row
 ])
 def test_f8f6_group_scaled_weights(M, N, K, wf, af, G, sdt, per_token):
     """FP8 / FP6 weights with one scale per row and group of G codes along K ([W8A8]
