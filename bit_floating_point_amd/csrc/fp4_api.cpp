@@ -468,6 +468,8 @@ fp4_status fp4_gemm(const fp4_gemm_desc* d, void* stream) {
             return hip_status(launch_w8a8_fp8(p, s), "fp4_gemm/w8a8");
         if (!grp && p.wg.bits == 8 && p.wg.e == 5 && qa.bits == 8 && qa.e == 5)
             return hip_status(launch_w8a8_e5m2(p, s), "fp4_gemm/w8a8-e5m2");
+        if (!grp && p.wg.bits == 8 && qa.bits == 8 && p.wg.e != qa.e)
+            return hip_status(launch_w8a8_mixed(p, s), "fp4_gemm/w8a8-mixed");
         if (!grp && p.wg.bits == 6 && qa.bits == 6 && p.wg.e == qa.e && w6a6_fits(p))
             return hip_status(launch_w6a6_fp6(p, s), "fp4_gemm/w6a6");
         // E4M3 x E4M3 with group-128 scales: the persistent kernel, when its operands fit

@@ -88,6 +88,7 @@ hipError_t launch_w4a4_fp4(const GemmParams& p, hipStream_t s);
 void set_split_limit(int64_t bytes);  // 0: the 32-bit buffer range
 hipError_t launch_w8a8_fp8(const GemmParams& p, hipStream_t s);  // FP8 E4M3 x E4M3
 hipError_t launch_w8a8_e5m2(const GemmParams& p, hipStream_t s); // FP8 E5M2 x E5M2
+hipError_t launch_w8a8_mixed(const GemmParams& p, hipStream_t s); // E4M3 x E5M2 either way
 bool w6a6_fits(const GemmParams& p);                                // FP6 x FP6, one format
 hipError_t launch_w6a6_fp6(const GemmParams& p, hipStream_t s);
 bool w8a8_group_fits(const GemmParams& p);                          // E4M3 x E4M3, group-128 scales

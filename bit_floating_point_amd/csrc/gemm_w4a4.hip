@@ -22,7 +22,7 @@
 // The same kernel also runs the LLaMA MLP's gate/up pair with SwiGLU and the next
 // layer's E2M1 quantization in the epilogue (GLU), and the FP8 E4M3 x E4M3 product
 // (F8: one code per byte, 64-code steps; fp32 sums not exact, so held to a tolerance;
-// E5M2 x E5M2 too; and FP6 x FP6 of one format, 96-byte rows of 128-code steps),
+// E5M2 x E5M2 and the mixed FP8 pairs too; and FP6 x FP6 of one format, 96-byte rows of 128-code steps),
 // with tensor or row weight scales or, on 128x256 tiles, one scale per row and group of
 // 128 codes ([W8A8] section 2.2's group size; F8 = 2 / 3 for f32 / f16 scales).
 #include <algorithm>
@@ -134,9 +134,11 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     // epilogue gives y = fl32(T * a_m)
     constexpr bool GRP = F8 == 2 || F8 == 3;
     constexpr bool GF16 = F8 == 3;
-    // F8 = 4: OCP FP8 E5M2 x E5M2 (the MFMA's format code 1 on both operands), tensor or
-    // row weight scales; every other FP8 instance is E4M3 (code 0)
-    constexpr int FC = F8 == 4 ? 1 : 0;
+    // F8 = 4 / 5 / 6: OCP FP8 E5M2 x E5M2, E4M3 weights x E5M2 activations, E5M2 weights x
+    // E4M3 activations (the MFMA's format codes: 0 E4M3, 1 E5M2; both formats take the same
+    // K order in the matrix cores), tensor or row weight scales; the other FP8 instances are
+    // E4M3 x E4M3
+    constexpr int FCW = (F8 == 4 || F8 == 6) ? 1 : 0, FCA = (F8 == 4 || F8 == 5) ? 1 : 0;
     // F8 = 8 / 9: FP6 E2M3 / E3M2 on both operands (128x128 tiles, 4 wavefronts).  A step
     // is 128 codes, 96 bytes per row (six 16-byte segments); a lane's fragment of a 64-code
     // K-block is the 24 bytes [48 H + 24 hk, +24) of its row, read as three 8-byte pieces.
@@ -391,7 +393,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
             _Pragma("unroll") for (int i = 0; i < TM; i++) {                                               \
                 const i32x8 af = i32x8{(int)xa[i].x, (int)xa[i].y, (int)xa[i].z, (int)xa[i].w,             \
                                        (int)ya[i].x, (int)ya[i].y, (int)ya[i].z, (int)ya[i].w};            \
-                acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[j][i], FC, FC, 0, 127, 0, 127); \
+                acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[j][i], FCW, FCA, 0, 127, 0, 127); \
             }                                                                                              \
             xb[j] = *reinterpret_cast<const uint4*>(&SN[BOFF + swz(brow(j) + r32, 2 * hk)]);               \
             yb[j] = *reinterpret_cast<const uint4*>(&SN[BOFF + swz(brow(j) + r32, 2 * hk + 1)]);           \
@@ -448,7 +450,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
             _Pragma("unroll") for (int i = 0; i < TM; i++) {                                               \
                 const i32x8 af = i32x8{(int)xa[i].x, (int)xa[i].y, (int)xa[i].z, (int)xa[i].w,             \
                                        (int)ya[i].x, (int)ya[i].y, (int)ya[i].z, (int)ya[i].w};            \
-                acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[j][i], FC, FC, 0, 127, 0, 127); \
+                acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af, acc[j][i], FCW, FCA, 0, 127, 0, 127); \
             }                                                                                              \
         }                                                                                                  \
     } while (0)
@@ -951,8 +953,11 @@ hipError_t launch_w4a4_fp4(const GemmParams& p, hipStream_t s) { return launch_s
 // FP8 E4M3 x E4M3 (W8A8): the same kernel, one code per byte
 hipError_t launch_w8a8_fp8(const GemmParams& p, hipStream_t s) { return launch_split<1>(p, s); }
 
-// FP8 E5M2 x E5M2: the same kernel with the MFMA's E5M2 format code
+// FP8 E5M2 x E5M2 and the mixed FP8 pairs: the same kernel with the MFMA's format codes
 hipError_t launch_w8a8_e5m2(const GemmParams& p, hipStream_t s) { return launch_split<4>(p, s); }
+hipError_t launch_w8a8_mixed(const GemmParams& p, hipStream_t s) {
+    return p.wg.e == 4 ? launch_split<5>(p, s) : launch_split<6>(p, s);
+}
 
 // FP6 x FP6 of one format (W6A6), tensor or row weight scales: 128x128 tiles on 4
 // wavefronts (a 96-byte step row; larger tiles leave no room in LDS for four stages), one

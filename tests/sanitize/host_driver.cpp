@@ -33,6 +33,7 @@ hipError_t launch_w8a16_small(const GemmParams&, hipStream_t) STUB()
 hipError_t launch_w4a4_fp4(const GemmParams&, hipStream_t) STUB()
 hipError_t launch_w8a8_fp8(const GemmParams&, hipStream_t) STUB()
 hipError_t launch_w8a8_e5m2(const GemmParams&, hipStream_t) STUB()
+hipError_t launch_w8a8_mixed(const GemmParams&, hipStream_t) STUB()
 bool w6a6_fits(const GemmParams& p) { return p.K % 128 == 0; }
 hipError_t launch_w6a6_fp6(const GemmParams&, hipStream_t) STUB()
 bool w8a8_group_fits(const GemmParams& p) { return p.w_group == 128 && p.K % 128 == 0; }

@@ -1036,6 +1036,8 @@ def _padded_rows(packed, align=16):
     (256, 384, 512, (5, 2), (5, 2), "row"),     # W8A8 with E5M2
     (2100, 2200, 1024, (5, 2), (5, 2), "row"),  # E5M2 x E5M2 on the persistent kernel: 128x128 tiles, ragged
     (4100, 6000, 256, (5, 2), (5, 2), "tensor"),  # E5M2 x E5M2: rounds of 256x256 tiles and a leftover block
+    (300, 520, 544, (4, 3), (5, 2), "row"),     # mixed FP8: E4M3 weights, E5M2 activations
+    (4100, 6000, 256, (5, 2), (4, 3), "tensor"),  # mixed FP8: E5M2 weights, E4M3 activations, 256x256 tiles
     (300, 520, 544, (4, 3), (2, 3), "row"),     # mixed: FP8 E4M3 weights, FP6 E2M3 activations
     (130, 270, 96, (2, 3), (5, 2), "tensor"),   # mixed: FP6 weights, FP8 E5M2 activations; K below one step
     (300, 520, 544, (4, 3), (2, 1), "row"),     # FP8 weights, FP4 E2M1 activations
