@@ -22,9 +22,10 @@
 // The same kernel also runs the LLaMA MLP's gate/up pair with SwiGLU and the next
 // layer's E2M1 quantization in the epilogue (GLU), and the FP8 E4M3 x E4M3 product
 // (F8: one code per byte, 64-code steps; fp32 sums not exact, so held to a tolerance;
-// E5M2 x E5M2 and the mixed FP8 pairs too; and FP6 x FP6 of one format, 96-byte rows of 128-code steps),
-// with tensor or row weight scales or, on 128x256 tiles, one scale per row and group of
-// 128 codes ([W8A8] section 2.2's group size; F8 = 2 / 3 for f32 / f16 scales).
+// E5M2 x E5M2 and the mixed FP8 pairs too) with tensor or row weight scales or, on
+// 128x256 tiles, one scale per row and group of 128 codes ([W8A8] section 2.2's group
+// size; F8 = 2 / 3 for f32 / f16 scales), and FP6 x FP6 of one format (F8 = 8 / 9:
+// 96-byte rows of 128-code steps, 128x128 tiles).
 #include <algorithm>
 #include <atomic>
 
