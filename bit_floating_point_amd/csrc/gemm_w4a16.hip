@@ -88,6 +88,29 @@ __device__ __forceinline__ bf16x8 decode_mini4_bf16(uint32_t w) {
     }
 }
 
+// 8 two-mode codes -> 8 bf16 values, exact, in one pass for either grid: the magnitude
+// code c goes to bits 0..2 of an FP8 E4M3 byte for E1M2 (the subnormal c * 2^-9, scale 2^7
+// as above) or to bits 2..4 for E2M1: exponent field p of the E2M1 code then lands in the
+// E4M3 exponent's low bits and its mantissa bit in the top mantissa bit, so the byte is
+// 2^-6 times the E2M1 value (p = 0: the subnormal m * 2^-7; p >= 1: 2^(p - 7) (1 + m / 2)),
+// and the scale 2^6 restores it.  The shift and the scale are per lane (the grid of the
+// lane's scale group).
+__device__ __forceinline__ bf16x8 decode_two_mode_bf16(uint32_t w, bool e1m2) {
+    const uint32_t sh = e1m2 ? 0u : 2u;
+    const float sc = e1m2 ? 128.0f : 64.0f;
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 0,2,4,6 / 1,3,5,7
+    const uint32_t blo = ((lo & 0x07070707u) << sh) | ((lo & 0x08080808u) << 4);
+    const uint32_t bhi = ((hi & 0x07070707u) << sh) | ((hi & 0x08080808u) << 4);
+    const uint32_t d0 = __builtin_amdgcn_perm(bhi, blo, 0x05010400u);  // codes 0..3 in byte order
+    const uint32_t d1 = __builtin_amdgcn_perm(bhi, blo, 0x07030602u);  // codes 4..7
+    uint32_t o[4];
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, sc, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, sc, true));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, sc, false));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, sc, true));
+    return __builtin_bit_cast(bf16x8, o);
+}
+
 // The 16-byte pieces of two chunk loads e (rows r16 / 2) and o (rows 8 + r16 / 2),
 // swapped between neighbouring lanes 2i, 2i + 1 so that each lane ends up with both
 // chunks of one row: lane 2i keeps e (row i, chunk 2j) and takes its neighbour's e
@@ -463,12 +486,10 @@ __global__ void __launch_bounds__(kSmallWaves * 64) w4a16_small_kernel(GemmParam
                             o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(d1, 1.0f, true));
                         }
                         wf = __builtin_bit_cast(bf16x8, o);
+                    } else if (TWO) {
+                        wf = decode_two_mode_bf16(wd[j], e1m2);
                     } else {
                         wf = decode_mini4_bf16<GE>(wd[j]);
-                    }
-                    if (TWO) {
-                        const bf16x8 w1 = decode_mini4_bf16<1>(wd[j]);
-                        wf = e1m2 ? w1 : wf;
                     }
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[j]), wf, acc, 0, 0, 0);
                 }
