@@ -23,9 +23,9 @@
 // layer's E2M1 quantization in the epilogue (GLU), and the FP8 E4M3 x E4M3 product
 // (F8: one code per byte, 64-code steps; fp32 sums not exact, so held to a tolerance;
 // E5M2 x E5M2 and the mixed FP8 pairs too) with tensor or row weight scales or, on
-// 128x256 tiles, one scale per row and group of 128 codes ([W8A8] section 2.2's group
-// size; F8 = 2 / 3 for f32 / f16 scales), and FP6 x FP6 of one format (F8 = 8 / 9:
-// 96-byte rows of 128-code steps, 128x128 tiles).
+// 128x256 tiles, one scale per row and group of 64 or 128 ([W8A8] section 2.2's group
+// size) codes (F8 = 12 / 13, 2 / 3 for f32 / f16 scales) or f32 scales per 256 (F8 = 14),
+// and FP6 x FP6 of one format (F8 = 8 / 9: 96-byte rows of 128-code steps, 128x128 tiles).
 #include <algorithm>
 #include <atomic>
 
@@ -130,11 +130,12 @@ template <int BM, int BN, bool GLU, int F8 = 0, int NWV = 4>
 __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int grid_m, int ntiles, GluParams gp) {
     constexpr int CPB = F8 ? 1 : 2;  // codes per byte
     // F8 = 2 / 3: E4M3 weights with one f32 / f16 scale per output row and group of 128
-    // codes along K: each group's MFMA sum P_g (two 64-code K-blocks) is folded into a
-    // running sum T = fma(P_g, s[n, g], T) once the group's last MFMA has issued, and the
-    // epilogue gives y = fl32(T * a_m)
-    constexpr bool GRP = F8 == 2 || F8 == 3;
-    constexpr bool GF16 = F8 == 3;
+    // codes along K (12 / 13: groups of 64, 14: f32 scales per 256): each group's MFMA sum
+    // P_g (GS 64-code K-blocks) is folded into a running sum T = fma(P_g, s[n, g], T) once
+    // the group's last MFMA has issued, and the epilogue gives y = fl32(T * a_m)
+    constexpr bool GRP = F8 == 2 || F8 == 3 || (F8 >= 12 && F8 <= 15);
+    constexpr bool GF16 = F8 == 3 || F8 == 13 || F8 == 15;
+    constexpr int GS = (F8 == 12 || F8 == 13) ? 1 : (F8 == 14 || F8 == 15) ? 4 : 2;  // steps per group
     // F8 = 4 / 5 / 6: OCP FP8 E5M2 x E5M2, E4M3 weights x E5M2 activations, E5M2 weights x
     // E4M3 activations (the MFMA's format codes: 0 E4M3, 1 E5M2; both formats take the same
     // K order in the matrix cores), tensor or row weight scales; the other FP8 instances are
@@ -146,7 +147,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     // Both operands take the same order of K, so the product is the same as in the matrix
     // cores' own FP6 order.  Segment g of stage row r sits in slot (g + 3 ((r >> 3) & 1)) % 6:
     // rows r and r + 8 (the same banks at a 96-byte row stride) then differ by 12 banks.
-    constexpr bool F6 = F8 >= 8;
+    constexpr bool F6 = F8 == 8 || F8 == 9;
     constexpr int FC6 = F8 == 9 ? 3 : 2;
     constexpr int RB = F6 ? 96 : kBKBytes;  // bytes per row and step
     constexpr int NSEG = RB / 16;
@@ -218,9 +219,9 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
         }
     }
     uint32_t offA[LA], offB[LB], offS, offK, offR, offG = kOOB;
-    // GRP: scale bytes per element and per output row (K / 128 groups)
+    // GRP: scale bytes per element and per output row (K / (64 GS) groups)
     constexpr int gsz = GF16 ? 2 : 4;
-    const int64_t grow = GRP ? p.K / 128 * gsz : 0;
+    const int64_t grow = GRP ? p.K / (64 * GS) * gsz : 0;
     const i32x4v rsG = buf_words(p.w_scales, GRP ? p.N * grow : 0);
     // Tile order.  Workgroups are dispatched to the 8 XCDs in turn (workgroup b on XCD
     // b % 8), each XCD with its own L2.  When the grid is a multiple of 8, XCD x takes the
@@ -330,13 +331,13 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
     } while (0)
 // GRP: the group scales of the four-step group that starts at step KB (a multiple of 4)
 // of the load stream's tile into scale block BLK: 16 bytes of each column's scale row
-// from group KB / 2 on (f32: groups KB/2 .. +3, f16: .. +7; the fold uses the first
-// two).  Every thread issues one load (wavefronts 4..7 an out-of-range one into the
+// from group KB / GS on (f32: four groups, f16: eight; the four steps use the first
+// 4 / GS).  Every thread issues one load (wavefronts 4..7 an out-of-range one into the
 // unread KiB), so that all threads issue the same number of memory operations.
 #define FP4_DMAG(KB, BLK)                                                                                  \
     do {                                                                                                   \
         if constexpr (GRP) {                                                                               \
-            const uint32_t go_ = offG == kOOB ? kOOB : offG + (uint32_t)((KB) / 2 * gsz);                  \
+            const uint32_t go_ = offG == kOOB ? kOOB : offG + (uint32_t)((KB) / GS * gsz);                 \
             const uint32_t gb_ = (uint32_t)(uintptr_t)gsb + (wave < 4 ? (BLK) * 4096 + wave * 1024 : 8192); \
             dma16(rsG, go_, __builtin_amdgcn_readfirstlane(gb_));                                          \
         }                                                                                                  \
@@ -521,7 +522,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
             FP4_READH(SQ, 0, xa, xb);                                                                      \
             FP4_READH(SQ, 1, ya, yb);                                                                      \
             FP4_MMA8_REGS();                                                                               \
-            if constexpr ((PH) & 1) FP4_FOLD((PH) >> 1);                                                   \
+            if constexpr (((PH) + 1) % GS == 0) FP4_FOLD((PH) / GS);                                       \
             FP4_SYNC(W);                                                                                   \
             D;                                                                                             \
         } else if constexpr (F8 && BM * BN < 256 * 256) {                                                  \
@@ -560,7 +561,7 @@ __global__ void __launch_bounds__(64 * NWV) w4a4_fp4_kernel(GemmParams p, int gr
         FP4_PHASE(2 * PER_STEP, st3, st0, D3, 3);                                                          \
         if constexpr (GRP) gcnt++;                                                                         \
     } while (0)
-// GRP: fold group 2 gcnt + GG of the tile (the MFMA sums of its two steps) into the running
+// GRP: fold group GG of the current four-step group (the MFMA sums of its GS steps) into the running
 // sums: value v of block (j, i) is column wn * WN + 32 j + 8 (v/4) + 4 hk + v%4 of the
 // tile; its scale is element GG of that column's 16 bytes in scale block gcnt % 2.  The
 // accumulators start the next group at zero.  (Steps past K read zero operands: their
@@ -977,24 +978,33 @@ hipError_t launch_w6a6_fp6(const GemmParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-// FP8 E4M3 x E4M3 with f32 or f16 weight scales per row and group of 128 codes: the same
-// kernel on 128x256 tiles (8 wavefronts; the running sums take the registers that 256x256
-// tiles would need for accumulators), one launch.
+// FP8 E4M3 x E4M3 with f32 or f16 weight scales per row and group of 64 or 128 codes, or
+// f32 scales per 256: the same kernel on 128x256 tiles (8 wavefronts; the running sums
+// take the registers that 256x256 tiles would need for accumulators), one launch.
 bool w8a8_group_fits(const GemmParams& p) {
-    const int64_t grow = p.K / 128 * (p.w_scale_f16 ? 2 : 4);  // scale bytes per output row
-    return p.w_mode == 2 && p.w_group == 128 && p.K % 128 == 0 && grow % 4 == 0 && p.M * p.lda < kMaxBufBytes &&
-           p.N * p.ldw < kMaxBufBytes && p.N * grow < kMaxBufBytes;
+    if (p.w_mode != 2 || (p.w_group != 64 && p.w_group != 128 && p.w_group != 256) || p.K % p.w_group != 0) return false;
+    const int esz = p.w_scale_f16 ? 2 : 4;
+    const int64_t grow = p.K / p.w_group * esz;  // scale bytes per output row
+    // the scale loads of successive four-step groups start 256 / G scales apart: whole
+    // 4-byte words (so not f16 scales with groups of 256), as are the rows
+    return grow % 4 == 0 && 256 / p.w_group * esz % 4 == 0 && p.M * p.lda < kMaxBufBytes && p.N * p.ldw < kMaxBufBytes &&
+           p.N * grow < kMaxBufBytes;
 }
 hipError_t launch_w8a8_fp8_group(const GemmParams& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     const int64_t cus = cu_count();
     const int64_t gm = (p.M + 127) / 128, gn = (p.N + 255) / 256, nt = gm * gn;
-    if (p.w_scale_f16)
-        hipLaunchKernelGGL((w4a4_fp4_kernel<128, 256, false, 3, kBigTileWaves>), dim3((unsigned)std::min(nt, cus)),
-                           dim3(64 * kBigTileWaves), 0, s, p, (int)gm, (int)nt, GluParams{});
-    else
-        hipLaunchKernelGGL((w4a4_fp4_kernel<128, 256, false, 2, kBigTileWaves>), dim3((unsigned)std::min(nt, cus)),
-                           dim3(64 * kBigTileWaves), 0, s, p, (int)gm, (int)nt, GluParams{});
+    const dim3 grid((unsigned)std::min(nt, cus)), block(64 * kBigTileWaves);
+    const bool h = p.w_scale_f16 != 0;
+    if (p.w_group == 64) {
+        if (h) hipLaunchKernelGGL((w4a4_fp4_kernel<128, 256, false, 13, kBigTileWaves>), grid, block, 0, s, p, (int)gm, (int)nt, GluParams{});
+        else hipLaunchKernelGGL((w4a4_fp4_kernel<128, 256, false, 12, kBigTileWaves>), grid, block, 0, s, p, (int)gm, (int)nt, GluParams{});
+    } else if (p.w_group == 256) {  // f32 scales only (w8a8_group_fits)
+        hipLaunchKernelGGL((w4a4_fp4_kernel<128, 256, false, 14, kBigTileWaves>), grid, block, 0, s, p, (int)gm, (int)nt, GluParams{});
+    } else {
+        if (h) hipLaunchKernelGGL((w4a4_fp4_kernel<128, 256, false, 3, kBigTileWaves>), grid, block, 0, s, p, (int)gm, (int)nt, GluParams{});
+        else hipLaunchKernelGGL((w4a4_fp4_kernel<128, 256, false, 2, kBigTileWaves>), grid, block, 0, s, p, (int)gm, (int)nt, GluParams{});
+    }
     return hipGetLastError();
 }
 

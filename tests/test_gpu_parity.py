@@ -990,6 +990,9 @@ def depth_packed_group(K, G):
     (4100, 2200, 1280, (4, 3), (4, 3), 128, "f32", True),  # several tiles per workgroup, per-token
     (130, 300, 128, (4, 3), (4, 3), 128, "f32", False),    # one group per row (a single four-step group)
     (64, 260, 256, (4, 3), (4, 3), 128, "f16", True),      # two groups, one partial tile row
+    (300, 520, 1024, (4, 3), (4, 3), 64, "f32", False),    # groups of 64: a fold after every step
+    (300, 520, 1024, (4, 3), (4, 3), 256, "f16", True),    # groups of 256: a fold every four steps
+    (130, 270, 1280, (4, 3), (4, 3), 256, "f32", False),   # five groups of 256
 ])
 def test_f8f6_group_scaled_weights(M, N, K, wf, af, G, sdt, per_token):
     """FP8 / FP6 weights with one scale per row and group of G codes along K ([W8A8]
