@@ -882,8 +882,8 @@ static GemmParams column_block(const GemmParams& p, int64_t n0, int64_t n1) {
 // 256x128 0.59, 128x128 0.35.  With at least one full round of 256x256 tiles, the
 // whole rounds stay 256x256 and the column block left over for a partial last round
 // takes the shape that finishes it soonest (a partial round of big tiles leaves
-// compute units idle).  Fewer 256x256 tiles than compute units: 128x256 (E2M1) when they
-// give every compute unit a tile, else 128x128.
+// compute units idle).  Fewer 256x256 tiles than compute units: 128x256 when they give
+// every compute unit a tile (FP8 at 2048x4096x4096: 44.6 -> 43.0 us), else 128x128.
 template <int F8 = 0>
 static hipError_t launch_block(const GemmParams& p, hipStream_t s) {
     const int64_t cus = cu_count();
@@ -891,7 +891,7 @@ static hipError_t launch_block(const GemmParams& p, hipStream_t s) {
     if (t256 < cus) {
         // (one round of 256 x 128 tiles on 4 wavefronts measured the same as two of 128 x 128
         // at 2048 x 4096)
-        if (!F8 && ((p.M + 127) / 128) * gn256 >= cus) launch_cfg<128, 256, F8>(p, s, cus);
+        if (((p.M + 127) / 128) * gn256 >= cus) launch_cfg<128, 256, F8>(p, s, cus);
         else launch_cfg<128, 128, F8>(p, s, cus);
         return hipGetLastError();
     }

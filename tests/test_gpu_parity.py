@@ -896,6 +896,7 @@ def test_fp8_w8a16_gemm(fmt, M, N, K, mode, adt):
     (300, 520, 544, "row"),      # ragged tiles, a K tail of half a step
     (2100, 2200, 1024, "row"),   # several tiles per workgroup
     (4096, 5120, 4096, "tensor"),
+    (2048, 4096, 320, "row"),    # one round of 128x256 tiles, a K tail of one step
 ])
 def test_fp8_w8a8_gemm(M, N, K, mode):
     """W8A8: FP8 E4M3 activations (per-tensor scale) x FP8 E4M3 weights on the FP8 matrix
